@@ -1,0 +1,131 @@
+"""CPU oracle for batched generated-topology construction (test infrastructure).
+
+Only the tests, ``__graft_entry__.smoke()`` and the benchmark's ``cpu_baseline``
+leg may import this package. The HIP library never links, loads or calls it,
+and it shares no code with the library. The arithmetic lives in
+``oracle/oracle.cpp`` (plain C++, compiled with g++); this module compiles it on
+demand and marshals numpy arrays in and out.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "oracle.cpp")
+LIB = os.path.join(HERE, "liboracle.so")
+
+# Op ids, as documented in oracle.cpp.
+IDENTITY, COARSEN, REFINE, DILATE, PAD_NEG, PAD_POS, CONV_T_K3S2 = range(7)
+OP_IDS = {
+    "identity": IDENTITY, "coarsen": COARSEN, "refine": REFINE, "dilate": DILATE,
+    "pad_neg": PAD_NEG, "pad_pos": PAD_POS, "conv_t_k3s2": CONV_T_K3S2,
+}
+
+OK, INVALID, OVERFLOW, NOMEM = 0, 1, 2, 3
+
+# (field id, dtype, row width)
+FIELDS = {
+    "headers": (0, np.int64, 16),
+    "upper_origin": (1, np.int32, 4),
+    "upper_key": (2, np.uint64, 1),
+    "upper_first": (3, np.int32, 1),
+    "upper_mask": (4, np.uint64, 512),
+    "lower_origin": (5, np.int32, 4),
+    "lower_first": (6, np.int32, 1),
+    "lower_mask": (7, np.uint64, 64),
+    "lower_prefix": (8, np.uint16, 64),
+    "leaf_origin": (9, np.int32, 4),
+    "leaf_parent": (10, np.int32, 1),
+    "leaf_mask": (11, np.uint64, 8),
+    "leaf_prefix": (12, np.uint64, 1),
+    "leaf_offset": (13, np.int64, 1),
+    "ijk": (14, np.int32, 3),
+}
+
+HEADER_COLUMNS = [
+    "grid_index", "grid_count", "upper_count", "lower_count", "leaf_count",
+    "upper_begin", "lower_begin", "leaf_begin", "voxel_count", "voxel_begin",
+    "bbox_min_x", "bbox_min_y", "bbox_min_z", "bbox_max_x", "bbox_max_y", "bbox_max_z",
+]
+
+_lock = threading.Lock()
+_lib = None
+
+
+class OracleError(RuntimeError):
+    def __init__(self, status: int):
+        super().__init__(f"oracle status {status}")
+        self.status = status
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.cpp into liboracle.so with g++ (no GPU code involved)."""
+    if force or not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+        tmp = LIB + ".tmp"
+        subprocess.check_call(
+            ["g++", "-O2", "-std=c++17", "-shared", "-fPIC", "-o", tmp, SRC])
+        os.replace(tmp, LIB)
+    return LIB
+
+
+def bind(path: str):
+    """Load a compiled oracle library and declare its C signatures."""
+    lib = ctypes.CDLL(path)
+    lib.oracle_build.restype = ctypes.c_int
+    lib.oracle_build.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                 ctypes.c_void_p, ctypes.c_int32,
+                                 ctypes.POINTER(ctypes.c_void_p)]
+    lib.oracle_size.restype = ctypes.c_int64
+    lib.oracle_size.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    lib.oracle_copy.restype = ctypes.c_int
+    lib.oracle_copy.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    lib.oracle_free.restype = None
+    lib.oracle_free.argtypes = [ctypes.c_void_p]
+    return lib
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build()
+            _lib = bind(LIB)
+    return _lib
+
+
+def run(op, factor: int, ijk: np.ndarray, offsets: np.ndarray, fields=None, lib=None) -> dict:
+    """Run the oracle; returns {field: numpy array} (rows reshaped to the field's width).
+
+    Raises OracleError(status) for invalid arguments (1) or int32 overflow (2).
+    ``lib`` selects another compiled oracle (used to check that planted mistakes
+    are caught by the pins).
+    """
+    lib = lib or _load()
+    if isinstance(op, str):
+        op = OP_IDS[op]
+    ijk = np.ascontiguousarray(np.asarray(ijk, dtype=np.int32).reshape(-1, 3))
+    offsets = np.ascontiguousarray(np.asarray(offsets, dtype=np.int64))
+    B = int(offsets.shape[0]) - 1
+    handle = ctypes.c_void_p()
+    st = lib.oracle_build(int(op), int(factor),
+                          ijk.ctypes.data if ijk.size else None,
+                          offsets.ctypes.data, B, ctypes.byref(handle))
+    if st != OK:
+        raise OracleError(st)
+    try:
+        out = {}
+        for name in (fields or FIELDS.keys()):
+            fid, dt, width = FIELDS[name]
+            n = lib.oracle_size(handle, fid)
+            arr = np.empty(n, dtype=dt)
+            if n:
+                lib.oracle_copy(handle, fid, arr.ctypes.data)
+            out[name] = arr.reshape(-1, width) if width > 1 else arr
+        return out
+    finally:
+        lib.oracle_free(handle)

@@ -1,0 +1,356 @@
+// CPU oracle for batched generated-topology construction.
+//
+// TEST INFRASTRUCTURE ONLY. Nothing in the product path may link, load or call
+// this file; only the tests, the smoke check and the benchmark's CPU-baseline
+// leg use it. It shares no code, header, table or helper with the HIP library.
+//
+// What it computes, member by member (set semantics, int64 arithmetic):
+//   1. the op on the member's voxel set S
+//        coarsen_f  : { floor(v / f) }                       f in {2,4,8}
+//        refine_f   : { f*v + d : d in [0,f)^3 }             f in {2,4,8}
+//        dilate     : { v + e : e in [-1,1]^3 }   (26-neighbour box dilation)
+//        pad_neg    : { v + e : e in {-1,0}^3 }
+//        pad_pos    : { v + e : e in {0,1}^3 }
+//        k3s2 transpose : pad_neg(refine_2(S))
+//        identity   : S (a grid built directly from ijk)
+//      Source: "Batched leaf-mask topology construction for generated conv grids"
+//      (PR page), sections 1 and 2; factors 4 and 8 are the closed forms of the
+//      chained x2 passes described in section 1.
+//   2. the canonical order: root tiles by signed x-major tile coordinate (the
+//      offset-shifted sort key), then the x-major upper-node child offset, then
+//      the x-major lower-node child offset, then the x-major in-leaf bit index
+//      (PR page section 1; test plan: elementwise ijk equality pins this order).
+//   3. the tree derived from the ordered voxels: 8^3 leaves with 512-bit masks,
+//      16^3-leaf lower nodes, 32^3-lower upper nodes (one root tile each), parent
+//      links, first-child indices, per-grid counts, leaf voxel offsets and prefix
+//      popcounts, per-grid bounding boxes (PR page section 1, last bullet).
+//
+// Readings where the pages are silent (each is listed in the design notes):
+//   * coarsening rounds toward -infinity; refinement anchors at f*v;
+//   * no empty leaves or nodes are ever produced;
+//   * in-leaf bit n = x*64 + y*8 + z (word x, bit y*8+z); lower child bit
+//     (x*16+y)*16+z; upper child bit (x*32+y)*32+z;
+//   * leaf voxel offset = 0-based running voxel count inside the grid;
+//   * leaf prefix word packs seven 9-bit fields, field w-1 = voxels in words < w;
+//   * lower prefix table entry w = active children in words < w;
+//   * root key = (Tx+2^19)<<40 | (Ty+2^19)<<20 | (Tz+2^19), T = floor(c/4096);
+//   * empty grid bbox = (INT32_MAX)^3 .. (INT32_MIN)^3;
+//   * any output coordinate outside int32 rejects the whole call (status 2).
+#include <algorithm>
+#include <array>
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <vector>
+
+namespace {
+
+using i64 = int64_t;
+using u64 = uint64_t;
+
+enum Op { OP_IDENTITY = 0, OP_COARSEN = 1, OP_REFINE = 2, OP_DILATE = 3,
+          OP_PAD_NEG = 4, OP_PAD_POS = 5, OP_CONV_T_K3S2 = 6 };
+
+enum Status { ST_OK = 0, ST_INVALID = 1, ST_OVERFLOW = 2, ST_NOMEM = 3 };
+
+i64 floordiv(i64 a, i64 b) {
+  i64 q = a / b;
+  if ((a % b != 0) && ((a < 0) != (b < 0))) --q;
+  return q;
+}
+i64 floormod(i64 a, i64 b) { return a - floordiv(a, b) * b; }
+
+struct Vox { i64 x, y, z; };
+
+// The canonical position of a voxel, compared lexicographically:
+// (tile x,y,z) (upper child x,y,z) (lower child x,y,z) (in-leaf x,y,z).
+using Key = std::array<i64, 12>;
+
+Key canonical_key(const Vox& v) {
+  const i64 c[3] = {v.x, v.y, v.z};
+  Key k{};
+  for (int a = 0; a < 3; ++a) {
+    k[a] = floordiv(c[a], 4096);
+    k[3 + a] = floormod(floordiv(c[a], 128), 32);
+    k[6 + a] = floormod(floordiv(c[a], 8), 16);
+    k[9 + a] = floormod(c[a], 8);
+  }
+  return k;
+}
+
+Vox voxel_of_key(const Key& k) {
+  i64 c[3];
+  for (int a = 0; a < 3; ++a) c[a] = k[a] * 4096 + k[3 + a] * 128 + k[6 + a] * 8 + k[9 + a];
+  return {c[0], c[1], c[2]};
+}
+
+bool in_int32(i64 c) { return c >= INT32_MIN && c <= INT32_MAX; }
+
+// Applies the op to one member's voxels (duplicates allowed in the output).
+bool apply_op(int op, int factor, const std::vector<Vox>& in, std::vector<Vox>& out) {
+  out.clear();
+  auto box = [&](int lo, int hi, const std::vector<Vox>& src) {
+    for (const Vox& v : src)
+      for (int ex = lo; ex <= hi; ++ex)
+        for (int ey = lo; ey <= hi; ++ey)
+          for (int ez = lo; ez <= hi; ++ez) out.push_back({v.x + ex, v.y + ey, v.z + ez});
+  };
+  switch (op) {
+    case OP_IDENTITY: out = in; break;
+    case OP_COARSEN:
+      for (const Vox& v : in)
+        out.push_back({floordiv(v.x, factor), floordiv(v.y, factor), floordiv(v.z, factor)});
+      break;
+    case OP_REFINE:
+      for (const Vox& v : in)
+        for (int dx = 0; dx < factor; ++dx)
+          for (int dy = 0; dy < factor; ++dy)
+            for (int dz = 0; dz < factor; ++dz)
+              out.push_back({v.x * factor + dx, v.y * factor + dy, v.z * factor + dz});
+      break;
+    case OP_DILATE: box(-1, 1, in); break;
+    case OP_PAD_NEG: box(-1, 0, in); break;
+    case OP_PAD_POS: box(0, 1, in); break;
+    case OP_CONV_T_K3S2: {
+      std::vector<Vox> fine;
+      for (const Vox& v : in)
+        for (int dx = 0; dx < 2; ++dx)
+          for (int dy = 0; dy < 2; ++dy)
+            for (int dz = 0; dz < 2; ++dz) fine.push_back({v.x * 2 + dx, v.y * 2 + dy, v.z * 2 + dz});
+      box(-1, 0, fine);
+      break;
+    }
+    default: return false;
+  }
+  for (const Vox& v : out)
+    if (!in_int32(v.x) || !in_int32(v.y) || !in_int32(v.z)) return false;
+  return true;
+}
+
+int popcount64(u64 w) {
+  int n = 0;
+  for (int b = 0; b < 64; ++b) n += (int)((w >> b) & 1u);
+  return n;
+}
+
+}  // namespace
+
+// Result arrays, laid out like the fields the library exposes so that the tests
+// can compare them element by element.
+struct oracle_result {
+  int32_t B = 0;
+  std::vector<i64> headers;        // [B][16], see oracle_field_header
+  std::vector<int32_t> upper_origin;  // [N2][4] x, y, z, grid
+  std::vector<u64> upper_key;         // [N2]
+  std::vector<int32_t> upper_first;   // [N2] index of first lower child
+  std::vector<u64> upper_mask;        // [N2][512]
+  std::vector<int32_t> lower_origin;  // [N1][4] x, y, z, parent upper
+  std::vector<int32_t> lower_first;   // [N1] index of first leaf child
+  std::vector<u64> lower_mask;        // [N1][64]
+  std::vector<uint16_t> lower_prefix; // [N1][64]
+  std::vector<int32_t> leaf_origin;   // [L][4] x, y, z, grid
+  std::vector<int32_t> leaf_parent;   // [L]
+  std::vector<u64> leaf_mask;         // [L][8]
+  std::vector<u64> leaf_prefix;       // [L]
+  std::vector<i64> leaf_offset;       // [L]
+  std::vector<int32_t> ijk;           // [V][3]
+};
+
+extern "C" {
+
+// Field ids for oracle_size / oracle_copy.
+enum {
+  ORACLE_HEADERS = 0, ORACLE_UPPER_ORIGIN, ORACLE_UPPER_KEY, ORACLE_UPPER_FIRST,
+  ORACLE_UPPER_MASK, ORACLE_LOWER_ORIGIN, ORACLE_LOWER_FIRST, ORACLE_LOWER_MASK,
+  ORACLE_LOWER_PREFIX, ORACLE_LEAF_ORIGIN, ORACLE_LEAF_PARENT, ORACLE_LEAF_MASK,
+  ORACLE_LEAF_PREFIX, ORACLE_LEAF_OFFSET, ORACLE_IJK, ORACLE_NUM_FIELDS
+};
+
+// Builds the op's output for a batch of B members given as int32 ijk rows and
+// int64 member offsets. Returns 0 on success, 1 for invalid arguments, 2 when an
+// output coordinate leaves int32 (no result then), 3 when memory runs out.
+int oracle_build(int op, int factor, const int32_t* ijk, const int64_t* offsets, int32_t B,
+                 oracle_result** out) {
+  if (!out) return ST_INVALID;
+  *out = nullptr;
+  if (B < 1 || !offsets) return ST_INVALID;
+  if (offsets[0] != 0) return ST_INVALID;
+  for (int g = 0; g < B; ++g)
+    if (offsets[g + 1] < offsets[g]) return ST_INVALID;
+  if (offsets[B] > 0 && !ijk) return ST_INVALID;
+  const bool pow2 = factor == 2 || factor == 4 || factor == 8;
+  switch (op) {
+    case OP_COARSEN: case OP_REFINE: if (!pow2) return ST_INVALID; break;
+    case OP_CONV_T_K3S2: if (factor != 2) return ST_INVALID; break;
+    case OP_IDENTITY: case OP_DILATE: case OP_PAD_NEG: case OP_PAD_POS:
+      if (factor != 1) return ST_INVALID; break;
+    default: return ST_INVALID;
+  }
+  oracle_result* r = new (std::nothrow) oracle_result();
+  if (!r) return ST_NOMEM;
+  try {
+    r->B = B;
+    r->headers.assign((size_t)B * 16, 0);
+    i64 voxel_total = 0;
+    for (int g = 0; g < B; ++g) {
+      std::vector<Vox> in;
+      for (i64 i = offsets[g]; i < offsets[g + 1]; ++i)
+        in.push_back({ijk[3 * i], ijk[3 * i + 1], ijk[3 * i + 2]});
+      std::vector<Vox> res;
+      if (!apply_op(op, factor, in, res)) { delete r; return ST_OVERFLOW; }
+      std::vector<Key> keys;
+      keys.reserve(res.size());
+      for (const Vox& v : res) keys.push_back(canonical_key(v));
+      std::vector<Vox>().swap(res);
+      std::sort(keys.begin(), keys.end());
+      keys.erase(std::unique(keys.begin(), keys.end()), keys.end());
+
+      i64* h = &r->headers[(size_t)g * 16];
+      const i64 upper_begin = (i64)r->upper_key.size();
+      const i64 lower_begin = (i64)r->lower_first.size();
+      const i64 leaf_begin = (i64)r->leaf_parent.size();
+      i64 bmin[3] = {INT32_MAX, INT32_MAX, INT32_MAX};
+      i64 bmax[3] = {INT32_MIN, INT32_MIN, INT32_MIN};
+      i64 nvox = 0;
+      for (size_t i = 0; i < keys.size(); ++i) {
+        const Key& k = keys[i];
+        const bool new_upper = i == 0 || !std::equal(k.begin(), k.begin() + 3, keys[i - 1].begin());
+        const bool new_lower = new_upper || !std::equal(k.begin(), k.begin() + 6, keys[i - 1].begin());
+        const bool new_leaf = new_lower || !std::equal(k.begin(), k.begin() + 9, keys[i - 1].begin());
+        if (new_upper) {
+          r->upper_origin.insert(r->upper_origin.end(),
+              {(int32_t)(k[0] * 4096), (int32_t)(k[1] * 4096), (int32_t)(k[2] * 4096), (int32_t)g});
+          const u64 ux = (u64)(k[0] + (1 << 19)), uy = (u64)(k[1] + (1 << 19)), uz = (u64)(k[2] + (1 << 19));
+          r->upper_key.push_back((ux << 40) | (uy << 20) | uz);
+          r->upper_first.push_back((int32_t)r->lower_first.size());
+          r->upper_mask.insert(r->upper_mask.end(), 512, 0);
+        }
+        const i64 upper_idx = (i64)r->upper_key.size() - 1;
+        if (new_lower) {
+          r->lower_origin.insert(r->lower_origin.end(),
+              {(int32_t)(k[0] * 4096 + k[3] * 128), (int32_t)(k[1] * 4096 + k[4] * 128),
+               (int32_t)(k[2] * 4096 + k[5] * 128), (int32_t)upper_idx});
+          r->lower_first.push_back((int32_t)r->leaf_parent.size());
+          r->lower_mask.insert(r->lower_mask.end(), 64, 0);
+          const i64 bit = (k[3] * 32 + k[4]) * 32 + k[5];
+          r->upper_mask[(size_t)upper_idx * 512 + bit / 64] |= (u64)1 << (bit % 64);
+        }
+        const i64 lower_idx = (i64)r->lower_first.size() - 1;
+        if (new_leaf) {
+          r->leaf_origin.insert(r->leaf_origin.end(),
+              {(int32_t)(k[0] * 4096 + k[3] * 128 + k[6] * 8), (int32_t)(k[1] * 4096 + k[4] * 128 + k[7] * 8),
+               (int32_t)(k[2] * 4096 + k[5] * 128 + k[8] * 8), (int32_t)g});
+          r->leaf_parent.push_back((int32_t)lower_idx);
+          r->leaf_mask.insert(r->leaf_mask.end(), 8, 0);
+          r->leaf_offset.push_back(nvox);
+          const i64 bit = (k[6] * 16 + k[7]) * 16 + k[8];
+          r->lower_mask[(size_t)lower_idx * 64 + bit / 64] |= (u64)1 << (bit % 64);
+        }
+        const i64 leaf_idx = (i64)r->leaf_parent.size() - 1;
+        const i64 n = k[9] * 64 + k[10] * 8 + k[11];
+        r->leaf_mask[(size_t)leaf_idx * 8 + n / 64] |= (u64)1 << (n % 64);
+        const Vox v = voxel_of_key(k);
+        r->ijk.insert(r->ijk.end(), {(int32_t)v.x, (int32_t)v.y, (int32_t)v.z});
+        const i64 c[3] = {v.x, v.y, v.z};
+        for (int a = 0; a < 3; ++a) {
+          bmin[a] = std::min(bmin[a], c[a]);
+          bmax[a] = std::max(bmax[a], c[a]);
+        }
+        ++nvox;
+      }
+      h[0] = g;
+      h[1] = B;
+      h[2] = (i64)r->upper_key.size() - upper_begin;
+      h[3] = (i64)r->lower_first.size() - lower_begin;
+      h[4] = (i64)r->leaf_parent.size() - leaf_begin;
+      h[5] = upper_begin;
+      h[6] = lower_begin;
+      h[7] = leaf_begin;
+      h[8] = nvox;
+      h[9] = voxel_total;
+      for (int a = 0; a < 3; ++a) { h[10 + a] = bmin[a]; h[13 + a] = bmax[a]; }
+      voxel_total += nvox;
+    }
+    // Lower prefix tables: entry w counts active children in words 0..w-1.
+    const size_t n1 = r->lower_first.size();
+    r->lower_prefix.assign(n1 * 64, 0);
+    for (size_t l = 0; l < n1; ++l) {
+      int run = 0;
+      for (int w = 0; w < 64; ++w) {
+        r->lower_prefix[l * 64 + w] = (uint16_t)run;
+        run += popcount64(r->lower_mask[l * 64 + w]);
+      }
+    }
+    // Leaf prefix words: field w-1 (bits 9(w-1) .. 9(w-1)+8) = voxels in words 0..w-1.
+    const size_t nl = r->leaf_parent.size();
+    r->leaf_prefix.assign(nl, 0);
+    for (size_t l = 0; l < nl; ++l) {
+      u64 packed = 0;
+      u64 run = 0;
+      for (int w = 1; w < 8; ++w) {
+        run += (u64)popcount64(r->leaf_mask[l * 8 + w - 1]);
+        packed |= run << (9 * (w - 1));
+      }
+      r->leaf_prefix[l] = packed;
+    }
+  } catch (const std::bad_alloc&) {
+    delete r;
+    return ST_NOMEM;
+  }
+  *out = r;
+  return ST_OK;
+}
+
+// Number of elements (not bytes) of a field.
+int64_t oracle_size(const oracle_result* r, int field) {
+  if (!r) return -1;
+  switch (field) {
+    case ORACLE_HEADERS: return (int64_t)r->headers.size();
+    case ORACLE_UPPER_ORIGIN: return (int64_t)r->upper_origin.size();
+    case ORACLE_UPPER_KEY: return (int64_t)r->upper_key.size();
+    case ORACLE_UPPER_FIRST: return (int64_t)r->upper_first.size();
+    case ORACLE_UPPER_MASK: return (int64_t)r->upper_mask.size();
+    case ORACLE_LOWER_ORIGIN: return (int64_t)r->lower_origin.size();
+    case ORACLE_LOWER_FIRST: return (int64_t)r->lower_first.size();
+    case ORACLE_LOWER_MASK: return (int64_t)r->lower_mask.size();
+    case ORACLE_LOWER_PREFIX: return (int64_t)r->lower_prefix.size();
+    case ORACLE_LEAF_ORIGIN: return (int64_t)r->leaf_origin.size();
+    case ORACLE_LEAF_PARENT: return (int64_t)r->leaf_parent.size();
+    case ORACLE_LEAF_MASK: return (int64_t)r->leaf_mask.size();
+    case ORACLE_LEAF_PREFIX: return (int64_t)r->leaf_prefix.size();
+    case ORACLE_LEAF_OFFSET: return (int64_t)r->leaf_offset.size();
+    case ORACLE_IJK: return (int64_t)r->ijk.size();
+    default: return -1;
+  }
+}
+
+// Copies a field into dst (which must hold oracle_size(field) elements).
+int oracle_copy(const oracle_result* r, int field, void* dst) {
+  if (!r || !dst) return ST_INVALID;
+  auto cp = [&](const auto& v) {
+    if (!v.empty()) std::memcpy(dst, v.data(), v.size() * sizeof(v[0]));
+    return (int)ST_OK;
+  };
+  switch (field) {
+    case ORACLE_HEADERS: return cp(r->headers);
+    case ORACLE_UPPER_ORIGIN: return cp(r->upper_origin);
+    case ORACLE_UPPER_KEY: return cp(r->upper_key);
+    case ORACLE_UPPER_FIRST: return cp(r->upper_first);
+    case ORACLE_UPPER_MASK: return cp(r->upper_mask);
+    case ORACLE_LOWER_ORIGIN: return cp(r->lower_origin);
+    case ORACLE_LOWER_FIRST: return cp(r->lower_first);
+    case ORACLE_LOWER_MASK: return cp(r->lower_mask);
+    case ORACLE_LOWER_PREFIX: return cp(r->lower_prefix);
+    case ORACLE_LEAF_ORIGIN: return cp(r->leaf_origin);
+    case ORACLE_LEAF_PARENT: return cp(r->leaf_parent);
+    case ORACLE_LEAF_MASK: return cp(r->leaf_mask);
+    case ORACLE_LEAF_PREFIX: return cp(r->leaf_prefix);
+    case ORACLE_LEAF_OFFSET: return cp(r->leaf_offset);
+    case ORACLE_IJK: return cp(r->ijk);
+    default: return ST_INVALID;
+  }
+}
+
+void oracle_free(oracle_result* r) { delete r; }
+
+}  // extern "C"

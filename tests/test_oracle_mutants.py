@@ -1,0 +1,91 @@
+"""Planted mistakes in the oracle must be caught by its pins.
+
+Each case copies oracle/oracle.cpp, changes one line the way a plausible slip
+would (a transposed operand, a dropped or wrong term, a wrong sign or index, an
+off-by-one), compiles the copy with g++ on the CPU and runs the pin battery of
+test_oracle_pins.py against it. The battery must fail for every mutant; the
+unmodified oracle passes it (that is test_oracle_pins.py itself).
+"""
+import functools
+import os
+import subprocess
+
+import pytest
+
+import oracle
+from tests import test_oracle_pins as pins
+
+MUTANTS = {
+    "leaf bit x/y swapped": ("const i64 n = k[9] * 64 + k[10] * 8 + k[11];",
+                             "const i64 n = k[10] * 64 + k[9] * 8 + k[11];"),
+    "coarsen truncates": ("out.push_back({floordiv(v.x, factor), floordiv(v.y, factor), floordiv(v.z, factor)});",
+                          "out.push_back({v.x / factor, floordiv(v.y, factor), floordiv(v.z, factor)});"),
+    "refine sign": ("out.push_back({v.x * factor + dx, v.y * factor + dy, v.z * factor + dz});",
+                    "out.push_back({v.x * factor - dx, v.y * factor + dy, v.z * factor + dz});"),
+    "pad_neg box": ("case OP_PAD_NEG: box(-1, 0, in); break;", "case OP_PAD_NEG: box(0, 1, in); break;"),
+    "dilate box": ("case OP_DILATE: box(-1, 1, in); break;", "case OP_DILATE: box(-1, 0, in); break;"),
+    "k3s2 pad side": ("box(-1, 0, fine);", "box(0, 1, fine);"),
+    "tile axes transposed": ("k[a] = floordiv(c[a], 4096);", "k[2 - a] = floordiv(c[a], 4096);"),
+    "leaf prefix off by one": ("run += (u64)popcount64(r->leaf_mask[l * 8 + w - 1]);",
+                               "run += (u64)popcount64(r->leaf_mask[l * 8 + w]);"),
+    "lower prefix inclusive": ("r->lower_prefix[l * 64 + w] = (uint16_t)run;\n        run += popcount64(r->lower_mask[l * 64 + w]);",
+                               "run += popcount64(r->lower_mask[l * 64 + w]);\n        r->lower_prefix[l * 64 + w] = (uint16_t)run;"),
+    "bbox operand": ("bmin[a] = std::min(bmin[a], c[a]);", "bmin[a] = std::min(bmin[a], c[(a + 1) % 3]);"),
+    "root key axes": ("r->upper_key.push_back((ux << 40) | (uy << 20) | uz);",
+                      "r->upper_key.push_back((uz << 40) | (uy << 20) | ux);"),
+    "upper child bit": ("const i64 bit = (k[3] * 32 + k[4]) * 32 + k[5];",
+                        "const i64 bit = (k[5] * 32 + k[4]) * 32 + k[3];"),
+    "lower child bit": ("const i64 bit = (k[6] * 16 + k[7]) * 16 + k[8];",
+                        "const i64 bit = (k[6] * 16 + k[8]) * 16 + k[7];"),
+    "voxel begin": ("h[9] = voxel_total;", "h[9] = 0;"),
+    "leaf offset base": ("r->leaf_offset.push_back(nvox);", "r->leaf_offset.push_back(nvox + 1);"),
+    "upper first child": ("r->upper_first.push_back((int32_t)r->lower_first.size());",
+                          "r->upper_first.push_back((int32_t)r->leaf_parent.size());"),
+    "lower parent": ("(int32_t)(k[2] * 4096 + k[5] * 128), (int32_t)upper_idx});",
+                     "(int32_t)(k[2] * 4096 + k[5] * 128), (int32_t)g});"),
+    "overflow z unchecked": ("if (!in_int32(v.x) || !in_int32(v.y) || !in_int32(v.z)) return false;",
+                             "if (!in_int32(v.x) || !in_int32(v.y)) return false;"),
+}
+
+BATTERY = [
+    functools.partial(pins.test_bruteforce_sets_and_order, "identity", 1),
+    functools.partial(pins.test_bruteforce_sets_and_order, "coarsen", 2),
+    functools.partial(pins.test_bruteforce_sets_and_order, "refine", 2),
+    functools.partial(pins.test_bruteforce_sets_and_order, "dilate", 1),
+    functools.partial(pins.test_bruteforce_sets_and_order, "pad_neg", 1),
+    functools.partial(pins.test_bruteforce_sets_and_order, "conv_t_k3s2", 2),
+    functools.partial(pins.test_refine_count_and_roundtrip, 2),
+    pins.test_golden_canonical_order,
+    pins.test_golden_tree_worked_example,
+    functools.partial(pins.test_invariants_config1, "identity", 1),
+    functools.partial(pins.test_invariants_config1, "dilate", 1),
+    pins.test_invariants_random_sets,
+    pins.test_overflow_and_limits,
+]
+
+
+@pytest.fixture(scope="module")
+def source():
+    with open(oracle.SRC) as fh:
+        return fh.read()
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name, source, tmp_path, monkeypatch):
+    old, new = MUTANTS[name]
+    assert source.count(old) == 1, f"mutation anchor not unique for {name!r}"
+    src = tmp_path / "mutant.cpp"
+    src.write_text(source.replace(old, new))
+    so = tmp_path / "libmutant.so"
+    subprocess.check_call(["g++", "-O1", "-std=c++17", "-shared", "-fPIC", "-o", str(so), str(src)])
+    lib = oracle.bind(str(so))
+    monkeypatch.setattr(oracle, "run", functools.partial(oracle.run, lib=lib))
+    failures = []
+    for check in BATTERY:
+        try:
+            check()
+        except (AssertionError, oracle.OracleError, KeyError, IndexError, ValueError,
+                pytest.fail.Exception) as exc:
+            failures.append((getattr(check, "__name__", str(check)), type(exc).__name__))
+            break
+    assert failures, f"mutant {name!r} passed every pin"

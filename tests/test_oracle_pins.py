@@ -1,0 +1,464 @@
+"""Pins for the CPU oracle: brute force, closed forms, invariants, hand-derived fixtures.
+
+The oracle is the parity reference for the HIP library, so before it is trusted
+it is tied here to things other than itself:
+  * gather-form brute force (membership tested from the set definition, the
+    oracle itself scatters) on tiny random sets near 0, +-4096 and negative
+    octants, for every op and factor;
+  * closed forms: |refine_f(S)| = f^3 |S|, coarsen_f(refine_f(S)) = S,
+    refine_4 = refine_2 o refine_2, coarsen likewise, k3s2 transpose =
+    {2v + e : e in [-1,1]^3}, dilate = pad_pos o pad_neg, the 27-voxel cube of a
+    dilated voxel, solid aligned cubes of side 8n;
+  * an independent packed-integer formulation of the canonical order;
+  * invariants of every derived field (masks against the enumeration, ranks
+    against prefix words and offsets, child masks against parent links, bboxes);
+  * hand-derived fixtures under tests/golden (each with its citation).
+Sources are the PR page "Batched leaf-mask topology construction for generated
+conv grids": section 1 (emission, canonical order, dedup, writers), section 2
+(box dilation and pads) and the test plan (edge cases).
+"""
+import itertools
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from topology_construction_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+ALL_OPS = [("identity", 1), ("coarsen", 2), ("coarsen", 4), ("coarsen", 8),
+           ("refine", 2), ("refine", 4), ("refine", 8), ("dilate", 1),
+           ("pad_neg", 1), ("pad_pos", 1), ("conv_t_k3s2", 2)]
+
+
+# ---------------------------------------------------------------- brute force
+def _members_from_sets(sets):
+    return synth.concat_members([np.array(sorted(s), dtype=np.int32).reshape(-1, 3) for s in sets])
+
+
+def gather_member(op, f, S):
+    """Output set of one member via gather-form membership tests on a superset."""
+    cand = set()
+    box = {"dilate": (-1, 1), "pad_neg": (-1, 0), "pad_pos": (0, 1)}
+    for (x, y, z) in S:
+        if op == "identity":
+            cand.add((x, y, z))
+        elif op == "coarsen":
+            for d in itertools.product((-1, 0, 1), repeat=3):
+                cand.add((x // f + d[0], y // f + d[1], z // f + d[2]))
+        elif op == "refine":
+            for d in itertools.product(range(-1, f + 1), repeat=3):
+                cand.add((f * x + d[0], f * y + d[1], f * z + d[2]))
+        elif op in box:
+            for d in itertools.product((-2, -1, 0, 1, 2), repeat=3):
+                cand.add((x + d[0], y + d[1], z + d[2]))
+        elif op == "conv_t_k3s2":
+            for d in itertools.product(range(-2, 4), repeat=3):
+                cand.add((2 * x + d[0], 2 * y + d[1], 2 * z + d[2]))
+    out = set()
+    for p in cand:
+        if op == "identity":
+            ok = p in S
+        elif op == "coarsen":
+            ok = any((f * p[0] + a, f * p[1] + b, f * p[2] + c) in S
+                     for a, b, c in itertools.product(range(f), repeat=3))
+        elif op == "refine":
+            ok = (p[0] // f, p[1] // f, p[2] // f) in S
+        elif op in box:
+            lo, hi = box[op]
+            ok = any((p[0] - a, p[1] - b, p[2] - c) in S
+                     for a, b, c in itertools.product(range(lo, hi + 1), repeat=3))
+        elif op == "conv_t_k3s2":
+            ok = any(((p[0] - a) // 2, (p[1] - b) // 2, (p[2] - c) // 2) in S
+                     for a, b, c in itertools.product((-1, 0), repeat=3))
+        if ok:
+            out.add(p)
+    return out
+
+
+def packed_order_key(p):
+    """Canonical position as one packed integer (independent of the oracle's tuple).
+
+    root key (60 bits) | upper child offset (15) | lower child offset (12) | leaf bit (9)
+    """
+    x, y, z = p
+    root = (((x >> 12) + (1 << 19)) << 40) | (((y >> 12) + (1 << 19)) << 20) | ((z >> 12) + (1 << 19))
+    up = ((((x >> 7) & 31) * 32 + ((y >> 7) & 31)) * 32) + ((z >> 7) & 31)
+    lo = ((((x >> 3) & 15) * 16 + ((y >> 3) & 15)) * 16) + ((z >> 3) & 15)
+    bit = (x & 7) * 64 + (y & 7) * 8 + (z & 7)
+    return (((root << 15 | up) << 12 | lo) << 9) | bit
+
+
+def random_sets(rng, n_members, max_vox, centres):
+    sets = []
+    for _ in range(n_members):
+        k = int(rng.integers(0, max_vox + 1))
+        s = set()
+        for _ in range(k):
+            c = centres[int(rng.integers(0, len(centres)))]
+            v = tuple(int(c[a] + rng.integers(-9, 10)) for a in range(3))
+            s.add(v)
+        sets.append(s)
+    return sets
+
+
+CENTRES = [(0, 0, 0), (4096, 0, -4096), (-4096, 4095, 127), (-1, -1, -1), (130, -130, 8),
+           (-8192, 8191, 0), ((1 << 29), -(1 << 29), 5)]
+
+
+@pytest.mark.parametrize("op,f", ALL_OPS)
+def test_bruteforce_sets_and_order(op, f):
+    rng = np.random.default_rng(1000 + ALL_OPS.index((op, f)))
+    for trial in range(3):
+        # refine by 4 or 8 would leave int32 around 2^29 (covered by the overflow test)
+        centres = CENTRES if not (op == "refine" and f > 2) else CENTRES[:-1]
+        sets = random_sets(rng, 3, 10 if op not in ("refine",) or f < 8 else 4, centres)
+        sets[1] = set() if trial == 1 else sets[1]
+        ijk, off = _members_from_sets(sets)
+        r = oracle.run(op, f, ijk, off)
+        hdr = r["headers"]
+        for g, S in enumerate(sets):
+            exp = gather_member(op, f, S)
+            b, n = hdr[g, 9], hdr[g, 8]
+            got = [tuple(v) for v in r["ijk"][b:b + n].tolist()]
+            assert set(got) == exp, (op, f, g)
+            assert len(got) == len(exp)
+            # enumeration order equals the packed canonical key order
+            assert got == sorted(exp, key=packed_order_key)
+
+
+# ---------------------------------------------------------------- closed forms
+def _run_sets(op, f, sets):
+    ijk, off = _members_from_sets(sets)
+    return oracle.run(op, f, ijk, off)
+
+
+def _grid_sets(r):
+    hdr = r["headers"]
+    return [set(map(tuple, r["ijk"][hdr[g, 9]:hdr[g, 9] + hdr[g, 8]].tolist())) for g in range(hdr.shape[0])]
+
+
+@pytest.mark.parametrize("f", [2, 4, 8])
+def test_refine_count_and_roundtrip(f):
+    ijk, off = synth.make_config(1)
+    r = oracle.run("refine", f, ijk, off)
+    base = oracle.run("identity", 1, ijk, off)
+    assert np.array_equal(r["headers"][:, 8], f ** 3 * base["headers"][:, 8])
+    back = oracle.run("coarsen", f, r["ijk"], np.concatenate([[0], np.cumsum(r["headers"][:, 8])]))
+    for name in ("ijk", "leaf_mask", "leaf_origin", "lower_mask", "upper_mask", "headers"):
+        assert np.array_equal(back[name], base[name]), name
+
+
+@pytest.mark.parametrize("op", ["refine", "coarsen"])
+def test_factor4_8_equal_chained_x2(op):
+    ijk, off = synth.make_config(1)
+    ijk = ijk.astype(np.int64)
+    ijk[:, 0] -= 9  # negative octant
+    ijk = ijk.astype(np.int32)
+    prev = oracle.run("identity", 1, ijk, off)
+    for f in (2, 4, 8):
+        step = oracle.run(op, 2, prev["ijk"], np.concatenate([[0], np.cumsum(prev["headers"][:, 8])]))
+        direct = oracle.run(op, f, ijk, off)
+        for k in oracle.FIELDS:
+            assert np.array_equal(step[k], direct[k]), (op, f, k)
+        prev = step
+
+
+def test_k3s2_transpose_closed_form():
+    rng = np.random.default_rng(7)
+    sets = random_sets(rng, 3, 12, CENTRES)
+    r = _run_sets("conv_t_k3s2", 2, sets)
+    for g, S in enumerate(sets):
+        exp = {(2 * x + a, 2 * y + b, 2 * z + c) for (x, y, z) in S
+               for a, b, c in itertools.product((-1, 0, 1), repeat=3)}
+        assert _grid_sets(r)[g] == exp
+
+
+def test_dilate_equals_pad_pos_of_pad_neg():
+    ijk, off = synth.make_config(3)
+    ijk, off = ijk[: off[8]], off[:9]
+    d = oracle.run("dilate", 1, ijk, off)
+    a = oracle.run("pad_neg", 1, ijk, off)
+    b = oracle.run("pad_pos", 1, a["ijk"], np.concatenate([[0], np.cumsum(a["headers"][:, 8])]))
+    for k in oracle.FIELDS:
+        assert np.array_equal(d[k], b[k]), k
+
+
+@pytest.mark.parametrize("v", [(0, 0, 0), (7, 7, 7), (-1, -1, -1), (4095, -4096, 8), (-(1 << 31), 5, (1 << 31) - 2)])
+def test_single_voxel_dilate_is_27_cube(v):
+    if v[0] == -(1 << 31):
+        with pytest.raises(oracle.OracleError) as e:
+            _run_sets("dilate", 1, [{v}])
+        assert e.value.status == oracle.OVERFLOW
+        return
+    r = _run_sets("dilate", 1, [{v}])
+    exp = sorted(((v[0] + a, v[1] + b, v[2] + c) for a, b, c in itertools.product((-1, 0, 1), repeat=3)),
+                 key=packed_order_key)
+    assert [tuple(p) for p in r["ijk"].tolist()] == exp
+
+
+@pytest.mark.parametrize("n,origin", [(1, (0, 0, 0)), (2, (-16, 8, 4096 - 8)), (1, (-8, -8, -8))])
+def test_solid_cube_closed_forms(n, origin):
+    side = 8 * n
+    cube = synth.cube_voxels(side, origin)
+    off = np.array([0, cube.shape[0]])
+    lo = np.array(origin)
+    for op, f, exp_side, exp_lo in (("refine", 2, 16 * n, 2 * lo), ("coarsen", 2, 4 * n, lo // 2),
+                                     ("dilate", 1, 8 * n + 2, lo - 1)):
+        r = oracle.run(op, f, cube, off)
+        got = r["ijk"]
+        assert got.shape[0] == exp_side ** 3
+        assert np.array_equal(got.min(0), exp_lo) and np.array_equal(got.max(0), exp_lo + exp_side - 1)
+        assert r["headers"][0, 10:13].tolist() == exp_lo.tolist()
+    # a solid aligned cube of side 8n consists of n^3 full leaves
+    r = oracle.run("identity", 1, cube, off)
+    assert r["leaf_mask"].shape[0] == n ** 3
+    assert np.all(r["leaf_mask"] == np.uint64(0xFFFFFFFFFFFFFFFF))
+
+
+# ---------------------------------------------------------------- invariants
+def _popcount(a):
+    a = np.asarray(a, dtype=np.uint64)
+    return np.unpackbits(a.view(np.uint8), axis=-1).reshape(a.shape + (64,)).sum(-1)
+
+
+def check_invariants(r):
+    hdr = r["headers"]
+    B = hdr.shape[0]
+    ijk = r["ijk"].astype(np.int64)
+    lo, lm, lp, lof = r["leaf_origin"], r["leaf_mask"], r["leaf_prefix"], r["leaf_offset"]
+    L = lo.shape[0]
+    lc = _popcount(lm).sum(-1) if L else np.zeros(0, np.int64)
+    # headers: begins are running sums, grid index / count
+    assert np.array_equal(hdr[:, 0], np.arange(B))
+    assert np.all(hdr[:, 1] == B)
+    for col_n, col_b in ((2, 5), (3, 6), (4, 7), (8, 9)):
+        assert np.array_equal(hdr[:, col_b], np.concatenate([[0], np.cumsum(hdr[:, col_n])[:-1]]))
+    assert hdr[:, 8].sum() == ijk.shape[0] == lc.sum()
+    for g in range(B):
+        vb, vn = hdr[g, 9], hdr[g, 8]
+        lb, ln = hdr[g, 7], hdr[g, 4]
+        pts = ijk[vb:vb + vn]
+        if vn == 0:
+            assert hdr[g, 10:13].tolist() == [2 ** 31 - 1] * 3 and hdr[g, 13:16].tolist() == [-2 ** 31] * 3
+            assert ln == 0 and hdr[g, 2] == 0 and hdr[g, 3] == 0
+            continue
+        assert np.array_equal(hdr[g, 10:13], pts.min(0)) and np.array_equal(hdr[g, 13:16], pts.max(0))
+        keys = [packed_order_key(tuple(p)) for p in pts.tolist()]
+        assert all(a < b for a, b in zip(keys, keys[1:]))  # strictly increasing
+        assert np.all(lo[lb:lb + ln, 3] == g)
+        # leaf offsets are running popcounts inside the grid
+        assert np.array_equal(lof[lb:lb + ln], np.concatenate([[0], np.cumsum(lc[lb:lb + ln])[:-1]]))
+        # every voxel: its rank from leaf offset + prefix field + in-word popcount
+        leaf_of = {tuple(lo[l, :3]): l for l in range(lb, lb + ln)}
+        for i, p in enumerate(pts.tolist()):
+            org = tuple(int(c) & ~7 for c in p)
+            l = leaf_of[org]
+            x, y, z = (p[0] & 7, p[1] & 7, p[2] & 7)
+            n = x * 64 + y * 8 + z
+            w, b = divmod(n, 64)
+            word = int(lm[l, w])
+            assert (word >> b) & 1
+            field = 0 if w == 0 else (int(lp[l]) >> (9 * (w - 1))) & 511
+            below = bin(word & ((1 << b) - 1)).count("1")
+            assert int(lof[l]) + field + below == i
+    # leaf masks decode to exactly the enumerated voxels of the leaf
+    rows = {}
+    for g in range(B):
+        for p in ijk[hdr[g, 9]:hdr[g, 9] + hdr[g, 8]].tolist():
+            rows.setdefault((g, p[0] & ~7, p[1] & ~7, p[2] & ~7), []).append(p)
+    for l in range(L):
+        o = lo[l, :3].tolist()
+        dec = []
+        for n in range(512):
+            if (int(lm[l, n // 64]) >> (n % 64)) & 1:
+                dec.append([o[0] + n // 64, o[1] + (n // 8) % 8, o[2] + n % 8])
+        assert sorted(dec) == sorted(rows[(int(lo[l, 3]),) + tuple(o)])
+    # lower nodes: child mask bits <-> the leaves whose parent it is, contiguous from first
+    low_o, low_f, low_m, low_p = r["lower_origin"], r["lower_first"], r["lower_mask"], r["lower_prefix"]
+    parent = r["leaf_parent"]
+    for k in range(low_o.shape[0]):
+        kids = np.nonzero(parent == k)[0]
+        assert kids.size > 0 and kids[0] == low_f[k] and np.array_equal(kids, np.arange(kids[0], kids[-1] + 1))
+        o = low_o[k, :3]
+        bits = []
+        for l in kids:
+            d = (lo[l, :3] - o) // 8
+            assert np.all((d >= 0) & (d < 16)) and np.all(lo[l, :3] - o - 8 * d == 0)
+            bits.append((d[0] * 16 + d[1]) * 16 + d[2])
+        assert bits == sorted(bits)
+        dec = [n for n in range(4096) if (int(low_m[k, n // 64]) >> (n % 64)) & 1]
+        assert dec == bits
+        # prefix table: entry w = active children in words < w
+        run = 0
+        for w in range(64):
+            assert low_p[k, w] == run
+            run += bin(int(low_m[k, w])).count("1")
+        assert np.all(lo[kids, 3] == lo[kids[0], 3])
+    # upper nodes
+    up_o, up_f, up_m, up_k = r["upper_origin"], r["upper_first"], r["upper_mask"], r["upper_key"]
+    for u in range(up_o.shape[0]):
+        kids = np.nonzero(low_o[:, 3] == u)[0]
+        assert kids.size > 0 and kids[0] == up_f[u] and np.array_equal(kids, np.arange(kids[0], kids[-1] + 1))
+        o = up_o[u, :3]
+        assert np.all(o % 4096 == 0)
+        T = o // 4096
+        assert int(up_k[u]) == ((int(T[0]) + (1 << 19)) << 40) | ((int(T[1]) + (1 << 19)) << 20) | (int(T[2]) + (1 << 19))
+        bits = []
+        for k in kids:
+            d = (low_o[k, :3] - o) // 128
+            assert np.all((d >= 0) & (d < 32))
+            bits.append((d[0] * 32 + d[1]) * 32 + d[2])
+        assert bits == sorted(bits)
+        dec = [n for n in range(32768) if (int(up_m[u, n // 64]) >> (n % 64)) & 1]
+        assert dec == bits
+        assert np.all(lo[parent == kids[0], 3] == up_o[u, 3])
+    for g in range(B):
+        ub, un = hdr[g, 5], hdr[g, 2]
+        assert np.all(up_o[ub:ub + un, 3] == g)
+        assert np.all(np.diff(up_k[ub:ub + un].astype(object)) > 0) if un > 1 else True
+
+
+@pytest.mark.parametrize("op,f", [("identity", 1), ("coarsen", 2), ("refine", 2), ("dilate", 1),
+                                  ("pad_neg", 1), ("pad_pos", 1), ("conv_t_k3s2", 2), ("refine", 4)])
+def test_invariants_config1(op, f):
+    ijk, off = synth.make_config(1)
+    check_invariants(oracle.run(op, f, ijk, off))
+
+
+@pytest.mark.parametrize("op,f", [("identity", 1), ("coarsen", 2), ("dilate", 1)])
+def test_invariants_straddling_members(op, f):
+    ijk, off = synth.make_config(3)
+    sel = [0, 1, 3, 5]  # empty first member + the three forced tile-straddling members
+    members = [ijk[off[g]:off[g + 1]] for g in sel]
+    ijk2, off2 = synth.concat_members(members)
+    check_invariants(oracle.run(op, f, ijk2, off2))
+
+
+def test_invariants_random_sets():
+    rng = np.random.default_rng(11)
+    sets = random_sets(rng, 5, 40, CENTRES[:-1])  # stay clear of int32 limits for refine x4
+    sets[0] = set()
+    sets[4] = set()
+    for op, f in ALL_OPS:
+        if op == "refine" and f == 8:
+            continue
+        check_invariants(_run_sets(op, f, sets))
+
+
+# ---------------------------------------------------------------- edge cases
+def test_all_members_empty():
+    off = np.zeros(4, dtype=np.int64)
+    for op, f in ALL_OPS:
+        r = oracle.run(op, f, np.zeros((0, 3), np.int32), off)
+        assert r["ijk"].shape[0] == 0 and r["leaf_mask"].shape[0] == 0
+        assert np.all(r["headers"][:, 2:10] == 0)
+        check_invariants(r)
+
+
+def test_overflow_and_limits():
+    ok = (1 << 30) - 1
+    r = _run_sets("refine", 2, [{(ok, -ok - 1, 0)}])
+    assert r["ijk"].max() == (1 << 31) - 1 and r["ijk"].min() == -(1 << 31)
+    for bad in [(1 << 30, 0, 0), (0, -(1 << 30) - 1, 0)]:
+        with pytest.raises(oracle.OracleError) as e:
+            _run_sets("refine", 2, [{bad}])
+        assert e.value.status == oracle.OVERFLOW
+    with pytest.raises(oracle.OracleError):
+        _run_sets("pad_pos", 1, [set(), {(0, 0, (1 << 31) - 1)}])
+    r = _run_sets("pad_neg", 1, [{(0, 0, (1 << 31) - 1)}])
+    assert r["ijk"].shape[0] == 8
+    r = _run_sets("coarsen", 8, [{(-(1 << 31), (1 << 31) - 1, 0)}])
+    assert r["ijk"].tolist() == [[-(1 << 28), (1 << 28) - 1, 0]]
+
+
+@pytest.mark.parametrize("op,f", [("refine", 3), ("coarsen", 1), ("dilate", 2), ("conv_t_k3s2", 4), ("bogus", 1)])
+def test_invalid_args(op, f):
+    with pytest.raises((oracle.OracleError, KeyError)):
+        oracle.run(op, f, np.zeros((1, 3), np.int32), np.array([0, 1]))
+    with pytest.raises(oracle.OracleError):
+        oracle.run("identity", 1, np.zeros((1, 3), np.int32), np.array([0]))  # B = 0
+
+
+def test_octant_corners_of_root_tile():
+    # one voxel at each of the 8 corners of tile (0,0,0), and just across it
+    corners = [(a, b, c) for a in (0, 4095) for b in (0, 4095) for c in (0, 4095)]
+    across = [(a + (1 if a else -1), b, c) for (a, b, c) in corners]
+    for op, f in ALL_OPS:
+        if op == "refine" and f == 8:
+            continue
+        r = _run_sets(op, f, [set(corners), set(across)])
+        check_invariants(r)
+        for g, S in enumerate([set(corners), set(across)]):
+            assert _grid_sets(r)[g] == gather_member(op, f, S)
+
+
+# ---------------------------------------------------------------- golden fixtures
+def _read_golden(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as fh:
+        for line in fh:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                rows.append(line.split())
+    return rows
+
+
+def test_golden_canonical_order():
+    rows = _read_golden("canonical_order.txt")
+    inp = [[int(v) for v in r[1:]] for r in rows if r[0] == "input"]
+    exp = [[int(v) for v in r[1:]] for r in rows if r[0] == "expect"]
+    r = oracle.run("identity", 1, np.array(inp, np.int32), np.array([0, len(inp)]))
+    assert r["ijk"].tolist() == exp
+    assert r["upper_origin"][:, 0].tolist() == [-8192, -4096, 0, 4096]
+
+
+def test_golden_tree_worked_example():
+    rows = _read_golden("tree_worked_example.txt")
+    B = int([r for r in rows if r[0] == "members"][0][1])
+    members = [[] for _ in range(B)]
+    for r in rows:
+        if r[0] == "input":
+            members[int(r[1])].append([int(v) for v in r[2:]])
+    ijk, off = synth.concat_members([np.array(m, np.int32).reshape(-1, 3) for m in members])
+    res = oracle.run("identity", 1, ijk, off)
+
+    def ints(r, a=1):
+        return [int(v, 0) for v in r[a:]]
+
+    for r in rows:
+        tag = r[0]
+        if tag == "header":
+            assert res["headers"][int(r[1])].tolist() == ints(r, 2)
+        elif tag == "upper":
+            u = int(r[1])
+            v = ints(r, 2)
+            assert res["upper_origin"][u].tolist() == v[:4]
+            assert int(res["upper_key"][u]) == v[4] and int(res["upper_first"][u]) == v[5]
+        elif tag == "upper_bits":
+            u = int(r[1])
+            m = res["upper_mask"][u]
+            assert [n for n in range(32768) if (int(m[n // 64]) >> (n % 64)) & 1] == ints(r, 2)
+        elif tag == "lower":
+            k = int(r[1])
+            v = ints(r, 2)
+            assert res["lower_origin"][k].tolist() == v[:4] and int(res["lower_first"][k]) == v[4]
+        elif tag == "lower_bits":
+            m = res["lower_mask"][int(r[1])]
+            assert [n for n in range(4096) if (int(m[n // 64]) >> (n % 64)) & 1] == ints(r, 2)
+        elif tag == "leaf":
+            l = int(r[1])
+            v = ints(r, 2)
+            assert res["leaf_origin"][l].tolist() == v[:4]
+            assert int(res["leaf_parent"][l]) == v[4] and int(res["leaf_offset"][l]) == v[5]
+            assert int(res["leaf_prefix"][l]) == v[6]
+        elif tag == "leaf_bits":
+            m = res["leaf_mask"][int(r[1])]
+            assert [n for n in range(512) if (int(m[n // 64]) >> (n % 64)) & 1] == ints(r, 2)
+    exp_ijk = [ints(r) for r in rows if r[0] == "ijk"]
+    assert res["ijk"].tolist() == exp_ijk
+    assert res["upper_origin"].shape[0] == len([r for r in rows if r[0] == "upper"])
+    assert res["lower_origin"].shape[0] == len([r for r in rows if r[0] == "lower"])
+    assert res["leaf_origin"].shape[0] == len([r for r in rows if r[0] == "leaf"])

@@ -1,0 +1,153 @@
+"""Benchmark of the batched topology hot path on one MI355X.
+
+A step is one pass of the whole hot path over the B=16 resolution-64 shell
+batch (16 ellipsoid shells, ~7.4k voxels each; it stands in for the pages'
+shape-VAE workload of 16 shoes at resolution 64): conv k2s2 (coarsen x2),
+k2s2 transpose (refine x2), k3s1 (box-dilate [-1,1]^3) and the chained k3s2
+transpose (refine x2 then pad {-1,0}^3), each followed by the jagged voxel
+enumeration. Inputs are resident in HBM before timing starts.
+
+Prints one JSON line (rank 0). `value` = output voxels per second over the K
+timed steps. `roofline` reports the dominant kernel's algorithmic bytes per
+launch over its HIP-event-timed average duration; `cpu_baseline` times the CPU
+oracle on one step of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "output voxels/s & ms per batched pass (k2s2 refine/coarsen, k3s1 dilate), B=16/48"
+STEP_OPS = [("coarsen", 2), ("refine", 2), ("dilate", 1), ("conv_t_k3s2", 2)]
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2, help="workload id (2: B=16 shells at res 64)")
+    ap.add_argument("--roofline-kernel", default="k_enumerate")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--large", action="store_true", help="also time the 64-shell res-512 + cube batch")
+    return ap.parse_args()
+
+
+def run_step(binding, src, outs=None):
+    """One step: every op, each followed by the voxel enumeration. Returns voxels."""
+    total = 0
+    for op, f in STEP_OPS:
+        out = binding.tc_build_batched_topology(src, op, f)
+        ijk = binding.tc_enumerate_ijk(out)
+        total += ijk.shape[0]
+        if outs is not None:
+            outs.append((op, f, out.leaf_count, int(ijk.shape[0])))
+    return total
+
+
+def kernel_bytes(name, leaves, voxels):
+    """Algorithmic bytes of one launch of the reported kernel.
+
+    k_enumerate reads per leaf its origin (16 B), mask (64 B), voxel offset
+    (8 B) and grid header voxel base (8 B), and writes 12 B per voxel.
+    """
+    if name == "k_enumerate":
+        return 96 * leaves + 12 * voxels
+    raise ValueError(name)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1"}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from topology_construction_amd import binding, synth
+
+    torch.cuda.set_device(0)
+    ijk, off = synth.make_config(args.config)
+    src = binding.tc_batch_from_ijk(torch.from_numpy(ijk).cuda(), off)
+    torch.cuda.synchronize()
+
+    # per-op launch facts for the roofline bytes
+    facts = []
+    run_step(binding, src, facts)
+    for _ in range(args.warmup):
+        run_step(binding, src)
+    torch.cuda.synchronize()
+
+    binding.tc_profile_enable(args.roofline_kernel)
+    t0 = time.perf_counter()
+    voxels = 0
+    for _ in range(args.steps):
+        voxels += run_step(binding, src)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    k_ms, k_n = binding.tc_profile_read()
+    binding.tc_profile_disable()
+    elapsed = t1 - t0
+    ms_step = elapsed * 1e3 / args.steps
+
+    # per-op breakdown (separate, untimed-by-the-step loop): pass and enumeration
+    ops = {}
+    for op, f in STEP_OPS:
+        pass_ms, enum_ms = [], []
+        for _ in range(20):
+            torch.cuda.synchronize()
+            a = time.perf_counter()
+            out = binding.tc_build_batched_topology(src, op, f)
+            torch.cuda.synchronize()
+            b = time.perf_counter()
+            ijk_out = binding.tc_enumerate_ijk(out)
+            torch.cuda.synchronize()
+            c = time.perf_counter()
+            pass_ms.append((b - a) * 1e3)
+            enum_ms.append((c - b) * 1e3)
+        ops[f"{op}x{f}"] = {"ms_pass_median": float(np.median(pass_ms)),
+                            "ms_enumerate_median": float(np.median(enum_ms)),
+                            "output_voxels": int(ijk_out.shape[0]), "output_leaves": int(out.leaf_count)}
+
+    bytes_per_step = sum(kernel_bytes(args.roofline_kernel, L, V) for (_, _, L, V) in facts)
+    launches_per_step = len(facts)
+    avg_ms = k_ms / max(k_n, 1)
+    avg_bytes = bytes_per_step / launches_per_step
+    achieved = avg_bytes / (avg_ms * 1e-3) / 1e9 if k_n else None
+    roofline = {"bound": "hbm", "kernel": args.roofline_kernel, "achieved": achieved, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": (achieved / HBM_PEAK_GBS) if achieved else None, "traffic": None,
+                "avg_launch_ms": avg_ms, "launches": k_n, "algorithmic_bytes_per_launch": avg_bytes}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        t = time.perf_counter()
+        cv = 0
+        for op, f in STEP_OPS:
+            r = oracle.run(op, f, ijk, off, fields=["headers"])
+            cv += int(r["headers"][:, 8].sum())
+        dt = time.perf_counter() - t
+        cpu = {"value": cv / dt, "unit": "voxels/s", "cores": 1, "kind": "oracle",
+               "sample": f"one full step of workload {args.config} (all members, {len(STEP_OPS)} ops), {dt:.1f} s"}
+
+    rec = {
+        "metric": METRIC, "value": voxels / elapsed, "unit": "voxels/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int32", "data": "synthetic",
+        "config": {"workload": synth.CONFIG_NAMES[args.config], "grids": int(len(off) - 1),
+                   "input_voxels": int(off[-1]), "ops": [f"{o}x{f}" for o, f in STEP_OPS]},
+        "roofline": roofline, "cpu_baseline": cpu, "ops": ops,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

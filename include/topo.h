@@ -1,0 +1,218 @@
+/*
+ * topo.h -- C ABI of the batched generated-topology library for MI355X (gfx950).
+ *
+ * The library builds, for a batch of B sparse voxel grids at once, the topology
+ * of a generated grid: coarsen by 2/4/8, refine by 2/4/8, box-dilate [-1,1]^3,
+ * pad {-1,0}^3 or {0,1}^3, and the k3s2 transposed-conv target (refine by 2 then
+ * pad {-1,0}^3). Each grid is a three-level tree of 8^3 leaves (512-bit active
+ * masks), 16^3-leaf lower nodes, 32^3-lower upper nodes and one root tile per
+ * upper node, stored in the canonical x-major tree order. One pass runs over all
+ * source leaves of all members, with one host readback of node counts.
+ *
+ * Source of the operations and outputs: the fvdb-core pages
+ *   - "Generated-topology grid construction dominates per-iteration
+ *     ConvolutionPlan cost" (issue page): Summary, Root cause, Suggested direction;
+ *   - "Batched leaf-mask topology construction for generated conv grids"
+ *     (PR page): section 1 (one emission pass, canonical order, dedup, one
+ *     readback, batched writers, empty members, multi-pass factors 4 and 8),
+ *     section 2 (box-dilate passes, pads, k3s2 transpose), Test plan.
+ *
+ * Conventions (all entry points):
+ *   - Pointers named d_* are HIP device pointers; h_* are host pointers.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream). All device
+ *     work is enqueued on it; device outputs become valid in stream order.
+ *   - Every entry point validates its arguments on the host before any launch.
+ *     On any non-TC_OK status, *out is set to NULL, nothing is leaked and
+ *     tc_last_error() returns a message for the calling thread.
+ *   - Calls on different streams or threads are independent. A tc_grid_batch is
+ *     immutable after creation and may be read concurrently.
+ *   - Coordinates are int32 voxel indices; counts are int32 (nodes) or int64
+ *     (voxels).
+ */
+#ifndef TOPO_H
+#define TOPO_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TC_ABI_VERSION 1
+
+typedef enum tc_status {
+  TC_OK = 0,
+  TC_ERR_INVALID_ARG = 1,  /* bad pointer, op, factor, B < 1, bad offsets, capacity */
+  TC_ERR_OVERFLOW = 2,     /* an output voxel coordinate would leave int32 */
+  TC_ERR_ALLOC = 3,        /* the allocator (or the HIP pool) returned no memory */
+  TC_ERR_HIP = 4,          /* a HIP runtime call failed; message has the HIP error */
+  TC_ERR_UNSUPPORTED = 5,  /* e.g. a factor that is not a power of two */
+  TC_ERR_INTERNAL = 6      /* a device-side consistency check failed */
+} tc_status;
+
+/* Operations (PR page sections 1 and 2).
+ *   TC_OP_COARSEN     factor 2, 4 or 8: { floor(v / f) }         (conv_grid k2s2 for f = 2)
+ *   TC_OP_REFINE      factor 2, 4 or 8: { f*v + d, d in [0,f)^3 } (conv_transpose_grid k2s2)
+ *   TC_OP_DILATE      factor 1: Minkowski sum with [-1,1]^3       (conv_grid k3s1)
+ *   TC_OP_PAD_NEG     factor 1: Minkowski sum with {-1,0}^3
+ *   TC_OP_PAD_POS     factor 1: Minkowski sum with {0,1}^3
+ *   TC_OP_CONV_T_K3S2 factor 2: refine by 2, then TC_OP_PAD_NEG   (conv_transpose_grid k3s2)
+ * Factors 4 and 8 (and k3s2) run chained x2 passes, each with its own readback.
+ * Coarsening rounds toward minus infinity. */
+typedef enum tc_op {
+  TC_OP_COARSEN = 1,
+  TC_OP_REFINE = 2,
+  TC_OP_DILATE = 3,
+  TC_OP_PAD_NEG = 4,
+  TC_OP_PAD_POS = 5,
+  TC_OP_CONV_T_K3S2 = 6
+} tc_op;
+
+/* Caller-supplied device allocator for output grid buffers (one allocation per
+ * output batch). `alloc` returns a device pointer usable on `stream`, aligned to
+ * at least 256 bytes, or NULL on failure. `free` receives the same pointer and
+ * byte count. Both may be called from the thread that calls into the library.
+ * Passing a NULL tc_allocator* makes the library use hipMallocAsync/hipFreeAsync
+ * on the call's stream. Scratch memory always comes from hipMallocAsync on the
+ * call's stream and is released, stream-ordered, before the call returns. */
+typedef struct tc_allocator {
+  void* (*alloc)(void* ctx, size_t bytes, void* stream);
+  void (*free)(void* ctx, void* ptr, size_t bytes, void* stream);
+  void* ctx;
+} tc_allocator;
+
+typedef struct tc_grid_batch tc_grid_batch; /* opaque, owned by the caller */
+
+/* Per-grid header (PR page section 1: every grid gets mGridIndex = g,
+ * mGridCount = B, its node counts and its bbox). 80 bytes, device resident. */
+typedef struct tc_grid_header {
+  int32_t grid_index;   /* g */
+  int32_t grid_count;   /* B */
+  int32_t upper_count;  /* upper nodes (= root tiles) of this grid */
+  int32_t lower_count;
+  int32_t leaf_count;
+  int32_t upper_begin;  /* batch-global index of the grid's first upper node */
+  int32_t lower_begin;
+  int32_t leaf_begin;
+  int64_t voxel_count;
+  int64_t voxel_begin;  /* batch-global index of the grid's first voxel */
+  int32_t bbox_min[3];  /* inclusive index-space bbox of active voxels; an empty */
+  int32_t bbox_max[3];  /* grid has min = INT32_MAX and max = INT32_MIN */
+  int32_t reserved[2];
+} tc_grid_header;
+
+/* Device arrays of a batch, all inside one allocation (`buffer`), in canonical
+ * order: grids in order; inside a grid root tiles by signed x-major tile
+ * coordinate, then x-major child offsets. Layouts:
+ *   upper_origin int32[N2][4]  x, y, z (multiple of 4096), grid
+ *   upper_key    uint64[N2]    (Tx+2^19)<<40 | (Ty+2^19)<<20 | (Tz+2^19), T = origin/4096
+ *   upper_first  int32[N2]     index of the first child lower node
+ *   upper_mask   uint64[N2][512] child bit (x*32+y)*32+z of the lower inside the upper
+ *   lower_origin int32[N1][4]  x, y, z (multiple of 128), parent upper index
+ *   lower_first  int32[N1]     index of the first child leaf
+ *   lower_mask   uint64[N1][64]  child bit (x*16+y)*16+z of the leaf inside the lower
+ *   lower_prefix uint16[N1][64]  active children in words < w
+ *   leaf_origin  int32[L][4]   x, y, z (multiple of 8), grid
+ *   leaf_parent  int32[L]      parent lower index
+ *   leaf_mask    uint64[L][8]  voxel bit n = x*64 + y*8 + z (word x, bit y*8+z)
+ *   leaf_prefix  uint64[L]     seven 9-bit fields; field w-1 = voxels in words < w
+ *   leaf_offset  int64[L]      0-based index of the leaf's first voxel in its grid
+ * Node indices are batch-global. */
+typedef struct tc_batch_info {
+  int32_t grid_count;
+  int32_t upper_count;
+  int32_t lower_count;
+  int32_t leaf_count;
+  const int32_t* h_upper_counts; /* [B], host, valid for the batch's lifetime */
+  const int32_t* h_lower_counts;
+  const int32_t* h_leaf_counts;
+  const void* d_buffer;
+  size_t buffer_bytes;
+  const tc_grid_header* d_headers;
+  const int32_t* d_upper_origin;
+  const uint64_t* d_upper_key;
+  const int32_t* d_upper_first;
+  const uint64_t* d_upper_mask;
+  const int32_t* d_lower_origin;
+  const int32_t* d_lower_first;
+  const uint64_t* d_lower_mask;
+  const uint16_t* d_lower_prefix;
+  const int32_t* d_leaf_origin;
+  const int32_t* d_leaf_parent;
+  const uint64_t* d_leaf_mask;
+  const uint64_t* d_leaf_prefix;
+  const int64_t* d_leaf_offset;
+} tc_batch_info;
+
+/* Library version of this header; a caller checks it equals TC_ABI_VERSION. */
+int32_t tc_abi_version(void);
+
+/* Static text for a status code. */
+const char* tc_status_string(tc_status status);
+
+/* Message describing the calling thread's most recent non-TC_OK status. */
+const char* tc_last_error(void);
+
+/* Builds a batch of B grids from int32 voxel rows (the ijk front-end; PR page,
+ * Measurements: follow-up ijk emission front-end, and Test plan: expected
+ * topologies built from ijk).
+ *   d_ijk      int32[N][3] device, N = h_offsets[B]; may be NULL when N = 0.
+ *   h_offsets  int64[B+1] host: member g owns rows [h_offsets[g], h_offsets[g+1]);
+ *              h_offsets[0] = 0, non-decreasing, N < 2^31.
+ *   Duplicate rows collapse; row order is irrelevant.
+ * Blocks on a few small readbacks. *out is owned by the caller. */
+tc_status tc_batch_from_ijk(const int32_t* d_ijk, const int64_t* h_offsets, int32_t grid_count,
+                            const tc_allocator* allocator, void* stream, tc_grid_batch** out);
+
+/* One batched pass (or a chain of passes) over every member of `src`
+ * (PR page section 1: emission, sorts, dedup, single readback, one allocation,
+ * writers; section 2: box-dilate and pads; factors 4, 8 and k3s2 chain passes).
+ *   op      a tc_op; factor as documented at tc_op.
+ * `src` is borrowed and never modified. Blocks exactly once per pass, on the
+ * readback of per-grid node counts; on return the host counts in
+ * tc_batch_info are valid and device arrays are valid in stream order.
+ * Returns TC_ERR_OVERFLOW (and no batch) when any output voxel would leave int32,
+ * TC_ERR_UNSUPPORTED for a non-power-of-two refine/coarsen factor. */
+tc_status tc_build_batched_topology(const tc_grid_batch* src, int32_t op, int32_t factor,
+                                    const tc_allocator* allocator, void* stream,
+                                    tc_grid_batch** out);
+
+/* Counts (host) and device array pointers of a batch. Never blocks. */
+tc_status tc_batch_get_info(const tc_grid_batch* batch, tc_batch_info* out);
+
+/* Copies the B headers to host memory h_out (tc_grid_header[B]); this blocks on
+ * `stream` (one small readback). Voxel counts and bboxes live only on the device
+ * until this is called. */
+tc_status tc_batch_read_headers(const tc_grid_batch* batch, tc_grid_header* h_out, void* stream);
+
+/* Total voxel count of the batch (blocks like tc_batch_read_headers the first
+ * time; cached afterwards). */
+tc_status tc_batch_voxel_total(const tc_grid_batch* batch, int64_t* h_total, void* stream);
+
+/* Writes the jagged voxel enumeration: d_ijk_out int32[V][3] device, V = voxel
+ * total, grid after grid, each grid in canonical order (test plan: ijk.jdata);
+ * member g's rows start at headers[g].voxel_begin. `capacity` is the row capacity
+ * of d_ijk_out; fewer than V rows is TC_ERR_INVALID_ARG. Enqueues one kernel
+ * (after a voxel-total readback the first time). */
+tc_status tc_enumerate_ijk(const tc_grid_batch* batch, int32_t* d_ijk_out, int64_t capacity,
+                           void* stream);
+
+/* Releases the batch's device buffer (through the allocator it was created with,
+ * stream-ordered on its creation stream) and the handle. NULL is ignored. */
+void tc_batch_free(tc_grid_batch* batch);
+
+/* Kernel timing for measurement: while enabled, every launch of the kernel whose
+ * name equals `kernel_name` is bracketed by HIP events on its stream.
+ * tc_profile_read() waits for those events and returns the summed milliseconds
+ * and launch count since tc_profile_enable(). Names are the __global__ function
+ * names (e.g. "k_leaf_gather"). Not thread-safe against concurrent passes. */
+tc_status tc_profile_enable(const char* kernel_name);
+tc_status tc_profile_read(double* h_total_ms, int64_t* h_launches);
+tc_status tc_profile_disable(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TOPO_H */

@@ -1,0 +1,293 @@
+// C ABI entry points (declared in include/topo.h): argument validation on the
+// host, pass chaining for factors 4/8 and k3s2 transpose, batch ownership and
+// error reporting. No exception crosses the boundary.
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "internal.hpp"
+
+namespace {
+
+thread_local std::string t_last_error;
+
+tc_status fail(tc_status s, const std::string& msg) {
+  t_last_error = msg;
+  return s;
+}
+
+template <typename F>
+tc_status guarded(F&& f) {
+  try {
+    return f();
+  } catch (const tc::Error& e) {
+    return fail(e.status, e.what());
+  } catch (const std::bad_alloc&) {
+    return fail(TC_ERR_ALLOC, "host allocation failed");
+  } catch (const std::exception& e) {
+    return fail(TC_ERR_INTERNAL, e.what());
+  }
+}
+
+int current_device() {
+  int d = 0;
+  tc::hip_check(hipGetDevice(&d), "hipGetDevice");
+  return d;
+}
+
+}  // namespace
+
+namespace tc {
+
+tc_grid_batch* new_batch(int32_t B, const int32_t* rb, const OutAlloc& oa) {
+  tc_grid_batch* b = new tc_grid_batch();
+  try {
+    b->B = B;
+    b->n2 = rb[1];
+    b->n1 = rb[2];
+    b->nl = rb[3];
+    b->h_upper.resize(B);
+    b->h_lower.resize(B);
+    b->h_leaf.resize(B);
+    for (int32_t g = 0; g < B; ++g) {
+      b->h_upper[g] = rb[4 + 3 * g];
+      b->h_lower[g] = rb[4 + 3 * g + 1];
+      b->h_leaf[g] = rb[4 + 3 * g + 2];
+    }
+    b->layout = make_layout(B, b->n2, b->n1, b->nl);
+    b->bytes = b->layout.total;
+    b->stream = oa.stream;
+    b->device = current_device();
+    if (oa.alloc) {
+      b->has_alloc = true;
+      b->alloc = *oa.alloc;
+      b->buffer = b->alloc.alloc(b->alloc.ctx, b->bytes, (void*)oa.stream);
+      if (!b->buffer) throw Error(TC_ERR_ALLOC, "allocator returned NULL for " + std::to_string(b->bytes) + " bytes");
+    } else {
+      b->buffer = device_alloc_async(b->bytes, oa.stream);
+    }
+  } catch (...) {
+    delete b;
+    throw;
+  }
+  return b;
+}
+
+void free_batch(tc_grid_batch* b) {
+  if (!b) return;
+  if (b->buffer) {
+    if (b->has_alloc) {
+      if (b->alloc.free) b->alloc.free(b->alloc.ctx, b->buffer, b->bytes, (void*)b->stream);
+    } else {
+      device_free_async(b->buffer, b->stream);
+    }
+  }
+  delete b;
+}
+
+static i64 read_voxel_total(const tc_grid_batch* b, hipStream_t s) {
+  if (b->vox_known) return b->vox_total;
+  tc_grid_header* h = static_cast<tc_grid_header*>(pinned_staging(sizeof(tc_grid_header)));
+  const GridView v = b->view();
+  hip_check(hipMemcpyAsync(h, v.headers + (b->B - 1), sizeof(tc_grid_header), hipMemcpyDeviceToHost, s),
+            "header readback");
+  hip_check(hipStreamSynchronize(s), "hipStreamSynchronize");
+  b->vox_total = h->voxel_begin + h->voxel_count;
+  b->vox_known = true;
+  return b->vox_total;
+}
+
+}  // namespace tc
+
+extern "C" {
+
+int32_t tc_abi_version(void) { return TC_ABI_VERSION; }
+
+const char* tc_status_string(tc_status s) {
+  switch (s) {
+    case TC_OK: return "ok";
+    case TC_ERR_INVALID_ARG: return "invalid argument";
+    case TC_ERR_OVERFLOW: return "int32 coordinate overflow";
+    case TC_ERR_ALLOC: return "allocation failed";
+    case TC_ERR_HIP: return "HIP runtime error";
+    case TC_ERR_UNSUPPORTED: return "unsupported";
+    case TC_ERR_INTERNAL: return "internal error";
+    default: return "unknown status";
+  }
+}
+
+const char* tc_last_error(void) { return t_last_error.c_str(); }
+
+tc_status tc_batch_from_ijk(const int32_t* d_ijk, const int64_t* h_offsets, int32_t grid_count,
+                            const tc_allocator* allocator, void* stream, tc_grid_batch** out) {
+  if (!out) return fail(TC_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (grid_count < 1) return fail(TC_ERR_INVALID_ARG, "grid_count must be >= 1");
+  if (!h_offsets) return fail(TC_ERR_INVALID_ARG, "h_offsets is NULL");
+  if (h_offsets[0] != 0) return fail(TC_ERR_INVALID_ARG, "h_offsets[0] must be 0");
+  for (int32_t g = 0; g < grid_count; ++g)
+    if (h_offsets[g + 1] < h_offsets[g]) return fail(TC_ERR_INVALID_ARG, "h_offsets must be non-decreasing");
+  const int64_t n = h_offsets[grid_count];
+  if (n >= (1ll << 30)) return fail(TC_ERR_UNSUPPORTED, "more than 2^30 voxel rows");
+  if (n > 0 && !d_ijk) return fail(TC_ERR_INVALID_ARG, "d_ijk is NULL");
+  if (allocator && (!allocator->alloc || !allocator->free))
+    return fail(TC_ERR_INVALID_ARG, "allocator callbacks are NULL");
+  return guarded([&]() {
+    *out = tc::build_from_ijk(d_ijk, h_offsets, grid_count, tc::OutAlloc{allocator, (hipStream_t)stream});
+    return TC_OK;
+  });
+}
+
+tc_status tc_build_batched_topology(const tc_grid_batch* src, int32_t op, int32_t factor,
+                                    const tc_allocator* allocator, void* stream, tc_grid_batch** out) {
+  if (!out) return fail(TC_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (!src) return fail(TC_ERR_INVALID_ARG, "src is NULL");
+  if (allocator && (!allocator->alloc || !allocator->free))
+    return fail(TC_ERR_INVALID_ARG, "allocator callbacks are NULL");
+  std::vector<int> passes;
+  switch (op) {
+    case TC_OP_COARSEN:
+    case TC_OP_REFINE: {
+      if (factor < 2) return fail(TC_ERR_INVALID_ARG, "refine/coarsen factor must be >= 2");
+      if (factor != 2 && factor != 4 && factor != 8)
+        return fail(TC_ERR_UNSUPPORTED, "refine/coarsen factor must be 2, 4 or 8");
+      for (int f = factor; f > 1; f >>= 1) passes.push_back(op);
+      break;
+    }
+    case TC_OP_DILATE:
+    case TC_OP_PAD_NEG:
+    case TC_OP_PAD_POS:
+      if (factor != 1) return fail(TC_ERR_INVALID_ARG, "box ops take factor 1");
+      passes.push_back(op);
+      break;
+    case TC_OP_CONV_T_K3S2:
+      if (factor != 2) return fail(TC_ERR_INVALID_ARG, "k3s2 transpose takes factor 2");
+      passes.push_back(TC_OP_REFINE);
+      passes.push_back(TC_OP_PAD_NEG);
+      break;
+    default:
+      return fail(TC_ERR_INVALID_ARG, "unknown op " + std::to_string(op));
+  }
+  return guarded([&]() {
+    if (current_device() != src->device) throw tc::Error(TC_ERR_INVALID_ARG, "src lives on another device");
+    hipStream_t s = (hipStream_t)stream;
+    const tc_grid_batch* cur = src;
+    tc_grid_batch* owned = nullptr;  // intermediate result of the previous pass
+    try {
+      for (size_t p = 0; p < passes.size(); ++p) {
+        const bool last = p + 1 == passes.size();
+        tc_grid_batch* next = tc::build_pass(cur, passes[p], tc::OutAlloc{last ? allocator : nullptr, s});
+        tc::free_batch(owned);
+        owned = next;
+        cur = next;
+      }
+    } catch (...) {
+      tc::free_batch(owned);
+      throw;
+    }
+    *out = owned;
+    return TC_OK;
+  });
+}
+
+tc_status tc_batch_get_info(const tc_grid_batch* b, tc_batch_info* out) {
+  if (!b || !out) return fail(TC_ERR_INVALID_ARG, "NULL argument");
+  const tc::GridView v = b->view();
+  out->grid_count = b->B;
+  out->upper_count = b->n2;
+  out->lower_count = b->n1;
+  out->leaf_count = b->nl;
+  out->h_upper_counts = b->h_upper.data();
+  out->h_lower_counts = b->h_lower.data();
+  out->h_leaf_counts = b->h_leaf.data();
+  out->d_buffer = b->buffer;
+  out->buffer_bytes = b->bytes;
+  out->d_headers = v.headers;
+  out->d_upper_origin = reinterpret_cast<const int32_t*>(v.upper_origin);
+  out->d_upper_key = v.upper_key;
+  out->d_upper_first = v.upper_first;
+  out->d_upper_mask = v.upper_mask;
+  out->d_lower_origin = reinterpret_cast<const int32_t*>(v.lower_origin);
+  out->d_lower_first = v.lower_first;
+  out->d_lower_mask = v.lower_mask;
+  out->d_lower_prefix = v.lower_prefix;
+  out->d_leaf_origin = reinterpret_cast<const int32_t*>(v.leaf_origin);
+  out->d_leaf_parent = v.leaf_parent;
+  out->d_leaf_mask = v.leaf_mask;
+  out->d_leaf_prefix = v.leaf_prefix;
+  out->d_leaf_offset = v.leaf_offset;
+  return TC_OK;
+}
+
+tc_status tc_batch_read_headers(const tc_grid_batch* b, tc_grid_header* h_out, void* stream) {
+  if (!b || !h_out) return fail(TC_ERR_INVALID_ARG, "NULL argument");
+  return guarded([&]() {
+    const size_t bytes = sizeof(tc_grid_header) * (size_t)b->B;
+    void* h = tc::pinned_staging(bytes);
+    hipStream_t s = (hipStream_t)stream;
+    tc::hip_check(hipMemcpyAsync(h, b->view().headers, bytes, hipMemcpyDeviceToHost, s), "header readback");
+    tc::hip_check(hipStreamSynchronize(s), "hipStreamSynchronize");
+    std::memcpy(h_out, h, bytes);
+    const tc_grid_header& last = h_out[b->B - 1];
+    b->vox_total = last.voxel_begin + last.voxel_count;
+    b->vox_known = true;
+    return TC_OK;
+  });
+}
+
+tc_status tc_batch_voxel_total(const tc_grid_batch* b, int64_t* h_total, void* stream) {
+  if (!b || !h_total) return fail(TC_ERR_INVALID_ARG, "NULL argument");
+  return guarded([&]() {
+    *h_total = tc::read_voxel_total(b, (hipStream_t)stream);
+    return TC_OK;
+  });
+}
+
+tc_status tc_enumerate_ijk(const tc_grid_batch* b, int32_t* d_ijk_out, int64_t capacity, void* stream) {
+  if (!b) return fail(TC_ERR_INVALID_ARG, "batch is NULL");
+  return guarded([&]() {
+    hipStream_t s = (hipStream_t)stream;
+    const int64_t total = tc::read_voxel_total(b, s);
+    if (total == 0) return TC_OK;
+    if (!d_ijk_out) throw tc::Error(TC_ERR_INVALID_ARG, "d_ijk_out is NULL");
+    if (capacity < total)
+      throw tc::Error(TC_ERR_INVALID_ARG, "capacity " + std::to_string(capacity) + " < voxel total " +
+                                              std::to_string(total));
+    tc::tree_enumerate(b->view(), d_ijk_out, s);
+    return TC_OK;
+  });
+}
+
+void tc_batch_free(tc_grid_batch* b) {
+  try {
+    tc::free_batch(b);
+  } catch (...) {
+  }
+}
+
+tc_status tc_profile_enable(const char* kernel_name) {
+  if (!kernel_name) return fail(TC_ERR_INVALID_ARG, "kernel_name is NULL");
+  return guarded([&]() {
+    tc::prof_enable(kernel_name);
+    return TC_OK;
+  });
+}
+
+tc_status tc_profile_read(double* h_total_ms, int64_t* h_launches) {
+  if (!h_total_ms || !h_launches) return fail(TC_ERR_INVALID_ARG, "NULL argument");
+  return guarded([&]() {
+    tc::prof_read(h_total_ms, h_launches);
+    return TC_OK;
+  });
+}
+
+tc_status tc_profile_disable(void) {
+  return guarded([&]() {
+    tc::prof_disable();
+    return TC_OK;
+  });
+}
+
+}  // extern "C"

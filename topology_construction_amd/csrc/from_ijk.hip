@@ -1,0 +1,327 @@
+// Grid batch from int32 voxel rows: the ijk emission front-end (PR page,
+// Measurements: the follow-up ijk front-end on the same back-end; Test plan:
+// expected topologies are built from ijk).
+//
+// Every voxel emits a single bit. Root tiles are deduplicated with an
+// open-addressing hash set (slots hold the index of a representative voxel), the
+// few unique tiles are sorted, and the rest reuses the bitmap-rank tree assembly
+// of the topology pass. Three small readbacks size the scratch arrays (unique
+// tiles, candidate lowers, node counts); the pass itself needs only one because
+// its bounds are known from the source batch.
+#include <cstring>
+
+#include "device.hpp"
+#include "internal.hpp"
+
+namespace tc {
+
+__global__ void __launch_bounds__(256) k_voxel_grid(const i64* offsets, int32_t B, i64 n, int32_t* vgrid) {
+  const i64 i = (i64)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  int32_t lo = 0, hi = B - 1;  // last g with offsets[g] <= i
+  while (lo < hi) {
+    const int32_t mid = lo + (hi - lo + 1) / 2;
+    if (offsets[mid] <= i) lo = mid;
+    else hi = mid - 1;
+  }
+  vgrid[i] = lo;
+}
+
+__device__ __forceinline__ u64 tile_hash(int32_t g, int32_t tx, int32_t ty, int32_t tz) {
+  u64 k = ((u64)(uint32_t)(tx + kTileBias) << 40) ^ ((u64)(uint32_t)(ty + kTileBias) << 20) ^
+          (u64)(uint32_t)(tz + kTileBias);
+  k ^= (u64)(uint32_t)g * 0x9e3779b97f4a7c15ull;
+  k ^= k >> 31;
+  k *= 0xbf58476d1ce4e5b9ull;
+  k ^= k >> 29;
+  k *= 0x94d049bb133111ebull;
+  k ^= k >> 32;
+  return k;
+}
+
+// table[H] holds -1 or the index of the first voxel seen for a (grid, tile).
+// Every probe sequence ends within H steps because fewer than H voxels exist.
+__global__ void __launch_bounds__(256) k_hash_tiles(const int32_t* ijk, const int32_t* vgrid, i64 n, int32_t* table,
+                                                    i64 H, int32_t* rep, int32_t* flags) {
+  const i64 i = (i64)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int32_t g = vgrid[i];
+  const int32_t tx = ijk[i * 3] >> 12, ty = ijk[i * 3 + 1] >> 12, tz = ijk[i * 3 + 2] >> 12;
+  i64 h = (i64)(tile_hash(g, tx, ty, tz) & (u64)(H - 1));
+  for (i64 probe = 0; probe < H; ++probe) {
+    int32_t e = __hip_atomic_load(&table[h], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (e < 0) {
+      const int32_t old = atomicCAS(&table[h], -1, (int32_t)i);
+      if (old < 0) {
+        rep[i] = (int32_t)i;
+        return;
+      }
+      e = old;
+    }
+    if (vgrid[e] == g && (ijk[(i64)e * 3] >> 12) == tx && (ijk[(i64)e * 3 + 1] >> 12) == ty &&
+        (ijk[(i64)e * 3 + 2] >> 12) == tz) {
+      rep[i] = e;
+      return;
+    }
+    h = (h + 1) & (H - 1);
+  }
+  rep[i] = (int32_t)i;
+  atomicOr(flags, 2);
+}
+
+__global__ void __launch_bounds__(256) k_rep_flags(const int32_t* rep, i64 n, int32_t* flag) {
+  const i64 i = (i64)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  flag[i] = rep[i] == i ? 1 : 0;
+}
+
+__global__ void __launch_bounds__(256) k_tile_compact(const int32_t* ijk, const int32_t* vgrid, const int32_t* flag,
+                                                      const int32_t* excl, i64 n, Key128* keys, uint32_t* vals) {
+  const i64 i = (i64)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n || !flag[i]) return;
+  const int32_t k = excl[i];
+  const u64 g = (uint32_t)vgrid[i];
+  const u64 tx = (u64)((ijk[i * 3] >> 12) + kTileBias), ty = (u64)((ijk[i * 3 + 1] >> 12) + kTileBias),
+            tz = (u64)((ijk[i * 3 + 2] >> 12) + kTileBias);
+  keys[k] = Key128{((g & 15ull) << 60) | (tx << 40) | (ty << 20) | tz, g >> 4};
+  vals[k] = (uint32_t)k;
+}
+
+__global__ void __launch_bounds__(256) k_tile_rank_scatter(const Key128* keys, const uint32_t* vals, i64 n,
+                                                           int32_t* rank_of, int4* utile) {
+  const i64 s = (i64)blockIdx.x * 256 + threadIdx.x;
+  if (s >= n) return;
+  const Key128 k = keys[s];
+  if ((i64)vals[s] >= n) return;  // consistency guard
+  rank_of[vals[s]] = (int32_t)s;
+  const int32_t g = (int32_t)((k.hi << 4) | (k.lo >> 60));
+  utile[s] = make_int4((int32_t)((k.lo >> 40) & 0xfffff) - kTileBias, (int32_t)((k.lo >> 20) & 0xfffff) - kTileBias,
+                       (int32_t)(k.lo & 0xfffff) - kTileBias, g);
+}
+
+__global__ void __launch_bounds__(256) k_voxel_tile(const int32_t* rep, const int32_t* excl, const int32_t* rank_of,
+                                                    i64 n, int32_t nt, int32_t* vtile, int32_t* flags) {
+  const i64 i = (i64)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int32_t r = rep[i];
+  const int32_t k = (r >= 0 && r < n) ? excl[r] : -1;
+  const int32_t t = (k >= 0 && k < nt) ? rank_of[k] : -1;
+  if (t < 0 || t >= nt) {
+    atomicOr(flags, 2);
+    vtile[i] = 0;
+    return;
+  }
+  vtile[i] = t;
+}
+
+__device__ __forceinline__ void or_if_clear(u64* word, u64 bit) {
+  if (!(__hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & bit))
+    atomicOr((unsigned long long*)word, bit);
+}
+
+__global__ void __launch_bounds__(256) k_voxel_mark_lower(const int32_t* ijk, const int32_t* vtile, i64 n,
+                                                          u64* tile_child) {
+  const i64 i = (i64)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const i64 t = vtile[i];
+  const int kx = (ijk[i * 3] >> 7) & 31, ky = (ijk[i * 3 + 1] >> 7) & 31, kz = (ijk[i * 3 + 2] >> 7) & 31;
+  const int bit = (kx * 32 + ky) * 32 + kz;
+  or_if_clear(&tile_child[t * 512 + (bit >> 6)], 1ull << (bit & 63));
+}
+
+__global__ void __launch_bounds__(256) k_voxel_cand(const int32_t* ijk, const int32_t* vtile, i64 n,
+                                                    const u64* tile_child, const uint16_t* tile_prefix,
+                                                    const int32_t* tile_lower_base, int32_t nc, int32_t* vcand,
+                                                    int4* cand_origin, u64* cand_child, int32_t* flags) {
+  const i64 i = (i64)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const i64 t = vtile[i];
+  const int32_t x = ijk[i * 3], y = ijk[i * 3 + 1], z = ijk[i * 3 + 2];
+  const int bit = (((x >> 7) & 31) * 32 + ((y >> 7) & 31)) * 32 + ((z >> 7) & 31);
+  const int w = bit >> 6, b = bit & 63;
+  const int32_t c = tile_lower_base[t] + tile_prefix[t * 512 + w] + popc64(tile_child[t * 512 + w] & ((1ull << b) - 1));
+  if (c < 0 || c >= nc) {
+    atomicOr(flags, 2);
+    vcand[i] = -1;
+    return;
+  }
+  vcand[i] = c;
+  cand_origin[c] = make_int4((x >> 7) * 128, (y >> 7) * 128, (z >> 7) * 128, (int32_t)t);
+  const int lb = (((x >> 3) & 15) * 16 + ((y >> 3) & 15)) * 16 + ((z >> 3) & 15);
+  or_if_clear(&cand_child[(i64)c * 64 + (lb >> 6)], 1ull << (lb & 63));
+}
+
+__global__ void __launch_bounds__(256) k_voxel_leaf(const int32_t* ijk, const int32_t* vcand, i64 n,
+                                                    const u64* cand_child, const uint16_t* cand_prefix,
+                                                    const int32_t* leaf_base, i64 n_leaf, u64* leaf_mask) {
+  const i64 i = (i64)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const i64 c = vcand[i];
+  if (c < 0) return;
+  const int32_t x = ijk[i * 3], y = ijk[i * 3 + 1], z = ijk[i * 3 + 2];
+  const int lb = (((x >> 3) & 15) * 16 + ((y >> 3) & 15)) * 16 + ((z >> 3) & 15);
+  const int w = lb >> 6, b = lb & 63;
+  const i64 leaf = leaf_base[c] + cand_prefix[c * 64 + w] + popc64(cand_child[c * 64 + w] & ((1ull << b) - 1));
+  if (leaf < 0 || leaf >= n_leaf) return;  // consistency guard
+  atomicOr((unsigned long long*)&leaf_mask[leaf * 8 + (x & 7)], 1ull << ((y & 7) * 8 + (z & 7)));
+}
+
+static int32_t read_i32(const int32_t* d, hipStream_t s) {
+  int32_t* h = static_cast<int32_t*>(pinned_staging(64));
+  hip_check(hipMemcpyAsync(h, d, 4, hipMemcpyDeviceToHost, s), "readback");
+  hip_check(hipStreamSynchronize(s), "hipStreamSynchronize");
+  return h[0];
+}
+
+tc_grid_batch* build_from_ijk(const int32_t* d_ijk, const int64_t* h_off, int32_t B, const OutAlloc& oa) {
+  hipStream_t s = oa.stream;
+  const i64 N = h_off[B];
+  i64 H = 1024;
+  while (H < 2 * N) H <<= 1;
+
+  // stage 1: voxel -> grid, tile representatives, unique tiles
+  Arena a1(s);
+  const size_t o_off = a1.reserve(8 * ((i64)B + 1));
+  const size_t o_vg = a1.reserve(4 * N);
+  const size_t o_tab = a1.reserve(4 * H);
+  const size_t o_rep = a1.reserve(4 * N);
+  const size_t o_flag = a1.reserve(4 * N);
+  const size_t o_excl = a1.reserve(4 * (N + 1));
+  const size_t o_vt = a1.reserve(4 * N);
+  const size_t o_vc = a1.reserve(4 * N);
+  const size_t o_rb = a1.reserve(4 * 4);
+  a1.commit();
+  i64* d_off = a1.at<i64>(o_off);
+  int32_t* vgrid = a1.at<int32_t>(o_vg);
+  int32_t* table = a1.at<int32_t>(o_tab);
+  int32_t* rep = a1.at<int32_t>(o_rep);
+  int32_t* flag = a1.at<int32_t>(o_flag);
+  int32_t* excl = a1.at<int32_t>(o_excl);
+  int32_t* vtile = a1.at<int32_t>(o_vt);
+  int32_t* vcand = a1.at<int32_t>(o_vc);
+  int32_t* flags = a1.at<int32_t>(o_rb);
+
+  const size_t off_bytes = 8 * ((size_t)B + 1);
+  void* h_stage = pinned_staging(off_bytes + 64);
+  std::memcpy(h_stage, h_off, off_bytes);
+  hip_check(hipMemcpyAsync(d_off, h_stage, off_bytes, hipMemcpyHostToDevice, s), "offsets upload");
+  fill_i32(flags, 0, 1, nullptr, 1, s);
+  fill_i32(table, -1, H, nullptr, 1, s);
+  launch("k_voxel_grid", k_voxel_grid, ceil_div(N, 256), 256, s, (const i64*)d_off, B, N, vgrid);
+  launch("k_hash_tiles", k_hash_tiles, ceil_div(N, 256), 256, s, d_ijk, (const int32_t*)vgrid, N, table, H, rep,
+         flags);
+  launch("k_rep_flags", k_rep_flags, ceil_div(N, 256), 256, s, (const int32_t*)rep, N, flag);
+  scan_excl_i32(flag, excl, N, nullptr, s);
+  hip_check(hipStreamSynchronize(s), "hipStreamSynchronize");  // the pinned offsets are consumed
+  const int32_t nt = read_i32(excl + N, s);
+  if (read_i32(flags, s) & 2) throw Error(TC_ERR_INTERNAL, "from_ijk: tile hash overflow");
+
+  // stage 2: sort the unique tiles, candidate lowers
+  Arena a2(s);
+  const size_t o_keys = a2.reserve(sizeof(Key128) * nt);
+  const size_t o_vals = a2.reserve(4 * (i64)nt);
+  const size_t o_rank = a2.reserve(4 * (i64)nt);
+  const size_t o_ntiles = a2.reserve(4);
+  const size_t o_ncand = a2.reserve(4);
+  const size_t o_utile = a2.reserve(16 * (i64)nt);
+  const size_t o_tchild = a2.reserve(4096 * (i64)nt);
+  const size_t o_tpre = a2.reserve(1024 * (i64)nt);
+  const size_t o_tlc = a2.reserve(4 * (i64)nt);
+  const size_t o_tlb = a2.reserve(4 * ((i64)nt + 1));
+  const size_t o_tne = a2.reserve(4 * (i64)nt);
+  const size_t o_uex = a2.reserve(4 * ((i64)nt + 1));
+  const size_t o_gtb = a2.reserve(4 * ((i64)B + 1));
+  a2.commit();
+  TreeScratch ts{};
+  ts.cap_tiles = nt;
+  ts.d_num_tiles = a2.at<int32_t>(o_ntiles);
+  ts.d_num_cands = a2.at<int32_t>(o_ncand);
+  ts.utile = a2.at<int4>(o_utile);
+  ts.tile_child = a2.at<u64>(o_tchild);
+  ts.tile_prefix = a2.at<uint16_t>(o_tpre);
+  ts.tile_lower_count = a2.at<int32_t>(o_tlc);
+  ts.tile_lower_base = a2.at<int32_t>(o_tlb);
+  ts.tile_nonempty = a2.at<int32_t>(o_tne);
+  ts.upper_excl = a2.at<int32_t>(o_uex);
+  ts.grid_tile_begin = a2.at<int32_t>(o_gtb);
+  Key128* keys = a2.at<Key128>(o_keys);
+  uint32_t* vals = a2.at<uint32_t>(o_vals);
+  int32_t* rank_of = a2.at<int32_t>(o_rank);
+
+  fill_i32(ts.d_num_tiles, nt, 1, nullptr, 1, s);
+  launch("k_tile_compact", k_tile_compact, ceil_div(N, 256), 256, s, d_ijk, (const int32_t*)vgrid,
+         (const int32_t*)flag, (const int32_t*)excl, N, keys, vals);
+  sort_pairs_128(keys, vals, nt, tile_key_bits(B), s);
+  launch("k_tile_rank_scatter", k_tile_rank_scatter, ceil_div(nt, 256), 256, s, (const Key128*)keys,
+         (const uint32_t*)vals, (i64)nt, rank_of, ts.utile);
+  launch("k_voxel_tile", k_voxel_tile, ceil_div(N, 256), 256, s, (const int32_t*)rep, (const int32_t*)excl,
+         (const int32_t*)rank_of, N, nt, vtile, flags);
+  tree_tile_ranges(ts, B, s);
+  fill_u64(ts.tile_child, 0, 512 * (i64)nt, nullptr, 1, s);
+  launch("k_voxel_mark_lower", k_voxel_mark_lower, ceil_div(N, 256), 256, s, d_ijk, (const int32_t*)vtile, N,
+         ts.tile_child);
+  tree_rank_tiles(ts, s);
+  const int32_t nc = read_i32(ts.d_num_cands, s);
+  if (read_i32(flags, s) & 2) throw Error(TC_ERR_INTERNAL, "from_ijk: tile ranking check failed");
+
+  // stage 3: candidate lowers, leaves, counts
+  Arena a3(s);
+  const size_t o_corig = a3.reserve(16 * (i64)nc);
+  const size_t o_cchild = a3.reserve(512 * (i64)nc);
+  const size_t o_cpre = a3.reserve(128 * (i64)nc);
+  const size_t o_clc = a3.reserve(4 * (i64)nc);
+  const size_t o_cne = a3.reserve(4 * (i64)nc);
+  const size_t o_lb = a3.reserve(4 * ((i64)nc + 1));
+  const size_t o_lex = a3.reserve(4 * ((i64)nc + 1));
+  const size_t o_ginfo = a3.reserve(4 * 6 * (i64)B);
+  const size_t o_rb3 = a3.reserve(4 * (4 + 3 * (i64)B));
+  a3.commit();
+  ts.cap_cands = nc;
+  ts.cand_origin = a3.at<int4>(o_corig);
+  ts.cand_child = a3.at<u64>(o_cchild);
+  ts.cand_prefix = a3.at<uint16_t>(o_cpre);
+  ts.cand_leaf_count = a3.at<int32_t>(o_clc);
+  ts.cand_nonempty = a3.at<int32_t>(o_cne);
+  ts.leaf_base = a3.at<int32_t>(o_lb);
+  ts.lower_excl = a3.at<int32_t>(o_lex);
+  ts.grid_info = a3.at<int32_t>(o_ginfo);
+  ts.readback = a3.at<int32_t>(o_rb3);
+  ts.flags = ts.readback;
+  fill_i32(ts.readback, 0, 1, nullptr, 1, s);
+  fill_u64(ts.cand_child, 0, 64 * (i64)nc, nullptr, 1, s);
+  launch("k_voxel_cand", k_voxel_cand, ceil_div(N, 256), 256, s, d_ijk, (const int32_t*)vtile, N,
+         (const u64*)ts.tile_child, (const uint16_t*)ts.tile_prefix, (const int32_t*)ts.tile_lower_base, nc, vcand,
+         ts.cand_origin, ts.cand_child, ts.flags);
+  tree_count_cands(ts, s);
+  tree_grid_counts(ts, B, s);
+  const size_t rb_bytes = 4 * (4 + 3 * (size_t)B);
+  int32_t* h_rb = static_cast<int32_t*>(pinned_staging(rb_bytes));
+  hip_check(hipMemcpyAsync(h_rb, ts.readback, rb_bytes, hipMemcpyDeviceToHost, s), "readback");
+  hip_check(hipStreamSynchronize(s), "hipStreamSynchronize");
+  if (h_rb[0] != 0) throw Error(TC_ERR_INTERNAL, "from_ijk: device consistency check failed");
+
+  tc_grid_batch* out = new_batch(B, h_rb, oa);
+  try {
+    const GridView ov = out->view();
+    const i64 L = out->nl;
+    Arena post(s);
+    const size_t o_lc = post.reserve(4 * L);
+    const size_t o_lv = post.reserve(8 * L);
+    const size_t o_vx = post.reserve(8 * (L + 1));
+    const size_t o_bb = post.reserve(4 * 6 * (i64)B);
+    post.commit();
+    tree_write_nodes(ts, ov, post.at<int32_t>(o_lc), s);
+    fill_u64(ov.leaf_mask, 0, 8 * L, nullptr, 1, s);
+    launch("k_voxel_leaf", k_voxel_leaf, ceil_div(N, 256), 256, s, d_ijk, (const int32_t*)vcand, N,
+           (const u64*)ts.cand_child, (const uint16_t*)ts.cand_prefix, (const int32_t*)ts.leaf_base, L,
+           ov.leaf_mask);
+    tree_finalize_leaves(ov, post.at<i64>(o_lv), post.at<i64>(o_vx), post.at<int32_t>(o_bb),
+                         (const int32_t*)ts.grid_info, s);
+  } catch (...) {
+    free_batch(out);
+    throw;
+  }
+  return out;
+}
+
+}  // namespace tc

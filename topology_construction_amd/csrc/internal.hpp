@@ -1,0 +1,288 @@
+// Internal declarations shared by the HIP translation units of the library.
+// Not part of the public ABI (see include/topo.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <stdexcept>
+#include <string>
+#include <vector>
+
+#include "../../include/topo.h"
+
+namespace tc {
+
+using u64 = uint64_t;
+using i64 = int64_t;
+
+// ------------------------------------------------------------------ errors
+struct Error : std::runtime_error {
+  tc_status status;
+  Error(tc_status s, const std::string& msg) : std::runtime_error(msg), status(s) {}
+};
+
+inline void hip_check(hipError_t e, const char* what) {
+  if (e != hipSuccess)
+    throw Error(TC_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// ------------------------------------------------------------------ op tables
+// Per-axis offset sets of the box ops (PR page section 2): DILATE {-1,0,1},
+// PAD_NEG {-1,0}, PAD_POS {0,1}. `m` = number of neighbour combinations; j in
+// [0, m) enumerates them x-major.
+struct OpInfo {
+  int op;
+  int m;       // candidate targets per source node (tiles per upper, lowers per lower)
+  int m_src;   // source lowers that can feed one candidate lower
+  int lo, hi;  // box offset range per axis (box ops only)
+};
+
+inline OpInfo op_info(int op) {
+  switch (op) {
+    case TC_OP_REFINE: return {op, 8, 1, 0, 0};
+    case TC_OP_COARSEN: return {op, 1, 8, 0, 0};
+    case TC_OP_DILATE: return {op, 27, 27, -1, 1};
+    case TC_OP_PAD_NEG: return {op, 8, 27, -1, 0};
+    case TC_OP_PAD_POS: return {op, 8, 27, 0, 1};
+    default: throw Error(TC_ERR_INVALID_ARG, "unknown op");
+  }
+}
+
+// ------------------------------------------------------------------ layout
+struct Layout {
+  size_t headers, upper_origin, upper_key, upper_first, upper_mask, lower_origin, lower_first,
+      lower_mask, lower_prefix, leaf_origin, leaf_parent, leaf_mask, leaf_prefix, leaf_offset;
+  size_t total;
+};
+
+inline size_t align_up(size_t x, size_t a = 256) { return (x + a - 1) / a * a; }
+
+inline Layout make_layout(i64 B, i64 n2, i64 n1, i64 nl) {
+  Layout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  L.headers = take(sizeof(tc_grid_header) * (size_t)B);
+  L.upper_origin = take(16 * (size_t)n2);
+  L.upper_key = take(8 * (size_t)n2);
+  L.upper_first = take(4 * (size_t)n2);
+  L.upper_mask = take(4096 * (size_t)n2);
+  L.lower_origin = take(16 * (size_t)n1);
+  L.lower_first = take(4 * (size_t)n1);
+  L.lower_mask = take(512 * (size_t)n1);
+  L.lower_prefix = take(128 * (size_t)n1);
+  L.leaf_origin = take(16 * (size_t)nl);
+  L.leaf_parent = take(4 * (size_t)nl);
+  L.leaf_mask = take(64 * (size_t)nl);
+  L.leaf_prefix = take(8 * (size_t)nl);
+  L.leaf_offset = take(8 * (size_t)nl);
+  L.total = off;
+  return L;
+}
+
+// Device views of a grid batch (all pointers into its single buffer).
+struct GridView {
+  int32_t B, n_upper, n_lower, n_leaf;
+  tc_grid_header* headers;
+  int4* upper_origin;
+  u64* upper_key;
+  int32_t* upper_first;
+  u64* upper_mask;
+  int4* lower_origin;
+  int32_t* lower_first;
+  u64* lower_mask;
+  uint16_t* lower_prefix;
+  int4* leaf_origin;
+  int32_t* leaf_parent;
+  u64* leaf_mask;
+  u64* leaf_prefix;
+  i64* leaf_offset;
+};
+
+inline GridView make_view(void* buffer, const Layout& L, int32_t B, int32_t n2, int32_t n1, int32_t nl) {
+  char* b = static_cast<char*>(buffer);
+  GridView v;
+  v.B = B;
+  v.n_upper = n2;
+  v.n_lower = n1;
+  v.n_leaf = nl;
+  v.headers = reinterpret_cast<tc_grid_header*>(b + L.headers);
+  v.upper_origin = reinterpret_cast<int4*>(b + L.upper_origin);
+  v.upper_key = reinterpret_cast<u64*>(b + L.upper_key);
+  v.upper_first = reinterpret_cast<int32_t*>(b + L.upper_first);
+  v.upper_mask = reinterpret_cast<u64*>(b + L.upper_mask);
+  v.lower_origin = reinterpret_cast<int4*>(b + L.lower_origin);
+  v.lower_first = reinterpret_cast<int32_t*>(b + L.lower_first);
+  v.lower_mask = reinterpret_cast<u64*>(b + L.lower_mask);
+  v.lower_prefix = reinterpret_cast<uint16_t*>(b + L.lower_prefix);
+  v.leaf_origin = reinterpret_cast<int4*>(b + L.leaf_origin);
+  v.leaf_parent = reinterpret_cast<int32_t*>(b + L.leaf_parent);
+  v.leaf_mask = reinterpret_cast<u64*>(b + L.leaf_mask);
+  v.leaf_prefix = reinterpret_cast<u64*>(b + L.leaf_prefix);
+  v.leaf_offset = reinterpret_cast<i64*>(b + L.leaf_offset);
+  return v;
+}
+
+// ------------------------------------------------------------------ host-side memory
+// Scratch arena: one hipMallocAsync block carved into 256-byte aligned arrays,
+// released with hipFreeAsync (stream-ordered) when the arena is destroyed.
+class Arena {
+ public:
+  explicit Arena(hipStream_t s) : stream_(s) {}
+  ~Arena() { release(); }
+  Arena(const Arena&) = delete;
+  Arena& operator=(const Arena&) = delete;
+  // Reserve `bytes` (rounded up); returns an offset handle resolved after commit().
+  size_t reserve(size_t bytes) {
+    size_t at = size_;
+    size_ = align_up(size_ + (bytes ? bytes : 1));
+    return at;
+  }
+  void commit();
+  template <typename T>
+  T* at(size_t off) const { return reinterpret_cast<T*>(base_ + off); }
+  void release();
+  size_t size() const { return size_; }
+
+ private:
+  hipStream_t stream_;
+  char* base_ = nullptr;
+  size_t size_ = 0;
+};
+
+// Per-thread pinned host staging buffer (grows on demand, never shrinks).
+void* pinned_staging(size_t bytes);
+
+// Stream-ordered device allocation from the device's default pool (release
+// threshold raised once per device so that memory is cached across calls).
+void* device_alloc_async(size_t bytes, hipStream_t s);
+void device_free_async(void* p, hipStream_t s);
+
+// ------------------------------------------------------------------ profiling
+void prof_before(const char* name, hipStream_t s);
+void prof_after(const char* name, hipStream_t s);
+
+template <typename Kernel, typename... Args>
+inline void launch(const char* name, Kernel kernel, i64 blocks, int threads, hipStream_t s, Args... args) {
+  if (blocks <= 0) return;
+  if (blocks > 0x7fffffffLL) throw Error(TC_ERR_UNSUPPORTED, std::string(name) + ": grid too large");
+  prof_before(name, s);
+  hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(threads), 0, s, args...);
+  hip_check(hipGetLastError(), name);
+  prof_after(name, s);
+}
+
+inline i64 ceil_div(i64 a, i64 b) { return (a + b - 1) / b; }
+
+// ------------------------------------------------------------------ primitives (primitives.hip)
+// Exclusive scan of n items (n read from d_n when non-null, else n_host; n_host
+// is the launch bound). out has n+1 entries; out[n] = total.
+void scan_excl_i32(const int32_t* in, int32_t* out, i64 n_host, const int32_t* d_n, hipStream_t s);
+void scan_excl_i64(const i64* in, i64* out, i64 n_host, const int32_t* d_n, hipStream_t s);
+void scan_excl_u32(const uint32_t* in, uint32_t* out, i64 n_host, const int32_t* d_n, hipStream_t s);
+
+void fill_i32(int32_t* p, int32_t v, i64 n_host, const int32_t* d_n, int32_t mult, hipStream_t s);
+void fill_u64(u64* p, u64 v, i64 n_host, const int32_t* d_n, int32_t mult, hipStream_t s);
+
+// Sorts (key_hi, key_lo) 128-bit keys with uint32 values ascending. `key_bits`
+// bounds the significant low bits of every key (keys above them compare by
+// those bits only). n is host-known.
+struct Key128 {
+  u64 lo, hi;
+};
+void sort_pairs_128(Key128* keys, uint32_t* vals, i64 n, int key_bits, hipStream_t s);
+
+// ------------------------------------------------------------------ tile keys
+// A tile key packs (grid, Tx+2^19, Ty+2^19, Tz+2^19) as grid<<60 | tx<<40 | ty<<20 | tz
+// over 128 bits; INVALID sorts after every valid key.
+constexpr int kTileBias = 1 << 19;
+inline int tile_key_bits(int32_t B) {
+  int gb = 0;
+  while (gb < 31 && ((int64_t)1 << gb) < B) ++gb;
+  return 61 + gb;  // one spare bit keeps INVALID above every valid key
+}
+
+// ------------------------------------------------------------------ tree assembly (tree.hip)
+// Candidate-node state shared by the topology pass and the ijk front-end.
+struct TreeScratch {
+  // tiles (unique, canonical order)
+  int32_t* d_num_tiles;      // [1]
+  int4* utile;               // [cap_tiles] Tx, Ty, Tz, grid
+  u64* tile_child;           // [cap_tiles][512]
+  uint16_t* tile_prefix;     // [cap_tiles][512]
+  int32_t* tile_lower_count; // [cap_tiles]
+  int32_t* tile_lower_base;  // [cap_tiles + 1]
+  int32_t* tile_nonempty;    // [cap_tiles]
+  int32_t* upper_excl;       // [cap_tiles + 1]
+  int32_t* grid_tile_begin;  // [B + 1]
+  // candidate lowers
+  int32_t* d_num_cands;      // points at tile_lower_base[num_tiles] after the tile scan
+  int4* cand_origin;         // [cap_cands] x, y, z (voxel origin), tile
+  u64* cand_child;           // [cap_cands][64]
+  uint16_t* cand_prefix;     // [cap_cands][64]
+  int32_t* cand_leaf_count;  // [cap_cands]
+  int32_t* cand_nonempty;    // [cap_cands]
+  int32_t* leaf_base;        // [cap_cands + 1]
+  int32_t* lower_excl;       // [cap_cands + 1]
+  // per-grid results
+  int32_t* grid_info;        // [B][6]: nU, nL1, nL, uBegin, lBegin, leafBegin
+  int32_t* readback;         // [4 + 3B]: flags, N2, N1, L, then per-grid counts
+  int32_t* flags;            // [1] bit 0 overflow, bit 1 internal error (inside readback)
+  i64 cap_tiles, cap_cands;
+};
+
+// Launch groups (implemented in tree.hip).
+void tree_tile_ranges(TreeScratch& t, int32_t B, hipStream_t s);
+void tree_grid_counts(TreeScratch& t, int32_t B, hipStream_t s);
+void tree_rank_tiles(TreeScratch& t, hipStream_t s);            // prefix per tile + scan -> cand numbering
+void tree_count_cands(TreeScratch& t, hipStream_t s);           // leaf counts per cand + scans + tile flags + grid counts
+void tree_write_nodes(TreeScratch& t, const GridView& out, int32_t* leaf_cand, hipStream_t s);
+void tree_finalize_leaves(const GridView& out, i64* leaf_vox, i64* vox_excl, int32_t* bbox_accum,
+                          const int32_t* grid_info, hipStream_t s);
+void tree_enumerate(const GridView& v, int32_t* ijk, hipStream_t s);
+
+// Allocation of the single output buffer of a batch.
+struct OutAlloc {
+  const tc_allocator* alloc;  // NULL: hipMallocAsync
+  hipStream_t stream;
+};
+
+void prof_enable(const char* name);
+void prof_read(double* ms, int64_t* n);
+void prof_disable();
+
+}  // namespace tc
+
+// The opaque batch handle of the C ABI.
+struct tc_grid_batch {
+  int32_t B = 0, n2 = 0, n1 = 0, nl = 0;
+  std::vector<int32_t> h_upper, h_lower, h_leaf;
+  void* buffer = nullptr;
+  size_t bytes = 0;
+  tc::Layout layout{};
+  bool has_alloc = false;
+  tc_allocator alloc{};
+  hipStream_t stream = nullptr;
+  int device = 0;
+  mutable bool vox_known = false;
+  mutable int64_t vox_total = 0;
+
+  tc::GridView view() const {
+    return tc::make_view(buffer, layout, B, n2, n1, nl);
+  }
+};
+
+namespace tc {
+// Creates the output batch from the readback of a tree assembly (counts per
+// grid) and allocates its buffer; throws on failure (nothing leaked).
+tc_grid_batch* new_batch(int32_t B, const int32_t* readback, const OutAlloc& oa);
+void free_batch(tc_grid_batch* b);
+
+// The two producers of grid batches.
+tc_grid_batch* build_from_ijk(const int32_t* d_ijk, const int64_t* h_offsets, int32_t B, const OutAlloc& oa);
+tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa);
+}  // namespace tc

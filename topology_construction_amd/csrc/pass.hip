@@ -1,0 +1,615 @@
+// One batched topology pass over every source leaf of every member
+// (PR page "Batched leaf-mask topology construction for generated conv grids",
+// section 1: emission over all source leaves of all members, canonical order,
+// dedup, one readback, one allocation, batched writers; section 2: box-dilate
+// [-1,1]^3 and the pads {-1,0}^3 / {0,1}^3 via per-axis bit shifts).
+//
+// Mask layout: leaf bit n = x*64 + y*8 + z, i.e. word x, byte y, bit z; lower
+// child bit (x*16+y)*16+z; upper child bit (x*32+y)*32+z.
+//
+// Stages (sizes are host-known bounds, so nothing waits before the readback):
+//   tiles   each source upper proposes its target root tiles; one small sort of
+//           the (grid, tile) keys and a head-flag scan give the unique tiles;
+//   lowers  each source lower sets its candidate target lowers in the target
+//           tile's 32^3 mask; ranks in those masks number the candidates;
+//   leaves  each source leaf sets the bit of every non-empty target leaf in the
+//           target lower's 16^3 mask (pass A, scatter, one atomic OR per target);
+//   counts  popcounts and scans give per-grid counts -> the single readback;
+//   writers node records, then every output leaf gathers its mask from the
+//           (at most 1 / 8 / 27) source leaves that feed it (pass B, no atomics).
+#include "device.hpp"
+#include "internal.hpp"
+
+namespace tc {
+
+constexpr u64 kZ0 = 0x0101010101010101ull;  // z = 0 bit of every (x, y) row
+constexpr u64 kZ7 = 0x8080808080808080ull;  // z = 7 bit of every row
+constexpr int kFlagOverflow = 1;
+constexpr int kFlagInternal = 2;
+
+struct I3 {
+  i64 x, y, z;
+};
+
+__device__ __forceinline__ I3 octant(int j) { return {(j >> 2) & 1, (j >> 1) & 1, j & 1}; }
+__device__ __forceinline__ int octant_index(i64 x, i64 y, i64 z) { return (int)((x << 2) | (y << 1) | z); }
+
+// j -> box offset of the op (DILATE: base-3 digits minus one; pads: sign * bits).
+__device__ __forceinline__ I3 box_offset(int j, int op) {
+  if (op == TC_OP_DILATE) return {j / 9 - 1, (j / 3) % 3 - 1, j % 3 - 1};
+  const i64 s = op == TC_OP_PAD_NEG ? -1 : 1;
+  return {s * ((j >> 2) & 1), s * ((j >> 1) & 1), s * (j & 1)};
+}
+__device__ __forceinline__ int box_index(i64 x, i64 y, i64 z, int op) {
+  if (op == TC_OP_DILATE) return (int)((x + 1) * 9 + (y + 1) * 3 + (z + 1));
+  const i64 s = op == TC_OP_PAD_NEG ? -1 : 1;
+  return (int)(((s * x) << 2) | ((s * y) << 1) | (s * z));
+}
+__device__ __forceinline__ int index27(i64 x, i64 y, i64 z) { return (int)((x + 1) * 9 + (y + 1) * 3 + (z + 1)); }
+
+__device__ __forceinline__ bool tile_ok(i64 t) { return t >= -kTileBias && t < kTileBias; }
+__device__ __forceinline__ bool lower_ok(i64 k) { return k >= -(1ll << 24) && k < (1ll << 24); }
+__device__ __forceinline__ bool leaf_ok(i64 l) { return l >= -(1ll << 28) && l < (1ll << 28); }
+
+__device__ __forceinline__ void set_flag(int32_t* flags, int f) { atomicOr(flags, f); }
+
+// ------------------------------------------------------------------ stage: tiles
+__global__ void __launch_bounds__(256) k_tile_candidates(const int4* upper_origin, i64 n, int op, int m,
+                                                         Key128* keys, uint32_t* vals) {
+  const i64 i = (i64)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const i64 u = i / m;
+  const int j = (int)(i % m);
+  const int4 o = upper_origin[u];
+  const i64 tx = o.x >> 12, ty = o.y >> 12, tz = o.z >> 12;
+  I3 t;
+  if (op == TC_OP_REFINE) {
+    const I3 q = octant(j);
+    t = {2 * tx + q.x, 2 * ty + q.y, 2 * tz + q.z};
+  } else if (op == TC_OP_COARSEN) {
+    t = {tx >> 1, ty >> 1, tz >> 1};
+  } else {
+    const I3 e = box_offset(j, op);
+    t = {tx + e.x, ty + e.y, tz + e.z};
+  }
+  Key128 k{~0ull, ~0ull};
+  if (tile_ok(t.x) && tile_ok(t.y) && tile_ok(t.z)) {
+    const u64 g = (uint32_t)o.w;
+    k.lo = ((g & 15ull) << 60) | ((u64)(t.x + kTileBias) << 40) | ((u64)(t.y + kTileBias) << 20) |
+           (u64)(t.z + kTileBias);
+    k.hi = g >> 4;
+  }
+  keys[i] = k;
+  vals[i] = (uint32_t)i;
+}
+
+__device__ __forceinline__ bool key_valid(const Key128& k) { return !(k.lo == ~0ull && k.hi == ~0ull); }
+
+__global__ void __launch_bounds__(256) k_tile_heads(const Key128* keys, i64 n, int32_t* head) {
+  const i64 i = (i64)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const Key128 k = keys[i];
+  bool h = key_valid(k);
+  if (h && i > 0) {
+    const Key128 p = keys[i - 1];
+    h = !(p.lo == k.lo && p.hi == k.hi);
+  }
+  head[i] = h ? 1 : 0;
+}
+
+__global__ void __launch_bounds__(256) k_tile_scatter(const Key128* keys, const uint32_t* vals, const int32_t* head,
+                                                      const int32_t* excl, i64 n, int4* utile, int32_t* tile_of_cand,
+                                                      int32_t* flags) {
+  const i64 i = (i64)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const Key128 k = keys[i];
+  const uint32_t v = vals[i];
+  if ((i64)v >= n) {
+    set_flag(flags, kFlagInternal);
+    return;
+  }
+  if (!key_valid(k)) {
+    tile_of_cand[v] = -1;
+    return;
+  }
+  const int32_t t = excl[i] + head[i] - 1;
+  if (t < 0 || t >= n) {
+    set_flag(flags, kFlagInternal);
+    return;
+  }
+  tile_of_cand[v] = t;
+  if (head[i]) {
+    const int32_t g = (int32_t)((k.hi << 4) | (k.lo >> 60));
+    const int32_t x = (int32_t)((k.lo >> 40) & 0xfffff) - kTileBias;
+    const int32_t y = (int32_t)((k.lo >> 20) & 0xfffff) - kTileBias;
+    const int32_t z = (int32_t)(k.lo & 0xfffff) - kTileBias;
+    utile[t] = make_int4(x, y, z, g);
+  }
+}
+
+// ------------------------------------------------------------------ stage: lowers
+// Target lower of source lower K for candidate j, and the index (among the
+// parent upper's tile candidates) of the tile that holds it.
+struct LowerTarget {
+  I3 k;
+  int jt;
+  bool ok;
+};
+
+__device__ __forceinline__ LowerTarget lower_target(const int4 o, int j, int op) {
+  const i64 kx = o.x >> 7, ky = o.y >> 7, kz = o.z >> 7;
+  LowerTarget r;
+  if (op == TC_OP_REFINE) {
+    const I3 q = octant(j);
+    r.k = {2 * kx + q.x, 2 * ky + q.y, 2 * kz + q.z};
+    r.jt = octant_index((r.k.x >> 5) - 2 * (kx >> 5), (r.k.y >> 5) - 2 * (ky >> 5), (r.k.z >> 5) - 2 * (kz >> 5));
+  } else if (op == TC_OP_COARSEN) {
+    r.k = {kx >> 1, ky >> 1, kz >> 1};
+    r.jt = 0;
+  } else {
+    const I3 e = box_offset(j, op);
+    r.k = {kx + e.x, ky + e.y, kz + e.z};
+    r.jt = box_index((r.k.x >> 5) - (kx >> 5), (r.k.y >> 5) - (ky >> 5), (r.k.z >> 5) - (kz >> 5), op);
+  }
+  r.ok = lower_ok(r.k.x) && lower_ok(r.k.y) && lower_ok(r.k.z);
+  return r;
+}
+
+__device__ __forceinline__ int upper_child_bit(const I3& k) {
+  return (int)((((k.x & 31) * 32) + (k.y & 31)) * 32 + (k.z & 31));
+}
+
+__global__ void __launch_bounds__(256) k_lower_mark(const int4* lower_origin, i64 n, int op, int m,
+                                                    const int32_t* tile_of_cand, const int32_t* d_num_tiles,
+                                                    u64* tile_child, int32_t* flags) {
+  const i64 i = (i64)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const i64 l = i / m;
+  const int j = (int)(i % m);
+  const int4 o = lower_origin[l];
+  const LowerTarget tg = lower_target(o, j, op);
+  if (!tg.ok) return;
+  const int32_t t = tile_of_cand[(i64)o.w * m + tg.jt];
+  if (t < 0 || t >= *d_num_tiles) {
+    set_flag(flags, kFlagInternal);
+    return;
+  }
+  const int bit = upper_child_bit(tg.k);
+  atomicOr((unsigned long long*)&tile_child[(i64)t * 512 + (bit >> 6)], 1ull << (bit & 63));
+}
+
+__global__ void __launch_bounds__(256) k_lower_nbr(const int4* lower_origin, i64 n, int op, int m, int m_src,
+                                                   const int32_t* tile_of_cand, const u64* tile_child,
+                                                   const uint16_t* tile_prefix, const int32_t* tile_lower_base,
+                                                   const int32_t* d_num_tiles, const int32_t* d_num_cands,
+                                                   int32_t* lower_nbr, int4* cand_origin, int32_t* cand_src,
+                                                   int32_t* flags) {
+  const i64 i = (i64)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const i64 l = i / m;
+  const int j = (int)(i % m);
+  const int4 o = lower_origin[l];
+  const LowerTarget tg = lower_target(o, j, op);
+  if (!tg.ok) {
+    lower_nbr[i] = -1;
+    return;
+  }
+  const int32_t t = tile_of_cand[(i64)o.w * m + tg.jt];
+  if (t < 0 || t >= *d_num_tiles) {
+    lower_nbr[i] = -1;
+    set_flag(flags, kFlagInternal);
+    return;
+  }
+  const int bit = upper_child_bit(tg.k);
+  const int w = bit >> 6, b = bit & 63;
+  const u64 word = tile_child[(i64)t * 512 + w];
+  const int32_t c = tile_lower_base[t] + tile_prefix[(i64)t * 512 + w] + popc64(word & ((1ull << b) - 1));
+  if (!((word >> b) & 1ull) || c < 0 || c >= *d_num_cands) {
+    lower_nbr[i] = -1;
+    set_flag(flags, kFlagInternal);
+    return;
+  }
+  lower_nbr[i] = c;
+  cand_origin[c] = make_int4((int32_t)(tg.k.x * 128), (int32_t)(tg.k.y * 128), (int32_t)(tg.k.z * 128), t);
+  int js;
+  if (op == TC_OP_REFINE) {
+    js = 0;
+  } else if (op == TC_OP_COARSEN) {
+    js = octant_index((o.x >> 7) & 1, (o.y >> 7) & 1, (o.z >> 7) & 1);
+  } else {
+    const I3 e = box_offset(j, op);
+    js = index27(-e.x, -e.y, -e.z);
+  }
+  cand_src[(i64)c * m_src + js] = (int32_t)l;
+}
+
+// ------------------------------------------------------------------ stage: leaves (pass A)
+// Non-emptiness of the target leaf reached with offset t (each component -1/0/+1)
+// under a box op: the source must hold a voxel on the faces that spill toward t.
+__device__ __forceinline__ bool spill_nonempty(const u64 W[8], const I3& t) {
+  u64 xs;
+  if (t.x > 0) xs = W[7];
+  else if (t.x < 0) xs = W[0];
+  else xs = W[0] | W[1] | W[2] | W[3] | W[4] | W[5] | W[6] | W[7];
+  const u64 ym = t.y > 0 ? 0xff00000000000000ull : (t.y < 0 ? 0xffull : ~0ull);
+  const u64 zm = t.z > 0 ? kZ7 : (t.z < 0 ? kZ0 : ~0ull);
+  return (xs & ym & zm) != 0;
+}
+
+// Refine: the 4^3 sub-block q of the source leaf becomes child leaf q.
+__device__ __forceinline__ bool subblock_nonempty(const u64 W[8], const I3& q) {
+  const u64 xs = q.x ? (W[4] | W[5] | W[6] | W[7]) : (W[0] | W[1] | W[2] | W[3]);
+  const u64 ym = q.y ? 0xffffffff00000000ull : 0x00000000ffffffffull;
+  const u64 zm = q.z ? 0xf0f0f0f0f0f0f0f0ull : 0x0f0f0f0f0f0f0f0full;
+  return (xs & ym & zm) != 0;
+}
+
+__device__ __forceinline__ void mark_leaf(u64* cand_child, int32_t c, i64 px, i64 py, i64 pz) {
+  const int bit = (int)((px * 16 + py) * 16 + pz);
+  atomicOr((unsigned long long*)&cand_child[(i64)c * 64 + (bit >> 6)], 1ull << (bit & 63));
+}
+
+__global__ void __launch_bounds__(256) k_leaf_mark(const int4* leaf_origin, const int32_t* leaf_parent,
+                                                   const u64* leaf_mask, i64 n, int op, int m,
+                                                   const int32_t* lower_nbr, const int32_t* d_num_cands,
+                                                   u64* cand_child, int32_t* flags) {
+  const i64 i = (i64)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int32_t ncand = *d_num_cands;
+  const int4 o = leaf_origin[i];
+  const i64 l = leaf_parent[i];
+  u64 W[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) W[k] = leaf_mask[i * 8 + k];
+  const i64 mx = o.x >> 3, my = o.y >> 3, mz = o.z >> 3;  // leaf coordinates
+  const i64 lx = mx & 15, ly = my & 15, lz = mz & 15;     // position inside the lower
+  if (op == TC_OP_REFINE) {
+    const int32_t c = lower_nbr[l * 8 + octant_index(lx >> 3, ly >> 3, lz >> 3)];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const I3 q = octant(j);
+      if (!subblock_nonempty(W, q)) continue;
+      if (!leaf_ok(2 * mx + q.x) || !leaf_ok(2 * my + q.y) || !leaf_ok(2 * mz + q.z)) {
+        set_flag(flags, kFlagOverflow);
+        continue;
+      }
+      if (c < 0 || c >= ncand) {
+        set_flag(flags, kFlagInternal);
+        continue;
+      }
+      mark_leaf(cand_child, c, (2 * lx + q.x) & 15, (2 * ly + q.y) & 15, (2 * lz + q.z) & 15);
+    }
+  } else if (op == TC_OP_COARSEN) {
+    const int32_t c = lower_nbr[l];
+    if (c < 0 || c >= ncand) {
+      set_flag(flags, kFlagInternal);
+      return;
+    }
+    mark_leaf(cand_child, c, (mx >> 1) & 15, (my >> 1) & 15, (mz >> 1) & 15);
+  } else {
+    for (int j = 0; j < m; ++j) {
+      const I3 t = box_offset(j, op);
+      if (!spill_nonempty(W, t)) continue;
+      if (!leaf_ok(mx + t.x) || !leaf_ok(my + t.y) || !leaf_ok(mz + t.z)) {
+        set_flag(flags, kFlagOverflow);
+        continue;
+      }
+      const i64 px = lx + t.x, py = ly + t.y, pz = lz + t.z;  // -1 .. 16
+      const int32_t c = lower_nbr[l * m + box_index(px >> 4, py >> 4, pz >> 4, op)];
+      if (c < 0 || c >= ncand) {
+        set_flag(flags, kFlagInternal);
+        continue;
+      }
+      mark_leaf(cand_child, c, px & 15, py & 15, pz & 15);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ writers: leaf masks (pass B)
+// Index of the source leaf at position p inside source lower s, or -1 when that
+// leaf is absent (or s / the result is out of range, which also flags an error).
+__device__ __forceinline__ int32_t src_leaf(const u64* lower_mask, const uint16_t* lower_prefix,
+                                            const int32_t* lower_first, int32_t s, i64 px, i64 py, i64 pz,
+                                            int32_t n_lower, int32_t n_leaf, int32_t* flags) {
+  if (s < 0 || s >= n_lower) {
+    set_flag(flags, kFlagInternal);
+    return -1;
+  }
+  const int bit = (int)((px * 16 + py) * 16 + pz);
+  const int w = bit >> 6, b = bit & 63;
+  const u64 word = lower_mask[(i64)s * 64 + w];
+  if (!((word >> b) & 1ull)) return -1;
+  const int32_t r = lower_first[s] + lower_prefix[(i64)s * 64 + w] + popc64(word & ((1ull << b) - 1));
+  if (r < 0 || r >= n_leaf) {
+    set_flag(flags, kFlagInternal);
+    return -1;
+  }
+  return r;
+}
+
+// Nibble (4 bits) -> byte with every bit doubled.
+__device__ __forceinline__ u64 double_bits4(u64 b) {
+  b = (b | (b << 2)) & 0x33ull;
+  b = (b | (b << 1)) & 0x55ull;
+  return b | (b << 1);
+}
+
+// Refine: output rows 2r, 2r+1 and bits 2c, 2c+1 come from row 4qy + r, bit 4qz + c of w.
+__device__ __forceinline__ u64 refine_word(u64 w, int qy, int qz) {
+  u64 out = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const u64 nib = (w >> ((4 * qy + r) * 8 + 4 * qz)) & 0xfull;
+    const u64 b = double_bits4(nib);
+    out |= (b << (16 * r)) | (b << (16 * r + 8));
+  }
+  return out;
+}
+
+// Coarsen: OR each 2x2x2 block of the source into one bit, giving a 4^3 block
+// placed at offset 4q of the output leaf.
+__device__ __forceinline__ void coarsen_place(u64 out[8], const u64 W[8], const I3& q) {
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    u64 v = W[2 * x] | W[2 * x + 1];
+    v = (v | (v >> 1)) & 0x5555555555555555ull;  // z pairs -> even bits
+    v = (v | (v >> 8)) & 0x00ff00ff00ff00ffull;  // y pairs -> even bytes
+    v = (v | (v >> 1)) & 0x3333333333333333ull;  // even bits 0,2,4,6 -> 0,1,4,5
+    v = (v | (v >> 2)) & 0x0f0f0f0f0f0f0f0full;  // -> 0..3
+    u64 placed = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) placed |= ((v >> (16 * r)) & 0xfull) << ((4 * q.y + r) * 8 + 4 * q.z);
+    out[4 * q.x + x] |= placed;
+  }
+}
+
+// Box op: contribution of source W to the neighbour at offset t (t is the
+// target's offset from the source), with per-axis box offsets in [lo, hi].
+__device__ __forceinline__ void box_contrib(u64 out[8], const u64 W[8], const I3& t, int lo, int hi) {
+#pragma unroll
+  for (int x = 0; x < 8; ++x) {
+    u64 a = 0;
+    if (t.x == 0) {
+      for (int e = lo; e <= hi; ++e) {
+        const int xs = x - e;
+        if (xs >= 0 && xs < 8) a |= W[xs];
+      }
+    } else if (t.x > 0) {
+      if (x == 0) a = W[7];
+    } else {
+      if (x == 7) a = W[0];
+    }
+    if (!a) continue;
+    u64 y;
+    if (t.y == 0) {
+      y = a;
+      if (hi > 0) y |= a << 8;
+      if (lo < 0) y |= a >> 8;
+    } else if (t.y > 0) {
+      y = a >> 56;
+    } else {
+      y = a << 56;
+    }
+    u64 z;
+    if (t.z == 0) {
+      z = y;
+      if (hi > 0) z |= (y & ~kZ7) << 1;
+      if (lo < 0) z |= (y & ~kZ0) >> 1;
+    } else if (t.z > 0) {
+      z = (y & kZ7) >> 7;
+    } else {
+      z = (y & kZ0) << 7;
+    }
+    out[x] |= z;
+  }
+}
+
+__global__ void __launch_bounds__(256) k_leaf_gather(const int4* out_origin, const int32_t* leaf_cand, i64 n,
+                                                     int op, int m, int lo, int hi, const int32_t* cand_src,
+                                                     const u64* src_lower_mask, const uint16_t* src_lower_prefix,
+                                                     const int32_t* src_lower_first, const u64* src_leaf_mask,
+                                                     int32_t n_src_lower, int32_t n_src_leaf,
+                                                     const int32_t* d_num_cands, u64* out_mask, int32_t* flags) {
+  const i64 i = (i64)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int4 o = out_origin[i];
+  const i64 c = leaf_cand[i];
+  if (c < 0 || c >= *d_num_cands) {
+    set_flag(flags, kFlagInternal);
+    return;
+  }
+  const i64 ax = o.x >> 3, ay = o.y >> 3, az = o.z >> 3;  // output leaf coordinates
+  const i64 lx = ax & 15, ly = ay & 15, lz = az & 15;
+  u64 out[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) out[k] = 0;
+  if (op == TC_OP_REFINE) {
+    const int32_t s = cand_src[c];
+    const int32_t src = src_leaf(src_lower_mask, src_lower_prefix, src_lower_first, s, (ax >> 1) & 15,
+                                 (ay >> 1) & 15, (az >> 1) & 15, n_src_lower, n_src_leaf, flags);
+    if (src < 0) {
+      set_flag(flags, kFlagInternal);
+    } else {
+      u64 W[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) W[k] = src_leaf_mask[(i64)src * 8 + k];
+      const int qx = (int)(ax & 1), qy = (int)(ay & 1), qz = (int)(az & 1);
+#pragma unroll
+      for (int x = 0; x < 8; ++x) out[x] = refine_word(W[4 * qx + (x >> 1)], qy, qz);
+    }
+  } else if (op == TC_OP_COARSEN) {
+    const int32_t s = cand_src[c * 8 + octant_index(lx >> 3, ly >> 3, lz >> 3)];
+    if (s >= 0) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const I3 q = octant(j);
+        const int32_t src = src_leaf(src_lower_mask, src_lower_prefix, src_lower_first, s, (2 * lx + q.x) & 15,
+                                     (2 * ly + q.y) & 15, (2 * lz + q.z) & 15, n_src_lower, n_src_leaf, flags);
+        if (src < 0) continue;
+        u64 W[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) W[k] = src_leaf_mask[(i64)src * 8 + k];
+        coarsen_place(out, W, q);
+      }
+    } else {
+      set_flag(flags, kFlagInternal);
+    }
+  } else {
+    for (int j = 0; j < m; ++j) {
+      const I3 t = box_offset(j, op);
+      const i64 px = lx - t.x, py = ly - t.y, pz = lz - t.z;  // source position, -1 .. 16
+      const int32_t s = cand_src[c * 27 + index27(px >> 4, py >> 4, pz >> 4)];
+      if (s < 0) continue;
+      const int32_t src = src_leaf(src_lower_mask, src_lower_prefix, src_lower_first, s, px & 15, py & 15, pz & 15,
+                                   n_src_lower, n_src_leaf, flags);
+      if (src < 0) continue;
+      u64 W[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) W[k] = src_leaf_mask[(i64)src * 8 + k];
+      box_contrib(out, W, t, lo, hi);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) out_mask[i * 8 + k] = out[k];
+}
+
+// ------------------------------------------------------------------ driver
+tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa) {
+  const OpInfo oi = op_info(op);
+  hipStream_t s = oa.stream;
+  const int32_t B = src->B;
+  const GridView sv = src->view();
+  const i64 nT = (i64)src->n2 * oi.m;
+  const i64 nL = (i64)src->n1 * oi.m;
+  const i64 Ls = src->nl;
+  if (nT > 0x7fffffffLL || nL > 0x7fffffffLL || nL * oi.m_src > (1ll << 40))
+    throw Error(TC_ERR_UNSUPPORTED, "pass: source batch too large");
+
+  Arena a(s);
+  const size_t o_keys = a.reserve(sizeof(Key128) * nT);
+  const size_t o_vals = a.reserve(4 * nT);
+  const size_t o_head = a.reserve(4 * nT);
+  const size_t o_texcl = a.reserve(4 * (nT + 1));
+  const size_t o_toc = a.reserve(4 * nT);
+  const size_t o_zero = a.reserve(4);
+  const size_t o_ncand = a.reserve(4);
+  const size_t o_utile = a.reserve(16 * nT);
+  const size_t o_tchild = a.reserve(4096 * nT);
+  const size_t o_tpre = a.reserve(1024 * nT);
+  const size_t o_tlc = a.reserve(4 * nT);
+  const size_t o_tlb = a.reserve(4 * (nT + 1));
+  const size_t o_tne = a.reserve(4 * nT);
+  const size_t o_uex = a.reserve(4 * (nT + 1));
+  const size_t o_gtb = a.reserve(4 * ((i64)B + 1));
+  const size_t o_corig = a.reserve(16 * nL);
+  const size_t o_cchild = a.reserve(512 * nL);
+  const size_t o_cpre = a.reserve(128 * nL);
+  const size_t o_clc = a.reserve(4 * nL);
+  const size_t o_cne = a.reserve(4 * nL);
+  const size_t o_lb = a.reserve(4 * (nL + 1));
+  const size_t o_lex = a.reserve(4 * (nL + 1));
+  const size_t o_nbr = a.reserve(4 * nL);
+  const size_t o_csrc = a.reserve(4 * nL * oi.m_src);
+  const size_t o_ginfo = a.reserve(4 * 6 * (i64)B);
+  const size_t o_rb = a.reserve(4 * (4 + 3 * (i64)B));
+  a.commit();
+
+  TreeScratch ts{};
+  ts.cap_tiles = nT;
+  ts.cap_cands = nL;
+  ts.utile = a.at<int4>(o_utile);
+  ts.tile_child = a.at<u64>(o_tchild);
+  ts.tile_prefix = a.at<uint16_t>(o_tpre);
+  ts.tile_lower_count = a.at<int32_t>(o_tlc);
+  ts.tile_lower_base = a.at<int32_t>(o_tlb);
+  ts.tile_nonempty = a.at<int32_t>(o_tne);
+  ts.upper_excl = a.at<int32_t>(o_uex);
+  ts.grid_tile_begin = a.at<int32_t>(o_gtb);
+  ts.d_num_cands = a.at<int32_t>(o_ncand);
+  ts.cand_origin = a.at<int4>(o_corig);
+  ts.cand_child = a.at<u64>(o_cchild);
+  ts.cand_prefix = a.at<uint16_t>(o_cpre);
+  ts.cand_leaf_count = a.at<int32_t>(o_clc);
+  ts.cand_nonempty = a.at<int32_t>(o_cne);
+  ts.leaf_base = a.at<int32_t>(o_lb);
+  ts.lower_excl = a.at<int32_t>(o_lex);
+  ts.grid_info = a.at<int32_t>(o_ginfo);
+  ts.readback = a.at<int32_t>(o_rb);
+  ts.flags = ts.readback;
+  Key128* keys = a.at<Key128>(o_keys);
+  uint32_t* vals = a.at<uint32_t>(o_vals);
+  int32_t* head = a.at<int32_t>(o_head);
+  int32_t* texcl = a.at<int32_t>(o_texcl);
+  int32_t* tile_of_cand = a.at<int32_t>(o_toc);
+  int32_t* lower_nbr = a.at<int32_t>(o_nbr);
+  int32_t* cand_src = a.at<int32_t>(o_csrc);
+
+  fill_i32(ts.readback, 0, 1, nullptr, 1, s);
+  // tiles
+  if (nT > 0) {
+    launch("k_tile_candidates", k_tile_candidates, ceil_div(nT, 256), 256, s, (const int4*)sv.upper_origin, nT,
+           op, oi.m, keys, vals);
+    sort_pairs_128(keys, vals, nT, tile_key_bits(B), s);
+    launch("k_tile_heads", k_tile_heads, ceil_div(nT, 256), 256, s, (const Key128*)keys, nT, head);
+    scan_excl_i32(head, texcl, nT, nullptr, s);
+    launch("k_tile_scatter", k_tile_scatter, ceil_div(nT, 256), 256, s, (const Key128*)keys,
+           (const uint32_t*)vals, (const int32_t*)head, (const int32_t*)texcl, nT, ts.utile, tile_of_cand, ts.flags);
+    ts.d_num_tiles = texcl + nT;
+  } else {
+    int32_t* zero = a.at<int32_t>(o_zero);
+    fill_i32(zero, 0, 1, nullptr, 1, s);
+    ts.d_num_tiles = zero;
+  }
+  tree_tile_ranges(ts, B, s);
+  // lowers
+  fill_u64(ts.tile_child, 0, nT * 512, ts.d_num_tiles, 512, s);
+  launch("k_lower_mark", k_lower_mark, ceil_div(nL, 256), 256, s, (const int4*)sv.lower_origin, nL, op, oi.m,
+         (const int32_t*)tile_of_cand, (const int32_t*)ts.d_num_tiles, ts.tile_child, ts.flags);
+  tree_rank_tiles(ts, s);
+  fill_i32(cand_src, -1, nL * oi.m_src, ts.d_num_cands, oi.m_src, s);
+  launch("k_lower_nbr", k_lower_nbr, ceil_div(nL, 256), 256, s, (const int4*)sv.lower_origin, nL, op, oi.m,
+         oi.m_src, (const int32_t*)tile_of_cand, (const u64*)ts.tile_child, (const uint16_t*)ts.tile_prefix,
+         (const int32_t*)ts.tile_lower_base, (const int32_t*)ts.d_num_tiles, (const int32_t*)ts.d_num_cands,
+         lower_nbr, ts.cand_origin, cand_src, ts.flags);
+  // leaves (pass A)
+  fill_u64(ts.cand_child, 0, nL * 64, ts.d_num_cands, 64, s);
+  launch("k_leaf_mark", k_leaf_mark, ceil_div(Ls, 256), 256, s, (const int4*)sv.leaf_origin,
+         (const int32_t*)sv.leaf_parent, (const u64*)sv.leaf_mask, Ls, op, oi.m, (const int32_t*)lower_nbr,
+         (const int32_t*)ts.d_num_cands, ts.cand_child, ts.flags);
+  // counts and the single readback
+  tree_count_cands(ts, s);
+  tree_grid_counts(ts, B, s);
+  const size_t rb_bytes = 4 * (4 + 3 * (size_t)B);
+  int32_t* h_rb = static_cast<int32_t*>(pinned_staging(rb_bytes));
+  hip_check(hipMemcpyAsync(h_rb, ts.readback, rb_bytes, hipMemcpyDeviceToHost, s), "readback");
+  hip_check(hipStreamSynchronize(s), "hipStreamSynchronize");
+  if (h_rb[0] & kFlagOverflow) throw Error(TC_ERR_OVERFLOW, "an output voxel coordinate leaves int32");
+  if (h_rb[0] & kFlagInternal) throw Error(TC_ERR_INTERNAL, "pass: device consistency check failed");
+
+  tc_grid_batch* out = new_batch(B, h_rb, oa);
+  try {
+    const GridView ov = out->view();
+    const i64 L = out->nl;
+    Arena post(s);
+    const size_t o_lc = post.reserve(4 * L);
+    const size_t o_lv = post.reserve(8 * L);
+    const size_t o_vx = post.reserve(8 * (L + 1));
+    const size_t o_bb = post.reserve(4 * 6 * (i64)B);
+    post.commit();
+    int32_t* leaf_cand = post.at<int32_t>(o_lc);
+    tree_write_nodes(ts, ov, leaf_cand, s);
+    launch("k_leaf_gather", k_leaf_gather, ceil_div(L, 256), 256, s, (const int4*)ov.leaf_origin,
+           (const int32_t*)leaf_cand, L, op, oi.m, oi.lo, oi.hi, (const int32_t*)cand_src,
+           (const u64*)sv.lower_mask, (const uint16_t*)sv.lower_prefix, (const int32_t*)sv.lower_first,
+           (const u64*)sv.leaf_mask, sv.n_lower, sv.n_leaf, (const int32_t*)ts.d_num_cands, ov.leaf_mask,
+           ts.flags);
+    tree_finalize_leaves(ov, post.at<i64>(o_lv), post.at<i64>(o_vx), post.at<int32_t>(o_bb),
+                         (const int32_t*)ts.grid_info, s);
+  } catch (...) {
+    free_batch(out);
+    throw;
+  }
+  return out;
+}
+
+}  // namespace tc

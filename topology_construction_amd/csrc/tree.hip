@@ -1,0 +1,413 @@
+// Tree assembly shared by the topology pass and the ijk front-end.
+//
+// Input state (TreeScratch): the unique root tiles of the output in canonical
+// order (sorted by grid, then signed x-major tile coordinate), for every tile a
+// 32^3-bit mask of candidate lower nodes, and for every candidate lower node a
+// 16^3-bit mask of its non-empty leaves. Candidate lower nodes are numbered tile
+// by tile in mask-bit order, which is the x-major upper-child order, so the
+// numbering is already canonical; leaves inside a lower are likewise numbered in
+// mask-bit (x-major lower-child) order. Empty candidates are compacted away.
+//
+// This replaces the per-slot sort and head-flag dedup of the PR page (section 1)
+// at leaf level with bitmap marking plus popcount ranks: duplicates collapse in
+// the bitmaps and ranks come from prefix popcounts, so no leaf-level sort runs.
+#include "device.hpp"
+#include "internal.hpp"
+
+namespace tc {
+
+// ------------------------------------------------------------------ tiles
+// grid_tile_begin[g] = first unique tile of grid g; grid_tile_begin[B] = num tiles.
+__global__ void __launch_bounds__(256) k_grid_tile_ranges(const int4* utile, const int32_t* d_num_tiles,
+                                                          int32_t B, int32_t* begin) {
+  const i64 t = (i64)blockIdx.x * 256 + threadIdx.x;
+  const int32_t nt = *d_num_tiles;
+  if (nt == 0) {
+    if (t == 0)
+      for (int32_t g = 0; g <= B; ++g) begin[g] = 0;
+    return;
+  }
+  if (t >= nt) return;
+  const int32_t g = utile[t].w;
+  const int32_t gp = t == 0 ? -1 : utile[t - 1].w;
+  for (int32_t q = gp + 1; q <= g; ++q) begin[q] = (int32_t)t;
+  if (t == nt - 1)
+    for (int32_t q = g + 1; q <= B; ++q) begin[q] = nt;
+}
+
+void tree_tile_ranges(TreeScratch& ts, int32_t B, hipStream_t s) {
+  const i64 n = ts.cap_tiles > 0 ? ts.cap_tiles : 1;
+  launch("k_grid_tile_ranges", k_grid_tile_ranges, ceil_div(n, 256), 256, s, (const int4*)ts.utile,
+         (const int32_t*)ts.d_num_tiles, B, ts.grid_tile_begin);
+}
+
+// One workgroup per tile: per-word exclusive popcount prefix of the 512-word
+// candidate-lower mask and the tile's candidate count.
+__global__ void __launch_bounds__(256) k_tile_rank(const u64* tile_child, uint16_t* tile_prefix,
+                                                   int32_t* tile_lower_count, const int32_t* d_num_tiles) {
+  __shared__ int32_t s_wave[4];
+  const i64 t = blockIdx.x;
+  if (t >= *d_num_tiles) return;
+  const int w0 = threadIdx.x * 2;
+  const u64 a = tile_child[t * 512 + w0];
+  const u64 b = tile_child[t * 512 + w0 + 1];
+  const int ca = popc64(a), cb = popc64(b);
+  int32_t total;
+  const int32_t ex = block_excl_scan<int32_t, 256>(ca + cb, s_wave, total);
+  tile_prefix[t * 512 + w0] = (uint16_t)ex;
+  tile_prefix[t * 512 + w0 + 1] = (uint16_t)(ex + ca);
+  if (threadIdx.x == 0) tile_lower_count[t] = total;
+}
+
+__global__ void k_copy_at(const int32_t* src, const int32_t* d_index, int32_t* dst) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) *dst = src[*d_index];
+}
+
+void tree_rank_tiles(TreeScratch& ts, hipStream_t s) {
+  launch("k_tile_rank", k_tile_rank, ts.cap_tiles, 256, s, (const u64*)ts.tile_child, ts.tile_prefix,
+         ts.tile_lower_count, (const int32_t*)ts.d_num_tiles);
+  scan_excl_i32(ts.tile_lower_count, ts.tile_lower_base, ts.cap_tiles, ts.d_num_tiles, s);
+  launch("k_copy_at", k_copy_at, 1, 64, s, (const int32_t*)ts.tile_lower_base, (const int32_t*)ts.d_num_tiles,
+         ts.d_num_cands);
+}
+
+// ------------------------------------------------------------------ candidate lowers
+// One wave per candidate lower: per-word exclusive popcount prefix of its 64-word
+// leaf mask, leaf count and non-empty flag.
+__global__ void __launch_bounds__(256) k_lower_count(const u64* cand_child, uint16_t* cand_prefix,
+                                                     int32_t* cand_leaf_count, int32_t* cand_nonempty,
+                                                     const int32_t* d_num_cands) {
+  const i64 c = (i64)blockIdx.x * 4 + threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  if (c >= *d_num_cands) return;  // uniform per wave
+  const u64 w = cand_child[c * 64 + lane];
+  const int cnt = popc64(w);
+  const int inc = wave_incl_scan(cnt);
+  cand_prefix[c * 64 + lane] = (uint16_t)(inc - cnt);
+  if (lane == kWave - 1) {
+    cand_leaf_count[c] = inc;
+    cand_nonempty[c] = inc > 0 ? 1 : 0;
+  }
+}
+
+__global__ void __launch_bounds__(256) k_tile_flags(const int32_t* tile_lower_base, const int32_t* leaf_base,
+                                                    int32_t* tile_nonempty, const int32_t* d_num_tiles) {
+  const i64 t = (i64)blockIdx.x * 256 + threadIdx.x;
+  if (t >= *d_num_tiles) return;
+  tile_nonempty[t] = leaf_base[tile_lower_base[t + 1]] > leaf_base[tile_lower_base[t]] ? 1 : 0;
+}
+
+// Per-grid counts and begins; thread 0 also writes the batch totals.
+__global__ void __launch_bounds__(256) k_grid_counts(const int32_t* grid_tile_begin, const int32_t* tile_lower_base,
+                                                     const int32_t* upper_excl, const int32_t* lower_excl,
+                                                     const int32_t* leaf_base, const int32_t* d_num_tiles,
+                                                     const int32_t* d_num_cands, int32_t B, int32_t* grid_info,
+                                                     int32_t* readback) {
+  const i64 g = (i64)blockIdx.x * 256 + threadIdx.x;
+  if (g == 0) {
+    readback[1] = upper_excl[*d_num_tiles];
+    readback[2] = lower_excl[*d_num_cands];
+    readback[3] = leaf_base[*d_num_cands];
+  }
+  if (g >= B) return;
+  const int32_t tb = grid_tile_begin[g], te = grid_tile_begin[g + 1];
+  const int32_t cb = tile_lower_base[tb], ce = tile_lower_base[te];
+  const int32_t nu = upper_excl[te] - upper_excl[tb];
+  const int32_t n1 = lower_excl[ce] - lower_excl[cb];
+  const int32_t nl = leaf_base[ce] - leaf_base[cb];
+  int32_t* gi = grid_info + g * 6;
+  gi[0] = nu;
+  gi[1] = n1;
+  gi[2] = nl;
+  gi[3] = upper_excl[tb];
+  gi[4] = lower_excl[cb];
+  gi[5] = leaf_base[cb];
+  readback[4 + g * 3 + 0] = nu;
+  readback[4 + g * 3 + 1] = n1;
+  readback[4 + g * 3 + 2] = nl;
+}
+
+void tree_count_cands(TreeScratch& ts, hipStream_t s) {
+  launch("k_lower_count", k_lower_count, ceil_div(ts.cap_cands, 4), 256, s, (const u64*)ts.cand_child,
+         ts.cand_prefix, ts.cand_leaf_count, ts.cand_nonempty, (const int32_t*)ts.d_num_cands);
+  scan_excl_i32(ts.cand_leaf_count, ts.leaf_base, ts.cap_cands, ts.d_num_cands, s);
+  scan_excl_i32(ts.cand_nonempty, ts.lower_excl, ts.cap_cands, ts.d_num_cands, s);
+  launch("k_tile_flags", k_tile_flags, ceil_div(ts.cap_tiles, 256), 256, s, (const int32_t*)ts.tile_lower_base,
+         (const int32_t*)ts.leaf_base, ts.tile_nonempty, (const int32_t*)ts.d_num_tiles);
+  scan_excl_i32(ts.tile_nonempty, ts.upper_excl, ts.cap_tiles, ts.d_num_tiles, s);
+}
+
+void tree_grid_counts(TreeScratch& ts, int32_t B, hipStream_t s) {
+  launch("k_grid_counts", k_grid_counts, ceil_div((i64)B, 256), 256, s, (const int32_t*)ts.grid_tile_begin,
+         (const int32_t*)ts.tile_lower_base, (const int32_t*)ts.upper_excl, (const int32_t*)ts.lower_excl,
+         (const int32_t*)ts.leaf_base, (const int32_t*)ts.d_num_tiles, (const int32_t*)ts.d_num_cands, B,
+         ts.grid_info, ts.readback);
+}
+
+// ------------------------------------------------------------------ node writers
+// One workgroup per non-empty tile: the upper node record and its child mask
+// (candidate bits whose lower turned out empty are cleared).
+__global__ void __launch_bounds__(256) k_write_uppers(const int4* utile, const u64* tile_child,
+                                                      const uint16_t* tile_prefix, const int32_t* tile_lower_base,
+                                                      const int32_t* cand_leaf_count, const int32_t* leaf_base,
+                                                      const int32_t* upper_excl, const int32_t* lower_excl,
+                                                      const int32_t* d_num_tiles, int32_t n_upper, int4* upper_origin,
+                                                      u64* upper_key, int32_t* upper_first, u64* upper_mask) {
+  const i64 t = blockIdx.x;
+  if (t >= *d_num_tiles) return;
+  const int32_t cb = tile_lower_base[t], ce = tile_lower_base[t + 1];
+  if (leaf_base[ce] == leaf_base[cb]) return;  // empty tile, uniform per block
+  const i64 u = upper_excl[t];
+  if (u < 0 || u >= n_upper) return;  // cannot happen for consistent counts
+  if (threadIdx.x == 0) {
+    const int4 T = utile[t];
+    upper_origin[u] = make_int4(T.x * 4096, T.y * 4096, T.z * 4096, T.w);
+    upper_key[u] = ((u64)(T.x + kTileBias) << 40) | ((u64)(T.y + kTileBias) << 20) | (u64)(T.z + kTileBias);
+    upper_first[u] = lower_excl[cb];
+  }
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int w = threadIdx.x * 2 + k;
+    u64 word = tile_child[t * 512 + w];
+    u64 out = 0;
+    int32_t c = cb + tile_prefix[t * 512 + w];
+    while (word) {
+      const int b = __builtin_ctzll(word);
+      if (cand_leaf_count[c] > 0) out |= 1ull << b;
+      word &= word - 1;
+      ++c;
+    }
+    upper_mask[u * 512 + w] = out;
+  }
+}
+
+// One wave per non-empty candidate lower: the lower node record, and one leaf
+// record (origin, grid, parent) per set bit of its leaf mask. leaf_cand[leaf]
+// remembers the candidate lower for the leaf-mask producers.
+__global__ void __launch_bounds__(256) k_write_lowers(const int4* utile, const int4* cand_origin,
+                                                      const u64* cand_child, const uint16_t* cand_prefix,
+                                                      const int32_t* cand_leaf_count, const int32_t* leaf_base,
+                                                      const int32_t* lower_excl, const int32_t* upper_excl,
+                                                      const int32_t* d_num_cands, int32_t n_lower, int32_t n_leaf,
+                                                      int4* lower_origin, int32_t* lower_first, u64* lower_mask,
+                                                      uint16_t* lower_prefix, int4* leaf_origin, int32_t* leaf_parent,
+                                                      int32_t* leaf_cand) {
+  const i64 c = (i64)blockIdx.x * 4 + threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  if (c >= *d_num_cands) return;
+  if (cand_leaf_count[c] == 0) return;  // uniform per wave
+  const i64 lo = lower_excl[c];
+  const int32_t lb = leaf_base[c];
+  if (lo < 0 || lo >= n_lower || lb < 0 || (i64)lb + cand_leaf_count[c] > n_leaf) return;  // consistency guard
+  const int4 co = cand_origin[c];
+  const int32_t g = utile[co.w].w;
+  const u64 word = cand_child[c * 64 + lane];
+  const uint16_t pre = cand_prefix[c * 64 + lane];
+  lower_mask[lo * 64 + lane] = word;
+  lower_prefix[lo * 64 + lane] = pre;
+  if (lane == 0) {
+    lower_origin[lo] = make_int4(co.x, co.y, co.z, upper_excl[co.w]);
+    lower_first[lo] = lb;
+  }
+  u64 rest = word;
+  int32_t idx = lb + pre;
+  while (rest) {
+    const int b = __builtin_ctzll(rest);
+    const int bit = lane * 64 + b;  // (x*16 + y)*16 + z
+    const int px = bit >> 8, py = (bit >> 4) & 15, pz = bit & 15;
+    leaf_origin[idx] = make_int4(co.x + px * 8, co.y + py * 8, co.z + pz * 8, g);
+    leaf_parent[idx] = (int32_t)lo;
+    leaf_cand[idx] = (int32_t)c;
+    rest &= rest - 1;
+    ++idx;
+  }
+}
+
+void tree_write_nodes(TreeScratch& ts, const GridView& out, int32_t* leaf_cand, hipStream_t s) {
+  launch("k_write_uppers", k_write_uppers, ts.cap_tiles, 256, s, (const int4*)ts.utile, (const u64*)ts.tile_child,
+         (const uint16_t*)ts.tile_prefix, (const int32_t*)ts.tile_lower_base, (const int32_t*)ts.cand_leaf_count,
+         (const int32_t*)ts.leaf_base, (const int32_t*)ts.upper_excl, (const int32_t*)ts.lower_excl,
+         (const int32_t*)ts.d_num_tiles, out.n_upper, out.upper_origin, out.upper_key, out.upper_first,
+         out.upper_mask);
+  launch("k_write_lowers", k_write_lowers, ceil_div(ts.cap_cands, 4), 256, s, (const int4*)ts.utile,
+         (const int4*)ts.cand_origin, (const u64*)ts.cand_child, (const uint16_t*)ts.cand_prefix,
+         (const int32_t*)ts.cand_leaf_count, (const int32_t*)ts.leaf_base, (const int32_t*)ts.lower_excl,
+         (const int32_t*)ts.upper_excl, (const int32_t*)ts.d_num_cands, out.n_lower, out.n_leaf, out.lower_origin,
+         out.lower_first,
+         out.lower_mask, out.lower_prefix, out.leaf_origin, out.leaf_parent, leaf_cand);
+}
+
+// ------------------------------------------------------------------ leaf statistics
+// Per leaf: packed prefix word, voxel count, and the per-grid bbox (reduced over
+// the wave when all its leaves belong to one grid, then one atomic per bound).
+__global__ void __launch_bounds__(256) k_leaf_finalize(const int4* leaf_origin, const u64* leaf_mask,
+                                                       u64* leaf_prefix, i64* leaf_vox, int32_t* bbox, int32_t B,
+                                                       i64 n_leaf) {
+  const i64 i = (i64)blockIdx.x * 256 + threadIdx.x;
+  const bool valid = i < n_leaf;
+  int g = -1;
+  int bmin[3] = {INT32_MAX, INT32_MAX, INT32_MAX};
+  int bmax[3] = {INT32_MIN, INT32_MIN, INT32_MIN};
+  if (valid) {
+    const int4 o = leaf_origin[i];
+    g = o.w;
+    u64 W[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) W[k] = leaf_mask[i * 8 + k];
+    u64 packed = 0, run = 0;
+    int xmin = 8, xmax = -1;
+    u64 orw = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (k > 0) packed |= run << (9 * (k - 1));
+      run += (u64)popc64(W[k]);
+      if (W[k]) {
+        xmin = min(xmin, k);
+        xmax = max(xmax, k);
+      }
+      orw |= W[k];
+    }
+    leaf_prefix[i] = packed;
+    leaf_vox[i] = (i64)run;
+    // y extent: non-zero bytes of the OR of all words; z extent: OR of those bytes
+    int ymin = 8, ymax = -1;
+    u64 zor = 0;
+#pragma unroll
+    for (int y = 0; y < 8; ++y) {
+      const u64 byte = (orw >> (8 * y)) & 0xffull;
+      if (byte) {
+        ymin = min(ymin, y);
+        ymax = max(ymax, y);
+      }
+      zor |= byte;
+    }
+    const int zmin = zor ? __builtin_ctzll(zor) : 8;
+    const int zmax = zor ? 63 - __builtin_clzll(zor) : -1;
+    if (run) {
+      bmin[0] = o.x + xmin;
+      bmin[1] = o.y + ymin;
+      bmin[2] = o.z + zmin;
+      bmax[0] = o.x + xmax;
+      bmax[1] = o.y + ymax;
+      bmax[2] = o.z + zmax;
+    }
+  }
+  // wave-uniform grid? (inactive lanes carry g = -1)
+  const int lane = threadIdx.x & (kWave - 1);
+  const u64 active = __ballot(valid);
+  if (active == 0) return;
+  const int first = __builtin_ctzll(active);
+  const int g0 = __shfl(g, first, kWave);
+  const bool same = __ballot(valid && g != g0) == 0;
+  if (same) {
+    int r[6];
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+      r[a] = wave_min_i32(bmin[a]);
+      r[3 + a] = wave_max_i32(bmax[a]);
+    }
+    if (lane == first && g0 >= 0 && g0 < B) {
+#pragma unroll
+      for (int a = 0; a < 3; ++a) {
+        if (r[a] != INT32_MAX) atomicMin(&bbox[a * B + g0], r[a]);
+        if (r[3 + a] != INT32_MIN) atomicMax(&bbox[(3 + a) * B + g0], r[3 + a]);
+      }
+    }
+  } else if (valid && g >= 0 && g < B && bmin[0] != INT32_MAX) {
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+      atomicMin(&bbox[a * B + g], bmin[a]);
+      atomicMax(&bbox[(3 + a) * B + g], bmax[a]);
+    }
+  }
+}
+
+__global__ void __launch_bounds__(256) k_leaf_offsets(const int4* leaf_origin, const i64* vox_excl,
+                                                      const int32_t* grid_info, i64* leaf_offset, i64 n_leaf) {
+  const i64 i = (i64)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n_leaf) return;
+  const int g = leaf_origin[i].w;
+  leaf_offset[i] = vox_excl[i] - vox_excl[grid_info[g * 6 + 5]];
+}
+
+__global__ void __launch_bounds__(256) k_write_headers(const int32_t* grid_info, const i64* vox_excl,
+                                                       const int32_t* bbox, int32_t B, tc_grid_header* hdr) {
+  const i64 g = (i64)blockIdx.x * 256 + threadIdx.x;
+  if (g >= B) return;
+  const int32_t* gi = grid_info + g * 6;
+  tc_grid_header h;
+  h.grid_index = (int32_t)g;
+  h.grid_count = B;
+  h.upper_count = gi[0];
+  h.lower_count = gi[1];
+  h.leaf_count = gi[2];
+  h.upper_begin = gi[3];
+  h.lower_begin = gi[4];
+  h.leaf_begin = gi[5];
+  h.voxel_begin = vox_excl[gi[5]];
+  h.voxel_count = vox_excl[gi[5] + gi[2]] - h.voxel_begin;
+  for (int a = 0; a < 3; ++a) {
+    h.bbox_min[a] = bbox[a * B + g];
+    h.bbox_max[a] = bbox[(3 + a) * B + g];
+  }
+  h.reserved[0] = 0;
+  h.reserved[1] = 0;
+  hdr[g] = h;
+}
+
+void tree_finalize_leaves(const GridView& out, i64* leaf_vox, i64* vox_excl, int32_t* bbox_accum,
+                          const int32_t* grid_info, hipStream_t s) {
+  const i64 L = out.n_leaf;
+  const int32_t B = out.B;
+  fill_i32(bbox_accum, INT32_MAX, 3 * (i64)B, nullptr, 1, s);
+  fill_i32(bbox_accum + 3 * (i64)B, INT32_MIN, 3 * (i64)B, nullptr, 1, s);
+  launch("k_leaf_finalize", k_leaf_finalize, ceil_div(L, 256), 256, s, (const int4*)out.leaf_origin,
+         (const u64*)out.leaf_mask, out.leaf_prefix, leaf_vox, bbox_accum, B, L);
+  scan_excl_i64(leaf_vox, vox_excl, L, nullptr, s);
+  launch("k_leaf_offsets", k_leaf_offsets, ceil_div(L, 256), 256, s, (const int4*)out.leaf_origin,
+         (const i64*)vox_excl, grid_info, out.leaf_offset, L);
+  launch("k_write_headers", k_write_headers, ceil_div((i64)B, 256), 256, s, grid_info, (const i64*)vox_excl,
+         (const int32_t*)bbox_accum, B, out.headers);
+}
+
+// ------------------------------------------------------------------ enumeration
+// One wave per leaf: lane k writes the k-th voxel (in-leaf bit order) of the leaf,
+// so each store instruction covers 64 consecutive rows.
+__global__ void __launch_bounds__(256) k_enumerate(const tc_grid_header* hdr, const int4* leaf_origin,
+                                                   const u64* leaf_mask, const i64* leaf_offset, int32_t* ijk,
+                                                   i64 n_leaf) {
+  const i64 l = (i64)blockIdx.x * 4 + threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  if (l >= n_leaf) return;
+  const int4 o = leaf_origin[l];
+  const i64 base = hdr[o.w].voxel_begin + leaf_offset[l];
+  u64 W[8];
+  int pre[9];
+  pre[0] = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    W[k] = leaf_mask[l * 8 + k];
+    pre[k + 1] = pre[k] + popc64(W[k]);
+  }
+  const int total = pre[8];
+  for (int k = lane; k < total; k += kWave) {
+    int w = 0;
+#pragma unroll
+    for (int q = 1; q < 8; ++q) w += (k >= pre[q]) ? 1 : 0;
+    u64 word = 0;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) word = (q == w) ? W[q] : word;
+    const int b = select_bit(word, k - pre[w]);
+    const i64 row = (base + k) * 3;
+    ijk[row + 0] = o.x + w;
+    ijk[row + 1] = o.y + (b >> 3);
+    ijk[row + 2] = o.z + (b & 7);
+  }
+}
+
+void tree_enumerate(const GridView& v, int32_t* ijk, hipStream_t s) {
+  launch("k_enumerate", k_enumerate, ceil_div((i64)v.n_leaf, 4), 256, s, (const tc_grid_header*)v.headers,
+         (const int4*)v.leaf_origin, (const u64*)v.leaf_mask, (const i64*)v.leaf_offset, ijk, (i64)v.n_leaf);
+}
+
+}  // namespace tc

@@ -37,7 +37,9 @@ def parse():
     ap.add_argument("--config", type=int, default=2, help="workload id (2: B=16 shells at res 64)")
     ap.add_argument("--roofline-kernel", default="k_enumerate")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--large", action="store_true", help="also time the 64-shell res-512 + cube batch")
+    ap.add_argument("--no-large", action="store_true", help="skip the 64-shell res-512 + cube batch")
+    ap.add_argument("--large-only", action="store_true",
+                    help="only the 64-shell res-512 + cube batch (prints its record), for profiling")
     return ap.parse_args()
 
 
@@ -53,15 +55,74 @@ def run_step(binding, src, outs=None):
     return total
 
 
-def kernel_bytes(name, leaves, voxels):
-    """Algorithmic bytes of one launch of the reported kernel.
-
-    k_enumerate reads per leaf its origin (16 B), mask (64 B), voxel offset
-    (8 B) and grid header voxel base (8 B), and writes 12 B per voxel.
-    """
+# Algorithmic bytes of one launch of each measured kernel: what the step itself
+# must move, not what the kernel happens to move.
+#   k_leaf_mark     reads every source leaf once: origin 16 B + parent 4 B + mask 64 B
+#   k_leaf_gather   reads every output leaf's origin 16 B + candidate id 4 B, every
+#                   source mask once (64 B), writes every output mask (64 B)
+#   k_leaf_finalize reads origin + mask (80 B), writes prefix + voxel count (16 B)
+#   k_enumerate     reads origin, mask, offset and grid base (96 B per leaf),
+#                   writes 12 B per voxel
+def kernel_bytes(name, src_leaves, leaves, voxels):
+    if name == "k_leaf_mark":
+        return 84 * src_leaves
+    if name == "k_leaf_gather":
+        return 84 * leaves + 64 * src_leaves
+    if name == "k_leaf_finalize":
+        return 96 * leaves
     if name == "k_enumerate":
         return 96 * leaves + 12 * voxels
     raise ValueError(name)
+
+
+LARGE_KERNELS = ["k_leaf_mark", "k_leaf_gather", "k_leaf_finalize", "k_enumerate"]
+
+
+def measure_large(binding, torch, np, synth):
+    """64 shells at res 512 + 8 solid 128^3 cubes: per-op pass / enumeration time
+    and per-kernel HIP-event timing against the HBM peak."""
+    ijk, off = synth.make_config(5)
+    src = binding.tc_batch_from_ijk(torch.from_numpy(ijk).cuda(), off)
+    del ijk
+    torch.cuda.synchronize()
+    res = {"workload": synth.CONFIG_NAMES[5], "grids": int(len(off) - 1), "input_voxels": int(off[-1]),
+           "input_leaves": int(src.leaf_count), "ops": {}}
+    for op, f in [("coarsen", 2), ("refine", 2), ("dilate", 1)]:
+        out = binding.tc_build_batched_topology(src, op, f)  # warm-up
+        binding.tc_enumerate_ijk(out)
+        del out
+        torch.cuda.synchronize()
+        binding.tc_profile_enable(",".join(LARGE_KERNELS))
+        pass_ms, enum_ms = [], []
+        for _ in range(3):
+            torch.cuda.synchronize()
+            a = time.perf_counter()
+            out = binding.tc_build_batched_topology(src, op, f)
+            torch.cuda.synchronize()
+            b = time.perf_counter()
+            e = binding.tc_enumerate_ijk(out)
+            torch.cuda.synchronize()
+            c = time.perf_counter()
+            pass_ms.append((b - a) * 1e3)
+            enum_ms.append((c - b) * 1e3)
+            V = int(e.shape[0])
+            L = int(out.leaf_count)
+            del e, out
+        kern = {}
+        for k in LARGE_KERNELS:
+            ms, n = binding.tc_profile_read(k)
+            if n:
+                avg = ms / n
+                byts = kernel_bytes(k, int(src.leaf_count), L, V)
+                gbs = byts / (avg * 1e-3) / 1e9
+                kern[k] = {"avg_ms": avg, "launches": n, "algorithmic_bytes": byts, "achieved_GBs": gbs,
+                           "frac_of_peak": gbs / HBM_PEAK_GBS}
+        binding.tc_profile_disable()
+        pm = float(np.median(pass_ms))
+        res["ops"][f"{op}x{f}"] = {"ms_pass_median": pm, "ms_enumerate_median": float(np.median(enum_ms)),
+                                   "output_voxels": V, "output_leaves": L,
+                                   "output_voxels_per_s_pass": V / (pm * 1e-3), "kernels": kern}
+    return res
 
 
 def main():
@@ -75,6 +136,9 @@ def main():
     from topology_construction_amd import binding, synth
 
     torch.cuda.set_device(0)
+    if args.large_only:
+        print(json.dumps({"large": measure_large(binding, torch, np, synth)}), flush=True)
+        return
     ijk, off = synth.make_config(args.config)
     src = binding.tc_batch_from_ijk(torch.from_numpy(ijk).cuda(), off)
     torch.cuda.synchronize()
@@ -93,7 +157,7 @@ def main():
         voxels += run_step(binding, src)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    k_ms, k_n = binding.tc_profile_read()
+    k_ms, k_n = binding.tc_profile_read(args.roofline_kernel)
     binding.tc_profile_disable()
     elapsed = t1 - t0
     ms_step = elapsed * 1e3 / args.steps
@@ -117,7 +181,7 @@ def main():
                             "ms_enumerate_median": float(np.median(enum_ms)),
                             "output_voxels": int(ijk_out.shape[0]), "output_leaves": int(out.leaf_count)}
 
-    bytes_per_step = sum(kernel_bytes(args.roofline_kernel, L, V) for (_, _, L, V) in facts)
+    bytes_per_step = sum(kernel_bytes(args.roofline_kernel, int(src.leaf_count), L, V) for (_, _, L, V) in facts)
     launches_per_step = len(facts)
     avg_ms = k_ms / max(k_n, 1)
     avg_bytes = bytes_per_step / launches_per_step
@@ -130,13 +194,20 @@ def main():
     if not args.no_cpu_baseline:
         import oracle
         t = time.perf_counter()
-        cv = 0
-        for op, f in STEP_OPS:
-            r = oracle.run(op, f, ijk, off, fields=["headers"])
-            cv += int(r["headers"][:, 8].sum())
+        cv, reps = 0, 0
+        while True:  # whole steps of the CPU oracle until at least 10 s have passed
+            for op, f in STEP_OPS:
+                r = oracle.run(op, f, ijk, off, fields=["headers"])
+                cv += int(r["headers"][:, 8].sum())
+            reps += 1
+            if time.perf_counter() - t >= 10.0 or reps >= 50:
+                break
         dt = time.perf_counter() - t
         cpu = {"value": cv / dt, "unit": "voxels/s", "cores": 1, "kind": "oracle",
-               "sample": f"one full step of workload {args.config} (all members, {len(STEP_OPS)} ops), {dt:.1f} s"}
+               "sample": f"{reps} full step(s) of workload {args.config} (all members, {len(STEP_OPS)} ops), "
+                         f"{dt:.1f} s on one host thread"}
+
+    large = None if args.no_large else measure_large(binding, torch, np, synth)
 
     rec = {
         "metric": METRIC, "value": voxels / elapsed, "unit": "voxels/s", "n_gpus": 1, "steps": args.steps,
@@ -144,7 +215,7 @@ def main():
         "vs_baseline": None, "dtype": "int32", "data": "synthetic",
         "config": {"workload": synth.CONFIG_NAMES[args.config], "grids": int(len(off) - 1),
                    "input_voxels": int(off[-1]), "ops": [f"{o}x{f}" for o, f in STEP_OPS]},
-        "roofline": roofline, "cpu_baseline": cpu, "ops": ops,
+        "roofline": roofline, "cpu_baseline": cpu, "ops": ops, "large": large,
     }
     print(json.dumps(rec), flush=True)
 

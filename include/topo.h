@@ -202,13 +202,14 @@ tc_status tc_enumerate_ijk(const tc_grid_batch* batch, int32_t* d_ijk_out, int64
  * stream-ordered on its creation stream) and the handle. NULL is ignored. */
 void tc_batch_free(tc_grid_batch* batch);
 
-/* Kernel timing for measurement: while enabled, every launch of the kernel whose
- * name equals `kernel_name` is bracketed by HIP events on its stream.
- * tc_profile_read() waits for those events and returns the summed milliseconds
- * and launch count since tc_profile_enable(). Names are the __global__ function
- * names (e.g. "k_leaf_gather"). Not thread-safe against concurrent passes. */
-tc_status tc_profile_enable(const char* kernel_name);
-tc_status tc_profile_read(double* h_total_ms, int64_t* h_launches);
+/* Kernel timing for measurement: while enabled, every launch of a kernel whose
+ * name is in `kernel_names` (comma-separated __global__ function names, e.g.
+ * "k_leaf_gather,k_enumerate"; "*" selects every kernel) is bracketed by HIP
+ * events on the stream it is launched on. tc_profile_read() waits for those
+ * events and returns the summed milliseconds and launch count of one kernel
+ * since tc_profile_enable(). Not thread-safe against concurrent passes. */
+tc_status tc_profile_enable(const char* kernel_names);
+tc_status tc_profile_read(const char* kernel_name, double* h_total_ms, int64_t* h_launches);
 tc_status tc_profile_disable(void);
 
 #ifdef __cplusplus

@@ -86,9 +86,10 @@ def test_null_handles_are_rejected(lib):
 
 def test_profiling_state_machine_without_launches(lib):
     assert lib.tc_profile_enable(None) == binding.TC_ERR_INVALID_ARG
-    assert lib.tc_profile_enable(b"k_leaf_gather") == 0
+    assert lib.tc_profile_enable(b"k_leaf_gather, k_enumerate") == 0
     ms, n = ctypes.c_double(), ctypes.c_int64()
-    assert lib.tc_profile_read(ctypes.byref(ms), ctypes.byref(n)) == 0
+    assert lib.tc_profile_read(b"k_enumerate", ctypes.byref(ms), ctypes.byref(n)) == 0
+    assert lib.tc_profile_read(None, ctypes.byref(ms), ctypes.byref(n)) == binding.TC_ERR_INVALID_ARG
     assert n.value == 0 and ms.value == 0.0
     assert lib.tc_profile_disable() == 0
 

@@ -1,0 +1,98 @@
+"""Full-size workload (64 shells at resolution 512 + 8 solid 128^3 cubes at random
+int32 offsets), in the launch configuration the benchmark times.
+
+The oracle cannot hold the whole output (the refine output alone is ~370M
+voxels), so parity is checked on sampled members computed one by one by the
+oracle, and everywhere else through properties that hold at any size:
+per-grid voxel counts of refine = 8x the source; coarsen(refine(g)) == g in
+every array; a dilated solid cube is the solid cube grown by one voxel; the
+enumeration is strictly increasing in canonical order inside every grid.
+Sources: PR page "Batched leaf-mask topology construction for generated conv
+grids", section 1 (refine/coarsen semantics, canonical order), section 2 (box
+dilation), Test plan (refine->coarsen round trip).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from tests.gpu_util import assert_same, gpu_fields, member_slice
+from topology_construction_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+SHELLS = [0, 31, 63]   # sampled shell members
+CUBES = [64, 71]       # sampled cube members
+
+
+@pytest.fixture(scope="module")
+def big():
+    import torch
+    from topology_construction_amd import binding
+    print("[large] generating 64 shells res512 + 8 cubes", flush=True)
+    ijk, off = synth.make_config(5)
+    src = binding.tc_batch_from_ijk(torch.from_numpy(ijk).cuda(), off)
+    torch.cuda.synchronize()
+    return ijk, off, src
+
+
+def _canonical_increasing(ijk: np.ndarray) -> bool:
+    """Rows strictly increasing in (root tile, upper child, lower child, leaf bit)."""
+    if ijk.shape[0] < 2:
+        return True
+    c = ijk.astype(np.int64)
+    t = c >> 12
+    root = ((t[:, 0] + (1 << 19)) << 40) | ((t[:, 1] + (1 << 19)) << 20) | (t[:, 2] + (1 << 19))
+    up = ((((c >> 7) & 31)[:, 0] * 32 + ((c >> 7) & 31)[:, 1]) * 32 + ((c >> 7) & 31)[:, 2])
+    lo = ((((c >> 3) & 15)[:, 0] * 16 + ((c >> 3) & 15)[:, 1]) * 16 + ((c >> 3) & 15)[:, 2])
+    bit = (c & 7)[:, 0] * 64 + (c & 7)[:, 1] * 8 + (c & 7)[:, 2]
+    node = (up << 21) | (lo << 9) | bit
+    d_root = np.diff(root)
+    d_node = np.diff(node)
+    return bool(np.all((d_root > 0) | ((d_root == 0) & (d_node > 0))))
+
+
+def _member_input(ijk, off, g):
+    return ijk[off[g]:off[g + 1]], np.array([0, off[g + 1] - off[g]], np.int64)
+
+
+@pytest.mark.parametrize("op,f", [("coarsen", 2), ("refine", 2), ("dilate", 1)])
+def test_large_sampled_members_and_properties(big, op, f):
+    from topology_construction_amd import binding
+    ijk, off, src = big
+    print(f"[large] {op} x{f}", flush=True)
+    out = binding.tc_build_batched_topology(src, op, f)
+    fo = gpu_fields(out)
+    h = fo["headers"]
+    B = len(off) - 1
+    assert np.array_equal(h[:, 0], np.arange(B)) and np.all(h[:, 1] == B)
+    # sampled members against the oracle, computed one by one
+    for g in SHELLS + (CUBES if op != "dilate" else []):
+        mi, mo = _member_input(ijk, off, g)
+        print(f"[large]   oracle member {g} ({mi.shape[0]} voxels)", flush=True)
+        ref = oracle.run(op, f, mi, mo)
+        assert_same(member_slice(fo, g), ref, f"large {op} member {g}")
+    # properties at full size
+    src_counts = np.diff(off)
+    if op == "refine":
+        assert np.array_equal(h[:, 8], 8 * src_counts)
+    if op == "dilate":
+        for g in CUBES:  # a dilated solid 128^3 cube is the 130^3 cube one voxel lower
+            lo = ijk[off[g]].astype(np.int64) - 1
+            assert h[g, 8] == 130 ** 3
+            assert np.array_equal(h[g, 10:13], lo) and np.array_equal(h[g, 13:16], lo + 129)
+    for g in range(B):
+        rows = fo["ijk"][h[g, 9]:h[g, 9] + h[g, 8]]
+        assert _canonical_increasing(rows), f"{op}: member {g} not in canonical order"
+        if h[g, 8]:
+            assert np.array_equal(rows.min(0), h[g, 10:13]) and np.array_equal(rows.max(0), h[g, 13:16])
+
+
+def test_large_refine_coarsen_roundtrip(big):
+    from topology_construction_amd import binding
+    ijk, off, src = big
+    fine = binding.tc_build_batched_topology(src, "refine", 2)
+    back = binding.tc_build_batched_topology(fine, "coarsen", 2)
+    del fine
+    fa, fb = gpu_fields(src), gpu_fields(back)
+    for k in fa:
+        assert np.array_equal(fa[k], fb[k]), k

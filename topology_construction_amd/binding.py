@@ -127,7 +127,7 @@ def load_library(path: str = LIB_PATH):
         lib.tc_profile_enable.restype = ctypes.c_int
         lib.tc_profile_enable.argtypes = [ctypes.c_char_p]
         lib.tc_profile_read.restype = ctypes.c_int
-        lib.tc_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
+        lib.tc_profile_read.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
         lib.tc_profile_disable.restype = ctypes.c_int
         if lib.tc_abi_version() != 1:
             raise ImportError("libtopo.so ABI version mismatch")
@@ -271,14 +271,16 @@ def tc_batch_read_headers(batch: GridBatch, stream=None) -> np.ndarray:
     return batch.headers(stream)
 
 
-def tc_profile_enable(kernel_name: str):
-    _check(load_library().tc_profile_enable(kernel_name.encode()))
+def tc_profile_enable(kernel_names: str):
+    """Time launches of the named kernels (comma-separated, or "*") with HIP events."""
+    _check(load_library().tc_profile_enable(kernel_names.encode()))
 
 
-def tc_profile_read():
+def tc_profile_read(kernel_name: str):
+    """(total ms, launches) of one kernel since tc_profile_enable."""
     ms = ctypes.c_double()
     n = ctypes.c_int64()
-    _check(load_library().tc_profile_read(ctypes.byref(ms), ctypes.byref(n)))
+    _check(load_library().tc_profile_read(kernel_name.encode(), ctypes.byref(ms), ctypes.byref(n)))
     return float(ms.value), int(n.value)
 
 

@@ -267,18 +267,18 @@ void tc_batch_free(tc_grid_batch* b) {
   }
 }
 
-tc_status tc_profile_enable(const char* kernel_name) {
-  if (!kernel_name) return fail(TC_ERR_INVALID_ARG, "kernel_name is NULL");
+tc_status tc_profile_enable(const char* kernel_names) {
+  if (!kernel_names) return fail(TC_ERR_INVALID_ARG, "kernel_names is NULL");
   return guarded([&]() {
-    tc::prof_enable(kernel_name);
+    tc::prof_enable(kernel_names);
     return TC_OK;
   });
 }
 
-tc_status tc_profile_read(double* h_total_ms, int64_t* h_launches) {
-  if (!h_total_ms || !h_launches) return fail(TC_ERR_INVALID_ARG, "NULL argument");
+tc_status tc_profile_read(const char* kernel_name, double* h_total_ms, int64_t* h_launches) {
+  if (!kernel_name || !h_total_ms || !h_launches) return fail(TC_ERR_INVALID_ARG, "NULL argument");
   return guarded([&]() {
-    tc::prof_read(h_total_ms, h_launches);
+    tc::prof_read(kernel_name, h_total_ms, h_launches);
     return TC_OK;
   });
 }

@@ -252,7 +252,7 @@ struct OutAlloc {
 };
 
 void prof_enable(const char* name);
-void prof_read(double* ms, int64_t* n);
+void prof_read(const char* name, double* ms, int64_t* n);
 void prof_disable();
 
 }  // namespace tc

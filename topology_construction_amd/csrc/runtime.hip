@@ -78,18 +78,47 @@ void* pinned_staging(size_t bytes) {
 
 // ------------------------------------------------------------------ profiling
 namespace {
+struct Timed {
+  std::string name;
+  hipEvent_t start, stop;
+};
 struct Prof {
   std::mutex mu;
   bool on = false;
-  std::string name;
-  std::vector<std::pair<hipEvent_t, hipEvent_t>> pending;
+  bool all = false;
+  std::vector<std::string> names;
+  std::vector<Timed> pending;
   hipEvent_t open_start = nullptr;
-  double total_ms = 0;
-  int64_t launches = 0;
+  std::vector<std::pair<std::string, std::pair<double, int64_t>>> totals;
+  bool wants(const char* n) const {
+    if (all) return true;
+    for (const auto& x : names)
+      if (x == n) return true;
+    return false;
+  }
 };
 Prof& prof() {
   static Prof* p = new Prof();
   return *p;
+}
+
+void prof_drain(Prof& p) {
+  for (auto& t : p.pending) {
+    hip_check(hipEventSynchronize(t.stop), "hipEventSynchronize");
+    float ms = 0;
+    hip_check(hipEventElapsedTime(&ms, t.start, t.stop), "hipEventElapsedTime");
+    bool found = false;
+    for (auto& kv : p.totals)
+      if (kv.first == t.name) {
+        kv.second.first += ms;
+        kv.second.second += 1;
+        found = true;
+      }
+    if (!found) p.totals.push_back({t.name, {(double)ms, 1}});
+    (void)hipEventDestroy(t.start);
+    (void)hipEventDestroy(t.stop);
+  }
+  p.pending.clear();
 }
 }  // namespace
 
@@ -97,7 +126,7 @@ void prof_before(const char* name, hipStream_t s) {
   Prof& p = prof();
   if (!p.on) return;
   std::lock_guard<std::mutex> lk(p.mu);
-  if (!p.on || p.name != name) return;
+  if (!p.on || !p.wants(name)) return;
   hipEvent_t e;
   hip_check(hipEventCreate(&e), "hipEventCreate");
   hip_check(hipEventRecord(e, s), "hipEventRecord");
@@ -108,47 +137,49 @@ void prof_after(const char* name, hipStream_t s) {
   Prof& p = prof();
   if (!p.on) return;
   std::lock_guard<std::mutex> lk(p.mu);
-  if (!p.on || p.name != name || !p.open_start) return;
+  if (!p.on || !p.open_start || !p.wants(name)) return;
   hipEvent_t e;
   hip_check(hipEventCreate(&e), "hipEventCreate");
   hip_check(hipEventRecord(e, s), "hipEventRecord");
-  p.pending.emplace_back(p.open_start, e);
+  p.pending.push_back({name, p.open_start, e});
   p.open_start = nullptr;
 }
 
-static void prof_drain(Prof& p) {
-  for (auto& pr : p.pending) {
-    hip_check(hipEventSynchronize(pr.second), "hipEventSynchronize");
-    float ms = 0;
-    hip_check(hipEventElapsedTime(&ms, pr.first, pr.second), "hipEventElapsedTime");
-    p.total_ms += ms;
-    p.launches += 1;
-    (void)hipEventDestroy(pr.first);
-    (void)hipEventDestroy(pr.second);
-  }
-  p.pending.clear();
-}
-
-void prof_enable(const char* name) {
+void prof_enable(const char* names) {
   Prof& p = prof();
   std::lock_guard<std::mutex> lk(p.mu);
-  for (auto& pr : p.pending) {
-    (void)hipEventDestroy(pr.first);
-    (void)hipEventDestroy(pr.second);
+  for (auto& t : p.pending) {
+    (void)hipEventDestroy(t.start);
+    (void)hipEventDestroy(t.stop);
   }
   p.pending.clear();
-  p.name = name;
-  p.total_ms = 0;
-  p.launches = 0;
+  p.totals.clear();
+  p.names.clear();
+  p.all = std::strcmp(names, "*") == 0;
+  std::string cur;
+  for (const char* c = names;; ++c) {
+    if (*c == ',' || *c == 0) {
+      if (!cur.empty()) p.names.push_back(cur);
+      cur.clear();
+      if (*c == 0) break;
+    } else if (*c != ' ') {
+      cur.push_back(*c);
+    }
+  }
   p.on = true;
 }
 
-void prof_read(double* ms, int64_t* n) {
+void prof_read(const char* name, double* ms, int64_t* n) {
   Prof& p = prof();
   std::lock_guard<std::mutex> lk(p.mu);
   prof_drain(p);
-  *ms = p.total_ms;
-  *n = p.launches;
+  *ms = 0;
+  *n = 0;
+  for (auto& kv : p.totals)
+    if (kv.first == name) {
+      *ms = kv.second.first;
+      *n = kv.second.second;
+    }
 }
 
 void prof_disable() {

@@ -70,4 +70,47 @@ __device__ __forceinline__ int wave_max_i32(int v) {
   return v;
 }
 
+// Statistics of a final leaf mask W (bit n = x*64 + y*8 + z):
+//   prefix  seven 9-bit fields, field w-1 = voxels in words < w
+//   count   voxels in the leaf
+//   box     local bbox packed as xmin | xmax<<3 | ymin<<6 | ymax<<9 | zmin<<12 |
+//           zmax<<15 (3 bits each); kEmptyBox for an empty mask
+constexpr uint32_t kEmptyBox = 0xffffffffu;
+
+__device__ __forceinline__ void leaf_stats(const uint64_t W[8], uint64_t& prefix, int& count, uint32_t& box) {
+  uint64_t packed = 0, run = 0, orw = 0;
+  int xmin = 8, xmax = -1;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    if (k > 0) packed |= run << (9 * (k - 1));
+    run += (uint64_t)__popcll(W[k]);
+    if (W[k]) {
+      xmin = min(xmin, k);
+      xmax = max(xmax, k);
+    }
+    orw |= W[k];
+  }
+  prefix = packed;
+  count = (int)run;
+  if (!orw) {
+    box = kEmptyBox;
+    return;
+  }
+  // y extent: non-zero bytes of the OR of all words; z extent: OR of those bytes
+  int ymin = 8, ymax = -1;
+  uint64_t zor = 0;
+#pragma unroll
+  for (int y = 0; y < 8; ++y) {
+    const uint64_t byte = (orw >> (8 * y)) & 0xffull;
+    if (byte) {
+      ymin = min(ymin, y);
+      ymax = max(ymax, y);
+    }
+    zor |= byte;
+  }
+  const int zmin = __builtin_ctzll(zor);
+  const int zmax = 63 - __builtin_clzll(zor);
+  box = (uint32_t)(xmin | (xmax << 3) | (ymin << 6) | (ymax << 9) | (zmin << 12) | (zmax << 15));
+}
+
 }  // namespace tc

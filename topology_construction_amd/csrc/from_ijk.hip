@@ -307,16 +307,18 @@ tc_grid_batch* build_from_ijk(const int32_t* d_ijk, const int64_t* h_off, int32_
     Arena post(s);
     const size_t o_lc = post.reserve(4 * L);
     const size_t o_lv = post.reserve(8 * L);
+    const size_t o_box = post.reserve(4 * L);
     const size_t o_vx = post.reserve(8 * (L + 1));
-    const size_t o_bb = post.reserve(4 * 6 * (i64)B);
+    const size_t o_bb = post.reserve(4 * 6 * (i64)B * bbox_replicas(B));
     post.commit();
     tree_write_nodes(ts, ov, post.at<int32_t>(o_lc), s);
     fill_u64(ov.leaf_mask, 0, 8 * L, nullptr, 1, s);
     launch("k_voxel_leaf", k_voxel_leaf, ceil_div(N, 256), 256, s, d_ijk, (const int32_t*)vcand, N,
            (const u64*)ts.cand_child, (const uint16_t*)ts.cand_prefix, (const int32_t*)ts.leaf_base, L,
            ov.leaf_mask);
-    tree_finalize_leaves(ov, post.at<i64>(o_lv), post.at<i64>(o_vx), post.at<int32_t>(o_bb),
-                         (const int32_t*)ts.grid_info, s);
+    tree_leaf_stats(ov, post.at<i64>(o_lv), post.at<uint32_t>(o_box), s);
+    tree_finalize_leaves(ov, post.at<i64>(o_lv), post.at<uint32_t>(o_box), post.at<i64>(o_vx),
+                         post.at<int32_t>(o_bb), (const int32_t*)ts.grid_info, s);
   } catch (...) {
     free_batch(out);
     throw;

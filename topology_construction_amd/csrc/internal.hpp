@@ -241,8 +241,10 @@ void tree_grid_counts(TreeScratch& t, int32_t B, hipStream_t s);
 void tree_rank_tiles(TreeScratch& t, hipStream_t s);            // prefix per tile + scan -> cand numbering
 void tree_count_cands(TreeScratch& t, hipStream_t s);           // leaf counts per cand + scans + tile flags + grid counts
 void tree_write_nodes(TreeScratch& t, const GridView& out, int32_t* leaf_cand, hipStream_t s);
-void tree_finalize_leaves(const GridView& out, i64* leaf_vox, i64* vox_excl, int32_t* bbox_accum,
-                          const int32_t* grid_info, hipStream_t s);
+void tree_leaf_stats(const GridView& out, i64* leaf_vox, uint32_t* leaf_box, hipStream_t s);
+int32_t bbox_replicas(int32_t B);  // replicas of the per-grid bbox accumulators
+void tree_finalize_leaves(const GridView& out, const i64* leaf_vox, const uint32_t* leaf_box, i64* vox_excl,
+                          int32_t* bbox_accum, const int32_t* grid_info, hipStream_t s);
 void tree_enumerate(const GridView& v, int32_t* ijk, hipStream_t s);
 
 // Allocation of the single output buffer of a batch.

@@ -244,64 +244,85 @@ __device__ __forceinline__ bool subblock_nonempty(const u64 W[8], const I3& q) {
   return (xs & ym & zm) != 0;
 }
 
-__device__ __forceinline__ void mark_leaf(u64* cand_child, int32_t c, i64 px, i64 py, i64 pz) {
+// One workgroup per source lower node: every leaf of that lower marks its
+// non-empty target leaves in LDS copies of the (at most m) target lowers' 16^3
+// masks, then the block flushes whole 64-bit words to the candidate lowers. For
+// refine each target lower has exactly one source lower, so the flush is a plain
+// store of all 64 words (no zero-fill needed); the other ops OR their non-zero
+// words with device-scope atomics, far fewer than one per target leaf.
+__device__ __forceinline__ void lds_mark(unsigned long long* s_mask, int j, i64 px, i64 py, i64 pz) {
   const int bit = (int)((px * 16 + py) * 16 + pz);
-  atomicOr((unsigned long long*)&cand_child[(i64)c * 64 + (bit >> 6)], 1ull << (bit & 63));
+  atomicOr(&s_mask[j * 64 + (bit >> 6)], 1ull << (bit & 63));
 }
 
-__global__ void __launch_bounds__(256) k_leaf_mark(const int4* leaf_origin, const int32_t* leaf_parent,
-                                                   const u64* leaf_mask, i64 n, int op, int m,
-                                                   const int32_t* lower_nbr, const int32_t* d_num_cands,
-                                                   u64* cand_child, int32_t* flags) {
-  const i64 i = (i64)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
+__global__ void __launch_bounds__(256) k_leaf_mark_lower(const int4* leaf_origin, const u64* leaf_mask,
+                                                         const int32_t* lower_first, const u64* lower_mask,
+                                                         const uint16_t* lower_prefix, int op, int m,
+                                                         const int32_t* lower_nbr, const int32_t* d_num_cands,
+                                                         u64* cand_child, int32_t* flags) {
+  __shared__ unsigned long long s_mask[27 * 64];
+  const i64 l = blockIdx.x;
+  for (int k = threadIdx.x; k < m * 64; k += 256) s_mask[k] = 0;
+  __syncthreads();
+  const i64 first = lower_first[l];
+  const int count = lower_prefix[l * 64 + 63] + popc64(lower_mask[l * 64 + 63]);
+  for (int k = threadIdx.x; k < count; k += 256) {
+    const i64 i = first + k;
+    const int4 o = leaf_origin[i];
+    u64 W[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) W[q] = leaf_mask[i * 8 + q];
+    const i64 mx = o.x >> 3, my = o.y >> 3, mz = o.z >> 3;  // leaf coordinates
+    const i64 lx = mx & 15, ly = my & 15, lz = mz & 15;     // position inside the lower
+    if (op == TC_OP_REFINE) {
+      const int j = octant_index(lx >> 3, ly >> 3, lz >> 3);  // all children share one target lower
+#pragma unroll
+      for (int qx = 0; qx < 2; ++qx) {
+        u64 word = 0;
+        const i64 x = (2 * lx + qx) & 15;
+#pragma unroll
+        for (int qy = 0; qy < 2; ++qy)
+#pragma unroll
+          for (int qz = 0; qz < 2; ++qz) {
+            const I3 q{qx, qy, qz};
+            if (!subblock_nonempty(W, q)) continue;
+            if (!leaf_ok(2 * mx + qx) || !leaf_ok(2 * my + qy) || !leaf_ok(2 * mz + qz)) {
+              set_flag(flags, kFlagOverflow);
+              continue;
+            }
+            word |= 1ull << ((((2 * ly + qy) & 3) * 16) + ((2 * lz + qz) & 15));
+          }
+        // children with this qx share the word x*4 + (y >> 2) of the target mask
+        if (word) atomicOr(&s_mask[j * 64 + x * 4 + (((2 * ly) & 15) >> 2)], word);
+      }
+    } else if (op == TC_OP_COARSEN) {
+      lds_mark(s_mask, 0, (mx >> 1) & 15, (my >> 1) & 15, (mz >> 1) & 15);
+    } else {
+      for (int j = 0; j < m; ++j) {
+        const I3 t = box_offset(j, op);
+        if (!spill_nonempty(W, t)) continue;
+        if (!leaf_ok(mx + t.x) || !leaf_ok(my + t.y) || !leaf_ok(mz + t.z)) {
+          set_flag(flags, kFlagOverflow);
+          continue;
+        }
+        const i64 px = lx + t.x, py = ly + t.y, pz = lz + t.z;  // -1 .. 16
+        lds_mark(s_mask, box_index(px >> 4, py >> 4, pz >> 4, op), px & 15, py & 15, pz & 15);
+      }
+    }
+  }
+  __syncthreads();
   const int32_t ncand = *d_num_cands;
-  const int4 o = leaf_origin[i];
-  const i64 l = leaf_parent[i];
-  u64 W[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) W[k] = leaf_mask[i * 8 + k];
-  const i64 mx = o.x >> 3, my = o.y >> 3, mz = o.z >> 3;  // leaf coordinates
-  const i64 lx = mx & 15, ly = my & 15, lz = mz & 15;     // position inside the lower
-  if (op == TC_OP_REFINE) {
-    const int32_t c = lower_nbr[l * 8 + octant_index(lx >> 3, ly >> 3, lz >> 3)];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const I3 q = octant(j);
-      if (!subblock_nonempty(W, q)) continue;
-      if (!leaf_ok(2 * mx + q.x) || !leaf_ok(2 * my + q.y) || !leaf_ok(2 * mz + q.z)) {
-        set_flag(flags, kFlagOverflow);
-        continue;
-      }
-      if (c < 0 || c >= ncand) {
-        set_flag(flags, kFlagInternal);
-        continue;
-      }
-      mark_leaf(cand_child, c, (2 * lx + q.x) & 15, (2 * ly + q.y) & 15, (2 * lz + q.z) & 15);
-    }
-  } else if (op == TC_OP_COARSEN) {
-    const int32_t c = lower_nbr[l];
+  for (int k = threadIdx.x; k < m * 64; k += 256) {
+    const int j = k >> 6, w = k & 63;
+    const u64 word = s_mask[k];
+    if (op != TC_OP_REFINE && !word) continue;
+    const int32_t c = lower_nbr[l * m + j];
     if (c < 0 || c >= ncand) {
-      set_flag(flags, kFlagInternal);
-      return;
+      if (word) set_flag(flags, kFlagInternal);  // a marked target must have a candidate
+      continue;
     }
-    mark_leaf(cand_child, c, (mx >> 1) & 15, (my >> 1) & 15, (mz >> 1) & 15);
-  } else {
-    for (int j = 0; j < m; ++j) {
-      const I3 t = box_offset(j, op);
-      if (!spill_nonempty(W, t)) continue;
-      if (!leaf_ok(mx + t.x) || !leaf_ok(my + t.y) || !leaf_ok(mz + t.z)) {
-        set_flag(flags, kFlagOverflow);
-        continue;
-      }
-      const i64 px = lx + t.x, py = ly + t.y, pz = lz + t.z;  // -1 .. 16
-      const int32_t c = lower_nbr[l * m + box_index(px >> 4, py >> 4, pz >> 4, op)];
-      if (c < 0 || c >= ncand) {
-        set_flag(flags, kFlagInternal);
-        continue;
-      }
-      mark_leaf(cand_child, c, px & 15, py & 15, pz & 15);
-    }
+    if (op == TC_OP_REFINE) cand_child[(i64)c * 64 + w] = word;
+    else atomicOr((unsigned long long*)&cand_child[(i64)c * 64 + w], word);
   }
 }
 
@@ -404,44 +425,58 @@ __device__ __forceinline__ void box_contrib(u64 out[8], const u64 W[8], const I3
   }
 }
 
+// Output leaf masks by gathering from the source leaves that feed them: the
+// unique parent (refine), the 8 children (coarsen) or the neighbours at the op's
+// box offsets (dilate, pads). Box ops and coarsen split the sources of one
+// output leaf over 4 adjacent lanes and OR the partial masks with shuffles, so
+// the dependent lookups run in parallel. Also writes the leaf's prefix word,
+// voxel count and packed local bbox.
 __global__ void __launch_bounds__(256) k_leaf_gather(const int4* out_origin, const int32_t* leaf_cand, i64 n,
                                                      int op, int m, int lo, int hi, const int32_t* cand_src,
                                                      const u64* src_lower_mask, const uint16_t* src_lower_prefix,
                                                      const int32_t* src_lower_first, const u64* src_leaf_mask,
                                                      int32_t n_src_lower, int32_t n_src_leaf,
-                                                     const int32_t* d_num_cands, u64* out_mask, int32_t* flags) {
-  const i64 i = (i64)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
-  const int4 o = out_origin[i];
-  const i64 c = leaf_cand[i];
-  if (c < 0 || c >= *d_num_cands) {
-    set_flag(flags, kFlagInternal);
-    return;
-  }
-  const i64 ax = o.x >> 3, ay = o.y >> 3, az = o.z >> 3;  // output leaf coordinates
-  const i64 lx = ax & 15, ly = ay & 15, lz = az & 15;
+                                                     const int32_t* d_num_cands, u64* out_mask, u64* out_prefix,
+                                                     i64* leaf_vox, uint32_t* leaf_box, int32_t* flags) {
+  const int lpl = op == TC_OP_REFINE ? 1 : 4;  // lanes per output leaf (uniform)
+  const i64 gt = (i64)blockIdx.x * 256 + threadIdx.x;
+  const i64 i = gt / lpl;
+  const int sub = (int)(gt % lpl);
+  bool valid = i < n;
   u64 out[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) out[k] = 0;
-  if (op == TC_OP_REFINE) {
-    const int32_t s = cand_src[c];
-    const int32_t src = src_leaf(src_lower_mask, src_lower_prefix, src_lower_first, s, (ax >> 1) & 15,
-                                 (ay >> 1) & 15, (az >> 1) & 15, n_src_lower, n_src_leaf, flags);
-    if (src < 0) {
+  i64 c = -1;
+  int4 o = make_int4(0, 0, 0, 0);
+  if (valid) {
+    o = out_origin[i];
+    c = leaf_cand[i];
+    if (c < 0 || c >= *d_num_cands) {
       set_flag(flags, kFlagInternal);
-    } else {
-      u64 W[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) W[k] = src_leaf_mask[(i64)src * 8 + k];
-      const int qx = (int)(ax & 1), qy = (int)(ay & 1), qz = (int)(az & 1);
-#pragma unroll
-      for (int x = 0; x < 8; ++x) out[x] = refine_word(W[4 * qx + (x >> 1)], qy, qz);
+      valid = false;
     }
-  } else if (op == TC_OP_COARSEN) {
-    const int32_t s = cand_src[c * 8 + octant_index(lx >> 3, ly >> 3, lz >> 3)];
-    if (s >= 0) {
+  }
+  if (valid) {
+    const i64 ax = o.x >> 3, ay = o.y >> 3, az = o.z >> 3;  // output leaf coordinates
+    const i64 lx = ax & 15, ly = ay & 15, lz = az & 15;
+    if (op == TC_OP_REFINE) {
+      const int32_t s = cand_src[c];
+      const int32_t src = src_leaf(src_lower_mask, src_lower_prefix, src_lower_first, s, (ax >> 1) & 15,
+                                   (ay >> 1) & 15, (az >> 1) & 15, n_src_lower, n_src_leaf, flags);
+      if (src < 0) {
+        set_flag(flags, kFlagInternal);
+      } else {
+        u64 W[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+        for (int k = 0; k < 8; ++k) W[k] = src_leaf_mask[(i64)src * 8 + k];
+        const int qx = (int)(ax & 1), qy = (int)(ay & 1), qz = (int)(az & 1);
+#pragma unroll
+        for (int x = 0; x < 8; ++x) out[x] = refine_word(W[4 * qx + (x >> 1)], qy, qz);
+      }
+    } else if (op == TC_OP_COARSEN) {
+      const int32_t s = cand_src[c * 8 + octant_index(lx >> 3, ly >> 3, lz >> 3)];
+      if (s < 0) set_flag(flags, kFlagInternal);
+      for (int j = sub; j < 8 && s >= 0; j += 4) {
         const I3 q = octant(j);
         const int32_t src = src_leaf(src_lower_mask, src_lower_prefix, src_lower_first, s, (2 * lx + q.x) & 15,
                                      (2 * ly + q.y) & 15, (2 * lz + q.z) & 15, n_src_lower, n_src_leaf, flags);
@@ -452,25 +487,43 @@ __global__ void __launch_bounds__(256) k_leaf_gather(const int4* out_origin, con
         coarsen_place(out, W, q);
       }
     } else {
-      set_flag(flags, kFlagInternal);
-    }
-  } else {
-    for (int j = 0; j < m; ++j) {
-      const I3 t = box_offset(j, op);
-      const i64 px = lx - t.x, py = ly - t.y, pz = lz - t.z;  // source position, -1 .. 16
-      const int32_t s = cand_src[c * 27 + index27(px >> 4, py >> 4, pz >> 4)];
-      if (s < 0) continue;
-      const int32_t src = src_leaf(src_lower_mask, src_lower_prefix, src_lower_first, s, px & 15, py & 15, pz & 15,
-                                   n_src_lower, n_src_leaf, flags);
-      if (src < 0) continue;
-      u64 W[8];
+      for (int j = sub; j < m; j += 4) {
+        const I3 t = box_offset(j, op);
+        const i64 px = lx - t.x, py = ly - t.y, pz = lz - t.z;  // source position, -1 .. 16
+        const int32_t s = cand_src[c * 27 + index27(px >> 4, py >> 4, pz >> 4)];
+        if (s < 0) continue;
+        const int32_t src = src_leaf(src_lower_mask, src_lower_prefix, src_lower_first, s, px & 15, py & 15,
+                                     pz & 15, n_src_lower, n_src_leaf, flags);
+        if (src < 0) continue;
+        u64 W[8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) W[k] = src_leaf_mask[(i64)src * 8 + k];
-      box_contrib(out, W, t, lo, hi);
+        for (int k = 0; k < 8; ++k) W[k] = src_leaf_mask[(i64)src * 8 + k];
+        box_contrib(out, W, t, lo, hi);
+      }
     }
+  }
+  if (lpl == 4) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      out[k] |= __shfl_xor(out[k], 1, kWave);
+      out[k] |= __shfl_xor(out[k], 2, kWave);
+    }
+  }
+  if (i >= n || sub != 0) return;
+  if (!valid) {
+    leaf_vox[i] = 0;
+    leaf_box[i] = kEmptyBox;
+    return;
   }
 #pragma unroll
   for (int k = 0; k < 8; ++k) out_mask[i * 8 + k] = out[k];
+  u64 prefix;
+  int count;
+  uint32_t box;
+  leaf_stats(out, prefix, count, box);
+  out_prefix[i] = prefix;
+  leaf_vox[i] = count;
+  leaf_box[i] = box;
 }
 
 // ------------------------------------------------------------------ driver
@@ -571,11 +624,12 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa) 
          oi.m_src, (const int32_t*)tile_of_cand, (const u64*)ts.tile_child, (const uint16_t*)ts.tile_prefix,
          (const int32_t*)ts.tile_lower_base, (const int32_t*)ts.d_num_tiles, (const int32_t*)ts.d_num_cands,
          lower_nbr, ts.cand_origin, cand_src, ts.flags);
-  // leaves (pass A)
-  fill_u64(ts.cand_child, 0, nL * 64, ts.d_num_cands, 64, s);
-  launch("k_leaf_mark", k_leaf_mark, ceil_div(Ls, 256), 256, s, (const int4*)sv.leaf_origin,
-         (const int32_t*)sv.leaf_parent, (const u64*)sv.leaf_mask, Ls, op, oi.m, (const int32_t*)lower_nbr,
-         (const int32_t*)ts.d_num_cands, ts.cand_child, ts.flags);
+  // leaves (pass A); refine overwrites every word of its candidates, the others OR into zeros
+  if (op != TC_OP_REFINE) fill_u64(ts.cand_child, 0, nL * 64, ts.d_num_cands, 64, s);
+  launch("k_leaf_mark_lower", k_leaf_mark_lower, (i64)src->n1, 256, s, (const int4*)sv.leaf_origin,
+         (const u64*)sv.leaf_mask, (const int32_t*)sv.lower_first, (const u64*)sv.lower_mask,
+         (const uint16_t*)sv.lower_prefix, op, oi.m, (const int32_t*)lower_nbr, (const int32_t*)ts.d_num_cands,
+         ts.cand_child, ts.flags);
   // counts and the single readback
   tree_count_cands(ts, s);
   tree_grid_counts(ts, B, s);
@@ -593,18 +647,20 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa) 
     Arena post(s);
     const size_t o_lc = post.reserve(4 * L);
     const size_t o_lv = post.reserve(8 * L);
+    const size_t o_box = post.reserve(4 * L);
     const size_t o_vx = post.reserve(8 * (L + 1));
-    const size_t o_bb = post.reserve(4 * 6 * (i64)B);
+    const size_t o_bb = post.reserve(4 * 6 * (i64)B * bbox_replicas(B));
     post.commit();
     int32_t* leaf_cand = post.at<int32_t>(o_lc);
     tree_write_nodes(ts, ov, leaf_cand, s);
-    launch("k_leaf_gather", k_leaf_gather, ceil_div(L, 256), 256, s, (const int4*)ov.leaf_origin,
+    const i64 lanes = op == TC_OP_REFINE ? 1 : 4;
+    launch("k_leaf_gather", k_leaf_gather, ceil_div(L * lanes, 256), 256, s, (const int4*)ov.leaf_origin,
            (const int32_t*)leaf_cand, L, op, oi.m, oi.lo, oi.hi, (const int32_t*)cand_src,
            (const u64*)sv.lower_mask, (const uint16_t*)sv.lower_prefix, (const int32_t*)sv.lower_first,
            (const u64*)sv.leaf_mask, sv.n_lower, sv.n_leaf, (const int32_t*)ts.d_num_cands, ov.leaf_mask,
-           ts.flags);
-    tree_finalize_leaves(ov, post.at<i64>(o_lv), post.at<i64>(o_vx), post.at<int32_t>(o_bb),
-                         (const int32_t*)ts.grid_info, s);
+           ov.leaf_prefix, post.at<i64>(o_lv), post.at<uint32_t>(o_box), ts.flags);
+    tree_finalize_leaves(ov, post.at<i64>(o_lv), post.at<uint32_t>(o_box), post.at<i64>(o_vx),
+                         post.at<int32_t>(o_bb), (const int32_t*)ts.grid_info, s);
   } catch (...) {
     free_batch(out);
     throw;

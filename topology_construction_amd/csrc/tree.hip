@@ -238,100 +238,91 @@ void tree_write_nodes(TreeScratch& ts, const GridView& out, int32_t* leaf_cand, 
 }
 
 // ------------------------------------------------------------------ leaf statistics
-// Per leaf: packed prefix word, voxel count, and the per-grid bbox (reduced over
-// the wave when all its leaves belong to one grid, then one atomic per bound).
-__global__ void __launch_bounds__(256) k_leaf_finalize(const int4* leaf_origin, const u64* leaf_mask,
-                                                       u64* leaf_prefix, i64* leaf_vox, int32_t* bbox, int32_t B,
-                                                       i64 n_leaf) {
+// Per leaf (masks written by the ijk front-end): prefix word, voxel count and
+// packed local bbox. The topology pass computes the same values in its gather.
+__global__ void __launch_bounds__(256) k_leaf_stats(const u64* leaf_mask, u64* leaf_prefix, i64* leaf_vox,
+                                                    uint32_t* leaf_box, i64 n_leaf) {
   const i64 i = (i64)blockIdx.x * 256 + threadIdx.x;
-  const bool valid = i < n_leaf;
+  if (i >= n_leaf) return;
+  u64 W[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) W[k] = leaf_mask[i * 8 + k];
+  u64 prefix;
+  int count;
+  uint32_t box;
+  leaf_stats(W, prefix, count, box);
+  leaf_prefix[i] = prefix;
+  leaf_vox[i] = count;
+  leaf_box[i] = box;
+}
+
+void tree_leaf_stats(const GridView& out, i64* leaf_vox, uint32_t* leaf_box, hipStream_t s) {
+  launch("k_leaf_stats", k_leaf_stats, ceil_div((i64)out.n_leaf, 256), 256, s, (const u64*)out.leaf_mask,
+         out.leaf_prefix, leaf_vox, leaf_box, (i64)out.n_leaf);
+}
+
+// Leaf voxel offsets (0-based inside the grid) and per-grid bboxes, one leaf per
+// thread. Bounds are reduced over the wave (leaves are sorted by grid, so a wave
+// nearly always holds one grid) and then folded with device-scope atomics into
+// one of R replicas of the per-grid accumulators, chosen by block. On this
+// multi-XCD part such atomics resolve past the per-XCD L2 and serialize per
+// address, so spreading them over replicas keeps each address cold;
+// k_write_headers folds the replicas.
+__device__ __forceinline__ void box_flush(int32_t* bbox, int32_t B, int32_t R, int rep, int g, const int v[6]) {
+  if (g < 0 || g >= B) return;
+#pragma unroll
+  for (int a = 0; a < 3; ++a) {
+    atomicMin(&bbox[((i64)a * R + rep) * B + g], v[a]);
+    atomicMax(&bbox[((i64)(3 + a) * R + rep) * B + g], v[3 + a]);
+  }
+}
+
+__global__ void __launch_bounds__(256) k_leaf_offsets_bbox(const int4* leaf_origin, const uint32_t* leaf_box,
+                                                           const i64* vox_excl, const int32_t* grid_info,
+                                                           i64* leaf_offset, int32_t* bbox, int32_t B, int32_t R,
+                                                           i64 n_leaf) {
+  const i64 i = (i64)blockIdx.x * 256 + threadIdx.x;
+  const int lane = threadIdx.x & (kWave - 1);
   int g = -1;
-  int bmin[3] = {INT32_MAX, INT32_MAX, INT32_MAX};
-  int bmax[3] = {INT32_MIN, INT32_MIN, INT32_MIN};
-  if (valid) {
+  int v[6] = {INT32_MAX, INT32_MAX, INT32_MAX, INT32_MIN, INT32_MIN, INT32_MIN};
+  if (i < n_leaf) {
     const int4 o = leaf_origin[i];
-    g = o.w;
-    u64 W[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) W[k] = leaf_mask[i * 8 + k];
-    u64 packed = 0, run = 0;
-    int xmin = 8, xmax = -1;
-    u64 orw = 0;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      if (k > 0) packed |= run << (9 * (k - 1));
-      run += (u64)popc64(W[k]);
-      if (W[k]) {
-        xmin = min(xmin, k);
-        xmax = max(xmax, k);
+    const uint32_t bx = leaf_box[i];
+    if (o.w >= 0 && o.w < B) {
+      leaf_offset[i] = vox_excl[i] - vox_excl[grid_info[o.w * 6 + 5]];
+      if (bx != kEmptyBox) {
+        g = o.w;
+        v[0] = o.x + (int)(bx & 7);
+        v[3] = o.x + (int)((bx >> 3) & 7);
+        v[1] = o.y + (int)((bx >> 6) & 7);
+        v[4] = o.y + (int)((bx >> 9) & 7);
+        v[2] = o.z + (int)((bx >> 12) & 7);
+        v[5] = o.z + (int)((bx >> 15) & 7);
       }
-      orw |= W[k];
-    }
-    leaf_prefix[i] = packed;
-    leaf_vox[i] = (i64)run;
-    // y extent: non-zero bytes of the OR of all words; z extent: OR of those bytes
-    int ymin = 8, ymax = -1;
-    u64 zor = 0;
-#pragma unroll
-    for (int y = 0; y < 8; ++y) {
-      const u64 byte = (orw >> (8 * y)) & 0xffull;
-      if (byte) {
-        ymin = min(ymin, y);
-        ymax = max(ymax, y);
-      }
-      zor |= byte;
-    }
-    const int zmin = zor ? __builtin_ctzll(zor) : 8;
-    const int zmax = zor ? 63 - __builtin_clzll(zor) : -1;
-    if (run) {
-      bmin[0] = o.x + xmin;
-      bmin[1] = o.y + ymin;
-      bmin[2] = o.z + zmin;
-      bmax[0] = o.x + xmax;
-      bmax[1] = o.y + ymax;
-      bmax[2] = o.z + zmax;
     }
   }
-  // wave-uniform grid? (inactive lanes carry g = -1)
-  const int lane = threadIdx.x & (kWave - 1);
-  const u64 active = __ballot(valid);
-  if (active == 0) return;
-  const int first = __builtin_ctzll(active);
+  const bool active = g >= 0;
+  const u64 act = __ballot(active);
+  if (!act) return;  // uniform per wave
+  const int rep = (int)(blockIdx.x % (unsigned)R);
+  const int first = __builtin_ctzll(act);
   const int g0 = __shfl(g, first, kWave);
-  const bool same = __ballot(valid && g != g0) == 0;
-  if (same) {
+  if (__ballot(active && g != g0) == 0) {
     int r[6];
 #pragma unroll
     for (int a = 0; a < 3; ++a) {
-      r[a] = wave_min_i32(bmin[a]);
-      r[3 + a] = wave_max_i32(bmax[a]);
+      r[a] = wave_min_i32(v[a]);
+      r[3 + a] = wave_max_i32(v[3 + a]);
     }
-    if (lane == first && g0 >= 0 && g0 < B) {
-#pragma unroll
-      for (int a = 0; a < 3; ++a) {
-        if (r[a] != INT32_MAX) atomicMin(&bbox[a * B + g0], r[a]);
-        if (r[3 + a] != INT32_MIN) atomicMax(&bbox[(3 + a) * B + g0], r[3 + a]);
-      }
-    }
-  } else if (valid && g >= 0 && g < B && bmin[0] != INT32_MAX) {
-#pragma unroll
-    for (int a = 0; a < 3; ++a) {
-      atomicMin(&bbox[a * B + g], bmin[a]);
-      atomicMax(&bbox[(3 + a) * B + g], bmax[a]);
-    }
+    if (lane == first) box_flush(bbox, B, R, rep, g0, r);
+  } else if (active) {
+    box_flush(bbox, B, R, rep, g, v);
   }
 }
 
-__global__ void __launch_bounds__(256) k_leaf_offsets(const int4* leaf_origin, const i64* vox_excl,
-                                                      const int32_t* grid_info, i64* leaf_offset, i64 n_leaf) {
-  const i64 i = (i64)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n_leaf) return;
-  const int g = leaf_origin[i].w;
-  leaf_offset[i] = vox_excl[i] - vox_excl[grid_info[g * 6 + 5]];
-}
-
 __global__ void __launch_bounds__(256) k_write_headers(const int32_t* grid_info, const i64* vox_excl,
-                                                       const int32_t* bbox, int32_t B, tc_grid_header* hdr) {
+                                                       const int32_t* bbox, int32_t B, int32_t R,
+                                                       tc_grid_header* hdr) {
   const i64 g = (i64)blockIdx.x * 256 + threadIdx.x;
   if (g >= B) return;
   const int32_t* gi = grid_info + g * 6;
@@ -347,62 +338,75 @@ __global__ void __launch_bounds__(256) k_write_headers(const int32_t* grid_info,
   h.voxel_begin = vox_excl[gi[5]];
   h.voxel_count = vox_excl[gi[5] + gi[2]] - h.voxel_begin;
   for (int a = 0; a < 3; ++a) {
-    h.bbox_min[a] = bbox[a * B + g];
-    h.bbox_max[a] = bbox[(3 + a) * B + g];
+    int lo = INT32_MAX, hi = INT32_MIN;
+    for (int r = 0; r < R; ++r) {
+      lo = min(lo, bbox[((i64)a * R + r) * B + g]);
+      hi = max(hi, bbox[((i64)(3 + a) * R + r) * B + g]);
+    }
+    h.bbox_min[a] = lo;
+    h.bbox_max[a] = hi;
   }
   h.reserved[0] = 0;
   h.reserved[1] = 0;
   hdr[g] = h;
 }
 
-void tree_finalize_leaves(const GridView& out, i64* leaf_vox, i64* vox_excl, int32_t* bbox_accum,
-                          const int32_t* grid_info, hipStream_t s) {
+int32_t bbox_replicas(int32_t B) {
+  int32_t r = 8192 / (B > 0 ? B : 1);
+  return r < 1 ? 1 : (r > 64 ? 64 : r);
+}
+
+void tree_finalize_leaves(const GridView& out, const i64* leaf_vox, const uint32_t* leaf_box, i64* vox_excl,
+                          int32_t* bbox_accum, const int32_t* grid_info, hipStream_t s) {
   const i64 L = out.n_leaf;
   const int32_t B = out.B;
-  fill_i32(bbox_accum, INT32_MAX, 3 * (i64)B, nullptr, 1, s);
-  fill_i32(bbox_accum + 3 * (i64)B, INT32_MIN, 3 * (i64)B, nullptr, 1, s);
-  launch("k_leaf_finalize", k_leaf_finalize, ceil_div(L, 256), 256, s, (const int4*)out.leaf_origin,
-         (const u64*)out.leaf_mask, out.leaf_prefix, leaf_vox, bbox_accum, B, L);
+  const int32_t R = bbox_replicas(B);
+  fill_i32(bbox_accum, INT32_MAX, 3 * (i64)R * B, nullptr, 1, s);
+  fill_i32(bbox_accum + 3 * (i64)R * B, INT32_MIN, 3 * (i64)R * B, nullptr, 1, s);
   scan_excl_i64(leaf_vox, vox_excl, L, nullptr, s);
-  launch("k_leaf_offsets", k_leaf_offsets, ceil_div(L, 256), 256, s, (const int4*)out.leaf_origin,
-         (const i64*)vox_excl, grid_info, out.leaf_offset, L);
+  launch("k_leaf_offsets_bbox", k_leaf_offsets_bbox, ceil_div(L, 256), 256, s, (const int4*)out.leaf_origin,
+         leaf_box, (const i64*)vox_excl, grid_info, out.leaf_offset, bbox_accum, B, R, L);
   launch("k_write_headers", k_write_headers, ceil_div((i64)B, 256), 256, s, grid_info, (const i64*)vox_excl,
-         (const int32_t*)bbox_accum, B, out.headers);
+         (const int32_t*)bbox_accum, B, R, out.headers);
 }
 
 // ------------------------------------------------------------------ enumeration
-// One wave per leaf: lane k writes the k-th voxel (in-leaf bit order) of the leaf,
-// so each store instruction covers 64 consecutive rows.
+// One wave per leaf. Lane r owns row r = x*8 + y of the leaf (byte y of word x,
+// at most 8 voxels along z); a wave scan of the row popcounts places every row,
+// lanes expand their rows into LDS in bit order, and the wave then streams the
+// leaf's rows out with contiguous 256-byte stores.
 __global__ void __launch_bounds__(256) k_enumerate(const tc_grid_header* hdr, const int4* leaf_origin,
                                                    const u64* leaf_mask, const i64* leaf_offset, int32_t* ijk,
                                                    i64 n_leaf) {
-  const i64 l = (i64)blockIdx.x * 4 + threadIdx.x / kWave;
+  __shared__ int32_t s_rows[4][3 * 512];
+  const int w = threadIdx.x / kWave;
+  const i64 l = (i64)blockIdx.x * 4 + w;
   const int lane = threadIdx.x & (kWave - 1);
-  if (l >= n_leaf) return;
+  if (l >= n_leaf) return;  // uniform per wave; no block barrier below
   const int4 o = leaf_origin[l];
   const i64 base = hdr[o.w].voxel_begin + leaf_offset[l];
-  u64 W[8];
-  int pre[9];
-  pre[0] = 0;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    W[k] = leaf_mask[l * 8 + k];
-    pre[k + 1] = pre[k] + popc64(W[k]);
+  const int x = lane >> 3, y = lane & 7;
+  const u64 row = (leaf_mask[l * 8 + x] >> (8 * y)) & 0xffull;
+  const int cnt = __popcll(row);
+  const int inc = wave_incl_scan(cnt);
+  const int total = __shfl(inc, kWave - 1, kWave);
+  int32_t* rows = s_rows[w];
+  int at = inc - cnt;
+  u64 rest = row;
+  while (rest) {
+    const int z = __builtin_ctzll(rest);
+    rows[3 * at + 0] = o.x + x;
+    rows[3 * at + 1] = o.y + y;
+    rows[3 * at + 2] = o.z + z;
+    rest &= rest - 1;
+    ++at;
   }
-  const int total = pre[8];
-  for (int k = lane; k < total; k += kWave) {
-    int w = 0;
-#pragma unroll
-    for (int q = 1; q < 8; ++q) w += (k >= pre[q]) ? 1 : 0;
-    u64 word = 0;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) word = (q == w) ? W[q] : word;
-    const int b = select_bit(word, k - pre[w]);
-    const i64 row = (base + k) * 3;
-    ijk[row + 0] = o.x + w;
-    ijk[row + 1] = o.y + (b >> 3);
-    ijk[row + 2] = o.z + (b & 7);
-  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  int32_t* dst = ijk + base * 3;
+  const int n = total * 3;
+  for (int e = lane; e < n; e += kWave) dst[e] = rows[e];
 }
 
 void tree_enumerate(const GridView& v, int32_t* ijk, hipStream_t s) {

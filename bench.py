@@ -57,25 +57,26 @@ def run_step(binding, src, outs=None):
 
 # Algorithmic bytes of one launch of each measured kernel: what the step itself
 # must move, not what the kernel happens to move.
-#   k_leaf_mark     reads every source leaf once: origin 16 B + parent 4 B + mask 64 B
-#   k_leaf_gather   reads every output leaf's origin 16 B + candidate id 4 B, every
-#                   source mask once (64 B), writes every output mask (64 B)
-#   k_leaf_finalize reads origin + mask (80 B), writes prefix + voxel count (16 B)
-#   k_enumerate     reads origin, mask, offset and grid base (96 B per leaf),
-#                   writes 12 B per voxel
+#   k_leaf_mark_lower    reads every source leaf once: origin 16 B + mask 64 B
+#   k_leaf_gather        reads every output leaf's origin 16 B + candidate id 4 B, every
+#                        source mask once (64 B), writes every output mask (64 B)
+#   k_leaf_offsets_bbox  reads origin 16 B + packed bbox 4 B + voxel scan 8 B,
+#                        writes the voxel offset 8 B, per output leaf
+#   k_enumerate          reads origin, mask, offset and grid base (96 B per leaf),
+#                        writes 12 B per voxel
 def kernel_bytes(name, src_leaves, leaves, voxels):
-    if name == "k_leaf_mark":
-        return 84 * src_leaves
+    if name == "k_leaf_mark_lower":
+        return 80 * src_leaves
     if name == "k_leaf_gather":
         return 84 * leaves + 64 * src_leaves
-    if name == "k_leaf_finalize":
-        return 96 * leaves
+    if name == "k_leaf_offsets_bbox":
+        return 36 * leaves
     if name == "k_enumerate":
         return 96 * leaves + 12 * voxels
     raise ValueError(name)
 
 
-LARGE_KERNELS = ["k_leaf_mark", "k_leaf_gather", "k_leaf_finalize", "k_enumerate"]
+LARGE_KERNELS = ["k_leaf_mark_lower", "k_leaf_gather", "k_leaf_offsets_bbox", "k_enumerate"]
 
 
 def measure_large(binding, torch, np, synth):

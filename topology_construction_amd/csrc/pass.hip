@@ -431,6 +431,8 @@ __device__ __forceinline__ void box_contrib(u64 out[8], const u64 W[8], const I3
 // output leaf over 4 adjacent lanes and OR the partial masks with shuffles, so
 // the dependent lookups run in parallel. Also writes the leaf's prefix word,
 // voxel count and packed local bbox.
+// KIND: 0 refine, 1 coarsen, 2 box op (dilate / pads); one instantiation each.
+template <int KIND>
 __global__ void __launch_bounds__(256) k_leaf_gather(const int4* out_origin, const int32_t* leaf_cand, i64 n,
                                                      int op, int m, int lo, int hi, const int32_t* cand_src,
                                                      const u64* src_lower_mask, const uint16_t* src_lower_prefix,
@@ -438,7 +440,7 @@ __global__ void __launch_bounds__(256) k_leaf_gather(const int4* out_origin, con
                                                      int32_t n_src_lower, int32_t n_src_leaf,
                                                      const int32_t* d_num_cands, u64* out_mask, u64* out_prefix,
                                                      i64* leaf_vox, uint32_t* leaf_box, int32_t* flags) {
-  const int lpl = op == TC_OP_REFINE ? 1 : 4;  // lanes per output leaf (uniform)
+  constexpr int lpl = KIND == 0 ? 1 : 4;  // lanes per output leaf
   const i64 gt = (i64)blockIdx.x * 256 + threadIdx.x;
   const i64 i = gt / lpl;
   const int sub = (int)(gt % lpl);
@@ -459,7 +461,7 @@ __global__ void __launch_bounds__(256) k_leaf_gather(const int4* out_origin, con
   if (valid) {
     const i64 ax = o.x >> 3, ay = o.y >> 3, az = o.z >> 3;  // output leaf coordinates
     const i64 lx = ax & 15, ly = ay & 15, lz = az & 15;
-    if (op == TC_OP_REFINE) {
+    if constexpr (KIND == 0) {
       const int32_t s = cand_src[c];
       const int32_t src = src_leaf(src_lower_mask, src_lower_prefix, src_lower_first, s, (ax >> 1) & 15,
                                    (ay >> 1) & 15, (az >> 1) & 15, n_src_lower, n_src_leaf, flags);
@@ -473,7 +475,7 @@ __global__ void __launch_bounds__(256) k_leaf_gather(const int4* out_origin, con
 #pragma unroll
         for (int x = 0; x < 8; ++x) out[x] = refine_word(W[4 * qx + (x >> 1)], qy, qz);
       }
-    } else if (op == TC_OP_COARSEN) {
+    } else if constexpr (KIND == 1) {
       const int32_t s = cand_src[c * 8 + octant_index(lx >> 3, ly >> 3, lz >> 3)];
       if (s < 0) set_flag(flags, kFlagInternal);
       for (int j = sub; j < 8 && s >= 0; j += 4) {
@@ -502,7 +504,7 @@ __global__ void __launch_bounds__(256) k_leaf_gather(const int4* out_origin, con
       }
     }
   }
-  if (lpl == 4) {
+  if constexpr (lpl == 4) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       out[k] |= __shfl_xor(out[k], 1, kWave);
@@ -654,7 +656,8 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa) 
     int32_t* leaf_cand = post.at<int32_t>(o_lc);
     tree_write_nodes(ts, ov, leaf_cand, s);
     const i64 lanes = op == TC_OP_REFINE ? 1 : 4;
-    launch("k_leaf_gather", k_leaf_gather, ceil_div(L * lanes, 256), 256, s, (const int4*)ov.leaf_origin,
+    auto gather = op == TC_OP_REFINE ? k_leaf_gather<0> : (op == TC_OP_COARSEN ? k_leaf_gather<1> : k_leaf_gather<2>);
+    launch("k_leaf_gather", gather, ceil_div(L * lanes, 256), 256, s, (const int4*)ov.leaf_origin,
            (const int32_t*)leaf_cand, L, op, oi.m, oi.lo, oi.hi, (const int32_t*)cand_src,
            (const u64*)sv.lower_mask, (const uint16_t*)sv.lower_prefix, (const int32_t*)sv.lower_first,
            (const u64*)sv.leaf_mask, sv.n_lower, sv.n_leaf, (const int32_t*)ts.d_num_cands, ov.leaf_mask,

@@ -320,11 +320,27 @@ __global__ void __launch_bounds__(256) k_leaf_offsets_bbox(const int4* leaf_orig
   }
 }
 
+// One wave per grid: lanes fold the bbox replicas, lane 0 writes the header.
 __global__ void __launch_bounds__(256) k_write_headers(const int32_t* grid_info, const i64* vox_excl,
                                                        const int32_t* bbox, int32_t B, int32_t R,
                                                        tc_grid_header* hdr) {
-  const i64 g = (i64)blockIdx.x * 256 + threadIdx.x;
-  if (g >= B) return;
+  const i64 g = (i64)blockIdx.x * 4 + threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  if (g >= B) return;  // uniform per wave
+  int v[6] = {INT32_MAX, INT32_MAX, INT32_MAX, INT32_MIN, INT32_MIN, INT32_MIN};
+  for (int r = lane; r < R; r += kWave) {
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+      v[a] = min(v[a], bbox[((i64)a * R + r) * B + g]);
+      v[3 + a] = max(v[3 + a], bbox[((i64)(3 + a) * R + r) * B + g]);
+    }
+  }
+#pragma unroll
+  for (int a = 0; a < 3; ++a) {
+    v[a] = wave_min_i32(v[a]);
+    v[3 + a] = wave_max_i32(v[3 + a]);
+  }
+  if (lane != 0) return;
   const int32_t* gi = grid_info + g * 6;
   tc_grid_header h;
   h.grid_index = (int32_t)g;
@@ -338,13 +354,8 @@ __global__ void __launch_bounds__(256) k_write_headers(const int32_t* grid_info,
   h.voxel_begin = vox_excl[gi[5]];
   h.voxel_count = vox_excl[gi[5] + gi[2]] - h.voxel_begin;
   for (int a = 0; a < 3; ++a) {
-    int lo = INT32_MAX, hi = INT32_MIN;
-    for (int r = 0; r < R; ++r) {
-      lo = min(lo, bbox[((i64)a * R + r) * B + g]);
-      hi = max(hi, bbox[((i64)(3 + a) * R + r) * B + g]);
-    }
-    h.bbox_min[a] = lo;
-    h.bbox_max[a] = hi;
+    h.bbox_min[a] = v[a];
+    h.bbox_max[a] = v[3 + a];
   }
   h.reserved[0] = 0;
   h.reserved[1] = 0;
@@ -366,52 +377,92 @@ void tree_finalize_leaves(const GridView& out, const i64* leaf_vox, const uint32
   scan_excl_i64(leaf_vox, vox_excl, L, nullptr, s);
   launch("k_leaf_offsets_bbox", k_leaf_offsets_bbox, ceil_div(L, 256), 256, s, (const int4*)out.leaf_origin,
          leaf_box, (const i64*)vox_excl, grid_info, out.leaf_offset, bbox_accum, B, R, L);
-  launch("k_write_headers", k_write_headers, ceil_div((i64)B, 256), 256, s, grid_info, (const i64*)vox_excl,
+  launch("k_write_headers", k_write_headers, ceil_div((i64)B, 4), 256, s, grid_info, (const i64*)vox_excl,
          (const int32_t*)bbox_accum, B, R, out.headers);
 }
 
 // ------------------------------------------------------------------ enumeration
-// One wave per leaf. Lane r owns row r = x*8 + y of the leaf (byte y of word x,
-// at most 8 voxels along z); a wave scan of the row popcounts places every row,
-// lanes expand their rows into LDS in bit order, and the wave then streams the
-// leaf's rows out with contiguous 256-byte stores.
+// One wave walks `lpw` (1..8) consecutive leaves. Their masks, origins and voxel
+// bases are loaded once, up front; many leaves per wave amortise the load
+// latency on large batches, one leaf per wave keeps small batches wide. For each leaf, lane r owns row r = x*8 + y
+// (byte y of word x, at most 8 voxels along z); a wave scan of the row popcounts
+// places every row, lanes expand their rows into LDS in bit order, and the wave
+// streams the leaf's rows out with 16-byte stores (the LDS image is shifted so
+// that its 16-byte chunks line up with the destination's).
+constexpr int kEnumMaxLeaves = 8;
+
 __global__ void __launch_bounds__(256) k_enumerate(const tc_grid_header* hdr, const int4* leaf_origin,
                                                    const u64* leaf_mask, const i64* leaf_offset, int32_t* ijk,
-                                                   i64 n_leaf) {
-  __shared__ int32_t s_rows[4][3 * 512];
+                                                   i64 n_leaf, int lpw, int vec_ok) {
+  __shared__ __align__(16) int32_t s_rows[4][3 * 512 + 4];
   const int w = threadIdx.x / kWave;
-  const i64 l = (i64)blockIdx.x * 4 + w;
   const int lane = threadIdx.x & (kWave - 1);
-  if (l >= n_leaf) return;  // uniform per wave; no block barrier below
-  const int4 o = leaf_origin[l];
-  const i64 base = hdr[o.w].voxel_begin + leaf_offset[l];
-  const int x = lane >> 3, y = lane & 7;
-  const u64 row = (leaf_mask[l * 8 + x] >> (8 * y)) & 0xffull;
-  const int cnt = __popcll(row);
-  const int inc = wave_incl_scan(cnt);
-  const int total = __shfl(inc, kWave - 1, kWave);
-  int32_t* rows = s_rows[w];
-  int at = inc - cnt;
-  u64 rest = row;
-  while (rest) {
-    const int z = __builtin_ctzll(rest);
-    rows[3 * at + 0] = o.x + x;
-    rows[3 * at + 1] = o.y + y;
-    rows[3 * at + 2] = o.z + z;
-    rest &= rest - 1;
-    ++at;
+  const i64 l0 = ((i64)blockIdx.x * 4 + w) * lpw;
+  if (l0 >= n_leaf) return;  // uniform per wave; no block barrier below
+  const int nl = (int)min((i64)lpw, n_leaf - l0);
+  const int jl = lane >> 3;
+  const u64 myword = jl < nl ? leaf_mask[(l0 + jl) * 8 + (lane & 7)] : 0ull;
+  int4 myo = make_int4(0, 0, 0, 0);
+  i64 mybase = 0;
+  if (lane < nl) {
+    myo = leaf_origin[l0 + lane];
+    mybase = hdr[myo.w].voxel_begin + leaf_offset[l0 + lane];
   }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  int32_t* dst = ijk + base * 3;
-  const int n = total * 3;
-  for (int e = lane; e < n; e += kWave) dst[e] = rows[e];
+  int32_t* rows = s_rows[w];
+  const int x = lane >> 3, y = lane & 7;
+  for (int j = 0; j < nl; ++j) {
+    const u64 word = __shfl(myword, j * 8 + x, kWave);
+    const int ox = __shfl(myo.x, j, kWave), oy = __shfl(myo.y, j, kWave), oz = __shfl(myo.z, j, kWave);
+    const i64 base = __shfl(mybase, j, kWave);
+    const u64 row = (word >> (8 * y)) & 0xffull;
+    const int cnt = __popcll(row);
+    const int inc = wave_incl_scan(cnt);
+    const int total = __shfl(inc, kWave - 1, kWave);
+    const int a = vec_ok ? (int)((base * 3) & 3) : 0;
+    int at = a + 3 * (inc - cnt);
+    u64 rest = row;
+    while (rest) {
+      const int z = __builtin_ctzll(rest);
+      rows[at + 0] = ox + x;
+      rows[at + 1] = oy + y;
+      rows[at + 2] = oz + z;
+      rest &= rest - 1;
+      at += 3;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int n = a + 3 * total;
+    int32_t* dst = ijk + base * 3 - a;  // 16-byte aligned when vec_ok
+    if (vec_ok) {
+      int4* dst4 = reinterpret_cast<int4*>(dst);
+      const int4* src4 = reinterpret_cast<const int4*>(rows);
+      for (int q = lane; q < ((n + 3) >> 2); q += kWave) {
+        const int e0 = q * 4;
+        if (e0 >= a && e0 + 4 <= n) {
+          dst4[q] = src4[q];
+        } else {
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            if (e0 + t >= a && e0 + t < n) dst[e0 + t] = rows[e0 + t];
+        }
+      }
+    } else {
+      for (int e = lane; e < n; e += kWave) dst[e] = rows[e];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
 }
 
 void tree_enumerate(const GridView& v, int32_t* ijk, hipStream_t s) {
-  launch("k_enumerate", k_enumerate, ceil_div((i64)v.n_leaf, 4), 256, s, (const tc_grid_header*)v.headers,
-         (const int4*)v.leaf_origin, (const u64*)v.leaf_mask, (const i64*)v.leaf_offset, ijk, (i64)v.n_leaf);
+  const int vec_ok = (reinterpret_cast<uintptr_t>(ijk) & 15) == 0 ? 1 : 0;
+  // enough waves to cover every CU several times before packing leaves per wave
+  const int lpw = v.n_leaf >= 256 * 1024 ? kEnumMaxLeaves : (v.n_leaf >= 64 * 1024 ? 2 : 1);
+  launch("k_enumerate", k_enumerate, ceil_div((i64)v.n_leaf, 4 * lpw), 256, s,
+         (const tc_grid_header*)v.headers, (const int4*)v.leaf_origin, (const u64*)v.leaf_mask,
+         (const i64*)v.leaf_offset, ijk, (i64)v.n_leaf, lpw, vec_ok);
 }
 
 }  // namespace tc

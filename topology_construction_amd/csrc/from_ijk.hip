@@ -153,7 +153,7 @@ __global__ void __launch_bounds__(256) k_voxel_cand(const int32_t* ijk, const in
 
 __global__ void __launch_bounds__(256) k_voxel_leaf(const int32_t* ijk, const int32_t* vcand, i64 n,
                                                     const u64* cand_child, const uint16_t* cand_prefix,
-                                                    const int32_t* leaf_base, i64 n_leaf, u64* leaf_mask) {
+                                                    const i64* cand_scan, i64 n_leaf, u64* leaf_mask) {
   const i64 i = (i64)blockIdx.x * 256 + threadIdx.x;
   if (i >= n) return;
   const i64 c = vcand[i];
@@ -161,7 +161,8 @@ __global__ void __launch_bounds__(256) k_voxel_leaf(const int32_t* ijk, const in
   const int32_t x = ijk[i * 3], y = ijk[i * 3 + 1], z = ijk[i * 3 + 2];
   const int lb = (((x >> 3) & 15) * 16 + ((y >> 3) & 15)) * 16 + ((z >> 3) & 15);
   const int w = lb >> 6, b = lb & 63;
-  const i64 leaf = leaf_base[c] + cand_prefix[c * 64 + w] + popc64(cand_child[c * 64 + w] & ((1ull << b) - 1));
+  const i64 leaf = (i64)(cand_scan[c] & 0xffffffffll) + cand_prefix[c * 64 + w] +
+                   popc64(cand_child[c * 64 + w] & ((1ull << b) - 1));
   if (leaf < 0 || leaf >= n_leaf) return;  // consistency guard
   atomicOr((unsigned long long*)&leaf_mask[leaf * 8 + (x & 7)], 1ull << ((y & 7) * 8 + (z & 7)));
 }
@@ -269,10 +270,8 @@ tc_grid_batch* build_from_ijk(const int32_t* d_ijk, const int64_t* h_off, int32_
   const size_t o_corig = a3.reserve(16 * (i64)nc);
   const size_t o_cchild = a3.reserve(512 * (i64)nc);
   const size_t o_cpre = a3.reserve(128 * (i64)nc);
-  const size_t o_clc = a3.reserve(4 * (i64)nc);
-  const size_t o_cne = a3.reserve(4 * (i64)nc);
-  const size_t o_lb = a3.reserve(4 * ((i64)nc + 1));
-  const size_t o_lex = a3.reserve(4 * ((i64)nc + 1));
+  const size_t o_clc = a3.reserve(8 * (i64)nc);
+  const size_t o_lb = a3.reserve(8 * ((i64)nc + 1));
   const size_t o_ginfo = a3.reserve(4 * 6 * (i64)B);
   const size_t o_rb3 = a3.reserve(4 * (4 + 3 * (i64)B));
   a3.commit();
@@ -280,10 +279,8 @@ tc_grid_batch* build_from_ijk(const int32_t* d_ijk, const int64_t* h_off, int32_
   ts.cand_origin = a3.at<int4>(o_corig);
   ts.cand_child = a3.at<u64>(o_cchild);
   ts.cand_prefix = a3.at<uint16_t>(o_cpre);
-  ts.cand_leaf_count = a3.at<int32_t>(o_clc);
-  ts.cand_nonempty = a3.at<int32_t>(o_cne);
-  ts.leaf_base = a3.at<int32_t>(o_lb);
-  ts.lower_excl = a3.at<int32_t>(o_lex);
+  ts.cand_counts = a3.at<i64>(o_clc);
+  ts.cand_scan = a3.at<i64>(o_lb);
   ts.grid_info = a3.at<int32_t>(o_ginfo);
   ts.readback = a3.at<int32_t>(o_rb3);
   ts.flags = ts.readback;
@@ -314,7 +311,7 @@ tc_grid_batch* build_from_ijk(const int32_t* d_ijk, const int64_t* h_off, int32_
     tree_write_nodes(ts, ov, post.at<int32_t>(o_lc), s);
     fill_u64(ov.leaf_mask, 0, 8 * L, nullptr, 1, s);
     launch("k_voxel_leaf", k_voxel_leaf, ceil_div(N, 256), 256, s, d_ijk, (const int32_t*)vcand, N,
-           (const u64*)ts.cand_child, (const uint16_t*)ts.cand_prefix, (const int32_t*)ts.leaf_base, L,
+           (const u64*)ts.cand_child, (const uint16_t*)ts.cand_prefix, (const i64*)ts.cand_scan, L,
            ov.leaf_mask);
     tree_leaf_stats(ov, post.at<i64>(o_lv), post.at<uint32_t>(o_box), s);
     tree_finalize_leaves(ov, post.at<i64>(o_lv), post.at<uint32_t>(o_box), post.at<i64>(o_vx),

@@ -181,12 +181,18 @@ inline i64 ceil_div(i64 a, i64 b) { return (a + b - 1) / b; }
 // ------------------------------------------------------------------ primitives (primitives.hip)
 // Exclusive scan of n items (n read from d_n when non-null, else n_host; n_host
 // is the launch bound). out has n+1 entries; out[n] = total.
-void scan_excl_i32(const int32_t* in, int32_t* out, i64 n_host, const int32_t* d_n, hipStream_t s);
-void scan_excl_i64(const i64* in, i64* out, i64 n_host, const int32_t* d_n, hipStream_t s);
+// total_out, when given, also receives the total (device memory).
+void scan_excl_i32(const int32_t* in, int32_t* out, i64 n_host, const int32_t* d_n, hipStream_t s,
+                   int32_t* total_out = nullptr);
+void scan_excl_i64(const i64* in, i64* out, i64 n_host, const int32_t* d_n, hipStream_t s,
+                   i64* total_out = nullptr);
 void scan_excl_u32(const uint32_t* in, uint32_t* out, i64 n_host, const int32_t* d_n, hipStream_t s);
 
 void fill_i32(int32_t* p, int32_t v, i64 n_host, const int32_t* d_n, int32_t mult, hipStream_t s);
 void fill_u64(u64* p, u64 v, i64 n_host, const int32_t* d_n, int32_t mult, hipStream_t s);
+void fill_pair(int32_t* a, int32_t va, i64 na_host, int32_t mult_a, u64* b, u64 vb, i64 nb_host, int32_t mult_b,
+               const int32_t* d_n, hipStream_t s);
+void fill_split_i32(int32_t* p, int32_t v0, i64 n0, int32_t v1, i64 n1, hipStream_t s);
 
 // Sorts (key_hi, key_lo) 128-bit keys with uint32 values ascending. `key_bits`
 // bounds the significant low bits of every key (keys above them compare by
@@ -220,14 +226,12 @@ struct TreeScratch {
   int32_t* upper_excl;       // [cap_tiles + 1]
   int32_t* grid_tile_begin;  // [B + 1]
   // candidate lowers
-  int32_t* d_num_cands;      // points at tile_lower_base[num_tiles] after the tile scan
+  int32_t* d_num_cands;      // [1] candidate lowers (total of the tile scan)
   int4* cand_origin;         // [cap_cands] x, y, z (voxel origin), tile
   u64* cand_child;           // [cap_cands][64]
   uint16_t* cand_prefix;     // [cap_cands][64]
-  int32_t* cand_leaf_count;  // [cap_cands]
-  int32_t* cand_nonempty;    // [cap_cands]
-  int32_t* leaf_base;        // [cap_cands + 1]
-  int32_t* lower_excl;       // [cap_cands + 1]
+  i64* cand_counts;          // [cap_cands] leaf count | non-empty << 32
+  i64* cand_scan;            // [cap_cands + 1] exclusive scan: first leaf | output lower index << 32
   // per-grid results
   int32_t* grid_info;        // [B][6]: nU, nL1, nL, uBegin, lBegin, leafBegin
   int32_t* readback;         // [4 + 3B]: flags, N2, N1, L, then per-grid counts

@@ -127,6 +127,220 @@ __global__ void __launch_bounds__(256) k_tile_scatter(const Key128* keys, const 
   }
 }
 
+// ------------------------------------------------------------------ candidate pruning
+// A source node proposes target j (a neighbour for box ops, a child octant for
+// refine) only when one of its own children can reach it: for box offset e,
+// a child on the boundary face/edge/corner that e points to; for refine, a child
+// inside octant j. Coarsen always proposes its single target. The leaf-level
+// marking only ever reaches targets that pass this test, because the child it
+// comes from is itself the witness.
+
+// Lower node: 16^3 leaves in 64 words; word x*4 + (y >> 2), bit (y & 3)*16 + z.
+__device__ __forceinline__ bool lower_reaches(const u64* m, int op, int j) {
+  if (op == TC_OP_COARSEN) return true;
+  if (op == TC_OP_REFINE) {
+    const I3 q = octant(j);
+    const u64 zm = q.z ? 0xff00ff00ff00ff00ull : 0x00ff00ff00ff00ffull;
+    u64 acc = 0;
+    for (i64 x = 8 * q.x; x < 8 * q.x + 8; ++x) acc |= m[x * 4 + 2 * q.y] | m[x * 4 + 2 * q.y + 1];
+    return (acc & zm) != 0;
+  }
+  const I3 e = box_offset(j, op);
+  if (e.x == 0 && e.y == 0 && e.z == 0) return true;
+  const int x0 = e.x > 0 ? 15 : 0, x1 = e.x < 0 ? 0 : 15;
+  const u64 zm = e.z > 0 ? 0x8000800080008000ull : (e.z < 0 ? 0x0001000100010001ull : ~0ull);
+  u64 acc = 0;
+  for (int x = x0; x <= x1; ++x) {
+    if (e.y > 0) acc |= m[x * 4 + 3] & 0xffff000000000000ull;  // y = 15
+    else if (e.y < 0) acc |= m[x * 4] & 0xffffull;              // y = 0
+    else acc |= m[x * 4] | m[x * 4 + 1] | m[x * 4 + 2] | m[x * 4 + 3];
+  }
+  return (acc & zm) != 0;
+}
+
+// Upper node: 32^3 lowers in 512 words; word x*16 + (y >> 1), bit (y & 1)*32 + z.
+// Returns the set of targets j reachable from the lowers present in word w.
+__device__ __forceinline__ uint32_t upper_word_code(u64 word, int w, int op, int m) {
+  if (!word) return 0;
+  const int ux = w >> 4;
+  if (op == TC_OP_REFINE) {
+    const int qx = ux >> 4, qy = (w & 15) >> 3;
+    uint32_t code = 0;
+    if (word & 0x0000ffff0000ffffull) code |= 1u << octant_index(qx, qy, 0);
+    if (word & 0xffff0000ffff0000ull) code |= 1u << octant_index(qx, qy, 1);
+    return code;
+  }
+  uint32_t code = 0;
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t v = (uint32_t)(word >> (32 * h));
+    if (!v) continue;
+    const int uy = 2 * (w & 15) + h;
+    for (int j = 0; j < m; ++j) {
+      const I3 e = box_offset(j, op);
+      const bool okx = e.x == 0 || (e.x > 0 ? ux == 31 : ux == 0);
+      const bool oky = e.y == 0 || (e.y > 0 ? uy == 31 : uy == 0);
+      const bool okz = e.z == 0 || (e.z > 0 ? (v >> 31) != 0 : (v & 1u) != 0);
+      if (okx && oky && okz) code |= 1u << j;
+    }
+  }
+  return code;
+}
+
+// ------------------------------------------------------------------ stage: tiles, fused (small batches)
+// At most 4096 tile candidates: one workgroup builds the reach code of every
+// source upper, emits the pruned candidates, sorts them in LDS (bitonic over
+// (key, value)), flags and scans the unique keys, scatters the unique tiles and
+// every candidate's tile index, writes the per-grid tile ranges and, when asked
+// (few tiles), zeroes the unique tiles' lower bitmaps; more tiles get a wide fill.
+constexpr int kTilesMax = 4096;
+constexpr int kTilesThreads = 1024;
+constexpr int kTilesItems = kTilesMax / kTilesThreads;
+
+__global__ void __launch_bounds__(kTilesThreads) k_tiles_small(const int4* upper_origin, const u64* upper_mask,
+                                                               int32_t n_upper, int op, int m, int32_t B,
+                                                               int4* utile, int32_t* tile_of_cand,
+                                                               int32_t* d_num_tiles, int32_t* grid_tile_begin,
+                                                               u64* tile_child, int zero_child, int32_t* readback) {
+  __shared__ u64 s_hi[kTilesMax];
+  __shared__ u64 s_lo[kTilesMax];
+  __shared__ uint32_t s_v[kTilesMax];
+  __shared__ int32_t s_g[kTilesMax];
+  __shared__ uint32_t s_code[kTilesMax];
+  __shared__ int32_t s_wave[kTilesThreads / kWave];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wv = tid / kWave;
+  const int n = n_upper * m;
+  if (tid == 0) readback[0] = 0;
+  if (op != TC_OP_COARSEN) {
+    for (int u = wv; u < n_upper; u += kTilesThreads / kWave) {
+      uint32_t code = 0;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int w = lane * 8 + k;
+        code |= upper_word_code(upper_mask[(i64)u * 512 + w], w, op, m);
+      }
+#pragma unroll
+      for (int d = 32; d >= 1; d >>= 1) code |= (uint32_t)__shfl_xor((int)code, d, kWave);
+      if (lane == 0) s_code[u] = code;
+    }
+  }
+  __syncthreads();
+  int P = 2;
+  while (P < n) P <<= 1;
+  for (int i = tid; i < P; i += kTilesThreads) {
+    u64 hi = ~0ull, lo = ~0ull;
+    uint32_t v = 0xffffffffu;
+    if (i < n) {
+      v = (uint32_t)i;
+      const int u = i / m, j = i % m;
+      const int4 o = upper_origin[u];
+      const i64 tx = o.x >> 12, ty = o.y >> 12, tz = o.z >> 12;
+      I3 t;
+      bool keep = true;
+      if (op == TC_OP_REFINE) {
+        const I3 q = octant(j);
+        t = {2 * tx + q.x, 2 * ty + q.y, 2 * tz + q.z};
+        keep = (s_code[u] >> j) & 1u;
+      } else if (op == TC_OP_COARSEN) {
+        t = {tx >> 1, ty >> 1, tz >> 1};
+      } else {
+        const I3 e = box_offset(j, op);
+        t = {tx + e.x, ty + e.y, tz + e.z};
+        if (e.x != 0 || e.y != 0 || e.z != 0) keep = (s_code[u] >> j) & 1u;
+      }
+      if (keep && tile_ok(t.x) && tile_ok(t.y) && tile_ok(t.z)) {
+        const u64 g = (uint32_t)o.w;
+        lo = ((g & 15ull) << 60) | ((u64)(t.x + kTileBias) << 40) | ((u64)(t.y + kTileBias) << 20) |
+             (u64)(t.z + kTileBias);
+        hi = g >> 4;
+      }
+    }
+    s_hi[i] = hi;
+    s_lo[i] = lo;
+    s_v[i] = v;
+  }
+  __syncthreads();
+  // bitonic sort by (key, value): padding (all-ones key, value 0xffffffff) sorts last
+  for (int k = 2; k <= P; k <<= 1) {
+    for (int jj = k >> 1; jj > 0; jj >>= 1) {
+      for (int i = tid; i < P; i += kTilesThreads) {
+        const int ixj = i ^ jj;
+        if (ixj > i) {
+          const bool up = (i & k) == 0;
+          const u64 ah = s_hi[i], al = s_lo[i], bh = s_hi[ixj], bl = s_lo[ixj];
+          const uint32_t av = s_v[i], bv = s_v[ixj];
+          const bool gt = ah != bh ? ah > bh : (al != bl ? al > bl : av > bv);
+          if (gt == up) {
+            s_hi[i] = bh;
+            s_lo[i] = bl;
+            s_v[i] = bv;
+            s_hi[ixj] = ah;
+            s_lo[ixj] = al;
+            s_v[ixj] = av;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  // heads of valid keys and their exclusive scan (blocked, 4 items per thread)
+  int f[kTilesItems];
+  int sum = 0;
+#pragma unroll
+  for (int k = 0; k < kTilesItems; ++k) {
+    const int i = tid * kTilesItems + k;
+    bool h = false;
+    if (i < n && !(s_hi[i] == ~0ull && s_lo[i] == ~0ull))
+      h = i == 0 || !(s_hi[i] == s_hi[i - 1] && s_lo[i] == s_lo[i - 1]);
+    f[k] = h ? 1 : 0;
+    sum += f[k];
+  }
+  int total;
+  int ex = block_excl_scan<int, kTilesThreads>(sum, s_wave, total);
+#pragma unroll
+  for (int k = 0; k < kTilesItems; ++k) {
+    const int i = tid * kTilesItems + k;
+    if (i < n) {
+      const uint32_t v = s_v[i];
+      if (v < (uint32_t)n) {
+        if (s_hi[i] == ~0ull && s_lo[i] == ~0ull) {
+          tile_of_cand[v] = -1;
+        } else {
+          const int t = ex + f[k] - 1;
+          tile_of_cand[v] = t;
+          if (f[k]) {
+            const u64 kh = s_hi[i], kl = s_lo[i];
+            const int32_t g = (int32_t)((kh << 4) | (kl >> 60));
+            utile[t] = make_int4((int32_t)((kl >> 40) & 0xfffff) - kTileBias,
+                                 (int32_t)((kl >> 20) & 0xfffff) - kTileBias, (int32_t)(kl & 0xfffff) - kTileBias, g);
+            s_g[t] = g;
+          }
+        }
+      }
+    }
+    ex += f[k];
+  }
+  if (tid == 0) *d_num_tiles = total;
+  __syncthreads();
+  const int nt = total;
+  if (nt == 0) {
+    for (int g = tid; g <= B; g += kTilesThreads) grid_tile_begin[g] = 0;
+  } else {
+    for (int t = tid; t < nt; t += kTilesThreads) {
+      const int g = s_g[t];
+      const int gp = t == 0 ? -1 : s_g[t - 1];
+      for (int q = gp + 1; q <= g; ++q) grid_tile_begin[q] = t;
+      if (t == nt - 1)
+        for (int q = g + 1; q <= B; ++q) grid_tile_begin[q] = nt;
+    }
+  }
+  if (zero_child) {
+    ulonglong2* tc = reinterpret_cast<ulonglong2*>(tile_child);
+    for (i64 k = tid; k < (i64)nt * 256; k += kTilesThreads) tc[k] = make_ulonglong2(0, 0);
+  }
+}
+
 // ------------------------------------------------------------------ stage: lowers
 // Target lower of source lower K for candidate j, and the index (among the
 // parent upper's tile candidates) of the tile that holds it.
@@ -159,8 +373,8 @@ __device__ __forceinline__ int upper_child_bit(const I3& k) {
   return (int)((((k.x & 31) * 32) + (k.y & 31)) * 32 + (k.z & 31));
 }
 
-__global__ void __launch_bounds__(256) k_lower_mark(const int4* lower_origin, i64 n, int op, int m,
-                                                    const int32_t* tile_of_cand, const int32_t* d_num_tiles,
+__global__ void __launch_bounds__(256) k_lower_mark(const int4* lower_origin, const u64* lower_mask, i64 n, int op,
+                                                    int m, const int32_t* tile_of_cand, const int32_t* d_num_tiles,
                                                     u64* tile_child, int32_t* flags) {
   const i64 i = (i64)blockIdx.x * 256 + threadIdx.x;
   if (i >= n) return;
@@ -168,7 +382,7 @@ __global__ void __launch_bounds__(256) k_lower_mark(const int4* lower_origin, i6
   const int j = (int)(i % m);
   const int4 o = lower_origin[l];
   const LowerTarget tg = lower_target(o, j, op);
-  if (!tg.ok) return;
+  if (!tg.ok || !lower_reaches(lower_mask + l * 64, op, j)) return;
   const int32_t t = tile_of_cand[(i64)o.w * m + tg.jt];
   if (t < 0 || t >= *d_num_tiles) {
     set_flag(flags, kFlagInternal);
@@ -178,7 +392,8 @@ __global__ void __launch_bounds__(256) k_lower_mark(const int4* lower_origin, i6
   atomicOr((unsigned long long*)&tile_child[(i64)t * 512 + (bit >> 6)], 1ull << (bit & 63));
 }
 
-__global__ void __launch_bounds__(256) k_lower_nbr(const int4* lower_origin, i64 n, int op, int m, int m_src,
+__global__ void __launch_bounds__(256) k_lower_nbr(const int4* lower_origin, const u64* lower_mask, i64 n, int op,
+                                                   int m, int m_src,
                                                    const int32_t* tile_of_cand, const u64* tile_child,
                                                    const uint16_t* tile_prefix, const int32_t* tile_lower_base,
                                                    const int32_t* d_num_tiles, const int32_t* d_num_cands,
@@ -190,7 +405,7 @@ __global__ void __launch_bounds__(256) k_lower_nbr(const int4* lower_origin, i64
   const int j = (int)(i % m);
   const int4 o = lower_origin[l];
   const LowerTarget tg = lower_target(o, j, op);
-  if (!tg.ok) {
+  if (!tg.ok || !lower_reaches(lower_mask + l * 64, op, j)) {
     lower_nbr[i] = -1;
     return;
   }
@@ -541,12 +756,14 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa) 
     throw Error(TC_ERR_UNSUPPORTED, "pass: source batch too large");
 
   Arena a(s);
-  const size_t o_keys = a.reserve(sizeof(Key128) * nT);
-  const size_t o_vals = a.reserve(4 * nT);
-  const size_t o_head = a.reserve(4 * nT);
-  const size_t o_texcl = a.reserve(4 * (nT + 1));
+  const bool small_tiles = nT > 0 && nT <= kTilesMax;
+  const i64 nTs = small_tiles ? 0 : nT;  // sort scratch only for the multi-kernel tile path
+  const size_t o_keys = a.reserve(sizeof(Key128) * nTs);
+  const size_t o_vals = a.reserve(4 * nTs);
+  const size_t o_head = a.reserve(4 * nTs);
+  const size_t o_texcl = a.reserve(4 * (nTs + 1));
   const size_t o_toc = a.reserve(4 * nT);
-  const size_t o_zero = a.reserve(4);
+  const size_t o_ntiles = a.reserve(4);
   const size_t o_ncand = a.reserve(4);
   const size_t o_utile = a.reserve(16 * nT);
   const size_t o_tchild = a.reserve(4096 * nT);
@@ -559,10 +776,8 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa) 
   const size_t o_corig = a.reserve(16 * nL);
   const size_t o_cchild = a.reserve(512 * nL);
   const size_t o_cpre = a.reserve(128 * nL);
-  const size_t o_clc = a.reserve(4 * nL);
-  const size_t o_cne = a.reserve(4 * nL);
-  const size_t o_lb = a.reserve(4 * (nL + 1));
-  const size_t o_lex = a.reserve(4 * (nL + 1));
+  const size_t o_ccnt = a.reserve(8 * nL);
+  const size_t o_cscan = a.reserve(8 * (nL + 1));
   const size_t o_nbr = a.reserve(4 * nL);
   const size_t o_csrc = a.reserve(4 * nL * oi.m_src);
   const size_t o_ginfo = a.reserve(4 * 6 * (i64)B);
@@ -572,6 +787,7 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa) 
   TreeScratch ts{};
   ts.cap_tiles = nT;
   ts.cap_cands = nL;
+  ts.d_num_tiles = a.at<int32_t>(o_ntiles);
   ts.utile = a.at<int4>(o_utile);
   ts.tile_child = a.at<u64>(o_tchild);
   ts.tile_prefix = a.at<uint16_t>(o_tpre);
@@ -584,50 +800,57 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa) 
   ts.cand_origin = a.at<int4>(o_corig);
   ts.cand_child = a.at<u64>(o_cchild);
   ts.cand_prefix = a.at<uint16_t>(o_cpre);
-  ts.cand_leaf_count = a.at<int32_t>(o_clc);
-  ts.cand_nonempty = a.at<int32_t>(o_cne);
-  ts.leaf_base = a.at<int32_t>(o_lb);
-  ts.lower_excl = a.at<int32_t>(o_lex);
+  ts.cand_counts = a.at<i64>(o_ccnt);
+  ts.cand_scan = a.at<i64>(o_cscan);
   ts.grid_info = a.at<int32_t>(o_ginfo);
   ts.readback = a.at<int32_t>(o_rb);
   ts.flags = ts.readback;
-  Key128* keys = a.at<Key128>(o_keys);
-  uint32_t* vals = a.at<uint32_t>(o_vals);
-  int32_t* head = a.at<int32_t>(o_head);
-  int32_t* texcl = a.at<int32_t>(o_texcl);
   int32_t* tile_of_cand = a.at<int32_t>(o_toc);
   int32_t* lower_nbr = a.at<int32_t>(o_nbr);
   int32_t* cand_src = a.at<int32_t>(o_csrc);
 
-  fill_i32(ts.readback, 0, 1, nullptr, 1, s);
   // tiles
-  if (nT > 0) {
-    launch("k_tile_candidates", k_tile_candidates, ceil_div(nT, 256), 256, s, (const int4*)sv.upper_origin, nT,
-           op, oi.m, keys, vals);
-    sort_pairs_128(keys, vals, nT, tile_key_bits(B), s);
-    launch("k_tile_heads", k_tile_heads, ceil_div(nT, 256), 256, s, (const Key128*)keys, nT, head);
-    scan_excl_i32(head, texcl, nT, nullptr, s);
-    launch("k_tile_scatter", k_tile_scatter, ceil_div(nT, 256), 256, s, (const Key128*)keys,
-           (const uint32_t*)vals, (const int32_t*)head, (const int32_t*)texcl, nT, ts.utile, tile_of_cand, ts.flags);
-    ts.d_num_tiles = texcl + nT;
+  if (small_tiles) {
+    const bool zero_in_kernel = nT <= 256;  // at most 1 MiB of bitmaps for one workgroup
+    launch("k_tiles_small", k_tiles_small, 1, kTilesThreads, s, (const int4*)sv.upper_origin,
+           (const u64*)sv.upper_mask, (int32_t)src->n2, op, oi.m, B, ts.utile, tile_of_cand, ts.d_num_tiles,
+           ts.grid_tile_begin, ts.tile_child, zero_in_kernel ? 1 : 0, ts.readback);
+    if (!zero_in_kernel) fill_u64(ts.tile_child, 0, nT * 512, ts.d_num_tiles, 512, s);
   } else {
-    int32_t* zero = a.at<int32_t>(o_zero);
-    fill_i32(zero, 0, 1, nullptr, 1, s);
-    ts.d_num_tiles = zero;
+    fill_i32(ts.readback, 0, 1, nullptr, 1, s);
+    if (nT > 0) {
+      Key128* keys = a.at<Key128>(o_keys);
+      uint32_t* vals = a.at<uint32_t>(o_vals);
+      int32_t* head = a.at<int32_t>(o_head);
+      int32_t* texcl = a.at<int32_t>(o_texcl);
+      launch("k_tile_candidates", k_tile_candidates, ceil_div(nT, 256), 256, s, (const int4*)sv.upper_origin, nT,
+             op, oi.m, keys, vals);
+      sort_pairs_128(keys, vals, nT, tile_key_bits(B), s);
+      launch("k_tile_heads", k_tile_heads, ceil_div(nT, 256), 256, s, (const Key128*)keys, nT, head);
+      scan_excl_i32(head, texcl, nT, nullptr, s, ts.d_num_tiles);
+      launch("k_tile_scatter", k_tile_scatter, ceil_div(nT, 256), 256, s, (const Key128*)keys,
+             (const uint32_t*)vals, (const int32_t*)head, (const int32_t*)texcl, nT, ts.utile, tile_of_cand,
+             ts.flags);
+    } else {
+      fill_i32(ts.d_num_tiles, 0, 1, nullptr, 1, s);
+    }
+    tree_tile_ranges(ts, B, s);
+    fill_u64(ts.tile_child, 0, nT * 512, ts.d_num_tiles, 512, s);
   }
-  tree_tile_ranges(ts, B, s);
   // lowers
-  fill_u64(ts.tile_child, 0, nT * 512, ts.d_num_tiles, 512, s);
-  launch("k_lower_mark", k_lower_mark, ceil_div(nL, 256), 256, s, (const int4*)sv.lower_origin, nL, op, oi.m,
-         (const int32_t*)tile_of_cand, (const int32_t*)ts.d_num_tiles, ts.tile_child, ts.flags);
+  launch("k_lower_mark", k_lower_mark, ceil_div(nL, 256), 256, s, (const int4*)sv.lower_origin,
+         (const u64*)sv.lower_mask, nL, op, oi.m, (const int32_t*)tile_of_cand, (const int32_t*)ts.d_num_tiles,
+         ts.tile_child, ts.flags);
   tree_rank_tiles(ts, s);
-  fill_i32(cand_src, -1, nL * oi.m_src, ts.d_num_cands, oi.m_src, s);
-  launch("k_lower_nbr", k_lower_nbr, ceil_div(nL, 256), 256, s, (const int4*)sv.lower_origin, nL, op, oi.m,
-         oi.m_src, (const int32_t*)tile_of_cand, (const u64*)ts.tile_child, (const uint16_t*)ts.tile_prefix,
-         (const int32_t*)ts.tile_lower_base, (const int32_t*)ts.d_num_tiles, (const int32_t*)ts.d_num_cands,
-         lower_nbr, ts.cand_origin, cand_src, ts.flags);
-  // leaves (pass A); refine overwrites every word of its candidates, the others OR into zeros
-  if (op != TC_OP_REFINE) fill_u64(ts.cand_child, 0, nL * 64, ts.d_num_cands, 64, s);
+  // candidate -> source table starts empty; refine overwrites every word of its
+  // candidates' leaf masks, the other ops OR into zeros
+  fill_pair(cand_src, -1, nL * oi.m_src, oi.m_src, ts.cand_child, 0, op == TC_OP_REFINE ? 0 : nL * 64, 64,
+            ts.d_num_cands, s);
+  launch("k_lower_nbr", k_lower_nbr, ceil_div(nL, 256), 256, s, (const int4*)sv.lower_origin,
+         (const u64*)sv.lower_mask, nL, op, oi.m, oi.m_src, (const int32_t*)tile_of_cand, (const u64*)ts.tile_child,
+         (const uint16_t*)ts.tile_prefix, (const int32_t*)ts.tile_lower_base, (const int32_t*)ts.d_num_tiles,
+         (const int32_t*)ts.d_num_cands, lower_nbr, ts.cand_origin, cand_src, ts.flags);
+  // leaves (pass A)
   launch("k_leaf_mark_lower", k_leaf_mark_lower, (i64)src->n1, 256, s, (const int4*)sv.leaf_origin,
          (const u64*)sv.leaf_mask, (const int32_t*)sv.lower_first, (const u64*)sv.lower_mask,
          (const uint16_t*)sv.lower_prefix, op, oi.m, (const int32_t*)lower_nbr, (const int32_t*)ts.d_num_cands,

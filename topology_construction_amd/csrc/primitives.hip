@@ -20,7 +20,7 @@ __device__ __forceinline__ i64 clamp_n(i64 n_host, const int32_t* d_n) {
 
 template <typename T>
 __global__ void __launch_bounds__(kScanThreads) k_scan_single(const T* in, T* out, i64 n_host,
-                                                              const int32_t* d_n) {
+                                                              const int32_t* d_n, T* total_out) {
   __shared__ T s_wave[kScanThreads / kWave];
   const i64 n = clamp_n(n_host, d_n);
   T v[kScanItems];
@@ -40,7 +40,10 @@ __global__ void __launch_bounds__(kScanThreads) k_scan_single(const T* in, T* ou
     if (i < n) out[i] = excl;
     excl += v[k];
   }
-  if (threadIdx.x == 0) out[n] = total;
+  if (threadIdx.x == 0) {
+    out[n] = total;
+    if (total_out) *total_out = total;
+  }
 }
 
 template <typename T>
@@ -63,7 +66,7 @@ __global__ void __launch_bounds__(kScanThreads) k_scan_reduce(const T* in, T* pa
 // One workgroup: exclusive scan of the per-block partials, in place, chunk by chunk.
 template <typename T>
 __global__ void __launch_bounds__(kScanThreads) k_scan_partials(T* partial, i64 nblk, T* out, i64 n_host,
-                                                                const int32_t* d_n) {
+                                                                const int32_t* d_n, T* total_out) {
   __shared__ T s_wave[kScanThreads / kWave];
   T carry = 0;
   for (i64 c = 0; c < nblk; c += kScanTile) {
@@ -86,7 +89,10 @@ __global__ void __launch_bounds__(kScanThreads) k_scan_partials(T* partial, i64 
     }
     carry += total;
   }
-  if (threadIdx.x == 0) out[clamp_n(n_host, d_n)] = carry;
+  if (threadIdx.x == 0) {
+    out[clamp_n(n_host, d_n)] = carry;
+    if (total_out) *total_out = carry;
+  }
 }
 
 template <typename T>
@@ -115,22 +121,24 @@ __global__ void __launch_bounds__(kScanThreads) k_scan_down(const T* in, T* out,
 }
 
 template <typename T>
-static void scan_excl(const char* tag, const T* in, T* out, i64 n_host, const int32_t* d_n, hipStream_t s) {
+static void scan_excl(const char* tag, const T* in, T* out, i64 n_host, const int32_t* d_n, hipStream_t s,
+                      T* total_out) {
   (void)tag;
   if (n_host <= 0) {
     // n is zero: out[0] = 0
-    launch("k_scan_single", k_scan_single<T>, 1, kScanThreads, s, in, out, (i64)0, (const int32_t*)nullptr);
+    launch("k_scan_single", k_scan_single<T>, 1, kScanThreads, s, in, out, (i64)0, (const int32_t*)nullptr,
+           total_out);
     return;
   }
   if (n_host <= kScanTile) {
-    launch("k_scan_single", k_scan_single<T>, 1, kScanThreads, s, in, out, n_host, d_n);
+    launch("k_scan_single", k_scan_single<T>, 1, kScanThreads, s, in, out, n_host, d_n, total_out);
     return;
   }
   const i64 nblk = ceil_div(n_host, kScanTile);
   T* partial = static_cast<T*>(device_alloc_async(sizeof(T) * (size_t)nblk, s));
   try {
     launch("k_scan_reduce", k_scan_reduce<T>, nblk, kScanThreads, s, in, partial, n_host, d_n);
-    launch("k_scan_partials", k_scan_partials<T>, 1, kScanThreads, s, partial, nblk, out, n_host, d_n);
+    launch("k_scan_partials", k_scan_partials<T>, 1, kScanThreads, s, partial, nblk, out, n_host, d_n, total_out);
     launch("k_scan_down", k_scan_down<T>, nblk, kScanThreads, s, in, out, (const T*)partial, n_host, d_n);
   } catch (...) {
     device_free_async(partial, s);
@@ -139,14 +147,15 @@ static void scan_excl(const char* tag, const T* in, T* out, i64 n_host, const in
   device_free_async(partial, s);
 }
 
-void scan_excl_i32(const int32_t* in, int32_t* out, i64 n_host, const int32_t* d_n, hipStream_t s) {
-  scan_excl("i32", in, out, n_host, d_n, s);
+void scan_excl_i32(const int32_t* in, int32_t* out, i64 n_host, const int32_t* d_n, hipStream_t s,
+                   int32_t* total_out) {
+  scan_excl("i32", in, out, n_host, d_n, s, total_out);
 }
-void scan_excl_i64(const i64* in, i64* out, i64 n_host, const int32_t* d_n, hipStream_t s) {
-  scan_excl("i64", in, out, n_host, d_n, s);
+void scan_excl_i64(const i64* in, i64* out, i64 n_host, const int32_t* d_n, hipStream_t s, i64* total_out) {
+  scan_excl("i64", in, out, n_host, d_n, s, total_out);
 }
 void scan_excl_u32(const uint32_t* in, uint32_t* out, i64 n_host, const int32_t* d_n, hipStream_t s) {
-  scan_excl("u32", in, out, n_host, d_n, s);
+  scan_excl("u32", in, out, n_host, d_n, s, (uint32_t*)nullptr);
 }
 
 // ------------------------------------------------------------------ fills
@@ -160,6 +169,34 @@ __global__ void __launch_bounds__(256) k_fill(T* p, T v, i64 n_host, const int32
 static i64 fill_blocks(i64 n) {
   i64 b = ceil_div(n, 256);
   return b > 8192 ? 8192 : b;
+}
+
+// Two fills in one launch: a[0 .. na) = va and b[0 .. nb) = vb, where na / nb are
+// d_n * mult_a / d_n * mult_b when d_n is given (bounded by the host counts).
+__global__ void __launch_bounds__(256) k_fill_pair(int32_t* a, int32_t va, i64 na_host, int32_t mult_a, u64* b, u64 vb,
+                                                   i64 nb_host, int32_t mult_b, const int32_t* d_n) {
+  i64 na = d_n ? (i64)(*d_n) * mult_a : na_host;
+  i64 nb = d_n ? (i64)(*d_n) * mult_b : nb_host;
+  if (na > na_host) na = na_host;
+  if (nb > nb_host) nb = nb_host;
+  const i64 stride = (i64)gridDim.x * 256;
+  for (i64 i = (i64)blockIdx.x * 256 + threadIdx.x; i < na; i += stride) a[i] = va;
+  for (i64 i = (i64)blockIdx.x * 256 + threadIdx.x; i < nb; i += stride) b[i] = vb;
+}
+
+void fill_pair(int32_t* a, int32_t va, i64 na_host, int32_t mult_a, u64* b, u64 vb, i64 nb_host, int32_t mult_b,
+               const int32_t* d_n, hipStream_t s) {
+  launch("k_fill_pair", k_fill_pair, fill_blocks(na_host > nb_host ? na_host : nb_host), 256, s, a, va, na_host,
+         mult_a, b, vb, nb_host, mult_b, d_n);
+}
+
+// p[0 .. n0) = v0 and p[n0 .. n0 + n1) = v1 in one launch.
+__global__ void __launch_bounds__(256) k_fill_split(int32_t* p, int32_t v0, i64 n0, int32_t v1, i64 n1) {
+  for (i64 i = (i64)blockIdx.x * 256 + threadIdx.x; i < n0 + n1; i += (i64)gridDim.x * 256) p[i] = i < n0 ? v0 : v1;
+}
+
+void fill_split_i32(int32_t* p, int32_t v0, i64 n0, int32_t v1, i64 n1, hipStream_t s) {
+  launch("k_fill_split", k_fill_split, fill_blocks(n0 + n1), 256, s, p, v0, n0, v1, n1);
 }
 
 void fill_i32(int32_t* p, int32_t v, i64 n_host, const int32_t* d_n, int32_t mult, hipStream_t s) {

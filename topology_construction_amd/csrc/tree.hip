@@ -59,23 +59,24 @@ __global__ void __launch_bounds__(256) k_tile_rank(const u64* tile_child, uint16
   if (threadIdx.x == 0) tile_lower_count[t] = total;
 }
 
-__global__ void k_copy_at(const int32_t* src, const int32_t* d_index, int32_t* dst) {
-  if (threadIdx.x == 0 && blockIdx.x == 0) *dst = src[*d_index];
-}
-
 void tree_rank_tiles(TreeScratch& ts, hipStream_t s) {
   launch("k_tile_rank", k_tile_rank, ts.cap_tiles, 256, s, (const u64*)ts.tile_child, ts.tile_prefix,
          ts.tile_lower_count, (const int32_t*)ts.d_num_tiles);
-  scan_excl_i32(ts.tile_lower_count, ts.tile_lower_base, ts.cap_tiles, ts.d_num_tiles, s);
-  launch("k_copy_at", k_copy_at, 1, 64, s, (const int32_t*)ts.tile_lower_base, (const int32_t*)ts.d_num_tiles,
-         ts.d_num_cands);
+  // the total of the scan is the number of candidate lowers
+  scan_excl_i32(ts.tile_lower_count, ts.tile_lower_base, ts.cap_tiles, ts.d_num_tiles, s, ts.d_num_cands);
 }
 
 // ------------------------------------------------------------------ candidate lowers
+// cand_counts[c] packs the candidate's leaf count (low 32 bits) and its
+// non-empty flag (high 32 bits); one 64-bit exclusive scan then gives, per
+// candidate, its first output leaf (low half) and its output lower index (high
+// half). Totals stay below 2^31, so the halves never carry into each other.
+__device__ __forceinline__ int32_t scan_leaf(i64 v) { return (int32_t)(v & 0xffffffffll); }
+__device__ __forceinline__ int32_t scan_lower(i64 v) { return (int32_t)(v >> 32); }
+
 // One wave per candidate lower: per-word exclusive popcount prefix of its 64-word
-// leaf mask, leaf count and non-empty flag.
-__global__ void __launch_bounds__(256) k_lower_count(const u64* cand_child, uint16_t* cand_prefix,
-                                                     int32_t* cand_leaf_count, int32_t* cand_nonempty,
+// leaf mask and its packed count.
+__global__ void __launch_bounds__(256) k_lower_count(const u64* cand_child, uint16_t* cand_prefix, i64* cand_counts,
                                                      const int32_t* d_num_cands) {
   const i64 c = (i64)blockIdx.x * 4 + threadIdx.x / kWave;
   const int lane = threadIdx.x & (kWave - 1);
@@ -84,121 +85,164 @@ __global__ void __launch_bounds__(256) k_lower_count(const u64* cand_child, uint
   const int cnt = popc64(w);
   const int inc = wave_incl_scan(cnt);
   cand_prefix[c * 64 + lane] = (uint16_t)(inc - cnt);
-  if (lane == kWave - 1) {
-    cand_leaf_count[c] = inc;
-    cand_nonempty[c] = inc > 0 ? 1 : 0;
-  }
+  if (lane == kWave - 1) cand_counts[c] = (i64)inc | ((i64)(inc > 0 ? 1 : 0) << 32);
 }
 
-__global__ void __launch_bounds__(256) k_tile_flags(const int32_t* tile_lower_base, const int32_t* leaf_base,
+__global__ void __launch_bounds__(256) k_tile_flags(const int32_t* tile_lower_base, const i64* cand_scan,
                                                     int32_t* tile_nonempty, const int32_t* d_num_tiles) {
   const i64 t = (i64)blockIdx.x * 256 + threadIdx.x;
   if (t >= *d_num_tiles) return;
-  tile_nonempty[t] = leaf_base[tile_lower_base[t + 1]] > leaf_base[tile_lower_base[t]] ? 1 : 0;
+  tile_nonempty[t] = scan_leaf(cand_scan[tile_lower_base[t + 1]]) > scan_leaf(cand_scan[tile_lower_base[t]]) ? 1 : 0;
 }
 
-// Per-grid counts and begins; thread 0 also writes the batch totals.
-__global__ void __launch_bounds__(256) k_grid_counts(const int32_t* grid_tile_begin, const int32_t* tile_lower_base,
-                                                     const int32_t* upper_excl, const int32_t* lower_excl,
-                                                     const int32_t* leaf_base, const int32_t* d_num_tiles,
-                                                     const int32_t* d_num_cands, int32_t B, int32_t* grid_info,
-                                                     int32_t* readback) {
-  const i64 g = (i64)blockIdx.x * 256 + threadIdx.x;
-  if (g == 0) {
-    readback[1] = upper_excl[*d_num_tiles];
-    readback[2] = lower_excl[*d_num_cands];
-    readback[3] = leaf_base[*d_num_cands];
-  }
-  if (g >= B) return;
+// Per-grid counts and begins of grid g (shared by both launch shapes).
+__device__ __forceinline__ void grid_counts_one(i64 g, const int32_t* grid_tile_begin, const int32_t* tile_lower_base,
+                                                const int32_t* upper_excl, const i64* cand_scan, int32_t* grid_info,
+                                                int32_t* readback) {
   const int32_t tb = grid_tile_begin[g], te = grid_tile_begin[g + 1];
-  const int32_t cb = tile_lower_base[tb], ce = tile_lower_base[te];
+  const i64 vb = cand_scan[tile_lower_base[tb]], ve = cand_scan[tile_lower_base[te]];
   const int32_t nu = upper_excl[te] - upper_excl[tb];
-  const int32_t n1 = lower_excl[ce] - lower_excl[cb];
-  const int32_t nl = leaf_base[ce] - leaf_base[cb];
+  const int32_t n1 = scan_lower(ve) - scan_lower(vb);
+  const int32_t nl = scan_leaf(ve) - scan_leaf(vb);
   int32_t* gi = grid_info + g * 6;
   gi[0] = nu;
   gi[1] = n1;
   gi[2] = nl;
   gi[3] = upper_excl[tb];
-  gi[4] = lower_excl[cb];
-  gi[5] = leaf_base[cb];
+  gi[4] = scan_lower(vb);
+  gi[5] = scan_leaf(vb);
   readback[4 + g * 3 + 0] = nu;
   readback[4 + g * 3 + 1] = n1;
   readback[4 + g * 3 + 2] = nl;
 }
 
+__device__ __forceinline__ void batch_totals(const int32_t* upper_excl, const i64* cand_scan, int32_t nt, int32_t nc,
+                                             int32_t* readback) {
+  const i64 last = cand_scan[nc];
+  readback[1] = upper_excl[nt];
+  readback[2] = scan_lower(last);
+  readback[3] = scan_leaf(last);
+}
+
+__global__ void __launch_bounds__(256) k_grid_counts(const int32_t* grid_tile_begin, const int32_t* tile_lower_base,
+                                                     const int32_t* upper_excl, const i64* cand_scan,
+                                                     const int32_t* d_num_tiles, const int32_t* d_num_cands, int32_t B,
+                                                     int32_t* grid_info, int32_t* readback) {
+  const i64 g = (i64)blockIdx.x * 256 + threadIdx.x;
+  if (g == 0) batch_totals(upper_excl, cand_scan, *d_num_tiles, *d_num_cands, readback);
+  if (g >= B) return;
+  grid_counts_one(g, grid_tile_begin, tile_lower_base, upper_excl, cand_scan, grid_info, readback);
+}
+
+// Small batches (at most 4096 tiles): non-empty tile flags, their exclusive
+// scan (output upper indices) and the per-grid counts in one workgroup.
+constexpr int kTailThreads = 1024;
+constexpr int kTailItems = 4;
+
+__global__ void __launch_bounds__(kTailThreads) k_counts_tail(const int32_t* grid_tile_begin,
+                                                              const int32_t* tile_lower_base, const i64* cand_scan,
+                                                              const int32_t* d_num_tiles, const int32_t* d_num_cands,
+                                                              int32_t B, int32_t* upper_excl, int32_t* grid_info,
+                                                              int32_t* readback) {
+  __shared__ int32_t s_wave[kTailThreads / kWave];
+  const int32_t nt = *d_num_tiles;
+  int f[kTailItems];
+  int sum = 0;
+#pragma unroll
+  for (int k = 0; k < kTailItems; ++k) {
+    const int t = threadIdx.x * kTailItems + k;
+    f[k] = (t < nt && scan_leaf(cand_scan[tile_lower_base[t + 1]]) > scan_leaf(cand_scan[tile_lower_base[t]])) ? 1 : 0;
+    sum += f[k];
+  }
+  int total;
+  int ex = block_excl_scan<int, kTailThreads>(sum, s_wave, total);
+#pragma unroll
+  for (int k = 0; k < kTailItems; ++k) {
+    const int t = threadIdx.x * kTailItems + k;
+    if (t < nt) upper_excl[t] = ex;
+    ex += f[k];
+  }
+  if (threadIdx.x == 0) upper_excl[nt] = total;
+  __syncthreads();  // upper_excl is read back below by other threads of this block
+  if (threadIdx.x == 0) batch_totals(upper_excl, cand_scan, nt, *d_num_cands, readback);
+  for (i64 g = threadIdx.x; g < B; g += kTailThreads)
+    grid_counts_one(g, grid_tile_begin, tile_lower_base, upper_excl, cand_scan, grid_info, readback);
+}
+
 void tree_count_cands(TreeScratch& ts, hipStream_t s) {
   launch("k_lower_count", k_lower_count, ceil_div(ts.cap_cands, 4), 256, s, (const u64*)ts.cand_child,
-         ts.cand_prefix, ts.cand_leaf_count, ts.cand_nonempty, (const int32_t*)ts.d_num_cands);
-  scan_excl_i32(ts.cand_leaf_count, ts.leaf_base, ts.cap_cands, ts.d_num_cands, s);
-  scan_excl_i32(ts.cand_nonempty, ts.lower_excl, ts.cap_cands, ts.d_num_cands, s);
-  launch("k_tile_flags", k_tile_flags, ceil_div(ts.cap_tiles, 256), 256, s, (const int32_t*)ts.tile_lower_base,
-         (const int32_t*)ts.leaf_base, ts.tile_nonempty, (const int32_t*)ts.d_num_tiles);
-  scan_excl_i32(ts.tile_nonempty, ts.upper_excl, ts.cap_tiles, ts.d_num_tiles, s);
+         ts.cand_prefix, ts.cand_counts, (const int32_t*)ts.d_num_cands);
+  scan_excl_i64(ts.cand_counts, ts.cand_scan, ts.cap_cands, ts.d_num_cands, s);
 }
 
 void tree_grid_counts(TreeScratch& ts, int32_t B, hipStream_t s) {
+  if (ts.cap_tiles <= (i64)kTailThreads * kTailItems) {
+    launch("k_counts_tail", k_counts_tail, 1, kTailThreads, s, (const int32_t*)ts.grid_tile_begin,
+           (const int32_t*)ts.tile_lower_base, (const i64*)ts.cand_scan, (const int32_t*)ts.d_num_tiles,
+           (const int32_t*)ts.d_num_cands, B, ts.upper_excl, ts.grid_info, ts.readback);
+    return;
+  }
+  launch("k_tile_flags", k_tile_flags, ceil_div(ts.cap_tiles, 256), 256, s, (const int32_t*)ts.tile_lower_base,
+         (const i64*)ts.cand_scan, ts.tile_nonempty, (const int32_t*)ts.d_num_tiles);
+  scan_excl_i32(ts.tile_nonempty, ts.upper_excl, ts.cap_tiles, ts.d_num_tiles, s);
   launch("k_grid_counts", k_grid_counts, ceil_div((i64)B, 256), 256, s, (const int32_t*)ts.grid_tile_begin,
-         (const int32_t*)ts.tile_lower_base, (const int32_t*)ts.upper_excl, (const int32_t*)ts.lower_excl,
-         (const int32_t*)ts.leaf_base, (const int32_t*)ts.d_num_tiles, (const int32_t*)ts.d_num_cands, B,
-         ts.grid_info, ts.readback);
+         (const int32_t*)ts.tile_lower_base, (const int32_t*)ts.upper_excl, (const i64*)ts.cand_scan,
+         (const int32_t*)ts.d_num_tiles, (const int32_t*)ts.d_num_cands, B, ts.grid_info, ts.readback);
 }
 
 // ------------------------------------------------------------------ node writers
-// One workgroup per non-empty tile: the upper node record and its child mask
-// (candidate bits whose lower turned out empty are cleared).
-__global__ void __launch_bounds__(256) k_write_uppers(const int4* utile, const u64* tile_child,
-                                                      const uint16_t* tile_prefix, const int32_t* tile_lower_base,
-                                                      const int32_t* cand_leaf_count, const int32_t* leaf_base,
-                                                      const int32_t* upper_excl, const int32_t* lower_excl,
-                                                      const int32_t* d_num_tiles, int32_t n_upper, int4* upper_origin,
-                                                      u64* upper_key, int32_t* upper_first, u64* upper_mask) {
-  const i64 t = blockIdx.x;
-  if (t >= *d_num_tiles) return;
-  const int32_t cb = tile_lower_base[t], ce = tile_lower_base[t + 1];
-  if (leaf_base[ce] == leaf_base[cb]) return;  // empty tile, uniform per block
-  const i64 u = upper_excl[t];
-  if (u < 0 || u >= n_upper) return;  // cannot happen for consistent counts
-  if (threadIdx.x == 0) {
-    const int4 T = utile[t];
-    upper_origin[u] = make_int4(T.x * 4096, T.y * 4096, T.z * 4096, T.w);
-    upper_key[u] = ((u64)(T.x + kTileBias) << 40) | ((u64)(T.y + kTileBias) << 20) | (u64)(T.z + kTileBias);
-    upper_first[u] = lower_excl[cb];
-  }
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int w = threadIdx.x * 2 + k;
-    u64 word = tile_child[t * 512 + w];
-    u64 out = 0;
-    int32_t c = cb + tile_prefix[t * 512 + w];
-    while (word) {
-      const int b = __builtin_ctzll(word);
-      if (cand_leaf_count[c] > 0) out |= 1ull << b;
-      word &= word - 1;
-      ++c;
+// One launch, two roles. Blocks [0, tile_blocks) each own one tile and write its
+// upper node record and child mask (candidate bits whose lower turned out empty
+// are cleared). The remaining blocks own four candidate lowers each (one wave
+// per candidate) and write the lower node record plus one leaf record (origin,
+// grid, parent) per set bit of its leaf mask; leaf_cand[leaf] remembers the
+// candidate for the leaf-mask producers.
+__global__ void __launch_bounds__(256) k_write_nodes(
+    int32_t tile_blocks, const int4* utile, const u64* tile_child, const uint16_t* tile_prefix,
+    const int32_t* tile_lower_base, const int4* cand_origin, const u64* cand_child, const uint16_t* cand_prefix,
+    const i64* cand_counts, const i64* cand_scan, const int32_t* upper_excl, const int32_t* d_num_tiles,
+    const int32_t* d_num_cands, int32_t n_upper, int32_t n_lower, int32_t n_leaf, int4* upper_origin,
+    u64* upper_key, int32_t* upper_first, u64* upper_mask, int4* lower_origin, int32_t* lower_first,
+    u64* lower_mask, uint16_t* lower_prefix, int4* leaf_origin, int32_t* leaf_parent, int32_t* leaf_cand) {
+  if ((int32_t)blockIdx.x < tile_blocks) {
+    const i64 t = blockIdx.x;
+    if (t >= *d_num_tiles) return;
+    const int32_t cb = tile_lower_base[t], ce = tile_lower_base[t + 1];
+    const i64 vb = cand_scan[cb];
+    if (scan_leaf(cand_scan[ce]) == scan_leaf(vb)) return;  // empty tile, uniform per block
+    const i64 u = upper_excl[t];
+    if (u < 0 || u >= n_upper) return;  // cannot happen for consistent counts
+    if (threadIdx.x == 0) {
+      const int4 T = utile[t];
+      upper_origin[u] = make_int4(T.x * 4096, T.y * 4096, T.z * 4096, T.w);
+      upper_key[u] = ((u64)(T.x + kTileBias) << 40) | ((u64)(T.y + kTileBias) << 20) | (u64)(T.z + kTileBias);
+      upper_first[u] = scan_lower(vb);
     }
-    upper_mask[u * 512 + w] = out;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int w = threadIdx.x * 2 + k;
+      u64 word = tile_child[t * 512 + w];
+      u64 out = 0;
+      int32_t c = cb + tile_prefix[t * 512 + w];
+      while (word) {
+        const int b = __builtin_ctzll(word);
+        if ((int32_t)cand_counts[c] > 0) out |= 1ull << b;
+        word &= word - 1;
+        ++c;
+      }
+      upper_mask[u * 512 + w] = out;
+    }
+    return;
   }
-}
-
-// One wave per non-empty candidate lower: the lower node record, and one leaf
-// record (origin, grid, parent) per set bit of its leaf mask. leaf_cand[leaf]
-// remembers the candidate lower for the leaf-mask producers.
-__global__ void __launch_bounds__(256) k_write_lowers(const int4* utile, const int4* cand_origin,
-                                                      const u64* cand_child, const uint16_t* cand_prefix,
-                                                      const int32_t* cand_leaf_count, const int32_t* leaf_base,
-                                                      const int32_t* lower_excl, const int32_t* upper_excl,
-                                                      const int32_t* d_num_cands, int32_t n_lower, int32_t n_leaf,
-                                                      int4* lower_origin, int32_t* lower_first, u64* lower_mask,
-                                                      uint16_t* lower_prefix, int4* leaf_origin, int32_t* leaf_parent,
-                                                      int32_t* leaf_cand) {
-  const i64 c = (i64)blockIdx.x * 4 + threadIdx.x / kWave;
+  const i64 c = ((i64)blockIdx.x - tile_blocks) * 4 + threadIdx.x / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   if (c >= *d_num_cands) return;
-  if (cand_leaf_count[c] == 0) return;  // uniform per wave
-  const i64 lo = lower_excl[c];
-  const int32_t lb = leaf_base[c];
-  if (lo < 0 || lo >= n_lower || lb < 0 || (i64)lb + cand_leaf_count[c] > n_leaf) return;  // consistency guard
+  const int32_t cnt = (int32_t)cand_counts[c];
+  if (cnt == 0) return;  // uniform per wave
+  const i64 v = cand_scan[c];
+  const i64 lo = scan_lower(v);
+  const int32_t lb = scan_leaf(v);
+  if (lo < 0 || lo >= n_lower || lb < 0 || (i64)lb + cnt > n_leaf) return;  // consistency guard
   const int4 co = cand_origin[c];
   const int32_t g = utile[co.w].w;
   const u64 word = cand_child[c * 64 + lane];
@@ -224,17 +268,14 @@ __global__ void __launch_bounds__(256) k_write_lowers(const int4* utile, const i
 }
 
 void tree_write_nodes(TreeScratch& ts, const GridView& out, int32_t* leaf_cand, hipStream_t s) {
-  launch("k_write_uppers", k_write_uppers, ts.cap_tiles, 256, s, (const int4*)ts.utile, (const u64*)ts.tile_child,
-         (const uint16_t*)ts.tile_prefix, (const int32_t*)ts.tile_lower_base, (const int32_t*)ts.cand_leaf_count,
-         (const int32_t*)ts.leaf_base, (const int32_t*)ts.upper_excl, (const int32_t*)ts.lower_excl,
-         (const int32_t*)ts.d_num_tiles, out.n_upper, out.upper_origin, out.upper_key, out.upper_first,
-         out.upper_mask);
-  launch("k_write_lowers", k_write_lowers, ceil_div(ts.cap_cands, 4), 256, s, (const int4*)ts.utile,
-         (const int4*)ts.cand_origin, (const u64*)ts.cand_child, (const uint16_t*)ts.cand_prefix,
-         (const int32_t*)ts.cand_leaf_count, (const int32_t*)ts.leaf_base, (const int32_t*)ts.lower_excl,
-         (const int32_t*)ts.upper_excl, (const int32_t*)ts.d_num_cands, out.n_lower, out.n_leaf, out.lower_origin,
-         out.lower_first,
-         out.lower_mask, out.lower_prefix, out.leaf_origin, out.leaf_parent, leaf_cand);
+  const i64 tile_blocks = ts.cap_tiles;
+  launch("k_write_nodes", k_write_nodes, tile_blocks + ceil_div(ts.cap_cands, 4), 256, s, (int32_t)tile_blocks,
+         (const int4*)ts.utile, (const u64*)ts.tile_child, (const uint16_t*)ts.tile_prefix,
+         (const int32_t*)ts.tile_lower_base, (const int4*)ts.cand_origin, (const u64*)ts.cand_child,
+         (const uint16_t*)ts.cand_prefix, (const i64*)ts.cand_counts, (const i64*)ts.cand_scan,
+         (const int32_t*)ts.upper_excl, (const int32_t*)ts.d_num_tiles, (const int32_t*)ts.d_num_cands, out.n_upper,
+         out.n_lower, out.n_leaf, out.upper_origin, out.upper_key, out.upper_first, out.upper_mask, out.lower_origin,
+         out.lower_first, out.lower_mask, out.lower_prefix, out.leaf_origin, out.leaf_parent, leaf_cand);
 }
 
 // ------------------------------------------------------------------ leaf statistics
@@ -372,8 +413,7 @@ void tree_finalize_leaves(const GridView& out, const i64* leaf_vox, const uint32
   const i64 L = out.n_leaf;
   const int32_t B = out.B;
   const int32_t R = bbox_replicas(B);
-  fill_i32(bbox_accum, INT32_MAX, 3 * (i64)R * B, nullptr, 1, s);
-  fill_i32(bbox_accum + 3 * (i64)R * B, INT32_MIN, 3 * (i64)R * B, nullptr, 1, s);
+  fill_split_i32(bbox_accum, INT32_MAX, 3 * (i64)R * B, INT32_MIN, 3 * (i64)R * B, s);
   scan_excl_i64(leaf_vox, vox_excl, L, nullptr, s);
   launch("k_leaf_offsets_bbox", k_leaf_offsets_bbox, ceil_div(L, 256), 256, s, (const int4*)out.leaf_origin,
          leaf_box, (const i64*)vox_excl, grid_info, out.leaf_offset, bbox_accum, B, R, L);

@@ -159,8 +159,23 @@ __device__ __forceinline__ bool lower_reaches(const u64* m, int op, int j) {
 }
 
 // Upper node: 32^3 lowers in 512 words; word x*16 + (y >> 1), bit (y & 1)*32 + z.
-// Returns the set of targets j reachable from the lowers present in word w.
-__device__ __forceinline__ uint32_t upper_word_code(u64 word, int w, int op, int m) {
+// Reach set of the lowers present in word w. Box ops: a 27-bit set indexed like
+// index27 (each lower reaches the product of its per-axis offset sets, {0} plus
+// -1 / +1 on the low / high face); refine: the 8-bit set of child octants.
+__device__ __forceinline__ uint32_t axis_set(bool lo_face, bool hi_face) {
+  return 2u | (lo_face ? 1u : 0u) | (hi_face ? 4u : 0u);  // bit e + 1
+}
+__device__ __forceinline__ uint32_t product27(uint32_t ax, uint32_t ay, uint32_t az) {
+  uint32_t yz = 0, xyz = 0;
+#pragma unroll
+  for (int b = 0; b < 3; ++b)
+    if ((ay >> b) & 1u) yz |= az << (3 * b);
+#pragma unroll
+  for (int b = 0; b < 3; ++b)
+    if ((ax >> b) & 1u) xyz |= yz << (9 * b);
+  return xyz;
+}
+__device__ __forceinline__ uint32_t upper_word_reach(u64 word, int w, int op) {
   if (!word) return 0;
   const int ux = w >> 4;
   if (op == TC_OP_REFINE) {
@@ -170,28 +185,25 @@ __device__ __forceinline__ uint32_t upper_word_code(u64 word, int w, int op, int
     if (word & 0xffff0000ffff0000ull) code |= 1u << octant_index(qx, qy, 1);
     return code;
   }
+  const uint32_t ax = axis_set(ux == 0, ux == 31);
   uint32_t code = 0;
+#pragma unroll
   for (int h = 0; h < 2; ++h) {
     const uint32_t v = (uint32_t)(word >> (32 * h));
     if (!v) continue;
     const int uy = 2 * (w & 15) + h;
-    for (int j = 0; j < m; ++j) {
-      const I3 e = box_offset(j, op);
-      const bool okx = e.x == 0 || (e.x > 0 ? ux == 31 : ux == 0);
-      const bool oky = e.y == 0 || (e.y > 0 ? uy == 31 : uy == 0);
-      const bool okz = e.z == 0 || (e.z > 0 ? (v >> 31) != 0 : (v & 1u) != 0);
-      if (okx && oky && okz) code |= 1u << j;
-    }
+    code |= product27(ax, axis_set(uy == 0, uy == 31), axis_set((v & 1u) != 0, (v >> 31) != 0));
   }
   return code;
 }
 
 // ------------------------------------------------------------------ stage: tiles, fused (small batches)
-// At most 4096 tile candidates: one workgroup builds the reach code of every
-// source upper, emits the pruned candidates, sorts them in LDS (bitonic over
-// (key, value)), flags and scans the unique keys, scatters the unique tiles and
-// every candidate's tile index, writes the per-grid tile ranges and, when asked
-// (few tiles), zeroes the unique tiles' lower bitmaps; more tiles get a wide fill.
+// At most 4096 tile candidates: one workgroup builds the reach set of every
+// source upper, compacts the reachable in-range candidates, sorts them in LDS
+// (bitonic over (key, value)), flags and scans the unique keys, scatters the
+// unique tiles and every candidate's tile index, writes the per-grid tile ranges
+// and, when asked (few tiles), zeroes the unique tiles' lower bitmaps; more
+// tiles get a wide fill.
 constexpr int kTilesMax = 4096;
 constexpr int kTilesThreads = 1024;
 constexpr int kTilesItems = kTilesMax / kTilesThreads;
@@ -204,9 +216,9 @@ __global__ void __launch_bounds__(kTilesThreads) k_tiles_small(const int4* upper
   __shared__ u64 s_hi[kTilesMax];
   __shared__ u64 s_lo[kTilesMax];
   __shared__ uint32_t s_v[kTilesMax];
-  __shared__ int32_t s_g[kTilesMax];
-  __shared__ uint32_t s_code[kTilesMax];
+  __shared__ int32_t s_g[kTilesMax];  // reach set per upper first, grid per unique tile later
   __shared__ int32_t s_wave[kTilesThreads / kWave];
+  uint32_t* s_code = reinterpret_cast<uint32_t*>(s_g);
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wv = tid / kWave;
@@ -217,51 +229,82 @@ __global__ void __launch_bounds__(kTilesThreads) k_tiles_small(const int4* upper
       uint32_t code = 0;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const int w = lane * 8 + k;
-        code |= upper_word_code(upper_mask[(i64)u * 512 + w], w, op, m);
+        const int w = k * kWave + lane;
+        code |= upper_word_reach(upper_mask[(i64)u * 512 + w], w, op);
       }
 #pragma unroll
       for (int d = 32; d >= 1; d >>= 1) code |= (uint32_t)__shfl_xor((int)code, d, kWave);
-      if (lane == 0) s_code[u] = code;
+      if (lane == 0) {
+        if (op != TC_OP_REFINE && op != TC_OP_DILATE) {  // 27-bit set -> the pad's 8 offsets
+          uint32_t c8 = 0;
+          for (int j = 0; j < m; ++j) {
+            const I3 e = box_offset(j, op);
+            c8 |= ((code >> index27(e.x, e.y, e.z)) & 1u) << j;
+          }
+          code = c8;
+        }
+        s_code[u] = code;
+      }
     }
   }
   __syncthreads();
-  int P = 2;
-  while (P < n) P <<= 1;
-  for (int i = tid; i < P; i += kTilesThreads) {
-    u64 hi = ~0ull, lo = ~0ull;
-    uint32_t v = 0xffffffffu;
+  // keys of the kept candidates (blocked: thread tid owns tid*4 .. tid*4+3)
+  u64 khi[kTilesItems], klo[kTilesItems];
+  int keep[kTilesItems];
+  int nkeep = 0;
+#pragma unroll
+  for (int k = 0; k < kTilesItems; ++k) {
+    const int i = tid * kTilesItems + k;
+    keep[k] = 0;
+    khi[k] = klo[k] = 0;
     if (i < n) {
-      v = (uint32_t)i;
       const int u = i / m, j = i % m;
       const int4 o = upper_origin[u];
       const i64 tx = o.x >> 12, ty = o.y >> 12, tz = o.z >> 12;
       I3 t;
-      bool keep = true;
+      bool reach = true;
       if (op == TC_OP_REFINE) {
         const I3 q = octant(j);
         t = {2 * tx + q.x, 2 * ty + q.y, 2 * tz + q.z};
-        keep = (s_code[u] >> j) & 1u;
+        reach = (s_code[u] >> j) & 1u;
       } else if (op == TC_OP_COARSEN) {
         t = {tx >> 1, ty >> 1, tz >> 1};
       } else {
         const I3 e = box_offset(j, op);
         t = {tx + e.x, ty + e.y, tz + e.z};
-        if (e.x != 0 || e.y != 0 || e.z != 0) keep = (s_code[u] >> j) & 1u;
+        reach = (s_code[u] >> j) & 1u;
       }
-      if (keep && tile_ok(t.x) && tile_ok(t.y) && tile_ok(t.z)) {
+      if (reach && tile_ok(t.x) && tile_ok(t.y) && tile_ok(t.z)) {
         const u64 g = (uint32_t)o.w;
-        lo = ((g & 15ull) << 60) | ((u64)(t.x + kTileBias) << 40) | ((u64)(t.y + kTileBias) << 20) |
-             (u64)(t.z + kTileBias);
-        hi = g >> 4;
+        klo[k] = ((g & 15ull) << 60) | ((u64)(t.x + kTileBias) << 40) | ((u64)(t.y + kTileBias) << 20) |
+                 (u64)(t.z + kTileBias);
+        khi[k] = g >> 4;
+        keep[k] = 1;
+      } else {
+        tile_of_cand[i] = -1;
       }
     }
-    s_hi[i] = hi;
-    s_lo[i] = lo;
-    s_v[i] = v;
+    nkeep += keep[k];
+  }
+  int K;
+  int pos = block_excl_scan<int, kTilesThreads>(nkeep, s_wave, K);
+#pragma unroll
+  for (int k = 0; k < kTilesItems; ++k) {
+    if (keep[k]) {
+      s_hi[pos] = khi[k];
+      s_lo[pos] = klo[k];
+      s_v[pos] = (uint32_t)(tid * kTilesItems + k);
+      ++pos;
+    }
+  }
+  int P = 2;
+  while (P < K) P <<= 1;
+  for (int i = K + tid; i < P; i += kTilesThreads) {  // padding sorts last
+    s_hi[i] = ~0ull;
+    s_lo[i] = ~0ull;
+    s_v[i] = 0xffffffffu;
   }
   __syncthreads();
-  // bitonic sort by (key, value): padding (all-ones key, value 0xffffffff) sorts last
   for (int k = 2; k <= P; k <<= 1) {
     for (int jj = k >> 1; jj > 0; jj >>= 1) {
       for (int i = tid; i < P; i += kTilesThreads) {
@@ -284,16 +327,13 @@ __global__ void __launch_bounds__(kTilesThreads) k_tiles_small(const int4* upper
       __syncthreads();
     }
   }
-  // heads of valid keys and their exclusive scan (blocked, 4 items per thread)
+  // heads among the K sorted keys and their exclusive scan (blocked again)
   int f[kTilesItems];
   int sum = 0;
 #pragma unroll
   for (int k = 0; k < kTilesItems; ++k) {
     const int i = tid * kTilesItems + k;
-    bool h = false;
-    if (i < n && !(s_hi[i] == ~0ull && s_lo[i] == ~0ull))
-      h = i == 0 || !(s_hi[i] == s_hi[i - 1] && s_lo[i] == s_lo[i - 1]);
-    f[k] = h ? 1 : 0;
+    f[k] = i < K && (i == 0 || !(s_hi[i] == s_hi[i - 1] && s_lo[i] == s_lo[i - 1])) ? 1 : 0;
     sum += f[k];
   }
   int total;
@@ -301,25 +341,19 @@ __global__ void __launch_bounds__(kTilesThreads) k_tiles_small(const int4* upper
 #pragma unroll
   for (int k = 0; k < kTilesItems; ++k) {
     const int i = tid * kTilesItems + k;
-    if (i < n) {
+    ex += f[k];
+    if (i < K) {
       const uint32_t v = s_v[i];
-      if (v < (uint32_t)n) {
-        if (s_hi[i] == ~0ull && s_lo[i] == ~0ull) {
-          tile_of_cand[v] = -1;
-        } else {
-          const int t = ex + f[k] - 1;
-          tile_of_cand[v] = t;
-          if (f[k]) {
-            const u64 kh = s_hi[i], kl = s_lo[i];
-            const int32_t g = (int32_t)((kh << 4) | (kl >> 60));
-            utile[t] = make_int4((int32_t)((kl >> 40) & 0xfffff) - kTileBias,
-                                 (int32_t)((kl >> 20) & 0xfffff) - kTileBias, (int32_t)(kl & 0xfffff) - kTileBias, g);
-            s_g[t] = g;
-          }
-        }
+      const int t = ex - 1;
+      if (v < (uint32_t)n) tile_of_cand[v] = t;
+      if (f[k]) {
+        const u64 kh = s_hi[i], kl = s_lo[i];
+        const int32_t g = (int32_t)((kh << 4) | (kl >> 60));
+        utile[t] = make_int4((int32_t)((kl >> 40) & 0xfffff) - kTileBias, (int32_t)((kl >> 20) & 0xfffff) - kTileBias,
+                             (int32_t)(kl & 0xfffff) - kTileBias, g);
+        s_g[t] = g;
       }
     }
-    ex += f[k];
   }
   if (tid == 0) *d_num_tiles = total;
   __syncthreads();
@@ -541,6 +575,178 @@ __global__ void __launch_bounds__(256) k_leaf_mark_lower(const int4* leaf_origin
   }
 }
 
+// ------------------------------------------------------------------ stage: leaves, box ops (pull)
+// Box ops mark from the target side: workgroup b takes candidate lowers C = b,
+// b + G, ... (G workgroups; usually one candidate each). C's
+// sources are the source lowers at C + d, d in {-1,0,1}^3; from the one at
+// offset d only the leaves on the face / edge / corner that touches C can reach
+// it (offset t = -d on each axis where d is non-zero). The workgroup stages the
+// mask words that hold such leaves and a block scan of their counts in LDS;
+// every thread then takes leaves a few at a time (finding each leaf's word by
+// binary search over the scan), tests which offsets of the box spill voxels
+// into C and ORs the target bits into an LDS copy of C's 16^3 leaf mask, which
+// is stored whole at the end: no device atomics on the masks and no zero fill.
+constexpr int kPullItems = 27 * 64;                 // (source slot, mask word) pairs
+constexpr int kPullPer = (kPullItems + 255) / 256;  // per thread
+
+__device__ __forceinline__ u64 face_word_mask(int js, int w, int lo, int hi) {
+  const int dx = js / 9 - 1, dy = (js / 3) % 3 - 1, dz = js % 3 - 1;
+  if ((dx != 0 && (-dx < lo || -dx > hi)) || (dy != 0 && (-dy < lo || -dy > hi)) ||
+      (dz != 0 && (-dz < lo || -dz > hi)))
+    return 0;
+  const int x = w >> 2, yq = w & 3;
+  if ((dx < 0 && x != 15) || (dx > 0 && x != 0)) return 0;
+  u64 m = ~0ull;
+  if (dy < 0) m = yq == 3 ? 0xffff000000000000ull : 0;  // y = 15
+  else if (dy > 0) m = yq == 0 ? 0xffffull : 0;         // y = 0
+  if (dz < 0) m &= 0x8000800080008000ull;               // z = 15
+  else if (dz > 0) m &= 0x0001000100010001ull;          // z = 0
+  return m;
+}
+
+// Position in C's frame (-1 .. 16 per axis) packed as 3 x 5 bits of p + 1.
+__device__ __forceinline__ uint32_t pack_pos(int px, int py, int pz) {
+  return (uint32_t)(px + 1) | ((uint32_t)(py + 1) << 5) | ((uint32_t)(pz + 1) << 10);
+}
+
+__device__ __forceinline__ void mark_box_leaf(const u64 W[8], uint32_t pos, int lo, int hi,
+                                              unsigned long long* s_mask) {
+  const int px = (int)(pos & 31) - 1, py = (int)((pos >> 5) & 31) - 1, pz = (int)((pos >> 10) & 31) - 1;
+  const u64 all = W[0] | W[1] | W[2] | W[3] | W[4] | W[5] | W[6] | W[7];
+  for (int tx = lo; tx <= hi; ++tx) {
+    const int qx = px + tx;
+    if (qx < 0 || qx > 15) continue;
+    const u64 xs = tx > 0 ? W[7] : (tx < 0 ? W[0] : all);  // voxels that spill toward tx
+    for (int ty = lo; ty <= hi; ++ty) {
+      const int qy = py + ty;
+      if (qy < 0 || qy > 15) continue;
+      const u64 xy = xs & (ty > 0 ? 0xff00000000000000ull : (ty < 0 ? 0xffull : ~0ull));
+      if (!xy) continue;
+      u64 bits = 0;
+      for (int tz = lo; tz <= hi; ++tz) {
+        const int qz = pz + tz;
+        if (qz < 0 || qz > 15) continue;
+        if (xy & (tz > 0 ? kZ7 : (tz < 0 ? kZ0 : ~0ull))) bits |= 1ull << ((qy & 3) * 16 + qz);
+      }
+      if (bits) atomicOr(&s_mask[qx * 4 + (qy >> 2)], bits);
+    }
+  }
+}
+
+constexpr int kMarkIlp = 2;  // leaves in flight per thread
+
+__global__ void __launch_bounds__(256) k_leaf_mark_box(const int32_t* cand_src, const int32_t* d_num_cands,
+                                                       int lo, int hi, int32_t B, const tc_grid_header* src_headers,
+                                                       const u64* src_lower_mask, const uint16_t* src_lower_prefix,
+                                                       const int32_t* src_lower_first, const u64* src_leaf_mask,
+                                                       int32_t n_src_lower, int32_t n_src_leaf, u64* cand_child,
+                                                       int32_t* flags) {
+  __shared__ u64 s_word[kPullItems];          // source mask word of each item (unmasked)
+  __shared__ int32_t s_base[kPullItems];      // leaf index of the word's first leaf
+  __shared__ int32_t s_excl[kPullItems + 1];  // exclusive scan of the items' reaching leaves
+  __shared__ unsigned long long s_mask[64];
+  __shared__ int32_t s_wave[256 / kWave];
+  const int tid = threadIdx.x;
+  // An output coordinate leaves int32 exactly when a grid's bbox, widened by
+  // the box, does (its extreme voxels are present).
+  if (blockIdx.x == 0) {
+    for (int g = tid; g < B; g += 256) {
+      const tc_grid_header h = src_headers[g];
+      bool over = false;
+      for (int a = 0; a < 3; ++a)
+        over |= (i64)h.bbox_min[a] <= (i64)h.bbox_max[a] &&
+                ((i64)h.bbox_min[a] + lo < INT32_MIN || (i64)h.bbox_max[a] + hi > INT32_MAX);
+      if (over) set_flag(flags, kFlagOverflow);
+    }
+  }
+  const i64 ncand = *d_num_cands;
+  for (i64 c = blockIdx.x; c < ncand; c += gridDim.x) {
+    if (tid < 64) s_mask[tid] = 0;
+    u64 wd[kPullPer];
+    int32_t base[kPullPer];
+    int cnt[kPullPer];
+    int sum = 0;
+#pragma unroll
+    for (int k = 0; k < kPullPer; ++k) {
+      const int item = tid * kPullPer + k;
+      wd[k] = 0;
+      base[k] = 0;
+      cnt[k] = 0;
+      if (item < kPullItems) {
+        const int js = item >> 6, w = item & 63;
+        const u64 fm = face_word_mask(js, w, lo, hi);
+        if (fm) {
+          int32_t sl = cand_src[c * 27 + js];
+          if (sl >= n_src_lower) {
+            set_flag(flags, kFlagInternal);
+            sl = -1;
+          }
+          if (sl >= 0) {
+            wd[k] = src_lower_mask[(i64)sl * 64 + w];
+            base[k] = src_lower_first[sl] + src_lower_prefix[(i64)sl * 64 + w];
+            cnt[k] = popc64(wd[k] & fm);
+          }
+        }
+      }
+      sum += cnt[k];
+    }
+    int total;
+    int ex = block_excl_scan<int, 256>(sum, s_wave, total);
+#pragma unroll
+    for (int k = 0; k < kPullPer; ++k) {
+      const int item = tid * kPullPer + k;
+      if (item < kPullItems) {
+        s_word[item] = wd[k];
+        s_base[item] = base[k];
+        s_excl[item] = ex;
+      }
+      ex += cnt[k];
+    }
+    if (tid == 0) s_excl[kPullItems] = total;
+    __syncthreads();
+    for (int k0 = 0; k0 < total; k0 += kMarkIlp * 256) {
+      int32_t lf[kMarkIlp];
+      uint32_t ps[kMarkIlp];
+#pragma unroll
+      for (int u = 0; u < kMarkIlp; ++u) {
+        const int k = k0 + u * 256 + tid;
+        lf[u] = -1;
+        ps[u] = 0;
+        if (k < total) {
+          int a = 0, z = kPullItems;  // largest item with s_excl[item] <= k
+          while (z - a > 1) {
+            const int mid = (a + z) >> 1;
+            if (s_excl[mid] <= k) a = mid;
+            else z = mid;
+          }
+          const int js = a >> 6, w = a & 63;
+          const u64 word = s_word[a];
+          const int bit = select_bit(word & face_word_mask(js, w, lo, hi), k - s_excl[a]);
+          const i64 leaf = (i64)s_base[a] + popc64(word & ((1ull << bit) - 1));
+          if (leaf < 0 || leaf >= n_src_leaf) {
+            set_flag(flags, kFlagInternal);
+          } else {
+            lf[u] = (int32_t)leaf;
+            ps[u] = pack_pos((w >> 2) + 16 * (js / 9 - 1), (w & 3) * 4 + (bit >> 4) + 16 * ((js / 3) % 3 - 1),
+                             (bit & 15) + 16 * (js % 3 - 1));
+          }
+        }
+      }
+      u64 W[kMarkIlp][8];
+#pragma unroll
+      for (int u = 0; u < kMarkIlp; ++u)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) W[u][q] = lf[u] >= 0 ? src_leaf_mask[(i64)lf[u] * 8 + q] : 0;
+#pragma unroll
+      for (int u = 0; u < kMarkIlp; ++u)
+        if (lf[u] >= 0) mark_box_leaf(W[u], ps[u], lo, hi, s_mask);
+    }
+    __syncthreads();
+    if (tid < 64) cand_child[c * 64 + tid] = s_mask[tid];
+    __syncthreads();
+  }
+}
+
 // ------------------------------------------------------------------ writers: leaf masks (pass B)
 // Index of the source leaf at position p inside source lower s, or -1 when that
 // leaf is absent (or s / the result is out of range, which also flags an error).
@@ -704,18 +910,53 @@ __global__ void __launch_bounds__(256) k_leaf_gather(const int4* out_origin, con
         coarsen_place(out, W, q);
       }
     } else {
-      for (int j = sub; j < m; j += 4) {
-        const I3 t = box_offset(j, op);
-        const i64 px = lx - t.x, py = ly - t.y, pz = lz - t.z;  // source position, -1 .. 16
-        const int32_t s = cand_src[c * 27 + index27(px >> 4, py >> 4, pz >> 4)];
-        if (s < 0) continue;
-        const int32_t src = src_leaf(src_lower_mask, src_lower_prefix, src_lower_first, s, px & 15, py & 15,
-                                     pz & 15, n_src_lower, n_src_leaf, flags);
-        if (src < 0) continue;
+      // The (at most 7) sources of this lane are looked up level by level so
+      // that their dependent loads overlap instead of running one chain at a time.
+      constexpr int kPer = 7;  // ceil(27 / 4)
+      int32_t sl[kPer], bit[kPer];
+#pragma unroll
+      for (int q = 0; q < kPer; ++q) {
+        const int j = sub + 4 * q;
+        sl[q] = -1;
+        bit[q] = 0;
+        if (j < m) {
+          const I3 t = box_offset(j, op);
+          const i64 px = lx - t.x, py = ly - t.y, pz = lz - t.z;  // source position, -1 .. 16
+          sl[q] = cand_src[c * 27 + index27(px >> 4, py >> 4, pz >> 4)];
+          bit[q] = (int)((((px & 15) * 16) + (py & 15)) * 16 + (pz & 15));
+          if (sl[q] >= n_src_lower) {
+            set_flag(flags, kFlagInternal);
+            sl[q] = -1;
+          }
+        }
+      }
+      u64 word[kPer];
+#pragma unroll
+      for (int q = 0; q < kPer; ++q) word[q] = sl[q] >= 0 ? src_lower_mask[(i64)sl[q] * 64 + (bit[q] >> 6)] : 0;
+      int32_t r[kPer];
+#pragma unroll
+      for (int q = 0; q < kPer; ++q) {
+        r[q] = -1;
+        const int b = bit[q] & 63;
+        if ((word[q] >> b) & 1ull) {
+          r[q] = src_lower_first[sl[q]] + src_lower_prefix[(i64)sl[q] * 64 + (bit[q] >> 6)] +
+                 popc64(word[q] & ((1ull << b) - 1));
+          if (r[q] < 0 || r[q] >= n_src_leaf) {
+            set_flag(flags, kFlagInternal);
+            r[q] = -1;
+          }
+        }
+      }
+      // absent sources read leaf 0 (there is at least one source leaf whenever an
+      // output leaf exists) and discard it, so no load waits behind a branch
+#pragma unroll
+      for (int q = 0; q < kPer; ++q) {
+        const i64 ri = r[q] >= 0 ? r[q] : 0;
+        const u64 keep = r[q] >= 0 ? ~0ull : 0ull;
         u64 W[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) W[k] = src_leaf_mask[(i64)src * 8 + k];
-        box_contrib(out, W, t, lo, hi);
+        for (int k = 0; k < 8; ++k) W[k] = src_leaf_mask[ri * 8 + k] & keep;
+        box_contrib(out, W, box_offset(sub + 4 * q, op), lo, hi);
       }
     }
   }
@@ -738,6 +979,141 @@ __global__ void __launch_bounds__(256) k_leaf_gather(const int4* out_origin, con
   int count;
   uint32_t box;
   leaf_stats(out, prefix, count, box);
+  out_prefix[i] = prefix;
+  leaf_vox[i] = count;
+  leaf_box[i] = box;
+}
+
+// ------------------------------------------------------------------ writers: box ops, separable
+// A box [lo, hi]^3 is the Minkowski sum of three axis segments, so an output
+// leaf's mask is the source set dilated along x, then y, then z, restricted to
+// the leaf. The x pass runs on each needed source column (y, z leaf offset), the
+// y pass on each needed z offset, the z pass once; each pass shifts whole 64-bit
+// words, and a neighbour leaf only ever supplies its boundary word / row / bit.
+// Four lanes share an output leaf, lane k owning output words 2k and 2k+1: the
+// y and z passes never mix words, and the x pass needs just one more word on
+// each side (from the x-neighbour leaf at the ends). The source lookups are
+// split over the four lanes and their results exchanged with shuffles.
+__global__ void __launch_bounds__(256) k_leaf_gather_box(const int4* out_origin, const int32_t* leaf_cand, i64 n,
+                                                         int lo, int hi, const int32_t* cand_src,
+                                                         const u64* src_lower_mask, const uint16_t* src_lower_prefix,
+                                                         const int32_t* src_lower_first, const u64* src_leaf_mask,
+                                                         int32_t n_src_lower, int32_t n_src_leaf,
+                                                         const int32_t* d_num_cands, u64* out_mask, u64* out_prefix,
+                                                         i64* leaf_vox, uint32_t* leaf_box, int32_t* flags) {
+  const i64 gt = (i64)blockIdx.x * 256 + threadIdx.x;
+  const i64 i = gt >> 2;
+  const int sub = (int)(gt & 3);
+  const int grp = (int)(threadIdx.x & (kWave - 1)) & ~3;
+  bool valid = i < n;
+  i64 c = -1;
+  int4 o = make_int4(0, 0, 0, 0);
+  if (valid) {
+    o = out_origin[i];
+    c = leaf_cand[i];
+    if (c < 0 || c >= *d_num_cands) {
+      set_flag(flags, kFlagInternal);
+      valid = false;
+    }
+  }
+  const int lx = (o.x >> 3) & 15, ly = (o.y >> 3) & 15, lz = (o.z >> 3) & 15;
+  // source leaf at leaf offset s = (j/9-1, (j/3)%3-1, j%3-1), s in [-hi, -lo]^3;
+  // this lane resolves j = sub + 4q, level by level so the loads overlap
+  constexpr int kPer = 7;
+  int32_t sl[kPer], bit[kPer];
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    const int j = sub + 4 * q;
+    sl[q] = -1;
+    bit[q] = 0;
+    const int sx = j / 9 - 1, sy = (j / 3) % 3 - 1, sz = j % 3 - 1;
+    if (valid && j < 27 && sx >= -hi && sx <= -lo && sy >= -hi && sy <= -lo && sz >= -hi && sz <= -lo) {
+      const int px = lx + sx, py = ly + sy, pz = lz + sz;  // -1 .. 16
+      sl[q] = cand_src[c * 27 + index27(px >> 4, py >> 4, pz >> 4)];
+      bit[q] = ((px & 15) * 16 + (py & 15)) * 16 + (pz & 15);
+      if (sl[q] >= n_src_lower) {
+        set_flag(flags, kFlagInternal);
+        sl[q] = -1;
+      }
+    }
+  }
+  u64 word[kPer];
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) word[q] = sl[q] >= 0 ? src_lower_mask[(i64)sl[q] * 64 + (bit[q] >> 6)] : 0;
+  int32_t r[kPer];
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    r[q] = -1;
+    const int b = bit[q] & 63;
+    if ((word[q] >> b) & 1ull) {
+      r[q] = src_lower_first[sl[q]] + src_lower_prefix[(i64)sl[q] * 64 + (bit[q] >> 6)] +
+             popc64(word[q] & ((1ull << b) - 1));
+      if (r[q] < 0 || r[q] >= n_src_leaf) {
+        set_flag(flags, kFlagInternal);
+        r[q] = -1;
+      }
+    }
+  }
+  const int x0 = 2 * sub;
+  u64 ys[3][2];
+#pragma unroll
+  for (int sz = -1; sz <= 1; ++sz) {
+    u64 xs[3][2] = {{0, 0}, {0, 0}, {0, 0}};
+#pragma unroll
+    for (int sy = -1; sy <= 1; ++sy) {
+      if (sz < -hi || sz > -lo || sy < -hi || sy > -lo) continue;
+      int32_t R[3];
+#pragma unroll
+      for (int sx = -1; sx <= 1; ++sx) {
+        const int j = (sx + 1) * 9 + (sy + 1) * 3 + (sz + 1);
+        R[sx + 1] = __shfl(r[j >> 2], grp | (j & 3), kWave);
+      }
+      u64 w[4];  // words x0-1 .. x0+2 of this row of leaves
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int x = x0 - 1 + k;
+        const int32_t rr = x < 0 ? R[0] : (x > 7 ? R[2] : R[1]);
+        w[k] = rr >= 0 ? src_leaf_mask[(i64)rr * 8 + (x & 7)] : 0;
+      }
+      xs[sy + 1][0] = w[1] | (hi > 0 ? w[0] : 0) | (lo < 0 ? w[2] : 0);
+      xs[sy + 1][1] = w[2] | (hi > 0 ? w[1] : 0) | (lo < 0 ? w[3] : 0);
+    }
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      u64 v = xs[1][e];
+      if (hi > 0) v |= (xs[1][e] << 8) | (xs[0][e] >> 56);
+      if (lo < 0) v |= (xs[1][e] >> 8) | (xs[2][e] << 56);
+      ys[sz + 1][e] = v;
+    }
+  }
+  u64 outw[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    u64 v = ys[1][e];
+    if (hi > 0) v |= ((ys[1][e] & ~kZ7) << 1) | ((ys[0][e] & kZ7) >> 7);
+    if (lo < 0) v |= ((ys[1][e] & ~kZ0) >> 1) | ((ys[2][e] & kZ0) << 7);
+    outw[e] = v;
+  }
+  u64 full[8];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    full[2 * k] = __shfl(outw[0], grp | k, kWave);
+    full[2 * k + 1] = __shfl(outw[1], grp | k, kWave);
+  }
+  if (i >= n) return;
+  if (!valid) {
+    if (sub == 0) {
+      leaf_vox[i] = 0;
+      leaf_box[i] = kEmptyBox;
+    }
+    return;
+  }
+  reinterpret_cast<ulonglong2*>(out_mask)[i * 4 + sub] = make_ulonglong2(outw[0], outw[1]);
+  if (sub != 0) return;
+  u64 prefix;
+  int count;
+  uint32_t box;
+  leaf_stats(full, prefix, count, box);
   out_prefix[i] = prefix;
   leaf_vox[i] = count;
   leaf_box[i] = box;
@@ -842,19 +1218,27 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa) 
          (const u64*)sv.lower_mask, nL, op, oi.m, (const int32_t*)tile_of_cand, (const int32_t*)ts.d_num_tiles,
          ts.tile_child, ts.flags);
   tree_rank_tiles(ts, s);
-  // candidate -> source table starts empty; refine overwrites every word of its
-  // candidates' leaf masks, the other ops OR into zeros
-  fill_pair(cand_src, -1, nL * oi.m_src, oi.m_src, ts.cand_child, 0, op == TC_OP_REFINE ? 0 : nL * 64, 64,
+  // candidate -> source table starts empty; refine and the box ops store every
+  // word of their candidates' leaf masks, coarsen ORs into zeros
+  fill_pair(cand_src, -1, nL * oi.m_src, oi.m_src, ts.cand_child, 0, op == TC_OP_COARSEN ? nL * 64 : 0, 64,
             ts.d_num_cands, s);
   launch("k_lower_nbr", k_lower_nbr, ceil_div(nL, 256), 256, s, (const int4*)sv.lower_origin,
          (const u64*)sv.lower_mask, nL, op, oi.m, oi.m_src, (const int32_t*)tile_of_cand, (const u64*)ts.tile_child,
          (const uint16_t*)ts.tile_prefix, (const int32_t*)ts.tile_lower_base, (const int32_t*)ts.d_num_tiles,
          (const int32_t*)ts.d_num_cands, lower_nbr, ts.cand_origin, cand_src, ts.flags);
   // leaves (pass A)
-  launch("k_leaf_mark_lower", k_leaf_mark_lower, (i64)src->n1, 256, s, (const int4*)sv.leaf_origin,
-         (const u64*)sv.leaf_mask, (const int32_t*)sv.lower_first, (const u64*)sv.lower_mask,
-         (const uint16_t*)sv.lower_prefix, op, oi.m, (const int32_t*)lower_nbr, (const int32_t*)ts.d_num_cands,
-         ts.cand_child, ts.flags);
+  if (op == TC_OP_REFINE || op == TC_OP_COARSEN) {
+    launch("k_leaf_mark_lower", k_leaf_mark_lower, (i64)src->n1, 256, s, (const int4*)sv.leaf_origin,
+           (const u64*)sv.leaf_mask, (const int32_t*)sv.lower_first, (const u64*)sv.lower_mask,
+           (const uint16_t*)sv.lower_prefix, op, oi.m, (const int32_t*)lower_nbr, (const int32_t*)ts.d_num_cands,
+           ts.cand_child, ts.flags);
+  } else if (nL > 0) {  // no source lowers: nothing to mark and every bbox is empty
+    const i64 blocks = nL < 8192 ? nL : 8192;
+    launch("k_leaf_mark_box", k_leaf_mark_box, blocks, 256, s, (const int32_t*)cand_src,
+           (const int32_t*)ts.d_num_cands, oi.lo, oi.hi, B, (const tc_grid_header*)sv.headers,
+           (const u64*)sv.lower_mask, (const uint16_t*)sv.lower_prefix, (const int32_t*)sv.lower_first,
+           (const u64*)sv.leaf_mask, sv.n_lower, sv.n_leaf, ts.cand_child, ts.flags);
+  }
   // counts and the single readback
   tree_count_cands(ts, s);
   tree_grid_counts(ts, B, s);
@@ -878,13 +1262,22 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa) 
     post.commit();
     int32_t* leaf_cand = post.at<int32_t>(o_lc);
     tree_write_nodes(ts, ov, leaf_cand, s);
-    const i64 lanes = op == TC_OP_REFINE ? 1 : 4;
-    auto gather = op == TC_OP_REFINE ? k_leaf_gather<0> : (op == TC_OP_COARSEN ? k_leaf_gather<1> : k_leaf_gather<2>);
-    launch("k_leaf_gather", gather, ceil_div(L * lanes, 256), 256, s, (const int4*)ov.leaf_origin,
-           (const int32_t*)leaf_cand, L, op, oi.m, oi.lo, oi.hi, (const int32_t*)cand_src,
-           (const u64*)sv.lower_mask, (const uint16_t*)sv.lower_prefix, (const int32_t*)sv.lower_first,
-           (const u64*)sv.leaf_mask, sv.n_lower, sv.n_leaf, (const int32_t*)ts.d_num_cands, ov.leaf_mask,
-           ov.leaf_prefix, post.at<i64>(o_lv), post.at<uint32_t>(o_box), ts.flags);
+    if (L > 0 && sv.n_leaf == 0) throw Error(TC_ERR_INTERNAL, "pass: output leaves without source leaves");
+    if (op == TC_OP_REFINE || op == TC_OP_COARSEN) {
+      const i64 lanes = op == TC_OP_REFINE ? 1 : 4;
+      auto gather = op == TC_OP_REFINE ? k_leaf_gather<0> : k_leaf_gather<1>;
+      launch("k_leaf_gather", gather, ceil_div(L * lanes, 256), 256, s, (const int4*)ov.leaf_origin,
+             (const int32_t*)leaf_cand, L, op, oi.m, oi.lo, oi.hi, (const int32_t*)cand_src,
+             (const u64*)sv.lower_mask, (const uint16_t*)sv.lower_prefix, (const int32_t*)sv.lower_first,
+             (const u64*)sv.leaf_mask, sv.n_lower, sv.n_leaf, (const int32_t*)ts.d_num_cands, ov.leaf_mask,
+             ov.leaf_prefix, post.at<i64>(o_lv), post.at<uint32_t>(o_box), ts.flags);
+    } else {
+      launch("k_leaf_gather", k_leaf_gather_box, ceil_div(L * 4, 256), 256, s, (const int4*)ov.leaf_origin,
+             (const int32_t*)leaf_cand, L, oi.lo, oi.hi, (const int32_t*)cand_src, (const u64*)sv.lower_mask,
+             (const uint16_t*)sv.lower_prefix, (const int32_t*)sv.lower_first, (const u64*)sv.leaf_mask,
+             sv.n_lower, sv.n_leaf, (const int32_t*)ts.d_num_cands, ov.leaf_mask, ov.leaf_prefix,
+             post.at<i64>(o_lv), post.at<uint32_t>(o_box), ts.flags);
+    }
     tree_finalize_leaves(ov, post.at<i64>(o_lv), post.at<uint32_t>(o_box), post.at<i64>(o_vx),
                          post.at<int32_t>(o_bb), (const int32_t*)ts.grid_info, s);
   } catch (...) {

@@ -15,6 +15,7 @@ oracle on one step of the same workload.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -27,6 +28,7 @@ if ROOT not in sys.path:
 METRIC = "output voxels/s & ms per batched pass (k2s2 refine/coarsen, k3s1 dilate), B=16/48"
 STEP_OPS = [("coarsen", 2), ("refine", 2), ("dilate", 1), ("conv_t_k3s2", 2)]
 HBM_PEAK_GBS = 8000.0
+WORKLOAD_TAGS = {2: "shells_b16_res64", 5: "shells512_cubes"}
 
 
 def parse():
@@ -40,6 +42,9 @@ def parse():
     ap.add_argument("--no-large", action="store_true", help="skip the 64-shell res-512 + cube batch")
     ap.add_argument("--large-only", action="store_true",
                     help="only the 64-shell res-512 + cube batch (prints its record), for profiling")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="after the run, copy a buffer of this many MiB device-to-device three times: "
+                         "a kernel of known traffic that scales the HBM byte counters of a profiling run")
     return ap.parse_args()
 
 
@@ -57,7 +62,8 @@ def run_step(binding, src, outs=None):
 
 # Algorithmic bytes of one launch of each measured kernel: what the step itself
 # must move, not what the kernel happens to move.
-#   k_leaf_mark_lower    reads every source leaf once: origin 16 B + mask 64 B
+#   k_leaf_mark_*        reads every source leaf once: origin 16 B + mask 64 B
+#                        (k_leaf_mark_lower: refine / coarsen; k_leaf_mark_box: box ops)
 #   k_leaf_gather        reads every output leaf's origin 16 B + candidate id 4 B, every
 #                        source mask once (64 B), writes every output mask (64 B)
 #   k_leaf_offsets_bbox  reads origin 16 B + packed bbox 4 B + voxel scan 8 B,
@@ -65,7 +71,7 @@ def run_step(binding, src, outs=None):
 #   k_enumerate          reads origin, mask, offset and grid base (96 B per leaf),
 #                        writes 12 B per voxel
 def kernel_bytes(name, src_leaves, leaves, voxels):
-    if name == "k_leaf_mark_lower":
+    if name in ("k_leaf_mark_lower", "k_leaf_mark_box"):
         return 80 * src_leaves
     if name == "k_leaf_gather":
         return 84 * leaves + 64 * src_leaves
@@ -76,7 +82,49 @@ def kernel_bytes(name, src_leaves, leaves, voxels):
     raise ValueError(name)
 
 
-LARGE_KERNELS = ["k_leaf_mark_lower", "k_leaf_gather", "k_leaf_offsets_bbox", "k_enumerate"]
+LARGE_KERNELS = ["k_leaf_mark_lower", "k_leaf_mark_box", "k_leaf_gather", "k_leaf_offsets_bbox", "k_enumerate"]
+
+
+def source_digest():
+    """sha256 over the library's kernel sources: counter readings taken from an
+    older build no longer describe the kernels and are then not reported."""
+    csrc = os.path.join(ROOT, "topology_construction_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp")):
+            with open(os.path.join(csrc, name), "rb") as fh:
+                h.update(name.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    profiles/traffic_<kernel>_<workload>.txt (lines `key value`), or None when
+    there is none or it was taken from other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            parts = line.split()
+            if len(parts) == 2:
+                kv[parts[0]] = parts[1]
+    if kv.get("source_sha256") != source_digest() or "hbm_bytes_per_launch" not in kv:
+        return None
+    return float(kv["hbm_bytes_per_launch"])
+
+
+def copy_calibration(torch, mib):
+    """Three device-to-device copies of `mib` MiB (reads and writes mib MiB each)."""
+    if mib <= 0:
+        return
+    a = torch.empty(mib << 20, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
 
 
 def measure_large(binding, torch, np, synth):
@@ -139,6 +187,7 @@ def main():
     torch.cuda.set_device(0)
     if args.large_only:
         print(json.dumps({"large": measure_large(binding, torch, np, synth)}), flush=True)
+        copy_calibration(torch, args.copy_mib)
         return
     ijk, off = synth.make_config(args.config)
     src = binding.tc_batch_from_ijk(torch.from_numpy(ijk).cuda(), off)
@@ -188,7 +237,8 @@ def main():
     avg_bytes = bytes_per_step / launches_per_step
     achieved = avg_bytes / (avg_ms * 1e-3) / 1e9 if k_n else None
     roofline = {"bound": "hbm", "kernel": args.roofline_kernel, "achieved": achieved, "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": (achieved / HBM_PEAK_GBS) if achieved else None, "traffic": None,
+                "unit": "GB/s", "frac": (achieved / HBM_PEAK_GBS) if achieved else None,
+                "traffic": recorded_traffic(args.roofline_kernel, WORKLOAD_TAGS.get(args.config, f"config{args.config}")),
                 "avg_launch_ms": avg_ms, "launches": k_n, "algorithmic_bytes_per_launch": avg_bytes}
 
     cpu = None
@@ -219,6 +269,7 @@ def main():
         "roofline": roofline, "cpu_baseline": cpu, "ops": ops, "large": large,
     }
     print(json.dumps(rec), flush=True)
+    copy_calibration(torch, args.copy_mib)
 
 
 if __name__ == "__main__":

@@ -274,6 +274,7 @@ tc_grid_batch* build_from_ijk(const int32_t* d_ijk, const int64_t* h_off, int32_
   const size_t o_lb = a3.reserve(8 * ((i64)nc + 1));
   const size_t o_ginfo = a3.reserve(4 * 6 * (i64)B);
   const size_t o_rb3 = a3.reserve(4 * (4 + 3 * (i64)B));
+  const size_t o_stmp3 = a3.reserve(std::max(scan_tmp_bytes(nt, 4), scan_tmp_bytes(nc, 8)));
   a3.commit();
   ts.cap_cands = nc;
   ts.cand_origin = a3.at<int4>(o_corig);
@@ -283,6 +284,7 @@ tc_grid_batch* build_from_ijk(const int32_t* d_ijk, const int64_t* h_off, int32_
   ts.cand_scan = a3.at<i64>(o_lb);
   ts.grid_info = a3.at<int32_t>(o_ginfo);
   ts.readback = a3.at<int32_t>(o_rb3);
+  ts.scan_tmp = a3.at<char>(o_stmp3);
   ts.flags = ts.readback;
   fill_i32(ts.readback, 0, 1, nullptr, 1, s);
   fill_u64(ts.cand_child, 0, 64 * (i64)nc, nullptr, 1, s);
@@ -307,6 +309,7 @@ tc_grid_batch* build_from_ijk(const int32_t* d_ijk, const int64_t* h_off, int32_
     const size_t o_box = post.reserve(4 * L);
     const size_t o_vx = post.reserve(8 * (L + 1));
     const size_t o_bb = post.reserve(4 * 6 * (i64)B * bbox_replicas(B));
+    const size_t o_stmp2 = post.reserve(scan_tmp_bytes(L, 8));
     post.commit();
     tree_write_nodes(ts, ov, post.at<int32_t>(o_lc), s);
     fill_u64(ov.leaf_mask, 0, 8 * L, nullptr, 1, s);
@@ -314,7 +317,7 @@ tc_grid_batch* build_from_ijk(const int32_t* d_ijk, const int64_t* h_off, int32_
            (const u64*)ts.cand_child, (const uint16_t*)ts.cand_prefix, (const i64*)ts.cand_scan, L,
            ov.leaf_mask);
     tree_leaf_stats(ov, post.at<i64>(o_lv), post.at<uint32_t>(o_box), s);
-    tree_finalize_leaves(ov, post.at<i64>(o_lv), post.at<uint32_t>(o_box), post.at<i64>(o_vx),
+    tree_finalize_leaves(ov, post.at<i64>(o_lv), post.at<uint32_t>(o_box), post.at<i64>(o_vx), post.at<char>(o_stmp2),
                          post.at<int32_t>(o_bb), (const int32_t*)ts.grid_info, s);
   } catch (...) {
     free_batch(out);

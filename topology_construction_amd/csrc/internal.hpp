@@ -163,6 +163,9 @@ void* device_alloc_async(size_t bytes, hipStream_t s);
 void device_free_async(void* p, hipStream_t s);
 
 // ------------------------------------------------------------------ profiling
+// When `name` is being timed, prof_before records a start event on the stream
+// and prof_after a stop event; the pair is read later (prof_read). The interval
+// includes the dispatch latency between the start marker and the kernel.
 void prof_before(const char* name, hipStream_t s);
 void prof_after(const char* name, hipStream_t s);
 
@@ -181,11 +184,14 @@ inline i64 ceil_div(i64 a, i64 b) { return (a + b - 1) / b; }
 // ------------------------------------------------------------------ primitives (primitives.hip)
 // Exclusive scan of n items (n read from d_n when non-null, else n_host; n_host
 // is the launch bound). out has n+1 entries; out[n] = total.
-// total_out, when given, also receives the total (device memory).
+// total_out, when given, also receives the total (device memory). Scans longer
+// than one tile need scan_tmp_bytes(n_host, sizeof(T)) of scratch: from `tmp`
+// when given, else allocated (and freed) on the stream.
+size_t scan_tmp_bytes(i64 n_host, size_t elem);
 void scan_excl_i32(const int32_t* in, int32_t* out, i64 n_host, const int32_t* d_n, hipStream_t s,
-                   int32_t* total_out = nullptr);
+                   int32_t* total_out = nullptr, void* tmp = nullptr);
 void scan_excl_i64(const i64* in, i64* out, i64 n_host, const int32_t* d_n, hipStream_t s,
-                   i64* total_out = nullptr);
+                   i64* total_out = nullptr, void* tmp = nullptr);
 void scan_excl_u32(const uint32_t* in, uint32_t* out, i64 n_host, const int32_t* d_n, hipStream_t s);
 
 void fill_i32(int32_t* p, int32_t v, i64 n_host, const int32_t* d_n, int32_t mult, hipStream_t s);
@@ -236,6 +242,7 @@ struct TreeScratch {
   int32_t* grid_info;        // [B][6]: nU, nL1, nL, uBegin, lBegin, leafBegin
   int32_t* readback;         // [4 + 3B]: flags, N2, N1, L, then per-grid counts
   int32_t* flags;            // [1] bit 0 overflow, bit 1 internal error (inside readback)
+  void* scan_tmp;            // scan scratch: scan_tmp_bytes over cap_tiles (i32) and cap_cands (i64)
   i64 cap_tiles, cap_cands;
 };
 
@@ -247,7 +254,7 @@ void tree_count_cands(TreeScratch& t, hipStream_t s);           // leaf counts p
 void tree_write_nodes(TreeScratch& t, const GridView& out, int32_t* leaf_cand, hipStream_t s);
 void tree_leaf_stats(const GridView& out, i64* leaf_vox, uint32_t* leaf_box, hipStream_t s);
 int32_t bbox_replicas(int32_t B);  // replicas of the per-grid bbox accumulators
-void tree_finalize_leaves(const GridView& out, const i64* leaf_vox, const uint32_t* leaf_box, i64* vox_excl,
+void tree_finalize_leaves(const GridView& out, const i64* leaf_vox, const uint32_t* leaf_box, i64* vox_excl, void* scan_tmp,
                           int32_t* bbox_accum, const int32_t* grid_info, hipStream_t s);
 void tree_enumerate(const GridView& v, int32_t* ijk, hipStream_t s);
 

@@ -225,25 +225,35 @@ __global__ void __launch_bounds__(kTilesThreads) k_tiles_small(const int4* upper
   const int n = n_upper * m;
   if (tid == 0) readback[0] = 0;
   if (op != TC_OP_COARSEN) {
-    for (int u = wv; u < n_upper; u += kTilesThreads / kWave) {
-      uint32_t code = 0;
+    // each wave reduces kUppersPerWave uppers at a time, so that many mask loads
+    // are in flight at once
+    constexpr int kUppersPerWave = 4;
+    constexpr int kWaves = kTilesThreads / kWave;
+    for (int u0 = wv * kUppersPerWave; u0 < n_upper; u0 += kWaves * kUppersPerWave) {
+      u64 words[kUppersPerWave][8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int w = k * kWave + lane;
-        code |= upper_word_reach(upper_mask[(i64)u * 512 + w], w, op);
-      }
+      for (int v = 0; v < kUppersPerWave; ++v)
 #pragma unroll
-      for (int d = 32; d >= 1; d >>= 1) code |= (uint32_t)__shfl_xor((int)code, d, kWave);
-      if (lane == 0) {
-        if (op != TC_OP_REFINE && op != TC_OP_DILATE) {  // 27-bit set -> the pad's 8 offsets
-          uint32_t c8 = 0;
-          for (int j = 0; j < m; ++j) {
-            const I3 e = box_offset(j, op);
-            c8 |= ((code >> index27(e.x, e.y, e.z)) & 1u) << j;
+        for (int k = 0; k < 8; ++k)
+          words[v][k] = u0 + v < n_upper ? upper_mask[(i64)(u0 + v) * 512 + k * kWave + lane] : 0;
+#pragma unroll
+      for (int v = 0; v < kUppersPerWave; ++v) {
+        uint32_t code = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) code |= upper_word_reach(words[v][k], k * kWave + lane, op);
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) code |= (uint32_t)__shfl_xor((int)code, d, kWave);
+        if (lane == 0 && u0 + v < n_upper) {
+          if (op != TC_OP_REFINE && op != TC_OP_DILATE) {  // 27-bit set -> the pad's 8 offsets
+            uint32_t c8 = 0;
+            for (int j = 0; j < m; ++j) {
+              const I3 e = box_offset(j, op);
+              c8 |= ((code >> index27(e.x, e.y, e.z)) & 1u) << j;
+            }
+            code = c8;
           }
-          code = c8;
+          s_code[u0 + v] = code;
         }
-        s_code[u] = code;
       }
     }
   }
@@ -1158,6 +1168,7 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa) 
   const size_t o_csrc = a.reserve(4 * nL * oi.m_src);
   const size_t o_ginfo = a.reserve(4 * 6 * (i64)B);
   const size_t o_rb = a.reserve(4 * (4 + 3 * (i64)B));
+  const size_t o_stmp = a.reserve(std::max(scan_tmp_bytes(nT, 4), scan_tmp_bytes(nL, 8)));
   a.commit();
 
   TreeScratch ts{};
@@ -1180,6 +1191,7 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa) 
   ts.cand_scan = a.at<i64>(o_cscan);
   ts.grid_info = a.at<int32_t>(o_ginfo);
   ts.readback = a.at<int32_t>(o_rb);
+  ts.scan_tmp = a.at<char>(o_stmp);
   ts.flags = ts.readback;
   int32_t* tile_of_cand = a.at<int32_t>(o_toc);
   int32_t* lower_nbr = a.at<int32_t>(o_nbr);
@@ -1203,7 +1215,7 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa) 
              op, oi.m, keys, vals);
       sort_pairs_128(keys, vals, nT, tile_key_bits(B), s);
       launch("k_tile_heads", k_tile_heads, ceil_div(nT, 256), 256, s, (const Key128*)keys, nT, head);
-      scan_excl_i32(head, texcl, nT, nullptr, s, ts.d_num_tiles);
+      scan_excl_i32(head, texcl, nT, nullptr, s, ts.d_num_tiles, ts.scan_tmp);
       launch("k_tile_scatter", k_tile_scatter, ceil_div(nT, 256), 256, s, (const Key128*)keys,
              (const uint32_t*)vals, (const int32_t*)head, (const int32_t*)texcl, nT, ts.utile, tile_of_cand,
              ts.flags);
@@ -1259,6 +1271,7 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa) 
     const size_t o_box = post.reserve(4 * L);
     const size_t o_vx = post.reserve(8 * (L + 1));
     const size_t o_bb = post.reserve(4 * 6 * (i64)B * bbox_replicas(B));
+    const size_t o_stmp2 = post.reserve(scan_tmp_bytes(L, 8));
     post.commit();
     int32_t* leaf_cand = post.at<int32_t>(o_lc);
     tree_write_nodes(ts, ov, leaf_cand, s);
@@ -1278,7 +1291,7 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa) 
              sv.n_lower, sv.n_leaf, (const int32_t*)ts.d_num_cands, ov.leaf_mask, ov.leaf_prefix,
              post.at<i64>(o_lv), post.at<uint32_t>(o_box), ts.flags);
     }
-    tree_finalize_leaves(ov, post.at<i64>(o_lv), post.at<uint32_t>(o_box), post.at<i64>(o_vx),
+    tree_finalize_leaves(ov, post.at<i64>(o_lv), post.at<uint32_t>(o_box), post.at<i64>(o_vx), post.at<char>(o_stmp2),
                          post.at<int32_t>(o_bb), (const int32_t*)ts.grid_info, s);
   } catch (...) {
     free_batch(out);

@@ -120,9 +120,13 @@ __global__ void __launch_bounds__(kScanThreads) k_scan_down(const T* in, T* out,
   }
 }
 
+size_t scan_tmp_bytes(i64 n_host, size_t elem) {
+  return n_host <= kScanTile ? 0 : elem * (size_t)ceil_div(n_host, kScanTile);
+}
+
 template <typename T>
 static void scan_excl(const char* tag, const T* in, T* out, i64 n_host, const int32_t* d_n, hipStream_t s,
-                      T* total_out) {
+                      T* total_out, void* tmp) {
   (void)tag;
   if (n_host <= 0) {
     // n is zero: out[0] = 0
@@ -135,27 +139,29 @@ static void scan_excl(const char* tag, const T* in, T* out, i64 n_host, const in
     return;
   }
   const i64 nblk = ceil_div(n_host, kScanTile);
-  T* partial = static_cast<T*>(device_alloc_async(sizeof(T) * (size_t)nblk, s));
+  const bool own = tmp == nullptr;
+  T* partial = static_cast<T*>(own ? device_alloc_async(sizeof(T) * (size_t)nblk, s) : tmp);
   try {
     launch("k_scan_reduce", k_scan_reduce<T>, nblk, kScanThreads, s, in, partial, n_host, d_n);
     launch("k_scan_partials", k_scan_partials<T>, 1, kScanThreads, s, partial, nblk, out, n_host, d_n, total_out);
     launch("k_scan_down", k_scan_down<T>, nblk, kScanThreads, s, in, out, (const T*)partial, n_host, d_n);
   } catch (...) {
-    device_free_async(partial, s);
+    if (own) device_free_async(partial, s);
     throw;
   }
-  device_free_async(partial, s);
+  if (own) device_free_async(partial, s);
 }
 
 void scan_excl_i32(const int32_t* in, int32_t* out, i64 n_host, const int32_t* d_n, hipStream_t s,
-                   int32_t* total_out) {
-  scan_excl("i32", in, out, n_host, d_n, s, total_out);
+                   int32_t* total_out, void* tmp) {
+  scan_excl("i32", in, out, n_host, d_n, s, total_out, tmp);
 }
-void scan_excl_i64(const i64* in, i64* out, i64 n_host, const int32_t* d_n, hipStream_t s, i64* total_out) {
-  scan_excl("i64", in, out, n_host, d_n, s, total_out);
+void scan_excl_i64(const i64* in, i64* out, i64 n_host, const int32_t* d_n, hipStream_t s, i64* total_out,
+                   void* tmp) {
+  scan_excl("i64", in, out, n_host, d_n, s, total_out, tmp);
 }
 void scan_excl_u32(const uint32_t* in, uint32_t* out, i64 n_host, const int32_t* d_n, hipStream_t s) {
-  scan_excl("u32", in, out, n_host, d_n, s, (uint32_t*)nullptr);
+  scan_excl("u32", in, out, n_host, d_n, s, (uint32_t*)nullptr, nullptr);
 }
 
 // ------------------------------------------------------------------ fills

@@ -88,6 +88,7 @@ struct Prof {
   bool all = false;
   std::vector<std::string> names;
   std::vector<Timed> pending;
+  std::vector<hipEvent_t> spare;  // events kept for reuse: creating one per launch costs host time
   hipEvent_t open_start = nullptr;
   std::vector<std::pair<std::string, std::pair<double, int64_t>>> totals;
   bool wants(const char* n) const {
@@ -115,10 +116,21 @@ void prof_drain(Prof& p) {
         found = true;
       }
     if (!found) p.totals.push_back({t.name, {(double)ms, 1}});
-    (void)hipEventDestroy(t.start);
-    (void)hipEventDestroy(t.stop);
+    p.spare.push_back(t.start);
+    p.spare.push_back(t.stop);
   }
   p.pending.clear();
+}
+
+hipEvent_t take_event(Prof& p) {
+  if (!p.spare.empty()) {
+    hipEvent_t e = p.spare.back();
+    p.spare.pop_back();
+    return e;
+  }
+  hipEvent_t e;
+  hip_check(hipEventCreate(&e), "hipEventCreate");
+  return e;
 }
 }  // namespace
 
@@ -127,8 +139,7 @@ void prof_before(const char* name, hipStream_t s) {
   if (!p.on) return;
   std::lock_guard<std::mutex> lk(p.mu);
   if (!p.on || !p.wants(name)) return;
-  hipEvent_t e;
-  hip_check(hipEventCreate(&e), "hipEventCreate");
+  hipEvent_t e = take_event(p);
   hip_check(hipEventRecord(e, s), "hipEventRecord");
   p.open_start = e;
 }
@@ -138,8 +149,7 @@ void prof_after(const char* name, hipStream_t s) {
   if (!p.on) return;
   std::lock_guard<std::mutex> lk(p.mu);
   if (!p.on || !p.open_start || !p.wants(name)) return;
-  hipEvent_t e;
-  hip_check(hipEventCreate(&e), "hipEventCreate");
+  hipEvent_t e = take_event(p);
   hip_check(hipEventRecord(e, s), "hipEventRecord");
   p.pending.push_back({name, p.open_start, e});
   p.open_start = nullptr;
@@ -149,8 +159,8 @@ void prof_enable(const char* names) {
   Prof& p = prof();
   std::lock_guard<std::mutex> lk(p.mu);
   for (auto& t : p.pending) {
-    (void)hipEventDestroy(t.start);
-    (void)hipEventDestroy(t.stop);
+    p.spare.push_back(t.start);
+    p.spare.push_back(t.stop);
   }
   p.pending.clear();
   p.totals.clear();
@@ -165,6 +175,14 @@ void prof_enable(const char* names) {
     } else if (*c != ' ') {
       cur.push_back(*c);
     }
+  }
+  while (p.spare.size() < 1024) {  // enough for a timed loop without creating events in it
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) {  // no device here: events are created when needed
+      (void)hipGetLastError();
+      break;
+    }
+    p.spare.push_back(e);
   }
   p.on = true;
 }

@@ -63,7 +63,8 @@ void tree_rank_tiles(TreeScratch& ts, hipStream_t s) {
   launch("k_tile_rank", k_tile_rank, ts.cap_tiles, 256, s, (const u64*)ts.tile_child, ts.tile_prefix,
          ts.tile_lower_count, (const int32_t*)ts.d_num_tiles);
   // the total of the scan is the number of candidate lowers
-  scan_excl_i32(ts.tile_lower_count, ts.tile_lower_base, ts.cap_tiles, ts.d_num_tiles, s, ts.d_num_cands);
+  scan_excl_i32(ts.tile_lower_count, ts.tile_lower_base, ts.cap_tiles, ts.d_num_tiles, s, ts.d_num_cands,
+                ts.scan_tmp);
 }
 
 // ------------------------------------------------------------------ candidate lowers
@@ -172,7 +173,7 @@ __global__ void __launch_bounds__(kTailThreads) k_counts_tail(const int32_t* gri
 void tree_count_cands(TreeScratch& ts, hipStream_t s) {
   launch("k_lower_count", k_lower_count, ceil_div(ts.cap_cands, 4), 256, s, (const u64*)ts.cand_child,
          ts.cand_prefix, ts.cand_counts, (const int32_t*)ts.d_num_cands);
-  scan_excl_i64(ts.cand_counts, ts.cand_scan, ts.cap_cands, ts.d_num_cands, s);
+  scan_excl_i64(ts.cand_counts, ts.cand_scan, ts.cap_cands, ts.d_num_cands, s, nullptr, ts.scan_tmp);
 }
 
 void tree_grid_counts(TreeScratch& ts, int32_t B, hipStream_t s) {
@@ -184,7 +185,7 @@ void tree_grid_counts(TreeScratch& ts, int32_t B, hipStream_t s) {
   }
   launch("k_tile_flags", k_tile_flags, ceil_div(ts.cap_tiles, 256), 256, s, (const int32_t*)ts.tile_lower_base,
          (const i64*)ts.cand_scan, ts.tile_nonempty, (const int32_t*)ts.d_num_tiles);
-  scan_excl_i32(ts.tile_nonempty, ts.upper_excl, ts.cap_tiles, ts.d_num_tiles, s);
+  scan_excl_i32(ts.tile_nonempty, ts.upper_excl, ts.cap_tiles, ts.d_num_tiles, s, nullptr, ts.scan_tmp);
   launch("k_grid_counts", k_grid_counts, ceil_div((i64)B, 256), 256, s, (const int32_t*)ts.grid_tile_begin,
          (const int32_t*)ts.tile_lower_base, (const int32_t*)ts.upper_excl, (const i64*)ts.cand_scan,
          (const int32_t*)ts.d_num_tiles, (const int32_t*)ts.d_num_cands, B, ts.grid_info, ts.readback);
@@ -408,13 +409,13 @@ int32_t bbox_replicas(int32_t B) {
   return r < 1 ? 1 : (r > 64 ? 64 : r);
 }
 
-void tree_finalize_leaves(const GridView& out, const i64* leaf_vox, const uint32_t* leaf_box, i64* vox_excl,
+void tree_finalize_leaves(const GridView& out, const i64* leaf_vox, const uint32_t* leaf_box, i64* vox_excl, void* scan_tmp,
                           int32_t* bbox_accum, const int32_t* grid_info, hipStream_t s) {
   const i64 L = out.n_leaf;
   const int32_t B = out.B;
   const int32_t R = bbox_replicas(B);
   fill_split_i32(bbox_accum, INT32_MAX, 3 * (i64)R * B, INT32_MIN, 3 * (i64)R * B, s);
-  scan_excl_i64(leaf_vox, vox_excl, L, nullptr, s);
+  scan_excl_i64(leaf_vox, vox_excl, L, nullptr, s, nullptr, scan_tmp);
   launch("k_leaf_offsets_bbox", k_leaf_offsets_bbox, ceil_div(L, 256), 256, s, (const int4*)out.leaf_origin,
          leaf_box, (const i64*)vox_excl, grid_info, out.leaf_offset, bbox_accum, B, R, L);
   launch("k_write_headers", k_write_headers, ceil_div((i64)B, 4), 256, s, grid_info, (const i64*)vox_excl,

@@ -291,8 +291,7 @@ tc_grid_batch* build_from_ijk(const int32_t* d_ijk, const int64_t* h_off, int32_
   launch("k_voxel_cand", k_voxel_cand, ceil_div(N, 256), 256, s, d_ijk, (const int32_t*)vtile, N,
          (const u64*)ts.tile_child, (const uint16_t*)ts.tile_prefix, (const int32_t*)ts.tile_lower_base, nc, vcand,
          ts.cand_origin, ts.cand_child, ts.flags);
-  tree_count_cands(ts, s);
-  tree_grid_counts(ts, B, s);
+  tree_counts(ts, B, s);
   const size_t rb_bytes = 4 * (4 + 3 * (size_t)B);
   int32_t* h_rb = static_cast<int32_t*>(pinned_staging(rb_bytes));
   hip_check(hipMemcpyAsync(h_rb, ts.readback, rb_bytes, hipMemcpyDeviceToHost, s), "readback");

@@ -250,7 +250,8 @@ struct TreeScratch {
 void tree_tile_ranges(TreeScratch& t, int32_t B, hipStream_t s);
 void tree_grid_counts(TreeScratch& t, int32_t B, hipStream_t s);
 void tree_rank_tiles(TreeScratch& t, hipStream_t s);            // prefix per tile + scan -> cand numbering
-void tree_count_cands(TreeScratch& t, hipStream_t s);           // leaf counts per cand + scans + tile flags + grid counts
+void tree_count_cands(TreeScratch& t, hipStream_t s);           // leaf counts per cand + their scan
+void tree_counts(TreeScratch& t, int32_t B, hipStream_t s);     // tree_count_cands + tree_grid_counts (fused when small)
 void tree_write_nodes(TreeScratch& t, const GridView& out, int32_t* leaf_cand, hipStream_t s);
 void tree_leaf_stats(const GridView& out, i64* leaf_vox, uint32_t* leaf_box, hipStream_t s);
 int32_t bbox_replicas(int32_t B);  // replicas of the per-grid bbox accumulators

@@ -158,6 +158,44 @@ __device__ __forceinline__ bool lower_reaches(const u64* m, int op, int j) {
   return (acc & zm) != 0;
 }
 
+// Reach set contributed by word w of a lower's 16^3 leaf mask, in the same
+// encoding as upper_word_reach (27-bit box offsets, or 8-bit child octants for
+// refine); the union over the 64 words equals lower_reaches for every target.
+__device__ __forceinline__ uint32_t product27(uint32_t ax, uint32_t ay, uint32_t az);
+__device__ __forceinline__ uint32_t axis_set(bool lo_face, bool hi_face);
+__device__ __forceinline__ uint32_t lower_word_reach(u64 word, int w, int op) {
+  if (!word) return 0;
+  const int x = w >> 2, yq = w & 3;
+  if (op == TC_OP_REFINE) {
+    const int qx = x >> 3, qy = yq >> 1;
+    uint32_t code = 0;
+    if (word & 0x00ff00ff00ff00ffull) code |= 1u << octant_index(qx, qy, 0);
+    if (word & 0xff00ff00ff00ff00ull) code |= 1u << octant_index(qx, qy, 1);
+    return code;
+  }
+  const uint32_t ax = axis_set(x == 0, x == 15);
+  uint32_t code = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t v = (uint32_t)(word >> (16 * r)) & 0xffffu;
+    if (!v) continue;
+    const int y = yq * 4 + r;
+    code |= product27(ax, axis_set(y == 0, y == 15), axis_set((v & 1u) != 0, (v >> 15) != 0));
+  }
+  return code;
+}
+
+// 27-bit box-offset set -> the op's candidate numbering (identity for dilate).
+__device__ __forceinline__ uint32_t box_code_for_op(uint32_t code27, int op, int m) {
+  if (op == TC_OP_DILATE) return code27;
+  uint32_t c = 0;
+  for (int j = 0; j < m; ++j) {
+    const I3 e = box_offset(j, op);
+    c |= ((code27 >> index27(e.x, e.y, e.z)) & 1u) << j;
+  }
+  return c;
+}
+
 // Upper node: 32^3 lowers in 512 words; word x*16 + (y >> 1), bit (y & 1)*32 + z.
 // Reach set of the lowers present in word w. Box ops: a 27-bit set indexed like
 // index27 (each lower reaches the product of its per-axis offset sets, {0} plus
@@ -243,17 +281,7 @@ __global__ void __launch_bounds__(kTilesThreads) k_tiles_small(const int4* upper
         for (int k = 0; k < 8; ++k) code |= upper_word_reach(words[v][k], k * kWave + lane, op);
 #pragma unroll
         for (int d = 32; d >= 1; d >>= 1) code |= (uint32_t)__shfl_xor((int)code, d, kWave);
-        if (lane == 0 && u0 + v < n_upper) {
-          if (op != TC_OP_REFINE && op != TC_OP_DILATE) {  // 27-bit set -> the pad's 8 offsets
-            uint32_t c8 = 0;
-            for (int j = 0; j < m; ++j) {
-              const I3 e = box_offset(j, op);
-              c8 |= ((code >> index27(e.x, e.y, e.z)) & 1u) << j;
-            }
-            code = c8;
-          }
-          s_code[u0 + v] = code;
-        }
+        if (lane == 0 && u0 + v < n_upper) s_code[u0 + v] = op == TC_OP_REFINE ? code : box_code_for_op(code, op, m);
       }
     }
   }
@@ -417,18 +445,25 @@ __device__ __forceinline__ int upper_child_bit(const I3& k) {
   return (int)((((k.x & 31) * 32) + (k.y & 31)) * 32 + (k.z & 31));
 }
 
-__global__ void __launch_bounds__(256) k_lower_mark(const int4* lower_origin, const u64* lower_mask, i64 n, int op,
-                                                    int m, const int32_t* tile_of_cand, const int32_t* d_num_tiles,
-                                                    u64* tile_child, int32_t* flags) {
-  const i64 i = (i64)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
+// Pair i = (source lower l, candidate j) sets its target lower's bit in the
+// target tile's 32^3 candidate mask.
+// `reach` (when non-null) holds every source lower's reach set, replacing the
+// per-pair mask scan of lower_reaches.
+__device__ __forceinline__ bool pair_reaches(const u64* lower_mask, const uint32_t* reach, i64 l, int op, int j) {
+  if (op == TC_OP_COARSEN) return true;
+  return reach ? ((reach[l] >> j) & 1u) != 0 : lower_reaches(lower_mask + l * 64, op, j);
+}
+
+__device__ __forceinline__ void lower_mark_one(i64 i, const int4* lower_origin, const u64* lower_mask,
+                                               const uint32_t* reach, int op, int m, const int32_t* tile_of_cand,
+                                               int32_t num_tiles, u64* tile_child, int32_t* flags) {
   const i64 l = i / m;
   const int j = (int)(i % m);
   const int4 o = lower_origin[l];
   const LowerTarget tg = lower_target(o, j, op);
-  if (!tg.ok || !lower_reaches(lower_mask + l * 64, op, j)) return;
+  if (!tg.ok || !pair_reaches(lower_mask, reach, l, op, j)) return;
   const int32_t t = tile_of_cand[(i64)o.w * m + tg.jt];
-  if (t < 0 || t >= *d_num_tiles) {
+  if (t < 0 || t >= num_tiles) {
     set_flag(flags, kFlagInternal);
     return;
   }
@@ -436,25 +471,25 @@ __global__ void __launch_bounds__(256) k_lower_mark(const int4* lower_origin, co
   atomicOr((unsigned long long*)&tile_child[(i64)t * 512 + (bit >> 6)], 1ull << (bit & 63));
 }
 
-__global__ void __launch_bounds__(256) k_lower_nbr(const int4* lower_origin, const u64* lower_mask, i64 n, int op,
-                                                   int m, int m_src,
-                                                   const int32_t* tile_of_cand, const u64* tile_child,
-                                                   const uint16_t* tile_prefix, const int32_t* tile_lower_base,
-                                                   const int32_t* d_num_tiles, const int32_t* d_num_cands,
-                                                   int32_t* lower_nbr, int4* cand_origin, int32_t* cand_src,
-                                                   int32_t* flags) {
-  const i64 i = (i64)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
+// Pair i = (l, j): the candidate index of its target (its rank in the tile's
+// mask, after the tile's base), the candidate's origin, and the candidate ->
+// source table entry of l.
+__device__ __forceinline__ void lower_nbr_one(i64 i, const int4* lower_origin, const u64* lower_mask,
+                                              const uint32_t* reach, int op, int m, int m_src,
+                                              const int32_t* tile_of_cand, const u64* tile_child,
+                                              const uint16_t* tile_prefix, const int32_t* tile_lower_base,
+                                              int32_t num_tiles, int32_t num_cands, int32_t* lower_nbr,
+                                              int4* cand_origin, int32_t* cand_src, int32_t* flags) {
   const i64 l = i / m;
   const int j = (int)(i % m);
   const int4 o = lower_origin[l];
   const LowerTarget tg = lower_target(o, j, op);
-  if (!tg.ok || !lower_reaches(lower_mask + l * 64, op, j)) {
+  if (!tg.ok || !pair_reaches(lower_mask, reach, l, op, j)) {
     lower_nbr[i] = -1;
     return;
   }
   const int32_t t = tile_of_cand[(i64)o.w * m + tg.jt];
-  if (t < 0 || t >= *d_num_tiles) {
+  if (t < 0 || t >= num_tiles) {
     lower_nbr[i] = -1;
     set_flag(flags, kFlagInternal);
     return;
@@ -463,7 +498,7 @@ __global__ void __launch_bounds__(256) k_lower_nbr(const int4* lower_origin, con
   const int w = bit >> 6, b = bit & 63;
   const u64 word = tile_child[(i64)t * 512 + w];
   const int32_t c = tile_lower_base[t] + tile_prefix[(i64)t * 512 + w] + popc64(word & ((1ull << b) - 1));
-  if (!((word >> b) & 1ull) || c < 0 || c >= *d_num_cands) {
+  if (!((word >> b) & 1ull) || c < 0 || c >= num_cands) {
     lower_nbr[i] = -1;
     set_flag(flags, kFlagInternal);
     return;
@@ -480,6 +515,128 @@ __global__ void __launch_bounds__(256) k_lower_nbr(const int4* lower_origin, con
     js = index27(-e.x, -e.y, -e.z);
   }
   cand_src[(i64)c * m_src + js] = (int32_t)l;
+}
+
+__global__ void __launch_bounds__(256) k_lower_mark(const int4* lower_origin, const u64* lower_mask, i64 n, int op,
+                                                    int m, const int32_t* tile_of_cand, const int32_t* d_num_tiles,
+                                                    u64* tile_child, int32_t* flags) {
+  const i64 i = (i64)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  lower_mark_one(i, lower_origin, lower_mask, nullptr, op, m, tile_of_cand, *d_num_tiles, tile_child, flags);
+}
+
+__global__ void __launch_bounds__(256) k_lower_nbr(const int4* lower_origin, const u64* lower_mask, i64 n, int op,
+                                                   int m, int m_src, const int32_t* tile_of_cand,
+                                                   const u64* tile_child, const uint16_t* tile_prefix,
+                                                   const int32_t* tile_lower_base, const int32_t* d_num_tiles,
+                                                   const int32_t* d_num_cands, int32_t* lower_nbr, int4* cand_origin,
+                                                   int32_t* cand_src, int32_t* flags) {
+  const i64 i = (i64)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  lower_nbr_one(i, lower_origin, lower_mask, nullptr, op, m, m_src, tile_of_cand, tile_child, tile_prefix,
+                tile_lower_base, *d_num_tiles, *d_num_cands, lower_nbr, cand_origin, cand_src, flags);
+}
+
+// Small batches (at most kLowersSmallMax (lower, candidate) pairs, at most
+// kLowersSmallTiles tile candidates): the whole lower stage in one workgroup:
+// every source lower's reach set, marking, per-tile popcount prefix tables, the
+// scan over tiles (candidate numbering), the empty candidate -> source table,
+// and the candidate indices / origins / sources. When the unique tiles are few
+// (at most kLdsTiles, known only here) their candidate masks, prefix tables and
+// bases live in LDS and are copied out at the end; otherwise the same steps run
+// on the global arrays. Replaces five launches of the general path; phases are
+// separated by a device fence and a block barrier where later phases read what
+// other waves wrote to global memory.
+constexpr int kLowersSmallMax = 4096;
+constexpr int kLowersSmallTiles = 1024;
+constexpr int kLowersThreads = 1024;
+constexpr int kLdsTiles = 24;
+
+__global__ void __launch_bounds__(kLowersThreads) k_lowers_small(
+    const int4* lower_origin, const u64* lower_mask, i64 n, int op, int m, int m_src, const int32_t* tile_of_cand,
+    const int32_t* d_num_tiles, u64* tile_child, uint16_t* tile_prefix, int32_t* tile_lower_base,
+    int32_t* d_num_cands, u64* cand_child, int zero_cand_child, int32_t* lower_nbr, int4* cand_origin,
+    int32_t* cand_src, int32_t* flags) {
+  __shared__ u64 s_tile[kLdsTiles * 512];
+  __shared__ uint16_t s_tpre[kLdsTiles * 512];
+  __shared__ int32_t s_base[kLowersSmallTiles + 1];
+  __shared__ uint32_t s_reach[kLowersSmallMax];
+  __shared__ int32_t s_wave[kLowersThreads / kWave];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wv = tid / kWave;
+  const int32_t nt = *d_num_tiles;
+  const bool in_lds = nt <= kLdsTiles;  // uniform
+  u64* tch = in_lds ? s_tile : tile_child;
+  uint16_t* tpre = in_lds ? s_tpre : tile_prefix;
+  if (in_lds) {
+    for (int k = tid; k < nt * 512; k += kLowersThreads) s_tile[k] = 0;
+  } else {
+    ulonglong2* tc2 = reinterpret_cast<ulonglong2*>(tile_child);
+    for (i64 k = tid; k < (i64)nt * 256; k += kLowersThreads) tc2[k] = make_ulonglong2(0, 0);
+  }
+  // reach set of every source lower: one wave per lower, one mask word per lane
+  const i64 n_lower = n / m;
+  if (op != TC_OP_COARSEN) {
+    for (i64 l = wv; l < n_lower; l += kLowersThreads / kWave) {
+      uint32_t code = lower_word_reach(lower_mask[l * 64 + lane], lane, op);
+#pragma unroll
+      for (int d = 32; d >= 1; d >>= 1) code |= (uint32_t)__shfl_xor((int)code, d, kWave);
+      if (lane == 0) s_reach[l] = op == TC_OP_REFINE ? code : box_code_for_op(code, op, m);
+    }
+  }
+  __threadfence();
+  __syncthreads();
+  for (i64 i = tid; i < n; i += kLowersThreads)
+    lower_mark_one(i, lower_origin, lower_mask, s_reach, op, m, tile_of_cand, nt, tch, flags);
+  __threadfence();
+  __syncthreads();
+  // per-tile prefix tables: one wave per tile, 8 words per lane
+  for (int t = wv; t < nt; t += kLowersThreads / kWave) {
+    u64 wd[8];
+    int sum = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      wd[k] = tch[(i64)t * 512 + lane * 8 + k];
+      sum += popc64(wd[k]);
+    }
+    const int inc = wave_incl_scan(sum);
+    int ex = inc - sum;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      tpre[(i64)t * 512 + lane * 8 + k] = (uint16_t)ex;
+      ex += popc64(wd[k]);
+    }
+    if (lane == kWave - 1) s_base[t] = inc;
+  }
+  __syncthreads();
+  // candidate numbering: exclusive scan of the tiles' counts (one per thread)
+  const int cnt = tid < nt ? s_base[tid] : 0;
+  int total;
+  const int ex = block_excl_scan<int, kLowersThreads>(cnt, s_wave, total);
+  if (tid < nt) {
+    s_base[tid] = ex;
+    tile_lower_base[tid] = ex;
+  }
+  if (tid == 0) {
+    s_base[nt] = total;
+    tile_lower_base[nt] = total;
+    *d_num_cands = total;
+  }
+  for (i64 k = tid; k < (i64)total * m_src; k += kLowersThreads) cand_src[k] = -1;
+  if (zero_cand_child)
+    for (i64 k = tid; k < (i64)total * 64; k += kLowersThreads) cand_child[k] = 0;
+  __threadfence();
+  __syncthreads();
+  for (i64 i = tid; i < n; i += kLowersThreads)
+    lower_nbr_one(i, lower_origin, lower_mask, s_reach, op, m, m_src, tile_of_cand, tch, tpre, s_base, nt, total,
+                  lower_nbr, cand_origin, cand_src, flags);
+  if (in_lds) {  // the node writers read the masks and prefix tables later
+    for (int k = tid; k < nt * 512; k += kLowersThreads) {
+      tile_child[k] = s_tile[k];
+      tile_prefix[k] = s_tpre[k];
+    }
+  }
 }
 
 // ------------------------------------------------------------------ stage: leaves (pass A)
@@ -1198,12 +1355,15 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa) 
   int32_t* cand_src = a.at<int32_t>(o_csrc);
 
   // tiles
+  const bool small_lowers = small_tiles && nT <= kLowersSmallTiles && nL <= kLowersSmallMax;
   if (small_tiles) {
-    const bool zero_in_kernel = nT <= 256;  // at most 1 MiB of bitmaps for one workgroup
+    // the bitmaps are zeroed in-kernel when few (at most 1 MiB for one workgroup):
+    // by the fused lower stage, or here; otherwise by a wide fill
+    const bool zero_here = !small_lowers && nT <= 256;
     launch("k_tiles_small", k_tiles_small, 1, kTilesThreads, s, (const int4*)sv.upper_origin,
            (const u64*)sv.upper_mask, (int32_t)src->n2, op, oi.m, B, ts.utile, tile_of_cand, ts.d_num_tiles,
-           ts.grid_tile_begin, ts.tile_child, zero_in_kernel ? 1 : 0, ts.readback);
-    if (!zero_in_kernel) fill_u64(ts.tile_child, 0, nT * 512, ts.d_num_tiles, 512, s);
+           ts.grid_tile_begin, ts.tile_child, zero_here ? 1 : 0, ts.readback);
+    if (!small_lowers && !zero_here) fill_u64(ts.tile_child, 0, nT * 512, ts.d_num_tiles, 512, s);
   } else {
     fill_i32(ts.readback, 0, 1, nullptr, 1, s);
     if (nT > 0) {
@@ -1225,19 +1385,26 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa) 
     tree_tile_ranges(ts, B, s);
     fill_u64(ts.tile_child, 0, nT * 512, ts.d_num_tiles, 512, s);
   }
-  // lowers
-  launch("k_lower_mark", k_lower_mark, ceil_div(nL, 256), 256, s, (const int4*)sv.lower_origin,
-         (const u64*)sv.lower_mask, nL, op, oi.m, (const int32_t*)tile_of_cand, (const int32_t*)ts.d_num_tiles,
-         ts.tile_child, ts.flags);
-  tree_rank_tiles(ts, s);
-  // candidate -> source table starts empty; refine and the box ops store every
-  // word of their candidates' leaf masks, coarsen ORs into zeros
-  fill_pair(cand_src, -1, nL * oi.m_src, oi.m_src, ts.cand_child, 0, op == TC_OP_COARSEN ? nL * 64 : 0, 64,
-            ts.d_num_cands, s);
-  launch("k_lower_nbr", k_lower_nbr, ceil_div(nL, 256), 256, s, (const int4*)sv.lower_origin,
-         (const u64*)sv.lower_mask, nL, op, oi.m, oi.m_src, (const int32_t*)tile_of_cand, (const u64*)ts.tile_child,
-         (const uint16_t*)ts.tile_prefix, (const int32_t*)ts.tile_lower_base, (const int32_t*)ts.d_num_tiles,
-         (const int32_t*)ts.d_num_cands, lower_nbr, ts.cand_origin, cand_src, ts.flags);
+  // lowers. The candidate -> source table starts empty; refine and the box ops
+  // store every word of their candidates' leaf masks, coarsen ORs into zeros.
+  if (small_lowers) {
+    launch("k_lowers_small", k_lowers_small, 1, kLowersThreads, s, (const int4*)sv.lower_origin,
+           (const u64*)sv.lower_mask, nL, op, oi.m, oi.m_src, (const int32_t*)tile_of_cand,
+           (const int32_t*)ts.d_num_tiles, ts.tile_child, ts.tile_prefix, ts.tile_lower_base, ts.d_num_cands,
+           ts.cand_child, op == TC_OP_COARSEN ? 1 : 0, lower_nbr, ts.cand_origin, cand_src, ts.flags);
+  } else {
+    launch("k_lower_mark", k_lower_mark, ceil_div(nL, 256), 256, s, (const int4*)sv.lower_origin,
+           (const u64*)sv.lower_mask, nL, op, oi.m, (const int32_t*)tile_of_cand, (const int32_t*)ts.d_num_tiles,
+           ts.tile_child, ts.flags);
+    tree_rank_tiles(ts, s);
+    fill_pair(cand_src, -1, nL * oi.m_src, oi.m_src, ts.cand_child, 0, op == TC_OP_COARSEN ? nL * 64 : 0, 64,
+              ts.d_num_cands, s);
+    launch("k_lower_nbr", k_lower_nbr, ceil_div(nL, 256), 256, s, (const int4*)sv.lower_origin,
+           (const u64*)sv.lower_mask, nL, op, oi.m, oi.m_src, (const int32_t*)tile_of_cand,
+           (const u64*)ts.tile_child, (const uint16_t*)ts.tile_prefix, (const int32_t*)ts.tile_lower_base,
+           (const int32_t*)ts.d_num_tiles, (const int32_t*)ts.d_num_cands, lower_nbr, ts.cand_origin, cand_src,
+           ts.flags);
+  }
   // leaves (pass A)
   if (op == TC_OP_REFINE || op == TC_OP_COARSEN) {
     launch("k_leaf_mark_lower", k_leaf_mark_lower, (i64)src->n1, 256, s, (const int4*)sv.leaf_origin,
@@ -1252,8 +1419,7 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa) 
            (const u64*)sv.leaf_mask, sv.n_lower, sv.n_leaf, ts.cand_child, ts.flags);
   }
   // counts and the single readback
-  tree_count_cands(ts, s);
-  tree_grid_counts(ts, B, s);
+  tree_counts(ts, B, s);
   const size_t rb_bytes = 4 * (4 + 3 * (size_t)B);
   int32_t* h_rb = static_cast<int32_t*>(pinned_staging(rb_bytes));
   hip_check(hipMemcpyAsync(h_rb, ts.readback, rb_bytes, hipMemcpyDeviceToHost, s), "readback");

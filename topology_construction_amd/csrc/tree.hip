@@ -140,13 +140,10 @@ __global__ void __launch_bounds__(256) k_grid_counts(const int32_t* grid_tile_be
 constexpr int kTailThreads = 1024;
 constexpr int kTailItems = 4;
 
-__global__ void __launch_bounds__(kTailThreads) k_counts_tail(const int32_t* grid_tile_begin,
-                                                              const int32_t* tile_lower_base, const i64* cand_scan,
-                                                              const int32_t* d_num_tiles, const int32_t* d_num_cands,
-                                                              int32_t B, int32_t* upper_excl, int32_t* grid_info,
-                                                              int32_t* readback) {
-  __shared__ int32_t s_wave[kTailThreads / kWave];
-  const int32_t nt = *d_num_tiles;
+__device__ __forceinline__ void counts_tail_body(const int32_t* grid_tile_begin, const int32_t* tile_lower_base,
+                                                 const i64* cand_scan, int32_t nt, int32_t nc, int32_t B,
+                                                 int32_t* upper_excl, int32_t* grid_info, int32_t* readback,
+                                                 int32_t* s_wave) {
   int f[kTailItems];
   int sum = 0;
 #pragma unroll
@@ -164,10 +161,104 @@ __global__ void __launch_bounds__(kTailThreads) k_counts_tail(const int32_t* gri
     ex += f[k];
   }
   if (threadIdx.x == 0) upper_excl[nt] = total;
+  __threadfence();
   __syncthreads();  // upper_excl is read back below by other threads of this block
-  if (threadIdx.x == 0) batch_totals(upper_excl, cand_scan, nt, *d_num_cands, readback);
+  if (threadIdx.x == 0) batch_totals(upper_excl, cand_scan, nt, nc, readback);
   for (i64 g = threadIdx.x; g < B; g += kTailThreads)
     grid_counts_one(g, grid_tile_begin, tile_lower_base, upper_excl, cand_scan, grid_info, readback);
+}
+
+__global__ void __launch_bounds__(kTailThreads) k_counts_tail(const int32_t* grid_tile_begin,
+                                                              const int32_t* tile_lower_base, const i64* cand_scan,
+                                                              const int32_t* d_num_tiles, const int32_t* d_num_cands,
+                                                              int32_t B, int32_t* upper_excl, int32_t* grid_info,
+                                                              int32_t* readback) {
+  __shared__ int32_t s_wave[kTailThreads / kWave];
+  counts_tail_body(grid_tile_begin, tile_lower_base, cand_scan, *d_num_tiles, *d_num_cands, B, upper_excl, grid_info,
+                   readback, s_wave);
+}
+
+// Small batches (at most kCountsSmallMax candidates and kTailThreads * kTailItems
+// tiles): candidate leaf counts and prefix tables, their packed scan and the
+// tail above, in one workgroup.
+constexpr int kCountsSmallMax = 4096;
+
+__global__ void __launch_bounds__(kTailThreads) k_counts_small(const u64* cand_child, uint16_t* cand_prefix,
+                                                               i64* cand_counts, i64* cand_scan,
+                                                               const int32_t* grid_tile_begin,
+                                                               const int32_t* tile_lower_base,
+                                                               const int32_t* d_num_tiles, const int32_t* d_num_cands,
+                                                               int32_t B, int32_t* upper_excl, int32_t* grid_info,
+                                                               int32_t* readback) {
+  __shared__ i64 s_cc[kCountsSmallMax + 1];
+  __shared__ int32_t s_wave[kTailThreads / kWave];
+  __shared__ i64 s_wave64[kTailThreads / kWave];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wv = tid / kWave;
+  const int32_t nc = *d_num_cands;
+  const int32_t nt = *d_num_tiles;
+  // one wave per candidate (four in flight): per-word prefix and the packed count
+  constexpr int kWaves = kTailThreads / kWave;
+  for (int c0 = wv * 4; c0 < nc; c0 += kWaves * 4) {
+    u64 w[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) w[v] = c0 + v < nc ? cand_child[(i64)(c0 + v) * 64 + lane] : 0;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      if (c0 + v >= nc) break;
+      const int cnt = popc64(w[v]);
+      const int inc = wave_incl_scan(cnt);
+      cand_prefix[(i64)(c0 + v) * 64 + lane] = (uint16_t)(inc - cnt);
+      if (lane == kWave - 1) {
+        const i64 packed = (i64)inc | ((i64)(inc > 0 ? 1 : 0) << 32);
+        cand_counts[c0 + v] = packed;
+        s_cc[c0 + v] = packed;
+      }
+    }
+  }
+  __syncthreads();
+  // exclusive scan of the packed counts (blocked, 4 per thread)
+  constexpr int kPer = kCountsSmallMax / kTailThreads;
+  i64 v[kPer];
+  i64 sum = 0;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int c = tid * kPer + k;
+    v[k] = c < nc ? s_cc[c] : 0;
+    sum += v[k];
+  }
+  i64 total;
+  i64 ex = block_excl_scan<i64, kTailThreads>(sum, s_wave64, total);
+  // every thread has read its counts from s_cc (the scan's barriers), so the
+  // scan can replace them in LDS for the tail below
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int c = tid * kPer + k;
+    if (c < nc) {
+      cand_scan[c] = ex;
+      s_cc[c] = ex;
+    }
+    ex += v[k];
+  }
+  if (tid == 0) {
+    cand_scan[nc] = total;
+    s_cc[nc] = total;
+  }
+  __syncthreads();
+  counts_tail_body(grid_tile_begin, tile_lower_base, s_cc, nt, nc, B, upper_excl, grid_info, readback, s_wave);
+}
+
+void tree_counts(TreeScratch& ts, int32_t B, hipStream_t s) {
+  if (ts.cap_cands <= kCountsSmallMax && ts.cap_tiles <= (i64)kTailThreads * kTailItems) {
+    launch("k_counts_small", k_counts_small, 1, kTailThreads, s, (const u64*)ts.cand_child, ts.cand_prefix,
+           ts.cand_counts, ts.cand_scan, (const int32_t*)ts.grid_tile_begin, (const int32_t*)ts.tile_lower_base,
+           (const int32_t*)ts.d_num_tiles, (const int32_t*)ts.d_num_cands, B, ts.upper_excl, ts.grid_info,
+           ts.readback);
+    return;
+  }
+  tree_count_cands(ts, s);
+  tree_grid_counts(ts, B, s);
 }
 
 void tree_count_cands(TreeScratch& ts, hipStream_t s) {
@@ -409,10 +500,166 @@ int32_t bbox_replicas(int32_t B) {
   return r < 1 ? 1 : (r > 64 ? 64 : r);
 }
 
+// Small batches (at most kFinSmallLeaves leaves and kFinSmallGrids grids): the
+// voxel scan, leaf offsets, bboxes (folded in LDS) and headers in one
+// workgroup. Leaves go in tiles of 16 waves x kFinPer x 64: wave w owns a
+// contiguous run of kFinPer * 64 leaves, its lanes reading them 64 at a time
+// (coalesced). The scan is a wave scan per group plus a 16-entry table of wave
+// totals; each lane folds the bbox of its leaves in registers (a run rarely
+// holds more than one grid), and the wave reduces once per tile.
+constexpr int kFinThreads = 1024;
+constexpr int kFinPer = 8;
+constexpr i64 kFinSmallLeaves = 65536;
+constexpr int kFinSmallGrids = 1024;
+
+__device__ __forceinline__ void box_fold_lds(int32_t (*s_box)[kFinSmallGrids], int g, const int v[6]) {
+  for (int a = 0; a < 3; ++a) {
+    atomicMin(&s_box[a][g], v[a]);
+    atomicMax(&s_box[3 + a][g], v[3 + a]);
+  }
+}
+
+__global__ void __launch_bounds__(kFinThreads) k_finalize_small(const int4* leaf_origin, const i64* leaf_vox,
+                                                                const uint32_t* leaf_box, const int32_t* grid_info,
+                                                                i64* vox_excl, i64* leaf_offset, int32_t B, i64 L,
+                                                                tc_grid_header* hdr) {
+  constexpr int kWaves = kFinThreads / kWave;
+  constexpr int kRun = kFinPer * kWave;  // leaves per wave per tile
+  __shared__ int32_t s_box[6][kFinSmallGrids];
+  __shared__ i64 s_gvb[kFinSmallGrids];  // scan value at each grid's first leaf
+  __shared__ i64 s_tot[kWaves];          // wave totals, then their exclusive offsets
+  __shared__ i64 s_carry;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wv = tid / kWave;
+  for (int g = tid; g < B; g += kFinThreads) {
+    for (int a = 0; a < 3; ++a) {
+      s_box[a][g] = INT32_MAX;
+      s_box[3 + a][g] = INT32_MIN;
+    }
+  }
+  if (tid == 0) s_carry = 0;
+  __syncthreads();
+  for (i64 base = 0; base < L; base += (i64)kWaves * kRun) {
+    const i64 run0 = base + (i64)wv * kRun;
+    i64 v[kFinPer];
+    int4 o[kFinPer];
+    uint32_t bx[kFinPer];
+    int32_t gfirst[kFinPer];
+#pragma unroll
+    for (int k = 0; k < kFinPer; ++k) {
+      const i64 i = run0 + k * kWave + lane;
+      const bool in = i < L;
+      v[k] = in ? leaf_vox[i] : 0;
+      o[k] = in ? leaf_origin[i] : make_int4(0, 0, 0, -1);
+      bx[k] = in ? leaf_box[i] : kEmptyBox;
+    }
+#pragma unroll
+    for (int k = 0; k < kFinPer; ++k) gfirst[k] = o[k].w >= 0 && o[k].w < B ? grid_info[o[k].w * 6 + 5] : -1;
+    i64 ex[kFinPer];
+    i64 carry = 0;
+#pragma unroll
+    for (int k = 0; k < kFinPer; ++k) {
+      const i64 inc = wave_incl_scan(v[k]);
+      ex[k] = carry + inc - v[k];
+      carry += __shfl(inc, kWave - 1, kWave);
+    }
+    if (lane == 0) s_tot[wv] = carry;
+    __syncthreads();
+    if (wv == 0) {  // exclusive offsets of the wave totals, after the running carry
+      const i64 t = lane < kWaves ? s_tot[lane] : 0;
+      const i64 inc = wave_incl_scan(t);
+      const i64 c0 = s_carry;
+      if (lane < kWaves) s_tot[lane] = c0 + inc - t;
+      if (lane == kWave - 1) s_carry = c0 + inc;
+    }
+    __syncthreads();
+    const i64 off = s_tot[wv];
+#pragma unroll
+    for (int k = 0; k < kFinPer; ++k) {
+      const i64 i = run0 + k * kWave + lane;
+      ex[k] += off;
+      if (i < L) vox_excl[i] = ex[k];
+      if (i < L && i == gfirst[k]) s_gvb[o[k].w] = ex[k];  // leaves come grid by grid
+    }
+    __syncthreads();  // the grids' first-leaf scan values are read below
+    int g = -1;
+    int bv[6] = {INT32_MAX, INT32_MAX, INT32_MAX, INT32_MIN, INT32_MIN, INT32_MIN};
+#pragma unroll
+    for (int k = 0; k < kFinPer; ++k) {
+      const i64 i = run0 + k * kWave + lane;
+      const int gk = o[k].w;
+      if (i >= L || gk < 0 || gk >= B) continue;
+      leaf_offset[i] = ex[k] - s_gvb[gk];
+      if (bx[k] == kEmptyBox) continue;
+      if (gk != g) {
+        if (g >= 0) box_fold_lds(s_box, g, bv);
+        g = gk;
+        for (int a = 0; a < 3; ++a) {
+          bv[a] = INT32_MAX;
+          bv[3 + a] = INT32_MIN;
+        }
+      }
+      bv[0] = min(bv[0], o[k].x + (int)(bx[k] & 7));
+      bv[3] = max(bv[3], o[k].x + (int)((bx[k] >> 3) & 7));
+      bv[1] = min(bv[1], o[k].y + (int)((bx[k] >> 6) & 7));
+      bv[4] = max(bv[4], o[k].y + (int)((bx[k] >> 9) & 7));
+      bv[2] = min(bv[2], o[k].z + (int)((bx[k] >> 12) & 7));
+      bv[5] = max(bv[5], o[k].z + (int)((bx[k] >> 15) & 7));
+    }
+    const bool act = g >= 0;
+    const u64 am = __ballot(act);
+    if (am) {  // uniform per wave
+      const int first = __builtin_ctzll(am);
+      const int g0 = __shfl(g, first, kWave);
+      if (__ballot(act && g != g0) == 0) {  // one grid left in every active lane
+        int r[6];
+#pragma unroll
+        for (int a = 0; a < 3; ++a) {
+          r[a] = wave_min_i32(bv[a]);
+          r[3 + a] = wave_max_i32(bv[3 + a]);
+        }
+        if (lane == first) box_fold_lds(s_box, g0, r);
+      } else if (act) {
+        box_fold_lds(s_box, g, bv);
+      }
+    }
+  }
+  if (tid == 0) vox_excl[L] = s_carry;
+  __threadfence();
+  __syncthreads();
+  for (int gg = tid; gg < B; gg += kFinThreads) {
+    const int32_t* gi = grid_info + (i64)gg * 6;
+    tc_grid_header h;
+    h.grid_index = gg;
+    h.grid_count = B;
+    h.upper_count = gi[0];
+    h.lower_count = gi[1];
+    h.leaf_count = gi[2];
+    h.upper_begin = gi[3];
+    h.lower_begin = gi[4];
+    h.leaf_begin = gi[5];
+    h.voxel_begin = vox_excl[gi[5]];
+    h.voxel_count = vox_excl[gi[5] + gi[2]] - h.voxel_begin;
+    for (int a = 0; a < 3; ++a) {
+      h.bbox_min[a] = s_box[a][gg];
+      h.bbox_max[a] = s_box[3 + a][gg];
+    }
+    h.reserved[0] = 0;
+    h.reserved[1] = 0;
+    hdr[gg] = h;
+  }
+}
+
 void tree_finalize_leaves(const GridView& out, const i64* leaf_vox, const uint32_t* leaf_box, i64* vox_excl, void* scan_tmp,
                           int32_t* bbox_accum, const int32_t* grid_info, hipStream_t s) {
   const i64 L = out.n_leaf;
   const int32_t B = out.B;
+  if (L <= kFinSmallLeaves && B <= kFinSmallGrids) {
+    launch("k_finalize_small", k_finalize_small, 1, kFinThreads, s, (const int4*)out.leaf_origin, leaf_vox, leaf_box,
+           grid_info, vox_excl, out.leaf_offset, B, L, out.headers);
+    return;
+  }
   const int32_t R = bbox_replicas(B);
   fill_split_i32(bbox_accum, INT32_MAX, 3 * (i64)R * B, INT32_MIN, 3 * (i64)R * B, s);
   scan_excl_i64(leaf_vox, vox_excl, L, nullptr, s, nullptr, scan_tmp);

@@ -335,6 +335,62 @@ __global__ void __launch_bounds__(kTilesThreads) k_tiles_small(const int4* upper
       ++pos;
     }
   }
+  __shared__ int32_t s_nt;
+  if (K <= kWave) {
+    // few keys: one wave sorts (bitonic over lanes), deduplicates and scatters,
+    // with no block barriers
+    __syncthreads();
+    if (wv == 0) {
+      u64 hi = lane < K ? s_hi[lane] : ~0ull, lo = lane < K ? s_lo[lane] : ~0ull;
+      uint32_t v = lane < K ? s_v[lane] : 0xffffffffu;
+#pragma unroll
+      for (int k = 2; k <= kWave; k <<= 1) {
+#pragma unroll
+        for (int jj = k >> 1; jj > 0; jj >>= 1) {
+          const u64 oh = __shfl_xor(hi, jj, kWave), ol = __shfl_xor(lo, jj, kWave);
+          const uint32_t ov = (uint32_t)__shfl_xor((int)v, jj, kWave);
+          const bool gt = hi != oh ? hi > oh : (lo != ol ? lo > ol : v > ov);
+          const bool lt = hi != oh ? hi < oh : (lo != ol ? lo < ol : v < ov);
+          const bool up = (lane & k) == 0, lower = (lane & jj) == 0;
+          const bool take = up ? (lower ? gt : lt) : (lower ? lt : gt);
+          if (take) {
+            hi = oh;
+            lo = ol;
+            v = ov;
+          }
+        }
+      }
+      const u64 ph = __shfl_up(hi, 1, kWave), pl = __shfl_up(lo, 1, kWave);
+      const int head = lane < K && (lane == 0 || !(ph == hi && pl == lo)) ? 1 : 0;
+      const int inc = wave_incl_scan(head);
+      const int nt = __shfl(inc, kWave - 1, kWave);
+      const int32_t g = (int32_t)((hi << 4) | (lo >> 60));  // grid of this lane's key
+      const int32_t gp = __shfl_up(g, 1, kWave);
+      if (lane < K) {
+        const int t = inc - 1;
+        if (v < (uint32_t)n) tile_of_cand[v] = t;
+        if (head) {
+          utile[t] = make_int4((int32_t)((lo >> 40) & 0xfffff) - kTileBias, (int32_t)((lo >> 20) & 0xfffff) - kTileBias,
+                               (int32_t)(lo & 0xfffff) - kTileBias, g);
+          for (int q = (lane == 0 ? -1 : gp) + 1; q <= g; ++q) grid_tile_begin[q] = t;
+          if (t == nt - 1)
+            for (int q = g + 1; q <= B; ++q) grid_tile_begin[q] = nt;
+        }
+      }
+      if (nt == 0)
+        for (int q = lane; q <= B; q += kWave) grid_tile_begin[q] = 0;
+      if (lane == 0) {
+        *d_num_tiles = nt;
+        s_nt = nt;
+      }
+    }
+    __syncthreads();
+    if (zero_child) {
+      ulonglong2* tc = reinterpret_cast<ulonglong2*>(tile_child);
+      for (i64 k = tid; k < (i64)s_nt * 256; k += kTilesThreads) tc[k] = make_ulonglong2(0, 0);
+    }
+    return;
+  }
   int P = 2;
   while (P < K) P <<= 1;
   for (int i = K + tid; i < P; i += kTilesThreads) {  // padding sorts last
@@ -542,15 +598,16 @@ __global__ void __launch_bounds__(256) k_lower_nbr(const int4* lower_origin, con
 // every source lower's reach set, marking, per-tile popcount prefix tables, the
 // scan over tiles (candidate numbering), the empty candidate -> source table,
 // and the candidate indices / origins / sources. When the unique tiles are few
-// (at most kLdsTiles, known only here) their candidate masks, prefix tables and
-// bases live in LDS and are copied out at the end; otherwise the same steps run
-// on the global arrays. Replaces five launches of the general path; phases are
+// (at most kLdsTiles, known only here) their candidate masks and bases live in
+// LDS and the masks are copied out at the end; otherwise the same steps run on
+// the global arrays. Replaces five launches of the general path; phases are
 // separated by a device fence and a block barrier where later phases read what
 // other waves wrote to global memory.
 constexpr int kLowersSmallMax = 4096;
 constexpr int kLowersSmallTiles = 1024;
 constexpr int kLowersThreads = 1024;
-constexpr int kLdsTiles = 24;
+constexpr int kLdsTiles = 36;
+constexpr int kReachMax = 512;  // source lowers with a reach set: n / m for m >= 8
 
 __global__ void __launch_bounds__(kLowersThreads) k_lowers_small(
     const int4* lower_origin, const u64* lower_mask, i64 n, int op, int m, int m_src, const int32_t* tile_of_cand,
@@ -558,9 +615,8 @@ __global__ void __launch_bounds__(kLowersThreads) k_lowers_small(
     int32_t* d_num_cands, u64* cand_child, int zero_cand_child, int32_t* lower_nbr, int4* cand_origin,
     int32_t* cand_src, int32_t* flags) {
   __shared__ u64 s_tile[kLdsTiles * 512];
-  __shared__ uint16_t s_tpre[kLdsTiles * 512];
   __shared__ int32_t s_base[kLowersSmallTiles + 1];
-  __shared__ uint32_t s_reach[kLowersSmallMax];
+  __shared__ uint32_t s_reach[kReachMax];
   __shared__ int32_t s_wave[kLowersThreads / kWave];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -568,7 +624,6 @@ __global__ void __launch_bounds__(kLowersThreads) k_lowers_small(
   const int32_t nt = *d_num_tiles;
   const bool in_lds = nt <= kLdsTiles;  // uniform
   u64* tch = in_lds ? s_tile : tile_child;
-  uint16_t* tpre = in_lds ? s_tpre : tile_prefix;
   if (in_lds) {
     for (int k = tid; k < nt * 512; k += kLowersThreads) s_tile[k] = 0;
   } else {
@@ -604,7 +659,7 @@ __global__ void __launch_bounds__(kLowersThreads) k_lowers_small(
     int ex = inc - sum;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      tpre[(i64)t * 512 + lane * 8 + k] = (uint16_t)ex;
+      tile_prefix[(i64)t * 512 + lane * 8 + k] = (uint16_t)ex;
       ex += popc64(wd[k]);
     }
     if (lane == kWave - 1) s_base[t] = inc;
@@ -629,14 +684,10 @@ __global__ void __launch_bounds__(kLowersThreads) k_lowers_small(
   __threadfence();
   __syncthreads();
   for (i64 i = tid; i < n; i += kLowersThreads)
-    lower_nbr_one(i, lower_origin, lower_mask, s_reach, op, m, m_src, tile_of_cand, tch, tpre, s_base, nt, total,
-                  lower_nbr, cand_origin, cand_src, flags);
-  if (in_lds) {  // the node writers read the masks and prefix tables later
-    for (int k = tid; k < nt * 512; k += kLowersThreads) {
-      tile_child[k] = s_tile[k];
-      tile_prefix[k] = s_tpre[k];
-    }
-  }
+    lower_nbr_one(i, lower_origin, lower_mask, s_reach, op, m, m_src, tile_of_cand, tch, tile_prefix, s_base, nt,
+                  total, lower_nbr, cand_origin, cand_src, flags);
+  if (in_lds)  // the node writers read the masks later
+    for (int k = tid; k < nt * 512; k += kLowersThreads) tile_child[k] = s_tile[k];
 }
 
 // ------------------------------------------------------------------ stage: leaves (pass A)
@@ -1355,7 +1406,8 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa) 
   int32_t* cand_src = a.at<int32_t>(o_csrc);
 
   // tiles
-  const bool small_lowers = small_tiles && nT <= kLowersSmallTiles && nL <= kLowersSmallMax;
+  const bool small_lowers = small_tiles && nT <= kLowersSmallTiles && nL <= kLowersSmallMax &&
+                            (op == TC_OP_COARSEN || nL / oi.m <= kReachMax);
   if (small_tiles) {
     // the bitmaps are zeroed in-kernel when few (at most 1 MiB for one workgroup):
     // by the fused lower stage, or here; otherwise by a wide fill

@@ -603,7 +603,7 @@ __global__ void __launch_bounds__(256) k_lower_nbr(const int4* lower_origin, con
 // the global arrays. Replaces five launches of the general path; phases are
 // separated by a device fence and a block barrier where later phases read what
 // other waves wrote to global memory.
-constexpr int kLowersSmallMax = 4096;
+constexpr int kLowersSmallMax = 2048;  // beyond this the five-launch path is faster
 constexpr int kLowersSmallTiles = 1024;
 constexpr int kLowersThreads = 1024;
 constexpr int kLdsTiles = 36;

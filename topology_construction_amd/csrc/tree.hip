@@ -181,7 +181,7 @@ __global__ void __launch_bounds__(kTailThreads) k_counts_tail(const int32_t* gri
 // Small batches (at most kCountsSmallMax candidates and kTailThreads * kTailItems
 // tiles): candidate leaf counts and prefix tables, their packed scan and the
 // tail above, in one workgroup.
-constexpr int kCountsSmallMax = 4096;
+constexpr int kCountsSmallMax = 2048;  // beyond this the multi-launch path is faster
 
 __global__ void __launch_bounds__(kTailThreads) k_counts_small(const u64* cand_child, uint16_t* cand_prefix,
                                                                i64* cand_counts, i64* cand_scan,

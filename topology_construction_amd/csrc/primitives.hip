@@ -18,6 +18,40 @@ __device__ __forceinline__ i64 clamp_n(i64 n_host, const int32_t* d_n) {
   return n;
 }
 
+// In the multi-block scan a tile of kScanTile items is held striped: item
+// k * kScanThreads + t in register k of thread t, so every load and store
+// instruction is coalesced. The tile's
+// exclusive scan is a wave scan per row k plus one 64-entry table of the
+// (row, wave) totals, scanned by one wave.
+static_assert(kScanItems * (kScanThreads / kWave) == kWave, "one table entry per lane");
+
+template <typename T>
+__device__ __forceinline__ T tile_scan_striped(const T v[kScanItems], T ex[kScanItems], T* s_tab) {
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  T inc[kScanItems];
+#pragma unroll
+  for (int k = 0; k < kScanItems; ++k) {
+    inc[k] = wave_incl_scan(v[k]);
+    if (lane == kWave - 1) s_tab[k * (kScanThreads / kWave) + w] = inc[k];
+  }
+  __syncthreads();
+  if (w == 0) {
+    const T t = s_tab[lane];
+    const T i2 = wave_incl_scan(t);
+    s_tab[lane] = i2 - t;
+    if (lane == kWave - 1) s_tab[kWave] = i2;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < kScanItems; ++k) ex[k] = s_tab[k * (kScanThreads / kWave) + w] + inc[k] - v[k];
+  const T total = s_tab[kWave];
+  __syncthreads();  // the table is free again
+  return total;
+}
+
+// Single-workgroup scans (at most one tile, and the partials) hold items blocked:
+// thread t owns items t*kScanItems .. +kScanItems-1, which needs one block scan
+// only; these launches are latency-bound, so fewer steps beat coalescing.
 template <typename T>
 __global__ void __launch_bounds__(kScanThreads) k_scan_single(const T* in, T* out, i64 n_host,
                                                               const int32_t* d_n, T* total_out) {
@@ -51,11 +85,11 @@ __global__ void __launch_bounds__(kScanThreads) k_scan_reduce(const T* in, T* pa
                                                               const int32_t* d_n) {
   __shared__ T s_wave[kScanThreads / kWave];
   const i64 n = clamp_n(n_host, d_n);
-  const i64 base = (i64)blockIdx.x * kScanTile + (i64)threadIdx.x * kScanItems;
+  const i64 base = (i64)blockIdx.x * kScanTile + threadIdx.x;
   T sum = 0;
 #pragma unroll
   for (int k = 0; k < kScanItems; ++k) {
-    const i64 i = base + k;
+    const i64 i = base + (i64)k * kScanThreads;
     if (i < n) sum += in[i];
   }
   T total;
@@ -98,25 +132,22 @@ __global__ void __launch_bounds__(kScanThreads) k_scan_partials(T* partial, i64 
 template <typename T>
 __global__ void __launch_bounds__(kScanThreads) k_scan_down(const T* in, T* out, const T* partial, i64 n_host,
                                                             const int32_t* d_n) {
-  __shared__ T s_wave[kScanThreads / kWave];
+  __shared__ T s_tab[kWave + 1];
   const i64 n = clamp_n(n_host, d_n);
-  const i64 base = (i64)blockIdx.x * kScanTile + (i64)threadIdx.x * kScanItems;
+  const i64 base = (i64)blockIdx.x * kScanTile + threadIdx.x;
   if ((i64)blockIdx.x * kScanTile >= n) return;  // uniform per block
-  T v[kScanItems];
-  T sum = 0;
+  T v[kScanItems], ex[kScanItems];
 #pragma unroll
   for (int k = 0; k < kScanItems; ++k) {
-    const i64 i = base + k;
+    const i64 i = base + (i64)k * kScanThreads;
     v[k] = i < n ? in[i] : T(0);
-    sum += v[k];
   }
-  T total;
-  T excl = block_excl_scan<T, kScanThreads>(sum, s_wave, total) + partial[blockIdx.x];
+  (void)tile_scan_striped(v, ex, s_tab);
+  const T off = partial[blockIdx.x];
 #pragma unroll
   for (int k = 0; k < kScanItems; ++k) {
-    const i64 i = base + k;
-    if (i < n) out[i] = excl;
-    excl += v[k];
+    const i64 i = base + (i64)k * kScanThreads;
+    if (i < n) out[i] = ex[k] + off;
   }
 }
 

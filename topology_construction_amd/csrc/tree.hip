@@ -345,17 +345,27 @@ __global__ void __launch_bounds__(256) k_write_nodes(
     lower_origin[lo] = make_int4(co.x, co.y, co.z, upper_excl[co.w]);
     lower_first[lo] = lb;
   }
-  u64 rest = word;
-  int32_t idx = lb + pre;
-  while (rest) {
-    const int b = __builtin_ctzll(rest);
-    const int bit = lane * 64 + b;  // (x*16 + y)*16 + z
+  // leaf records in output order, 64 at a time: lane j takes leaf r = k0 + j, finds
+  // its word (last word whose prefix is <= r, by binary search over the lanes'
+  // prefixes) and bit, so consecutive lanes store consecutive records
+  const int pre_i = pre;
+  for (int32_t k0 = 0; k0 < cnt; k0 += kWave) {
+    const int32_t r = k0 + lane;
+    int w = 0;
+#pragma unroll
+    for (int step = 32; step >= 1; step >>= 1) {
+      const int p = __shfl(pre_i, w + step, kWave);
+      if (w + step < kWave && p <= r) w += step;
+    }
+    const u64 ww = __shfl(word, w, kWave);
+    const int pw = __shfl(pre_i, w, kWave);
+    if (r >= cnt) continue;
+    const int bit = w * 64 + select_bit(ww, r - pw);  // (x*16 + y)*16 + z
     const int px = bit >> 8, py = (bit >> 4) & 15, pz = bit & 15;
+    const i64 idx = (i64)lb + r;
     leaf_origin[idx] = make_int4(co.x + px * 8, co.y + py * 8, co.z + pz * 8, g);
     leaf_parent[idx] = (int32_t)lo;
     leaf_cand[idx] = (int32_t)c;
-    rest &= rest - 1;
-    ++idx;
   }
 }
 

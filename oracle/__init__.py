@@ -20,10 +20,11 @@ SRC = os.path.join(HERE, "oracle.cpp")
 LIB = os.path.join(HERE, "liboracle.so")
 
 # Op ids, as documented in oracle.cpp.
-IDENTITY, COARSEN, REFINE, DILATE, PAD_NEG, PAD_POS, CONV_T_K3S2 = range(7)
+IDENTITY, COARSEN, REFINE, DILATE, PAD_NEG, PAD_POS, CONV_T_K3S2, CONV_S1, CONV_T_S1 = range(9)
 OP_IDS = {
     "identity": IDENTITY, "coarsen": COARSEN, "refine": REFINE, "dilate": DILATE,
     "pad_neg": PAD_NEG, "pad_pos": PAD_POS, "conv_t_k3s2": CONV_T_K3S2,
+    "conv_s1": CONV_S1, "conv_t_s1": CONV_T_S1,
 }
 
 OK, INVALID, OVERFLOW, NOMEM = 0, 1, 2, 3

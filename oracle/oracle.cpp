@@ -12,10 +12,16 @@
 //        pad_neg    : { v + e : e in {-1,0}^3 }
 //        pad_pos    : { v + e : e in {0,1}^3 }
 //        k3s2 transpose : pad_neg(refine_2(S))
+//        conv_s1 K  : { v + e : e in [-floor(K/2), floor((K-1)/2)]^3 }   K in [1,8]
+//        conv_t_s1 K: { v + e : e in [-floor((K-1)/2), floor(K/2)]^3 }   K in [1,8]
 //        identity   : S (a grid built directly from ijk)
 //      Source: "Batched leaf-mask topology construction for generated conv grids"
 //      (PR page), sections 1 and 2; factors 4 and 8 are the closed forms of the
-//      chained x2 passes described in section 1.
+//      chained x2 passes described in section 1. The stride-1 kernel-K targets
+//      (section 2, and K in {2,3,4,5} in the test plan) are the Minkowski sums
+//      with the kernel's offset box O_K = [-floor((K-1)/2), floor(K/2)]^3: the
+//      transposed conv scatters to S + O_K, the conv gathers from it, giving
+//      S - O_K (reading: the pages do not fix which side an even kernel leans to).
 //   2. the canonical order: root tiles by signed x-major tile coordinate (the
 //      offset-shifted sort key), then the x-major upper-node child offset, then
 //      the x-major lower-node child offset, then the x-major in-leaf bit index
@@ -49,7 +55,7 @@ using i64 = int64_t;
 using u64 = uint64_t;
 
 enum Op { OP_IDENTITY = 0, OP_COARSEN = 1, OP_REFINE = 2, OP_DILATE = 3,
-          OP_PAD_NEG = 4, OP_PAD_POS = 5, OP_CONV_T_K3S2 = 6 };
+          OP_PAD_NEG = 4, OP_PAD_POS = 5, OP_CONV_T_K3S2 = 6, OP_CONV_S1 = 7, OP_CONV_T_S1 = 8 };
 
 enum Status { ST_OK = 0, ST_INVALID = 1, ST_OVERFLOW = 2, ST_NOMEM = 3 };
 
@@ -120,6 +126,8 @@ bool apply_op(int op, int factor, const std::vector<Vox>& in, std::vector<Vox>& 
       box(-1, 0, fine);
       break;
     }
+    case OP_CONV_S1: box(-(factor / 2), (factor - 1) / 2, in); break;
+    case OP_CONV_T_S1: box(-((factor - 1) / 2), factor / 2, in); break;
     default: return false;
   }
   for (const Vox& v : out)
@@ -184,6 +192,7 @@ int oracle_build(int op, int factor, const int32_t* ijk, const int64_t* offsets,
     case OP_CONV_T_K3S2: if (factor != 2) return ST_INVALID; break;
     case OP_IDENTITY: case OP_DILATE: case OP_PAD_NEG: case OP_PAD_POS:
       if (factor != 1) return ST_INVALID; break;
+    case OP_CONV_S1: case OP_CONV_T_S1: if (factor < 1 || factor > 8) return ST_INVALID; break;
     default: return ST_INVALID;
   }
   oracle_result* r = new (std::nothrow) oracle_result();

@@ -45,6 +45,10 @@ MUTANTS = {
                      "(int32_t)(k[2] * 4096 + k[5] * 128), (int32_t)g});"),
     "overflow z unchecked": ("if (!in_int32(v.x) || !in_int32(v.y) || !in_int32(v.z)) return false;",
                              "if (!in_int32(v.x) || !in_int32(v.y)) return false;"),
+    "conv_s1 leans the wrong way": ("case OP_CONV_S1: box(-(factor / 2), (factor - 1) / 2, in); break;",
+                                    "case OP_CONV_S1: box(-((factor - 1) / 2), factor / 2, in); break;"),
+    "conv_t_s1 box one short": ("case OP_CONV_T_S1: box(-((factor - 1) / 2), factor / 2, in); break;",
+                                "case OP_CONV_T_S1: box(-((factor - 1) / 2), (factor - 1) / 2, in); break;"),
 }
 
 BATTERY = [
@@ -54,6 +58,8 @@ BATTERY = [
     functools.partial(pins.test_bruteforce_sets_and_order, "dilate", 1),
     functools.partial(pins.test_bruteforce_sets_and_order, "pad_neg", 1),
     functools.partial(pins.test_bruteforce_sets_and_order, "conv_t_k3s2", 2),
+    functools.partial(pins.test_bruteforce_sets_and_order, "conv_s1", 4),
+    functools.partial(pins.test_bruteforce_sets_and_order, "conv_t_s1", 4),
     functools.partial(pins.test_refine_count_and_roundtrip, 2),
     pins.test_golden_canonical_order,
     pins.test_golden_tree_worked_example,

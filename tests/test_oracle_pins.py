@@ -30,7 +30,17 @@ GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 ALL_OPS = [("identity", 1), ("coarsen", 2), ("coarsen", 4), ("coarsen", 8),
            ("refine", 2), ("refine", 4), ("refine", 8), ("dilate", 1),
-           ("pad_neg", 1), ("pad_pos", 1), ("conv_t_k3s2", 2)]
+           ("pad_neg", 1), ("pad_pos", 1), ("conv_t_k3s2", 2)] + \
+          [(op, k) for op in ("conv_s1", "conv_t_s1") for k in (1, 2, 3, 4, 5, 8)]
+
+
+def kernel_box(op, k):
+    """Per-axis offset range of the stride-1 kernel-K target (PR page section 2,
+    test plan K in {2,3,4,5}). The kernel's offsets are O_K = [-(K-1)//2, K//2];
+    the transposed conv scatters every voxel to v + O_K, the conv's outputs are
+    the p with p + O_K meeting the input, i.e. v - O_K."""
+    o_lo, o_hi = -((k - 1) // 2), k // 2
+    return (o_lo, o_hi) if op == "conv_t_s1" else (-o_hi, -o_lo)
 
 
 # ---------------------------------------------------------------- brute force
@@ -54,6 +64,9 @@ def gather_member(op, f, S):
         elif op in box:
             for d in itertools.product((-2, -1, 0, 1, 2), repeat=3):
                 cand.add((x + d[0], y + d[1], z + d[2]))
+        elif op in ("conv_s1", "conv_t_s1"):
+            for d in itertools.product(range(-5, 6), repeat=3):
+                cand.add((x + d[0], y + d[1], z + d[2]))
         elif op == "conv_t_k3s2":
             for d in itertools.product(range(-2, 4), repeat=3):
                 cand.add((2 * x + d[0], 2 * y + d[1], 2 * z + d[2]))
@@ -68,6 +81,10 @@ def gather_member(op, f, S):
             ok = (p[0] // f, p[1] // f, p[2] // f) in S
         elif op in box:
             lo, hi = box[op]
+            ok = any((p[0] - a, p[1] - b, p[2] - c) in S
+                     for a, b, c in itertools.product(range(lo, hi + 1), repeat=3))
+        elif op in ("conv_s1", "conv_t_s1"):
+            lo, hi = kernel_box(op, f)
             ok = any((p[0] - a, p[1] - b, p[2] - c) in S
                      for a, b, c in itertools.product(range(lo, hi + 1), repeat=3))
         elif op == "conv_t_k3s2":
@@ -184,6 +201,59 @@ def test_dilate_equals_pad_pos_of_pad_neg():
     b = oracle.run("pad_pos", 1, a["ijk"], np.concatenate([[0], np.cumsum(a["headers"][:, 8])]))
     for k in oracle.FIELDS:
         assert np.array_equal(d[k], b[k]), k
+
+
+def _same_fields(a, b, what):
+    for k in oracle.FIELDS:
+        assert np.array_equal(a[k], b[k]), (what, k)
+
+
+def _chain(ops, ijk, off):
+    """Run oracle ops one after the other, feeding each the previous enumeration."""
+    r = None
+    for op, f in ops:
+        r = oracle.run(op, f, ijk, off)
+        ijk, off = r["ijk"], np.concatenate([[0], np.cumsum(r["headers"][:, 8])])
+    return r
+
+
+def test_kernel_k_equals_box_pass_sequences():
+    # The stride-1 kernel-K targets are the sequences of box passes the PR page
+    # (section 2) names: K = 1 identity, 2 one pad, 3 dilate, 4 dilate + pad,
+    # 5 two dilates; the conv leans to -1 for even K, its transpose to +1.
+    ijk, off = synth.make_config(3)
+    ijk, off = ijk[: off[6]], off[:7]
+    cases = {
+        ("conv_s1", 1): [("identity", 1)], ("conv_t_s1", 1): [("identity", 1)],
+        ("conv_s1", 2): [("pad_neg", 1)], ("conv_t_s1", 2): [("pad_pos", 1)],
+        ("conv_s1", 3): [("dilate", 1)], ("conv_t_s1", 3): [("dilate", 1)],
+        ("conv_s1", 4): [("dilate", 1), ("pad_neg", 1)], ("conv_t_s1", 4): [("pad_pos", 1), ("dilate", 1)],
+        ("conv_s1", 5): [("dilate", 1), ("dilate", 1)], ("conv_t_s1", 5): [("dilate", 1), ("dilate", 1)],
+    }
+    for (op, k), seq in cases.items():
+        _same_fields(oracle.run(op, k, ijk, off), _chain(seq, ijk, off), (op, k))
+
+
+@pytest.mark.parametrize("k", [2, 4, 5, 8])
+def test_kernel_k_transpose_is_mirrored_conv(k):
+    # S + O_K = -((-S) - O_K): the transposed target is the mirror image of the conv target
+    rng = np.random.default_rng(50 + k)
+    sets = random_sets(rng, 3, 10, CENTRES[:-1])
+    t = _grid_sets(_run_sets("conv_t_s1", k, sets))
+    c = _grid_sets(_run_sets("conv_s1", k, [{(-x, -y, -z) for (x, y, z) in S} for S in sets]))
+    for g in range(len(sets)):
+        assert t[g] == {(-x, -y, -z) for (x, y, z) in c[g]}
+
+
+@pytest.mark.parametrize("op", ["conv_s1", "conv_t_s1"])
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_single_voxel_kernel_k_is_k_cube(op, k):
+    v = (4095, -4096, 0)
+    r = _run_sets(op, k, [{v}])
+    lo = -(k // 2) if op == "conv_s1" else -((k - 1) // 2)  # the cube's low corner offset
+    assert r["headers"][0, 8] == k ** 3
+    assert tuple(r["headers"][0, 10:13]) == (v[0] + lo, v[1] + lo, v[2] + lo)
+    assert tuple(r["headers"][0, 13:16]) == (v[0] + lo + k - 1, v[1] + lo + k - 1, v[2] + lo + k - 1)
 
 
 @pytest.mark.parametrize("v", [(0, 0, 0), (7, 7, 7), (-1, -1, -1), (4095, -4096, 8), (-(1 << 31), 5, (1 << 31) - 2)])
@@ -374,7 +444,8 @@ def test_overflow_and_limits():
     assert r["ijk"].tolist() == [[-(1 << 28), (1 << 28) - 1, 0]]
 
 
-@pytest.mark.parametrize("op,f", [("refine", 3), ("coarsen", 1), ("dilate", 2), ("conv_t_k3s2", 4), ("bogus", 1)])
+@pytest.mark.parametrize("op,f", [("refine", 3), ("coarsen", 1), ("dilate", 2), ("conv_t_k3s2", 4), ("bogus", 1),
+                                  ("conv_s1", 0), ("conv_t_s1", 9)])
 def test_invalid_args(op, f):
     with pytest.raises((oracle.OracleError, KeyError)):
         oracle.run(op, f, np.zeros((1, 3), np.int32), np.array([0, 1]))

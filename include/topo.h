@@ -58,7 +58,15 @@ typedef enum tc_status {
  *   TC_OP_PAD_NEG     factor 1: Minkowski sum with {-1,0}^3
  *   TC_OP_PAD_POS     factor 1: Minkowski sum with {0,1}^3
  *   TC_OP_CONV_T_K3S2 factor 2: refine by 2, then TC_OP_PAD_NEG   (conv_transpose_grid k3s2)
+ *   TC_OP_CONV_S1     factor K in [1,8]: Minkowski sum with [-floor(K/2), floor((K-1)/2)]^3
+ *                     (conv_grid, kernel K, stride 1)
+ *   TC_OP_CONV_T_S1   factor K in [1,8]: Minkowski sum with [-floor((K-1)/2), floor(K/2)]^3
+ *                     (conv_transpose_grid, kernel K, stride 1)
  * Factors 4 and 8 (and k3s2) run chained x2 passes, each with its own readback.
+ * The kernel-K ops run as sequences of TC_OP_DILATE / TC_OP_PAD_* passes (PR page
+ * section 2; K in {2,3,4,5} in its test plan): the kernel's offsets are
+ * [-floor((K-1)/2), floor(K/2)] per axis, the transposed conv scatters to them and
+ * the conv gathers from them; K = 1 returns a copy of the source.
  * Coarsening rounds toward minus infinity. */
 typedef enum tc_op {
   TC_OP_COARSEN = 1,
@@ -66,7 +74,9 @@ typedef enum tc_op {
   TC_OP_DILATE = 3,
   TC_OP_PAD_NEG = 4,
   TC_OP_PAD_POS = 5,
-  TC_OP_CONV_T_K3S2 = 6
+  TC_OP_CONV_T_K3S2 = 6,
+  TC_OP_CONV_S1 = 7,
+  TC_OP_CONV_T_S1 = 8
 } tc_op;
 
 /* Caller-supplied device allocator for output grid buffers (one allocation per

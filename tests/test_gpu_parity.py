@@ -67,6 +67,24 @@ def test_config3_mixed_straddling_empty(op, f):
     _check(op, f, ijk, off, "config3")
 
 
+@pytest.mark.parametrize("op", ["conv_s1", "conv_t_s1"])
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
+def test_kernel_k_stride1(op, k):
+    # PR page section 2 / test plan: conv and transposed conv, K in {2,3,4,5} at
+    # stride 1, as box-pass sequences (K = 1 copies the source)
+    ijk, off = synth.make_config(3)
+    _check(op, k, ijk, off, "config3")
+
+
+@pytest.mark.parametrize("op", ["conv_s1", "conv_t_s1"])
+def test_kernel_k_stride1_config2_k8_and_empty(op):
+    ijk, off = synth.make_config(2)
+    _check(op, 8, ijk, off, "config2")
+    members = [np.zeros((0, 3), np.int32), np.array([[5, -4097, 4095]], np.int32), np.zeros((0, 3), np.int32)]
+    ijk2, off2 = synth.concat_members(members)
+    _check(op, 4, ijk2, off2, "single voxel between empties")
+
+
 CENTRES = [(0, 0, 0), (4096, 0, -4096), (-4096, 4095, 127), (-1, -1, -1), (130, -130, 8), (-8192, 8191, 0)]
 
 

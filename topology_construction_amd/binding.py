@@ -21,7 +21,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libtopo.so")
 
 TC_OK, TC_ERR_INVALID_ARG, TC_ERR_OVERFLOW, TC_ERR_ALLOC, TC_ERR_HIP, TC_ERR_UNSUPPORTED, TC_ERR_INTERNAL = range(7)
-OPS = {"coarsen": 1, "refine": 2, "dilate": 3, "pad_neg": 4, "pad_pos": 5, "conv_t_k3s2": 6}
+OPS = {"coarsen": 1, "refine": 2, "dilate": 3, "pad_neg": 4, "pad_pos": 5, "conv_t_k3s2": 6,
+       "conv_s1": 7, "conv_t_s1": 8}
 
 ABI_SYMBOLS = [
     "tc_abi_version", "tc_status_string", "tc_last_error", "tc_batch_from_ijk",

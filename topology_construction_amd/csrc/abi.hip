@@ -1,6 +1,7 @@
 // C ABI entry points (declared in include/topo.h): argument validation on the
 // host, pass chaining for factors 4/8 and k3s2 transpose, batch ownership and
 // error reporting. No exception crosses the boundary.
+#include <algorithm>
 #include <cstring>
 #include <new>
 #include <string>
@@ -69,6 +70,28 @@ tc_grid_batch* new_batch(int32_t B, const int32_t* rb, const OutAlloc& oa) {
     }
   } catch (...) {
     delete b;
+    throw;
+  }
+  return b;
+}
+
+tc_grid_batch* copy_batch(const tc_grid_batch* src, const OutAlloc& oa) {
+  std::vector<int32_t> rb(4 + 3 * (size_t)src->B);
+  rb[0] = 0;
+  rb[1] = src->n2;
+  rb[2] = src->n1;
+  rb[3] = src->nl;
+  for (int32_t g = 0; g < src->B; ++g) {
+    rb[4 + 3 * g] = src->h_upper[g];
+    rb[4 + 3 * g + 1] = src->h_lower[g];
+    rb[4 + 3 * g + 2] = src->h_leaf[g];
+  }
+  tc_grid_batch* b = new_batch(src->B, rb.data(), oa);
+  try {
+    // identical counts give the identical layout, so one copy moves every array
+    hip_check(hipMemcpyAsync(b->buffer, src->buffer, src->bytes, hipMemcpyDeviceToDevice, oa.stream), "copy batch");
+  } catch (...) {
+    free_batch(b);
     throw;
   }
   return b;
@@ -167,12 +190,28 @@ tc_status tc_build_batched_topology(const tc_grid_batch* src, int32_t op, int32_
       passes.push_back(TC_OP_REFINE);
       passes.push_back(TC_OP_PAD_NEG);
       break;
+    case TC_OP_CONV_S1:
+    case TC_OP_CONV_T_S1: {
+      if (factor < 1 || factor > 8) return fail(TC_ERR_INVALID_ARG, "kernel size must be in [1, 8]");
+      // per-axis box [lo, hi]: each dilate adds one step on both sides, each pad one on its side
+      const int o_lo = -((factor - 1) / 2), o_hi = factor / 2;
+      const int lo = op == TC_OP_CONV_T_S1 ? o_lo : -o_hi, hi = op == TC_OP_CONV_T_S1 ? o_hi : -o_lo;
+      const int both = std::min(-lo, hi);
+      for (int i = 0; i < both; ++i) passes.push_back(TC_OP_DILATE);
+      for (int i = 0; i < -lo - both; ++i) passes.push_back(TC_OP_PAD_NEG);
+      for (int i = 0; i < hi - both; ++i) passes.push_back(TC_OP_PAD_POS);
+      break;
+    }
     default:
       return fail(TC_ERR_INVALID_ARG, "unknown op " + std::to_string(op));
   }
   return guarded([&]() {
     if (current_device() != src->device) throw tc::Error(TC_ERR_INVALID_ARG, "src lives on another device");
     hipStream_t s = (hipStream_t)stream;
+    if (passes.empty()) {  // kernel size 1: the target is the source
+      *out = tc::copy_batch(src, tc::OutAlloc{allocator, s});
+      return TC_OK;
+    }
     const tc_grid_batch* cur = src;
     tc_grid_batch* owned = nullptr;  // intermediate result of the previous pass
     try {

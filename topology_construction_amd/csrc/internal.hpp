@@ -295,6 +295,7 @@ namespace tc {
 // grid) and allocates its buffer; throws on failure (nothing leaked).
 tc_grid_batch* new_batch(int32_t B, const int32_t* readback, const OutAlloc& oa);
 void free_batch(tc_grid_batch* b);
+tc_grid_batch* copy_batch(const tc_grid_batch* src, const OutAlloc& oa);  // same counts, one D2D copy
 
 // The two producers of grid batches.
 tc_grid_batch* build_from_ijk(const int32_t* d_ijk, const int64_t* h_offsets, int32_t B, const OutAlloc& oa);

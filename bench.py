@@ -127,15 +127,38 @@ def copy_calibration(torch, mib):
     torch.cuda.synchronize()
 
 
+def time_from_ijk(binding, torch, np, d_ijk, off, reps):
+    """The ijk front-end on device-resident rows: median wall ms and its rate.
+    Algorithmic bytes: 12 B read per input voxel, 100 B written per output leaf
+    (origin, mask, prefix, offset, parent)."""
+    ms, leaves = [], 0
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        a = time.perf_counter()
+        b = binding.tc_batch_from_ijk(d_ijk, off)
+        torch.cuda.synchronize()
+        ms.append((time.perf_counter() - a) * 1e3)
+        leaves = int(b.leaf_count)
+        del b
+    m = float(np.median(ms))
+    n = int(off[-1])
+    byts = 12 * n + 100 * leaves
+    return {"ms_median": m, "input_voxels": n, "output_leaves": leaves, "input_voxels_per_s": n / (m * 1e-3),
+            "algorithmic_bytes": byts, "achieved_GBs": byts / (m * 1e-3) / 1e9}
+
+
 def measure_large(binding, torch, np, synth):
     """64 shells at res 512 + 8 solid 128^3 cubes: per-op pass / enumeration time
     and per-kernel HIP-event timing against the HBM peak."""
     ijk, off = synth.make_config(5)
-    src = binding.tc_batch_from_ijk(torch.from_numpy(ijk).cuda(), off)
+    d_ijk = torch.from_numpy(ijk).cuda()
     del ijk
+    src = binding.tc_batch_from_ijk(d_ijk, off)
     torch.cuda.synchronize()
     res = {"workload": synth.CONFIG_NAMES[5], "grids": int(len(off) - 1), "input_voxels": int(off[-1]),
-           "input_leaves": int(src.leaf_count), "ops": {}}
+           "input_leaves": int(src.leaf_count), "from_ijk": time_from_ijk(binding, torch, np, d_ijk, off, 3),
+           "ops": {}}
+    del d_ijk
     for op, f in [("coarsen", 2), ("refine", 2), ("dilate", 1)]:
         out = binding.tc_build_batched_topology(src, op, f)  # warm-up
         binding.tc_enumerate_ijk(out)
@@ -190,7 +213,8 @@ def main():
         copy_calibration(torch, args.copy_mib)
         return
     ijk, off = synth.make_config(args.config)
-    src = binding.tc_batch_from_ijk(torch.from_numpy(ijk).cuda(), off)
+    d_ijk = torch.from_numpy(ijk).cuda()
+    src = binding.tc_batch_from_ijk(d_ijk, off)
     torch.cuda.synchronize()
 
     # per-op launch facts for the roofline bytes
@@ -266,7 +290,8 @@ def main():
         "vs_baseline": None, "dtype": "int32", "data": "synthetic",
         "config": {"workload": synth.CONFIG_NAMES[args.config], "grids": int(len(off) - 1),
                    "input_voxels": int(off[-1]), "ops": [f"{o}x{f}" for o, f in STEP_OPS]},
-        "roofline": roofline, "cpu_baseline": cpu, "ops": ops, "large": large,
+        "roofline": roofline, "cpu_baseline": cpu, "ops": ops,
+        "from_ijk": time_from_ijk(binding, torch, np, d_ijk, off, 20), "large": large,
     }
     print(json.dumps(rec), flush=True)
     copy_calibration(torch, args.copy_mib)

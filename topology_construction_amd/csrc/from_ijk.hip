@@ -27,6 +27,35 @@ __global__ void __launch_bounds__(256) k_voxel_grid(const i64* offsets, int32_t 
   vgrid[i] = lo;
 }
 
+// Voxels that arrive together usually share their tile, lower and leaf, so the
+// lanes of a wave first merge the bits they set in the same 64-bit word: one
+// lane per distinct word ORs the union (after a plain read shows bits missing).
+// Same-address device atomics serialize on this part; a wave issues at most a
+// few of them instead of up to 64. Lanes that are still waiting after
+// kDedupRounds distinct words fall back to one atomic each.
+constexpr int kDedupRounds = 8;
+
+__device__ __forceinline__ u64 wave_or_u64(u64 v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v |= __shfl_xor(v, d, kWave);
+  return v;
+}
+
+__device__ __forceinline__ void wave_or_into(u64* word, u64 bits, bool active) {
+  const int lane = threadIdx.x & (kWave - 1);
+  u64 todo = __ballot(active);
+  for (int round = 0; todo && round < kDedupRounds; ++round) {
+    const int leader = __builtin_ctzll(todo);
+    const u64 lw = (u64)__shfl((long long)(uintptr_t)word, leader, kWave);
+    const bool same = ((todo >> lane) & 1ull) && (u64)(uintptr_t)word == lw;
+    const u64 sm = __ballot(same);
+    const u64 all = wave_or_u64(same ? bits : 0);
+    if (lane == leader && (*word & all) != all) atomicOr((unsigned long long*)word, all);
+    todo &= ~sm;
+  }
+  if ((todo >> lane) & 1ull) atomicOr((unsigned long long*)word, bits);
+}
+
 __device__ __forceinline__ u64 tile_hash(int32_t g, int32_t tx, int32_t ty, int32_t tz) {
   u64 k = ((u64)(uint32_t)(tx + kTileBias) << 40) ^ ((u64)(uint32_t)(ty + kTileBias) << 20) ^
           (u64)(uint32_t)(tz + kTileBias);
@@ -41,32 +70,55 @@ __device__ __forceinline__ u64 tile_hash(int32_t g, int32_t tx, int32_t ty, int3
 
 // table[H] holds -1 or the index of the first voxel seen for a (grid, tile).
 // Every probe sequence ends within H steps because fewer than H voxels exist.
-__global__ void __launch_bounds__(256) k_hash_tiles(const int32_t* ijk, const int32_t* vgrid, i64 n, int32_t* table,
-                                                    i64 H, int32_t* rep, int32_t* flags) {
-  const i64 i = (i64)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
-  const int32_t g = vgrid[i];
-  const int32_t tx = ijk[i * 3] >> 12, ty = ijk[i * 3 + 1] >> 12, tz = ijk[i * 3 + 2] >> 12;
+// Returns the representative voxel of voxel i's (grid, tile).
+__device__ int32_t tile_probe(const int32_t* ijk, const int32_t* vgrid, i64 i, int32_t g, int32_t tx, int32_t ty,
+                              int32_t tz, int32_t* table, i64 H, int32_t* flags) {
   i64 h = (i64)(tile_hash(g, tx, ty, tz) & (u64)(H - 1));
   for (i64 probe = 0; probe < H; ++probe) {
     int32_t e = __hip_atomic_load(&table[h], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (e < 0) {
       const int32_t old = atomicCAS(&table[h], -1, (int32_t)i);
-      if (old < 0) {
-        rep[i] = (int32_t)i;
-        return;
-      }
+      if (old < 0) return (int32_t)i;
       e = old;
     }
     if (vgrid[e] == g && (ijk[(i64)e * 3] >> 12) == tx && (ijk[(i64)e * 3 + 1] >> 12) == ty &&
-        (ijk[(i64)e * 3 + 2] >> 12) == tz) {
-      rep[i] = e;
-      return;
-    }
+        (ijk[(i64)e * 3 + 2] >> 12) == tz)
+      return e;
     h = (h + 1) & (H - 1);
   }
-  rep[i] = (int32_t)i;
   atomicOr(flags, 2);
+  return (int32_t)i;
+}
+
+// Lanes of a wave that share a (grid, tile) probe once, through one leader.
+__global__ void __launch_bounds__(256) k_hash_tiles(const int32_t* ijk, const int32_t* vgrid, i64 n, int32_t* table,
+                                                    i64 H, int32_t* rep, int32_t* flags) {
+  const i64 i = (i64)blockIdx.x * 256 + threadIdx.x;
+  const int lane = threadIdx.x & (kWave - 1);
+  const bool in = i < n;
+  int32_t g = 0, tx = 0, ty = 0, tz = 0;
+  if (in) {
+    g = vgrid[i];
+    tx = ijk[i * 3] >> 12;
+    ty = ijk[i * 3 + 1] >> 12;
+    tz = ijk[i * 3 + 2] >> 12;
+  }
+  int32_t mine = -1;
+  u64 todo = __ballot(in);
+  for (int round = 0; todo && round < kDedupRounds; ++round) {
+    const int leader = __builtin_ctzll(todo);
+    const int32_t lg = __shfl(g, leader, kWave), lx = __shfl(tx, leader, kWave), ly = __shfl(ty, leader, kWave),
+                  lz = __shfl(tz, leader, kWave);
+    const bool same = ((todo >> lane) & 1ull) && g == lg && tx == lx && ty == ly && tz == lz;
+    const u64 sm = __ballot(same);
+    int32_t r = -1;
+    if (lane == leader) r = tile_probe(ijk, vgrid, i, g, tx, ty, tz, table, H, flags);
+    r = __shfl(r, leader, kWave);
+    if (same) mine = r;
+    todo &= ~sm;
+  }
+  if ((todo >> lane) & 1ull) mine = tile_probe(ijk, vgrid, i, g, tx, ty, tz, table, H, flags);
+  if (in) rep[i] = mine;
 }
 
 __global__ void __launch_bounds__(256) k_rep_flags(const int32_t* rep, i64 n, int32_t* flag) {
@@ -114,57 +166,82 @@ __global__ void __launch_bounds__(256) k_voxel_tile(const int32_t* rep, const in
   vtile[i] = t;
 }
 
-__device__ __forceinline__ void or_if_clear(u64* word, u64 bit) {
-  if (!(__hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & bit))
-    atomicOr((unsigned long long*)word, bit);
-}
-
 __global__ void __launch_bounds__(256) k_voxel_mark_lower(const int32_t* ijk, const int32_t* vtile, i64 n,
                                                           u64* tile_child) {
   const i64 i = (i64)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
-  const i64 t = vtile[i];
-  const int kx = (ijk[i * 3] >> 7) & 31, ky = (ijk[i * 3 + 1] >> 7) & 31, kz = (ijk[i * 3 + 2] >> 7) & 31;
-  const int bit = (kx * 32 + ky) * 32 + kz;
-  or_if_clear(&tile_child[t * 512 + (bit >> 6)], 1ull << (bit & 63));
+  const bool in = i < n;
+  u64* word = tile_child;
+  u64 b = 0;
+  if (in) {
+    const i64 t = vtile[i];
+    const int kx = (ijk[i * 3] >> 7) & 31, ky = (ijk[i * 3 + 1] >> 7) & 31, kz = (ijk[i * 3 + 2] >> 7) & 31;
+    const int bit = (kx * 32 + ky) * 32 + kz;
+    word = &tile_child[t * 512 + (bit >> 6)];
+    b = 1ull << (bit & 63);
+  }
+  wave_or_into(word, b, in);
 }
 
+// All lanes stay active to the end of these kernels (no early return), so the
+// wave-wide merges see every lane.
 __global__ void __launch_bounds__(256) k_voxel_cand(const int32_t* ijk, const int32_t* vtile, i64 n,
                                                     const u64* tile_child, const uint16_t* tile_prefix,
                                                     const int32_t* tile_lower_base, int32_t nc, int32_t* vcand,
                                                     int4* cand_origin, u64* cand_child, int32_t* flags) {
   const i64 i = (i64)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
-  const i64 t = vtile[i];
-  const int32_t x = ijk[i * 3], y = ijk[i * 3 + 1], z = ijk[i * 3 + 2];
-  const int bit = (((x >> 7) & 31) * 32 + ((y >> 7) & 31)) * 32 + ((z >> 7) & 31);
-  const int w = bit >> 6, b = bit & 63;
-  const int32_t c = tile_lower_base[t] + tile_prefix[t * 512 + w] + popc64(tile_child[t * 512 + w] & ((1ull << b) - 1));
-  if (c < 0 || c >= nc) {
-    atomicOr(flags, 2);
-    vcand[i] = -1;
-    return;
+  const int lane = threadIdx.x & (kWave - 1);
+  bool ok = i < n;
+  int32_t c = -1, x = 0, y = 0, z = 0;
+  i64 t = 0;
+  if (ok) {
+    t = vtile[i];
+    x = ijk[i * 3];
+    y = ijk[i * 3 + 1];
+    z = ijk[i * 3 + 2];
+    const int bit = (((x >> 7) & 31) * 32 + ((y >> 7) & 31)) * 32 + ((z >> 7) & 31);
+    const int w = bit >> 6, b = bit & 63;
+    c = tile_lower_base[t] + tile_prefix[t * 512 + w] + popc64(tile_child[t * 512 + w] & ((1ull << b) - 1));
+    if (c < 0 || c >= nc) {
+      atomicOr(flags, 2);
+      c = -1;
+      ok = false;
+    }
+    vcand[i] = c;
   }
-  vcand[i] = c;
-  cand_origin[c] = make_int4((x >> 7) * 128, (y >> 7) * 128, (z >> 7) * 128, (int32_t)t);
+  // one lane per run of equal candidates writes the candidate's origin
+  const int32_t cprev = __shfl_up(c, 1, kWave);
+  if (ok && (lane == 0 || cprev != c))
+    cand_origin[c] = make_int4((x >> 7) * 128, (y >> 7) * 128, (z >> 7) * 128, (int32_t)t);
   const int lb = (((x >> 3) & 15) * 16 + ((y >> 3) & 15)) * 16 + ((z >> 3) & 15);
-  or_if_clear(&cand_child[(i64)c * 64 + (lb >> 6)], 1ull << (lb & 63));
+  wave_or_into(ok ? &cand_child[(i64)c * 64 + (lb >> 6)] : cand_child, ok ? 1ull << (lb & 63) : 0, ok);
 }
 
 __global__ void __launch_bounds__(256) k_voxel_leaf(const int32_t* ijk, const int32_t* vcand, i64 n,
                                                     const u64* cand_child, const uint16_t* cand_prefix,
                                                     const i64* cand_scan, i64 n_leaf, u64* leaf_mask) {
   const i64 i = (i64)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
-  const i64 c = vcand[i];
-  if (c < 0) return;
-  const int32_t x = ijk[i * 3], y = ijk[i * 3 + 1], z = ijk[i * 3 + 2];
-  const int lb = (((x >> 3) & 15) * 16 + ((y >> 3) & 15)) * 16 + ((z >> 3) & 15);
-  const int w = lb >> 6, b = lb & 63;
-  const i64 leaf = (i64)(cand_scan[c] & 0xffffffffll) + cand_prefix[c * 64 + w] +
-                   popc64(cand_child[c * 64 + w] & ((1ull << b) - 1));
-  if (leaf < 0 || leaf >= n_leaf) return;  // consistency guard
-  atomicOr((unsigned long long*)&leaf_mask[leaf * 8 + (x & 7)], 1ull << ((y & 7) * 8 + (z & 7)));
+  bool ok = i < n;
+  u64* word = leaf_mask;
+  u64 bits = 0;
+  if (ok) {
+    const i64 c = vcand[i];
+    if (c < 0) {
+      ok = false;
+    } else {
+      const int32_t x = ijk[i * 3], y = ijk[i * 3 + 1], z = ijk[i * 3 + 2];
+      const int lb = (((x >> 3) & 15) * 16 + ((y >> 3) & 15)) * 16 + ((z >> 3) & 15);
+      const int w = lb >> 6, b = lb & 63;
+      const i64 leaf = (i64)(cand_scan[c] & 0xffffffffll) + cand_prefix[c * 64 + w] +
+                       popc64(cand_child[c * 64 + w] & ((1ull << b) - 1));
+      if (leaf < 0 || leaf >= n_leaf) {  // consistency guard
+        ok = false;
+      } else {
+        word = &leaf_mask[leaf * 8 + (x & 7)];
+        bits = 1ull << ((y & 7) * 8 + (z & 7));
+      }
+    }
+  }
+  wave_or_into(word, bits, ok);
 }
 
 static int32_t read_i32(const int32_t* d, hipStream_t s) {

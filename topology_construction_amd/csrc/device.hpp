@@ -43,6 +43,17 @@ __device__ __forceinline__ T block_excl_scan(T v, T* s_wave, T& total) {
 
 __device__ __forceinline__ int popc64(uint64_t x) { return __popcll(x); }
 
+// Sum of v over a 256-thread block, written to *dst by thread 0. Every thread of
+// the block must call it (it holds a block barrier).
+__device__ __forceinline__ void block_sum_to(int64_t v, int64_t* dst) {
+  __shared__ int64_t s_part[4];
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
+  if ((threadIdx.x & (kWave - 1)) == 0) s_part[threadIdx.x / kWave] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) *dst = s_part[0] + s_part[1] + s_part[2] + s_part[3];
+}
+
 // Index of the r-th set bit (0-based) of w; w must have more than r set bits.
 __device__ __forceinline__ int select_bit(uint64_t w, int r) {
   int pos = 0;

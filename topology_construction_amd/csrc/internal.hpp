@@ -198,7 +198,6 @@ void fill_i32(int32_t* p, int32_t v, i64 n_host, const int32_t* d_n, int32_t mul
 void fill_u64(u64* p, u64 v, i64 n_host, const int32_t* d_n, int32_t mult, hipStream_t s);
 void fill_pair(int32_t* a, int32_t va, i64 na_host, int32_t mult_a, u64* b, u64 vb, i64 nb_host, int32_t mult_b,
                const int32_t* d_n, hipStream_t s);
-void fill_split_i32(int32_t* p, int32_t v0, i64 n0, int32_t v1, i64 n1, hipStream_t s);
 
 // Sorts (key_hi, key_lo) 128-bit keys with uint32 values ascending. `key_bits`
 // bounds the significant low bits of every key (keys above them compare by
@@ -253,10 +252,13 @@ void tree_rank_tiles(TreeScratch& t, hipStream_t s);            // prefix per ti
 void tree_count_cands(TreeScratch& t, hipStream_t s);           // leaf counts per cand + their scan
 void tree_counts(TreeScratch& t, int32_t B, hipStream_t s);     // tree_count_cands + tree_grid_counts (fused when small)
 void tree_write_nodes(TreeScratch& t, const GridView& out, int32_t* leaf_cand, hipStream_t s);
-void tree_leaf_stats(const GridView& out, i64* leaf_vox, uint32_t* leaf_box, hipStream_t s);
+void tree_leaf_stats(const GridView& out, i64* leaf_vox, uint32_t* leaf_box, i64* vox_part, hipStream_t s);
 int32_t bbox_replicas(int32_t B);  // replicas of the per-grid bbox accumulators
-void tree_finalize_leaves(const GridView& out, const i64* leaf_vox, const uint32_t* leaf_box, i64* vox_excl, void* scan_tmp,
-                          int32_t* bbox_accum, const int32_t* grid_info, hipStream_t s);
+// Leaf voxel offsets, per-grid bboxes and headers. vox_part holds one voxel sum
+// per run of `gran` leaves (gran divides 256), written by the leaf producer.
+void tree_finalize_leaves(const GridView& out, const i64* leaf_vox, const uint32_t* leaf_box, i64* vox_part,
+                          i64 gran, i64* vox_excl, i64* gvb, int32_t* bbox_accum, const int32_t* grid_info,
+                          hipStream_t s);
 void tree_enumerate(const GridView& v, int32_t* ijk, hipStream_t s);
 
 // Allocation of the single output buffer of a batch.

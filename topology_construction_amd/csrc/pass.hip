@@ -1127,7 +1127,8 @@ __global__ void __launch_bounds__(256) k_leaf_gather(const int4* out_origin, con
                                                      const int32_t* src_lower_first, const u64* src_leaf_mask,
                                                      int32_t n_src_lower, int32_t n_src_leaf,
                                                      const int32_t* d_num_cands, u64* out_mask, u64* out_prefix,
-                                                     i64* leaf_vox, uint32_t* leaf_box, int32_t* flags) {
+                                                     i64* leaf_vox, uint32_t* leaf_box, i64* vox_part,
+                                                     int32_t* flags) {
   constexpr int lpl = KIND == 0 ? 1 : 4;  // lanes per output leaf
   const i64 gt = (i64)blockIdx.x * 256 + threadIdx.x;
   const i64 i = gt / lpl;
@@ -1234,21 +1235,21 @@ __global__ void __launch_bounds__(256) k_leaf_gather(const int4* out_origin, con
       out[k] |= __shfl_xor(out[k], 2, kWave);
     }
   }
-  if (i >= n || sub != 0) return;
-  if (!valid) {
-    leaf_vox[i] = 0;
-    leaf_box[i] = kEmptyBox;
-    return;
-  }
+  const bool writer = i < n && sub == 0;
+  u64 prefix = 0;
+  int count = 0;
+  uint32_t box = kEmptyBox;
+  if (writer && valid) {
 #pragma unroll
-  for (int k = 0; k < 8; ++k) out_mask[i * 8 + k] = out[k];
-  u64 prefix;
-  int count;
-  uint32_t box;
-  leaf_stats(out, prefix, count, box);
-  out_prefix[i] = prefix;
-  leaf_vox[i] = count;
-  leaf_box[i] = box;
+    for (int k = 0; k < 8; ++k) out_mask[i * 8 + k] = out[k];
+    leaf_stats(out, prefix, count, box);
+    out_prefix[i] = prefix;
+  }
+  if (writer) {
+    leaf_vox[i] = count;
+    leaf_box[i] = box;
+  }
+  block_sum_to(count, &vox_part[blockIdx.x]);  // voxels of this block's leaves
 }
 
 // ------------------------------------------------------------------ writers: box ops, separable
@@ -1267,7 +1268,8 @@ __global__ void __launch_bounds__(256) k_leaf_gather_box(const int4* out_origin,
                                                          const int32_t* src_lower_first, const u64* src_leaf_mask,
                                                          int32_t n_src_lower, int32_t n_src_leaf,
                                                          const int32_t* d_num_cands, u64* out_mask, u64* out_prefix,
-                                                         i64* leaf_vox, uint32_t* leaf_box, int32_t* flags) {
+                                                         i64* leaf_vox, uint32_t* leaf_box, i64* vox_part,
+                                                         int32_t* flags) {
   const i64 gt = (i64)blockIdx.x * 256 + threadIdx.x;
   const i64 i = gt >> 2;
   const int sub = (int)(gt & 3);
@@ -1367,23 +1369,21 @@ __global__ void __launch_bounds__(256) k_leaf_gather_box(const int4* out_origin,
     full[2 * k] = __shfl(outw[0], grp | k, kWave);
     full[2 * k + 1] = __shfl(outw[1], grp | k, kWave);
   }
-  if (i >= n) return;
-  if (!valid) {
+  u64 prefix = 0;
+  int count = 0;
+  uint32_t box = kEmptyBox;
+  if (i < n && valid) {
+    reinterpret_cast<ulonglong2*>(out_mask)[i * 4 + sub] = make_ulonglong2(outw[0], outw[1]);
     if (sub == 0) {
-      leaf_vox[i] = 0;
-      leaf_box[i] = kEmptyBox;
+      leaf_stats(full, prefix, count, box);
+      out_prefix[i] = prefix;
     }
-    return;
   }
-  reinterpret_cast<ulonglong2*>(out_mask)[i * 4 + sub] = make_ulonglong2(outw[0], outw[1]);
-  if (sub != 0) return;
-  u64 prefix;
-  int count;
-  uint32_t box;
-  leaf_stats(full, prefix, count, box);
-  out_prefix[i] = prefix;
-  leaf_vox[i] = count;
-  leaf_box[i] = box;
+  if (i < n && sub == 0) {
+    leaf_vox[i] = count;
+    leaf_box[i] = box;
+  }
+  block_sum_to(count, &vox_part[blockIdx.x]);  // voxels of this block's leaves
 }
 
 // ------------------------------------------------------------------ driver
@@ -1538,9 +1538,13 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa) 
     const size_t o_box = post.reserve(4 * L);
     const size_t o_vx = post.reserve(8 * (L + 1));
     const size_t o_bb = post.reserve(4 * 6 * (i64)B * bbox_replicas(B));
-    const size_t o_stmp2 = post.reserve(scan_tmp_bytes(L, 8));
+    // voxel sums per gather workgroup: 256 output leaves (refine) or 64 (4 lanes per leaf)
+    const i64 gran = op == TC_OP_REFINE ? 256 : 64;
+    const size_t o_part = post.reserve(8 * (ceil_div(L, gran) + 1));
+    const size_t o_gvb = post.reserve(8 * ((i64)B + 1));
     post.commit();
     int32_t* leaf_cand = post.at<int32_t>(o_lc);
+    i64* vox_part = post.at<i64>(o_part);
     tree_write_nodes(ts, ov, leaf_cand, s);
     if (L > 0 && sv.n_leaf == 0) throw Error(TC_ERR_INTERNAL, "pass: output leaves without source leaves");
     if (op == TC_OP_REFINE || op == TC_OP_COARSEN) {
@@ -1550,16 +1554,16 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa) 
              (const int32_t*)leaf_cand, L, op, oi.m, oi.lo, oi.hi, (const int32_t*)cand_src,
              (const u64*)sv.lower_mask, (const uint16_t*)sv.lower_prefix, (const int32_t*)sv.lower_first,
              (const u64*)sv.leaf_mask, sv.n_lower, sv.n_leaf, (const int32_t*)ts.d_num_cands, ov.leaf_mask,
-             ov.leaf_prefix, post.at<i64>(o_lv), post.at<uint32_t>(o_box), ts.flags);
+             ov.leaf_prefix, post.at<i64>(o_lv), post.at<uint32_t>(o_box), vox_part, ts.flags);
     } else {
       launch("k_leaf_gather", k_leaf_gather_box, ceil_div(L * 4, 256), 256, s, (const int4*)ov.leaf_origin,
              (const int32_t*)leaf_cand, L, oi.lo, oi.hi, (const int32_t*)cand_src, (const u64*)sv.lower_mask,
              (const uint16_t*)sv.lower_prefix, (const int32_t*)sv.lower_first, (const u64*)sv.leaf_mask,
              sv.n_lower, sv.n_leaf, (const int32_t*)ts.d_num_cands, ov.leaf_mask, ov.leaf_prefix,
-             post.at<i64>(o_lv), post.at<uint32_t>(o_box), ts.flags);
+             post.at<i64>(o_lv), post.at<uint32_t>(o_box), vox_part, ts.flags);
     }
-    tree_finalize_leaves(ov, post.at<i64>(o_lv), post.at<uint32_t>(o_box), post.at<i64>(o_vx), post.at<char>(o_stmp2),
-                         post.at<int32_t>(o_bb), (const int32_t*)ts.grid_info, s);
+    tree_finalize_leaves(ov, post.at<i64>(o_lv), post.at<uint32_t>(o_box), vox_part, gran, post.at<i64>(o_vx),
+                         post.at<i64>(o_gvb), post.at<int32_t>(o_bb), (const int32_t*)ts.grid_info, s);
   } catch (...) {
     free_batch(out);
     throw;

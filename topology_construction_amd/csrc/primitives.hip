@@ -227,15 +227,6 @@ void fill_pair(int32_t* a, int32_t va, i64 na_host, int32_t mult_a, u64* b, u64 
          mult_a, b, vb, nb_host, mult_b, d_n);
 }
 
-// p[0 .. n0) = v0 and p[n0 .. n0 + n1) = v1 in one launch.
-__global__ void __launch_bounds__(256) k_fill_split(int32_t* p, int32_t v0, i64 n0, int32_t v1, i64 n1) {
-  for (i64 i = (i64)blockIdx.x * 256 + threadIdx.x; i < n0 + n1; i += (i64)gridDim.x * 256) p[i] = i < n0 ? v0 : v1;
-}
-
-void fill_split_i32(int32_t* p, int32_t v0, i64 n0, int32_t v1, i64 n1, hipStream_t s) {
-  launch("k_fill_split", k_fill_split, fill_blocks(n0 + n1), 256, s, p, v0, n0, v1, n1);
-}
-
 void fill_i32(int32_t* p, int32_t v, i64 n_host, const int32_t* d_n, int32_t mult, hipStream_t s) {
   launch("k_fill_i32", k_fill<int32_t>, fill_blocks(n_host), 256, s, p, v, n_host, d_n, mult);
 }

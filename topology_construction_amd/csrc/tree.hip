@@ -384,33 +384,34 @@ void tree_write_nodes(TreeScratch& ts, const GridView& out, int32_t* leaf_cand, 
 // Per leaf (masks written by the ijk front-end): prefix word, voxel count and
 // packed local bbox. The topology pass computes the same values in its gather.
 __global__ void __launch_bounds__(256) k_leaf_stats(const u64* leaf_mask, u64* leaf_prefix, i64* leaf_vox,
-                                                    uint32_t* leaf_box, i64 n_leaf) {
+                                                    uint32_t* leaf_box, i64* vox_part, i64 n_leaf) {
   const i64 i = (i64)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n_leaf) return;
-  u64 W[8];
+  int count = 0;
+  if (i < n_leaf) {
+    u64 W[8];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) W[k] = leaf_mask[i * 8 + k];
-  u64 prefix;
-  int count;
-  uint32_t box;
-  leaf_stats(W, prefix, count, box);
-  leaf_prefix[i] = prefix;
-  leaf_vox[i] = count;
-  leaf_box[i] = box;
+    for (int k = 0; k < 8; ++k) W[k] = leaf_mask[i * 8 + k];
+    u64 prefix;
+    uint32_t box;
+    leaf_stats(W, prefix, count, box);
+    leaf_prefix[i] = prefix;
+    leaf_vox[i] = count;
+    leaf_box[i] = box;
+  }
+  block_sum_to(count, &vox_part[blockIdx.x]);
 }
 
-void tree_leaf_stats(const GridView& out, i64* leaf_vox, uint32_t* leaf_box, hipStream_t s) {
+void tree_leaf_stats(const GridView& out, i64* leaf_vox, uint32_t* leaf_box, i64* vox_part, hipStream_t s) {
   launch("k_leaf_stats", k_leaf_stats, ceil_div((i64)out.n_leaf, 256), 256, s, (const u64*)out.leaf_mask,
-         out.leaf_prefix, leaf_vox, leaf_box, (i64)out.n_leaf);
+         out.leaf_prefix, leaf_vox, leaf_box, vox_part, (i64)out.n_leaf);
 }
 
-// Leaf voxel offsets (0-based inside the grid) and per-grid bboxes, one leaf per
-// thread. Bounds are reduced over the wave (leaves are sorted by grid, so a wave
-// nearly always holds one grid) and then folded with device-scope atomics into
-// one of R replicas of the per-grid accumulators, chosen by block. On this
-// multi-XCD part such atomics resolve past the per-XCD L2 and serialize per
-// address, so spreading them over replicas keeps each address cold;
-// k_write_headers folds the replicas.
+// Per-grid bboxes of large batches: leaf bounds are reduced over the wave (leaves
+// are sorted by grid, so a wave nearly always holds one grid) and then folded
+// with device-scope atomics into one of R replicas of the per-grid accumulators,
+// chosen by block. On this multi-XCD part such atomics resolve past the per-XCD
+// L2 and serialize per address, so spreading them over replicas keeps each
+// address cold; the header writer folds the replicas.
 __device__ __forceinline__ void box_flush(int32_t* bbox, int32_t B, int32_t R, int rep, int g, const int v[6]) {
   if (g < 0 || g >= B) return;
 #pragma unroll
@@ -418,91 +419,6 @@ __device__ __forceinline__ void box_flush(int32_t* bbox, int32_t B, int32_t R, i
     atomicMin(&bbox[((i64)a * R + rep) * B + g], v[a]);
     atomicMax(&bbox[((i64)(3 + a) * R + rep) * B + g], v[3 + a]);
   }
-}
-
-__global__ void __launch_bounds__(256) k_leaf_offsets_bbox(const int4* leaf_origin, const uint32_t* leaf_box,
-                                                           const i64* vox_excl, const int32_t* grid_info,
-                                                           i64* leaf_offset, int32_t* bbox, int32_t B, int32_t R,
-                                                           i64 n_leaf) {
-  const i64 i = (i64)blockIdx.x * 256 + threadIdx.x;
-  const int lane = threadIdx.x & (kWave - 1);
-  int g = -1;
-  int v[6] = {INT32_MAX, INT32_MAX, INT32_MAX, INT32_MIN, INT32_MIN, INT32_MIN};
-  if (i < n_leaf) {
-    const int4 o = leaf_origin[i];
-    const uint32_t bx = leaf_box[i];
-    if (o.w >= 0 && o.w < B) {
-      leaf_offset[i] = vox_excl[i] - vox_excl[grid_info[o.w * 6 + 5]];
-      if (bx != kEmptyBox) {
-        g = o.w;
-        v[0] = o.x + (int)(bx & 7);
-        v[3] = o.x + (int)((bx >> 3) & 7);
-        v[1] = o.y + (int)((bx >> 6) & 7);
-        v[4] = o.y + (int)((bx >> 9) & 7);
-        v[2] = o.z + (int)((bx >> 12) & 7);
-        v[5] = o.z + (int)((bx >> 15) & 7);
-      }
-    }
-  }
-  const bool active = g >= 0;
-  const u64 act = __ballot(active);
-  if (!act) return;  // uniform per wave
-  const int rep = (int)(blockIdx.x % (unsigned)R);
-  const int first = __builtin_ctzll(act);
-  const int g0 = __shfl(g, first, kWave);
-  if (__ballot(active && g != g0) == 0) {
-    int r[6];
-#pragma unroll
-    for (int a = 0; a < 3; ++a) {
-      r[a] = wave_min_i32(v[a]);
-      r[3 + a] = wave_max_i32(v[3 + a]);
-    }
-    if (lane == first) box_flush(bbox, B, R, rep, g0, r);
-  } else if (active) {
-    box_flush(bbox, B, R, rep, g, v);
-  }
-}
-
-// One wave per grid: lanes fold the bbox replicas, lane 0 writes the header.
-__global__ void __launch_bounds__(256) k_write_headers(const int32_t* grid_info, const i64* vox_excl,
-                                                       const int32_t* bbox, int32_t B, int32_t R,
-                                                       tc_grid_header* hdr) {
-  const i64 g = (i64)blockIdx.x * 4 + threadIdx.x / kWave;
-  const int lane = threadIdx.x & (kWave - 1);
-  if (g >= B) return;  // uniform per wave
-  int v[6] = {INT32_MAX, INT32_MAX, INT32_MAX, INT32_MIN, INT32_MIN, INT32_MIN};
-  for (int r = lane; r < R; r += kWave) {
-#pragma unroll
-    for (int a = 0; a < 3; ++a) {
-      v[a] = min(v[a], bbox[((i64)a * R + r) * B + g]);
-      v[3 + a] = max(v[3 + a], bbox[((i64)(3 + a) * R + r) * B + g]);
-    }
-  }
-#pragma unroll
-  for (int a = 0; a < 3; ++a) {
-    v[a] = wave_min_i32(v[a]);
-    v[3 + a] = wave_max_i32(v[3 + a]);
-  }
-  if (lane != 0) return;
-  const int32_t* gi = grid_info + g * 6;
-  tc_grid_header h;
-  h.grid_index = (int32_t)g;
-  h.grid_count = B;
-  h.upper_count = gi[0];
-  h.lower_count = gi[1];
-  h.leaf_count = gi[2];
-  h.upper_begin = gi[3];
-  h.lower_begin = gi[4];
-  h.leaf_begin = gi[5];
-  h.voxel_begin = vox_excl[gi[5]];
-  h.voxel_count = vox_excl[gi[5] + gi[2]] - h.voxel_begin;
-  for (int a = 0; a < 3; ++a) {
-    h.bbox_min[a] = v[a];
-    h.bbox_max[a] = v[3 + a];
-  }
-  h.reserved[0] = 0;
-  h.reserved[1] = 0;
-  hdr[g] = h;
 }
 
 int32_t bbox_replicas(int32_t B) {
@@ -661,8 +577,153 @@ __global__ void __launch_bounds__(kFinThreads) k_finalize_small(const int4* leaf
   }
 }
 
-void tree_finalize_leaves(const GridView& out, const i64* leaf_vox, const uint32_t* leaf_box, i64* vox_excl, void* scan_tmp,
-                          int32_t* bbox_accum, const int32_t* grid_info, hipStream_t s) {
+// Large batches: the leaf producer left one voxel sum per run of `gran` leaves
+// (vox_part). One workgroup scans those sums, sets up the bbox accumulators and
+// derives every grid's voxel begin (its first leaf's run offset plus the leaves
+// before it in that run; gvb[B] = total); then every leaf's offset comes from its
+// block's run offset plus a block scan, with no pass over all leaves just to scan.
+constexpr int kPartThreads = 1024;
+constexpr int kPartItems = 16;
+
+__global__ void __launch_bounds__(kPartThreads) k_vox_partials(i64* vox_part, i64 np, const i64* leaf_vox, i64 gran,
+                                                               const int32_t* grid_info, int32_t B, i64 L,
+                                                               int32_t* bbox, int32_t R, i64* gvb) {
+  __shared__ i64 s_wave[kPartThreads / kWave];
+  i64 carry = 0;
+  for (i64 c = 0; c < np; c += (i64)kPartThreads * kPartItems) {
+    i64 v[kPartItems];
+    i64 sum = 0;
+    const i64 base = c + (i64)threadIdx.x * kPartItems;
+#pragma unroll
+    for (int k = 0; k < kPartItems; ++k) {
+      v[k] = base + k < np ? vox_part[base + k] : 0;
+      sum += v[k];
+    }
+    i64 total;
+    i64 ex = block_excl_scan<i64, kPartThreads>(sum, s_wave, total) + carry;
+#pragma unroll
+    for (int k = 0; k < kPartItems; ++k) {
+      if (base + k < np) vox_part[base + k] = ex;
+      ex += v[k];
+    }
+    carry += total;
+  }
+  for (i64 k = threadIdx.x; k < 3 * (i64)R * B; k += kPartThreads) {
+    bbox[k] = INT32_MAX;
+    bbox[3 * (i64)R * B + k] = INT32_MIN;
+  }
+  __threadfence();
+  __syncthreads();  // the scanned runs are read below
+  // one wave per grid: its first leaf's run offset plus the leaves before it in the run
+  const int lane = threadIdx.x & (kWave - 1);
+  for (int32_t g = threadIdx.x / kWave; g <= B; g += kPartThreads / kWave) {
+    const i64 f = g < B ? grid_info[g * 6 + 5] : L;
+    if (f >= L) {  // uniform per wave
+      if (lane == 0) gvb[g] = carry;
+      continue;
+    }
+    const i64 run = f / gran;
+    i64 sum = 0;
+    for (i64 j = run * gran + lane; j < f; j += kWave) sum += leaf_vox[j];
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) sum += __shfl_xor(sum, d, kWave);
+    if (lane == 0) gvb[g] = vox_part[run] + sum;
+  }
+}
+
+// Per leaf: offset inside its grid and the per-grid bbox (as k_leaf_offsets_bbox).
+__global__ void __launch_bounds__(256) k_leaf_offsets_runs(const int4* leaf_origin, const i64* leaf_vox,
+                                                           const uint32_t* leaf_box, const i64* vox_part, i64 gran,
+                                                           const i64* gvb, i64* leaf_offset, int32_t* bbox,
+                                                           int32_t B, int32_t R, i64 n_leaf) {
+  __shared__ i64 s_wave[256 / kWave];
+  const i64 i = (i64)blockIdx.x * 256 + threadIdx.x;
+  const int lane = threadIdx.x & (kWave - 1);
+  const i64 v = i < n_leaf ? leaf_vox[i] : 0;
+  i64 total;
+  const i64 ex = block_excl_scan<i64, 256>(v, s_wave, total) + vox_part[((i64)blockIdx.x * 256) / gran];
+  int g = -1;
+  int bv[6] = {INT32_MAX, INT32_MAX, INT32_MAX, INT32_MIN, INT32_MIN, INT32_MIN};
+  if (i < n_leaf) {
+    const int4 o = leaf_origin[i];
+    const uint32_t bx = leaf_box[i];
+    if (o.w >= 0 && o.w < B) {
+      leaf_offset[i] = ex - gvb[o.w];
+      if (bx != kEmptyBox) {
+        g = o.w;
+        bv[0] = o.x + (int)(bx & 7);
+        bv[3] = o.x + (int)((bx >> 3) & 7);
+        bv[1] = o.y + (int)((bx >> 6) & 7);
+        bv[4] = o.y + (int)((bx >> 9) & 7);
+        bv[2] = o.z + (int)((bx >> 12) & 7);
+        bv[5] = o.z + (int)((bx >> 15) & 7);
+      }
+    }
+  }
+  const bool active = g >= 0;
+  const u64 act = __ballot(active);
+  if (!act) return;  // uniform per wave; no barrier follows
+  const int rep = (int)(blockIdx.x % (unsigned)R);
+  const int first = __builtin_ctzll(act);
+  const int g0 = __shfl(g, first, kWave);
+  if (__ballot(active && g != g0) == 0) {
+    int r[6];
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+      r[a] = wave_min_i32(bv[a]);
+      r[3 + a] = wave_max_i32(bv[3 + a]);
+    }
+    if (lane == first) box_flush(bbox, B, R, rep, g0, r);
+  } else if (active) {
+    box_flush(bbox, B, R, rep, g, bv);
+  }
+}
+
+// One wave per grid: lanes fold the bbox replicas, lane 0 writes the header.
+__global__ void __launch_bounds__(256) k_write_headers_gvb(const int32_t* grid_info, const i64* gvb,
+                                                           const int32_t* bbox, int32_t B, int32_t R,
+                                                           tc_grid_header* hdr) {
+  const i64 g = (i64)blockIdx.x * 4 + threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  if (g >= B) return;  // uniform per wave
+  int v[6] = {INT32_MAX, INT32_MAX, INT32_MAX, INT32_MIN, INT32_MIN, INT32_MIN};
+  for (int r = lane; r < R; r += kWave) {
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+      v[a] = min(v[a], bbox[((i64)a * R + r) * B + g]);
+      v[3 + a] = max(v[3 + a], bbox[((i64)(3 + a) * R + r) * B + g]);
+    }
+  }
+#pragma unroll
+  for (int a = 0; a < 3; ++a) {
+    v[a] = wave_min_i32(v[a]);
+    v[3 + a] = wave_max_i32(v[3 + a]);
+  }
+  if (lane != 0) return;
+  const int32_t* gi = grid_info + g * 6;
+  tc_grid_header h;
+  h.grid_index = (int32_t)g;
+  h.grid_count = B;
+  h.upper_count = gi[0];
+  h.lower_count = gi[1];
+  h.leaf_count = gi[2];
+  h.upper_begin = gi[3];
+  h.lower_begin = gi[4];
+  h.leaf_begin = gi[5];
+  h.voxel_begin = gvb[g];
+  h.voxel_count = gvb[g + 1] - gvb[g];
+  for (int a = 0; a < 3; ++a) {
+    h.bbox_min[a] = v[a];
+    h.bbox_max[a] = v[3 + a];
+  }
+  h.reserved[0] = 0;
+  h.reserved[1] = 0;
+  hdr[g] = h;
+}
+
+void tree_finalize_leaves(const GridView& out, const i64* leaf_vox, const uint32_t* leaf_box, i64* vox_part,
+                          i64 gran, i64* vox_excl, i64* gvb, int32_t* bbox_accum, const int32_t* grid_info,
+                          hipStream_t s) {
   const i64 L = out.n_leaf;
   const int32_t B = out.B;
   if (L <= kFinSmallLeaves && B <= kFinSmallGrids) {
@@ -671,11 +732,11 @@ void tree_finalize_leaves(const GridView& out, const i64* leaf_vox, const uint32
     return;
   }
   const int32_t R = bbox_replicas(B);
-  fill_split_i32(bbox_accum, INT32_MAX, 3 * (i64)R * B, INT32_MIN, 3 * (i64)R * B, s);
-  scan_excl_i64(leaf_vox, vox_excl, L, nullptr, s, nullptr, scan_tmp);
-  launch("k_leaf_offsets_bbox", k_leaf_offsets_bbox, ceil_div(L, 256), 256, s, (const int4*)out.leaf_origin,
-         leaf_box, (const i64*)vox_excl, grid_info, out.leaf_offset, bbox_accum, B, R, L);
-  launch("k_write_headers", k_write_headers, ceil_div((i64)B, 4), 256, s, grid_info, (const i64*)vox_excl,
+  launch("k_vox_partials", k_vox_partials, 1, kPartThreads, s, vox_part, ceil_div(L, gran), leaf_vox, gran, grid_info,
+         B, L, bbox_accum, R, gvb);
+  launch("k_leaf_offsets_bbox", k_leaf_offsets_runs, ceil_div(L, 256), 256, s, (const int4*)out.leaf_origin, leaf_vox,
+         leaf_box, (const i64*)vox_part, gran, (const i64*)gvb, out.leaf_offset, bbox_accum, B, R, L);
+  launch("k_write_headers", k_write_headers_gvb, ceil_div((i64)B, 4), 256, s, grid_info, (const i64*)gvb,
          (const int32_t*)bbox_accum, B, R, out.headers);
 }
 

@@ -81,6 +81,9 @@ def bind(path: str):
     lib.oracle_build.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
                                  ctypes.c_void_p, ctypes.c_int32,
                                  ctypes.POINTER(ctypes.c_void_p)]
+    lib.oracle_build_masked_refine.restype = ctypes.c_int
+    lib.oracle_build_masked_refine.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                               ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(ctypes.c_void_p)]
     lib.oracle_size.restype = ctypes.c_int64
     lib.oracle_size.argtypes = [ctypes.c_void_p, ctypes.c_int]
     lib.oracle_copy.restype = ctypes.c_int
@@ -97,6 +100,38 @@ def _load():
             build()
             _lib = bind(LIB)
     return _lib
+
+
+def _collect(lib, handle, fields):
+    try:
+        out = {}
+        for name in (fields or FIELDS.keys()):
+            fid, dt, width = FIELDS[name]
+            n = lib.oracle_size(handle, fid)
+            arr = np.empty(n, dtype=dt)
+            if n:
+                lib.oracle_copy(handle, fid, arr.ctypes.data)
+            out[name] = arr.reshape(-1, width) if width > 1 else arr
+        return out
+    finally:
+        lib.oracle_free(handle)
+
+
+def run_masked_refine(factor: int, ijk: np.ndarray, offsets: np.ndarray, keep: np.ndarray, fields=None,
+                      lib=None) -> dict:
+    """Masked refine: keep (one byte per voxel, in the canonical enumeration order
+    of the batch built from ijk) prunes voxels, the rest are refined by factor."""
+    lib = lib or _load()
+    ijk = np.ascontiguousarray(np.asarray(ijk, dtype=np.int32).reshape(-1, 3))
+    offsets = np.ascontiguousarray(np.asarray(offsets, dtype=np.int64))
+    keep = np.ascontiguousarray(np.asarray(keep, dtype=np.uint8).reshape(-1))
+    handle = ctypes.c_void_p()
+    st = lib.oracle_build_masked_refine(int(factor), ijk.ctypes.data if ijk.size else None, offsets.ctypes.data,
+                                        int(offsets.shape[0]) - 1, keep.ctypes.data if keep.size else None,
+                                        int(keep.shape[0]), ctypes.byref(handle))
+    if st != OK:
+        raise OracleError(st)
+    return _collect(lib, handle, fields)
 
 
 def run(op, factor: int, ijk: np.ndarray, offsets: np.ndarray, fields=None, lib=None) -> dict:
@@ -118,15 +153,4 @@ def run(op, factor: int, ijk: np.ndarray, offsets: np.ndarray, fields=None, lib=
                           offsets.ctypes.data, B, ctypes.byref(handle))
     if st != OK:
         raise OracleError(st)
-    try:
-        out = {}
-        for name in (fields or FIELDS.keys()):
-            fid, dt, width = FIELDS[name]
-            n = lib.oracle_size(handle, fid)
-            arr = np.empty(n, dtype=dt)
-            if n:
-                lib.oracle_copy(handle, fid, arr.ctypes.data)
-            out[name] = arr.reshape(-1, width) if width > 1 else arr
-        return out
-    finally:
-        lib.oracle_free(handle)
+    return _collect(lib, handle, fields)

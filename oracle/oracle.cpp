@@ -15,6 +15,9 @@
 //        conv_s1 K  : { v + e : e in [-floor(K/2), floor((K-1)/2)]^3 }   K in [1,8]
 //        conv_t_s1 K: { v + e : e in [-floor((K-1)/2), floor(K/2)]^3 }   K in [1,8]
 //        identity   : S (a grid built directly from ijk)
+//        masked refine f : refine_f({ v in S : keep[v] }), keep given per voxel
+//                     in the canonical enumeration order of S (PR page, test
+//                     plan: masked refine; the mask prunes voxels, then refines)
 //      Source: "Batched leaf-mask topology construction for generated conv grids"
 //      (PR page), sections 1 and 2; factors 4 and 8 are the closed forms of the
 //      chained x2 passes described in section 1. The stride-1 kernel-K targets
@@ -361,5 +364,48 @@ int oracle_copy(const oracle_result* r, int field, void* dst) {
 }
 
 void oracle_free(oracle_result* r) { delete r; }
+
+// Masked refine: keep[j] (one byte per voxel, non-zero keeps) refers to the j-th
+// voxel of the batch in canonical enumeration order (members in order, each
+// member's distinct voxels sorted by canonical key). The kept voxels of every
+// member are refined by `factor` (2, 4 or 8). Same statuses as oracle_build.
+int oracle_build_masked_refine(int factor, const int32_t* ijk, const int64_t* offsets, int32_t B,
+                               const uint8_t* keep, int64_t n_keep, oracle_result** out) {
+  if (!out) return ST_INVALID;
+  *out = nullptr;
+  if (B < 1 || !offsets || offsets[0] != 0) return ST_INVALID;
+  for (int g = 0; g < B; ++g)
+    if (offsets[g + 1] < offsets[g]) return ST_INVALID;
+  if (offsets[B] > 0 && !ijk) return ST_INVALID;
+  try {
+    std::vector<int32_t> kept_ijk;
+    std::vector<int64_t> kept_off(1, 0);
+    i64 j = 0;  // running index in the canonical enumeration
+    for (int g = 0; g < B; ++g) {
+      std::vector<std::pair<Key, Vox>> m;
+      for (i64 i = offsets[g]; i < offsets[g + 1]; ++i) {
+        const Vox v{ijk[3 * i], ijk[3 * i + 1], ijk[3 * i + 2]};
+        m.push_back({canonical_key(v), v});
+      }
+      std::sort(m.begin(), m.end(), [](const std::pair<Key, Vox>& a, const std::pair<Key, Vox>& b) {
+        return a.first < b.first;
+      });
+      m.erase(std::unique(m.begin(), m.end(),
+                          [](const std::pair<Key, Vox>& a, const std::pair<Key, Vox>& b) { return a.first == b.first; }),
+              m.end());
+      for (const auto& kv : m) {
+        if (j >= n_keep || !keep) return ST_INVALID;  // fewer flags than voxels
+        if (keep[j])
+          kept_ijk.insert(kept_ijk.end(), {(int32_t)kv.second.x, (int32_t)kv.second.y, (int32_t)kv.second.z});
+        ++j;
+      }
+      kept_off.push_back((int64_t)(kept_ijk.size() / 3));
+    }
+    if (j != n_keep) return ST_INVALID;  // more flags than voxels
+    return oracle_build(OP_REFINE, factor, kept_ijk.empty() ? nullptr : kept_ijk.data(), kept_off.data(), B, out);
+  } catch (const std::bad_alloc&) {
+    return ST_NOMEM;
+  }
+}
 
 }  // extern "C"

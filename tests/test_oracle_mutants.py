@@ -47,6 +47,7 @@ MUTANTS = {
                              "if (!in_int32(v.x) || !in_int32(v.y)) return false;"),
     "conv_s1 leans the wrong way": ("case OP_CONV_S1: box(-(factor / 2), (factor - 1) / 2, in); break;",
                                     "case OP_CONV_S1: box(-((factor - 1) / 2), factor / 2, in); break;"),
+    "masked refine inverts the mask": ("        if (keep[j])\n", "        if (!keep[j])\n"),
     "conv_t_s1 box one short": ("case OP_CONV_T_S1: box(-((factor - 1) / 2), factor / 2, in); break;",
                                 "case OP_CONV_T_S1: box(-((factor - 1) / 2), (factor - 1) / 2, in); break;"),
 }
@@ -60,6 +61,7 @@ BATTERY = [
     functools.partial(pins.test_bruteforce_sets_and_order, "conv_t_k3s2", 2),
     functools.partial(pins.test_bruteforce_sets_and_order, "conv_s1", 4),
     functools.partial(pins.test_bruteforce_sets_and_order, "conv_t_s1", 4),
+    functools.partial(pins.test_masked_refine_bruteforce, 2),
     functools.partial(pins.test_refine_count_and_roundtrip, 2),
     pins.test_golden_canonical_order,
     pins.test_golden_tree_worked_example,
@@ -86,6 +88,7 @@ def test_planted_mistake_is_caught(name, source, tmp_path, monkeypatch):
     subprocess.check_call(["g++", "-O1", "-std=c++17", "-shared", "-fPIC", "-o", str(so), str(src)])
     lib = oracle.bind(str(so))
     monkeypatch.setattr(oracle, "run", functools.partial(oracle.run, lib=lib))
+    monkeypatch.setattr(oracle, "run_masked_refine", functools.partial(oracle.run_masked_refine, lib=lib))
     failures = []
     for check in BATTERY:
         try:

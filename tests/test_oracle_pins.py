@@ -256,6 +256,43 @@ def test_single_voxel_kernel_k_is_k_cube(op, k):
     assert tuple(r["headers"][0, 13:16]) == (v[0] + lo + k - 1, v[1] + lo + k - 1, v[2] + lo + k - 1)
 
 
+# ---------------------------------------------------------------- masked refine
+# PR page, test plan: masked refine (a per-voxel mask prunes the grid, the kept
+# voxels are refined). The mask is one flag per voxel in canonical enumeration
+# order; here that order comes from the test's own packed key, not the oracle.
+@pytest.mark.parametrize("f", [2, 4])
+def test_masked_refine_bruteforce(f):
+    rng = np.random.default_rng(300 + f)
+    for trial in range(3):
+        sets = random_sets(rng, 3, 10, CENTRES[:-1])
+        if trial == 1:
+            sets[0] = set()
+        ordered = [sorted(S, key=packed_order_key) for S in sets]
+        keep = [rng.integers(0, 2, size=len(o)).astype(np.uint8) for o in ordered]
+        ijk, off = _members_from_sets(sets)
+        r = oracle.run_masked_refine(f, ijk, off, np.concatenate(keep) if keep else np.zeros(0, np.uint8))
+        got = _grid_sets(r)
+        for g in range(len(sets)):
+            kept = {v for v, k in zip(ordered[g], keep[g]) if k}
+            exp = gather_member("refine", f, kept)
+            assert got[g] == exp, (f, trial, g)
+            b, n = r["headers"][g, 9], r["headers"][g, 8]
+            assert [tuple(v) for v in r["ijk"][b:b + n].tolist()] == sorted(exp, key=packed_order_key)
+
+
+def test_masked_refine_all_none_and_length():
+    ijk, off = synth.make_config(1)
+    n = int(oracle.run("identity", 1, ijk, off)["headers"][:, 8].sum())
+    full = oracle.run_masked_refine(2, ijk, off, np.ones(n, np.uint8))
+    _same_fields(full, oracle.run("refine", 2, ijk, off), "all kept")
+    none = oracle.run_masked_refine(2, ijk, off, np.zeros(n, np.uint8))
+    assert int(none["headers"][:, 8].sum()) == 0 and none["ijk"].shape == (0, 3)
+    for bad in (n - 1, n + 1):
+        with pytest.raises(oracle.OracleError) as e:
+            oracle.run_masked_refine(2, ijk, off, np.ones(bad, np.uint8))
+        assert e.value.status == oracle.INVALID
+
+
 @pytest.mark.parametrize("v", [(0, 0, 0), (7, 7, 7), (-1, -1, -1), (4095, -4096, 8), (-(1 << 31), 5, (1 << 31) - 2)])
 def test_single_voxel_dilate_is_27_cube(v):
     if v[0] == -(1 << 31):

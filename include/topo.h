@@ -188,6 +188,20 @@ tc_status tc_build_batched_topology(const tc_grid_batch* src, int32_t op, int32_
                                     const tc_allocator* allocator, void* stream,
                                     tc_grid_batch** out);
 
+/* Masked refine (PR page, test plan: masked refine): the voxels of `src` whose
+ * keep flag is zero are dropped, the rest are refined by `factor` (2, 4 or 8),
+ * as tc_build_batched_topology(TC_OP_REFINE) would refine the pruned batch.
+ *   d_keep  device array of n_keep bytes, one per voxel of src in enumeration
+ *           order (grid by grid, the order tc_enumerate_ijk writes); non-zero
+ *           keeps the voxel. Read only; the caller keeps ownership.
+ *   n_keep  must equal src's voxel total (tc_batch_voxel_total), else
+ *           TC_ERR_INVALID_ARG; d_keep may be NULL only when it is 0.
+ * Other arguments and the result as for tc_build_batched_topology. Blocks on the
+ * voxel total (if not yet known), one flag check and the passes' readbacks. */
+tc_status tc_build_masked_refine(const tc_grid_batch* src, const uint8_t* d_keep, int64_t n_keep,
+                                 int32_t factor, const tc_allocator* allocator, void* stream,
+                                 tc_grid_batch** out);
+
 /* Counts (host) and device array pointers of a batch. Never blocks. */
 tc_status tc_batch_get_info(const tc_grid_batch* batch, tc_batch_info* out);
 

@@ -85,6 +85,40 @@ def test_kernel_k_stride1_config2_k8_and_empty(op):
     _check(op, 4, ijk2, off2, "single voxel between empties")
 
 
+def _voxel_total(ijk, off):
+    return int(oracle.run("identity", 1, ijk, off, fields=["headers"])["headers"][:, 8].sum())
+
+
+@pytest.mark.parametrize("cfg,f", [(1, 2), (2, 2), (3, 2), (3, 4), (1, 8)])
+def test_masked_refine(cfg, f):
+    # PR page test plan: masked refine (per-voxel keep flags, then refine)
+    import torch
+    from topology_construction_amd import binding
+    ijk, off = synth.make_config(cfg)
+    keep = (np.random.default_rng(700 + cfg).random(_voxel_total(ijk, off)) < 0.6).astype(np.uint8)
+    print(f"[parity] masked refine config{cfg} f={f} kept={int(keep.sum())}/{keep.size}", flush=True)
+    ref = oracle.run_masked_refine(f, ijk, off, keep)
+    _, src = gpu_build("identity", 1, ijk, off)
+    out = binding.tc_build_masked_refine(src, torch.from_numpy(keep).cuda(), f)
+    assert_same(gpu_fields(out), ref, f"masked refine config{cfg} x{f}")
+
+
+def test_masked_refine_all_none_and_bad_length():
+    import torch
+    from topology_construction_amd import binding
+    ijk, off = synth.make_config(3)
+    n = _voxel_total(ijk, off)
+    _, src = gpu_build("identity", 1, ijk, off)
+    full = binding.tc_build_masked_refine(src, torch.ones(n, dtype=torch.uint8, device="cuda"), 2)
+    assert_same(gpu_fields(full), oracle.run("refine", 2, ijk, off), "all kept")
+    none = binding.tc_build_masked_refine(src, torch.zeros(n, dtype=torch.bool, device="cuda"), 2)
+    assert_same(gpu_fields(none), oracle.run_masked_refine(2, ijk, off, np.zeros(n, np.uint8)), "none kept")
+    for bad in (n - 1, n + 1):
+        with pytest.raises(binding.TopoError) as e:
+            binding.tc_build_masked_refine(src, torch.ones(bad, dtype=torch.uint8, device="cuda"), 2)
+        assert e.value.status == binding.TC_ERR_INVALID_ARG
+
+
 CENTRES = [(0, 0, 0), (4096, 0, -4096), (-4096, 4095, 127), (-1, -1, -1), (130, -130, 8), (-8192, 8191, 0)]
 
 

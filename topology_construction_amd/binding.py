@@ -26,7 +26,7 @@ OPS = {"coarsen": 1, "refine": 2, "dilate": 3, "pad_neg": 4, "pad_pos": 5, "conv
 
 ABI_SYMBOLS = [
     "tc_abi_version", "tc_status_string", "tc_last_error", "tc_batch_from_ijk",
-    "tc_build_batched_topology", "tc_batch_get_info", "tc_batch_read_headers",
+    "tc_build_batched_topology", "tc_build_masked_refine", "tc_batch_get_info", "tc_batch_read_headers",
     "tc_batch_voxel_total", "tc_enumerate_ijk", "tc_batch_free", "tc_profile_enable",
     "tc_profile_read", "tc_profile_disable",
 ]
@@ -115,6 +115,8 @@ def load_library(path: str = LIB_PATH):
         lib.tc_batch_from_ijk.argtypes = [vp, vp, i32, vp, vp, ctypes.POINTER(vp)]
         lib.tc_build_batched_topology.restype = ctypes.c_int
         lib.tc_build_batched_topology.argtypes = [vp, i32, i32, vp, vp, ctypes.POINTER(vp)]
+        lib.tc_build_masked_refine.restype = ctypes.c_int
+        lib.tc_build_masked_refine.argtypes = [vp, vp, i64, i32, vp, vp, ctypes.POINTER(vp)]
         lib.tc_batch_get_info.restype = ctypes.c_int
         lib.tc_batch_get_info.argtypes = [vp, ctypes.POINTER(tc_batch_info)]
         lib.tc_batch_read_headers.restype = ctypes.c_int
@@ -252,6 +254,21 @@ def tc_build_batched_topology(src: GridBatch, op, factor: int, stream=None, allo
     h = ctypes.c_void_p()
     _check(lib.tc_build_batched_topology(src.handle, op_id, int(factor), alloc, _stream_handle(stream),
                                          ctypes.byref(h)))
+    return GridBatch(h, allocator == "torch")
+
+
+def tc_build_masked_refine(src: GridBatch, keep, factor: int, stream=None, allocator: str = "torch") -> GridBatch:
+    """Masked refine: `keep` is a device uint8 (or bool) tensor, one flag per voxel
+    of `src` in enumeration order; kept voxels are refined by `factor`."""
+    import torch
+    lib = load_library()
+    if keep.device.type != "cuda" or keep.dim() != 1:
+        raise ValueError("keep must be a 1-D device tensor")
+    keep = keep.to(torch.uint8).contiguous()
+    alloc = ctypes.byref(TORCH_ALLOCATOR) if allocator == "torch" else None
+    h = ctypes.c_void_p()
+    _check(lib.tc_build_masked_refine(src.handle, keep.data_ptr() if keep.numel() else None, int(keep.numel()),
+                                      int(factor), alloc, _stream_handle(stream), ctypes.byref(h)))
     return GridBatch(h, allocator == "torch")
 
 

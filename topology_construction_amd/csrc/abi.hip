@@ -231,6 +231,63 @@ tc_status tc_build_batched_topology(const tc_grid_batch* src, int32_t op, int32_
   });
 }
 
+tc_status tc_build_masked_refine(const tc_grid_batch* src, const uint8_t* d_keep, int64_t n_keep, int32_t factor,
+                                 const tc_allocator* allocator, void* stream, tc_grid_batch** out) {
+  if (!out) return fail(TC_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (!src) return fail(TC_ERR_INVALID_ARG, "src is NULL");
+  if (allocator && (!allocator->alloc || !allocator->free))
+    return fail(TC_ERR_INVALID_ARG, "allocator callbacks are NULL");
+  if (factor != 2 && factor != 4 && factor != 8)
+    return fail(factor < 2 ? TC_ERR_INVALID_ARG : TC_ERR_UNSUPPORTED, "refine factor must be 2, 4 or 8");
+  return guarded([&]() {
+    if (current_device() != src->device) throw tc::Error(TC_ERR_INVALID_ARG, "src lives on another device");
+    hipStream_t s = (hipStream_t)stream;
+    const int64_t total = tc::read_voxel_total(src, s);
+    if (n_keep != total)
+      throw tc::Error(TC_ERR_INVALID_ARG, "keep holds " + std::to_string(n_keep) + " flags for " +
+                                              std::to_string(total) + " voxels");
+    if (total > 0 && !d_keep) throw tc::Error(TC_ERR_INVALID_ARG, "d_keep is NULL");
+    // masked copies of the source leaf masks (plus a consistency flag), then the
+    // refine passes; the first reads the masked copies
+    tc::Arena a(s);
+    const size_t o_mask = a.reserve(64 * (size_t)src->nl);
+    const size_t o_flag = a.reserve(4);
+    a.commit();
+    tc::u64* masked = a.at<tc::u64>(o_mask);
+    int32_t* flag = a.at<int32_t>(o_flag);
+    tc::fill_i32(flag, 0, 1, nullptr, 1, s);
+    tc::mask_leaves(src, d_keep, n_keep, masked, flag, s);
+    const int npass = factor == 2 ? 1 : (factor == 4 ? 2 : 3);
+    const tc_grid_batch* cur = src;
+    tc_grid_batch* owned = nullptr;
+    try {
+      for (int p = 0; p < npass; ++p) {
+        const bool last = p + 1 == npass;
+        tc_grid_batch* next = tc::build_pass(cur, TC_OP_REFINE, tc::OutAlloc{last ? allocator : nullptr, s},
+                                             p == 0 ? masked : nullptr);
+        if (p == 0) {
+          int32_t* h = static_cast<int32_t*>(tc::pinned_staging(64));
+          tc::hip_check(hipMemcpyAsync(h, flag, 4, hipMemcpyDeviceToHost, s), "readback");
+          tc::hip_check(hipStreamSynchronize(s), "hipStreamSynchronize");
+          if (h[0] != 0) {
+            tc::free_batch(next);
+            throw tc::Error(TC_ERR_INTERNAL, "masked refine: keep index out of range");
+          }
+        }
+        tc::free_batch(owned);
+        owned = next;
+        cur = next;
+      }
+    } catch (...) {
+      tc::free_batch(owned);
+      throw;
+    }
+    *out = owned;
+    return TC_OK;
+  });
+}
+
 tc_status tc_batch_get_info(const tc_grid_batch* b, tc_batch_info* out) {
   if (!b || !out) return fail(TC_ERR_INVALID_ARG, "NULL argument");
   const tc::GridView v = b->view();

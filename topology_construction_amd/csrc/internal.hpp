@@ -301,5 +301,12 @@ tc_grid_batch* copy_batch(const tc_grid_batch* src, const OutAlloc& oa);  // sam
 
 // The two producers of grid batches.
 tc_grid_batch* build_from_ijk(const int32_t* d_ijk, const int64_t* h_offsets, int32_t B, const OutAlloc& oa);
-tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa);
+// One batched pass. leaf_mask_override (device, one 512-bit mask per source leaf)
+// replaces the source leaf masks, e.g. masked copies for masked refine.
+tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa,
+                          const u64* leaf_mask_override = nullptr);
+// Masked copies of src's leaf masks from per-voxel keep flags (enumeration order);
+// a flag index outside [0, n_keep) sets the internal-error bit in *flags.
+void mask_leaves(const tc_grid_batch* src, const uint8_t* keep, i64 n_keep, u64* out_mask, int32_t* flags,
+                 hipStream_t s);
 }  // namespace tc

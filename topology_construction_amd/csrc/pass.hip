@@ -1386,12 +1386,58 @@ __global__ void __launch_bounds__(256) k_leaf_gather_box(const int4* out_origin,
   block_sum_to(count, &vox_part[blockIdx.x]);  // voxels of this block's leaves
 }
 
+// ------------------------------------------------------------------ masked refine
+// Keep flags (one byte per voxel, in enumeration order) -> masked copies of the
+// source leaf masks. One wave per leaf: lane r owns row r = x*8 + y (byte y of
+// word x); a wave scan of the row popcounts gives each row's first voxel, the
+// lane keeps the bits whose flags are set, and the 8 lanes of a word OR their
+// rows together.
+__global__ void __launch_bounds__(256) k_mask_leaves(const tc_grid_header* hdr, const int4* leaf_origin,
+                                                     const u64* leaf_mask, const i64* leaf_offset,
+                                                     const uint8_t* keep, i64 n_keep, i64 n_leaf, u64* out_mask,
+                                                     int32_t B, int32_t* flags) {
+  const i64 l = (i64)blockIdx.x * 4 + threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  if (l >= n_leaf) return;  // uniform per wave; no block barrier
+  const int x = lane >> 3, y = lane & 7;
+  const uint32_t row = (uint32_t)(leaf_mask[l * 8 + x] >> (8 * y)) & 0xffu;
+  const int cnt = __popc(row);
+  const int before = wave_incl_scan(cnt) - cnt;
+  const int g = leaf_origin[l].w;
+  i64 base = -1;
+  if (g >= 0 && g < B) base = hdr[g].voxel_begin + leaf_offset[l] + before;
+  uint32_t kept = 0;
+  int k = 0;
+  for (uint32_t m = row; m; m &= m - 1, ++k) {
+    const i64 j = base + k;
+    if (base < 0 || j >= n_keep) {
+      set_flag(flags, kFlagInternal);
+      break;
+    }
+    if (keep[j]) kept |= m & (~m + 1);  // lowest set bit of m
+  }
+  u64 w = (u64)kept << (8 * y);
+  w |= __shfl_xor(w, 1, kWave);
+  w |= __shfl_xor(w, 2, kWave);
+  w |= __shfl_xor(w, 4, kWave);
+  if (y == 0) out_mask[l * 8 + x] = w;
+}
+
+void mask_leaves(const tc_grid_batch* src, const uint8_t* keep, i64 n_keep, u64* out_mask, int32_t* flags,
+                 hipStream_t s) {
+  const GridView v = src->view();
+  launch("k_mask_leaves", k_mask_leaves, ceil_div((i64)v.n_leaf, 4), 256, s, (const tc_grid_header*)v.headers,
+         (const int4*)v.leaf_origin, (const u64*)v.leaf_mask, (const i64*)v.leaf_offset, keep, n_keep,
+         (i64)v.n_leaf, out_mask, v.B, flags);
+}
+
 // ------------------------------------------------------------------ driver
-tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa) {
+tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, const u64* leaf_mask_override) {
   const OpInfo oi = op_info(op);
   hipStream_t s = oa.stream;
   const int32_t B = src->B;
-  const GridView sv = src->view();
+  GridView sv = src->view();
+  if (leaf_mask_override) sv.leaf_mask = const_cast<u64*>(leaf_mask_override);
   const i64 nT = (i64)src->n2 * oi.m;
   const i64 nL = (i64)src->n1 * oi.m;
   const i64 Ls = src->nl;

@@ -10,7 +10,10 @@ enumeration. Inputs are resident in HBM before timing starts.
 Prints one JSON line (rank 0). `value` = output voxels per second over the K
 timed steps. `roofline` reports the dominant kernel's algorithmic bytes per
 launch over its HIP-event-timed average duration; `cpu_baseline` times the CPU
-oracle on one step of the same workload.
+oracle on whole steps of the same workload. Outside the timed steps the line
+also carries per-op medians (`ops`), the stride-1 kernel-K targets and masked
+refine (`more_ops`), the ijk front-end (`from_ijk`) and the 46M-voxel batch
+(`large`).
 """
 from __future__ import annotations
 
@@ -255,6 +258,26 @@ def main():
                             "ms_enumerate_median": float(np.median(enum_ms)),
                             "output_voxels": int(ijk_out.shape[0]), "output_leaves": int(out.leaf_count)}
 
+    # the rows beyond the step: stride-1 kernel-K targets and masked refine (60% kept)
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    keep = (torch.rand(src.voxel_total(), device="cuda", generator=gen) < 0.6).to(torch.uint8)
+    extra_ops = [("conv_s1", 2), ("conv_s1", 4), ("conv_s1", 5), ("conv_t_s1", 2), ("conv_t_s1", 4), ("masked_refine", 2)]
+    extra = {}
+    for op, f in extra_ops:
+        pass_ms = []
+        for _ in range(20):
+            torch.cuda.synchronize()
+            a = time.perf_counter()
+            if op == "masked_refine":
+                out = binding.tc_build_masked_refine(src, keep, f)
+            else:
+                out = binding.tc_build_batched_topology(src, op, f)
+            torch.cuda.synchronize()
+            pass_ms.append((time.perf_counter() - a) * 1e3)
+        extra[f"{op}x{f}"] = {"ms_median": float(np.median(pass_ms)), "output_voxels": int(out.voxel_total()),
+                              "output_leaves": int(out.leaf_count)}
+        del out
+
     bytes_per_step = sum(kernel_bytes(args.roofline_kernel, int(src.leaf_count), L, V) for (_, _, L, V) in facts)
     launches_per_step = len(facts)
     avg_ms = k_ms / max(k_n, 1)
@@ -290,7 +313,7 @@ def main():
         "vs_baseline": None, "dtype": "int32", "data": "synthetic",
         "config": {"workload": synth.CONFIG_NAMES[args.config], "grids": int(len(off) - 1),
                    "input_voxels": int(off[-1]), "ops": [f"{o}x{f}" for o, f in STEP_OPS]},
-        "roofline": roofline, "cpu_baseline": cpu, "ops": ops,
+        "roofline": roofline, "cpu_baseline": cpu, "ops": ops, "more_ops": extra,
         "from_ijk": time_from_ijk(binding, torch, np, d_ijk, off, 20), "large": large,
     }
     print(json.dumps(rec), flush=True)

@@ -817,8 +817,9 @@ __global__ void __launch_bounds__(256) k_enumerate(const tc_grid_header* hdr, co
 
 void tree_enumerate(const GridView& v, int32_t* ijk, hipStream_t s) {
   const int vec_ok = (reinterpret_cast<uintptr_t>(ijk) & 15) == 0 ? 1 : 0;
-  // enough waves to cover every CU several times before packing leaves per wave
-  const int lpw = v.n_leaf >= 256 * 1024 ? kEnumMaxLeaves : (v.n_leaf >= 64 * 1024 ? 2 : 1);
+  // one leaf per wave while the waves fit in one round of the chip (about 6k
+  // resident at this LDS use), then two, then eight on large batches
+  const int lpw = v.n_leaf >= 256 * 1024 ? kEnumMaxLeaves : (v.n_leaf >= 6 * 1024 ? 2 : 1);
   launch("k_enumerate", k_enumerate, ceil_div((i64)v.n_leaf, 4 * lpw), 256, s,
          (const tc_grid_header*)v.headers, (const int4*)v.leaf_origin, (const u64*)v.leaf_mask,
          (const i64*)v.leaf_offset, ijk, (i64)v.n_leaf, lpw, vec_ok);

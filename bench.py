@@ -203,7 +203,7 @@ def measure_large(binding, torch, np, synth):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1"}))
+        print(json.dumps({"error": "this benchmark runs on one GPU only; run with --gpus 1"}))
         sys.exit(2)
     import numpy as np
     import torch

@@ -15,8 +15,8 @@ def pytest_configure(config):
 
 def pytest_collection_modifyitems(config, items):
     # GPU tests are skipped (not failed) when no HIP device is visible, so that a
-    # plain `pytest` run on a CPU-only machine stays green. On the GPU machine the
-    # marker selection `-m gpu` runs them.
+    # plain `pytest` run on a CPU-only machine stays green. On a machine with an
+    # MI355X the marker selection `-m gpu` runs them.
     try:
         import torch
         have_gpu = torch.cuda.is_available()

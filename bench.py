@@ -51,6 +51,29 @@ def parse():
     return ap.parse_args()
 
 
+def op_medians(binding, torch, np, src, reps=20):
+    """Per-op pass and enumeration medians over `reps` runs (the Measurements
+    protocol of the PR page: median of 20 timed iterations)."""
+    ops = {}
+    for op, f in STEP_OPS:
+        pass_ms, enum_ms = [], []
+        for _ in range(reps):
+            torch.cuda.synchronize()
+            a = time.perf_counter()
+            out = binding.tc_build_batched_topology(src, op, f)
+            torch.cuda.synchronize()
+            b = time.perf_counter()
+            ijk_out = binding.tc_enumerate_ijk(out)
+            torch.cuda.synchronize()
+            c = time.perf_counter()
+            pass_ms.append((b - a) * 1e3)
+            enum_ms.append((c - b) * 1e3)
+        ops[f"{op}x{f}"] = {"ms_pass_median": float(np.median(pass_ms)),
+                            "ms_enumerate_median": float(np.median(enum_ms)),
+                            "output_voxels": int(ijk_out.shape[0]), "output_leaves": int(out.leaf_count)}
+    return ops
+
+
 def run_step(binding, src, outs=None):
     """One step: every op, each followed by the voxel enumeration. Returns voxels."""
     total = 0
@@ -240,23 +263,16 @@ def main():
     ms_step = elapsed * 1e3 / args.steps
 
     # per-op breakdown (separate, untimed-by-the-step loop): pass and enumeration
-    ops = {}
-    for op, f in STEP_OPS:
-        pass_ms, enum_ms = [], []
-        for _ in range(20):
-            torch.cuda.synchronize()
-            a = time.perf_counter()
-            out = binding.tc_build_batched_topology(src, op, f)
-            torch.cuda.synchronize()
-            b = time.perf_counter()
-            ijk_out = binding.tc_enumerate_ijk(out)
-            torch.cuda.synchronize()
-            c = time.perf_counter()
-            pass_ms.append((b - a) * 1e3)
-            enum_ms.append((c - b) * 1e3)
-        ops[f"{op}x{f}"] = {"ms_pass_median": float(np.median(pass_ms)),
-                            "ms_enumerate_median": float(np.median(enum_ms)),
-                            "output_voxels": int(ijk_out.shape[0]), "output_leaves": int(out.leaf_count)}
+    ops = op_medians(binding, torch, np, src)
+    # the same at B=48 (mixed member sizes, three empty members, members
+    # straddling +-4096 tiles): how flat the batched pass stays as B triples
+    ijk48, off48 = synth.make_config(3)
+    src48 = binding.tc_batch_from_ijk(torch.from_numpy(ijk48).cuda(), off48)
+    ops48 = op_medians(binding, torch, np, src48)
+    b48 = {"workload": synth.CONFIG_NAMES[3], "grids": int(len(off48) - 1), "input_voxels": int(off48[-1]),
+           "ops": ops48,
+           "pass_ratio_b48_over_b16": {k: ops48[k]["ms_pass_median"] / ops[k]["ms_pass_median"] for k in ops}}
+    del src48
 
     # the rows beyond the step: stride-1 kernel-K targets and masked refine (60% kept)
     gen = torch.Generator(device="cuda").manual_seed(11)
@@ -313,7 +329,7 @@ def main():
         "vs_baseline": None, "dtype": "int32", "data": "synthetic",
         "config": {"workload": synth.CONFIG_NAMES[args.config], "grids": int(len(off) - 1),
                    "input_voxels": int(off[-1]), "ops": [f"{o}x{f}" for o, f in STEP_OPS]},
-        "roofline": roofline, "cpu_baseline": cpu, "ops": ops, "more_ops": extra,
+        "roofline": roofline, "cpu_baseline": cpu, "ops": ops, "b48": b48, "more_ops": extra,
         "from_ijk": time_from_ijk(binding, torch, np, d_ijk, off, 20), "large": large,
     }
     print(json.dumps(rec), flush=True)

@@ -43,15 +43,24 @@ __device__ __forceinline__ T block_excl_scan(T v, T* s_wave, T& total) {
 
 __device__ __forceinline__ int popc64(uint64_t x) { return __popcll(x); }
 
-// Sum of v over a 256-thread block, written to *dst by thread 0. Every thread of
-// the block must call it (it holds a block barrier).
-__device__ __forceinline__ void block_sum_to(int64_t v, int64_t* dst) {
-  __shared__ int64_t s_part[4];
+// Voxel counts of a 256-thread block's leaves (v = 0 on lanes that own no leaf):
+// returns this thread's exclusive prefix inside the block and writes the block's
+// total to *total_dst. Every thread of the block must call it (block barriers).
+__device__ __forceinline__ int32_t block_run_scan(int32_t v, int64_t* total_dst) {
+  __shared__ int32_t s_wave[4];
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  int32_t inc = v;
 #pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
-  if ((threadIdx.x & (kWave - 1)) == 0) s_part[threadIdx.x / kWave] = v;
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int32_t t = __shfl_up(inc, d, kWave);
+    if (lane >= d) inc += t;
+  }
+  if (lane == kWave - 1) s_wave[w] = inc;
   __syncthreads();
-  if (threadIdx.x == 0) *dst = s_part[0] + s_part[1] + s_part[2] + s_part[3];
+  int32_t off = 0;
+  for (int i = 0; i < w; ++i) off += s_wave[i];
+  if (threadIdx.x == 0) *total_dst = (int64_t)s_wave[0] + s_wave[1] + s_wave[2] + s_wave[3];
+  return off + inc - v;
 }
 
 // Index of the r-th set bit (0-based) of w; w must have more than r set bits.

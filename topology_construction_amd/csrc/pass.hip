@@ -235,6 +235,26 @@ __device__ __forceinline__ uint32_t upper_word_reach(u64 word, int w, int op) {
   return code;
 }
 
+// Reach set of every source node, one wave per node (uppers: 8 mask words per
+// lane; lowers: one), for batches too large to do it inside the single-workgroup
+// stages.
+__global__ void __launch_bounds__(256) k_node_reach(const u64* mask, i64 n_nodes, int words, int op, int m,
+                                                    uint32_t* reach) {
+  const i64 u = (i64)blockIdx.x * 4 + threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  if (u >= n_nodes) return;  // uniform per wave
+  uint32_t code = 0;
+  if (words == 512) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) code |= upper_word_reach(mask[u * 512 + k * kWave + lane], k * kWave + lane, op);
+  } else {
+    code = lower_word_reach(mask[u * 64 + lane], lane, op);
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) code |= (uint32_t)__shfl_xor((int)code, d, kWave);
+  if (lane == 0) reach[u] = op == TC_OP_REFINE ? code : box_code_for_op(code, op, m);
+}
+
 // ------------------------------------------------------------------ stage: tiles, fused (small batches)
 // At most 4096 tile candidates: one workgroup builds the reach set of every
 // source upper, compacts the reachable in-range candidates, sorts them in LDS
@@ -250,7 +270,8 @@ __global__ void __launch_bounds__(kTilesThreads) k_tiles_small(const int4* upper
                                                                int32_t n_upper, int op, int m, int32_t B,
                                                                int4* utile, int32_t* tile_of_cand,
                                                                int32_t* d_num_tiles, int32_t* grid_tile_begin,
-                                                               u64* tile_child, int zero_child, int32_t* readback) {
+                                                               u64* tile_child, int zero_child,
+                                                               const uint32_t* upper_reach, int32_t* readback) {
   __shared__ u64 s_hi[kTilesMax];
   __shared__ u64 s_lo[kTilesMax];
   __shared__ uint32_t s_v[kTilesMax];
@@ -262,7 +283,9 @@ __global__ void __launch_bounds__(kTilesThreads) k_tiles_small(const int4* upper
   const int wv = tid / kWave;
   const int n = n_upper * m;
   if (tid == 0) readback[0] = 0;
-  if (op != TC_OP_COARSEN) {
+  if (op != TC_OP_COARSEN && upper_reach) {  // computed by k_node_reach
+    for (int u = tid; u < n_upper; u += kTilesThreads) s_code[u] = upper_reach[u];
+  } else if (op != TC_OP_COARSEN) {
     // each wave reduces kUppersPerWave uppers at a time, so that many mask loads
     // are in flight at once
     constexpr int kUppersPerWave = 4;
@@ -622,15 +645,17 @@ __device__ __forceinline__ void lower_nbr_one(i64 i, const int4* lower_origin, c
   cand_src[(i64)c * m_src + js] = (int32_t)l;
 }
 
-__global__ void __launch_bounds__(256) k_lower_mark(const int4* lower_origin, const u64* lower_mask, i64 n, int op,
-                                                    int m, const int32_t* tile_of_cand, const int32_t* d_num_tiles,
+__global__ void __launch_bounds__(256) k_lower_mark(const int4* lower_origin, const u64* lower_mask,
+                                                    const uint32_t* reach, i64 n, int op, int m,
+                                                    const int32_t* tile_of_cand, const int32_t* d_num_tiles,
                                                     u64* tile_child, int32_t* flags) {
   const i64 i = (i64)blockIdx.x * 256 + threadIdx.x;
   if (i >= n) return;
-  lower_mark_one(i, lower_origin, lower_mask, nullptr, op, m, tile_of_cand, *d_num_tiles, tile_child, flags);
+  lower_mark_one(i, lower_origin, lower_mask, reach, op, m, tile_of_cand, *d_num_tiles, tile_child, flags);
 }
 
-__global__ void __launch_bounds__(256) k_lower_nbr(const int4* lower_origin, const u64* lower_mask, i64 n, int op,
+__global__ void __launch_bounds__(256) k_lower_nbr(const int4* lower_origin, const u64* lower_mask,
+                                                   const uint32_t* reach, i64 n, int op,
                                                    int m, int m_src, const int32_t* tile_of_cand,
                                                    const u64* tile_child, const uint16_t* tile_prefix,
                                                    const int32_t* tile_lower_base, const int32_t* d_num_tiles,
@@ -638,7 +663,7 @@ __global__ void __launch_bounds__(256) k_lower_nbr(const int4* lower_origin, con
                                                    int32_t* cand_src, int32_t* flags) {
   const i64 i = (i64)blockIdx.x * 256 + threadIdx.x;
   if (i >= n) return;
-  lower_nbr_one(i, lower_origin, lower_mask, nullptr, op, m, m_src, tile_of_cand, tile_child, tile_prefix,
+  lower_nbr_one(i, lower_origin, lower_mask, reach, op, m, m_src, tile_of_cand, tile_child, tile_prefix,
                 tile_lower_base, *d_num_tiles, *d_num_cands, lower_nbr, cand_origin, cand_src, flags);
 }
 
@@ -1127,8 +1152,8 @@ __global__ void __launch_bounds__(256) k_leaf_gather(const int4* out_origin, con
                                                      const int32_t* src_lower_first, const u64* src_leaf_mask,
                                                      int32_t n_src_lower, int32_t n_src_leaf,
                                                      const int32_t* d_num_cands, u64* out_mask, u64* out_prefix,
-                                                     i64* leaf_vox, uint32_t* leaf_box, i64* vox_part,
-                                                     int32_t* flags) {
+                                                     i64* leaf_vox, uint32_t* leaf_box, int32_t* leaf_inrun,
+                                                     i64* vox_part, int32_t* flags) {
   constexpr int lpl = KIND == 0 ? 1 : 4;  // lanes per output leaf
   const i64 gt = (i64)blockIdx.x * 256 + threadIdx.x;
   const i64 i = gt / lpl;
@@ -1245,11 +1270,13 @@ __global__ void __launch_bounds__(256) k_leaf_gather(const int4* out_origin, con
     leaf_stats(out, prefix, count, box);
     out_prefix[i] = prefix;
   }
+  // voxels before this leaf within the block's leaves, and the block's total
+  const int32_t inrun = block_run_scan(count, &vox_part[blockIdx.x]);
   if (writer) {
-    leaf_vox[i] = count;
+    if (leaf_vox) leaf_vox[i] = count;
     leaf_box[i] = box;
+    leaf_inrun[i] = inrun;
   }
-  block_sum_to(count, &vox_part[blockIdx.x]);  // voxels of this block's leaves
 }
 
 // ------------------------------------------------------------------ writers: box ops, separable
@@ -1268,8 +1295,8 @@ __global__ void __launch_bounds__(256) k_leaf_gather_box(const int4* out_origin,
                                                          const int32_t* src_lower_first, const u64* src_leaf_mask,
                                                          int32_t n_src_lower, int32_t n_src_leaf,
                                                          const int32_t* d_num_cands, u64* out_mask, u64* out_prefix,
-                                                         i64* leaf_vox, uint32_t* leaf_box, i64* vox_part,
-                                                         int32_t* flags) {
+                                                         i64* leaf_vox, uint32_t* leaf_box, int32_t* leaf_inrun,
+                                                         i64* vox_part, int32_t* flags) {
   const i64 gt = (i64)blockIdx.x * 256 + threadIdx.x;
   const i64 i = gt >> 2;
   const int sub = (int)(gt & 3);
@@ -1379,11 +1406,13 @@ __global__ void __launch_bounds__(256) k_leaf_gather_box(const int4* out_origin,
       out_prefix[i] = prefix;
     }
   }
+  // voxels before this leaf within the block's leaves, and the block's total
+  const int32_t inrun = block_run_scan(count, &vox_part[blockIdx.x]);
   if (i < n && sub == 0) {
-    leaf_vox[i] = count;
+    if (leaf_vox) leaf_vox[i] = count;
     leaf_box[i] = box;
+    leaf_inrun[i] = inrun;
   }
-  block_sum_to(count, &vox_part[blockIdx.x]);  // voxels of this block's leaves
 }
 
 // ------------------------------------------------------------------ masked refine
@@ -1471,6 +1500,8 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, 
   const size_t o_csrc = a.reserve(4 * nL * oi.m_src);
   const size_t o_ginfo = a.reserve(4 * 6 * (i64)B);
   const size_t o_rb = a.reserve(4 * (4 + 3 * (i64)B));
+  const size_t o_ureach = a.reserve(4 * (i64)src->n2);
+  const size_t o_lreach = a.reserve(4 * (i64)src->n1);
   const size_t o_stmp = a.reserve(std::max(scan_tmp_bytes(nT, 4), scan_tmp_bytes(nL, 8)));
   a.commit();
 
@@ -1507,9 +1538,16 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, 
     // the bitmaps are zeroed in-kernel when few (at most 1 MiB for one workgroup):
     // by the fused lower stage, or here; otherwise by a wide fill
     const bool zero_here = !small_lowers && nT <= 256;
+    // many source uppers: their reach sets in a wide launch first
+    uint32_t* ureach = nullptr;
+    if (op != TC_OP_COARSEN && src->n2 > 64) {
+      ureach = a.at<uint32_t>(o_ureach);
+      launch("k_node_reach", k_node_reach, ceil_div((i64)src->n2, 4), 256, s, (const u64*)sv.upper_mask,
+             (i64)src->n2, 512, op, oi.m, ureach);
+    }
     launch("k_tiles_small", k_tiles_small, 1, kTilesThreads, s, (const int4*)sv.upper_origin,
            (const u64*)sv.upper_mask, (int32_t)src->n2, op, oi.m, B, ts.utile, tile_of_cand, ts.d_num_tiles,
-           ts.grid_tile_begin, ts.tile_child, zero_here ? 1 : 0, ts.readback);
+           ts.grid_tile_begin, ts.tile_child, zero_here ? 1 : 0, (const uint32_t*)ureach, ts.readback);
     if (!small_lowers && !zero_here) fill_u64(ts.tile_child, 0, nT * 512, ts.d_num_tiles, 512, s);
   } else {
     fill_i32(ts.readback, 0, 1, nullptr, 1, s);
@@ -1540,14 +1578,20 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, 
            (const int32_t*)ts.d_num_tiles, ts.tile_child, ts.tile_prefix, ts.tile_lower_base, ts.d_num_cands,
            ts.cand_child, op == TC_OP_COARSEN ? 1 : 0, lower_nbr, ts.cand_origin, cand_src, ts.flags);
   } else {
+    uint32_t* lreach = nullptr;
+    if (op != TC_OP_COARSEN) {
+      lreach = a.at<uint32_t>(o_lreach);
+      launch("k_node_reach", k_node_reach, ceil_div((i64)src->n1, 4), 256, s, (const u64*)sv.lower_mask,
+             (i64)src->n1, 64, op, oi.m, lreach);
+    }
     launch("k_lower_mark", k_lower_mark, ceil_div(nL, 256), 256, s, (const int4*)sv.lower_origin,
-           (const u64*)sv.lower_mask, nL, op, oi.m, (const int32_t*)tile_of_cand, (const int32_t*)ts.d_num_tiles,
-           ts.tile_child, ts.flags);
+           (const u64*)sv.lower_mask, (const uint32_t*)lreach, nL, op, oi.m, (const int32_t*)tile_of_cand,
+           (const int32_t*)ts.d_num_tiles, ts.tile_child, ts.flags);
     tree_rank_tiles(ts, s);
     fill_pair(cand_src, -1, nL * oi.m_src, oi.m_src, ts.cand_child, 0, op == TC_OP_COARSEN ? nL * 64 : 0, 64,
               ts.d_num_cands, s);
     launch("k_lower_nbr", k_lower_nbr, ceil_div(nL, 256), 256, s, (const int4*)sv.lower_origin,
-           (const u64*)sv.lower_mask, nL, op, oi.m, oi.m_src, (const int32_t*)tile_of_cand,
+           (const u64*)sv.lower_mask, (const uint32_t*)lreach, nL, op, oi.m, oi.m_src, (const int32_t*)tile_of_cand,
            (const u64*)ts.tile_child, (const uint16_t*)ts.tile_prefix, (const int32_t*)ts.tile_lower_base,
            (const int32_t*)ts.d_num_tiles, (const int32_t*)ts.d_num_cands, lower_nbr, ts.cand_origin, cand_src,
            ts.flags);
@@ -1588,9 +1632,12 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, 
     const i64 gran = op == TC_OP_REFINE ? 256 : 64;
     const size_t o_part = post.reserve(8 * (ceil_div(L, gran) + 1));
     const size_t o_gvb = post.reserve(8 * ((i64)B + 1));
+    const size_t o_inrun = post.reserve(4 * L);
     post.commit();
     int32_t* leaf_cand = post.at<int32_t>(o_lc);
     i64* vox_part = post.at<i64>(o_part);
+    i64* leaf_vox = finalize_is_small(L, B) ? post.at<i64>(o_lv) : nullptr;  // per-leaf counts: small path only
+    int32_t* leaf_inrun = post.at<int32_t>(o_inrun);
     tree_write_nodes(ts, ov, leaf_cand, s);
     if (L > 0 && sv.n_leaf == 0) throw Error(TC_ERR_INTERNAL, "pass: output leaves without source leaves");
     if (op == TC_OP_REFINE || op == TC_OP_COARSEN) {
@@ -1600,15 +1647,15 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, 
              (const int32_t*)leaf_cand, L, op, oi.m, oi.lo, oi.hi, (const int32_t*)cand_src,
              (const u64*)sv.lower_mask, (const uint16_t*)sv.lower_prefix, (const int32_t*)sv.lower_first,
              (const u64*)sv.leaf_mask, sv.n_lower, sv.n_leaf, (const int32_t*)ts.d_num_cands, ov.leaf_mask,
-             ov.leaf_prefix, post.at<i64>(o_lv), post.at<uint32_t>(o_box), vox_part, ts.flags);
+             ov.leaf_prefix, leaf_vox, post.at<uint32_t>(o_box), leaf_inrun, vox_part, ts.flags);
     } else {
       launch("k_leaf_gather", k_leaf_gather_box, ceil_div(L * 4, 256), 256, s, (const int4*)ov.leaf_origin,
              (const int32_t*)leaf_cand, L, oi.lo, oi.hi, (const int32_t*)cand_src, (const u64*)sv.lower_mask,
              (const uint16_t*)sv.lower_prefix, (const int32_t*)sv.lower_first, (const u64*)sv.leaf_mask,
              sv.n_lower, sv.n_leaf, (const int32_t*)ts.d_num_cands, ov.leaf_mask, ov.leaf_prefix,
-             post.at<i64>(o_lv), post.at<uint32_t>(o_box), vox_part, ts.flags);
+             leaf_vox, post.at<uint32_t>(o_box), leaf_inrun, vox_part, ts.flags);
     }
-    tree_finalize_leaves(ov, post.at<i64>(o_lv), post.at<uint32_t>(o_box), vox_part, gran, post.at<i64>(o_vx),
+    tree_finalize_leaves(ov, leaf_vox, post.at<uint32_t>(o_box), leaf_inrun, vox_part, gran, post.at<i64>(o_vx),
                          post.at<i64>(o_gvb), post.at<int32_t>(o_bb), (const int32_t*)ts.grid_info, s);
   } catch (...) {
     free_batch(out);

@@ -384,26 +384,31 @@ void tree_write_nodes(TreeScratch& ts, const GridView& out, int32_t* leaf_cand, 
 // Per leaf (masks written by the ijk front-end): prefix word, voxel count and
 // packed local bbox. The topology pass computes the same values in its gather.
 __global__ void __launch_bounds__(256) k_leaf_stats(const u64* leaf_mask, u64* leaf_prefix, i64* leaf_vox,
-                                                    uint32_t* leaf_box, i64* vox_part, i64 n_leaf) {
+                                                    uint32_t* leaf_box, int32_t* leaf_inrun, i64* vox_part,
+                                                    i64 n_leaf) {
   const i64 i = (i64)blockIdx.x * 256 + threadIdx.x;
   int count = 0;
+  u64 prefix = 0;
+  uint32_t box = kEmptyBox;
   if (i < n_leaf) {
     u64 W[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) W[k] = leaf_mask[i * 8 + k];
-    u64 prefix;
-    uint32_t box;
     leaf_stats(W, prefix, count, box);
-    leaf_prefix[i] = prefix;
-    leaf_vox[i] = count;
-    leaf_box[i] = box;
   }
-  block_sum_to(count, &vox_part[blockIdx.x]);
+  const int32_t inrun = block_run_scan(count, &vox_part[blockIdx.x]);
+  if (i < n_leaf) {
+    leaf_prefix[i] = prefix;
+    if (leaf_vox) leaf_vox[i] = count;
+    leaf_box[i] = box;
+    leaf_inrun[i] = inrun;
+  }
 }
 
-void tree_leaf_stats(const GridView& out, i64* leaf_vox, uint32_t* leaf_box, i64* vox_part, hipStream_t s) {
+void tree_leaf_stats(const GridView& out, i64* leaf_vox, uint32_t* leaf_box, int32_t* leaf_inrun, i64* vox_part,
+                     hipStream_t s) {
   launch("k_leaf_stats", k_leaf_stats, ceil_div((i64)out.n_leaf, 256), 256, s, (const u64*)out.leaf_mask,
-         out.leaf_prefix, leaf_vox, leaf_box, vox_part, (i64)out.n_leaf);
+         out.leaf_prefix, leaf_vox, leaf_box, leaf_inrun, vox_part, (i64)out.n_leaf);
 }
 
 // Per-grid bboxes of large batches: leaf bounds are reduced over the wave (leaves
@@ -585,8 +590,8 @@ __global__ void __launch_bounds__(kFinThreads) k_finalize_small(const int4* leaf
 constexpr int kPartThreads = 1024;
 constexpr int kPartItems = 16;
 
-__global__ void __launch_bounds__(kPartThreads) k_vox_partials(i64* vox_part, i64 np, const i64* leaf_vox, i64 gran,
-                                                               const int32_t* grid_info, int32_t B, i64 L,
+__global__ void __launch_bounds__(kPartThreads) k_vox_partials(i64* vox_part, i64 np, const int32_t* leaf_inrun,
+                                                               i64 gran, const int32_t* grid_info, int32_t B, i64 L,
                                                                int32_t* bbox, int32_t R, i64* gvb) {
   __shared__ i64 s_wave[kPartThreads / kWave];
   i64 carry = 0;
@@ -614,34 +619,21 @@ __global__ void __launch_bounds__(kPartThreads) k_vox_partials(i64* vox_part, i6
   }
   __threadfence();
   __syncthreads();  // the scanned runs are read below
-  // one wave per grid: its first leaf's run offset plus the leaves before it in the run
-  const int lane = threadIdx.x & (kWave - 1);
-  for (int32_t g = threadIdx.x / kWave; g <= B; g += kPartThreads / kWave) {
+  // a grid's voxel begin: its first leaf's run offset plus that leaf's in-run prefix
+  for (int32_t g = threadIdx.x; g <= B; g += kPartThreads) {
     const i64 f = g < B ? grid_info[g * 6 + 5] : L;
-    if (f >= L) {  // uniform per wave
-      if (lane == 0) gvb[g] = carry;
-      continue;
-    }
-    const i64 run = f / gran;
-    i64 sum = 0;
-    for (i64 j = run * gran + lane; j < f; j += kWave) sum += leaf_vox[j];
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) sum += __shfl_xor(sum, d, kWave);
-    if (lane == 0) gvb[g] = vox_part[run] + sum;
+    gvb[g] = f < L ? vox_part[f / gran] + leaf_inrun[f] : carry;
   }
 }
 
 // Per leaf: offset inside its grid and the per-grid bbox (as k_leaf_offsets_bbox).
-__global__ void __launch_bounds__(256) k_leaf_offsets_runs(const int4* leaf_origin, const i64* leaf_vox,
+__global__ void __launch_bounds__(256) k_leaf_offsets_runs(const int4* leaf_origin, const int32_t* leaf_inrun,
                                                            const uint32_t* leaf_box, const i64* vox_part, i64 gran,
                                                            const i64* gvb, i64* leaf_offset, int32_t* bbox,
                                                            int32_t B, int32_t R, i64 n_leaf) {
-  __shared__ i64 s_wave[256 / kWave];
   const i64 i = (i64)blockIdx.x * 256 + threadIdx.x;
   const int lane = threadIdx.x & (kWave - 1);
-  const i64 v = i < n_leaf ? leaf_vox[i] : 0;
-  i64 total;
-  const i64 ex = block_excl_scan<i64, 256>(v, s_wave, total) + vox_part[((i64)blockIdx.x * 256) / gran];
+  const i64 ex = i < n_leaf ? vox_part[i / gran] + leaf_inrun[i] : 0;  // batch-global voxel index of the leaf
   int g = -1;
   int bv[6] = {INT32_MAX, INT32_MAX, INT32_MAX, INT32_MIN, INT32_MIN, INT32_MIN};
   if (i < n_leaf) {
@@ -721,21 +713,23 @@ __global__ void __launch_bounds__(256) k_write_headers_gvb(const int32_t* grid_i
   hdr[g] = h;
 }
 
-void tree_finalize_leaves(const GridView& out, const i64* leaf_vox, const uint32_t* leaf_box, i64* vox_part,
-                          i64 gran, i64* vox_excl, i64* gvb, int32_t* bbox_accum, const int32_t* grid_info,
-                          hipStream_t s) {
+bool finalize_is_small(i64 L, int32_t B) { return L <= kFinSmallLeaves && B <= kFinSmallGrids; }
+
+void tree_finalize_leaves(const GridView& out, const i64* leaf_vox, const uint32_t* leaf_box,
+                          const int32_t* leaf_inrun, i64* vox_part, i64 gran, i64* vox_excl, i64* gvb,
+                          int32_t* bbox_accum, const int32_t* grid_info, hipStream_t s) {
   const i64 L = out.n_leaf;
   const int32_t B = out.B;
-  if (L <= kFinSmallLeaves && B <= kFinSmallGrids) {
+  if (finalize_is_small(L, B)) {
     launch("k_finalize_small", k_finalize_small, 1, kFinThreads, s, (const int4*)out.leaf_origin, leaf_vox, leaf_box,
            grid_info, vox_excl, out.leaf_offset, B, L, out.headers);
     return;
   }
   const int32_t R = bbox_replicas(B);
-  launch("k_vox_partials", k_vox_partials, 1, kPartThreads, s, vox_part, ceil_div(L, gran), leaf_vox, gran, grid_info,
-         B, L, bbox_accum, R, gvb);
-  launch("k_leaf_offsets_bbox", k_leaf_offsets_runs, ceil_div(L, 256), 256, s, (const int4*)out.leaf_origin, leaf_vox,
-         leaf_box, (const i64*)vox_part, gran, (const i64*)gvb, out.leaf_offset, bbox_accum, B, R, L);
+  launch("k_vox_partials", k_vox_partials, 1, kPartThreads, s, vox_part, ceil_div(L, gran), leaf_inrun, gran,
+         grid_info, B, L, bbox_accum, R, gvb);
+  launch("k_leaf_offsets_bbox", k_leaf_offsets_runs, ceil_div(L, 256), 256, s, (const int4*)out.leaf_origin,
+         leaf_inrun, leaf_box, (const i64*)vox_part, gran, (const i64*)gvb, out.leaf_offset, bbox_accum, B, R, L);
   launch("k_write_headers", k_write_headers_gvb, ceil_div((i64)B, 4), 256, s, grid_info, (const i64*)gvb,
          (const int32_t*)bbox_accum, B, R, out.headers);
 }

@@ -84,6 +84,9 @@ def bind(path: str):
     lib.oracle_build_masked_refine.restype = ctypes.c_int
     lib.oracle_build_masked_refine.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                                                ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(ctypes.c_void_p)]
+    lib.oracle_kernel_map.restype = ctypes.c_int
+    lib.oracle_kernel_map.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_int32, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     lib.oracle_size.restype = ctypes.c_int64
     lib.oracle_size.argtypes = [ctypes.c_void_p, ctypes.c_int]
     lib.oracle_copy.restype = ctypes.c_int
@@ -154,3 +157,37 @@ def run(op, factor: int, ijk: np.ndarray, offsets: np.ndarray, fields=None, lib=
     if st != OK:
         raise OracleError(st)
     return _collect(lib, handle, fields)
+
+
+def member_offsets(result: dict) -> np.ndarray:
+    """Member row offsets of a result's enumeration, from its headers."""
+    h = result["headers"]
+    return np.concatenate([h[:, 9], [h[-1, 9] + h[-1, 8]]]).astype(np.int64)
+
+
+def kernel_map_rows(src_ijk, src_off, dst_ijk, dst_off, kernel: int, stride: int, transposed: bool,
+                    lib=None) -> np.ndarray:
+    """Kernel map (int32 [V_dst, K^3], -1 where no source voxel) between two batches
+    given as canonical enumerations: ijk rows and member row offsets."""
+    lib = lib or _load()
+    src_ijk = np.ascontiguousarray(np.asarray(src_ijk, dtype=np.int32).reshape(-1, 3))
+    dst_ijk = np.ascontiguousarray(np.asarray(dst_ijk, dtype=np.int32).reshape(-1, 3))
+    src_off = np.ascontiguousarray(np.asarray(src_off, dtype=np.int64))
+    dst_off = np.ascontiguousarray(np.asarray(dst_off, dtype=np.int64))
+    if src_off.shape != dst_off.shape:
+        raise ValueError("source and target member counts differ")
+    kk = int(kernel) ** 3
+    out = np.empty((dst_ijk.shape[0], kk), dtype=np.int32)
+    st = lib.oracle_kernel_map(src_ijk.ctypes.data if src_ijk.size else None, src_off.ctypes.data,
+                               dst_ijk.ctypes.data if dst_ijk.size else None, dst_off.ctypes.data,
+                               int(src_off.shape[0]) - 1, int(kernel), int(stride), int(bool(transposed)),
+                               out.ctypes.data if out.size else None)
+    if st != OK:
+        raise OracleError(st)
+    return out
+
+
+def kernel_map(src: dict, dst: dict, kernel: int, stride: int, transposed: bool, **kw) -> np.ndarray:
+    """Kernel map between two oracle results (each holding "ijk" and "headers")."""
+    return kernel_map_rows(src["ijk"], member_offsets(src), dst["ijk"], member_offsets(dst), kernel, stride,
+                           transposed, **kw)

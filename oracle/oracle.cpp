@@ -33,6 +33,9 @@
 //      16^3-leaf lower nodes, 32^3-lower upper nodes (one root tile each), parent
 //      links, first-child indices, per-grid counts, leaf voxel offsets and prefix
 //      popcounts, per-grid bounding boxes (PR page section 1, last bullet).
+//   4. kernel maps between two such batches: for every target voxel and kernel
+//      offset, the index of the source voxel it reads (issue page, Measurements;
+//      see oracle_kernel_map for the reading).
 //
 // Readings where the pages are silent (each is listed in the design notes):
 //   * coarsening rounds toward -infinity; refinement anchors at f*v;
@@ -47,6 +50,7 @@
 //   * any output coordinate outside int32 rejects the whole call (status 2).
 #include <algorithm>
 #include <array>
+#include <map>
 #include <cstdint>
 #include <cstring>
 #include <new>
@@ -406,6 +410,63 @@ int oracle_build_masked_refine(int factor, const int32_t* ijk, const int64_t* of
   } catch (const std::bad_alloc&) {
     return ST_NOMEM;
   }
+}
+
+
+// Kernel map between a source and a target batch with the same member count.
+// The issue page ("Generated-topology grid construction dominates per-iteration
+// ConvolutionPlan cost", Measurements) names two kernel-map builds of a plan: a
+// k3 s1 map on one topology and the k2s2 transposed-conv map. It gives neither
+// their layout nor their offset order; reading: one row per target voxel, one
+// column per kernel offset d in O_K^3 with O_K = [-floor((K-1)/2), floor(K/2)]
+// (the offset box of the kernel-K targets above), columns x-major over d. For
+// target voxel o of member g the entry is the index of the source voxel of
+// member g at
+//   conv:            S*o + d
+//   transposed conv: (o - d) / S   when S divides every component of o - d,
+// or -1 when there is none. Both batches are given as their canonical
+// enumerations (ijk rows, member offsets); an index is a row of src_ijk.
+// Returns 1 for invalid arguments, 2 when a source index would leave int32.
+int oracle_kernel_map(const int32_t* src_ijk, const int64_t* src_off, const int32_t* dst_ijk,
+                      const int64_t* dst_off, int32_t B, int K, int S, int transposed, int32_t* out) {
+  if (B < 1 || !src_off || !dst_off || K < 1 || K > 8 || S < 1 || (transposed != 0 && transposed != 1))
+    return ST_INVALID;
+  if (src_off[0] != 0 || dst_off[0] != 0) return ST_INVALID;
+  for (int g = 0; g < B; ++g)
+    if (src_off[g + 1] < src_off[g] || dst_off[g + 1] < dst_off[g]) return ST_INVALID;
+  if ((src_off[B] > 0 && !src_ijk) || (dst_off[B] > 0 && (!dst_ijk || !out))) return ST_INVALID;
+  if (src_off[B] > (i64)INT32_MAX) return ST_OVERFLOW;
+  const i64 lo = -((K - 1) / 2);
+  const i64 kk = (i64)K * K * K;
+  try {
+    for (int g = 0; g < B; ++g) {
+      std::map<std::array<i64, 3>, i64> index;  // this member's source voxels
+      for (i64 i = src_off[g]; i < src_off[g + 1]; ++i)
+        index[{src_ijk[3 * i], src_ijk[3 * i + 1], src_ijk[3 * i + 2]}] = i;
+      for (i64 j = dst_off[g]; j < dst_off[g + 1]; ++j) {
+        const i64 o[3] = {dst_ijk[3 * j], dst_ijk[3 * j + 1], dst_ijk[3 * j + 2]};
+        for (i64 k = 0; k < kk; ++k) {
+          const i64 d[3] = {lo + k / (K * K), lo + (k / K) % K, lo + k % K};
+          std::array<i64, 3> c{};
+          bool exact = true;
+          for (int a = 0; a < 3; ++a) {
+            if (transposed) {
+              const i64 q = o[a] - d[a];
+              if (floormod(q, S) != 0) exact = false;
+              c[a] = floordiv(q, S);
+            } else {
+              c[a] = (i64)S * o[a] + d[a];
+            }
+          }
+          const auto it = exact ? index.find(c) : index.end();
+          out[j * kk + k] = it == index.end() ? -1 : (int32_t)it->second;
+        }
+      }
+    }
+  } catch (const std::bad_alloc&) {
+    return ST_NOMEM;
+  }
+  return ST_OK;
 }
 
 }  // extern "C"

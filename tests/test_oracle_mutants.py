@@ -48,6 +48,14 @@ MUTANTS = {
     "conv_s1 leans the wrong way": ("case OP_CONV_S1: box(-(factor / 2), (factor - 1) / 2, in); break;",
                                     "case OP_CONV_S1: box(-((factor - 1) / 2), factor / 2, in); break;"),
     "masked refine inverts the mask": ("        if (keep[j])\n", "        if (!keep[j])\n"),
+    "kernel map transposed sign": ("const i64 q = o[a] - d[a];", "const i64 q = o[a] + d[a];"),
+    "kernel map offsets z-major": ("const i64 d[3] = {lo + k / (K * K), lo + (k / K) % K, lo + k % K};",
+                                   "const i64 d[3] = {lo + k % K, lo + (k / K) % K, lo + k / (K * K)};"),
+    "kernel map box leans": ("const i64 lo = -((K - 1) / 2);\n  const i64 kk", "const i64 lo = -(K / 2);\n  const i64 kk"),
+    "kernel map stride dropped": ("c[a] = (i64)S * o[a] + d[a];", "c[a] = o[a] + d[a];"),
+    "kernel map inexact division kept": ("              if (floormod(q, S) != 0) exact = false;\n", ""),
+    "kernel map members mix": ("for (i64 i = src_off[g]; i < src_off[g + 1]; ++i)\n        index[",
+                               "for (i64 i = 0; i < src_off[B]; ++i)\n        index["),
     "conv_t_s1 box one short": ("case OP_CONV_T_S1: box(-((factor - 1) / 2), factor / 2, in); break;",
                                 "case OP_CONV_T_S1: box(-((factor - 1) / 2), (factor - 1) / 2, in); break;"),
 }
@@ -69,6 +77,10 @@ BATTERY = [
     functools.partial(pins.test_invariants_config1, "dilate", 1),
     pins.test_invariants_random_sets,
     pins.test_overflow_and_limits,
+    pins.test_golden_kernel_map,
+    functools.partial(pins.test_kernel_map_bruteforce, 2, 1, True),
+    functools.partial(pins.test_kernel_map_bruteforce, 3, 2, False),
+    functools.partial(pins.test_kernel_map_bruteforce, 3, 2, True),
 ]
 
 
@@ -89,6 +101,7 @@ def test_planted_mistake_is_caught(name, source, tmp_path, monkeypatch):
     lib = oracle.bind(str(so))
     monkeypatch.setattr(oracle, "run", functools.partial(oracle.run, lib=lib))
     monkeypatch.setattr(oracle, "run_masked_refine", functools.partial(oracle.run_masked_refine, lib=lib))
+    monkeypatch.setattr(oracle, "kernel_map_rows", functools.partial(oracle.kernel_map_rows, lib=lib))
     failures = []
     for check in BATTERY:
         try:

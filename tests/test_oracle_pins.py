@@ -570,3 +570,180 @@ def test_golden_tree_worked_example():
     assert res["upper_origin"].shape[0] == len([r for r in rows if r[0] == "upper"])
     assert res["lower_origin"].shape[0] == len([r for r in rows if r[0] == "lower"])
     assert res["leaf_origin"].shape[0] == len([r for r in rows if r[0] == "leaf"])
+
+
+# ---------------------------------------------------------------- kernel maps
+# Issue page, Measurements: a plan builds a k3 s1 kernel map on one topology and
+# a k2s2 transposed-conv kernel map. Reading (the pages fix no layout): row j =
+# target voxel j in canonical order, column k = x-major offset d in O_K^3, entry
+# = source index at S*o + d (conv) or (o - d)/S when exact (transposed), else -1.
+def kmap_column(d, k):
+    lo = -((k - 1) // 2)
+    return ((d[0] - lo) * k + (d[1] - lo)) * k + (d[2] - lo)
+
+
+def kmap_bruteforce(src, dst, k, s, transposed):
+    """Pairwise form: for every (target, source) pair of one member, solve for the
+    offset that relates them and keep it when it lies in the kernel's box."""
+    lo, hi = -((k - 1) // 2), k // 2
+    sh, dh = src["headers"], dst["headers"]
+    out = np.full((dst["ijk"].shape[0], k ** 3), -1, dtype=np.int64)
+    for g in range(sh.shape[0]):
+        srows = range(sh[g, 9], sh[g, 9] + sh[g, 8])
+        for j in range(dh[g, 9], dh[g, 9] + dh[g, 8]):
+            o = [int(c) for c in dst["ijk"][j]]
+            for i in srows:
+                v = [int(c) for c in src["ijk"][i]]
+                d = [o[a] - s * v[a] for a in range(3)] if transposed else [v[a] - s * o[a] for a in range(3)]
+                if all(lo <= c <= hi for c in d):
+                    col = kmap_column(d, k)
+                    assert out[j, col] == -1
+                    out[j, col] = i
+    return out
+
+
+KMAP_CASES = [(3, 1, False), (3, 1, True), (2, 1, False), (2, 1, True), (2, 2, False), (2, 2, True),
+              (3, 2, False), (3, 2, True), (4, 1, False), (5, 1, True), (1, 1, False), (4, 2, True)]
+
+
+@pytest.mark.parametrize("k,s,transposed", KMAP_CASES)
+def test_kernel_map_bruteforce(k, s, transposed):
+    rng = np.random.default_rng(700 + KMAP_CASES.index((k, s, transposed)))
+    centres = CENTRES[:-1]
+    for trial in range(2):
+        src_sets = random_sets(rng, 3, 12, centres)
+        src_sets[2] = set() if trial == 0 else src_sets[2]
+        src = _run_sets("identity", 1, src_sets)
+        # targets: the op's own output, and an unrelated set near the same places
+        if s == 1:
+            dst = _run_sets("conv_t_s1" if transposed else "conv_s1", k, src_sets)
+        else:
+            dst = _run_sets("refine" if transposed else "coarsen", 2, src_sets)
+        other = _run_sets("identity", 1, random_sets(rng, 3, 12, centres))
+        for d in (dst, other):
+            got = oracle.kernel_map(src, d, k, s, transposed)
+            assert got.shape == (d["ijk"].shape[0], k ** 3)
+            np.testing.assert_array_equal(got, kmap_bruteforce(src, d, k, s, transposed))
+
+
+def test_golden_kernel_map():
+    rows = _read_golden("kernel_map_tiny.txt")
+    cases = []
+    for r in rows:
+        if r[0] == "case":
+            cases.append({"name": r[1], "k": int(r[2]), "s": int(r[3]), "t": bool(int(r[4])),
+                          "src": [], "dst": [], "entries": []})
+        elif r[0] in ("src", "dst"):
+            cases[-1][r[0]].append([int(v) for v in r[1:]])
+        elif r[0] == "entry":
+            cases[-1]["entries"].append([int(v) for v in r[1:]])
+    assert len(cases) == 10
+    for c in cases:
+        def rows_of(tag):
+            m = max([v[0] for v in c["src"] + c["dst"]]) + 1
+            members = [np.array([v[1:] for v in c[tag] if v[0] == g], np.int32).reshape(-1, 3) for g in range(m)]
+            ijk, off = synth.concat_members(members)
+            # the fixture lists each member in canonical order already
+            res = oracle.run("identity", 1, ijk, off)
+            assert res["ijk"].tolist() == ijk.tolist(), (c["name"], tag)
+            return ijk, off
+        s_ijk, s_off = rows_of("src")
+        d_ijk, d_off = rows_of("dst")
+        got = oracle.kernel_map_rows(s_ijk, s_off, d_ijk, d_off, c["k"], c["s"], c["t"])
+        exp = np.full((d_ijk.shape[0], c["k"] ** 3), -1, dtype=np.int32)
+        for j, col, v in c["entries"]:
+            exp[j, col] = v
+        np.testing.assert_array_equal(got, exp, err_msg=c["name"])
+
+
+KMAP_OPS = [("conv_s1", 3, 3, 1, False), ("conv_s1", 2, 2, 1, False), ("conv_s1", 5, 5, 1, False),
+            ("conv_t_s1", 2, 2, 1, True), ("conv_t_s1", 4, 4, 1, True), ("dilate", 1, 3, 1, False),
+            ("dilate", 1, 3, 1, True), ("coarsen", 2, 2, 2, False), ("refine", 2, 2, 2, True),
+            ("conv_t_k3s2", 2, 3, 2, True)]
+
+
+@pytest.mark.parametrize("op,f,k,s,transposed", KMAP_OPS)
+def test_kernel_map_support_is_the_generated_target(op, f, k, s, transposed):
+    """The generated target of a conv is exactly the set of outputs that read at
+    least one input: built against a larger target (its dilation), the rows with
+    an entry are the target's voxels, and every source voxel is read somewhere."""
+    rng = np.random.default_rng(900 + KMAP_OPS.index((op, f, k, s, transposed)))
+    sets = random_sets(rng, 3, 15, CENTRES[:-1])
+    src = _run_sets("identity", 1, sets)
+    tgt = _run_sets(op, f, sets)
+    tgt_sets = _grid_sets(tgt)
+    big = _run_sets("dilate", 1, tgt_sets)
+    m = oracle.kernel_map(src, big, k, s, transposed)
+    hdr = big["headers"]
+    for g in range(hdr.shape[0]):
+        b, n = hdr[g, 9], hdr[g, 8]
+        rows = big["ijk"][b:b + n]
+        read = (m[b:b + n] >= 0).any(axis=1)
+        assert set(map(tuple, rows[read].tolist())) == tgt_sets[g], (op, g)
+    m_t = oracle.kernel_map(src, tgt, k, s, transposed)
+    assert (m_t >= 0).any(axis=1).all()
+    assert set(m_t[m_t >= 0].tolist()) == set(range(src["ijk"].shape[0]))
+
+
+def test_kernel_map_coarsen_and_refine_counts():
+    rng = np.random.default_rng(950)
+    sets = random_sets(rng, 4, 40, CENTRES[:-1])
+    src = _run_sets("identity", 1, sets)
+    n = src["ijk"].shape[0]
+    # k2s2 conv onto coarsen x2: every source voxel is read exactly once
+    co = _run_sets("coarsen", 2, sets)
+    m = oracle.kernel_map(src, co, 2, 2, False)
+    assert sorted(m[m >= 0].tolist()) == list(range(n))
+    # k2s2 transposed conv onto refine x2: one entry per row, at column p mod 2
+    # (x-major), naming the voxel p // 2 of the same member
+    fine = _run_sets("refine", 2, sets)
+    mt = oracle.kernel_map(src, fine, 2, 2, True)
+    assert ((mt >= 0).sum(axis=1) == 1).all()
+    index = {}
+    sh = src["headers"]
+    for g in range(sh.shape[0]):
+        for i in range(sh[g, 9], sh[g, 9] + sh[g, 8]):
+            index[(g,) + tuple(int(c) for c in src["ijk"][i])] = i
+    fh = fine["headers"]
+    for g in range(fh.shape[0]):
+        for j in range(fh[g, 9], fh[g, 9] + fh[g, 8]):
+            p = [int(c) for c in fine["ijk"][j]]
+            col = (p[0] % 2) * 4 + (p[1] % 2) * 2 + (p[2] % 2)
+            assert mt[j, col] == index[(g, p[0] // 2, p[1] // 2, p[2] // 2)]
+    assert mt.shape[0] == 8 * n
+
+
+@pytest.mark.parametrize("k,s", [(2, 1), (3, 1), (2, 2), (3, 2), (4, 2)])
+def test_kernel_map_conv_and_transpose_are_dual(k, s):
+    """conv(A -> B)[o, d] = i exactly when transposed(B -> A)[i, d] = o."""
+    rng = np.random.default_rng(980 + 10 * k + s)
+    a = _run_sets("identity", 1, random_sets(rng, 2, 25, CENTRES[:-1]))
+    b = _run_sets("coarsen" if s == 2 else "dilate", 2 if s == 2 else 1, _grid_sets(a))
+    fwd = oracle.kernel_map(a, b, k, s, False)
+    bwd = oracle.kernel_map(b, a, k, s, True)
+    pairs_f = {(int(o), int(d), int(fwd[o, d])) for (o, d) in zip(*np.nonzero(fwd >= 0))}
+    pairs_b = {(int(bwd[i, d]), int(d), int(i)) for (i, d) in zip(*np.nonzero(bwd >= 0))}
+    assert len(pairs_f) > 0
+    assert pairs_f == pairs_b
+
+
+def test_kernel_map_same_topology_symmetry():
+    rng = np.random.default_rng(990)
+    g = _run_sets("identity", 1, random_sets(rng, 3, 30, CENTRES[:-1]))
+    m = oracle.kernel_map(g, g, 3, 1, False)
+    n = g["ijk"].shape[0]
+    assert m[:, 13].tolist() == list(range(n))
+    for j, c in zip(*np.nonzero(m >= 0)):
+        assert m[m[j, c], 26 - c] == j
+
+
+def test_kernel_map_invalid_args():
+    r = _run_sets("identity", 1, [{(0, 0, 0)}])
+    r2 = _run_sets("identity", 1, [{(0, 0, 0)}, {(1, 1, 1)}])
+    for k, s, t in [(0, 1, False), (9, 1, False), (3, 0, False)]:
+        with pytest.raises(oracle.OracleError) as e:
+            oracle.kernel_map(r, r, k, s, t)
+        assert e.value.status == oracle.INVALID
+    with pytest.raises((oracle.OracleError, ValueError)):
+        oracle.kernel_map_rows(r["ijk"], oracle.member_offsets(r), r2["ijk"], oracle.member_offsets(r2), 3, 1,
+                               False)

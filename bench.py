@@ -12,8 +12,8 @@ timed steps. `roofline` reports the dominant kernel's algorithmic bytes per
 launch over its HIP-event-timed average duration; `cpu_baseline` times the CPU
 oracle on whole steps of the same workload. Outside the timed steps the line
 also carries per-op medians (`ops`), the stride-1 kernel-K targets and masked
-refine (`more_ops`), the ijk front-end (`from_ijk`) and the 46M-voxel batch
-(`large`).
+refine (`more_ops`), the ijk front-end (`from_ijk`), the plan's kernel maps
+(`kernel_maps`) and the 46M-voxel batch (`large`).
 """
 from __future__ import annotations
 
@@ -173,6 +173,42 @@ def time_from_ijk(binding, torch, np, d_ijk, off, reps):
             "algorithmic_bytes": byts, "achieved_GBs": byts / (m * 1e-3) / 1e9}
 
 
+def time_kernel_maps(binding, torch, np, src, reps):
+    """The two kernel maps a plan builds (issue page, Measurements): k3 s1 on the
+    source's own topology and k2s2 transposed conv onto refine x2. Output tables
+    are allocated once, outside the timing. Algorithmic bytes of one
+    k_kernel_map launch: the table it writes (4 B per entry) plus one read of
+    every target leaf (origin, mask, offset: 88 B) and source leaf (mask,
+    prefix, offset: 80 B)."""
+    fine = binding.tc_build_batched_topology(src, "refine", 2)
+    res = {}
+    for name, dst, k, s, t in [("k3s1_same_topology", src, 3, 1, False), ("k2s2_transposed_onto_refine", fine, 2, 2, True)]:
+        rows = dst.voxel_total()
+        out = torch.empty((rows, k ** 3), dtype=torch.int32, device="cuda")
+        binding.tc_build_kernel_map(src, dst, k, s, t, out=out)  # warm-up
+        torch.cuda.synchronize()
+        binding.tc_profile_enable("k_kernel_map")
+        ms = []
+        for _ in range(reps):
+            torch.cuda.synchronize()
+            a = time.perf_counter()
+            binding.tc_build_kernel_map(src, dst, k, s, t, out=out)
+            torch.cuda.synchronize()
+            ms.append((time.perf_counter() - a) * 1e3)
+        k_ms, k_n = binding.tc_profile_read("k_kernel_map")
+        binding.tc_profile_disable()
+        entries = rows * k ** 3
+        byts = 4 * entries + 88 * int(dst.leaf_count) + 80 * int(src.leaf_count)
+        avg = k_ms / max(k_n, 1)
+        res[name] = {"ms_median": float(np.median(ms)), "kernel_avg_ms": avg, "rows": int(rows),
+                     "entries": int(entries), "valid_entries": int((out >= 0).sum().item()),
+                     "algorithmic_bytes": byts, "achieved_GBs": byts / (avg * 1e-3) / 1e9,
+                     "frac_of_peak": byts / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        del out
+    del fine
+    return res
+
+
 def measure_large(binding, torch, np, synth):
     """64 shells at res 512 + 8 solid 128^3 cubes: per-op pass / enumeration time
     and per-kernel HIP-event timing against the HBM peak."""
@@ -220,6 +256,7 @@ def measure_large(binding, torch, np, synth):
         res["ops"][f"{op}x{f}"] = {"ms_pass_median": pm, "ms_enumerate_median": float(np.median(enum_ms)),
                                    "output_voxels": V, "output_leaves": L,
                                    "output_voxels_per_s_pass": V / (pm * 1e-3), "kernels": kern}
+    res["kernel_maps"] = time_kernel_maps(binding, torch, np, src, 3)
     return res
 
 
@@ -330,7 +367,8 @@ def main():
         "config": {"workload": synth.CONFIG_NAMES[args.config], "grids": int(len(off) - 1),
                    "input_voxels": int(off[-1]), "ops": [f"{o}x{f}" for o, f in STEP_OPS]},
         "roofline": roofline, "cpu_baseline": cpu, "ops": ops, "b48": b48, "more_ops": extra,
-        "from_ijk": time_from_ijk(binding, torch, np, d_ijk, off, 20), "large": large,
+        "from_ijk": time_from_ijk(binding, torch, np, d_ijk, off, 20),
+        "kernel_maps": time_kernel_maps(binding, torch, np, src, 20), "large": large,
     }
     print(json.dumps(rec), flush=True)
     copy_calibration(torch, args.copy_mib)

@@ -222,6 +222,31 @@ tc_status tc_batch_voxel_total(const tc_grid_batch* batch, int64_t* h_total, voi
 tc_status tc_enumerate_ijk(const tc_grid_batch* batch, int32_t* d_ijk_out, int64_t capacity,
                            void* stream);
 
+/* Kernel map of a convolution plan between two batches with the same member
+ * count (issue page "Generated-topology grid construction dominates
+ * per-iteration ConvolutionPlan cost", Measurements: a plan builds a k3 s1 map
+ * on one topology and a k2s2 transposed-conv map; the layout is this library's).
+ *   src, dst     source (input) and target (output) batches; read only.
+ *   kernel_size  K in [1, 8]; offsets O_K = [-floor((K-1)/2), floor(K/2)] per
+ *                axis, the same offset box as TC_OP_CONV_S1 / TC_OP_CONV_T_S1.
+ *   stride       S in {1, 2} (others: TC_ERR_UNSUPPORTED).
+ *   transposed   0: conv, target o reads source S*o + d;
+ *                1: transposed conv, target o reads source (o - d)/S when S
+ *                divides o - d in every component.
+ *   d_out        device int32[V_dst][K^3]: row j = target voxel j in the order of
+ *                tc_enumerate_ijk(dst), column k = offset d taken x-major,
+ *                k = ((dx-lo)*K + (dy-lo))*K + (dz-lo) with lo = -floor((K-1)/2);
+ *                the entry is the index (in the order of tc_enumerate_ijk(src))
+ *                of the same member's source voxel, or -1. Owned by the caller.
+ *   capacity     int32 entries available at d_out; fewer than V_dst * K^3 is
+ *                TC_ERR_INVALID_ARG (d_out may be NULL only when that is 0).
+ * Different member counts, K outside [1, 8] or S < 1 are TC_ERR_INVALID_ARG; a
+ * source of more than INT32_MAX voxels is TC_ERR_UNSUPPORTED. Blocks on the two
+ * voxel totals (if not yet known), then enqueues two kernels on `stream`. */
+tc_status tc_build_kernel_map(const tc_grid_batch* src, const tc_grid_batch* dst, int32_t kernel_size,
+                              int32_t stride, int32_t transposed, int32_t* d_out, int64_t capacity,
+                              void* stream);
+
 /* Releases the batch's device buffer (through the allocator it was created with,
  * stream-ordered on its creation stream) and the handle. NULL is ignored. */
 void tc_batch_free(tc_grid_batch* batch);

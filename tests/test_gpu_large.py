@@ -96,3 +96,89 @@ def test_large_refine_coarsen_roundtrip(big):
     fa, fb = gpu_fields(src), gpu_fields(back)
     for k in fa:
         assert np.array_equal(fa[k], fb[k]), k
+
+
+# ---------------------------------------------------------------- kernel maps
+# Issue page "Generated-topology grid construction dominates per-iteration
+# ConvolutionPlan cost", Measurements: the k3 s1 same-topology map and the k2s2
+# transposed-conv map. At full size: sampled members against the oracle, and on
+# every row, properties that fix each entry given the enumerations (which the
+# tests above pin): an entry names the voxel at o + d (or (o - d)/2), every
+# refine row has exactly one entry, at column o mod 2, every source voxel is
+# read by exactly 8 refine rows, and the k3 s1 map is its own mirror.
+def _offsets_of_columns(k, device):
+    import torch
+    lo = -((k - 1) // 2)
+    c = torch.arange(k ** 3, device=device)
+    return torch.stack([c // (k * k), (c // k) % k, c % k], 1).to(torch.int32) + lo
+
+
+def test_large_kernel_map_k3s1_same_topology(big):
+    import torch
+    from topology_construction_amd import binding
+    ijk, off, src = big
+    print("[large] kernel map k3 s1", flush=True)
+    m = binding.tc_build_kernel_map(src, src, 3, 1, False)
+    e = binding.tc_enumerate_ijk(src)
+    h = binding.tc_batch_read_headers(src)
+    n = e.shape[0]
+    assert tuple(m.shape) == (n, 27)
+    assert torch.equal(m[:, 13], torch.arange(n, device=m.device, dtype=torch.int32))
+    d = _offsets_of_columns(3, m.device)
+    for c0 in range(0, n, 1 << 22):
+        blk = m[c0:c0 + (1 << 22)].long()
+        rows = torch.arange(c0, c0 + blk.shape[0], device=m.device)
+        ok = blk >= 0
+        j, col = torch.nonzero(ok, as_tuple=True)
+        tgt = blk[j, col]
+        assert torch.equal(e[tgt], e[rows[j]] + d[col]), "entry names the wrong voxel"
+        assert torch.equal(m[tgt, 26 - col].long(), rows[j]), "k3 s1 map is not its own mirror"
+    for g in SHELLS:
+        mi, mo = _member_input(ijk, off, g)
+        print(f"[large]   oracle kernel map member {g} ({mi.shape[0]} voxels)", flush=True)
+        r = oracle.run("identity", 1, mi, mo, fields=["headers", "ijk"])
+        ref = oracle.kernel_map(r, r, 3, 1, False)
+        vb, nv = int(h["voxel_begin"][g]), int(h["voxel_count"][g])
+        got = m[vb:vb + nv].cpu().numpy().astype(np.int64)
+        got[got >= 0] -= vb
+        assert np.array_equal(got, ref), f"member {g}"
+    del m
+    torch.cuda.synchronize()
+
+
+def test_large_kernel_map_k2s2_transposed_onto_refine(big):
+    import torch
+    from topology_construction_amd import binding
+    ijk, off, src = big
+    print("[large] kernel map k2s2 transposed onto refine x2", flush=True)
+    fine = binding.tc_build_batched_topology(src, "refine", 2)
+    m = binding.tc_build_kernel_map(src, fine, 2, 2, True)
+    es = binding.tc_enumerate_ijk(src)
+    ef = binding.tc_enumerate_ijk(fine)
+    n = ef.shape[0]
+    assert tuple(m.shape) == (n, 8) and n == 8 * es.shape[0]
+    reads = torch.zeros(es.shape[0], dtype=torch.int64, device=m.device)
+    for c0 in range(0, n, 1 << 24):
+        blk = m[c0:c0 + (1 << 24)].long()
+        p = ef[c0:c0 + blk.shape[0]]
+        assert torch.equal((blk >= 0).sum(1), torch.ones(blk.shape[0], dtype=torch.int64, device=m.device))
+        col = ((p[:, 0] & 1) * 4 + (p[:, 1] & 1) * 2 + (p[:, 2] & 1)).long()
+        v = blk.gather(1, col[:, None])[:, 0]
+        assert bool((v >= 0).all()), "entry not at column o mod 2"
+        assert torch.equal(es[v], p >> 1), "entry is not the parent voxel"
+        reads += torch.bincount(v, minlength=es.shape[0])
+    assert bool((reads == 8).all())
+    h = binding.tc_batch_read_headers(fine)
+    hs = binding.tc_batch_read_headers(src)
+    g = SHELLS[0]
+    mi, mo = _member_input(ijk, off, g)
+    print(f"[large]   oracle kernel map member {g}", flush=True)
+    rs = oracle.run("identity", 1, mi, mo, fields=["headers", "ijk"])
+    rf = oracle.run("refine", 2, mi, mo, fields=["headers", "ijk"])
+    ref = oracle.kernel_map(rs, rf, 2, 2, True)
+    vb, nv = int(h["voxel_begin"][g]), int(h["voxel_count"][g])
+    got = m[vb:vb + nv].cpu().numpy().astype(np.int64)
+    got[got >= 0] -= int(hs["voxel_begin"][g])
+    assert np.array_equal(got, ref)
+    del m, fine
+    torch.cuda.synchronize()

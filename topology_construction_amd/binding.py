@@ -27,7 +27,7 @@ OPS = {"coarsen": 1, "refine": 2, "dilate": 3, "pad_neg": 4, "pad_pos": 5, "conv
 ABI_SYMBOLS = [
     "tc_abi_version", "tc_status_string", "tc_last_error", "tc_batch_from_ijk",
     "tc_build_batched_topology", "tc_build_masked_refine", "tc_batch_get_info", "tc_batch_read_headers",
-    "tc_batch_voxel_total", "tc_enumerate_ijk", "tc_batch_free", "tc_profile_enable",
+    "tc_batch_voxel_total", "tc_enumerate_ijk", "tc_build_kernel_map", "tc_batch_free", "tc_profile_enable",
     "tc_profile_read", "tc_profile_disable",
 ]
 
@@ -125,6 +125,8 @@ def load_library(path: str = LIB_PATH):
         lib.tc_batch_voxel_total.argtypes = [vp, ctypes.POINTER(i64), vp]
         lib.tc_enumerate_ijk.restype = ctypes.c_int
         lib.tc_enumerate_ijk.argtypes = [vp, vp, i64, vp]
+        lib.tc_build_kernel_map.restype = ctypes.c_int
+        lib.tc_build_kernel_map.argtypes = [vp, vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, i64, vp]
         lib.tc_batch_free.restype = None
         lib.tc_batch_free.argtypes = [vp]
         lib.tc_profile_enable.restype = ctypes.c_int
@@ -283,6 +285,22 @@ def tc_enumerate_ijk(batch: GridBatch, out=None, stream=None):
     _check(lib.tc_enumerate_ijk(batch.handle, ctypes.c_void_p(out.data_ptr() if out.numel() else 0), int(cap),
                                 _stream_handle(stream)))
     return out[:total]
+
+
+def tc_build_kernel_map(src: GridBatch, dst: GridBatch, kernel_size: int, stride: int, transposed: bool,
+                        out=None, stream=None):
+    """Kernel map int32 [V_dst, K^3]: for target voxel j and x-major offset k, the
+    index of the source voxel it reads (S*o + d, or (o - d)/S transposed), or -1."""
+    import torch
+    lib = load_library()
+    kk = int(kernel_size) ** 3
+    rows = dst.voxel_total(stream)
+    if out is None:
+        out = torch.empty((rows, kk), dtype=torch.int32, device="cuda")
+    _check(lib.tc_build_kernel_map(src.handle, dst.handle, int(kernel_size), int(stride), int(bool(transposed)),
+                                   ctypes.c_void_p(out.data_ptr() if out.numel() else 0), int(out.numel()),
+                                   _stream_handle(stream)))
+    return out.view(-1)[:rows * kk].view(rows, kk)
 
 
 def tc_batch_read_headers(batch: GridBatch, stream=None) -> np.ndarray:

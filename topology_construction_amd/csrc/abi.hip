@@ -356,6 +356,31 @@ tc_status tc_enumerate_ijk(const tc_grid_batch* b, int32_t* d_ijk_out, int64_t c
   });
 }
 
+tc_status tc_build_kernel_map(const tc_grid_batch* src, const tc_grid_batch* dst, int32_t kernel_size,
+                              int32_t stride, int32_t transposed, int32_t* d_out, int64_t capacity,
+                              void* stream) {
+  if (!src || !dst) return fail(TC_ERR_INVALID_ARG, "batch is NULL");
+  if (src->B != dst->B) return fail(TC_ERR_INVALID_ARG, "source and target member counts differ");
+  if (kernel_size < 1 || kernel_size > 8) return fail(TC_ERR_INVALID_ARG, "kernel_size must be in [1, 8]");
+  if (stride < 1) return fail(TC_ERR_INVALID_ARG, "stride must be positive");
+  if (stride > 2) return fail(TC_ERR_UNSUPPORTED, "stride must be 1 or 2");
+  if (transposed != 0 && transposed != 1) return fail(TC_ERR_INVALID_ARG, "transposed must be 0 or 1");
+  return guarded([&]() {
+    hipStream_t s = (hipStream_t)stream;
+    const int64_t n_src = tc::read_voxel_total(src, s);
+    if (n_src > (int64_t)INT32_MAX) throw tc::Error(TC_ERR_UNSUPPORTED, "source voxel indices exceed int32");
+    const int64_t kk = (int64_t)kernel_size * kernel_size * kernel_size;
+    const int64_t need = tc::read_voxel_total(dst, s) * kk;
+    if (need == 0) return TC_OK;
+    if (!d_out) throw tc::Error(TC_ERR_INVALID_ARG, "d_out is NULL");
+    if (capacity < need)
+      throw tc::Error(TC_ERR_INVALID_ARG,
+                      "capacity " + std::to_string(capacity) + " < " + std::to_string(need) + " entries");
+    tc::kernel_map(src->view(), dst->view(), kernel_size, stride, transposed, d_out, s);
+    return TC_OK;
+  });
+}
+
 void tc_batch_free(tc_grid_batch* b) {
   try {
     tc::free_batch(b);

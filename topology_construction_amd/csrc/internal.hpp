@@ -179,6 +179,18 @@ inline void launch(const char* name, Kernel kernel, i64 blocks, int threads, hip
   prof_after(name, s);
 }
 
+// As launch(), with `lds_bytes` of dynamic shared memory.
+template <typename Kernel, typename... Args>
+inline void launch_lds(const char* name, Kernel kernel, i64 blocks, int threads, size_t lds_bytes, hipStream_t s,
+                       Args... args) {
+  if (blocks <= 0) return;
+  if (blocks > 0x7fffffffLL) throw Error(TC_ERR_UNSUPPORTED, std::string(name) + ": grid too large");
+  prof_before(name, s);
+  hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(threads), lds_bytes, s, args...);
+  hip_check(hipGetLastError(), name);
+  prof_after(name, s);
+}
+
 inline i64 ceil_div(i64 a, i64 b) { return (a + b - 1) / b; }
 
 // ------------------------------------------------------------------ primitives (primitives.hip)
@@ -302,6 +314,9 @@ namespace tc {
 tc_grid_batch* new_batch(int32_t B, const int32_t* readback, const OutAlloc& oa);
 void free_batch(tc_grid_batch* b);
 tc_grid_batch* copy_batch(const tc_grid_batch* src, const OutAlloc& oa);  // same counts, one D2D copy
+// Kernel map of `dst` against `src` (same member count): out int32[V_dst][K^3].
+void kernel_map(const GridView& src, const GridView& dst, int K, int S, int transposed, int32_t* out,
+                hipStream_t s);
 
 // The two producers of grid batches.
 tc_grid_batch* build_from_ijk(const int32_t* d_ijk, const int64_t* h_offsets, int32_t B, const OutAlloc& oa);

@@ -164,7 +164,8 @@ def _torch_alloc(ctx, nbytes, stream):
 
 
 def _torch_free(ctx, ptr, nbytes, stream):
-    _live_buffers.pop(int(ptr or 0), None)
+    if _live_buffers is not None:  # None while the interpreter tears the module down
+        _live_buffers.pop(int(ptr or 0), None)
 
 
 _alloc_cb = _ALLOC_FN(_torch_alloc)

@@ -376,7 +376,7 @@ tc_status tc_build_kernel_map(const tc_grid_batch* src, const tc_grid_batch* dst
     if (capacity < need)
       throw tc::Error(TC_ERR_INVALID_ARG,
                       "capacity " + std::to_string(capacity) + " < " + std::to_string(need) + " entries");
-    tc::kernel_map(src->view(), dst->view(), kernel_size, stride, transposed, d_out, s);
+    tc::kernel_map(src->view(), dst->view(), kernel_size, stride, transposed, d_out, need, s);
     return TC_OK;
   });
 }

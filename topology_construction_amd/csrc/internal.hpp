@@ -314,8 +314,9 @@ namespace tc {
 tc_grid_batch* new_batch(int32_t B, const int32_t* readback, const OutAlloc& oa);
 void free_batch(tc_grid_batch* b);
 tc_grid_batch* copy_batch(const tc_grid_batch* src, const OutAlloc& oa);  // same counts, one D2D copy
-// Kernel map of `dst` against `src` (same member count): out int32[V_dst][K^3].
-void kernel_map(const GridView& src, const GridView& dst, int K, int S, int transposed, int32_t* out,
+// Kernel map of `dst` against `src` (same member count): out int32[V_dst][K^3],
+// `entries` = V_dst * K^3.
+void kernel_map(const GridView& src, const GridView& dst, int K, int S, int transposed, int32_t* out, i64 entries,
                 hipStream_t s);
 
 // The two producers of grid batches.

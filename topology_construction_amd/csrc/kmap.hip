@@ -48,6 +48,7 @@ struct KmapGeom {
   int R;           // volume side: 7S + K (conv) or 7 + K (transposed conv)
   int KK;          // K^3 columns
   int q64, r64;    // 64 = q64 * KK + r64
+  int vol_words;   // R^3 rounded up to a multiple of 4
   int wave_words;  // LDS words per wave
 };
 
@@ -100,10 +101,93 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-__global__ void __launch_bounds__(256) k_kernel_map(const int4* t_origin, const u64* t_mask, const i64* t_offset,
+// Source-coordinate region [A0, A1] of target leaf origin o (clamped to int32),
+// the volume's origin F0, and the window of source leaves: L0 + [0, W) per axis.
+struct Region {
+  i64 F0[3], A0[3], A1[3];
+  int L0[3], W[3];
+  bool empty;
+};
+
+__device__ __forceinline__ Region leaf_region(const int4& o, const KmapGeom& gm) {
+  Region r;
+  const int oc[3] = {o.x, o.y, o.z};
+  r.empty = false;
+#pragma unroll
+  for (int a = 0; a < 3; ++a) {
+    if (gm.transposed) {
+      r.F0[a] = (i64)oc[a] - gm.hi;
+      r.A0[a] = -floor_div_s(-r.F0[a], gm.S);  // ceil(F0 / S)
+      r.A1[a] = floor_div_s((i64)oc[a] + 7 - gm.lo, gm.S);
+    } else {
+      r.F0[a] = (i64)gm.S * oc[a] + gm.lo;
+      r.A0[a] = r.F0[a];
+      r.A1[a] = (i64)gm.S * (oc[a] + 7) + gm.hi;
+    }
+    r.A0[a] = imax64(r.A0[a], (i64)INT32_MIN);
+    r.A1[a] = imin64(r.A1[a], (i64)INT32_MAX);
+    r.empty = r.empty || r.A0[a] > r.A1[a];
+  }
+#pragma unroll
+  for (int a = 0; a < 3; ++a) {
+    r.L0[a] = r.empty ? 0 : (int)(r.A0[a] >> 3);
+    r.W[a] = r.empty ? 0 : (int)(r.A1[a] >> 3) - r.L0[a] + 1;
+  }
+  return r;
+}
+
+// One thread per (target leaf, window slot): the source leaf there and the
+// batch-global index of its first voxel, or (-1, 0). `sm` slots per leaf. Also
+// the batch-global index of every target leaf's first voxel (its first row).
+__global__ void __launch_bounds__(256) k_kmap_slots(const int4* t_origin, const i64* t_offset,
                                                     const tc_grid_header* t_hdr, i64 n_leaf, KmapSrc src,
-                                                    KmapGeom gm, int32_t* out, int waves) {
-  extern __shared__ int32_t s_dyn[];
+                                                    KmapGeom gm, int sm, int2* slots, i64* t_first) {
+  const i64 t = (i64)blockIdx.x * 256 + threadIdx.x;
+  if (t >= n_leaf * sm) return;
+  const i64 l = t / sm;
+  const int slot = (int)(t - l * sm);
+  const int4 o = t_origin[l];
+  if (slot == 0) t_first[l] = t_hdr[o.w].voxel_begin + t_offset[l];  // the leaf's first row
+  const Region r = leaf_region(o, gm);
+  int2 e = make_int2(-1, 0);
+  if (slot < r.W[0] * r.W[1] * r.W[2]) {
+    const tc_grid_header& h = src.hdr[o.w];
+    const int ix = slot / (r.W[1] * r.W[2]), iy = (slot / r.W[2]) % r.W[1], iz = slot % r.W[2];
+    const int leaf = find_leaf(src, h.upper_begin, h.upper_count, (r.L0[0] + ix) * 8, (r.L0[1] + iy) * 8,
+                               (r.L0[2] + iz) * 8);
+    if (leaf >= 0) e = make_int2(leaf, (int32_t)(h.voxel_begin + src.leaf_offset[leaf]));
+  }
+  slots[t] = e;
+}
+
+// Per-leaf inputs of the main kernel, loaded one leaf ahead.
+struct LeafIn {
+  int4 o;
+  u64 tword;  // target mask word lane >> 3
+  i64 first;  // batch-global index of the leaf's first row
+  int2 slot;  // window slot `lane` (lanes below sm)
+};
+
+__device__ __forceinline__ LeafIn load_leaf(const int4* t_origin, const u64* t_mask, const i64* t_first,
+                                            const int2* slots, int sm, i64 l, int lane) {
+  LeafIn in;
+  in.o = t_origin[l];
+  in.tword = t_mask[l * 8 + (lane >> 3)];
+  in.first = t_first[l];
+  in.slot = slots[l * sm + min(lane, sm - 1)];  // lanes at or above sm ignore theirs
+  return in;
+}
+
+// Main kernel. Per wave and target leaf, with the next leaf's inputs already in
+// flight: lanes below sm load their slot's source leaf (8 mask words, prefix
+// word) into LDS; the region's active voxels are ranked into the volume; the
+// rows are streamed out. Volume coordinates are small and non-negative, so they
+// are computed exactly in wrapping 32-bit arithmetic even where the region's
+// origin lies outside int32.
+__global__ void __launch_bounds__(256) k_kernel_map(const int4* t_origin, const u64* t_mask, const i64* t_first,
+                                                    i64 n_leaf, KmapSrc src, KmapGeom gm, const int2* slots,
+                                                    int sm, int32_t* out, int waves) {
+  extern __shared__ __align__(16) int32_t s_dyn[];
   const int w = threadIdx.x / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   const int K = gm.K, S = gm.S, R = gm.R, KK = gm.KK;
@@ -117,106 +201,106 @@ __global__ void __launch_bounds__(256) k_kernel_map(const int4* t_origin, const 
     s_koff[k] = (d[0] * R + d[1]) * R + d[2];
   }
   __syncthreads();
+  // per-wave LDS: volume int32[vol_words] (R^3 rounded up to 4), slot masks
+  // u64[sm][8], slot prefixes u64[sm], slot bases int32[sm], row offsets uint16[512]
   int32_t* vol = s_dyn + 512 + w * gm.wave_words;
-  int32_t* s_voff = vol + R * R * R;
-  int32_t* s_leaf = s_voff + 512;
-  int32_t* s_lbase = s_leaf + kKmapMaxSlots;
-  const int v_first = lane / KK, k_first = lane % KK;
+  u64* s_smask = reinterpret_cast<u64*>(vol + gm.vol_words);
+  u64* s_spre = s_smask + 8 * sm;
+  int32_t* s_sbase = reinterpret_cast<int32_t*>(s_spre + sm);
+  uint16_t* s_voff = reinterpret_cast<uint16_t*>(s_sbase + sm);
+  // row streaming: up to 64 columns, lane owns column lane % KK of row lane / KK
+  // (rows_per_it rows per store); wider rows take ceil(KK / 64) stores per row
+  const int rows_per_it = KK <= kWave ? kWave / KK : 1;
+  const bool col_lane = KK <= kWave && lane < rows_per_it * KK;
+  const int my_row = KK <= kWave ? lane / KK : 0;
+  int32_t koff[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int k = KK <= kWave ? lane % KK : lane + kWave * j;
+    koff[j] = k < KK ? s_koff[k] : 0;
+  }
 
-  for (i64 l = (i64)blockIdx.x * waves + w; l < n_leaf; l += (i64)gridDim.x * waves) {  // uniform per wave
-    const int4 o = t_origin[l];
-    const int g = o.w;
-    const u64 tword = t_mask[l * 8 + (lane >> 3)];
-    const int trow = (int)((tword >> (8 * (lane & 7))) & 0xffull);
+  i64 l = (i64)blockIdx.x * waves + w;
+  const i64 stride = (i64)gridDim.x * waves;
+  if (l >= n_leaf) return;  // uniform per wave; no block barrier below
+  LeafIn cur = load_leaf(t_origin, t_mask, t_first, slots, sm, l, lane);
+  for (; l < n_leaf; l += stride) {
+    // this leaf's slot leaves, then the next leaf's inputs. The loads are
+    // unconditional (absent slots read source leaf 0, clamped indices past the
+    // end) so that no branch has to wait for them; selects come at the use.
+    const bool have = lane < sm && cur.slot.x >= 0;
+    const i64 sl = have ? cur.slot.x : 0;
+    u64 m[8];
+    const ulonglong2* mp = reinterpret_cast<const ulonglong2*>(src.leaf_mask + sl * 8);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const ulonglong2 v = mp[q];
+      m[2 * q] = v.x;
+      m[2 * q + 1] = v.y;
+    }
+    const u64 pre = src.leaf_prefix[sl];
+    const i64 ln = l + stride;
+    const LeafIn nxt = load_leaf(t_origin, t_mask, t_first, slots, sm, ln < n_leaf ? ln : l, lane);
+
+    // row voxel offsets (lane owns target row (x, y) = (lane >> 3, lane & 7)) and the empty volume
+    const uint32_t trow = (uint32_t)(cur.tword >> (8 * (lane & 7))) & 0xffu;
     const int tcnt = __popc(trow);
     const int tinc = wave_incl_scan(tcnt);
     const int n = __shfl(tinc, kWave - 1, kWave);
-    const i64 jb = t_hdr[g].voxel_begin + t_offset[l];
-    const int32_t ub = src.hdr[g].upper_begin, uc = src.hdr[g].upper_count;
-    const i64 vb = src.hdr[g].voxel_begin;
-
-    // region of source coordinates [A0, A1] and the volume's fine origin F0
-    i64 F0[3], A0[3], A1[3];
-    const int oc[3] = {o.x, o.y, o.z};
-    bool empty = uc == 0;
-#pragma unroll
-    for (int a = 0; a < 3; ++a) {
-      if (gm.transposed) {
-        F0[a] = (i64)oc[a] - gm.hi;
-        A0[a] = -floor_div_s(-F0[a], S);                      // ceil(F0 / S)
-        A1[a] = floor_div_s((i64)oc[a] + 7 - gm.lo, S);
-      } else {
-        F0[a] = (i64)S * oc[a] + gm.lo;
-        A0[a] = F0[a];
-        A1[a] = (i64)S * (oc[a] + 7) + gm.hi;
-      }
-      A0[a] = imax64(A0[a], (i64)INT32_MIN);
-      A1[a] = imin64(A1[a], (i64)INT32_MAX);
-      empty = empty || A0[a] > A1[a];
-    }
-    int L0[3] = {0, 0, 0}, W[3] = {0, 0, 0};
-    if (!empty) {
-#pragma unroll
-      for (int a = 0; a < 3; ++a) {
-        L0[a] = (int)(A0[a] >> 3);
-        W[a] = (int)(A1[a] >> 3) - L0[a] + 1;
-      }
-    }
-    const int nslots = W[0] * W[1] * W[2];  // <= kKmapMaxSlots for S <= 2, K <= 8
-
-    // 1. the region's source leaves
-    if (lane < nslots) {
-      const int ix = lane / (W[1] * W[2]), iy = (lane / W[2]) % W[1], iz = lane % W[2];
-      const int leaf = find_leaf(src, ub, uc, (L0[0] + ix) * 8, (L0[1] + iy) * 8, (L0[2] + iz) * 8);
-      s_leaf[lane] = leaf;
-      s_lbase[lane] = leaf >= 0 ? (int32_t)(vb + src.leaf_offset[leaf]) : 0;
-    }
-    const int R3 = R * R * R;
-    for (int c = lane; c < R3; c += kWave) vol[c] = -1;
-    // row voxel offsets: lane owns target row (x, y) = (lane >> 3, lane & 7)
     {
-      const int m = gm.transposed ? 1 : S;  // the transposed conv's volume is at the target's resolution
-      const int x = lane >> 3, y = lane & 7;
+      const int mv = gm.transposed ? 1 : S;  // the transposed conv's volume is at the target's resolution
+      const int base = ((mv * (lane >> 3)) * R + mv * (lane & 7)) * R;
       int at = tinc - tcnt;
-      int rest = trow;
+      uint32_t rest = trow;
       while (rest) {
         const int z = __builtin_ctz(rest);
-        s_voff[at++] = ((m * x) * R + m * y) * R + m * z;
+        s_voff[at++] = (uint16_t)(base + mv * z);
         rest &= rest - 1;
       }
     }
+    for (int c = lane; c < (gm.vol_words >> 2); c += kWave)
+      reinterpret_cast<int4*>(vol)[c] = make_int4(-1, -1, -1, -1);
+    if (lane < sm) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) s_smask[lane * 8 + q] = have ? m[q] : 0ull;
+      s_spre[lane] = pre;
+      s_sbase[lane] = cur.slot.y;
+    }
     wave_sync();
 
-    // 2. scatter the region's active source voxels into the volume
-    if (!empty) {
-      const int m = gm.transposed ? S : 1;  // source coordinate -> volume coordinate scale
-      const int nx = (int)(A1[0] - A0[0] + 1), ny = (int)(A1[1] - A0[1] + 1);
-      const int zl0 = (int)(A0[2] >> 3), zl1 = (int)(A1[2] >> 3);
-      for (int r = lane; r < nx * ny; r += kWave) {
-        const int x = (int)(A0[0] + r / ny), y = (int)(A0[1] + r % ny);
-        const int sx = (x >> 3) - L0[0], sy = (y >> 3) - L0[1];
-        const i64 ux = (i64)m * x - F0[0], uy = (i64)m * y - F0[1];
-        const int urow = (int)((ux * R + uy) * R);
-        for (int zl = zl0; zl <= zl1; ++zl) {
-          const int slot = (sx * W[1] + sy) * W[2] + (zl - L0[2]);
-          const int leaf = s_leaf[slot];
-          if (leaf < 0) continue;
-          const u64 word = src.leaf_mask[(i64)leaf * 8 + (x & 7)];
-          const int row = (int)((word >> (8 * (y & 7))) & 0xffull);
-          // z bits of this leaf inside [A0z, A1z]
-          const int lb = (int)(imax64(A0[2], (i64)zl * 8) - (i64)zl * 8);
-          const int hb = (int)(imin64(A1[2], (i64)zl * 8 + 7) - (i64)zl * 8);
-          int bits = row & ((2 << hb) - 1) & ~((1 << lb) - 1);
+    // scatter the region's active source voxels into the volume
+    const Region r = leaf_region(cur.o, gm);
+    if (!r.empty) {
+      const uint32_t ms = gm.transposed ? (uint32_t)S : 1u;  // source coordinate -> volume coordinate scale
+      const int ax0 = (int)r.A0[0], ay0 = (int)r.A0[1], az0 = (int)r.A0[2], az1 = (int)r.A1[2];
+      const uint32_t fx = (uint32_t)r.F0[0], fy = (uint32_t)r.F0[1], fz = (uint32_t)r.F0[2];
+      const int nx = (int)(r.A1[0] - r.A0[0] + 1), ny = (int)(r.A1[1] - r.A0[1] + 1);
+      const int zl0 = az0 >> 3, nzl = (az1 >> 3) - zl0 + 1;
+      const float inv_ny = 1.0f / (float)ny;
+      for (int q = lane; q < nx * ny; q += kWave) {
+        // q / ny for q < 2^11, ny <= 22: the float quotient is far from the next integer
+        const int qx = (int)(((float)q + 0.5f) * inv_ny);
+        const int x = ax0 + qx, y = ay0 + (q - qx * ny);
+        const int sxy = (((x >> 3) - r.L0[0]) * r.W[1] + ((y >> 3) - r.L0[1])) * r.W[2];
+        const uint32_t urow = ((ms * (uint32_t)x - fx) * (uint32_t)R + (ms * (uint32_t)y - fy)) * (uint32_t)R;
+        const int wx = x & 7, by = 8 * (y & 7);
+        for (int zi = 0; zi < nzl; ++zi) {
+          const int zl = zl0 + zi;
+          const int slot = sxy + zi;
+          const u64 word = s_smask[slot * 8 + wx];
+          const uint32_t row = (uint32_t)(word >> by) & 0xffu;
+          // z bits of this leaf inside [az0, az1]
+          const int lb = zi == 0 ? (az0 & 7) : 0;
+          const int hb = zi == nzl - 1 ? (az1 & 7) : 7;
+          uint32_t bits = row & ((2u << hb) - 1u) & ~((1u << lb) - 1u);
           if (!bits) continue;
-          const u64 pre = src.leaf_prefix[leaf];
-          const int wx = x & 7;
-          const int before_word = wx == 0 ? 0 : (int)((pre >> (9 * (wx - 1))) & 511ull);
-          const int before_row = __popcll(word & ((1ull << (8 * (y & 7))) - 1ull));
-          const int32_t rank0 = s_lbase[slot] + before_word + before_row;
+          const int before_word = wx == 0 ? 0 : (int)((s_spre[slot] >> (9 * (wx - 1))) & 511ull);
+          const int before_row = __popcll(word & ((1ull << by) - 1ull));
+          const int32_t rank0 = s_sbase[slot] + before_word + before_row;
+          const uint32_t uz0 = ms * (uint32_t)(zl * 8) - fz;
           while (bits) {
             const int z = __builtin_ctz(bits);
-            const i64 uz = (i64)m * (zl * 8 + z) - F0[2];
-            vol[urow + (int)uz] = rank0 + __popc(row & ((1 << z) - 1));
+            vol[urow + uz0 + ms * (uint32_t)z] = rank0 + __popc(row & ((1u << z) - 1u));
             bits &= bits - 1;
           }
         }
@@ -224,35 +308,42 @@ __global__ void __launch_bounds__(256) k_kernel_map(const int4* t_origin, const 
     }
     wave_sync();
 
-    // 3. rows out, K^3 entries each, coalesced
-    int32_t* dst = out + jb * KK;
-    const int P = n * KK;
-    int v = v_first, k = k_first;
-    for (int p = lane; p < P; p += kWave) {
-      dst[p] = vol[s_voff[v] + s_koff[k]];
-      v += gm.q64;
-      k += gm.r64;
-      if (k >= KK) {
-        k -= KK;
-        ++v;
+    // rows out, K^3 entries each, coalesced
+    int32_t* dst = out + cur.first * KK;
+    if (KK <= kWave) {
+      for (int v0 = 0; v0 < n; v0 += rows_per_it) {
+        const int v = v0 + my_row;
+        if (col_lane && v < n) dst[lane] = vol[s_voff[v] + koff[0]];
+        dst += rows_per_it * KK;
+      }
+    } else {
+      for (int v = 0; v < n; ++v) {
+        const int vo = s_voff[v];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int k = lane + kWave * j;
+          if (k < KK) dst[k] = vol[vo + koff[j]];
+        }
+        dst += KK;
       }
     }
     wave_sync();  // the next leaf reuses the wave's LDS
+    cur = nxt;
   }
 }
 
 }  // namespace
 
-void kernel_map(const GridView& sv, const GridView& tv, int K, int S, int transposed, int32_t* out,
+static i64 host_floor_div(i64 a, i64 b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }
+
+void kernel_map(const GridView& sv, const GridView& tv, int K, int S, int transposed, int32_t* out, i64 entries,
                 hipStream_t s) {
   if (tv.n_leaf == 0) return;
   if (K < 1 || K > 8 || S < 1 || S > 2) throw Error(TC_ERR_UNSUPPORTED, "kernel_map: kernel/stride out of range");
-  Arena arena(s);
-  const size_t o_up = arena.reserve(sizeof(uint16_t) * 512 * (size_t)max(sv.n_upper, 1));
-  arena.commit();
-  uint16_t* upper_prefix = arena.at<uint16_t>(o_up);
-  launch("k_upper_prefix", k_upper_prefix, sv.n_upper, 256, s, (const u64*)sv.upper_mask, upper_prefix);
-
+  if (sv.n_leaf == 0) {  // no source voxel anywhere: every entry is -1
+    fill_i32(out, -1, entries, nullptr, 1, s);
+    return;
+  }
   KmapGeom gm;
   gm.K = K;
   gm.S = S;
@@ -263,21 +354,60 @@ void kernel_map(const GridView& sv, const GridView& tv, int K, int S, int transp
   gm.KK = K * K * K;
   gm.q64 = kWave / gm.KK;
   gm.r64 = kWave % gm.KK;
-  gm.wave_words = gm.R * gm.R * gm.R + 512 + 2 * kKmapMaxSlots;
-  const size_t wave_bytes = 4 * (size_t)gm.wave_words;
-  // waves per block while the block's LDS stays within 64 KiB
-  int waves = 4;
-  while (waves > 1 && 4 * 512 + waves * wave_bytes > 64 * 1024) waves >>= 1;
-  const size_t lds = 4 * 512 + waves * wave_bytes;
-  const i64 blocks = std::min<i64>(ceil_div(tv.n_leaf, waves), 1 << 20);
+  gm.vol_words = gm.wave_words = 0;  // set once the slot count is known
+  // window slots per target leaf: the region's alignment to the leaf grid only
+  // depends on the leaf origin modulo 16, so origins 0 and 8 give the maximum
+  int sm = 0;
+  for (int o = 0; o <= 8; o += 8) {
+    i64 a0, a1;
+    if (transposed) {
+      a0 = -host_floor_div(-(o - gm.hi), S);
+      a1 = host_floor_div(o + 7 - gm.lo, S);
+    } else {
+      a0 = (i64)S * o + gm.lo;
+      a1 = (i64)S * (o + 7) + gm.hi;
+    }
+    const int w = (int)(host_floor_div(a1, 8) - host_floor_div(a0, 8) + 1);
+    sm = std::max(sm, w * w * w);
+  }
+  if (sm > kKmapMaxSlots) throw Error(TC_ERR_INTERNAL, "kernel_map: window exceeds the slot table");
+  // per wave: volume, slot masks and prefixes (18 words per slot), slot bases, 512 uint16 row offsets
+  gm.vol_words = (gm.R * gm.R * gm.R + 3) & ~3;
+  gm.wave_words = (gm.vol_words + 18 * sm + sm + 256 + 3) & ~3;  // 16-byte aligned waves
+
+  Arena arena(s);
+  const size_t o_up = arena.reserve(sizeof(uint16_t) * 512 * (size_t)std::max(sv.n_upper, 1));
+  const size_t o_slots = arena.reserve(sizeof(int2) * (size_t)tv.n_leaf * sm);
+  const size_t o_first = arena.reserve(sizeof(i64) * (size_t)tv.n_leaf);
+  arena.commit();
+  uint16_t* upper_prefix = arena.at<uint16_t>(o_up);
+  int2* slots = arena.at<int2>(o_slots);
+  i64* t_first = arena.at<i64>(o_first);
+  launch("k_upper_prefix", k_upper_prefix, sv.n_upper, 256, s, (const u64*)sv.upper_mask, upper_prefix);
 
   KmapSrc src{(const tc_grid_header*)sv.headers, (const u64*)sv.upper_key, (const int32_t*)sv.upper_first,
               (const u64*)sv.upper_mask, (const uint16_t*)upper_prefix, (const int32_t*)sv.lower_first,
               (const u64*)sv.lower_mask, (const uint16_t*)sv.lower_prefix, (const u64*)sv.leaf_mask,
               (const u64*)sv.leaf_prefix, (const i64*)sv.leaf_offset};
+  launch("k_kmap_slots", k_kmap_slots, ceil_div((i64)tv.n_leaf * sm, 256), 256, s, (const int4*)tv.leaf_origin,
+         (const i64*)tv.leaf_offset, (const tc_grid_header*)tv.headers, (i64)tv.n_leaf, src, gm, sm, slots,
+         t_first);
+
+  const size_t wave_bytes = 4 * (size_t)gm.wave_words;
+  // waves per block while the block's LDS stays within 64 KiB
+  int waves = 4;
+  while (waves > 1 && 4 * 512 + waves * wave_bytes > 64 * 1024) waves >>= 1;
+  const size_t lds = 4 * 512 + waves * wave_bytes;
+  // one round of resident blocks (LDS and wave slots per CU decide how many);
+  // each wave then walks many leaves, so the next leaf's inputs are always in flight
+  int dev = 0, cus = 256;
+  hip_check(hipGetDevice(&dev), "hipGetDevice");
+  hip_check(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev), "hipDeviceGetAttribute");
+  const int per_cu = std::max(1, std::min(32 / waves, (int)((160 * 1024) / lds)));
+  const i64 blocks = std::min<i64>(ceil_div(tv.n_leaf, waves), (i64)cus * per_cu);
   launch_lds("k_kernel_map", k_kernel_map, blocks, kWave * waves, lds, s, (const int4*)tv.leaf_origin,
-             (const u64*)tv.leaf_mask, (const i64*)tv.leaf_offset, (const tc_grid_header*)tv.headers,
-             (i64)tv.n_leaf, src, gm, out, waves);
+             (const u64*)tv.leaf_mask, (const i64*)t_first, (i64)tv.n_leaf, src, gm, (const int2*)slots, sm, out,
+             waves);
 }
 
 }  // namespace tc

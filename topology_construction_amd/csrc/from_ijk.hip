@@ -28,11 +28,14 @@ __global__ void __launch_bounds__(256) k_voxel_grid(const i64* offsets, int32_t 
 }
 
 // Voxels that arrive together usually share their tile, lower and leaf, so the
-// lanes of a wave first merge the bits they set in the same 64-bit word: one
-// lane per distinct word ORs the union (after a plain read shows bits missing).
-// Same-address device atomics serialize on this part; a wave issues at most a
-// few of them instead of up to 64. Lanes that are still waiting after
-// kDedupRounds distinct words fall back to one atomic each.
+// lanes of a wave first merge the bits they set in the same 64-bit word (up to
+// kDedupRounds distinct words, found with ballots and shuffles, no memory
+// traffic); then every group's leader issues one OR for the union, all groups
+// at once. Lanes still waiting after kDedupRounds words OR their own bit. With
+// kCheck the leaders first read their word and skip the atomic when the bits
+// are already set: the words of tiles and lower nodes are shared by many waves
+// and same-address device atomics serialize, whereas leaf words mostly receive
+// new bits and are ORed without the read.
 constexpr int kDedupRounds = 8;
 
 __device__ __forceinline__ u64 wave_or_u64(u64 v) {
@@ -41,19 +44,22 @@ __device__ __forceinline__ u64 wave_or_u64(u64 v) {
   return v;
 }
 
+template <bool kCheck>
 __device__ __forceinline__ void wave_or_into(u64* word, u64 bits, bool active) {
   const int lane = threadIdx.x & (kWave - 1);
   u64 todo = __ballot(active);
+  u64 mine = 0;  // the union this lane ORs, if it leads a group
   for (int round = 0; todo && round < kDedupRounds; ++round) {
     const int leader = __builtin_ctzll(todo);
     const u64 lw = (u64)__shfl((long long)(uintptr_t)word, leader, kWave);
     const bool same = ((todo >> lane) & 1ull) && (u64)(uintptr_t)word == lw;
     const u64 sm = __ballot(same);
     const u64 all = wave_or_u64(same ? bits : 0);
-    if (lane == leader && (*word & all) != all) atomicOr((unsigned long long*)word, all);
+    if (lane == leader) mine = all;
     todo &= ~sm;
   }
-  if ((todo >> lane) & 1ull) atomicOr((unsigned long long*)word, bits);
+  if ((todo >> lane) & 1ull) mine = bits;
+  if (mine && (!kCheck || (*word & mine) != mine)) atomicOr((unsigned long long*)word, mine);
 }
 
 __device__ __forceinline__ u64 tile_hash(int32_t g, int32_t tx, int32_t ty, int32_t tz) {
@@ -179,7 +185,7 @@ __global__ void __launch_bounds__(256) k_voxel_mark_lower(const int32_t* ijk, co
     word = &tile_child[t * 512 + (bit >> 6)];
     b = 1ull << (bit & 63);
   }
-  wave_or_into(word, b, in);
+  wave_or_into<true>(word, b, in);
 }
 
 // All lanes stay active to the end of these kernels (no early return), so the
@@ -213,7 +219,7 @@ __global__ void __launch_bounds__(256) k_voxel_cand(const int32_t* ijk, const in
   if (ok && (lane == 0 || cprev != c))
     cand_origin[c] = make_int4((x >> 7) * 128, (y >> 7) * 128, (z >> 7) * 128, (int32_t)t);
   const int lb = (((x >> 3) & 15) * 16 + ((y >> 3) & 15)) * 16 + ((z >> 3) & 15);
-  wave_or_into(ok ? &cand_child[(i64)c * 64 + (lb >> 6)] : cand_child, ok ? 1ull << (lb & 63) : 0, ok);
+  wave_or_into<true>(ok ? &cand_child[(i64)c * 64 + (lb >> 6)] : cand_child, ok ? 1ull << (lb & 63) : 0, ok);
 }
 
 __global__ void __launch_bounds__(256) k_voxel_leaf(const int32_t* ijk, const int32_t* vcand, i64 n,
@@ -241,7 +247,7 @@ __global__ void __launch_bounds__(256) k_voxel_leaf(const int32_t* ijk, const in
       }
     }
   }
-  wave_or_into(word, bits, ok);
+  wave_or_into<false>(word, bits, ok);
 }
 
 static int32_t read_i32(const int32_t* d, hipStream_t s) {

@@ -387,24 +387,20 @@ tc_grid_batch* build_from_ijk(const int32_t* d_ijk, const int64_t* h_off, int32_
     const i64 L = out->nl;
     Arena post(s);
     const size_t o_lc = post.reserve(4 * L);
-    const size_t o_lv = post.reserve(8 * L);
     const size_t o_box = post.reserve(4 * L);
-    const size_t o_vx = post.reserve(8 * (L + 1));
     const size_t o_bb = post.reserve(4 * 6 * (i64)B * bbox_replicas(B));
     const size_t o_part = post.reserve(8 * (ceil_div(L, 256) + 1));  // voxel sums per 256 leaves
     const size_t o_gvb = post.reserve(8 * ((i64)B + 1));
     const size_t o_inrun = post.reserve(4 * L);
     post.commit();
-    i64* leaf_vox = finalize_is_small(L, B) ? post.at<i64>(o_lv) : nullptr;  // per-leaf counts: small path only
     tree_write_nodes(ts, ov, post.at<int32_t>(o_lc), s);
     fill_u64(ov.leaf_mask, 0, 8 * L, nullptr, 1, s);
     launch("k_voxel_leaf", k_voxel_leaf, ceil_div(N, 256), 256, s, d_ijk, (const int32_t*)vcand, N,
            (const u64*)ts.cand_child, (const uint16_t*)ts.cand_prefix, (const i64*)ts.cand_scan, L,
            ov.leaf_mask);
-    tree_leaf_stats(ov, leaf_vox, post.at<uint32_t>(o_box), post.at<int32_t>(o_inrun), post.at<i64>(o_part), s);
-    tree_finalize_leaves(ov, leaf_vox, post.at<uint32_t>(o_box), post.at<int32_t>(o_inrun), post.at<i64>(o_part),
-                         256, post.at<i64>(o_vx), post.at<i64>(o_gvb), post.at<int32_t>(o_bb),
-                         (const int32_t*)ts.grid_info, s);
+    tree_leaf_stats(ov, post.at<uint32_t>(o_box), post.at<int32_t>(o_inrun), post.at<i64>(o_part), s);
+    tree_finalize_leaves(ov, post.at<uint32_t>(o_box), post.at<int32_t>(o_inrun), post.at<i64>(o_part), 256,
+                         post.at<i64>(o_gvb), post.at<int32_t>(o_bb), (const int32_t*)ts.grid_info, s);
   } catch (...) {
     free_batch(out);
     throw;

@@ -264,17 +264,13 @@ void tree_rank_tiles(TreeScratch& t, hipStream_t s);            // prefix per ti
 void tree_count_cands(TreeScratch& t, hipStream_t s);           // leaf counts per cand + their scan
 void tree_counts(TreeScratch& t, int32_t B, hipStream_t s);     // tree_count_cands + tree_grid_counts (fused when small)
 void tree_write_nodes(TreeScratch& t, const GridView& out, int32_t* leaf_cand, hipStream_t s);
-void tree_leaf_stats(const GridView& out, i64* leaf_vox, uint32_t* leaf_box, int32_t* leaf_inrun, i64* vox_part,
-                     hipStream_t s);
+void tree_leaf_stats(const GridView& out, uint32_t* leaf_box, int32_t* leaf_inrun, i64* vox_part, hipStream_t s);
 int32_t bbox_replicas(int32_t B);  // replicas of the per-grid bbox accumulators
 // Leaf voxel offsets, per-grid bboxes and headers. The leaf producer wrote, per
 // run of `gran` leaves (gran divides 256), the run's voxel sum (vox_part) and
-// every leaf's voxels before it inside its run (leaf_inrun); batches for which
-// finalize_is_small holds use leaf_vox (per-leaf counts) instead.
-bool finalize_is_small(i64 L, int32_t B);
-void tree_finalize_leaves(const GridView& out, const i64* leaf_vox, const uint32_t* leaf_box,
-                          const int32_t* leaf_inrun, i64* vox_part, i64 gran, i64* vox_excl, i64* gvb,
-                          int32_t* bbox_accum, const int32_t* grid_info, hipStream_t s);
+// every leaf's voxels before it inside its run (leaf_inrun).
+void tree_finalize_leaves(const GridView& out, const uint32_t* leaf_box, const int32_t* leaf_inrun, i64* vox_part,
+                          i64 gran, i64* gvb, int32_t* bbox_accum, const int32_t* grid_info, hipStream_t s);
 void tree_enumerate(const GridView& v, int32_t* ijk, hipStream_t s);
 
 // Allocation of the single output buffer of a batch.

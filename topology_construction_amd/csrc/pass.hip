@@ -1152,7 +1152,7 @@ __global__ void __launch_bounds__(256) k_leaf_gather(const int4* out_origin, con
                                                      const int32_t* src_lower_first, const u64* src_leaf_mask,
                                                      int32_t n_src_lower, int32_t n_src_leaf,
                                                      const int32_t* d_num_cands, u64* out_mask, u64* out_prefix,
-                                                     i64* leaf_vox, uint32_t* leaf_box, int32_t* leaf_inrun,
+                                                     uint32_t* leaf_box, int32_t* leaf_inrun,
                                                      i64* vox_part, int32_t* flags) {
   constexpr int lpl = KIND == 0 ? 1 : 4;  // lanes per output leaf
   const i64 gt = (i64)blockIdx.x * 256 + threadIdx.x;
@@ -1273,7 +1273,6 @@ __global__ void __launch_bounds__(256) k_leaf_gather(const int4* out_origin, con
   // voxels before this leaf within the block's leaves, and the block's total
   const int32_t inrun = block_run_scan(count, &vox_part[blockIdx.x]);
   if (writer) {
-    if (leaf_vox) leaf_vox[i] = count;
     leaf_box[i] = box;
     leaf_inrun[i] = inrun;
   }
@@ -1295,7 +1294,7 @@ __global__ void __launch_bounds__(256) k_leaf_gather_box(const int4* out_origin,
                                                          const int32_t* src_lower_first, const u64* src_leaf_mask,
                                                          int32_t n_src_lower, int32_t n_src_leaf,
                                                          const int32_t* d_num_cands, u64* out_mask, u64* out_prefix,
-                                                         i64* leaf_vox, uint32_t* leaf_box, int32_t* leaf_inrun,
+                                                         uint32_t* leaf_box, int32_t* leaf_inrun,
                                                          i64* vox_part, int32_t* flags) {
   const i64 gt = (i64)blockIdx.x * 256 + threadIdx.x;
   const i64 i = gt >> 2;
@@ -1409,7 +1408,6 @@ __global__ void __launch_bounds__(256) k_leaf_gather_box(const int4* out_origin,
   // voxels before this leaf within the block's leaves, and the block's total
   const int32_t inrun = block_run_scan(count, &vox_part[blockIdx.x]);
   if (i < n && sub == 0) {
-    if (leaf_vox) leaf_vox[i] = count;
     leaf_box[i] = box;
     leaf_inrun[i] = inrun;
   }
@@ -1624,9 +1622,7 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, 
     const i64 L = out->nl;
     Arena post(s);
     const size_t o_lc = post.reserve(4 * L);
-    const size_t o_lv = post.reserve(8 * L);
     const size_t o_box = post.reserve(4 * L);
-    const size_t o_vx = post.reserve(8 * (L + 1));
     const size_t o_bb = post.reserve(4 * 6 * (i64)B * bbox_replicas(B));
     // voxel sums per gather workgroup: 256 output leaves (refine) or 64 (4 lanes per leaf)
     const i64 gran = op == TC_OP_REFINE ? 256 : 64;
@@ -1636,7 +1632,6 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, 
     post.commit();
     int32_t* leaf_cand = post.at<int32_t>(o_lc);
     i64* vox_part = post.at<i64>(o_part);
-    i64* leaf_vox = finalize_is_small(L, B) ? post.at<i64>(o_lv) : nullptr;  // per-leaf counts: small path only
     int32_t* leaf_inrun = post.at<int32_t>(o_inrun);
     tree_write_nodes(ts, ov, leaf_cand, s);
     if (L > 0 && sv.n_leaf == 0) throw Error(TC_ERR_INTERNAL, "pass: output leaves without source leaves");
@@ -1647,16 +1642,16 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, 
              (const int32_t*)leaf_cand, L, op, oi.m, oi.lo, oi.hi, (const int32_t*)cand_src,
              (const u64*)sv.lower_mask, (const uint16_t*)sv.lower_prefix, (const int32_t*)sv.lower_first,
              (const u64*)sv.leaf_mask, sv.n_lower, sv.n_leaf, (const int32_t*)ts.d_num_cands, ov.leaf_mask,
-             ov.leaf_prefix, leaf_vox, post.at<uint32_t>(o_box), leaf_inrun, vox_part, ts.flags);
+             ov.leaf_prefix, post.at<uint32_t>(o_box), leaf_inrun, vox_part, ts.flags);
     } else {
       launch("k_leaf_gather", k_leaf_gather_box, ceil_div(L * 4, 256), 256, s, (const int4*)ov.leaf_origin,
              (const int32_t*)leaf_cand, L, oi.lo, oi.hi, (const int32_t*)cand_src, (const u64*)sv.lower_mask,
              (const uint16_t*)sv.lower_prefix, (const int32_t*)sv.lower_first, (const u64*)sv.leaf_mask,
              sv.n_lower, sv.n_leaf, (const int32_t*)ts.d_num_cands, ov.leaf_mask, ov.leaf_prefix,
-             leaf_vox, post.at<uint32_t>(o_box), leaf_inrun, vox_part, ts.flags);
+             post.at<uint32_t>(o_box), leaf_inrun, vox_part, ts.flags);
     }
-    tree_finalize_leaves(ov, leaf_vox, post.at<uint32_t>(o_box), leaf_inrun, vox_part, gran, post.at<i64>(o_vx),
-                         post.at<i64>(o_gvb), post.at<int32_t>(o_bb), (const int32_t*)ts.grid_info, s);
+    tree_finalize_leaves(ov, post.at<uint32_t>(o_box), leaf_inrun, vox_part, gran, post.at<i64>(o_gvb),
+                         post.at<int32_t>(o_bb), (const int32_t*)ts.grid_info, s);
   } catch (...) {
     free_batch(out);
     throw;

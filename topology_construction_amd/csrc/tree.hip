@@ -383,9 +383,8 @@ void tree_write_nodes(TreeScratch& ts, const GridView& out, int32_t* leaf_cand, 
 // ------------------------------------------------------------------ leaf statistics
 // Per leaf (masks written by the ijk front-end): prefix word, voxel count and
 // packed local bbox. The topology pass computes the same values in its gather.
-__global__ void __launch_bounds__(256) k_leaf_stats(const u64* leaf_mask, u64* leaf_prefix, i64* leaf_vox,
-                                                    uint32_t* leaf_box, int32_t* leaf_inrun, i64* vox_part,
-                                                    i64 n_leaf) {
+__global__ void __launch_bounds__(256) k_leaf_stats(const u64* leaf_mask, u64* leaf_prefix, uint32_t* leaf_box,
+                                                    int32_t* leaf_inrun, i64* vox_part, i64 n_leaf) {
   const i64 i = (i64)blockIdx.x * 256 + threadIdx.x;
   int count = 0;
   u64 prefix = 0;
@@ -399,16 +398,14 @@ __global__ void __launch_bounds__(256) k_leaf_stats(const u64* leaf_mask, u64* l
   const int32_t inrun = block_run_scan(count, &vox_part[blockIdx.x]);
   if (i < n_leaf) {
     leaf_prefix[i] = prefix;
-    if (leaf_vox) leaf_vox[i] = count;
     leaf_box[i] = box;
     leaf_inrun[i] = inrun;
   }
 }
 
-void tree_leaf_stats(const GridView& out, i64* leaf_vox, uint32_t* leaf_box, int32_t* leaf_inrun, i64* vox_part,
-                     hipStream_t s) {
+void tree_leaf_stats(const GridView& out, uint32_t* leaf_box, int32_t* leaf_inrun, i64* vox_part, hipStream_t s) {
   launch("k_leaf_stats", k_leaf_stats, ceil_div((i64)out.n_leaf, 256), 256, s, (const u64*)out.leaf_mask,
-         out.leaf_prefix, leaf_vox, leaf_box, leaf_inrun, vox_part, (i64)out.n_leaf);
+         out.leaf_prefix, leaf_box, leaf_inrun, vox_part, (i64)out.n_leaf);
 }
 
 // Per-grid bboxes of large batches: leaf bounds are reduced over the wave (leaves
@@ -431,16 +428,19 @@ int32_t bbox_replicas(int32_t B) {
   return r < 1 ? 1 : (r > 64 ? 64 : r);
 }
 
-// Small batches (at most kFinSmallLeaves leaves and kFinSmallGrids grids): the
-// voxel scan, leaf offsets, bboxes (folded in LDS) and headers in one
-// workgroup. Leaves go in tiles of 16 waves x kFinPer x 64: wave w owns a
-// contiguous run of kFinPer * 64 leaves, its lanes reading them 64 at a time
-// (coalesced). The scan is a wave scan per group plus a 16-entry table of wave
-// totals; each lane folds the bbox of its leaves in registers (a run rarely
-// holds more than one grid), and the wave reduces once per tile.
+// Small batches (at most kFinSmallLeaves leaves and kFinSmallGrids grids): leaf
+// offsets, bboxes (folded in LDS) and headers in one workgroup. The leaf
+// producer left, per run of `gran` leaves, the run's voxel sum (at most 1024
+// runs here) and every leaf's voxels before it inside its run, so one block scan
+// of the run sums gives every run's offset; every grid's voxel begin is its
+// first leaf's run offset plus that leaf's in-run count. Leaves then go in tiles
+// of 16 waves x kFinPer x 64: wave w owns a contiguous run of kFinPer * 64
+// leaves, its lanes reading them 64 at a time (coalesced); each lane folds the
+// bbox of its leaves in registers (a run rarely holds more than one grid), and
+// the wave reduces once per tile.
 constexpr int kFinThreads = 1024;
 constexpr int kFinPer = 8;
-constexpr i64 kFinSmallLeaves = 65536;
+constexpr i64 kFinSmallLeaves = 65536;  // with runs of >= 64 leaves: <= kFinThreads runs
 constexpr int kFinSmallGrids = 1024;
 
 __device__ __forceinline__ void box_fold_lds(int32_t (*s_box)[kFinSmallGrids], int g, const int v[6]) {
@@ -450,70 +450,49 @@ __device__ __forceinline__ void box_fold_lds(int32_t (*s_box)[kFinSmallGrids], i
   }
 }
 
-__global__ void __launch_bounds__(kFinThreads) k_finalize_small(const int4* leaf_origin, const i64* leaf_vox,
-                                                                const uint32_t* leaf_box, const int32_t* grid_info,
-                                                                i64* vox_excl, i64* leaf_offset, int32_t B, i64 L,
+__global__ void __launch_bounds__(kFinThreads) k_finalize_small(const int4* leaf_origin, const int32_t* leaf_inrun,
+                                                                const uint32_t* leaf_box, const i64* vox_part,
+                                                                i64 np, i64 gran, const int32_t* grid_info,
+                                                                i64* leaf_offset, int32_t B, i64 L,
                                                                 tc_grid_header* hdr) {
   constexpr int kWaves = kFinThreads / kWave;
   constexpr int kRun = kFinPer * kWave;  // leaves per wave per tile
   __shared__ int32_t s_box[6][kFinSmallGrids];
-  __shared__ i64 s_gvb[kFinSmallGrids];  // scan value at each grid's first leaf
-  __shared__ i64 s_tot[kWaves];          // wave totals, then their exclusive offsets
-  __shared__ i64 s_carry;
+  __shared__ i64 s_part[kFinThreads];        // exclusive voxel offset of every run
+  __shared__ i64 s_gvb[kFinSmallGrids + 1];  // voxel begin of every grid, then the total
+  __shared__ i64 s_wave[kWaves];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wv = tid / kWave;
+  const i64 pv = tid < np ? vox_part[tid] : 0;
   for (int g = tid; g < B; g += kFinThreads) {
     for (int a = 0; a < 3; ++a) {
       s_box[a][g] = INT32_MAX;
       s_box[3 + a][g] = INT32_MIN;
     }
   }
-  if (tid == 0) s_carry = 0;
+  i64 total;
+  const i64 pex = block_excl_scan<i64, kFinThreads>(pv, s_wave, total);
+  if (tid < np) s_part[tid] = pex;
+  __syncthreads();
+  for (int g = tid; g <= B; g += kFinThreads) {
+    const i64 f = g < B ? grid_info[g * 6 + 5] : L;
+    s_gvb[g] = f < L ? s_part[f / gran] + leaf_inrun[f] : total;
+  }
   __syncthreads();
   for (i64 base = 0; base < L; base += (i64)kWaves * kRun) {
     const i64 run0 = base + (i64)wv * kRun;
-    i64 v[kFinPer];
     int4 o[kFinPer];
     uint32_t bx[kFinPer];
-    int32_t gfirst[kFinPer];
+    int32_t in_run[kFinPer];
 #pragma unroll
     for (int k = 0; k < kFinPer; ++k) {
       const i64 i = run0 + k * kWave + lane;
       const bool in = i < L;
-      v[k] = in ? leaf_vox[i] : 0;
       o[k] = in ? leaf_origin[i] : make_int4(0, 0, 0, -1);
       bx[k] = in ? leaf_box[i] : kEmptyBox;
+      in_run[k] = in ? leaf_inrun[i] : 0;
     }
-#pragma unroll
-    for (int k = 0; k < kFinPer; ++k) gfirst[k] = o[k].w >= 0 && o[k].w < B ? grid_info[o[k].w * 6 + 5] : -1;
-    i64 ex[kFinPer];
-    i64 carry = 0;
-#pragma unroll
-    for (int k = 0; k < kFinPer; ++k) {
-      const i64 inc = wave_incl_scan(v[k]);
-      ex[k] = carry + inc - v[k];
-      carry += __shfl(inc, kWave - 1, kWave);
-    }
-    if (lane == 0) s_tot[wv] = carry;
-    __syncthreads();
-    if (wv == 0) {  // exclusive offsets of the wave totals, after the running carry
-      const i64 t = lane < kWaves ? s_tot[lane] : 0;
-      const i64 inc = wave_incl_scan(t);
-      const i64 c0 = s_carry;
-      if (lane < kWaves) s_tot[lane] = c0 + inc - t;
-      if (lane == kWave - 1) s_carry = c0 + inc;
-    }
-    __syncthreads();
-    const i64 off = s_tot[wv];
-#pragma unroll
-    for (int k = 0; k < kFinPer; ++k) {
-      const i64 i = run0 + k * kWave + lane;
-      ex[k] += off;
-      if (i < L) vox_excl[i] = ex[k];
-      if (i < L && i == gfirst[k]) s_gvb[o[k].w] = ex[k];  // leaves come grid by grid
-    }
-    __syncthreads();  // the grids' first-leaf scan values are read below
     int g = -1;
     int bv[6] = {INT32_MAX, INT32_MAX, INT32_MAX, INT32_MIN, INT32_MIN, INT32_MIN};
 #pragma unroll
@@ -521,7 +500,7 @@ __global__ void __launch_bounds__(kFinThreads) k_finalize_small(const int4* leaf
       const i64 i = run0 + k * kWave + lane;
       const int gk = o[k].w;
       if (i >= L || gk < 0 || gk >= B) continue;
-      leaf_offset[i] = ex[k] - s_gvb[gk];
+      leaf_offset[i] = s_part[i / gran] + in_run[k] - s_gvb[gk];
       if (bx[k] == kEmptyBox) continue;
       if (gk != g) {
         if (g >= 0) box_fold_lds(s_box, g, bv);
@@ -556,8 +535,6 @@ __global__ void __launch_bounds__(kFinThreads) k_finalize_small(const int4* leaf
       }
     }
   }
-  if (tid == 0) vox_excl[L] = s_carry;
-  __threadfence();
   __syncthreads();
   for (int gg = tid; gg < B; gg += kFinThreads) {
     const int32_t* gi = grid_info + (i64)gg * 6;
@@ -570,8 +547,8 @@ __global__ void __launch_bounds__(kFinThreads) k_finalize_small(const int4* leaf
     h.upper_begin = gi[3];
     h.lower_begin = gi[4];
     h.leaf_begin = gi[5];
-    h.voxel_begin = vox_excl[gi[5]];
-    h.voxel_count = vox_excl[gi[5] + gi[2]] - h.voxel_begin;
+    h.voxel_begin = s_gvb[gg];
+    h.voxel_count = s_gvb[gg + 1] - s_gvb[gg];
     for (int a = 0; a < 3; ++a) {
       h.bbox_min[a] = s_box[a][gg];
       h.bbox_max[a] = s_box[3 + a][gg];
@@ -713,16 +690,13 @@ __global__ void __launch_bounds__(256) k_write_headers_gvb(const int32_t* grid_i
   hdr[g] = h;
 }
 
-bool finalize_is_small(i64 L, int32_t B) { return L <= kFinSmallLeaves && B <= kFinSmallGrids; }
-
-void tree_finalize_leaves(const GridView& out, const i64* leaf_vox, const uint32_t* leaf_box,
-                          const int32_t* leaf_inrun, i64* vox_part, i64 gran, i64* vox_excl, i64* gvb,
-                          int32_t* bbox_accum, const int32_t* grid_info, hipStream_t s) {
+void tree_finalize_leaves(const GridView& out, const uint32_t* leaf_box, const int32_t* leaf_inrun, i64* vox_part,
+                          i64 gran, i64* gvb, int32_t* bbox_accum, const int32_t* grid_info, hipStream_t s) {
   const i64 L = out.n_leaf;
   const int32_t B = out.B;
-  if (finalize_is_small(L, B)) {
-    launch("k_finalize_small", k_finalize_small, 1, kFinThreads, s, (const int4*)out.leaf_origin, leaf_vox, leaf_box,
-           grid_info, vox_excl, out.leaf_offset, B, L, out.headers);
+  if (L <= kFinSmallLeaves && B <= kFinSmallGrids && ceil_div(L, gran) <= kFinThreads) {
+    launch("k_finalize_small", k_finalize_small, 1, kFinThreads, s, (const int4*)out.leaf_origin, leaf_inrun,
+           leaf_box, (const i64*)vox_part, ceil_div(L, gran), gran, grid_info, out.leaf_offset, B, L, out.headers);
     return;
   }
   const int32_t R = bbox_replicas(B);

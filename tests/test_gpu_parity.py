@@ -248,6 +248,28 @@ def test_deterministic_bits():
             assert np.array_equal(fa[k], fb[k]), k
 
 
+def test_scratch_cache_reuse_and_release():
+    """Passes reuse the calling thread's cached scratch blocks; results stay the
+    same when blocks are reused by a different op (stale contents), after they
+    are released, and on another stream."""
+    import torch
+    from topology_construction_amd import binding
+    ijk, off = synth.make_config(3)
+    ref = {op: oracle.run(op, f, ijk, off) for op, f in [("dilate", 1), ("refine", 2)]}
+    src = binding.tc_batch_from_ijk(torch.from_numpy(ijk).cuda(), off)
+    for op, f in [("dilate", 1), ("refine", 2), ("dilate", 1)]:
+        assert_same(gpu_fields(binding.tc_build_batched_topology(src, op, f)), ref[op], f"reuse {op}")
+    binding.tc_scratch_release()
+    assert_same(gpu_fields(binding.tc_build_batched_topology(src, "refine", 2)), ref["refine"], "after release")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        out = binding.tc_build_batched_topology(src, "dilate", 1, stream=s)
+    s.synchronize()
+    assert_same(gpu_fields(out), ref["dilate"], "second stream")
+    binding.tc_scratch_release()
+    torch.cuda.synchronize()
+
+
 def test_self_consistency_from_ijk_of_enumeration():
     """from_ijk(enumerate(op(g))) == op(g) elementwise (the pages' pinning method)."""
     from topology_construction_amd import binding

@@ -27,7 +27,8 @@ OPS = {"coarsen": 1, "refine": 2, "dilate": 3, "pad_neg": 4, "pad_pos": 5, "conv
 ABI_SYMBOLS = [
     "tc_abi_version", "tc_status_string", "tc_last_error", "tc_batch_from_ijk",
     "tc_build_batched_topology", "tc_build_masked_refine", "tc_batch_get_info", "tc_batch_read_headers",
-    "tc_batch_voxel_total", "tc_enumerate_ijk", "tc_build_kernel_map", "tc_batch_free", "tc_profile_enable",
+    "tc_batch_voxel_total", "tc_enumerate_ijk", "tc_build_kernel_map", "tc_scratch_release", "tc_batch_free",
+    "tc_profile_enable",
     "tc_profile_read", "tc_profile_disable",
 ]
 
@@ -127,6 +128,8 @@ def load_library(path: str = LIB_PATH):
         lib.tc_enumerate_ijk.argtypes = [vp, vp, i64, vp]
         lib.tc_build_kernel_map.restype = ctypes.c_int
         lib.tc_build_kernel_map.argtypes = [vp, vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, i64, vp]
+        lib.tc_scratch_release.restype = ctypes.c_int
+        lib.tc_scratch_release.argtypes = []
         lib.tc_batch_free.restype = None
         lib.tc_batch_free.argtypes = [vp]
         lib.tc_profile_enable.restype = ctypes.c_int
@@ -302,6 +305,11 @@ def tc_build_kernel_map(src: GridBatch, dst: GridBatch, kernel_size: int, stride
                                    ctypes.c_void_p(out.data_ptr() if out.numel() else 0), int(out.numel()),
                                    _stream_handle(stream)))
     return out.view(-1)[:rows * kk].view(rows, kk)
+
+
+def tc_scratch_release():
+    """Return the calling thread's cached scratch blocks to the device pool."""
+    _check(load_library().tc_scratch_release())
 
 
 def tc_batch_read_headers(batch: GridBatch, stream=None) -> np.ndarray:

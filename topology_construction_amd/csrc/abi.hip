@@ -381,6 +381,13 @@ tc_status tc_build_kernel_map(const tc_grid_batch* src, const tc_grid_batch* dst
   });
 }
 
+tc_status tc_scratch_release(void) {
+  return guarded([&]() {
+    tc::scratch_release_all();
+    return TC_OK;
+  });
+}
+
 void tc_batch_free(tc_grid_batch* b) {
   try {
     tc::free_batch(b);

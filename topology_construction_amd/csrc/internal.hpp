@@ -128,8 +128,9 @@ inline GridView make_view(void* buffer, const Layout& L, int32_t B, int32_t n2, 
 }
 
 // ------------------------------------------------------------------ host-side memory
-// Scratch arena: one hipMallocAsync block carved into 256-byte aligned arrays,
-// released with hipFreeAsync (stream-ordered) when the arena is destroyed.
+// Scratch arena: one block carved into 256-byte aligned arrays. The block comes
+// from the calling thread's scratch cache (below) and returns to it when the
+// arena is destroyed.
 class Arena {
  public:
   explicit Arena(hipStream_t s) : stream_(s) {}
@@ -152,7 +153,17 @@ class Arena {
   hipStream_t stream_;
   char* base_ = nullptr;
   size_t size_ = 0;
+  int slot_ = -1;
 };
+
+// Scratch blocks cached per calling thread, device and stream: an arena takes
+// an idle block of its stream that is large enough (or replaces the largest
+// idle one), and gives it back when destroyed, without freeing it. Reuse is
+// ordered by the stream itself, so no event is needed. scratch_release_all()
+// frees the calling thread's idle blocks (stream-ordered).
+int scratch_acquire(size_t bytes, hipStream_t s, char** p);
+void scratch_give_back(int slot);
+void scratch_release_all();
 
 // Per-thread pinned host staging buffer (grows on demand, never shrinks).
 void* pinned_staging(size_t bytes);

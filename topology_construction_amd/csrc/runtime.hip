@@ -43,14 +43,72 @@ void device_free_async(void* p, hipStream_t s) {
   if (p) (void)hipFreeAsync(p, s);
 }
 
+namespace {
+struct ScratchSlot {
+  int device;
+  hipStream_t stream;
+  char* p;
+  size_t bytes;
+  bool busy;
+};
+thread_local std::vector<ScratchSlot> t_scratch;
+}  // namespace
+
+int scratch_acquire(size_t bytes, hipStream_t s, char** p) {
+  int dev = 0;
+  hip_check(hipGetDevice(&dev), "hipGetDevice");
+  int fit = -1, idle = -1;
+  for (int i = 0; i < (int)t_scratch.size(); ++i) {
+    const ScratchSlot& z = t_scratch[i];
+    if (z.busy || z.device != dev || z.stream != s) continue;
+    if (z.bytes >= bytes && (fit < 0 || z.bytes < t_scratch[fit].bytes)) fit = i;
+    if (idle < 0 || z.bytes > t_scratch[idle].bytes) idle = i;
+  }
+  if (fit < 0) {
+    // grow: replace the largest idle block of this stream, or add one
+    const size_t want = bytes + bytes / 4 + 4096;
+    char* np = static_cast<char*>(device_alloc_async(want, s));
+    if (idle >= 0) {
+      if (t_scratch[idle].p) device_free_async(t_scratch[idle].p, s);
+      t_scratch[idle].p = np;
+      t_scratch[idle].bytes = want;
+      fit = idle;
+    } else {
+      t_scratch.push_back(ScratchSlot{dev, s, np, want, false});
+      fit = (int)t_scratch.size() - 1;
+    }
+  }
+  t_scratch[fit].busy = true;
+  *p = t_scratch[fit].p;
+  return fit;
+}
+
+void scratch_give_back(int slot) {
+  if (slot >= 0 && slot < (int)t_scratch.size()) t_scratch[slot].busy = false;
+}
+
+void scratch_release_all() {
+  int cur = 0;
+  hip_check(hipGetDevice(&cur), "hipGetDevice");
+  for (ScratchSlot& z : t_scratch) {  // slots keep their indices (busy ones belong to live arenas)
+    if (z.busy || !z.p) continue;
+    if (z.device != cur) hip_check(hipSetDevice(z.device), "hipSetDevice");
+    device_free_async(z.p, z.stream);
+    if (z.device != cur) hip_check(hipSetDevice(cur), "hipSetDevice");
+    z.p = nullptr;
+    z.bytes = 0;
+  }
+}
+
 void Arena::commit() {
   if (base_) throw Error(TC_ERR_INTERNAL, "arena committed twice");
-  base_ = static_cast<char*>(device_alloc_async(size_, stream_));
+  slot_ = scratch_acquire(size_, stream_, &base_);
 }
 
 void Arena::release() {
-  if (base_) device_free_async(base_, stream_);
+  if (base_) scratch_give_back(slot_);
   base_ = nullptr;
+  slot_ = -1;
 }
 
 // ------------------------------------------------------------------ pinned staging

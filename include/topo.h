@@ -247,12 +247,14 @@ tc_status tc_build_kernel_map(const tc_grid_batch* src, const tc_grid_batch* dst
                               int32_t stride, int32_t transposed, int32_t* d_out, int64_t capacity,
                               void* stream);
 
-/* Scratch memory: every call takes its scratch arrays from blocks cached per
- * calling thread, device and stream, and keeps them for the next call on the
- * same stream (reuse is ordered by that stream, so none is waited for). This
- * returns the calling thread's cached blocks to the device's memory pool,
- * stream-ordered on the streams that used them. Calls that run afterwards
- * allocate again. Never fails except for a HIP error. */
+/* Cached device memory: every call takes its scratch arrays from blocks cached
+ * per calling thread, device and stream, and keeps them for the next call on
+ * the same stream (reuse is ordered by that stream, so none is waited for).
+ * Likewise tc_batch_free keeps the buffer of a batch built without an allocator
+ * (up to 64 buffers, 4 GiB) for the next batch on the same device and stream.
+ * This returns the calling thread's scratch blocks and every cached batch
+ * buffer to the device's memory pool, stream-ordered on the streams that used
+ * them; later calls allocate again. Fails only with a HIP error. */
 tc_status tc_scratch_release(void);
 
 /* Releases the batch's device buffer (through the allocator it was created with,

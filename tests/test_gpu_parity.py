@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 
 import oracle
-from tests.gpu_util import assert_same, gpu_build, gpu_fields
+from tests.gpu_util import assert_same, gpu_build, gpu_fields, headers_as_oracle
 from topology_construction_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -266,7 +266,20 @@ def test_scratch_cache_reuse_and_release():
         out = binding.tc_build_batched_topology(src, "dilate", 1, stream=s)
     s.synchronize()
     assert_same(gpu_fields(out), ref["dilate"], "second stream")
+    # batch buffers of the library's own allocation go back to its cache on free
+    # and are taken again by the next batch that fits (stale contents)
+    # (field views need torch-owned buffers: compare headers and the enumeration)
+    def same_ijk_headers(b, r, what):
+        assert np.array_equal(headers_as_oracle(b.headers()), r["headers"]), what
+        assert np.array_equal(b.ijk().cpu().numpy(), r["ijk"]), what
+
+    for op, f in [("refine", 2), ("dilate", 1), ("refine", 2)]:
+        b = binding.tc_build_batched_topology(src, op, f, allocator="none")
+        same_ijk_headers(b, ref[op], f"cached buffer {op}")
+        del b
     binding.tc_scratch_release()
+    same_ijk_headers(binding.tc_build_batched_topology(src, "dilate", 1, allocator="none"), ref["dilate"],
+                     "after release")
     torch.cuda.synchronize()
 
 

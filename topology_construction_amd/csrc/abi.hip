@@ -66,7 +66,7 @@ tc_grid_batch* new_batch(int32_t B, const int32_t* rb, const OutAlloc& oa) {
       b->buffer = b->alloc.alloc(b->alloc.ctx, b->bytes, (void*)oa.stream);
       if (!b->buffer) throw Error(TC_ERR_ALLOC, "allocator returned NULL for " + std::to_string(b->bytes) + " bytes");
     } else {
-      b->buffer = device_alloc_async(b->bytes, oa.stream);
+      b->buffer = batch_buffer_take(b->bytes, oa.stream, &b->cap);
     }
   } catch (...) {
     delete b;
@@ -103,7 +103,7 @@ void free_batch(tc_grid_batch* b) {
     if (b->has_alloc) {
       if (b->alloc.free) b->alloc.free(b->alloc.ctx, b->buffer, b->bytes, (void*)b->stream);
     } else {
-      device_free_async(b->buffer, b->stream);
+      batch_buffer_give(b->buffer, b->cap, b->device, b->stream);
     }
   }
   delete b;
@@ -384,6 +384,7 @@ tc_status tc_build_kernel_map(const tc_grid_batch* src, const tc_grid_batch* dst
 tc_status tc_scratch_release(void) {
   return guarded([&]() {
     tc::scratch_release_all();
+    tc::batch_buffers_release();
     return TC_OK;
   });
 }

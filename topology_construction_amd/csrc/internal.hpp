@@ -165,6 +165,12 @@ int scratch_acquire(size_t bytes, hipStream_t s, char** p);
 void scratch_give_back(int slot);
 void scratch_release_all();
 
+// Buffers of batches built without an allocator, cached per device and stream
+// between tc_batch_free and the next batch that fits (capacity in *cap).
+void* batch_buffer_take(size_t bytes, hipStream_t s, size_t* cap);
+void batch_buffer_give(void* p, size_t cap, int device, hipStream_t s);
+void batch_buffers_release();
+
 // Per-thread pinned host staging buffer (grows on demand, never shrinks).
 void* pinned_staging(size_t bytes);
 
@@ -302,6 +308,7 @@ struct tc_grid_batch {
   std::vector<int32_t> h_upper, h_lower, h_leaf;
   void* buffer = nullptr;
   size_t bytes = 0;
+  size_t cap = 0;  // buffer capacity when the library allocated it
   tc::Layout layout{};
   bool has_alloc = false;
   tc_allocator alloc{};

@@ -100,6 +100,86 @@ void scratch_release_all() {
   }
 }
 
+// ------------------------------------------------------------------ batch buffers
+// Buffers of batches built without an allocator: tc_batch_free hands them back
+// here, and the next batch on the same device and stream that fits (using at
+// least half of the buffer) takes one instead of allocating. Reuse is ordered
+// by that stream, as a stream-ordered free would be.
+namespace {
+struct CachedBuffer {
+  int device;
+  hipStream_t stream;
+  void* p;
+  size_t cap;
+};
+std::mutex g_buf_mu;
+std::vector<CachedBuffer> g_bufs;
+size_t g_buf_bytes = 0;
+constexpr size_t kBufCacheBytes = size_t(4) << 30;  // beyond this the oldest buffers are freed
+constexpr size_t kBufCacheCount = 64;
+}  // namespace
+
+void* batch_buffer_take(size_t bytes, hipStream_t s, size_t* cap) {
+  int dev = 0;
+  hip_check(hipGetDevice(&dev), "hipGetDevice");
+  {
+    std::lock_guard<std::mutex> lk(g_buf_mu);
+    int best = -1;
+    for (int i = 0; i < (int)g_bufs.size(); ++i) {
+      const CachedBuffer& c = g_bufs[i];
+      if (c.device != dev || c.stream != s || c.cap < bytes || c.cap / 2 > bytes) continue;
+      if (best < 0 || c.cap < g_bufs[best].cap) best = i;
+    }
+    if (best >= 0) {
+      void* p = g_bufs[best].p;
+      *cap = g_bufs[best].cap;
+      g_buf_bytes -= g_bufs[best].cap;
+      g_bufs.erase(g_bufs.begin() + best);
+      return p;
+    }
+  }
+  *cap = bytes ? bytes : 256;
+  return device_alloc_async(*cap, s);
+}
+
+void batch_buffer_give(void* p, size_t cap, int device, hipStream_t s) {
+  if (!p) return;
+  std::vector<CachedBuffer> drop;
+  {
+    std::lock_guard<std::mutex> lk(g_buf_mu);
+    g_bufs.push_back(CachedBuffer{device, s, p, cap});
+    g_buf_bytes += cap;
+    while (!g_bufs.empty() && (g_buf_bytes > kBufCacheBytes || g_bufs.size() > kBufCacheCount)) {
+      drop.push_back(g_bufs.front());
+      g_buf_bytes -= g_bufs.front().cap;
+      g_bufs.erase(g_bufs.begin());
+    }
+  }
+  for (const CachedBuffer& c : drop) {
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess) continue;
+    if (c.device != cur) (void)hipSetDevice(c.device);
+    device_free_async(c.p, c.stream);
+    if (c.device != cur) (void)hipSetDevice(cur);
+  }
+}
+
+void batch_buffers_release() {
+  std::vector<CachedBuffer> drop;
+  {
+    std::lock_guard<std::mutex> lk(g_buf_mu);
+    drop.swap(g_bufs);
+    g_buf_bytes = 0;
+  }
+  int cur = 0;
+  hip_check(hipGetDevice(&cur), "hipGetDevice");
+  for (const CachedBuffer& c : drop) {
+    if (c.device != cur) hip_check(hipSetDevice(c.device), "hipSetDevice");
+    device_free_async(c.p, c.stream);
+    if (c.device != cur) hip_check(hipSetDevice(cur), "hipSetDevice");
+  }
+}
+
 void Arena::commit() {
   if (base_) throw Error(TC_ERR_INTERNAL, "arena committed twice");
   slot_ = scratch_acquire(size_, stream_, &base_);

@@ -1093,7 +1093,9 @@ __device__ __forceinline__ void coarsen_place(u64 out[8], const u64 W[8], const 
     u64 placed = 0;
 #pragma unroll
     for (int r = 0; r < 4; ++r) placed |= ((v >> (16 * r)) & 0xfull) << ((4 * q.y + r) * 8 + 4 * q.z);
-    out[4 * q.x + x] |= placed;
+    // constant indices keep `out` in registers (a runtime index would put it in scratch memory)
+    out[x] |= q.x ? 0ull : placed;
+    out[4 + x] |= q.x ? placed : 0ull;
   }
 }
 

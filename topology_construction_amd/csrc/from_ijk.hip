@@ -44,11 +44,13 @@ __device__ __forceinline__ u64 wave_or_u64(u64 v) {
   return v;
 }
 
-template <bool kCheck>
-__device__ __forceinline__ void wave_or_into(u64* word, u64 bits, bool active) {
+// The union this lane has to OR into `word` (0 if none): the group's union when
+// the lane leads a group of lanes with the same word, its own bits when it is
+// left over after kDedupRounds groups.
+__device__ __forceinline__ u64 wave_merge_bits(const u64* word, u64 bits, bool active) {
   const int lane = threadIdx.x & (kWave - 1);
   u64 todo = __ballot(active);
-  u64 mine = 0;  // the union this lane ORs, if it leads a group
+  u64 mine = 0;
   for (int round = 0; todo && round < kDedupRounds; ++round) {
     const int leader = __builtin_ctzll(todo);
     const u64 lw = (u64)__shfl((long long)(uintptr_t)word, leader, kWave);
@@ -59,7 +61,38 @@ __device__ __forceinline__ void wave_or_into(u64* word, u64 bits, bool active) {
     todo &= ~sm;
   }
   if ((todo >> lane) & 1ull) mine = bits;
-  if (mine && (!kCheck || (*word & mine) != mine)) atomicOr((unsigned long long*)word, mine);
+  return mine;
+}
+
+// V independent sets of 64 voxels (one per slot): merge each, then issue every
+// slot's read (kCheck) and OR together.
+template <int V, bool kCheck>
+__device__ __forceinline__ void wave_or_into_v(u64* const word[V], const u64 bits[V], const bool active[V]) {
+  u64 mine[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) mine[v] = wave_merge_bits(word[v], bits[v], active[v]);
+  if (kCheck) {
+    u64 cur[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) cur[v] = mine[v] ? *word[v] : 0ull;
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+      if (mine[v] && (cur[v] & mine[v]) != mine[v]) atomicOr((unsigned long long*)word[v], mine[v]);
+  } else {
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+      if (mine[v]) atomicOr((unsigned long long*)word[v], mine[v]);
+  }
+}
+
+// Voxels per lane of the per-voxel kernels: slot v of a wave covers the 64
+// consecutive voxels base + 64 v + lane, and the slots' loads go out together.
+constexpr int kVoxPerLane = 4;
+constexpr int kVoxPerBlock = 256 * kVoxPerLane;
+
+__device__ __forceinline__ i64 vox_index(int v) {
+  return (i64)blockIdx.x * kVoxPerBlock + (threadIdx.x / kWave) * (kWave * kVoxPerLane) + v * kWave +
+         (threadIdx.x & (kWave - 1));
 }
 
 __device__ __forceinline__ u64 tile_hash(int32_t g, int32_t tx, int32_t ty, int32_t tz) {
@@ -159,33 +192,53 @@ __global__ void __launch_bounds__(256) k_tile_rank_scatter(const Key128* keys, c
 
 __global__ void __launch_bounds__(256) k_voxel_tile(const int32_t* rep, const int32_t* excl, const int32_t* rank_of,
                                                     i64 n, int32_t nt, int32_t* vtile, int32_t* flags) {
-  const i64 i = (i64)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
-  const int32_t r = rep[i];
-  const int32_t k = (r >= 0 && r < n) ? excl[r] : -1;
-  const int32_t t = (k >= 0 && k < nt) ? rank_of[k] : -1;
-  if (t < 0 || t >= nt) {
-    atomicOr(flags, 2);
-    vtile[i] = 0;
-    return;
+  constexpr int V = kVoxPerLane;
+  int32_t r[V], k[V], t[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const i64 i = vox_index(v);
+    r[v] = i < n ? rep[i] : -1;
   }
-  vtile[i] = t;
+#pragma unroll
+  for (int v = 0; v < V; ++v) k[v] = (r[v] >= 0 && r[v] < n) ? excl[r[v]] : -1;
+#pragma unroll
+  for (int v = 0; v < V; ++v) t[v] = (k[v] >= 0 && k[v] < nt) ? rank_of[k[v]] : -1;
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const i64 i = vox_index(v);
+    if (i >= n) continue;
+    if (t[v] < 0 || t[v] >= nt) {
+      atomicOr(flags, 2);
+      vtile[i] = 0;
+    } else {
+      vtile[i] = t[v];
+    }
+  }
 }
 
 __global__ void __launch_bounds__(256) k_voxel_mark_lower(const int32_t* ijk, const int32_t* vtile, i64 n,
                                                           u64* tile_child) {
-  const i64 i = (i64)blockIdx.x * 256 + threadIdx.x;
-  const bool in = i < n;
-  u64* word = tile_child;
-  u64 b = 0;
-  if (in) {
-    const i64 t = vtile[i];
-    const int kx = (ijk[i * 3] >> 7) & 31, ky = (ijk[i * 3 + 1] >> 7) & 31, kz = (ijk[i * 3 + 2] >> 7) & 31;
-    const int bit = (kx * 32 + ky) * 32 + kz;
-    word = &tile_child[t * 512 + (bit >> 6)];
-    b = 1ull << (bit & 63);
+  constexpr int V = kVoxPerLane;
+  u64* word[V];
+  u64 b[V];
+  bool in[V];
+  int32_t t[V], x[V], y[V], z[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const i64 i = vox_index(v);
+    in[v] = i < n;
+    t[v] = in[v] ? vtile[i] : 0;
+    x[v] = in[v] ? ijk[i * 3] : 0;
+    y[v] = in[v] ? ijk[i * 3 + 1] : 0;
+    z[v] = in[v] ? ijk[i * 3 + 2] : 0;
   }
-  wave_or_into<true>(word, b, in);
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const int bit = ((((x[v] >> 7) & 31) * 32 + ((y[v] >> 7) & 31)) * 32) + ((z[v] >> 7) & 31);
+    word[v] = in[v] ? &tile_child[(i64)t[v] * 512 + (bit >> 6)] : tile_child;
+    b[v] = in[v] ? 1ull << (bit & 63) : 0ull;
+  }
+  wave_or_into_v<V, true>(word, b, in);
 }
 
 // All lanes stay active to the end of these kernels (no early return), so the
@@ -194,60 +247,112 @@ __global__ void __launch_bounds__(256) k_voxel_cand(const int32_t* ijk, const in
                                                     const u64* tile_child, const uint16_t* tile_prefix,
                                                     const int32_t* tile_lower_base, int32_t nc, int32_t* vcand,
                                                     int4* cand_origin, u64* cand_child, int32_t* flags) {
-  const i64 i = (i64)blockIdx.x * 256 + threadIdx.x;
+  constexpr int V = kVoxPerLane;
   const int lane = threadIdx.x & (kWave - 1);
-  bool ok = i < n;
-  int32_t c = -1, x = 0, y = 0, z = 0;
-  i64 t = 0;
-  if (ok) {
-    t = vtile[i];
-    x = ijk[i * 3];
-    y = ijk[i * 3 + 1];
-    z = ijk[i * 3 + 2];
-    const int bit = (((x >> 7) & 31) * 32 + ((y >> 7) & 31)) * 32 + ((z >> 7) & 31);
-    const int w = bit >> 6, b = bit & 63;
-    c = tile_lower_base[t] + tile_prefix[t * 512 + w] + popc64(tile_child[t * 512 + w] & ((1ull << b) - 1));
-    if (c < 0 || c >= nc) {
-      atomicOr(flags, 2);
-      c = -1;
-      ok = false;
+  bool ok[V];
+  int32_t t[V], x[V], y[V], z[V], c[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const i64 i = vox_index(v);
+    ok[v] = i < n;
+    t[v] = ok[v] ? vtile[i] : 0;
+    x[v] = ok[v] ? ijk[i * 3] : 0;
+    y[v] = ok[v] ? ijk[i * 3 + 1] : 0;
+    z[v] = ok[v] ? ijk[i * 3 + 2] : 0;
+  }
+  int w[V], bb[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const int bit = (((x[v] >> 7) & 31) * 32 + ((y[v] >> 7) & 31)) * 32 + ((z[v] >> 7) & 31);
+    w[v] = bit >> 6;
+    bb[v] = bit & 63;
+  }
+  int32_t base[V];
+  uint16_t pre[V];
+  u64 cw[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const i64 tt = ok[v] ? t[v] : 0;
+    base[v] = tile_lower_base[tt];
+    pre[v] = tile_prefix[tt * 512 + w[v]];
+    cw[v] = tile_child[tt * 512 + w[v]];
+  }
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const i64 i = vox_index(v);
+    c[v] = -1;
+    if (ok[v]) {
+      c[v] = base[v] + pre[v] + popc64(cw[v] & ((1ull << bb[v]) - 1));
+      if (c[v] < 0 || c[v] >= nc) {
+        atomicOr(flags, 2);
+        c[v] = -1;
+        ok[v] = false;
+      }
+      vcand[i] = c[v];
     }
-    vcand[i] = c;
   }
   // one lane per run of equal candidates writes the candidate's origin
-  const int32_t cprev = __shfl_up(c, 1, kWave);
-  if (ok && (lane == 0 || cprev != c))
-    cand_origin[c] = make_int4((x >> 7) * 128, (y >> 7) * 128, (z >> 7) * 128, (int32_t)t);
-  const int lb = (((x >> 3) & 15) * 16 + ((y >> 3) & 15)) * 16 + ((z >> 3) & 15);
-  wave_or_into<true>(ok ? &cand_child[(i64)c * 64 + (lb >> 6)] : cand_child, ok ? 1ull << (lb & 63) : 0, ok);
+  u64* word[V];
+  u64 bits[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const int32_t cprev = __shfl_up(c[v], 1, kWave);
+    if (ok[v] && (lane == 0 || cprev != c[v]))
+      cand_origin[c[v]] = make_int4((x[v] >> 7) * 128, (y[v] >> 7) * 128, (z[v] >> 7) * 128, t[v]);
+    const int lb = (((x[v] >> 3) & 15) * 16 + ((y[v] >> 3) & 15)) * 16 + ((z[v] >> 3) & 15);
+    word[v] = ok[v] ? &cand_child[(i64)c[v] * 64 + (lb >> 6)] : cand_child;
+    bits[v] = ok[v] ? 1ull << (lb & 63) : 0ull;
+  }
+  wave_or_into_v<V, true>(word, bits, ok);
 }
 
 __global__ void __launch_bounds__(256) k_voxel_leaf(const int32_t* ijk, const int32_t* vcand, i64 n,
                                                     const u64* cand_child, const uint16_t* cand_prefix,
                                                     const i64* cand_scan, i64 n_leaf, u64* leaf_mask) {
-  const i64 i = (i64)blockIdx.x * 256 + threadIdx.x;
-  bool ok = i < n;
-  u64* word = leaf_mask;
-  u64 bits = 0;
-  if (ok) {
-    const i64 c = vcand[i];
-    if (c < 0) {
-      ok = false;
-    } else {
-      const int32_t x = ijk[i * 3], y = ijk[i * 3 + 1], z = ijk[i * 3 + 2];
-      const int lb = (((x >> 3) & 15) * 16 + ((y >> 3) & 15)) * 16 + ((z >> 3) & 15);
-      const int w = lb >> 6, b = lb & 63;
-      const i64 leaf = (i64)(cand_scan[c] & 0xffffffffll) + cand_prefix[c * 64 + w] +
-                       popc64(cand_child[c * 64 + w] & ((1ull << b) - 1));
+  constexpr int V = kVoxPerLane;
+  bool ok[V];
+  int32_t c[V], x[V], y[V], z[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const i64 i = vox_index(v);
+    const bool in = i < n;
+    c[v] = in ? vcand[i] : -1;
+    x[v] = in ? ijk[i * 3] : 0;
+    y[v] = in ? ijk[i * 3 + 1] : 0;
+    z[v] = in ? ijk[i * 3 + 2] : 0;
+    ok[v] = in && c[v] >= 0;
+  }
+  int w[V], b[V];
+  i64 sc[V];
+  uint16_t pre[V];
+  u64 cw[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const int lb = (((x[v] >> 3) & 15) * 16 + ((y[v] >> 3) & 15)) * 16 + ((z[v] >> 3) & 15);
+    w[v] = lb >> 6;
+    b[v] = lb & 63;
+    const i64 cc = ok[v] ? c[v] : 0;
+    sc[v] = cand_scan[cc];
+    pre[v] = cand_prefix[cc * 64 + w[v]];
+    cw[v] = cand_child[cc * 64 + w[v]];
+  }
+  u64* word[V];
+  u64 bits[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    word[v] = leaf_mask;
+    bits[v] = 0;
+    if (ok[v]) {
+      const i64 leaf = (i64)(sc[v] & 0xffffffffll) + pre[v] + popc64(cw[v] & ((1ull << b[v]) - 1));
       if (leaf < 0 || leaf >= n_leaf) {  // consistency guard
-        ok = false;
+        ok[v] = false;
       } else {
-        word = &leaf_mask[leaf * 8 + (x & 7)];
-        bits = 1ull << ((y & 7) * 8 + (z & 7));
+        word[v] = &leaf_mask[leaf * 8 + (x[v] & 7)];
+        bits[v] = 1ull << ((y[v] & 7) * 8 + (z[v] & 7));
       }
     }
   }
-  wave_or_into<false>(word, bits, ok);
+  wave_or_into_v<V, false>(word, bits, ok);
 }
 
 static int32_t read_i32(const int32_t* d, hipStream_t s) {
@@ -338,11 +443,11 @@ tc_grid_batch* build_from_ijk(const int32_t* d_ijk, const int64_t* h_off, int32_
   sort_pairs_128(keys, vals, nt, tile_key_bits(B), s);
   launch("k_tile_rank_scatter", k_tile_rank_scatter, ceil_div(nt, 256), 256, s, (const Key128*)keys,
          (const uint32_t*)vals, (i64)nt, rank_of, ts.utile);
-  launch("k_voxel_tile", k_voxel_tile, ceil_div(N, 256), 256, s, (const int32_t*)rep, (const int32_t*)excl,
+  launch("k_voxel_tile", k_voxel_tile, ceil_div(N, kVoxPerBlock), 256, s, (const int32_t*)rep, (const int32_t*)excl,
          (const int32_t*)rank_of, N, nt, vtile, flags);
   tree_tile_ranges(ts, B, s);
   fill_u64(ts.tile_child, 0, 512 * (i64)nt, nullptr, 1, s);
-  launch("k_voxel_mark_lower", k_voxel_mark_lower, ceil_div(N, 256), 256, s, d_ijk, (const int32_t*)vtile, N,
+  launch("k_voxel_mark_lower", k_voxel_mark_lower, ceil_div(N, kVoxPerBlock), 256, s, d_ijk, (const int32_t*)vtile, N,
          ts.tile_child);
   tree_rank_tiles(ts, s);
   const int32_t nc = read_i32(ts.d_num_cands, s);
@@ -371,7 +476,7 @@ tc_grid_batch* build_from_ijk(const int32_t* d_ijk, const int64_t* h_off, int32_
   ts.flags = ts.readback;
   fill_i32(ts.readback, 0, 1, nullptr, 1, s);
   fill_u64(ts.cand_child, 0, 64 * (i64)nc, nullptr, 1, s);
-  launch("k_voxel_cand", k_voxel_cand, ceil_div(N, 256), 256, s, d_ijk, (const int32_t*)vtile, N,
+  launch("k_voxel_cand", k_voxel_cand, ceil_div(N, kVoxPerBlock), 256, s, d_ijk, (const int32_t*)vtile, N,
          (const u64*)ts.tile_child, (const uint16_t*)ts.tile_prefix, (const int32_t*)ts.tile_lower_base, nc, vcand,
          ts.cand_origin, ts.cand_child, ts.flags);
   tree_counts(ts, B, s);
@@ -395,7 +500,7 @@ tc_grid_batch* build_from_ijk(const int32_t* d_ijk, const int64_t* h_off, int32_
     post.commit();
     tree_write_nodes(ts, ov, post.at<int32_t>(o_lc), s);
     fill_u64(ov.leaf_mask, 0, 8 * L, nullptr, 1, s);
-    launch("k_voxel_leaf", k_voxel_leaf, ceil_div(N, 256), 256, s, d_ijk, (const int32_t*)vcand, N,
+    launch("k_voxel_leaf", k_voxel_leaf, ceil_div(N, kVoxPerBlock), 256, s, d_ijk, (const int32_t*)vcand, N,
            (const u64*)ts.cand_child, (const uint16_t*)ts.cand_prefix, (const i64*)ts.cand_scan, L,
            ov.leaf_mask);
     tree_leaf_stats(ov, post.at<uint32_t>(o_box), post.at<int32_t>(o_inrun), post.at<i64>(o_part), s);

@@ -15,17 +15,20 @@
 
 namespace tc {
 
-__global__ void __launch_bounds__(256) k_voxel_grid(const i64* offsets, int32_t B, i64 n, int32_t* vgrid) {
-  const i64 i = (i64)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
-  int32_t lo = 0, hi = B - 1;  // last g with offsets[g] <= i
+// Member of voxel i: the last g with offsets[g] <= i (binary search).
+__device__ __forceinline__ int32_t member_of(const i64* offsets, int32_t B, i64 i) {
+  int32_t lo = 0, hi = B - 1;
   while (lo < hi) {
     const int32_t mid = lo + (hi - lo + 1) / 2;
     if (offsets[mid] <= i) lo = mid;
     else hi = mid - 1;
   }
-  vgrid[i] = lo;
+  return lo;
 }
+
+// With at most kLdsMembers members the hashing kernel searches the member
+// offsets in LDS.
+constexpr int kLdsMembers = 4095;
 
 // Voxels that arrive together usually share their tile, lower and leaf, so the
 // lanes of a wave first merge the bits they set in the same 64-bit word (up to
@@ -110,8 +113,8 @@ __device__ __forceinline__ u64 tile_hash(int32_t g, int32_t tx, int32_t ty, int3
 // table[H] holds -1 or the index of the first voxel seen for a (grid, tile).
 // Every probe sequence ends within H steps because fewer than H voxels exist.
 // Returns the representative voxel of voxel i's (grid, tile).
-__device__ int32_t tile_probe(const int32_t* ijk, const int32_t* vgrid, i64 i, int32_t g, int32_t tx, int32_t ty,
-                              int32_t tz, int32_t* table, i64 H, int32_t* flags) {
+__device__ int32_t tile_probe(const int32_t* ijk, const i64* offsets, int32_t B, i64 i, int32_t g, int32_t tx,
+                              int32_t ty, int32_t tz, int32_t* table, i64 H, int32_t* flags) {
   i64 h = (i64)(tile_hash(g, tx, ty, tz) & (u64)(H - 1));
   for (i64 probe = 0; probe < H; ++probe) {
     int32_t e = __hip_atomic_load(&table[h], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -120,8 +123,8 @@ __device__ int32_t tile_probe(const int32_t* ijk, const int32_t* vgrid, i64 i, i
       if (old < 0) return (int32_t)i;
       e = old;
     }
-    if (vgrid[e] == g && (ijk[(i64)e * 3] >> 12) == tx && (ijk[(i64)e * 3 + 1] >> 12) == ty &&
-        (ijk[(i64)e * 3 + 2] >> 12) == tz)
+    if ((ijk[(i64)e * 3] >> 12) == tx && (ijk[(i64)e * 3 + 1] >> 12) == ty && (ijk[(i64)e * 3 + 2] >> 12) == tz &&
+        member_of(offsets, B, e) == g)
       return e;
     h = (h + 1) & (H - 1);
   }
@@ -130,48 +133,59 @@ __device__ int32_t tile_probe(const int32_t* ijk, const int32_t* vgrid, i64 i, i
 }
 
 // Lanes of a wave that share a (grid, tile) probe once, through one leader.
-__global__ void __launch_bounds__(256) k_hash_tiles(const int32_t* ijk, const int32_t* vgrid, i64 n, int32_t* table,
-                                                    i64 H, int32_t* rep, int32_t* flags) {
-  const i64 i = (i64)blockIdx.x * 256 + threadIdx.x;
+// Also flags the representatives (rep[i] == i): exactly the voxels whose probe
+// inserted their own index. Blocks walk 256-voxel chunks (grid-stride), so the
+// member offsets are staged in LDS once per block.
+__global__ void __launch_bounds__(256) k_hash_tiles(const int32_t* ijk, const i64* offsets, int32_t B, i64 n,
+                                                    int32_t* table, i64 H, int32_t* rep, int32_t* is_rep,
+                                                    int32_t* flags) {
+  __shared__ i64 s_off[kLdsMembers + 1];
+  const bool lds = B <= kLdsMembers;  // uniform
+  if (lds) {
+    for (int g = threadIdx.x; g <= B; g += 256) s_off[g] = offsets[g];
+    __syncthreads();
+  }
+  const i64* off = lds ? s_off : offsets;
   const int lane = threadIdx.x & (kWave - 1);
-  const bool in = i < n;
-  int32_t g = 0, tx = 0, ty = 0, tz = 0;
-  if (in) {
-    g = vgrid[i];
-    tx = ijk[i * 3] >> 12;
-    ty = ijk[i * 3 + 1] >> 12;
-    tz = ijk[i * 3 + 2] >> 12;
+  for (i64 base = (i64)blockIdx.x * 256; base < n; base += (i64)gridDim.x * 256) {  // uniform per block
+    const i64 i = base + threadIdx.x;
+    const bool in = i < n;
+    int32_t g = 0, tx = 0, ty = 0, tz = 0;
+    if (in) {
+      g = member_of(off, B, i);
+      tx = ijk[i * 3] >> 12;
+      ty = ijk[i * 3 + 1] >> 12;
+      tz = ijk[i * 3 + 2] >> 12;
+    }
+    int32_t mine = -1;
+    u64 todo = __ballot(in);
+    for (int round = 0; todo && round < kDedupRounds; ++round) {
+      const int leader = __builtin_ctzll(todo);
+      const int32_t lg = __shfl(g, leader, kWave), lx = __shfl(tx, leader, kWave),
+                    ly = __shfl(ty, leader, kWave), lz = __shfl(tz, leader, kWave);
+      const bool same = ((todo >> lane) & 1ull) && g == lg && tx == lx && ty == ly && tz == lz;
+      const u64 sm = __ballot(same);
+      int32_t r = -1;
+      if (lane == leader) r = tile_probe(ijk, off, B, i, g, tx, ty, tz, table, H, flags);
+      r = __shfl(r, leader, kWave);
+      if (same) mine = r;
+      todo &= ~sm;
+    }
+    if ((todo >> lane) & 1ull) mine = tile_probe(ijk, off, B, i, g, tx, ty, tz, table, H, flags);
+    if (in) {
+      rep[i] = mine;
+      is_rep[i] = mine == i ? 1 : 0;
+    }
   }
-  int32_t mine = -1;
-  u64 todo = __ballot(in);
-  for (int round = 0; todo && round < kDedupRounds; ++round) {
-    const int leader = __builtin_ctzll(todo);
-    const int32_t lg = __shfl(g, leader, kWave), lx = __shfl(tx, leader, kWave), ly = __shfl(ty, leader, kWave),
-                  lz = __shfl(tz, leader, kWave);
-    const bool same = ((todo >> lane) & 1ull) && g == lg && tx == lx && ty == ly && tz == lz;
-    const u64 sm = __ballot(same);
-    int32_t r = -1;
-    if (lane == leader) r = tile_probe(ijk, vgrid, i, g, tx, ty, tz, table, H, flags);
-    r = __shfl(r, leader, kWave);
-    if (same) mine = r;
-    todo &= ~sm;
-  }
-  if ((todo >> lane) & 1ull) mine = tile_probe(ijk, vgrid, i, g, tx, ty, tz, table, H, flags);
-  if (in) rep[i] = mine;
 }
 
-__global__ void __launch_bounds__(256) k_rep_flags(const int32_t* rep, i64 n, int32_t* flag) {
-  const i64 i = (i64)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
-  flag[i] = rep[i] == i ? 1 : 0;
-}
-
-__global__ void __launch_bounds__(256) k_tile_compact(const int32_t* ijk, const int32_t* vgrid, const int32_t* flag,
-                                                      const int32_t* excl, i64 n, Key128* keys, uint32_t* vals) {
+__global__ void __launch_bounds__(256) k_tile_compact(const int32_t* ijk, const i64* offsets, int32_t B,
+                                                      const int32_t* flag, const int32_t* excl, i64 n, Key128* keys,
+                                                      uint32_t* vals) {
   const i64 i = (i64)blockIdx.x * 256 + threadIdx.x;
   if (i >= n || !flag[i]) return;
   const int32_t k = excl[i];
-  const u64 g = (uint32_t)vgrid[i];
+  const u64 g = (uint32_t)member_of(offsets, B, i);
   const u64 tx = (u64)((ijk[i * 3] >> 12) + kTileBias), ty = (u64)((ijk[i * 3 + 1] >> 12) + kTileBias),
             tz = (u64)((ijk[i * 3 + 2] >> 12) + kTileBias);
   keys[k] = Key128{((g & 15ull) << 60) | (tx << 40) | (ty << 20) | tz, g >> 4};
@@ -371,7 +385,6 @@ tc_grid_batch* build_from_ijk(const int32_t* d_ijk, const int64_t* h_off, int32_
   // stage 1: voxel -> grid, tile representatives, unique tiles
   Arena a1(s);
   const size_t o_off = a1.reserve(8 * ((i64)B + 1));
-  const size_t o_vg = a1.reserve(4 * N);
   const size_t o_tab = a1.reserve(4 * H);
   const size_t o_rep = a1.reserve(4 * N);
   const size_t o_flag = a1.reserve(4 * N);
@@ -381,7 +394,6 @@ tc_grid_batch* build_from_ijk(const int32_t* d_ijk, const int64_t* h_off, int32_
   const size_t o_rb = a1.reserve(4 * 4);
   a1.commit();
   i64* d_off = a1.at<i64>(o_off);
-  int32_t* vgrid = a1.at<int32_t>(o_vg);
   int32_t* table = a1.at<int32_t>(o_tab);
   int32_t* rep = a1.at<int32_t>(o_rep);
   int32_t* flag = a1.at<int32_t>(o_flag);
@@ -396,10 +408,8 @@ tc_grid_batch* build_from_ijk(const int32_t* d_ijk, const int64_t* h_off, int32_
   hip_check(hipMemcpyAsync(d_off, h_stage, off_bytes, hipMemcpyHostToDevice, s), "offsets upload");
   fill_i32(flags, 0, 1, nullptr, 1, s);
   fill_i32(table, -1, H, nullptr, 1, s);
-  launch("k_voxel_grid", k_voxel_grid, ceil_div(N, 256), 256, s, (const i64*)d_off, B, N, vgrid);
-  launch("k_hash_tiles", k_hash_tiles, ceil_div(N, 256), 256, s, d_ijk, (const int32_t*)vgrid, N, table, H, rep,
-         flags);
-  launch("k_rep_flags", k_rep_flags, ceil_div(N, 256), 256, s, (const int32_t*)rep, N, flag);
+  launch("k_hash_tiles", k_hash_tiles, std::min<i64>(ceil_div(N, 256), 8192), 256, s, d_ijk, (const i64*)d_off, B, N,
+         table, H, rep, flag, flags);
   scan_excl_i32(flag, excl, N, nullptr, s);
   hip_check(hipStreamSynchronize(s), "hipStreamSynchronize");  // the pinned offsets are consumed
   const int32_t nt = read_i32(excl + N, s);
@@ -438,7 +448,7 @@ tc_grid_batch* build_from_ijk(const int32_t* d_ijk, const int64_t* h_off, int32_
   int32_t* rank_of = a2.at<int32_t>(o_rank);
 
   fill_i32(ts.d_num_tiles, nt, 1, nullptr, 1, s);
-  launch("k_tile_compact", k_tile_compact, ceil_div(N, 256), 256, s, d_ijk, (const int32_t*)vgrid,
+  launch("k_tile_compact", k_tile_compact, ceil_div(N, 256), 256, s, d_ijk, (const i64*)d_off, B,
          (const int32_t*)flag, (const int32_t*)excl, N, keys, vals);
   sort_pairs_128(keys, vals, nt, tile_key_bits(B), s);
   launch("k_tile_rank_scatter", k_tile_rank_scatter, ceil_div(nt, 256), 256, s, (const Key128*)keys,

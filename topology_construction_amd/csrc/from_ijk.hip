@@ -30,16 +30,12 @@ __device__ __forceinline__ int32_t member_of(const i64* offsets, int32_t B, i64 
 // offsets in LDS.
 constexpr int kLdsMembers = 4095;
 
-// Voxels that arrive together usually share their tile, lower and leaf, so the
-// lanes of a wave first merge the bits they set in the same 64-bit word (up to
-// kDedupRounds distinct words, found with ballots and shuffles, no memory
-// traffic); then every group's leader issues one OR for the union, all groups
-// at once. Lanes still waiting after kDedupRounds words OR their own bit. With
-// kCheck the leaders first read their word and skip the atomic when the bits
-// are already set: the words of tiles and lower nodes are shared by many waves
-// and same-address device atomics serialize, whereas leaf words mostly receive
-// new bits and are ORed without the read.
+// Voxels that arrive together usually share their tile, so the lanes of a
+// wave that hash the same (grid, tile) probe once, through one leader (up to
+// kDedupRounds distinct tiles per wave, found with ballots and shuffles); the
+// rest probe on their own.
 constexpr int kDedupRounds = 8;
+
 
 __device__ __forceinline__ u64 wave_or_u64(u64 v) {
 #pragma unroll
@@ -47,9 +43,10 @@ __device__ __forceinline__ u64 wave_or_u64(u64 v) {
   return v;
 }
 
-// The union this lane has to OR into `word` (0 if none): the group's union when
-// the lane leads a group of lanes with the same word, its own bits when it is
-// left over after kDedupRounds groups.
+// Ballot merge, for words that most voxels of a wave share (a tile's lower
+// bits): the union this lane has to OR into `word` (0 if none) is its group's
+// union when it leads a group of lanes with the same word, or its own bits when
+// it is left over after kDedupRounds groups.
 __device__ __forceinline__ u64 wave_merge_bits(const u64* word, u64 bits, bool active) {
   const int lane = threadIdx.x & (kWave - 1);
   u64 todo = __ballot(active);
@@ -67,25 +64,53 @@ __device__ __forceinline__ u64 wave_merge_bits(const u64* word, u64 bits, bool a
   return mine;
 }
 
-// V independent sets of 64 voxels (one per slot): merge each, then issue every
-// slot's read (kCheck) and OR together.
-template <int V, bool kCheck>
-__device__ __forceinline__ void wave_or_into_v(u64* const word[V], const u64 bits[V], const bool active[V]) {
-  u64 mine[V];
-#pragma unroll
-  for (int v = 0; v < V; ++v) mine[v] = wave_merge_bits(word[v], bits[v], active[v]);
-  if (kCheck) {
-    u64 cur[V];
-#pragma unroll
-    for (int v = 0; v < V; ++v) cur[v] = mine[v] ? *word[v] : 0ull;
-#pragma unroll
-    for (int v = 0; v < V; ++v)
-      if (mine[v] && (cur[v] & mine[v]) != mine[v]) atomicOr((unsigned long long*)word[v], mine[v]);
-  } else {
-#pragma unroll
-    for (int v = 0; v < V; ++v)
-      if (mine[v]) atomicOr((unsigned long long*)word[v], mine[v]);
+// Candidate and leaf words are many (about ten leaf words per 64 consecutive
+// voxels of a shell, ~95 per 1024): there the block ORs the bits of its
+// kVoxPerBlock voxels into an LDS hash table keyed by word address (LDS
+// compare-and-swap claims a key, LDS OR merges the bits), then ORs each
+// distinct word once, all of them at once. With kCheck the global word is read
+// first and the OR skipped when its bits are already set.
+constexpr int kBlockTable = 2048;  // entries; at most kVoxPerBlock keys, so probes stay short
+
+__device__ __forceinline__ void table_clear(unsigned long long* key, unsigned long long* val) {
+  for (int e = threadIdx.x; e < kBlockTable; e += 256) {
+    key[e] = 0ull;
+    val[e] = 0ull;
   }
+}
+
+// Every insert finds its key or a free entry within kBlockTable probes because
+// the table holds at most kVoxPerBlock keys.
+__device__ __forceinline__ void table_or(unsigned long long* key, unsigned long long* val, const u64* word, u64 bits) {
+  const unsigned long long k = (unsigned long long)(uintptr_t)word;
+  unsigned h = (unsigned)(((k >> 3) * 0x9e3779b97f4a7c15ull) >> 53);  // 11 bits
+  for (int probe = 0; probe < kBlockTable; ++probe) {
+    const unsigned long long prev = atomicCAS(&key[h], 0ull, k);
+    if (prev == 0ull || prev == k) {
+      atomicOr(&val[h], (unsigned long long)bits);
+      return;
+    }
+    h = (h + 1) & (kBlockTable - 1);
+  }
+}
+
+template <bool kCheck>
+__device__ __forceinline__ void table_flush(const unsigned long long* key, const unsigned long long* val) {
+  constexpr int kPer = kBlockTable / 256;
+  unsigned long long k[kPer], v[kPer], cur[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    k[j] = key[threadIdx.x + 256 * j];
+    v[j] = val[threadIdx.x + 256 * j];
+  }
+  if (kCheck) {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) cur[j] = k[j] ? *reinterpret_cast<const u64*>((uintptr_t)k[j]) : 0ull;
+  }
+#pragma unroll
+  for (int j = 0; j < kPer; ++j)
+    if (k[j] && (!kCheck || (cur[j] & v[j]) != v[j]))
+      atomicOr(reinterpret_cast<unsigned long long*>((uintptr_t)k[j]), v[j]);
 }
 
 // Voxels per lane of the per-voxel kernels: slot v of a wave covers the 64
@@ -252,7 +277,14 @@ __global__ void __launch_bounds__(256) k_voxel_mark_lower(const int32_t* ijk, co
     word[v] = in[v] ? &tile_child[(i64)t[v] * 512 + (bit >> 6)] : tile_child;
     b[v] = in[v] ? 1ull << (bit & 63) : 0ull;
   }
-  wave_or_into_v<V, true>(word, b, in);
+  u64 mine[V], cur[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) mine[v] = wave_merge_bits(word[v], b[v], in[v]);
+#pragma unroll
+  for (int v = 0; v < V; ++v) cur[v] = mine[v] ? *word[v] : 0ull;  // the reads go out together
+#pragma unroll
+  for (int v = 0; v < V; ++v)
+    if (mine[v] && (cur[v] & mine[v]) != mine[v]) atomicOr((unsigned long long*)word[v], mine[v]);
 }
 
 // All lanes stay active to the end of these kernels (no early return), so the
@@ -262,6 +294,8 @@ __global__ void __launch_bounds__(256) k_voxel_cand(const int32_t* ijk, const in
                                                     const int32_t* tile_lower_base, int32_t nc, int32_t* vcand,
                                                     int4* cand_origin, u64* cand_child, int32_t* flags) {
   constexpr int V = kVoxPerLane;
+  __shared__ unsigned long long s_key[kBlockTable], s_val[kBlockTable];
+  table_clear(s_key, s_val);
   const int lane = threadIdx.x & (kWave - 1);
   bool ok[V];
   int32_t t[V], x[V], y[V], z[V], c[V];
@@ -317,13 +351,20 @@ __global__ void __launch_bounds__(256) k_voxel_cand(const int32_t* ijk, const in
     word[v] = ok[v] ? &cand_child[(i64)c[v] * 64 + (lb >> 6)] : cand_child;
     bits[v] = ok[v] ? 1ull << (lb & 63) : 0ull;
   }
-  wave_or_into_v<V, true>(word, bits, ok);
+  __syncthreads();  // the cleared table
+#pragma unroll
+  for (int v = 0; v < V; ++v)
+    if (ok[v]) table_or(s_key, s_val, word[v], bits[v]);
+  __syncthreads();
+  table_flush<true>(s_key, s_val);
 }
 
 __global__ void __launch_bounds__(256) k_voxel_leaf(const int32_t* ijk, const int32_t* vcand, i64 n,
                                                     const u64* cand_child, const uint16_t* cand_prefix,
                                                     const i64* cand_scan, i64 n_leaf, u64* leaf_mask) {
   constexpr int V = kVoxPerLane;
+  __shared__ unsigned long long s_key[kBlockTable], s_val[kBlockTable];
+  table_clear(s_key, s_val);
   bool ok[V];
   int32_t c[V], x[V], y[V], z[V];
 #pragma unroll
@@ -366,7 +407,12 @@ __global__ void __launch_bounds__(256) k_voxel_leaf(const int32_t* ijk, const in
       }
     }
   }
-  wave_or_into_v<V, false>(word, bits, ok);
+  __syncthreads();  // the cleared table
+#pragma unroll
+  for (int v = 0; v < V; ++v)
+    if (ok[v]) table_or(s_key, s_val, word[v], bits[v]);
+  __syncthreads();
+  table_flush<false>(s_key, s_val);
 }
 
 static int32_t read_i32(const int32_t* d, hipStream_t s) {

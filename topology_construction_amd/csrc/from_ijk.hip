@@ -157,47 +157,67 @@ __device__ int32_t tile_probe(const int32_t* ijk, const i64* offsets, int32_t B,
   return (int32_t)i;
 }
 
-// Lanes of a wave that share a (grid, tile) probe once, through one leader.
-// Also flags the representatives (rep[i] == i): exactly the voxels whose probe
-// inserted their own index. Blocks walk 256-voxel chunks (grid-stride), so the
-// member offsets are staged in LDS once per block.
+// Lanes of a wave that share a (grid, tile) probe once, through one leader, and
+// a key equal to the wave's previous one reuses its result without probing
+// (voxels that arrive together share their tile, so one probe per wave is
+// typical). Four voxels per lane (kVoxPerLane slots), their loads and member
+// searches together. Also flags the representatives (rep[i] == i): exactly the
+// voxels whose probe inserted their own index.
 __global__ void __launch_bounds__(256) k_hash_tiles(const int32_t* ijk, const i64* offsets, int32_t B, i64 n,
                                                     int32_t* table, i64 H, int32_t* rep, int32_t* is_rep,
                                                     int32_t* flags) {
+  constexpr int V = kVoxPerLane;
   __shared__ i64 s_off[kLdsMembers + 1];
   const bool lds = B <= kLdsMembers;  // uniform
+  const int lane = threadIdx.x & (kWave - 1);
+  bool in[V];
+  int32_t tx[V], ty[V], tz[V], g[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const i64 i = vox_index(v);
+    in[v] = i < n;
+    tx[v] = in[v] ? ijk[i * 3] >> 12 : 0;
+    ty[v] = in[v] ? ijk[i * 3 + 1] >> 12 : 0;
+    tz[v] = in[v] ? ijk[i * 3 + 2] >> 12 : 0;
+  }
   if (lds) {
-    for (int g = threadIdx.x; g <= B; g += 256) s_off[g] = offsets[g];
+    for (int k = threadIdx.x; k <= B; k += 256) s_off[k] = offsets[k];
     __syncthreads();
   }
   const i64* off = lds ? s_off : offsets;
-  const int lane = threadIdx.x & (kWave - 1);
-  for (i64 base = (i64)blockIdx.x * 256; base < n; base += (i64)gridDim.x * 256) {  // uniform per block
-    const i64 i = base + threadIdx.x;
-    const bool in = i < n;
-    int32_t g = 0, tx = 0, ty = 0, tz = 0;
-    if (in) {
-      g = member_of(off, B, i);
-      tx = ijk[i * 3] >> 12;
-      ty = ijk[i * 3 + 1] >> 12;
-      tz = ijk[i * 3 + 2] >> 12;
-    }
+#pragma unroll
+  for (int v = 0; v < V; ++v) g[v] = in[v] ? member_of(off, B, vox_index(v)) : 0;
+  // the wave's last resolved key and its representative (uniform)
+  int32_t kg = -1, kx = 0, ky = 0, kz = 0, krep = -1;
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const i64 i = vox_index(v);
     int32_t mine = -1;
-    u64 todo = __ballot(in);
+    u64 todo = __ballot(in[v]);
     for (int round = 0; todo && round < kDedupRounds; ++round) {
       const int leader = __builtin_ctzll(todo);
-      const int32_t lg = __shfl(g, leader, kWave), lx = __shfl(tx, leader, kWave),
-                    ly = __shfl(ty, leader, kWave), lz = __shfl(tz, leader, kWave);
-      const bool same = ((todo >> lane) & 1ull) && g == lg && tx == lx && ty == ly && tz == lz;
+      const int32_t lg = __shfl(g[v], leader, kWave), lx = __shfl(tx[v], leader, kWave),
+                    ly = __shfl(ty[v], leader, kWave), lz = __shfl(tz[v], leader, kWave);
+      const bool same = ((todo >> lane) & 1ull) && g[v] == lg && tx[v] == lx && ty[v] == ly && tz[v] == lz;
       const u64 sm = __ballot(same);
-      int32_t r = -1;
-      if (lane == leader) r = tile_probe(ijk, off, B, i, g, tx, ty, tz, table, H, flags);
-      r = __shfl(r, leader, kWave);
+      int32_t r;
+      if (lg == kg && lx == kx && ly == ky && lz == kz) {
+        r = krep;
+      } else {
+        r = -1;
+        if (lane == leader) r = tile_probe(ijk, off, B, i, lg, lx, ly, lz, table, H, flags);
+        r = __shfl(r, leader, kWave);
+        kg = lg;
+        kx = lx;
+        ky = ly;
+        kz = lz;
+        krep = r;
+      }
       if (same) mine = r;
       todo &= ~sm;
     }
-    if ((todo >> lane) & 1ull) mine = tile_probe(ijk, off, B, i, g, tx, ty, tz, table, H, flags);
-    if (in) {
+    if ((todo >> lane) & 1ull) mine = tile_probe(ijk, off, B, i, g[v], tx[v], ty[v], tz[v], table, H, flags);
+    if (in[v]) {
       rep[i] = mine;
       is_rep[i] = mine == i ? 1 : 0;
     }
@@ -454,8 +474,8 @@ tc_grid_batch* build_from_ijk(const int32_t* d_ijk, const int64_t* h_off, int32_
   hip_check(hipMemcpyAsync(d_off, h_stage, off_bytes, hipMemcpyHostToDevice, s), "offsets upload");
   fill_i32(flags, 0, 1, nullptr, 1, s);
   fill_i32(table, -1, H, nullptr, 1, s);
-  launch("k_hash_tiles", k_hash_tiles, std::min<i64>(ceil_div(N, 256), 8192), 256, s, d_ijk, (const i64*)d_off, B, N,
-         table, H, rep, flag, flags);
+  launch("k_hash_tiles", k_hash_tiles, ceil_div(N, kVoxPerBlock), 256, s, d_ijk, (const i64*)d_off, B, N, table, H,
+         rep, flag, flags);
   scan_excl_i32(flag, excl, N, nullptr, s);
   hip_check(hipStreamSynchronize(s), "hipStreamSynchronize");  // the pinned offsets are consumed
   const int32_t nt = read_i32(excl + N, s);

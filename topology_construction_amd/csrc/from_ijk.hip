@@ -115,12 +115,17 @@ __device__ __forceinline__ void table_flush(const unsigned long long* key, const
 
 // Voxels per lane of the per-voxel kernels: slot v of a wave covers the 64
 // consecutive voxels base + 64 v + lane, and the slots' loads go out together.
+// The kernels that merge through the block's LDS table take kVoxPerLane voxels
+// per lane (the table holds twice the block's voxels); the others take
+// kVoxPerLaneWide (more loads in flight per wave).
 constexpr int kVoxPerLane = 4;
 constexpr int kVoxPerBlock = 256 * kVoxPerLane;
+constexpr int kVoxPerLaneWide = 8;
+constexpr int kVoxPerBlockWide = 256 * kVoxPerLaneWide;
 
+template <int V>
 __device__ __forceinline__ i64 vox_index(int v) {
-  return (i64)blockIdx.x * kVoxPerBlock + (threadIdx.x / kWave) * (kWave * kVoxPerLane) + v * kWave +
-         (threadIdx.x & (kWave - 1));
+  return (i64)blockIdx.x * (256 * V) + (threadIdx.x / kWave) * (kWave * V) + v * kWave + (threadIdx.x & (kWave - 1));
 }
 
 __device__ __forceinline__ u64 tile_hash(int32_t g, int32_t tx, int32_t ty, int32_t tz) {
@@ -160,13 +165,13 @@ __device__ int32_t tile_probe(const int32_t* ijk, const i64* offsets, int32_t B,
 // Lanes of a wave that share a (grid, tile) probe once, through one leader, and
 // a key equal to the wave's previous one reuses its result without probing
 // (voxels that arrive together share their tile, so one probe per wave is
-// typical). Four voxels per lane (kVoxPerLane slots), their loads and member
+// typical). kVoxPerLaneWide voxels per lane (slots), their loads and member
 // searches together. Also flags the representatives (rep[i] == i): exactly the
 // voxels whose probe inserted their own index.
 __global__ void __launch_bounds__(256) k_hash_tiles(const int32_t* ijk, const i64* offsets, int32_t B, i64 n,
                                                     int32_t* table, i64 H, int32_t* rep, int32_t* is_rep,
                                                     int32_t* flags) {
-  constexpr int V = kVoxPerLane;
+  constexpr int V = kVoxPerLaneWide;
   __shared__ i64 s_off[kLdsMembers + 1];
   const bool lds = B <= kLdsMembers;  // uniform
   const int lane = threadIdx.x & (kWave - 1);
@@ -174,7 +179,7 @@ __global__ void __launch_bounds__(256) k_hash_tiles(const int32_t* ijk, const i6
   int32_t tx[V], ty[V], tz[V], g[V];
 #pragma unroll
   for (int v = 0; v < V; ++v) {
-    const i64 i = vox_index(v);
+    const i64 i = vox_index<V>(v);
     in[v] = i < n;
     tx[v] = in[v] ? ijk[i * 3] >> 12 : 0;
     ty[v] = in[v] ? ijk[i * 3 + 1] >> 12 : 0;
@@ -186,12 +191,12 @@ __global__ void __launch_bounds__(256) k_hash_tiles(const int32_t* ijk, const i6
   }
   const i64* off = lds ? s_off : offsets;
 #pragma unroll
-  for (int v = 0; v < V; ++v) g[v] = in[v] ? member_of(off, B, vox_index(v)) : 0;
+  for (int v = 0; v < V; ++v) g[v] = in[v] ? member_of(off, B, vox_index<V>(v)) : 0;
   // the wave's last resolved key and its representative (uniform)
   int32_t kg = -1, kx = 0, ky = 0, kz = 0, krep = -1;
 #pragma unroll
   for (int v = 0; v < V; ++v) {
-    const i64 i = vox_index(v);
+    const i64 i = vox_index<V>(v);
     int32_t mine = -1;
     u64 todo = __ballot(in[v]);
     for (int round = 0; todo && round < kDedupRounds; ++round) {
@@ -251,11 +256,11 @@ __global__ void __launch_bounds__(256) k_tile_rank_scatter(const Key128* keys, c
 
 __global__ void __launch_bounds__(256) k_voxel_tile(const int32_t* rep, const int32_t* excl, const int32_t* rank_of,
                                                     i64 n, int32_t nt, int32_t* vtile, int32_t* flags) {
-  constexpr int V = kVoxPerLane;
+  constexpr int V = kVoxPerLaneWide;
   int32_t r[V], k[V], t[V];
 #pragma unroll
   for (int v = 0; v < V; ++v) {
-    const i64 i = vox_index(v);
+    const i64 i = vox_index<V>(v);
     r[v] = i < n ? rep[i] : -1;
   }
 #pragma unroll
@@ -264,7 +269,7 @@ __global__ void __launch_bounds__(256) k_voxel_tile(const int32_t* rep, const in
   for (int v = 0; v < V; ++v) t[v] = (k[v] >= 0 && k[v] < nt) ? rank_of[k[v]] : -1;
 #pragma unroll
   for (int v = 0; v < V; ++v) {
-    const i64 i = vox_index(v);
+    const i64 i = vox_index<V>(v);
     if (i >= n) continue;
     if (t[v] < 0 || t[v] >= nt) {
       atomicOr(flags, 2);
@@ -277,14 +282,14 @@ __global__ void __launch_bounds__(256) k_voxel_tile(const int32_t* rep, const in
 
 __global__ void __launch_bounds__(256) k_voxel_mark_lower(const int32_t* ijk, const int32_t* vtile, i64 n,
                                                           u64* tile_child) {
-  constexpr int V = kVoxPerLane;
+  constexpr int V = kVoxPerLaneWide;
   u64* word[V];
   u64 b[V];
   bool in[V];
   int32_t t[V], x[V], y[V], z[V];
 #pragma unroll
   for (int v = 0; v < V; ++v) {
-    const i64 i = vox_index(v);
+    const i64 i = vox_index<V>(v);
     in[v] = i < n;
     t[v] = in[v] ? vtile[i] : 0;
     x[v] = in[v] ? ijk[i * 3] : 0;
@@ -321,7 +326,7 @@ __global__ void __launch_bounds__(256) k_voxel_cand(const int32_t* ijk, const in
   int32_t t[V], x[V], y[V], z[V], c[V];
 #pragma unroll
   for (int v = 0; v < V; ++v) {
-    const i64 i = vox_index(v);
+    const i64 i = vox_index<V>(v);
     ok[v] = i < n;
     t[v] = ok[v] ? vtile[i] : 0;
     x[v] = ok[v] ? ijk[i * 3] : 0;
@@ -347,7 +352,7 @@ __global__ void __launch_bounds__(256) k_voxel_cand(const int32_t* ijk, const in
   }
 #pragma unroll
   for (int v = 0; v < V; ++v) {
-    const i64 i = vox_index(v);
+    const i64 i = vox_index<V>(v);
     c[v] = -1;
     if (ok[v]) {
       c[v] = base[v] + pre[v] + popc64(cw[v] & ((1ull << bb[v]) - 1));
@@ -389,7 +394,7 @@ __global__ void __launch_bounds__(256) k_voxel_leaf(const int32_t* ijk, const in
   int32_t c[V], x[V], y[V], z[V];
 #pragma unroll
   for (int v = 0; v < V; ++v) {
-    const i64 i = vox_index(v);
+    const i64 i = vox_index<V>(v);
     const bool in = i < n;
     c[v] = in ? vcand[i] : -1;
     x[v] = in ? ijk[i * 3] : 0;
@@ -474,7 +479,7 @@ tc_grid_batch* build_from_ijk(const int32_t* d_ijk, const int64_t* h_off, int32_
   hip_check(hipMemcpyAsync(d_off, h_stage, off_bytes, hipMemcpyHostToDevice, s), "offsets upload");
   fill_i32(flags, 0, 1, nullptr, 1, s);
   fill_i32(table, -1, H, nullptr, 1, s);
-  launch("k_hash_tiles", k_hash_tiles, ceil_div(N, kVoxPerBlock), 256, s, d_ijk, (const i64*)d_off, B, N, table, H,
+  launch("k_hash_tiles", k_hash_tiles, ceil_div(N, kVoxPerBlockWide), 256, s, d_ijk, (const i64*)d_off, B, N, table, H,
          rep, flag, flags);
   scan_excl_i32(flag, excl, N, nullptr, s);
   hip_check(hipStreamSynchronize(s), "hipStreamSynchronize");  // the pinned offsets are consumed
@@ -519,11 +524,11 @@ tc_grid_batch* build_from_ijk(const int32_t* d_ijk, const int64_t* h_off, int32_
   sort_pairs_128(keys, vals, nt, tile_key_bits(B), s);
   launch("k_tile_rank_scatter", k_tile_rank_scatter, ceil_div(nt, 256), 256, s, (const Key128*)keys,
          (const uint32_t*)vals, (i64)nt, rank_of, ts.utile);
-  launch("k_voxel_tile", k_voxel_tile, ceil_div(N, kVoxPerBlock), 256, s, (const int32_t*)rep, (const int32_t*)excl,
+  launch("k_voxel_tile", k_voxel_tile, ceil_div(N, kVoxPerBlockWide), 256, s, (const int32_t*)rep, (const int32_t*)excl,
          (const int32_t*)rank_of, N, nt, vtile, flags);
   tree_tile_ranges(ts, B, s);
   fill_u64(ts.tile_child, 0, 512 * (i64)nt, nullptr, 1, s);
-  launch("k_voxel_mark_lower", k_voxel_mark_lower, ceil_div(N, kVoxPerBlock), 256, s, d_ijk, (const int32_t*)vtile, N,
+  launch("k_voxel_mark_lower", k_voxel_mark_lower, ceil_div(N, kVoxPerBlockWide), 256, s, d_ijk, (const int32_t*)vtile, N,
          ts.tile_child);
   tree_rank_tiles(ts, s);
   const int32_t nc = read_i32(ts.d_num_cands, s);

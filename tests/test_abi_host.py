@@ -98,3 +98,26 @@ def test_header_struct_layout_matches_binding():
     assert binding.HEADER_DTYPE.itemsize == 80
     assert binding.HEADER_DTYPE.fields["voxel_count"][1] == 32
     assert binding.HEADER_DTYPE.fields["bbox_min"][1] == 48
+
+
+def test_no_kernel_uses_scratch_memory(tmp_path):
+    """Every kernel keeps its arrays in registers or LDS: a runtime index into a
+    register array (or a spill) would put it in scratch memory, which lives in HBM
+    and once cost one gather kernel twice its time. Compiles the device code of
+    every source for gfx950 to assembly and reads each kernel's private segment."""
+    import subprocess
+    from topology_construction_amd import build
+    csrc = build.CSRC
+    bad = []
+    for src in build.SOURCES:
+        out = tmp_path / (src + ".s")
+        subprocess.check_call([build.HIPCC, f"--offload-arch={build.ARCH}", "-O3", "-std=c++17",
+                               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                               "--cuda-device-only", "-S", os.path.join(csrc, src), "-o", str(out)],
+                              stderr=subprocess.DEVNULL)
+        text = out.read_text()
+        for m in re.finditer(r"\.amdhsa_kernel (\S+)\n(.*?)\.end_amdhsa_kernel", text, flags=re.S):
+            seg = re.search(r"\.amdhsa_private_segment_fixed_size (\d+)", m.group(2))
+            if seg and int(seg.group(1)) != 0:
+                bad.append((src, m.group(1), int(seg.group(1))))
+    assert not bad, bad

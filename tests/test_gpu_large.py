@@ -182,3 +182,27 @@ def test_large_kernel_map_k2s2_transposed_onto_refine(big):
     assert np.array_equal(got, ref)
     del m, fine
     torch.cuda.synchronize()
+
+
+def test_large_from_ijk_unsorted_with_duplicates(big):
+    """Set semantics at full size: every member's rows shuffled, a tenth of them
+    repeated, give the same batch, array for array, as the sorted rows."""
+    import torch
+    from topology_construction_amd import binding
+    ijk, off, src = big
+    print("[large] from_ijk of shuffled rows with duplicates", flush=True)
+    d = torch.from_numpy(ijk).cuda()
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    parts, offs = [], [0]
+    for g in range(len(off) - 1):
+        seg = d[off[g]:off[g + 1]]
+        k = seg.shape[0]
+        seg = torch.cat([seg, seg[: k // 10]])
+        parts.append(seg[torch.randperm(seg.shape[0], device="cuda", generator=gen)])
+        offs.append(offs[-1] + parts[-1].shape[0])
+    shuffled = binding.tc_batch_from_ijk(torch.cat(parts).contiguous(), np.array(offs, np.int64))
+    fa, fb = gpu_fields(src), gpu_fields(shuffled)
+    for k in fa:
+        assert np.array_equal(fa[k], fb[k]), k
+    del shuffled, parts, d
+    torch.cuda.synchronize()

@@ -710,31 +710,41 @@ void tree_finalize_leaves(const GridView& out, const uint32_t* leaf_box, const i
 
 // ------------------------------------------------------------------ enumeration
 // One wave walks `lpw` (1..8) consecutive leaves. Their masks, origins and voxel
-// bases are loaded once, up front; many leaves per wave amortise the load
+// offsets are loaded once, up front, while the block stages the grids' voxel
+// begins in LDS (so no load waits on a leaf's grid index); many leaves per wave amortise the load
 // latency on large batches, one leaf per wave keeps small batches wide. For each leaf, lane r owns row r = x*8 + y
 // (byte y of word x, at most 8 voxels along z); a wave scan of the row popcounts
 // places every row, lanes expand their rows into LDS in bit order, and the wave
 // streams the leaf's rows out with 16-byte stores (the LDS image is shifted so
 // that its 16-byte chunks line up with the destination's).
 constexpr int kEnumMaxLeaves = 8;
+constexpr int kEnumLdsGrids = 256;  // up to this many grids, voxel begins come from LDS
 
 __global__ void __launch_bounds__(256) k_enumerate(const tc_grid_header* hdr, const int4* leaf_origin,
                                                    const u64* leaf_mask, const i64* leaf_offset, int32_t* ijk,
-                                                   i64 n_leaf, int lpw, int vec_ok) {
+                                                   i64 n_leaf, int32_t B, int lpw, int vec_ok) {
   __shared__ __align__(16) int32_t s_rows[4][3 * 512 + 4];
+  __shared__ i64 s_vb[kEnumLdsGrids];  // grids' voxel begins, loaded beside the leaves
   const int w = threadIdx.x / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   const i64 l0 = ((i64)blockIdx.x * 4 + w) * lpw;
-  if (l0 >= n_leaf) return;  // uniform per wave; no block barrier below
-  const int nl = (int)min((i64)lpw, n_leaf - l0);
+  const int nl = (int)max((i64)0, min((i64)lpw, n_leaf - l0));
   const int jl = lane >> 3;
   const u64 myword = jl < nl ? leaf_mask[(l0 + jl) * 8 + (lane & 7)] : 0ull;
   int4 myo = make_int4(0, 0, 0, 0);
-  i64 mybase = 0;
+  i64 myoff = 0;
   if (lane < nl) {
     myo = leaf_origin[l0 + lane];
-    mybase = hdr[myo.w].voxel_begin + leaf_offset[l0 + lane];
+    myoff = leaf_offset[l0 + lane];
   }
+  const bool lds_vb = B <= kEnumLdsGrids;  // uniform
+  if (lds_vb) {
+    for (int g = threadIdx.x; g < B; g += 256) s_vb[g] = hdr[g].voxel_begin;
+    __syncthreads();
+  }
+  if (nl == 0) return;  // uniform per wave; no block barrier below
+  i64 mybase = 0;
+  if (lane < nl) mybase = (lds_vb ? s_vb[myo.w] : hdr[myo.w].voxel_begin) + myoff;
   int32_t* rows = s_rows[w];
   const int x = lane >> 3, y = lane & 7;
   for (int j = 0; j < nl; ++j) {
@@ -790,7 +800,7 @@ void tree_enumerate(const GridView& v, int32_t* ijk, hipStream_t s) {
   const int lpw = v.n_leaf >= 256 * 1024 ? kEnumMaxLeaves : (v.n_leaf >= 6 * 1024 ? 2 : 1);
   launch("k_enumerate", k_enumerate, ceil_div((i64)v.n_leaf, 4 * lpw), 256, s,
          (const tc_grid_header*)v.headers, (const int4*)v.leaf_origin, (const u64*)v.leaf_mask,
-         (const i64*)v.leaf_offset, ijk, (i64)v.n_leaf, lpw, vec_ok);
+         (const i64*)v.leaf_offset, ijk, (i64)v.n_leaf, v.B, lpw, vec_ok);
 }
 
 }  // namespace tc

@@ -191,3 +191,47 @@ def kernel_map(src: dict, dst: dict, kernel: int, stride: int, transposed: bool,
     """Kernel map between two oracle results (each holding "ijk" and "headers")."""
     return kernel_map_rows(src["ijk"], member_offsets(src), dst["ijk"], member_offsets(dst), kernel, stride,
                            transposed, **kw)
+
+
+# ---------------------------------------------------------------- points front-end
+# The issue/PR pages list from_points beside from_ijk as a front-end that feeds
+# the same batched back-end (PR page, Measurements, follow-ups). Reading (the
+# pages give no formula): member g's point p lies in index space at
+# x = (p - origin_g) / voxel_size_g, computed in float32 as the kernels do;
+#   mode 0 (voxel of the point): the voxel whose centre is nearest, floor(x + 1/2)
+#          per axis (a tie goes to the larger index);
+#   mode 1 (nearest voxels):      the 2^3 voxels around it, floor(x) + {0, 1}^3.
+# Duplicates collapse as in from_ijk. A non-finite x is an invalid argument, an
+# index outside int32 an overflow.
+def points_to_ijk(points, offsets, voxel_size, origin, mode: int):
+    """int32 ijk rows and member offsets for the points front-end (float32 arithmetic)."""
+    pts = np.asarray(points, dtype=np.float32).reshape(-1, 3)
+    off = np.asarray(offsets, dtype=np.int64)
+    vs = np.asarray(voxel_size, dtype=np.float32).reshape(-1, 3)
+    org = np.asarray(origin, dtype=np.float32).reshape(-1, 3)
+    B = off.shape[0] - 1
+    if vs.shape[0] != B or org.shape[0] != B or mode not in (0, 1):
+        raise OracleError(INVALID)
+    if not (np.isfinite(vs).all() and (vs > 0).all() and np.isfinite(org).all()):
+        raise OracleError(INVALID)
+    g = np.repeat(np.arange(B), np.diff(off))
+    with np.errstate(all="ignore"):
+        x = (pts - org[g]) / vs[g]  # float32 subtract, then float32 divide
+        if not np.isfinite(x).all():
+            raise OracleError(INVALID)
+        base = np.floor(x + np.float32(0.5)) if mode == 0 else np.floor(x)
+    hi = base.max(initial=0) + (1 if mode == 1 else 0)
+    if base.size and (base.min() < -2.0 ** 31 or hi > 2.0 ** 31 - 1):
+        raise OracleError(OVERFLOW)
+    base = base.astype(np.int64)
+    if mode == 0:
+        return base.astype(np.int32), off.copy()
+    corners = np.array([[a, b, c] for a in (0, 1) for b in (0, 1) for c in (0, 1)], dtype=np.int64)
+    rows = (base[:, None, :] + corners[None, :, :]).reshape(-1, 3)
+    return rows.astype(np.int32), off * 8
+
+
+def run_points(points, offsets, voxel_size, origin, mode: int, fields=None, lib=None) -> dict:
+    """Oracle batch built from points: points_to_ijk, then the ijk front-end."""
+    ijk, off = points_to_ijk(points, offsets, voxel_size, origin, mode)
+    return run(IDENTITY, 1, ijk, off, fields=fields, lib=lib)

@@ -111,3 +111,36 @@ def test_planted_mistake_is_caught(name, source, tmp_path, monkeypatch):
             failures.append((getattr(check, "__name__", str(check)), type(exc).__name__))
             break
     assert failures, f"mutant {name!r} passed every pin"
+
+
+# Planted mistakes in the oracle's points front-end (Python): each must fail the
+# points pins.
+POINT_MUTANTS = {
+    "points sign": ("x = (pts - org[g]) / vs[g]", "x = (org[g] - pts) / vs[g]"),
+    "points scale": ("x = (pts - org[g]) / vs[g]", "x = (pts - org[g]) * vs[g]"),
+    "points ties down": ("np.floor(x + np.float32(0.5)) if mode == 0", "np.ceil(x - np.float32(0.5)) if mode == 0"),
+    "points mode 1 corners": ("for a in (0, 1) for b in (0, 1) for c in (0, 1)]",
+                              "for a in (-1, 0) for b in (0, 1) for c in (0, 1)]"),
+    "points member of row": ("g = np.repeat(np.arange(B), np.diff(off))", "g = np.zeros(off[-1], dtype=np.int64)"),
+    "points origin axes": ("org = np.asarray(origin, dtype=np.float32).reshape(-1, 3)",
+                           "org = np.asarray(origin, dtype=np.float32).reshape(-1, 3)[:, ::-1]"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(POINT_MUTANTS))
+def test_planted_points_mistake_is_caught(name, monkeypatch):
+    import inspect
+    old, new = POINT_MUTANTS[name]
+    src = inspect.getsource(oracle.points_to_ijk)
+    assert src.count(old) == 1, name
+    ns = dict(oracle.__dict__)
+    exec(src.replace(old, new), ns)
+    monkeypatch.setattr(oracle, "points_to_ijk", ns["points_to_ijk"])
+    battery = [pins.test_golden_points, functools.partial(pins.test_points_recover_jittered_centres, 0),
+               functools.partial(pins.test_points_recover_jittered_centres, 1)]
+    for check in battery:
+        try:
+            check()
+        except (AssertionError, oracle.OracleError, ValueError, IndexError):
+            return
+    pytest.fail(f"points mutant {name!r} passed every pin")

@@ -747,3 +747,84 @@ def test_kernel_map_invalid_args():
     with pytest.raises((oracle.OracleError, ValueError)):
         oracle.kernel_map_rows(r["ijk"], oracle.member_offsets(r), r2["ijk"], oracle.member_offsets(r2), 3, 1,
                                False)
+
+
+# ---------------------------------------------------------------- points front-end
+def test_golden_points():
+    rows = _read_golden("points_tiny.txt")
+    cases, cur = [], None
+    for r in rows:
+        if r[0] == "case":
+            cur = {"members": {}, "points": [], "expect": [], "mode": None}
+            cases.append(cur)
+        elif r[0] == "member":
+            cur["members"][int(r[1])] = ([float(v) for v in r[2:5]], [float(v) for v in r[5:8]])
+        elif r[0] == "point":
+            cur["mode"] = int(r[2])
+            cur["points"].append((int(r[1]), [float(v) for v in r[3:6]]))
+        elif r[0] == "expect":
+            cur["expect"].append([int(v) for v in r[1:]])
+    assert len(cases) == 2
+    for c in cases:
+        B = max(c["members"]) + 1
+        pts = [[p for g, p in c["points"] if g == m] for m in range(B)]
+        off = np.concatenate([[0], np.cumsum([len(p) for p in pts])]).astype(np.int64)
+        flat = np.array([p for m in pts for p in m], np.float32).reshape(-1, 3)
+        vs = np.array([c["members"][m][0] for m in range(B)], np.float32)
+        org = np.array([c["members"][m][1] for m in range(B)], np.float32)
+        r = oracle.run_points(flat, off, vs, org, c["mode"], fields=["headers", "ijk"])
+        got = []
+        for m in range(B):
+            b, n = r["headers"][m, 9], r["headers"][m, 8]
+            got += [[m] + v for v in r["ijk"][b:b + n].tolist()]
+        assert got == c["expect"], got
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_points_recover_jittered_centres(mode):
+    """Points drawn around voxel centres (offsets strictly inside the half-voxel,
+    away from ties) give back exactly those voxels (mode 0), or 8-voxel blocks that
+    contain them (mode 1), for per-member voxel sizes and origins, negatives and
+    tile boundaries included."""
+    rng = np.random.default_rng(321 + mode)
+    sets = random_sets(rng, 3, 30, CENTRES[:-1])
+    vs = np.array([[0.5, 0.25, 2.0], [1.0, 1.0, 1.0], [0.1, 0.3, 0.7]], np.float32)
+    org = np.array([[1.5, -3.0, 0.25], [0.0, 0.0, 0.0], [-7.0, 2.5, 100.0]], np.float32)
+    pts, off = [], [0]
+    for g, S in enumerate(sets):
+        for v in sorted(S):
+            for _ in range(2):  # duplicates of a voxel collapse
+                j = rng.uniform(-0.4, 0.4, 3)
+                pts.append(org[g].astype(np.float64) + (np.array(v, np.float64) + j) * vs[g].astype(np.float64))
+        off.append(len(pts))
+    pts = np.array(pts, np.float64).reshape(-1, 3).astype(np.float32)
+    r = oracle.run_points(pts, np.array(off, np.int64), vs, org, mode, fields=["headers", "ijk"])
+    got = _grid_sets(r)
+    for g, S in enumerate(sets):
+        if mode == 0:
+            assert got[g] == S, g
+        else:  # every block holds its centre's voxel and stays within one voxel of it
+            assert S <= got[g] and len(got[g]) <= 16 * len(S), g  # two points per voxel
+            for w in got[g]:
+                assert any(max(abs(w[a] - v[a]) for a in range(3)) <= 1 for v in S), (g, w)
+
+
+def test_points_invalid_and_overflow():
+    pts = np.array([[0, 0, 0]], np.float32)
+    off = np.array([0, 1], np.int64)
+    for vs in ([[0, 1, 1]], [[-1, 1, 1]], [[np.nan, 1, 1]]):
+        with pytest.raises(oracle.OracleError) as e:
+            oracle.points_to_ijk(pts, off, np.array(vs, np.float32), np.zeros((1, 3), np.float32), 0)
+        assert e.value.status == oracle.INVALID
+    with pytest.raises(oracle.OracleError) as e:
+        oracle.points_to_ijk(np.array([[np.inf, 0, 0]], np.float32), off, np.ones((1, 3), np.float32),
+                             np.zeros((1, 3), np.float32), 0)
+    assert e.value.status == oracle.INVALID
+    with pytest.raises(oracle.OracleError) as e:
+        oracle.points_to_ijk(np.array([[3e9, 0, 0]], np.float32), off, np.ones((1, 3), np.float32),
+                             np.zeros((1, 3), np.float32), 0)
+    assert e.value.status == oracle.OVERFLOW
+    # the largest index that fits stays valid (mode 0); mode 1 adds one and overflows there
+    big = np.array([[2.0 ** 31 - 128, 0, 0]], np.float32)
+    ijk, _ = oracle.points_to_ijk(big, off, np.ones((1, 3), np.float32), np.zeros((1, 3), np.float32), 0)
+    assert int(ijk[0, 0]) == 2 ** 31 - 128

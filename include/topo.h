@@ -175,6 +175,22 @@ const char* tc_last_error(void);
 tc_status tc_batch_from_ijk(const int32_t* d_ijk, const int64_t* h_offsets, int32_t grid_count,
                             const tc_allocator* allocator, void* stream, tc_grid_batch** out);
 
+/* Builds a batch from float32 points (the points front-end beside the ijk
+ * front-end; PR page, Measurements, follow-ups).
+ *   d_xyz         float32[N][3] device, N = h_offsets[B]; may be NULL when N = 0.
+ *   h_offsets     int64[B+1] host, as for tc_batch_from_ijk.
+ *   h_voxel_size  float32[B][3] host, finite and > 0; h_origin float32[B][3] host, finite.
+ *   mode          0: the voxel whose centre is nearest to the point, per axis
+ *                    floor(x + 1/2) with x = (p - origin) / voxel_size computed in
+ *                    float32 (a tie goes to the larger index);
+ *                 1: the 8 voxels floor(x) + {0,1}^3 around the point.
+ * Duplicates collapse. A point whose x is not finite is TC_ERR_INVALID_ARG, an
+ * index outside int32 TC_ERR_OVERFLOW. More than 2^30 voxel rows (N, or 8N in
+ * mode 1) is TC_ERR_UNSUPPORTED. Blocks on a few small readbacks. */
+tc_status tc_batch_from_points(const float* d_xyz, const int64_t* h_offsets, int32_t grid_count,
+                              const float* h_voxel_size, const float* h_origin, int32_t mode,
+                              const tc_allocator* allocator, void* stream, tc_grid_batch** out);
+
 /* One batched pass (or a chain of passes) over every member of `src`
  * (PR page section 1: emission, sorts, dedup, single readback, one allocation,
  * writers; section 2: box-dilate and pads; factors 4, 8 and k3s2 chain passes).

@@ -206,3 +206,32 @@ def test_large_from_ijk_unsorted_with_duplicates(big):
         assert np.array_equal(fa[k], fb[k]), k
     del shuffled, parts, d
     torch.cuda.synchronize()
+
+
+def test_large_points_at_voxel_centres(big):
+    """At full size, points at the voxel centres (voxel size 1, origin 0) give the
+    ijk batch itself, array for array."""
+    import torch
+    from topology_construction_amd import binding
+    ijk, off, src = big
+    print("[large] from_points at voxel centres", flush=True)
+    pts = torch.from_numpy(ijk).cuda().to(torch.float32)
+    B = len(off) - 1
+    keep = np.all(np.abs(ijk) < (1 << 24), axis=1)
+    if keep.all():
+        b = binding.tc_batch_from_points(pts, off, np.ones((B, 3), np.float32), np.zeros((B, 3), np.float32), 0)
+        fa, fb = gpu_fields(src), gpu_fields(b)
+        for k in fa:
+            assert np.array_equal(fa[k], fb[k]), k
+    else:
+        # members far out (cubes at offsets up to 2^29) are not exact floats: compare the shells
+        shells = list(range(64))
+        sub = np.concatenate([ijk[off[g]:off[g + 1]] for g in shells])
+        soff = np.concatenate([[0], np.cumsum(np.diff(off)[:64])]).astype(np.int64)
+        ref = binding.tc_batch_from_ijk(torch.from_numpy(sub).cuda(), soff)
+        b = binding.tc_batch_from_points(torch.from_numpy(sub).cuda().to(torch.float32), soff,
+                                         np.ones((64, 3), np.float32), np.zeros((64, 3), np.float32), 0)
+        fa, fb = gpu_fields(ref), gpu_fields(b)
+        for k in fa:
+            assert np.array_equal(fa[k], fb[k]), k
+    torch.cuda.synchronize()

@@ -1,0 +1,88 @@
+"""Points front-end on the GPU vs the oracle, element by element, through the C ABI.
+
+PR page "Batched leaf-mask topology construction for generated conv grids",
+Measurements (follow-ups): from_points beside from_ijk on the same back-end.
+Both sides compute the index-space coordinate in float32 with correctly rounded
+operations, so the voxel each point lands in is decided identically; every
+exposed array must then be equal bit for bit. Cases: jittered voxel centres of
+the B=16 workload with per-member voxel sizes and origins, exact ties, random
+points spread over negative and positive space, the 8-voxel mode, empty members,
+non-finite points and indices outside int32.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from tests.gpu_util import assert_same, gpu_fields
+from topology_construction_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(points, off, vs, org, mode, ctx):
+    import torch
+    from topology_construction_amd import binding
+    print(f"[points] {ctx} mode={mode} B={len(off) - 1} N={int(off[-1])}", flush=True)
+    ref = oracle.run_points(points, off, vs, org, mode)
+    b = binding.tc_batch_from_points(torch.from_numpy(np.ascontiguousarray(points, np.float32)).cuda(), off, vs, org,
+                                     mode)
+    assert_same(gpu_fields(b), ref, ctx)
+
+
+def _member_params(rng, B):
+    vs = rng.uniform(0.05, 3.0, size=(B, 3)).astype(np.float32)
+    org = rng.uniform(-50, 50, size=(B, 3)).astype(np.float32)
+    return vs, org
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_jittered_centres_config2(mode):
+    rng = np.random.default_rng(40 + mode)
+    ijk, off = synth.make_config(2)
+    B = len(off) - 1
+    vs, org = _member_params(rng, B)
+    g = np.repeat(np.arange(B), np.diff(off))
+    jit = rng.uniform(-0.45, 0.45, size=ijk.shape)
+    pts = (org[g].astype(np.float64) + (ijk + jit) * vs[g].astype(np.float64)).astype(np.float32)
+    _check(pts, off, vs, org, mode, "config2 centres")
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_random_points_and_ties(mode):
+    rng = np.random.default_rng(60 + mode)
+    members = [rng.uniform(-200, 200, size=(int(rng.integers(0, 4000)), 3)).astype(np.float32) for _ in range(5)]
+    members[2] = np.zeros((0, 3), np.float32)
+    # exact ties: multiples of 0.25 with voxel size 0.5 put x on k + 1/2
+    members.append((rng.integers(-400, 400, size=(3000, 3)) * 0.25).astype(np.float32))
+    pts = np.concatenate(members).astype(np.float32)  # (synth.concat_members would round to int32)
+    off = np.concatenate([[0], np.cumsum([m.shape[0] for m in members])]).astype(np.int64)
+    B = len(off) - 1
+    vs, org = _member_params(rng, B)
+    vs[-1] = 0.5
+    org[-1] = 0.0
+    _check(pts, off, vs, org, mode, "random + ties")
+
+
+def test_errors():
+    import torch
+    from topology_construction_amd import binding
+    off = np.array([0, 2], np.int64)
+    vs, org = np.ones((1, 3), np.float32), np.zeros((1, 3), np.float32)
+    for pts, status in [([[0, 0, 0], [np.nan, 0, 0]], 1), ([[0, 0, 0], [np.inf, 1, 1]], 1),
+                        ([[0, 0, 0], [5e9, 0, 0]], 2), ([[-5e9, 0, 0], [0, 0, 0]], 2)]:
+        with pytest.raises(binding.TopoError) as e:
+            binding.tc_batch_from_points(torch.tensor(pts, dtype=torch.float32, device="cuda"), off, vs, org, 0)
+        assert e.value.status == status, pts
+    p = torch.zeros((2, 3), dtype=torch.float32, device="cuda")
+    for bad_vs in ([[0, 1, 1]], [[-1, 1, 1]], [[np.nan, 1, 1]]):
+        with pytest.raises(binding.TopoError) as e:
+            binding.tc_batch_from_points(p, off, np.array(bad_vs, np.float32), org, 0)
+        assert e.value.status == 1
+    with pytest.raises(binding.TopoError) as e:
+        binding.tc_batch_from_points(p, off, vs, org, 2)
+    assert e.value.status == 1
+    e0 = binding.tc_batch_from_points(torch.zeros((0, 3), dtype=torch.float32, device="cuda"),
+                                      np.array([0, 0, 0], np.int64), np.ones((2, 3), np.float32),
+                                      np.zeros((2, 3), np.float32), 1)
+    assert e0.voxel_total() == 0
+    torch.cuda.synchronize()

@@ -25,7 +25,7 @@ OPS = {"coarsen": 1, "refine": 2, "dilate": 3, "pad_neg": 4, "pad_pos": 5, "conv
        "conv_s1": 7, "conv_t_s1": 8}
 
 ABI_SYMBOLS = [
-    "tc_abi_version", "tc_status_string", "tc_last_error", "tc_batch_from_ijk",
+    "tc_abi_version", "tc_status_string", "tc_last_error", "tc_batch_from_ijk", "tc_batch_from_points",
     "tc_build_batched_topology", "tc_build_masked_refine", "tc_batch_get_info", "tc_batch_read_headers",
     "tc_batch_voxel_total", "tc_enumerate_ijk", "tc_build_kernel_map", "tc_scratch_release", "tc_batch_free",
     "tc_profile_enable",
@@ -128,6 +128,8 @@ def load_library(path: str = LIB_PATH):
         lib.tc_enumerate_ijk.argtypes = [vp, vp, i64, vp]
         lib.tc_build_kernel_map.restype = ctypes.c_int
         lib.tc_build_kernel_map.argtypes = [vp, vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, i64, vp]
+        lib.tc_batch_from_points.restype = ctypes.c_int
+        lib.tc_batch_from_points.argtypes = [vp, vp, i32, vp, vp, i32, vp, vp, ctypes.POINTER(vp)]
         lib.tc_scratch_release.restype = ctypes.c_int
         lib.tc_scratch_release.argtypes = []
         lib.tc_batch_free.restype = None
@@ -249,6 +251,31 @@ def tc_batch_from_ijk(ijk, offsets, stream=None, allocator: str = "torch") -> Gr
     h = ctypes.c_void_p()
     _check(lib.tc_batch_from_ijk(ctypes.c_void_p(ijk.data_ptr() if ijk.numel() else 0), off.ctypes.data,
                                  off.shape[0] - 1, alloc, _stream_handle(stream), ctypes.byref(h)))
+    return GridBatch(h, allocator == "torch")
+
+
+def tc_batch_from_points(points, offsets, voxel_size, origin, mode: int = 0, stream=None,
+                         allocator: str = "torch") -> GridBatch:
+    """Build a GridBatch from a device float32 [N, 3] tensor of points, int64
+    offsets [B+1] and per-member voxel sizes / origins ([B, 3], host). mode 0:
+    the voxel of the nearest centre; mode 1: the 8 voxels around each point."""
+    import torch
+    lib = load_library()
+    if not (isinstance(points, torch.Tensor) and points.is_cuda and points.dtype == torch.float32):
+        raise TypeError("points must be a cuda float32 tensor")
+    points = points.contiguous().view(-1, 3)
+    off = np.ascontiguousarray(np.asarray(offsets, dtype=np.int64))
+    if off.ndim != 1 or off.shape[0] < 2 or int(off[-1]) != points.shape[0]:
+        raise ValueError("offsets must be [B+1] with offsets[-1] == number of points")
+    vs = np.ascontiguousarray(np.asarray(voxel_size, dtype=np.float32).reshape(-1, 3))
+    org = np.ascontiguousarray(np.asarray(origin, dtype=np.float32).reshape(-1, 3))
+    if vs.shape[0] != off.shape[0] - 1 or org.shape[0] != off.shape[0] - 1:
+        raise ValueError("voxel_size and origin must be [B, 3]")
+    alloc = ctypes.byref(TORCH_ALLOCATOR) if allocator == "torch" else None
+    h = ctypes.c_void_p()
+    _check(lib.tc_batch_from_points(ctypes.c_void_p(points.data_ptr() if points.numel() else 0), off.ctypes.data,
+                                    off.shape[0] - 1, vs.ctypes.data, org.ctypes.data, int(mode), alloc,
+                                    _stream_handle(stream), ctypes.byref(h)))
     return GridBatch(h, allocator == "torch")
 
 

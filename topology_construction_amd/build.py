@@ -18,7 +18,7 @@ LIB = os.path.join(HERE, "libtopo.so")
 ARCH = os.environ.get("TOPO_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["runtime.hip", "primitives.hip", "tree.hip", "pass.hip", "from_ijk.hip", "kmap.hip", "abi.hip"]
+SOURCES = ["runtime.hip", "primitives.hip", "tree.hip", "pass.hip", "from_ijk.hip", "points.hip", "kmap.hip", "abi.hip"]
 
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

@@ -2,6 +2,7 @@
 // host, pass chaining for factors 4/8 and k3s2 transpose, batch ownership and
 // error reporting. No exception crosses the boundary.
 #include <algorithm>
+#include <cmath>
 #include <cstring>
 #include <new>
 #include <string>
@@ -158,6 +159,35 @@ tc_status tc_batch_from_ijk(const int32_t* d_ijk, const int64_t* h_offsets, int3
     return fail(TC_ERR_INVALID_ARG, "allocator callbacks are NULL");
   return guarded([&]() {
     *out = tc::build_from_ijk(d_ijk, h_offsets, grid_count, tc::OutAlloc{allocator, (hipStream_t)stream});
+    return TC_OK;
+  });
+}
+
+tc_status tc_batch_from_points(const float* d_xyz, const int64_t* h_offsets, int32_t grid_count,
+                              const float* h_voxel_size, const float* h_origin, int32_t mode,
+                              const tc_allocator* allocator, void* stream, tc_grid_batch** out) {
+  if (!out) return fail(TC_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (grid_count < 1) return fail(TC_ERR_INVALID_ARG, "grid_count must be >= 1");
+  if (!h_offsets || !h_voxel_size || !h_origin) return fail(TC_ERR_INVALID_ARG, "NULL host argument");
+  if (mode != 0 && mode != 1) return fail(TC_ERR_INVALID_ARG, "mode must be 0 or 1");
+  if (h_offsets[0] != 0) return fail(TC_ERR_INVALID_ARG, "h_offsets[0] must be 0");
+  for (int32_t g = 0; g < grid_count; ++g) {
+    if (h_offsets[g + 1] < h_offsets[g]) return fail(TC_ERR_INVALID_ARG, "h_offsets must be non-decreasing");
+    for (int k = 0; k < 3; ++k) {
+      const float vs = h_voxel_size[g * 3 + k], o = h_origin[g * 3 + k];
+      if (!std::isfinite(vs) || !(vs > 0.0f)) return fail(TC_ERR_INVALID_ARG, "voxel sizes must be finite and > 0");
+      if (!std::isfinite(o)) return fail(TC_ERR_INVALID_ARG, "origins must be finite");
+    }
+  }
+  const int64_t n = h_offsets[grid_count];
+  if ((mode == 0 ? n : 8 * n) >= (1ll << 30)) return fail(TC_ERR_UNSUPPORTED, "more than 2^30 voxel rows");
+  if (n > 0 && !d_xyz) return fail(TC_ERR_INVALID_ARG, "d_xyz is NULL");
+  if (allocator && (!allocator->alloc || !allocator->free))
+    return fail(TC_ERR_INVALID_ARG, "allocator callbacks are NULL");
+  return guarded([&]() {
+    *out = tc::build_from_points(d_xyz, h_offsets, grid_count, h_voxel_size, h_origin, mode,
+                                 tc::OutAlloc{allocator, (hipStream_t)stream});
     return TC_OK;
   });
 }

@@ -335,6 +335,10 @@ void kernel_map(const GridView& src, const GridView& dst, int K, int S, int tran
 
 // The two producers of grid batches.
 tc_grid_batch* build_from_ijk(const int32_t* d_ijk, const int64_t* h_offsets, int32_t B, const OutAlloc& oa);
+// Points front-end: float32 points -> voxel rows (mode 0: nearest voxel centre,
+// mode 1: the 8 surrounding voxels) -> build_from_ijk.
+tc_grid_batch* build_from_points(const float* d_xyz, const int64_t* h_offsets, int32_t B, const float* h_voxel_size,
+                                 const float* h_origin, int mode, const OutAlloc& oa);
 // One batched pass. leaf_mask_override (device, one 512-bit mask per source leaf)
 // replaces the source leaf masks, e.g. masked copies for masked refine.
 tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa,

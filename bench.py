@@ -12,7 +12,7 @@ timed steps. `roofline` reports the dominant kernel's algorithmic bytes per
 launch over its HIP-event-timed average duration; `cpu_baseline` times the CPU
 oracle on whole steps of the same workload. Outside the timed steps the line
 also carries per-op medians (`ops`), the stride-1 kernel-K targets and masked
-refine (`more_ops`), the ijk front-end (`from_ijk`), the plan's kernel maps
+refine (`more_ops`), the ijk and points front-ends (`from_ijk`, `from_points`), the plan's kernel maps
 (`kernel_maps`) and the 46M-voxel batch (`large`).
 """
 from __future__ import annotations
@@ -173,6 +173,27 @@ def time_from_ijk(binding, torch, np, d_ijk, off, reps):
             "algorithmic_bytes": byts, "achieved_GBs": byts / (m * 1e-3) / 1e9}
 
 
+def time_from_points(binding, torch, np, d_ijk, off, reps):
+    """The points front-end (mode 0, voxel size 1, origin 0) on device-resident
+    float32 points a quarter voxel off the centres: median wall ms and its rate."""
+    B = len(off) - 1
+    pts = d_ijk.to(torch.float32) + 0.25
+    vs, org = np.ones((B, 3), np.float32), np.zeros((B, 3), np.float32)
+    ms, leaves = [], 0
+    binding.tc_batch_from_points(pts, off, vs, org, 0)  # warm-up
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        a = time.perf_counter()
+        b = binding.tc_batch_from_points(pts, off, vs, org, 0)
+        torch.cuda.synchronize()
+        ms.append((time.perf_counter() - a) * 1e3)
+        leaves = int(b.leaf_count)
+        del b
+    m = float(np.median(ms))
+    n = int(off[-1])
+    return {"ms_median": m, "input_points": n, "output_leaves": leaves, "input_points_per_s": n / (m * 1e-3)}
+
+
 def time_kernel_maps(binding, torch, np, src, reps):
     """The two kernel maps a plan builds (issue page, Measurements): k3 s1 on the
     source's own topology and k2s2 transposed conv onto refine x2. Output tables
@@ -219,7 +240,7 @@ def measure_large(binding, torch, np, synth):
     torch.cuda.synchronize()
     res = {"workload": synth.CONFIG_NAMES[5], "grids": int(len(off) - 1), "input_voxels": int(off[-1]),
            "input_leaves": int(src.leaf_count), "from_ijk": time_from_ijk(binding, torch, np, d_ijk, off, 3),
-           "ops": {}}
+           "from_points": time_from_points(binding, torch, np, d_ijk, off, 3), "ops": {}}
     del d_ijk
     for op, f in [("coarsen", 2), ("refine", 2), ("dilate", 1)]:
         out = binding.tc_build_batched_topology(src, op, f)  # warm-up
@@ -368,6 +389,7 @@ def main():
                    "input_voxels": int(off[-1]), "ops": [f"{o}x{f}" for o, f in STEP_OPS]},
         "roofline": roofline, "cpu_baseline": cpu, "ops": ops, "b48": b48, "more_ops": extra,
         "from_ijk": time_from_ijk(binding, torch, np, d_ijk, off, 20),
+        "from_points": time_from_points(binding, torch, np, d_ijk, off, 20),
         "kernel_maps": time_kernel_maps(binding, torch, np, src, 20), "large": large,
     }
     print(json.dumps(rec), flush=True)

@@ -1099,54 +1099,13 @@ __device__ __forceinline__ void coarsen_place(u64 out[8], const u64 W[8], const 
   }
 }
 
-// Box op: contribution of source W to the neighbour at offset t (t is the
-// target's offset from the source), with per-axis box offsets in [lo, hi].
-__device__ __forceinline__ void box_contrib(u64 out[8], const u64 W[8], const I3& t, int lo, int hi) {
-#pragma unroll
-  for (int x = 0; x < 8; ++x) {
-    u64 a = 0;
-    if (t.x == 0) {
-      for (int e = lo; e <= hi; ++e) {
-        const int xs = x - e;
-        if (xs >= 0 && xs < 8) a |= W[xs];
-      }
-    } else if (t.x > 0) {
-      if (x == 0) a = W[7];
-    } else {
-      if (x == 7) a = W[0];
-    }
-    if (!a) continue;
-    u64 y;
-    if (t.y == 0) {
-      y = a;
-      if (hi > 0) y |= a << 8;
-      if (lo < 0) y |= a >> 8;
-    } else if (t.y > 0) {
-      y = a >> 56;
-    } else {
-      y = a << 56;
-    }
-    u64 z;
-    if (t.z == 0) {
-      z = y;
-      if (hi > 0) z |= (y & ~kZ7) << 1;
-      if (lo < 0) z |= (y & ~kZ0) >> 1;
-    } else if (t.z > 0) {
-      z = (y & kZ7) >> 7;
-    } else {
-      z = (y & kZ0) << 7;
-    }
-    out[x] |= z;
-  }
-}
-
 // Output leaf masks by gathering from the source leaves that feed them: the
-// unique parent (refine), the 8 children (coarsen) or the neighbours at the op's
-// box offsets (dilate, pads). Box ops and coarsen split the sources of one
-// output leaf over 4 adjacent lanes and OR the partial masks with shuffles, so
-// the dependent lookups run in parallel. Also writes the leaf's prefix word,
-// voxel count and packed local bbox.
-// KIND: 0 refine, 1 coarsen, 2 box op (dilate / pads); one instantiation each.
+// unique parent (refine) or the 8 children (coarsen; box ops have their own
+// separable gather below). Coarsen splits the sources of one output leaf over 4
+// adjacent lanes and ORs the partial masks with shuffles, so the dependent
+// lookups run in parallel. Also writes the leaf's prefix word, packed local bbox
+// and in-run voxel count.
+// KIND: 0 refine, 1 coarsen; one instantiation each.
 template <int KIND>
 __global__ void __launch_bounds__(256) k_leaf_gather(const int4* out_origin, const int32_t* leaf_cand, i64 n,
                                                      int op, int m, int lo, int hi, const int32_t* cand_src,
@@ -1203,55 +1162,6 @@ __global__ void __launch_bounds__(256) k_leaf_gather(const int4* out_origin, con
 #pragma unroll
         for (int k = 0; k < 8; ++k) W[k] = src_leaf_mask[(i64)src * 8 + k];
         coarsen_place(out, W, q);
-      }
-    } else {
-      // The (at most 7) sources of this lane are looked up level by level so
-      // that their dependent loads overlap instead of running one chain at a time.
-      constexpr int kPer = 7;  // ceil(27 / 4)
-      int32_t sl[kPer], bit[kPer];
-#pragma unroll
-      for (int q = 0; q < kPer; ++q) {
-        const int j = sub + 4 * q;
-        sl[q] = -1;
-        bit[q] = 0;
-        if (j < m) {
-          const I3 t = box_offset(j, op);
-          const i64 px = lx - t.x, py = ly - t.y, pz = lz - t.z;  // source position, -1 .. 16
-          sl[q] = cand_src[c * 27 + index27(px >> 4, py >> 4, pz >> 4)];
-          bit[q] = (int)((((px & 15) * 16) + (py & 15)) * 16 + (pz & 15));
-          if (sl[q] >= n_src_lower) {
-            set_flag(flags, kFlagInternal);
-            sl[q] = -1;
-          }
-        }
-      }
-      u64 word[kPer];
-#pragma unroll
-      for (int q = 0; q < kPer; ++q) word[q] = sl[q] >= 0 ? src_lower_mask[(i64)sl[q] * 64 + (bit[q] >> 6)] : 0;
-      int32_t r[kPer];
-#pragma unroll
-      for (int q = 0; q < kPer; ++q) {
-        r[q] = -1;
-        const int b = bit[q] & 63;
-        if ((word[q] >> b) & 1ull) {
-          r[q] = src_lower_first[sl[q]] + src_lower_prefix[(i64)sl[q] * 64 + (bit[q] >> 6)] +
-                 popc64(word[q] & ((1ull << b) - 1));
-          if (r[q] < 0 || r[q] >= n_src_leaf) {
-            set_flag(flags, kFlagInternal);
-            r[q] = -1;
-          }
-        }
-      }
-      // absent sources read leaf 0 (there is at least one source leaf whenever an
-      // output leaf exists) and discard it, so no load waits behind a branch
-#pragma unroll
-      for (int q = 0; q < kPer; ++q) {
-        const i64 ri = r[q] >= 0 ? r[q] : 0;
-        const u64 keep = r[q] >= 0 ? ~0ull : 0ull;
-        u64 W[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) W[k] = src_leaf_mask[ri * 8 + k] & keep;
-        box_contrib(out, W, box_offset(sub + 4 * q, op), lo, hi);
       }
     }
   }
@@ -1469,7 +1379,6 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, 
   if (leaf_mask_override) sv.leaf_mask = const_cast<u64*>(leaf_mask_override);
   const i64 nT = (i64)src->n2 * oi.m;
   const i64 nL = (i64)src->n1 * oi.m;
-  const i64 Ls = src->nl;
   if (nT > 0x7fffffffLL || nL > 0x7fffffffLL || nL * oi.m_src > (1ll << 40))
     throw Error(TC_ERR_UNSUPPORTED, "pass: source batch too large");
 

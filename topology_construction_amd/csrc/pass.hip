@@ -255,6 +255,65 @@ __global__ void __launch_bounds__(256) k_node_reach(const u64* mask, i64 n_nodes
   if (lane == 0) reach[u] = op == TC_OP_REFINE ? code : box_code_for_op(code, op, m);
 }
 
+// Box ops, voxel-exact faces: reach sets of every source upper and lower from
+// which faces of the node hold a voxel (the node's voxels at local coordinate 0
+// or at the far end, per axis). A node reaches the neighbour at offset e only if
+// every axis with e != 0 has a voxel on that face, so the product of the per-axis
+// sets stays a superset of the true targets while dropping the neighbours that
+// the child-bit sets above add whenever a child merely sits on a face. One
+// workgroup per source upper: a wave per lower, lanes over its leaves; each lower
+// writes its set, the upper ORs the face bits of its lowers on the tile faces.
+// Face bits: 2a for the low face of axis a, 2a + 1 for the high face.
+__device__ __forceinline__ uint32_t faces_to_code(uint32_t f, int op, int m) {
+  const uint32_t code = product27(axis_set(f & 1u, f & 2u), axis_set(f & 4u, f & 8u), axis_set(f & 16u, f & 32u));
+  return box_code_for_op(code, op, m);
+}
+
+__global__ void __launch_bounds__(256) k_box_reach(const int4* upper_origin, const int32_t* upper_first,
+                                                   int32_t n_upper, const int4* lower_origin,
+                                                   const int32_t* lower_first, int32_t n_lower,
+                                                   const int4* leaf_origin, const u64* leaf_mask, int32_t n_leaf,
+                                                   int op, int m, uint32_t* upper_reach, uint32_t* lower_reach) {
+  __shared__ uint32_t s_face;
+  const int u = blockIdx.x;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = threadIdx.x / kWave;
+  if (threadIdx.x == 0) s_face = 0;
+  __syncthreads();
+  const int4 uo = upper_origin[u];
+  const int32_t l0 = upper_first[u], l1 = u + 1 < n_upper ? upper_first[u + 1] : n_lower;
+  for (int32_t l = l0 + wv; l < l1; l += 4) {
+    const int4 lo = lower_origin[l];
+    const int32_t f0 = lower_first[l], f1 = l + 1 < n_lower ? lower_first[l + 1] : n_leaf;
+    uint32_t face = 0;
+    for (int32_t f = f0 + lane; f < f1; f += kWave) {
+      const int4 o = leaf_origin[f];
+      const int px = (o.x - lo.x) >> 3, py = (o.y - lo.y) >> 3, pz = (o.z - lo.z) >> 3;  // 0..15 in the lower
+      u64 w[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) w[k] = leaf_mask[(i64)f * 8 + k];
+      const u64 all = w[0] | w[1] | w[2] | w[3] | w[4] | w[5] | w[6] | w[7];
+      if (px == 0 && w[0]) face |= 1u;
+      if (px == 15 && w[7]) face |= 2u;
+      if (py == 0 && (all & 0xffull)) face |= 4u;
+      if (py == 15 && (all & 0xff00000000000000ull)) face |= 8u;
+      if (pz == 0 && (all & kZ0)) face |= 16u;
+      if (pz == 15 && (all & kZ7)) face |= 32u;
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) face |= (uint32_t)__shfl_xor((int)face, d, kWave);
+    if (lane == 0) {
+      lower_reach[l] = faces_to_code(face, op, m);
+      const int qx = (lo.x - uo.x) >> 7, qy = (lo.y - uo.y) >> 7, qz = (lo.z - uo.z) >> 7;  // 0..31 in the tile
+      const uint32_t tile_face = (face & ((qx == 0 ? 1u : 0u) | (qx == 31 ? 2u : 0u) | (qy == 0 ? 4u : 0u) |
+                                          (qy == 31 ? 8u : 0u) | (qz == 0 ? 16u : 0u) | (qz == 31 ? 32u : 0u)));
+      if (tile_face) atomicOr(&s_face, tile_face);
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) upper_reach[u] = faces_to_code(s_face, op, m);
+}
+
 // ------------------------------------------------------------------ stage: tiles, fused (small batches)
 // At most 4096 tile candidates: one workgroup builds the reach set of every
 // source upper, compacts the reachable in-range candidates, sorts them in LDS
@@ -296,7 +355,7 @@ __global__ void __launch_bounds__(kTilesThreads) k_tiles_small(const int4* upper
       for (int v = 0; v < kUppersPerWave; ++v)
 #pragma unroll
         for (int k = 0; k < 8; ++k)
-          words[v][k] = u0 + v < n_upper ? upper_mask[(i64)(u0 + v) * 512 + k * kWave + lane] : 0;
+          words[v][k] = upper_mask[(i64)min(u0 + v, n_upper - 1) * 512 + k * kWave + lane];  // clamped: no wait per load
 #pragma unroll
       for (int v = 0; v < kUppersPerWave; ++v) {
         uint32_t code = 0;
@@ -309,10 +368,14 @@ __global__ void __launch_bounds__(kTilesThreads) k_tiles_small(const int4* upper
     }
   }
   __syncthreads();
-  // keys of the kept candidates (blocked: thread tid owns tid*4 .. tid*4+3)
+  // keys of the kept candidates (blocked: thread tid owns tid*4 .. tid*4+3);
+  // the origins are loaded first, at clamped indices, all in flight at once
   u64 khi[kTilesItems], klo[kTilesItems];
   int keep[kTilesItems];
+  int4 org[kTilesItems];
   int nkeep = 0;
+#pragma unroll
+  for (int k = 0; k < kTilesItems; ++k) org[k] = upper_origin[min(tid * kTilesItems + k, n - 1) / m];  // n >= 1
 #pragma unroll
   for (int k = 0; k < kTilesItems; ++k) {
     const int i = tid * kTilesItems + k;
@@ -320,7 +383,7 @@ __global__ void __launch_bounds__(kTilesThreads) k_tiles_small(const int4* upper
     khi[k] = klo[k] = 0;
     if (i < n) {
       const int u = i / m, j = i % m;
-      const int4 o = upper_origin[u];
+      const int4 o = org[k];
       const i64 tx = o.x >> 12, ty = o.y >> 12, tz = o.z >> 12;
       I3 t;
       bool reach = true;
@@ -667,35 +730,64 @@ __global__ void __launch_bounds__(256) k_lower_nbr(const int4* lower_origin, con
                 tile_lower_base, *d_num_tiles, *d_num_cands, lower_nbr, cand_origin, cand_src, flags);
 }
 
-// Small batches (at most kLowersSmallMax (lower, candidate) pairs, at most
-// kLowersSmallTiles tile candidates): the whole lower stage in one workgroup:
+// Small batches (at least one and at most kLowersSmallMax (lower, candidate)
+// pairs, at most kLowersSmallTiles tile candidates): the whole lower stage in
+// one workgroup:
 // every source lower's reach set, marking, per-tile popcount prefix tables, the
 // scan over tiles (candidate numbering), the empty candidate -> source table,
 // and the candidate indices / origins / sources. When the unique tiles are few
-// (at most kLdsTiles, known only here) their candidate masks and bases live in
-// LDS and the masks are copied out at the end; otherwise the same steps run on
-// the global arrays. Replaces five launches of the general path; phases are
-// separated by a device fence and a block barrier where later phases read what
-// other waves wrote to global memory.
+// (at most kLdsTiles, known only here) their candidate masks, prefix tables and
+// bases live in LDS and the masks are copied out at the end; otherwise the same
+// steps run on the global arrays, with a device fence where a later phase reads
+// what other waves wrote. Each thread owns two pairs, whose origins and tile
+// indices are loaded once, up front, all in flight together. Replaces five
+// launches of the general path.
 constexpr int kLowersSmallMax = 2048;  // beyond this the five-launch path is faster
 constexpr int kLowersSmallTiles = 1024;
 constexpr int kLowersThreads = 1024;
-constexpr int kLdsTiles = 36;
+constexpr int kLowersItems = kLowersSmallMax / kLowersThreads;
+constexpr int kLdsTiles = 28;
 constexpr int kReachMax = 512;  // source lowers with a reach set: n / m for m >= 8
 
 __global__ void __launch_bounds__(kLowersThreads) k_lowers_small(
     const int4* lower_origin, const u64* lower_mask, i64 n, int op, int m, int m_src, const int32_t* tile_of_cand,
     const int32_t* d_num_tiles, u64* tile_child, uint16_t* tile_prefix, int32_t* tile_lower_base,
     int32_t* d_num_cands, u64* cand_child, int zero_cand_child, int32_t* lower_nbr, int4* cand_origin,
-    int32_t* cand_src, int32_t* flags) {
+    int32_t* cand_src, int32_t* flags, const uint32_t* lower_reach) {
   __shared__ u64 s_tile[kLdsTiles * 512];
+  __shared__ uint16_t s_tpre[kLdsTiles * 512];
   __shared__ int32_t s_base[kLowersSmallTiles + 1];
   __shared__ uint32_t s_reach[kReachMax];
   __shared__ int32_t s_wave[kLowersThreads / kWave];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wv = tid / kWave;
+  constexpr int kWaves = kLowersThreads / kWave;
   const int32_t nt = *d_num_tiles;
+  const i64 n_lower = n / m;
+  // the origins of this thread's pairs (clamped, n >= 1: no load waits on another)
+  int4 po[kLowersItems];
+#pragma unroll
+  for (int k = 0; k < kLowersItems; ++k) po[k] = lower_origin[min((i64)(tid + k * kLowersThreads), n - 1) / m];
+  // reach set of every source lower: given (k_box_reach), or one wave per lower,
+  // one mask word per lane, four lowers per wave in flight
+  if (lower_reach) {
+    for (i64 l = tid; l < n_lower; l += kLowersThreads) s_reach[l] = lower_reach[l];
+  } else if (op != TC_OP_COARSEN) {
+    constexpr int kPer = 4;
+    for (i64 l0 = wv * kPer; l0 < n_lower; l0 += kWaves * kPer) {
+      u64 w4[kPer];
+#pragma unroll
+      for (int v = 0; v < kPer; ++v) w4[v] = lower_mask[min(l0 + v, n_lower - 1) * 64 + lane];
+#pragma unroll
+      for (int v = 0; v < kPer; ++v) {
+        uint32_t code = lower_word_reach(w4[v], lane, op);
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) code |= (uint32_t)__shfl_xor((int)code, d, kWave);
+        if (lane == 0 && l0 + v < n_lower) s_reach[l0 + v] = op == TC_OP_REFINE ? code : box_code_for_op(code, op, m);
+      }
+    }
+  }
   const bool in_lds = nt <= kLdsTiles;  // uniform
   u64* tch = in_lds ? s_tile : tile_child;
   if (in_lds) {
@@ -703,25 +795,38 @@ __global__ void __launch_bounds__(kLowersThreads) k_lowers_small(
   } else {
     ulonglong2* tc2 = reinterpret_cast<ulonglong2*>(tile_child);
     for (i64 k = tid; k < (i64)nt * 256; k += kLowersThreads) tc2[k] = make_ulonglong2(0, 0);
+    __threadfence();  // the zeros land before any wave's atomics below
   }
-  // reach set of every source lower: one wave per lower, one mask word per lane
-  const i64 n_lower = n / m;
-  if (op != TC_OP_COARSEN) {
-    for (i64 l = wv; l < n_lower; l += kLowersThreads / kWave) {
-      uint32_t code = lower_word_reach(lower_mask[l * 64 + lane], lane, op);
-#pragma unroll
-      for (int d = 32; d >= 1; d >>= 1) code |= (uint32_t)__shfl_xor((int)code, d, kWave);
-      if (lane == 0) s_reach[l] = op == TC_OP_REFINE ? code : box_code_for_op(code, op, m);
-    }
-  }
-  __threadfence();
   __syncthreads();
-  for (i64 i = tid; i < n; i += kLowersThreads)
-    lower_mark_one(i, lower_origin, lower_mask, s_reach, op, m, tile_of_cand, nt, tch, flags);
-  __threadfence();
+  // targets of the thread's pairs and their tiles
+  LowerTarget tg[kLowersItems];
+  int32_t tt[kLowersItems];
+  bool act[kLowersItems];
+#pragma unroll
+  for (int k = 0; k < kLowersItems; ++k) {
+    const i64 i = tid + k * kLowersThreads;
+    const i64 ic = min(i, n - 1);
+    const i64 l = ic / m;
+    const int j = (int)(ic % m);
+    tg[k] = lower_target(po[k], j, op);
+    act[k] = i < n && tg[k].ok && (op == TC_OP_COARSEN || ((s_reach[l] >> j) & 1u) != 0);
+  }
+#pragma unroll
+  for (int k = 0; k < kLowersItems; ++k) tt[k] = tile_of_cand[act[k] ? (i64)po[k].w * m + tg[k].jt : 0];
+#pragma unroll
+  for (int k = 0; k < kLowersItems; ++k) {
+    if (!act[k]) continue;
+    if (tt[k] < 0 || tt[k] >= nt) {
+      set_flag(flags, kFlagInternal);
+      continue;
+    }
+    const int bit = upper_child_bit(tg[k].k);
+    atomicOr((unsigned long long*)&tch[(i64)tt[k] * 512 + (bit >> 6)], 1ull << (bit & 63));
+  }
+  if (!in_lds) __threadfence();
   __syncthreads();
   // per-tile prefix tables: one wave per tile, 8 words per lane
-  for (int t = wv; t < nt; t += kLowersThreads / kWave) {
+  for (int t = wv; t < nt; t += kWaves) {
     u64 wd[8];
     int sum = 0;
 #pragma unroll
@@ -734,6 +839,7 @@ __global__ void __launch_bounds__(kLowersThreads) k_lowers_small(
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       tile_prefix[(i64)t * 512 + lane * 8 + k] = (uint16_t)ex;
+      if (in_lds) s_tpre[t * 512 + lane * 8 + k] = (uint16_t)ex;
       ex += popc64(wd[k]);
     }
     if (lane == kWave - 1) s_base[t] = inc;
@@ -755,11 +861,43 @@ __global__ void __launch_bounds__(kLowersThreads) k_lowers_small(
   for (i64 k = tid; k < (i64)total * m_src; k += kLowersThreads) cand_src[k] = -1;
   if (zero_cand_child)
     for (i64 k = tid; k < (i64)total * 64; k += kLowersThreads) cand_child[k] = 0;
-  __threadfence();
+  __threadfence();  // the fills land before other waves' table entries below
   __syncthreads();
-  for (i64 i = tid; i < n; i += kLowersThreads)
-    lower_nbr_one(i, lower_origin, lower_mask, s_reach, op, m, m_src, tile_of_cand, tch, tile_prefix, s_base, nt,
-                  total, lower_nbr, cand_origin, cand_src, flags);
+  // candidate index of every pair, its origin and its candidate -> source entry
+#pragma unroll
+  for (int k = 0; k < kLowersItems; ++k) {
+    const i64 i = tid + k * kLowersThreads;
+    if (i >= n) break;
+    if (!act[k] || tt[k] < 0 || tt[k] >= nt) {
+      lower_nbr[i] = -1;
+      continue;
+    }
+    const int t = tt[k];
+    const int bit = upper_child_bit(tg[k].k);
+    const int w = bit >> 6, b = bit & 63;
+    const u64 word = tch[(i64)t * 512 + w];
+    const int pre = in_lds ? s_tpre[t * 512 + w] : tile_prefix[(i64)t * 512 + w];
+    const int32_t c = s_base[t] + pre + popc64(word & ((1ull << b) - 1));
+    if (!((word >> b) & 1ull) || c < 0 || c >= total) {
+      lower_nbr[i] = -1;
+      set_flag(flags, kFlagInternal);
+      continue;
+    }
+    const int4 o = po[k];
+    const i64 l = i / m;
+    lower_nbr[i] = c;
+    cand_origin[c] = make_int4((int32_t)(tg[k].k.x * 128), (int32_t)(tg[k].k.y * 128), (int32_t)(tg[k].k.z * 128), t);
+    int js;
+    if (op == TC_OP_REFINE) {
+      js = 0;
+    } else if (op == TC_OP_COARSEN) {
+      js = octant_index((o.x >> 7) & 1, (o.y >> 7) & 1, (o.z >> 7) & 1);
+    } else {
+      const I3 e = box_offset((int)(i % m), op);
+      js = index27(-e.x, -e.y, -e.z);
+    }
+    cand_src[(i64)c * m_src + js] = (int32_t)l;
+  }
   if (in_lds)  // the node writers read the masks later
     for (int k = tid; k < nt * 512; k += kLowersThreads) tile_child[k] = s_tile[k];
 }
@@ -1441,15 +1579,25 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, 
   int32_t* cand_src = a.at<int32_t>(o_csrc);
 
   // tiles
-  const bool small_lowers = small_tiles && nT <= kLowersSmallTiles && nL <= kLowersSmallMax &&
+  const bool small_lowers = small_tiles && nT <= kLowersSmallTiles && nL > 0 && nL <= kLowersSmallMax &&
                             (op == TC_OP_COARSEN || nL / oi.m <= kReachMax);
+  // box ops on small batches: voxel-exact face reach sets of uppers and lowers
+  const bool box_op = op != TC_OP_REFINE && op != TC_OP_COARSEN;
+  uint32_t* box_lreach = nullptr;
+  if (small_lowers && box_op) {
+    box_lreach = a.at<uint32_t>(o_lreach);
+    launch("k_box_reach", k_box_reach, src->n2, 256, s, (const int4*)sv.upper_origin, (const int32_t*)sv.upper_first,
+           (int32_t)src->n2, (const int4*)sv.lower_origin, (const int32_t*)sv.lower_first, (int32_t)src->n1,
+           (const int4*)sv.leaf_origin, (const u64*)sv.leaf_mask, (int32_t)src->nl, op, oi.m,
+           a.at<uint32_t>(o_ureach), box_lreach);
+  }
   if (small_tiles) {
     // the bitmaps are zeroed in-kernel when few (at most 1 MiB for one workgroup):
     // by the fused lower stage, or here; otherwise by a wide fill
     const bool zero_here = !small_lowers && nT <= 256;
     // many source uppers: their reach sets in a wide launch first
-    uint32_t* ureach = nullptr;
-    if (op != TC_OP_COARSEN && src->n2 > 64) {
+    uint32_t* ureach = box_lreach ? a.at<uint32_t>(o_ureach) : nullptr;
+    if (!box_lreach && op != TC_OP_COARSEN && src->n2 > 64) {
       ureach = a.at<uint32_t>(o_ureach);
       launch("k_node_reach", k_node_reach, ceil_div((i64)src->n2, 4), 256, s, (const u64*)sv.upper_mask,
              (i64)src->n2, 512, op, oi.m, ureach);
@@ -1485,7 +1633,8 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, 
     launch("k_lowers_small", k_lowers_small, 1, kLowersThreads, s, (const int4*)sv.lower_origin,
            (const u64*)sv.lower_mask, nL, op, oi.m, oi.m_src, (const int32_t*)tile_of_cand,
            (const int32_t*)ts.d_num_tiles, ts.tile_child, ts.tile_prefix, ts.tile_lower_base, ts.d_num_cands,
-           ts.cand_child, op == TC_OP_COARSEN ? 1 : 0, lower_nbr, ts.cand_origin, cand_src, ts.flags);
+           ts.cand_child, op == TC_OP_COARSEN ? 1 : 0, lower_nbr, ts.cand_origin, cand_src, ts.flags,
+           (const uint32_t*)box_lreach);
   } else {
     uint32_t* lreach = nullptr;
     if (op != TC_OP_COARSEN) {

@@ -139,58 +139,120 @@ __global__ void __launch_bounds__(256) k_grid_counts(const int32_t* grid_tile_be
 // scan (output upper indices) and the per-grid counts in one workgroup.
 constexpr int kTailThreads = 1024;
 constexpr int kTailItems = 4;
+constexpr int kTailTiles = kTailThreads * kTailItems;
 
-__device__ __forceinline__ void counts_tail_body(const int32_t* grid_tile_begin, const int32_t* tile_lower_base,
-                                                 const i64* cand_scan, int32_t nt, int32_t nc, int32_t B,
+// Stages tile_lower_base[0, cap_t] (cap_t <= kTailTiles, the tile capacity known
+// to the host) in LDS. The loads do not wait for the tile count, and all of
+// them are in flight at once (clamped indices, no conditional load).
+__device__ __forceinline__ void stage_tile_bases(const int32_t* tile_lower_base, int32_t cap_t, int32_t* s_tlb) {
+  int32_t v[kTailItems + 1];
+#pragma unroll
+  for (int k = 0; k <= kTailItems; ++k) v[k] = tile_lower_base[min(k * kTailThreads + (int)threadIdx.x, cap_t)];
+#pragma unroll
+  for (int k = 0; k <= kTailItems; ++k) {
+    const int t = k * kTailThreads + threadIdx.x;
+    if (t <= cap_t) s_tlb[t] = v[k];
+  }
+}
+
+// Tile t (< nt) is non-empty when its candidate lowers hold a leaf. s_tlb holds
+// the tiles' candidate bases (staged, the caller has synchronised), cs the
+// packed candidate scan (LDS or global), gt the grid_tile_begin pair of grid
+// threadIdx.x (loaded early by the caller). Upper indices stay in LDS (s_uex) for
+// the per-grid counts and go to upper_excl for the node writers.
+__device__ __forceinline__ void counts_tail_body(const int32_t* grid_tile_begin, int2 gt, const int32_t* s_tlb,
+                                                 const i64* cs, int32_t nt, int32_t nc, int32_t B, int32_t* s_uex,
                                                  int32_t* upper_excl, int32_t* grid_info, int32_t* readback,
                                                  int32_t* s_wave) {
+  const int tid = threadIdx.x;
+  int32_t lv[kTailItems + 1];
+#pragma unroll
+  for (int k = 0; k <= kTailItems; ++k) lv[k] = scan_leaf(cs[s_tlb[min(tid * kTailItems + k, nt)]]);
   int f[kTailItems];
   int sum = 0;
 #pragma unroll
   for (int k = 0; k < kTailItems; ++k) {
-    const int t = threadIdx.x * kTailItems + k;
-    f[k] = (t < nt && scan_leaf(cand_scan[tile_lower_base[t + 1]]) > scan_leaf(cand_scan[tile_lower_base[t]])) ? 1 : 0;
+    f[k] = tid * kTailItems + k < nt && lv[k + 1] > lv[k] ? 1 : 0;
     sum += f[k];
   }
   int total;
   int ex = block_excl_scan<int, kTailThreads>(sum, s_wave, total);
 #pragma unroll
   for (int k = 0; k < kTailItems; ++k) {
-    const int t = threadIdx.x * kTailItems + k;
-    if (t < nt) upper_excl[t] = ex;
+    const int t = tid * kTailItems + k;
+    if (t < nt) {
+      s_uex[t] = ex;
+      upper_excl[t] = ex;
+    }
     ex += f[k];
   }
-  if (threadIdx.x == 0) upper_excl[nt] = total;
-  __threadfence();
-  __syncthreads();  // upper_excl is read back below by other threads of this block
-  if (threadIdx.x == 0) batch_totals(upper_excl, cand_scan, nt, nc, readback);
-  for (i64 g = threadIdx.x; g < B; g += kTailThreads)
-    grid_counts_one(g, grid_tile_begin, tile_lower_base, upper_excl, cand_scan, grid_info, readback);
+  if (tid == 0) {
+    s_uex[nt] = total;
+    upper_excl[nt] = total;
+    const i64 last = cs[nc];
+    readback[1] = total;
+    readback[2] = scan_lower(last);
+    readback[3] = scan_leaf(last);
+  }
+  __syncthreads();
+  for (int32_t g = tid; g < B; g += kTailThreads) {
+    const int32_t tb = g == tid ? gt.x : grid_tile_begin[g], te = g == tid ? gt.y : grid_tile_begin[g + 1];
+    const i64 vb = cs[s_tlb[tb]], ve = cs[s_tlb[te]];
+    const int32_t nu = s_uex[te] - s_uex[tb];
+    const int32_t n1 = scan_lower(ve) - scan_lower(vb);
+    const int32_t nl = scan_leaf(ve) - scan_leaf(vb);
+    int32_t* gi = grid_info + (i64)g * 6;
+    gi[0] = nu;
+    gi[1] = n1;
+    gi[2] = nl;
+    gi[3] = s_uex[tb];
+    gi[4] = scan_lower(vb);
+    gi[5] = scan_leaf(vb);
+    readback[4 + g * 3 + 0] = nu;
+    readback[4 + g * 3 + 1] = n1;
+    readback[4 + g * 3 + 2] = nl;
+  }
+}
+
+__device__ __forceinline__ int2 load_grid_tiles(const int32_t* grid_tile_begin, int32_t B) {
+  const int g = min((int)threadIdx.x, B);  // grid_tile_begin has B + 1 entries
+  return make_int2(grid_tile_begin[g], grid_tile_begin[min(g + 1, B)]);
 }
 
 __global__ void __launch_bounds__(kTailThreads) k_counts_tail(const int32_t* grid_tile_begin,
-                                                              const int32_t* tile_lower_base, const i64* cand_scan,
-                                                              const int32_t* d_num_tiles, const int32_t* d_num_cands,
-                                                              int32_t B, int32_t* upper_excl, int32_t* grid_info,
+                                                              const int32_t* tile_lower_base, int32_t cap_t,
+                                                              const i64* cand_scan, const int32_t* d_num_tiles,
+                                                              const int32_t* d_num_cands, int32_t B,
+                                                              int32_t* upper_excl, int32_t* grid_info,
                                                               int32_t* readback) {
+  __shared__ int32_t s_tlb[kTailTiles + 1];
+  __shared__ int32_t s_uex[kTailTiles + 1];
   __shared__ int32_t s_wave[kTailThreads / kWave];
-  counts_tail_body(grid_tile_begin, tile_lower_base, cand_scan, *d_num_tiles, *d_num_cands, B, upper_excl, grid_info,
-                   readback, s_wave);
+  const int32_t nt = *d_num_tiles, nc = *d_num_cands;
+  const int2 gt = load_grid_tiles(grid_tile_begin, B);
+  stage_tile_bases(tile_lower_base, cap_t, s_tlb);
+  __syncthreads();
+  counts_tail_body(grid_tile_begin, gt, s_tlb, cand_scan, nt, nc, B, s_uex, upper_excl, grid_info, readback, s_wave);
 }
 
-// Small batches (at most kCountsSmallMax candidates and kTailThreads * kTailItems
-// tiles): candidate leaf counts and prefix tables, their packed scan and the
-// tail above, in one workgroup.
+// Small batches (at most kCountsSmallMax candidates and kTailTiles tiles):
+// candidate leaf counts and prefix tables, their packed scan and the tail above,
+// in one workgroup. Every global load (the counts, the candidate masks up to
+// the host-known capacity cap_c, the tile bases, the grid ranges) is issued
+// before the first wait.
 constexpr int kCountsSmallMax = 2048;  // beyond this the multi-launch path is faster
 
-__global__ void __launch_bounds__(kTailThreads) k_counts_small(const u64* cand_child, uint16_t* cand_prefix,
-                                                               i64* cand_counts, i64* cand_scan,
-                                                               const int32_t* grid_tile_begin,
-                                                               const int32_t* tile_lower_base,
-                                                               const int32_t* d_num_tiles, const int32_t* d_num_cands,
-                                                               int32_t B, int32_t* upper_excl, int32_t* grid_info,
+__global__ void __launch_bounds__(kTailThreads) k_counts_small(const u64* cand_child, int32_t cap_c,
+                                                               uint16_t* cand_prefix, i64* cand_counts,
+                                                               i64* cand_scan, const int32_t* grid_tile_begin,
+                                                               const int32_t* tile_lower_base, int32_t cap_t,
+                                                               const int32_t* d_num_tiles,
+                                                               const int32_t* d_num_cands, int32_t B,
+                                                               int32_t* upper_excl, int32_t* grid_info,
                                                                int32_t* readback) {
   __shared__ i64 s_cc[kCountsSmallMax + 1];
+  __shared__ int32_t s_tlb[kTailTiles + 1];
+  __shared__ int32_t s_uex[kTailTiles + 1];
   __shared__ int32_t s_wave[kTailThreads / kWave];
   __shared__ i64 s_wave64[kTailThreads / kWave];
   const int tid = threadIdx.x;
@@ -198,14 +260,19 @@ __global__ void __launch_bounds__(kTailThreads) k_counts_small(const u64* cand_c
   const int wv = tid / kWave;
   const int32_t nc = *d_num_cands;
   const int32_t nt = *d_num_tiles;
-  // one wave per candidate (four in flight): per-word prefix and the packed count
+  const int2 gt = load_grid_tiles(grid_tile_begin, B);
+  stage_tile_bases(tile_lower_base, cap_t, s_tlb);
+  // one wave per candidate, up to 2048 / 16 = 128 per wave: per-word prefix and
+  // the packed count. The masks are loaded up to the capacity (clamped), so no
+  // load waits for the candidate count.
   constexpr int kWaves = kTailThreads / kWave;
-  for (int c0 = wv * 4; c0 < nc; c0 += kWaves * 4) {
-    u64 w[4];
+  constexpr int kPerWave = 4;
+  for (int c0 = wv * kPerWave; c0 < cap_c; c0 += kWaves * kPerWave) {
+    u64 w[kPerWave];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) w[v] = c0 + v < nc ? cand_child[(i64)(c0 + v) * 64 + lane] : 0;
+    for (int v = 0; v < kPerWave; ++v) w[v] = cand_child[(i64)min(c0 + v, cap_c - 1) * 64 + lane];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
+    for (int v = 0; v < kPerWave; ++v) {
       if (c0 + v >= nc) break;
       const int cnt = popc64(w[v]);
       const int inc = wave_incl_scan(cnt);
@@ -218,7 +285,7 @@ __global__ void __launch_bounds__(kTailThreads) k_counts_small(const u64* cand_c
     }
   }
   __syncthreads();
-  // exclusive scan of the packed counts (blocked, 4 per thread)
+  // exclusive scan of the packed counts (blocked, 2 per thread)
   constexpr int kPer = kCountsSmallMax / kTailThreads;
   i64 v[kPer];
   i64 sum = 0;
@@ -246,15 +313,15 @@ __global__ void __launch_bounds__(kTailThreads) k_counts_small(const u64* cand_c
     s_cc[nc] = total;
   }
   __syncthreads();
-  counts_tail_body(grid_tile_begin, tile_lower_base, s_cc, nt, nc, B, upper_excl, grid_info, readback, s_wave);
+  counts_tail_body(grid_tile_begin, gt, s_tlb, s_cc, nt, nc, B, s_uex, upper_excl, grid_info, readback, s_wave);
 }
 
 void tree_counts(TreeScratch& ts, int32_t B, hipStream_t s) {
   if (ts.cap_cands <= kCountsSmallMax && ts.cap_tiles <= (i64)kTailThreads * kTailItems) {
-    launch("k_counts_small", k_counts_small, 1, kTailThreads, s, (const u64*)ts.cand_child, ts.cand_prefix,
-           ts.cand_counts, ts.cand_scan, (const int32_t*)ts.grid_tile_begin, (const int32_t*)ts.tile_lower_base,
-           (const int32_t*)ts.d_num_tiles, (const int32_t*)ts.d_num_cands, B, ts.upper_excl, ts.grid_info,
-           ts.readback);
+    launch("k_counts_small", k_counts_small, 1, kTailThreads, s, (const u64*)ts.cand_child, (int32_t)ts.cap_cands,
+           ts.cand_prefix, ts.cand_counts, ts.cand_scan, (const int32_t*)ts.grid_tile_begin,
+           (const int32_t*)ts.tile_lower_base, (int32_t)ts.cap_tiles, (const int32_t*)ts.d_num_tiles,
+           (const int32_t*)ts.d_num_cands, B, ts.upper_excl, ts.grid_info, ts.readback);
     return;
   }
   tree_count_cands(ts, s);
@@ -270,8 +337,9 @@ void tree_count_cands(TreeScratch& ts, hipStream_t s) {
 void tree_grid_counts(TreeScratch& ts, int32_t B, hipStream_t s) {
   if (ts.cap_tiles <= (i64)kTailThreads * kTailItems) {
     launch("k_counts_tail", k_counts_tail, 1, kTailThreads, s, (const int32_t*)ts.grid_tile_begin,
-           (const int32_t*)ts.tile_lower_base, (const i64*)ts.cand_scan, (const int32_t*)ts.d_num_tiles,
-           (const int32_t*)ts.d_num_cands, B, ts.upper_excl, ts.grid_info, ts.readback);
+           (const int32_t*)ts.tile_lower_base, (int32_t)ts.cap_tiles, (const i64*)ts.cand_scan,
+           (const int32_t*)ts.d_num_tiles, (const int32_t*)ts.d_num_cands, B, ts.upper_excl, ts.grid_info,
+           ts.readback);
     return;
   }
   launch("k_tile_flags", k_tile_flags, ceil_div(ts.cap_tiles, 256), 256, s, (const int32_t*)ts.tile_lower_base,
@@ -464,6 +532,7 @@ __global__ void __launch_bounds__(kFinThreads) k_finalize_small(const int4* leaf
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wv = tid / kWave;
+  const int gs = __builtin_ctzll((u64)gran);  // gran is a power of two
   const i64 pv = tid < np ? vox_part[tid] : 0;
   for (int g = tid; g < B; g += kFinThreads) {
     for (int a = 0; a < 3; ++a) {
@@ -477,7 +546,7 @@ __global__ void __launch_bounds__(kFinThreads) k_finalize_small(const int4* leaf
   __syncthreads();
   for (int g = tid; g <= B; g += kFinThreads) {
     const i64 f = g < B ? grid_info[g * 6 + 5] : L;
-    s_gvb[g] = f < L ? s_part[f / gran] + leaf_inrun[f] : total;
+    s_gvb[g] = f < L ? s_part[f >> gs] + leaf_inrun[f] : total;
   }
   __syncthreads();
   for (i64 base = 0; base < L; base += (i64)kWaves * kRun) {
@@ -485,13 +554,14 @@ __global__ void __launch_bounds__(kFinThreads) k_finalize_small(const int4* leaf
     int4 o[kFinPer];
     uint32_t bx[kFinPer];
     int32_t in_run[kFinPer];
+    // unconditional loads at clamped indices: all of them in flight at once
+    // (lanes past L are skipped below)
 #pragma unroll
     for (int k = 0; k < kFinPer; ++k) {
-      const i64 i = run0 + k * kWave + lane;
-      const bool in = i < L;
-      o[k] = in ? leaf_origin[i] : make_int4(0, 0, 0, -1);
-      bx[k] = in ? leaf_box[i] : kEmptyBox;
-      in_run[k] = in ? leaf_inrun[i] : 0;
+      const i64 i = min(run0 + k * kWave + lane, L - 1);
+      o[k] = leaf_origin[i];
+      bx[k] = leaf_box[i];
+      in_run[k] = leaf_inrun[i];
     }
     int g = -1;
     int bv[6] = {INT32_MAX, INT32_MAX, INT32_MAX, INT32_MIN, INT32_MIN, INT32_MIN};
@@ -500,7 +570,7 @@ __global__ void __launch_bounds__(kFinThreads) k_finalize_small(const int4* leaf
       const i64 i = run0 + k * kWave + lane;
       const int gk = o[k].w;
       if (i >= L || gk < 0 || gk >= B) continue;
-      leaf_offset[i] = s_part[i / gran] + in_run[k] - s_gvb[gk];
+      leaf_offset[i] = s_part[i >> gs] + in_run[k] - s_gvb[gk];
       if (bx[k] == kEmptyBox) continue;
       if (gk != g) {
         if (g >= 0) box_fold_lds(s_box, g, bv);
@@ -599,7 +669,7 @@ __global__ void __launch_bounds__(kPartThreads) k_vox_partials(i64* vox_part, i6
   // a grid's voxel begin: its first leaf's run offset plus that leaf's in-run prefix
   for (int32_t g = threadIdx.x; g <= B; g += kPartThreads) {
     const i64 f = g < B ? grid_info[g * 6 + 5] : L;
-    gvb[g] = f < L ? vox_part[f / gran] + leaf_inrun[f] : carry;
+    gvb[g] = f < L ? vox_part[f >> __builtin_ctzll((u64)gran)] + leaf_inrun[f] : carry;
   }
 }
 
@@ -610,7 +680,7 @@ __global__ void __launch_bounds__(256) k_leaf_offsets_runs(const int4* leaf_orig
                                                            int32_t B, int32_t R, i64 n_leaf) {
   const i64 i = (i64)blockIdx.x * 256 + threadIdx.x;
   const int lane = threadIdx.x & (kWave - 1);
-  const i64 ex = i < n_leaf ? vox_part[i / gran] + leaf_inrun[i] : 0;  // batch-global voxel index of the leaf
+  const i64 ex = i < n_leaf ? vox_part[i >> __builtin_ctzll((u64)gran)] + leaf_inrun[i] : 0;  // batch-global voxel index of the leaf
   int g = -1;
   int bv[6] = {INT32_MAX, INT32_MAX, INT32_MAX, INT32_MIN, INT32_MIN, INT32_MIN};
   if (i < n_leaf) {
@@ -694,6 +764,7 @@ void tree_finalize_leaves(const GridView& out, const uint32_t* leaf_box, const i
                           i64 gran, i64* gvb, int32_t* bbox_accum, const int32_t* grid_info, hipStream_t s) {
   const i64 L = out.n_leaf;
   const int32_t B = out.B;
+  if (gran <= 0 || (gran & (gran - 1)) != 0) throw Error(TC_ERR_INTERNAL, "finalize: run length not a power of two");
   if (L <= kFinSmallLeaves && B <= kFinSmallGrids && ceil_div(L, gran) <= kFinThreads) {
     launch("k_finalize_small", k_finalize_small, 1, kFinThreads, s, (const int4*)out.leaf_origin, leaf_inrun,
            leaf_box, (const i64*)vox_part, ceil_div(L, gran), gran, grid_info, out.leaf_offset, B, L, out.headers);

@@ -153,8 +153,13 @@ def _check(status: int):
 
 def _stream_handle(stream=None):
     import torch
-    s = stream if stream is not None else torch.cuda.current_stream()
-    return ctypes.c_void_p(s.cuda_stream)
+    if stream is not None:
+        return ctypes.c_void_p(stream.cuda_stream)
+    # the current stream's raw handle without building a Stream object per call
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None:
+        return ctypes.c_void_p(raw(torch._C._cuda_getDevice()))
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
 def _torch_alloc(ctx, nbytes, stream):

@@ -3,6 +3,7 @@
 // error reporting. No exception crosses the boundary.
 #include <algorithm>
 #include <cmath>
+#include <cstddef>
 #include <cstring>
 #include <new>
 #include <string>
@@ -100,6 +101,7 @@ tc_grid_batch* copy_batch(const tc_grid_batch* src, const OutAlloc& oa) {
 
 void free_batch(tc_grid_batch* b) {
   if (!b) return;
+  vox_slot_give(b->vox_slot);  // a copy still in flight is waited for by the slot's next taker
   if (b->buffer) {
     if (b->has_alloc) {
       if (b->alloc.free) b->alloc.free(b->alloc.ctx, b->buffer, b->bytes, (void*)b->stream);
@@ -110,8 +112,48 @@ void free_batch(tc_grid_batch* b) {
   delete b;
 }
 
+static_assert(offsetof(tc_grid_header, voxel_begin) == offsetof(tc_grid_header, voxel_count) + 8,
+              "voxel count and begin are read back as one 16-byte pair");
+
+// Queues the copy of the last member's voxel count and begin behind the
+// builder's kernels (stream s) and records the slot's event, so that the first
+// request for the total waits for that event instead of a new round trip.
+static void queue_voxel_total(tc_grid_batch* b, hipStream_t s) {
+  if (b->vox_known || b->B <= 0) return;
+  if (b->vox_slot < 0) {
+    const VoxTicket t = vox_slot_take(b->device);
+    b->vox_slot = t.slot;
+    b->vox_h = t.h;
+    b->vox_ev = t.ev;
+  }
+  const GridView v = b->view();
+  hip_check(hipMemcpyAsync(b->vox_h, &v.headers[b->B - 1].voxel_count, 16, hipMemcpyDeviceToHost, s),
+            "voxel total readback");
+  hip_check(hipEventRecord(b->vox_ev, s), "hipEventRecord");
+  b->vox_pending = true;
+}
+
+// Hands a finished batch to the caller with its voxel total queued; frees it if
+// queueing fails.
+static tc_grid_batch* finish_batch(tc_grid_batch* b, hipStream_t s) {
+  try {
+    queue_voxel_total(b, s);
+  } catch (...) {
+    free_batch(b);
+    throw;
+  }
+  return b;
+}
+
 static i64 read_voxel_total(const tc_grid_batch* b, hipStream_t s) {
   if (b->vox_known) return b->vox_total;
+  if (b->vox_pending) {
+    hip_check(hipEventSynchronize(b->vox_ev), "hipEventSynchronize");
+    b->vox_total = b->vox_h[0] + b->vox_h[1];
+    b->vox_known = true;
+    b->vox_pending = false;
+    return b->vox_total;
+  }
   tc_grid_header* h = static_cast<tc_grid_header*>(pinned_staging(sizeof(tc_grid_header)));
   const GridView v = b->view();
   hip_check(hipMemcpyAsync(h, v.headers + (b->B - 1), sizeof(tc_grid_header), hipMemcpyDeviceToHost, s),
@@ -158,7 +200,9 @@ tc_status tc_batch_from_ijk(const int32_t* d_ijk, const int64_t* h_offsets, int3
   if (allocator && (!allocator->alloc || !allocator->free))
     return fail(TC_ERR_INVALID_ARG, "allocator callbacks are NULL");
   return guarded([&]() {
-    *out = tc::build_from_ijk(d_ijk, h_offsets, grid_count, tc::OutAlloc{allocator, (hipStream_t)stream});
+    *out = tc::finish_batch(
+        tc::build_from_ijk(d_ijk, h_offsets, grid_count, tc::OutAlloc{allocator, (hipStream_t)stream}),
+        (hipStream_t)stream);
     return TC_OK;
   });
 }
@@ -186,8 +230,9 @@ tc_status tc_batch_from_points(const float* d_xyz, const int64_t* h_offsets, int
   if (allocator && (!allocator->alloc || !allocator->free))
     return fail(TC_ERR_INVALID_ARG, "allocator callbacks are NULL");
   return guarded([&]() {
-    *out = tc::build_from_points(d_xyz, h_offsets, grid_count, h_voxel_size, h_origin, mode,
-                                 tc::OutAlloc{allocator, (hipStream_t)stream});
+    *out = tc::finish_batch(tc::build_from_points(d_xyz, h_offsets, grid_count, h_voxel_size, h_origin, mode,
+                                                  tc::OutAlloc{allocator, (hipStream_t)stream}),
+                            (hipStream_t)stream);
     return TC_OK;
   });
 }
@@ -239,7 +284,7 @@ tc_status tc_build_batched_topology(const tc_grid_batch* src, int32_t op, int32_
     if (current_device() != src->device) throw tc::Error(TC_ERR_INVALID_ARG, "src lives on another device");
     hipStream_t s = (hipStream_t)stream;
     if (passes.empty()) {  // kernel size 1: the target is the source
-      *out = tc::copy_batch(src, tc::OutAlloc{allocator, s});
+      *out = tc::finish_batch(tc::copy_batch(src, tc::OutAlloc{allocator, s}), s);
       return TC_OK;
     }
     const tc_grid_batch* cur = src;
@@ -256,7 +301,7 @@ tc_status tc_build_batched_topology(const tc_grid_batch* src, int32_t op, int32_
       tc::free_batch(owned);
       throw;
     }
-    *out = owned;
+    *out = tc::finish_batch(owned, s);
     return TC_OK;
   });
 }
@@ -313,7 +358,7 @@ tc_status tc_build_masked_refine(const tc_grid_batch* src, const uint8_t* d_keep
       tc::free_batch(owned);
       throw;
     }
-    *out = owned;
+    *out = tc::finish_batch(owned, s);
     return TC_OK;
   });
 }

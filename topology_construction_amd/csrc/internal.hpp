@@ -174,6 +174,17 @@ void batch_buffers_release();
 // Per-thread pinned host staging buffer (grows on demand, never shrinks).
 void* pinned_staging(size_t bytes);
 
+// Pinned 16-byte host slots, each with an event, for the voxel total of a batch:
+// the copy is queued behind a builder's last kernel and read when first asked.
+// Slots belong to a device; taking one waits for its previous copy to land.
+struct VoxTicket {
+  int slot;
+  int64_t* h;
+  hipEvent_t ev;
+};
+VoxTicket vox_slot_take(int device);
+void vox_slot_give(int slot);
+
 // Stream-ordered device allocation from the device's default pool (release
 // threshold raised once per device so that memory is cached across calls).
 void* device_alloc_async(size_t bytes, hipStream_t s);
@@ -316,6 +327,11 @@ struct tc_grid_batch {
   int device = 0;
   mutable bool vox_known = false;
   mutable int64_t vox_total = 0;
+  // voxel total queued for readback (queue_voxel_total): slot, host words, event
+  mutable bool vox_pending = false;
+  mutable int vox_slot = -1;
+  mutable int64_t* vox_h = nullptr;
+  mutable hipEvent_t vox_ev = nullptr;
 
   tc::GridView view() const {
     return tc::make_view(buffer, layout, B, n2, n1, nl);

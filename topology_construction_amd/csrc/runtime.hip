@@ -214,6 +214,65 @@ void* pinned_staging(size_t bytes) {
   return p;
 }
 
+// ------------------------------------------------------------------ voxel-total slots
+namespace {
+constexpr int kVoxChunk = 256;  // slots per pinned allocation, 16 bytes each
+struct VoxSlot {
+  int64_t* h;
+  hipEvent_t ev;
+  int device;
+};
+struct VoxPool {
+  std::mutex mu;
+  std::vector<VoxSlot> slots;
+  std::vector<int> idle;
+};
+VoxPool& vox_pool() {
+  static VoxPool* p = new VoxPool();  // never destroyed: batches may outlive static teardown
+  return *p;
+}
+}  // namespace
+
+VoxTicket vox_slot_take(int device) {
+  VoxPool& p = vox_pool();
+  VoxTicket t{-1, nullptr, nullptr};
+  {
+    std::lock_guard<std::mutex> g(p.mu);
+    for (size_t k = 0; k < p.idle.size(); ++k) {
+      if (p.slots[p.idle[k]].device == device) {
+        t.slot = p.idle[k];
+        p.idle[k] = p.idle.back();
+        p.idle.pop_back();
+        break;
+      }
+    }
+    if (t.slot < 0) {
+      void* h = nullptr;
+      hip_check(hipHostMalloc(&h, 16 * kVoxChunk, hipHostMallocDefault), "hipHostMalloc");
+      const int base = (int)p.slots.size();
+      for (int k = 0; k < kVoxChunk; ++k) {
+        p.slots.push_back(VoxSlot{static_cast<int64_t*>(h) + 2 * k, nullptr, device});
+        if (k) p.idle.push_back(base + k);
+      }
+      t.slot = base;
+    }
+    VoxSlot& v = p.slots[t.slot];
+    if (!v.ev) hip_check(hipEventCreateWithFlags(&v.ev, hipEventDisableTiming), "hipEventCreateWithFlags");
+    t.h = v.h;
+    t.ev = v.ev;
+  }
+  // the slot's previous copy (its batch may have been freed unread) has landed
+  if (hipEventQuery(t.ev) != hipSuccess) hip_check(hipEventSynchronize(t.ev), "hipEventSynchronize");
+  return t;
+}
+
+void vox_slot_give(int slot) {
+  if (slot < 0) return;
+  VoxPool& p = vox_pool();
+  std::lock_guard<std::mutex> g(p.mu);
+  p.idle.push_back(slot);
+}
+
 // ------------------------------------------------------------------ profiling
 namespace {
 struct Timed {

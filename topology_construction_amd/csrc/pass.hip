@@ -423,29 +423,46 @@ __global__ void __launch_bounds__(kTilesThreads) k_tiles_small(const int4* upper
   }
   __shared__ int32_t s_nt;
   if (K <= kWave) {
-    // few keys: one wave sorts (bitonic over lanes), deduplicates and scatters,
-    // with no block barriers
+    // few keys: a rank sort (keys are distinct through their candidate index):
+    // wave w compares every key with keys 4w .. 4w+3, wave 0 adds the partial
+    // ranks, places each key at its rank (LDS, past the first kWave entries),
+    // reads the sorted keys back, deduplicates and scatters
+    __shared__ int32_t s_cnt[kTilesThreads / kWave][kWave];
     __syncthreads();
-    if (wv == 0) {
-      u64 hi = lane < K ? s_hi[lane] : ~0ull, lo = lane < K ? s_lo[lane] : ~0ull;
-      uint32_t v = lane < K ? s_v[lane] : 0xffffffffu;
+    {
+      int c = 0;
+      if (lane < K) {
+        const u64 hi = s_hi[lane], lo = s_lo[lane];
+        const uint32_t v = s_v[lane];
 #pragma unroll
-      for (int k = 2; k <= kWave; k <<= 1) {
-#pragma unroll
-        for (int jj = k >> 1; jj > 0; jj >>= 1) {
-          const u64 oh = __shfl_xor(hi, jj, kWave), ol = __shfl_xor(lo, jj, kWave);
-          const uint32_t ov = (uint32_t)__shfl_xor((int)v, jj, kWave);
-          const bool gt = hi != oh ? hi > oh : (lo != ol ? lo > ol : v > ov);
-          const bool lt = hi != oh ? hi < oh : (lo != ol ? lo < ol : v < ov);
-          const bool up = (lane & k) == 0, lower = (lane & jj) == 0;
-          const bool take = up ? (lower ? gt : lt) : (lower ? lt : gt);
-          if (take) {
-            hi = oh;
-            lo = ol;
-            v = ov;
+        for (int q = 0; q < 4; ++q) {
+          const int j = wv * 4 + q;
+          if (j < K) {
+            const u64 oh = s_hi[j], ol = s_lo[j];
+            const uint32_t ov = s_v[j];
+            c += (oh != hi ? oh < hi : (ol != lo ? ol < lo : ov < v)) ? 1 : 0;
           }
         }
       }
+      s_cnt[wv][lane] = c;
+    }
+    __syncthreads();
+    if (wv == 0) {
+      if (lane < K) {
+        int rank = 0;
+#pragma unroll
+        for (int w = 0; w < kTilesThreads / kWave; ++w) rank += s_cnt[w][lane];
+        const u64 h0 = s_hi[lane], l0 = s_lo[lane];
+        const uint32_t v0 = s_v[lane];
+        s_hi[kWave + rank] = h0;
+        s_lo[kWave + rank] = l0;
+        s_v[kWave + rank] = v0;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const u64 hi = lane < K ? s_hi[kWave + lane] : ~0ull, lo = lane < K ? s_lo[kWave + lane] : ~0ull;
+      const uint32_t v = lane < K ? s_v[kWave + lane] : 0xffffffffu;
       const u64 ph = __shfl_up(hi, 1, kWave), pl = __shfl_up(lo, 1, kWave);
       const int head = lane < K && (lane == 0 || !(ph == hi && pl == lo)) ? 1 : 0;
       const int inc = wave_incl_scan(head);
@@ -754,8 +771,8 @@ __global__ void __launch_bounds__(kLowersThreads) k_lowers_small(
     const int32_t* d_num_tiles, u64* tile_child, uint16_t* tile_prefix, int32_t* tile_lower_base,
     int32_t* d_num_cands, u64* cand_child, int zero_cand_child, int32_t* lower_nbr, int4* cand_origin,
     int32_t* cand_src, int32_t* flags, const uint32_t* lower_reach) {
-  __shared__ u64 s_tile[kLdsTiles * 512];
-  __shared__ uint16_t s_tpre[kLdsTiles * 512];
+  __shared__ __align__(16) u64 s_tile[kLdsTiles * 512];
+  __shared__ __align__(16) uint16_t s_tpre[kLdsTiles * 512];
   __shared__ int32_t s_base[kLowersSmallTiles + 1];
   __shared__ uint32_t s_reach[kReachMax];
   __shared__ int32_t s_wave[kLowersThreads / kWave];
@@ -836,12 +853,17 @@ __global__ void __launch_bounds__(kLowersThreads) k_lowers_small(
     }
     const int inc = wave_incl_scan(sum);
     int ex = inc - sum;
+    uint32_t pk[4];  // the lane's 8 prefixes as 16-bit pairs: one 16-byte store
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      tile_prefix[(i64)t * 512 + lane * 8 + k] = (uint16_t)ex;
-      if (in_lds) s_tpre[t * 512 + lane * 8 + k] = (uint16_t)ex;
-      ex += popc64(wd[k]);
+    for (int k = 0; k < 4; ++k) {
+      const int e0 = ex;
+      ex += popc64(wd[2 * k]);
+      pk[k] = (uint32_t)e0 | ((uint32_t)ex << 16);
+      ex += popc64(wd[2 * k + 1]);
     }
+    const uint4 pv = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    reinterpret_cast<uint4*>(tile_prefix)[(i64)t * 64 + lane] = pv;
+    if (in_lds) reinterpret_cast<uint4*>(s_tpre)[t * 64 + lane] = pv;
     if (lane == kWave - 1) s_base[t] = inc;
   }
   __syncthreads();
@@ -898,8 +920,11 @@ __global__ void __launch_bounds__(kLowersThreads) k_lowers_small(
     }
     cand_src[(i64)c * m_src + js] = (int32_t)l;
   }
-  if (in_lds)  // the node writers read the masks later
-    for (int k = tid; k < nt * 512; k += kLowersThreads) tile_child[k] = s_tile[k];
+  if (in_lds) {  // the node writers read the masks later
+    const ulonglong2* src2 = reinterpret_cast<const ulonglong2*>(s_tile);
+    ulonglong2* dst2 = reinterpret_cast<ulonglong2*>(tile_child);
+    for (int k = tid; k < nt * 256; k += kLowersThreads) dst2[k] = src2[k];
+  }
 }
 
 // ------------------------------------------------------------------ stage: leaves (pass A)

@@ -11,6 +11,8 @@
 // This replaces the per-slot sort and head-flag dedup of the PR page (section 1)
 // at leaf level with bitmap marking plus popcount ranks: duplicates collapse in
 // the bitmaps and ranks come from prefix popcounts, so no leaf-level sort runs.
+#include <algorithm>
+
 #include "device.hpp"
 #include "internal.hpp"
 
@@ -356,14 +358,24 @@ void tree_grid_counts(TreeScratch& ts, int32_t B, hipStream_t s) {
 // are cleared). The remaining blocks own four candidate lowers each (one wave
 // per candidate) and write the lower node record plus one leaf record (origin,
 // grid, parent) per set bit of its leaf mask; leaf_cand[leaf] remembers the
-// candidate for the leaf-mask producers.
+// candidate for the leaf-mask producers. Block 0 also sets every header's box
+// to empty for the leaf finalizer.
 __global__ void __launch_bounds__(256) k_write_nodes(
     int32_t tile_blocks, const int4* utile, const u64* tile_child, const uint16_t* tile_prefix,
     const int32_t* tile_lower_base, const int4* cand_origin, const u64* cand_child, const uint16_t* cand_prefix,
     const i64* cand_counts, const i64* cand_scan, const int32_t* upper_excl, const int32_t* d_num_tiles,
     const int32_t* d_num_cands, int32_t n_upper, int32_t n_lower, int32_t n_leaf, int4* upper_origin,
     u64* upper_key, int32_t* upper_first, u64* upper_mask, int4* lower_origin, int32_t* lower_first,
-    u64* lower_mask, uint16_t* lower_prefix, int4* leaf_origin, int32_t* leaf_parent, int32_t* leaf_cand) {
+    u64* lower_mask, uint16_t* lower_prefix, int4* leaf_origin, int32_t* leaf_parent, int32_t* leaf_cand,
+    tc_grid_header* hdr, int32_t B) {
+  if (blockIdx.x == 0) {  // every grid's box starts empty; the leaf finalizer folds into it
+    for (int32_t g = threadIdx.x; g < B; g += 256) {
+      for (int a = 0; a < 3; ++a) {
+        hdr[g].bbox_min[a] = INT32_MAX;
+        hdr[g].bbox_max[a] = INT32_MIN;
+      }
+    }
+  }
   if ((int32_t)blockIdx.x < tile_blocks) {
     const i64 t = blockIdx.x;
     if (t >= *d_num_tiles) return;
@@ -445,7 +457,8 @@ void tree_write_nodes(TreeScratch& ts, const GridView& out, int32_t* leaf_cand, 
          (const uint16_t*)ts.cand_prefix, (const i64*)ts.cand_counts, (const i64*)ts.cand_scan,
          (const int32_t*)ts.upper_excl, (const int32_t*)ts.d_num_tiles, (const int32_t*)ts.d_num_cands, out.n_upper,
          out.n_lower, out.n_leaf, out.upper_origin, out.upper_key, out.upper_first, out.upper_mask, out.lower_origin,
-         out.lower_first, out.lower_mask, out.lower_prefix, out.leaf_origin, out.leaf_parent, leaf_cand);
+         out.lower_first, out.lower_mask, out.lower_prefix, out.leaf_origin, out.leaf_parent, leaf_cand, out.headers,
+         out.B);
 }
 
 // ------------------------------------------------------------------ leaf statistics
@@ -496,19 +509,24 @@ int32_t bbox_replicas(int32_t B) {
   return r < 1 ? 1 : (r > 64 ? 64 : r);
 }
 
-// Small batches (at most kFinSmallLeaves leaves and kFinSmallGrids grids): leaf
-// offsets, bboxes (folded in LDS) and headers in one workgroup. The leaf
-// producer left, per run of `gran` leaves, the run's voxel sum (at most 1024
-// runs here) and every leaf's voxels before it inside its run, so one block scan
-// of the run sums gives every run's offset; every grid's voxel begin is its
-// first leaf's run offset plus that leaf's in-run count. Leaves then go in tiles
-// of 16 waves x kFinPer x 64: wave w owns a contiguous run of kFinPer * 64
-// leaves, its lanes reading them 64 at a time (coalesced); each lane folds the
-// bbox of its leaves in registers (a run rarely holds more than one grid), and
-// the wave reduces once per tile.
-constexpr int kFinThreads = 1024;
+// Small batches (at most kFinSmallLeaves leaves, kFinSmallGrids grids and
+// kFinRuns runs): leaf offsets, bboxes and headers in one launch of
+// ceil(L / kFinSlice) workgroups. The leaf producer left, per run of `gran`
+// leaves, the run's voxel sum and every leaf's voxels before it inside its run.
+// Every workgroup scans the (at most kFinRuns) run sums itself, so each run's
+// offset is known without a second launch; a grid's voxel begin is its first
+// leaf's run offset plus that leaf's in-run count. Each workgroup then writes
+// the offsets of its kFinSlice leaves (wave w: a contiguous run of kFinPer * 64),
+// folds their boxes per grid in LDS, and then into the headers with one set of
+// atomics per grid it touched (the node writer has set every box to empty);
+// workgroup 0 writes the other header fields. Totals stay below 2^31 here (L * 512), so offsets
+// are computed in 32 bits. All global loads that do not depend on another are
+// issued first, at clamped indices.
+constexpr int kFinThreads = 256;
 constexpr int kFinPer = 8;
-constexpr i64 kFinSmallLeaves = 65536;  // with runs of >= 64 leaves: <= kFinThreads runs
+constexpr int kFinSlice = kFinThreads * kFinPer;  // leaves per workgroup
+constexpr int kFinRuns = 1024;
+constexpr i64 kFinSmallLeaves = 65536;
 constexpr int kFinSmallGrids = 1024;
 
 __device__ __forceinline__ void box_fold_lds(int32_t (*s_box)[kFinSmallGrids], int g, const int v[6]) {
@@ -520,57 +538,78 @@ __device__ __forceinline__ void box_fold_lds(int32_t (*s_box)[kFinSmallGrids], i
 
 __global__ void __launch_bounds__(kFinThreads) k_finalize_small(const int4* leaf_origin, const int32_t* leaf_inrun,
                                                                 const uint32_t* leaf_box, const i64* vox_part,
-                                                                i64 np, i64 gran, const int32_t* grid_info,
-                                                                i64* leaf_offset, int32_t B, i64 L,
+                                                                int32_t np, int32_t gs, const int32_t* grid_info,
+                                                                i64* leaf_offset, int32_t B, int32_t L,
                                                                 tc_grid_header* hdr) {
-  constexpr int kWaves = kFinThreads / kWave;
-  constexpr int kRun = kFinPer * kWave;  // leaves per wave per tile
+  constexpr int kR = kFinRuns / kFinThreads;
+  constexpr int kG = kFinSmallGrids / kFinThreads;
+  __shared__ int32_t s_part[kFinRuns];           // exclusive voxel offset of every run
+  __shared__ int32_t s_gvb[kFinSmallGrids + 1];  // voxel begin of every grid, then the total
+  __shared__ int32_t s_wave[kFinThreads / kWave];
   __shared__ int32_t s_box[6][kFinSmallGrids];
-  __shared__ i64 s_part[kFinThreads];        // exclusive voxel offset of every run
-  __shared__ i64 s_gvb[kFinSmallGrids + 1];  // voxel begin of every grid, then the total
-  __shared__ i64 s_wave[kWaves];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wv = tid / kWave;
-  const int gs = __builtin_ctzll((u64)gran);  // gran is a power of two
-  const i64 pv = tid < np ? vox_part[tid] : 0;
-  for (int g = tid; g < B; g += kFinThreads) {
-    for (int a = 0; a < 3; ++a) {
-      s_box[a][g] = INT32_MAX;
-      s_box[3 + a][g] = INT32_MIN;
-    }
-  }
-  i64 total;
-  const i64 pex = block_excl_scan<i64, kFinThreads>(pv, s_wave, total);
-  if (tid < np) s_part[tid] = pex;
-  __syncthreads();
-  for (int g = tid; g <= B; g += kFinThreads) {
-    const i64 f = g < B ? grid_info[g * 6 + 5] : L;
-    s_gvb[g] = f < L ? s_part[f >> gs] + leaf_inrun[f] : total;
-  }
-  __syncthreads();
-  for (i64 base = 0; base < L; base += (i64)kWaves * kRun) {
-    const i64 run0 = base + (i64)wv * kRun;
+  const int32_t base = (int32_t)blockIdx.x * kFinSlice + (tid / kWave) * (kFinPer * kWave);  // this wave's run
+  int32_t total = 0;
+  if (L > 0) {  // uniform; np >= 1
+    i64 pv[kR];
+    int32_t gf[kG];
     int4 o[kFinPer];
     uint32_t bx[kFinPer];
-    int32_t in_run[kFinPer];
-    // unconditional loads at clamped indices: all of them in flight at once
-    // (lanes past L are skipped below)
+    int32_t inr[kFinPer];
+#pragma unroll
+    for (int k = 0; k < kR; ++k) pv[k] = vox_part[min(tid * kR + k, np - 1)];
+#pragma unroll
+    for (int k = 0; k < kG; ++k) gf[k] = grid_info[(i64)min(tid * kG + k, B - 1) * 6 + 5];
 #pragma unroll
     for (int k = 0; k < kFinPer; ++k) {
-      const i64 i = min(run0 + k * kWave + lane, L - 1);
+      const int32_t i = min(base + k * kWave + lane, L - 1);
       o[k] = leaf_origin[i];
       bx[k] = leaf_box[i];
-      in_run[k] = leaf_inrun[i];
+      inr[k] = leaf_inrun[i];
     }
+    // run offsets
+    int32_t rv[kR];
+    int32_t sum = 0;
+#pragma unroll
+    for (int k = 0; k < kR; ++k) {
+      rv[k] = tid * kR + k < np ? (int32_t)pv[k] : 0;
+      sum += rv[k];
+    }
+    for (int g = tid; g < B; g += kFinThreads) {
+      for (int a = 0; a < 3; ++a) {
+        s_box[a][g] = INT32_MAX;
+        s_box[3 + a][g] = INT32_MIN;
+      }
+    }
+    int32_t ex = block_excl_scan<int32_t, kFinThreads>(sum, s_wave, total);
+#pragma unroll
+    for (int k = 0; k < kR; ++k) {
+      s_part[tid * kR + k] = ex;
+      ex += rv[k];
+    }
+    // first leaves' in-run counts (a grid without leaves points at the next
+    // grid's first leaf, or at L)
+    int32_t fi[kG];
+#pragma unroll
+    for (int k = 0; k < kG; ++k) fi[k] = leaf_inrun[min(gf[k], L - 1)];
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kG; ++k) {
+      const int g = tid * kG + k;
+      if (g < B) s_gvb[g] = gf[k] < L ? s_part[gf[k] >> gs] + fi[k] : total;
+    }
+    if (tid == 0) s_gvb[B] = total;
+    __syncthreads();
+    // leaf offsets and boxes: lane owns leaves base + k * 64 + lane
     int g = -1;
     int bv[6] = {INT32_MAX, INT32_MAX, INT32_MAX, INT32_MIN, INT32_MIN, INT32_MIN};
 #pragma unroll
     for (int k = 0; k < kFinPer; ++k) {
-      const i64 i = run0 + k * kWave + lane;
+      const int32_t i = base + k * kWave + lane;
       const int gk = o[k].w;
       if (i >= L || gk < 0 || gk >= B) continue;
-      leaf_offset[i] = s_part[i >> gs] + in_run[k] - s_gvb[gk];
+      leaf_offset[i] = (i64)(s_part[i >> gs] + inr[k] - s_gvb[gk]);
       if (bx[k] == kEmptyBox) continue;
       if (gk != g) {
         if (g >= 0) box_fold_lds(s_box, g, bv);
@@ -592,7 +631,7 @@ __global__ void __launch_bounds__(kFinThreads) k_finalize_small(const int4* leaf
     if (am) {  // uniform per wave
       const int first = __builtin_ctzll(am);
       const int g0 = __shfl(g, first, kWave);
-      if (__ballot(act && g != g0) == 0) {  // one grid left in every active lane
+      if (__ballot(act && g != g0) == 0) {  // one grid in every active lane: reduce, then one lane folds
         int r[6];
 #pragma unroll
         for (int a = 0; a < 3; ++a) {
@@ -604,28 +643,40 @@ __global__ void __launch_bounds__(kFinThreads) k_finalize_small(const int4* leaf
         box_fold_lds(s_box, g, bv);
       }
     }
+    __syncthreads();
+    for (int gg = tid; gg < B; gg += kFinThreads) {
+      if (s_box[0][gg] == INT32_MAX) continue;  // no voxel of grid gg in this slice
+      for (int a = 0; a < 3; ++a) {
+        atomicMin(&hdr[gg].bbox_min[a], s_box[a][gg]);
+        atomicMax(&hdr[gg].bbox_max[a], s_box[3 + a][gg]);
+      }
+    }
+  } else {
+    for (int g = tid; g <= B; g += kFinThreads) s_gvb[g] = 0;
+    __syncthreads();
   }
-  __syncthreads();
+  if (blockIdx.x != 0) return;
   for (int gg = tid; gg < B; gg += kFinThreads) {
     const int32_t* gi = grid_info + (i64)gg * 6;
-    tc_grid_header h;
-    h.grid_index = gg;
-    h.grid_count = B;
-    h.upper_count = gi[0];
-    h.lower_count = gi[1];
-    h.leaf_count = gi[2];
-    h.upper_begin = gi[3];
-    h.lower_begin = gi[4];
-    h.leaf_begin = gi[5];
-    h.voxel_begin = s_gvb[gg];
-    h.voxel_count = s_gvb[gg + 1] - s_gvb[gg];
-    for (int a = 0; a < 3; ++a) {
-      h.bbox_min[a] = s_box[a][gg];
-      h.bbox_max[a] = s_box[3 + a][gg];
+    tc_grid_header* h = hdr + gg;
+    h->grid_index = gg;
+    h->grid_count = B;
+    h->upper_count = gi[0];
+    h->lower_count = gi[1];
+    h->leaf_count = gi[2];
+    h->upper_begin = gi[3];
+    h->lower_begin = gi[4];
+    h->leaf_begin = gi[5];
+    h->voxel_begin = s_gvb[gg];
+    h->voxel_count = s_gvb[gg + 1] - s_gvb[gg];
+    if (L == 0) {  // no leaves: no node writer ran and no box was folded
+      for (int a = 0; a < 3; ++a) {
+        h->bbox_min[a] = INT32_MAX;
+        h->bbox_max[a] = INT32_MIN;
+      }
     }
-    h.reserved[0] = 0;
-    h.reserved[1] = 0;
-    hdr[gg] = h;
+    h->reserved[0] = 0;
+    h->reserved[1] = 0;
   }
 }
 
@@ -765,9 +816,10 @@ void tree_finalize_leaves(const GridView& out, const uint32_t* leaf_box, const i
   const i64 L = out.n_leaf;
   const int32_t B = out.B;
   if (gran <= 0 || (gran & (gran - 1)) != 0) throw Error(TC_ERR_INTERNAL, "finalize: run length not a power of two");
-  if (L <= kFinSmallLeaves && B <= kFinSmallGrids && ceil_div(L, gran) <= kFinThreads) {
-    launch("k_finalize_small", k_finalize_small, 1, kFinThreads, s, (const int4*)out.leaf_origin, leaf_inrun,
-           leaf_box, (const i64*)vox_part, ceil_div(L, gran), gran, grid_info, out.leaf_offset, B, L, out.headers);
+  if (L <= kFinSmallLeaves && B <= kFinSmallGrids && ceil_div(L, gran) <= kFinRuns) {
+    launch("k_finalize_small", k_finalize_small, std::max<i64>(1, ceil_div(L, kFinSlice)), kFinThreads, s,
+           (const int4*)out.leaf_origin, leaf_inrun, leaf_box, (const i64*)vox_part, (int32_t)ceil_div(L, gran),
+           (int32_t)__builtin_ctzll((u64)gran), grid_info, out.leaf_offset, B, (int32_t)L, out.headers);
     return;
   }
   const int32_t R = bbox_replicas(B);

@@ -261,56 +261,71 @@ __global__ void __launch_bounds__(256) k_node_reach(const u64* mask, i64 n_nodes
 // every axis with e != 0 has a voxel on that face, so the product of the per-axis
 // sets stays a superset of the true targets while dropping the neighbours that
 // the child-bit sets above add whenever a child merely sits on a face. One
-// workgroup per source upper: a wave per lower, lanes over its leaves; each lower
-// writes its set, the upper ORs the face bits of its lowers on the tile faces.
-// Face bits: 2a for the low face of axis a, 2a + 1 for the high face.
+// workgroup per source upper; its threads take the upper's leaves (contiguous,
+// two at a time in flight). A leaf's position in its lower and tile comes from
+// its origin alone; the lowers' face bits gather in LDS (an upper has at most
+// kBoxReachLowers lowers here). Face bits: 2a for the low face of axis a, 2a + 1
+// for the high face.
+constexpr int kBoxReachLowers = 512;
+
 __device__ __forceinline__ uint32_t faces_to_code(uint32_t f, int op, int m) {
   const uint32_t code = product27(axis_set(f & 1u, f & 2u), axis_set(f & 4u, f & 8u), axis_set(f & 16u, f & 32u));
   return box_code_for_op(code, op, m);
 }
 
-__global__ void __launch_bounds__(256) k_box_reach(const int4* upper_origin, const int32_t* upper_first,
-                                                   int32_t n_upper, const int4* lower_origin,
+// Faces of the node (side `side` = 8 << level voxels, origins aligned to it)
+// that leaf origin o with mask words w touches.
+__device__ __forceinline__ uint32_t leaf_faces(const int4 o, const u64 w[8], int side) {
+  const u64 all = w[0] | w[1] | w[2] | w[3] | w[4] | w[5] | w[6] | w[7];
+  const int m = side - 1, far = side - 8;
+  const int px = o.x & m, py = o.y & m, pz = o.z & m;
+  uint32_t f = 0;
+  if (px == 0 && w[0]) f |= 1u;
+  if (px == far && w[7]) f |= 2u;
+  if (py == 0 && (all & 0xffull)) f |= 4u;
+  if (py == far && (all & 0xff00000000000000ull)) f |= 8u;
+  if (pz == 0 && (all & kZ0)) f |= 16u;
+  if (pz == far && (all & kZ7)) f |= 32u;
+  return f;
+}
+
+__global__ void __launch_bounds__(256) k_box_reach(const int32_t* upper_first, int32_t n_upper,
                                                    const int32_t* lower_first, int32_t n_lower,
-                                                   const int4* leaf_origin, const u64* leaf_mask, int32_t n_leaf,
-                                                   int op, int m, uint32_t* upper_reach, uint32_t* lower_reach) {
+                                                   const int4* leaf_origin, const int32_t* leaf_parent,
+                                                   const u64* leaf_mask, int32_t n_leaf, int op, int m,
+                                                   uint32_t* upper_reach, uint32_t* lower_reach) {
+  __shared__ uint32_t s_lface[kBoxReachLowers];
   __shared__ uint32_t s_face;
   const int u = blockIdx.x;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wv = threadIdx.x / kWave;
-  if (threadIdx.x == 0) s_face = 0;
-  __syncthreads();
-  const int4 uo = upper_origin[u];
   const int32_t l0 = upper_first[u], l1 = u + 1 < n_upper ? upper_first[u + 1] : n_lower;
-  for (int32_t l = l0 + wv; l < l1; l += 4) {
-    const int4 lo = lower_origin[l];
-    const int32_t f0 = lower_first[l], f1 = l + 1 < n_lower ? lower_first[l + 1] : n_leaf;
-    uint32_t face = 0;
-    for (int32_t f = f0 + lane; f < f1; f += kWave) {
-      const int4 o = leaf_origin[f];
-      const int px = (o.x - lo.x) >> 3, py = (o.y - lo.y) >> 3, pz = (o.z - lo.z) >> 3;  // 0..15 in the lower
-      u64 w[8];
+  for (int k = threadIdx.x; k < l1 - l0; k += 256) s_lface[k] = 0;
+  if (threadIdx.x == 0) s_face = 0;
+  const int32_t f0 = lower_first[l0], f1 = l1 < n_lower ? lower_first[l1] : n_leaf;
+  __syncthreads();
+  for (int32_t f = f0 + threadIdx.x; f < f1; f += 2 * 256) {
+    int4 o[2];
+    int32_t lp[2];
+    u64 w[2][8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) w[k] = leaf_mask[(i64)f * 8 + k];
-      const u64 all = w[0] | w[1] | w[2] | w[3] | w[4] | w[5] | w[6] | w[7];
-      if (px == 0 && w[0]) face |= 1u;
-      if (px == 15 && w[7]) face |= 2u;
-      if (py == 0 && (all & 0xffull)) face |= 4u;
-      if (py == 15 && (all & 0xff00000000000000ull)) face |= 8u;
-      if (pz == 0 && (all & kZ0)) face |= 16u;
-      if (pz == 15 && (all & kZ7)) face |= 32u;
+    for (int q = 0; q < 2; ++q) {
+      const int32_t fq = min(f + q * 256, f1 - 1);
+      o[q] = leaf_origin[fq];
+      lp[q] = leaf_parent[fq];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) w[q][k] = leaf_mask[(i64)fq * 8 + k];
     }
 #pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) face |= (uint32_t)__shfl_xor((int)face, d, kWave);
-    if (lane == 0) {
-      lower_reach[l] = faces_to_code(face, op, m);
-      const int qx = (lo.x - uo.x) >> 7, qy = (lo.y - uo.y) >> 7, qz = (lo.z - uo.z) >> 7;  // 0..31 in the tile
-      const uint32_t tile_face = (face & ((qx == 0 ? 1u : 0u) | (qx == 31 ? 2u : 0u) | (qy == 0 ? 4u : 0u) |
-                                          (qy == 31 ? 8u : 0u) | (qz == 0 ? 16u : 0u) | (qz == 31 ? 32u : 0u)));
-      if (tile_face) atomicOr(&s_face, tile_face);
+    for (int q = 0; q < 2; ++q) {
+      if (f + q * 256 >= f1) continue;
+      const uint32_t lf = leaf_faces(o[q], w[q], 128);
+      const uint32_t tf = leaf_faces(o[q], w[q], 4096);
+      const int32_t li = lp[q] - l0;
+      if (lf && li >= 0 && li < l1 - l0) atomicOr(&s_lface[li], lf);
+      if (tf) atomicOr(&s_face, tf);
     }
   }
   __syncthreads();
+  for (int k = threadIdx.x; k < l1 - l0; k += 256) lower_reach[l0 + k] = faces_to_code(s_lface[k], op, m);
   if (threadIdx.x == 0) upper_reach[u] = faces_to_code(s_face, op, m);
 }
 
@@ -1121,28 +1136,35 @@ __global__ void __launch_bounds__(256) k_leaf_mark_box(const int32_t* cand_src, 
     int32_t base[kPullPer];
     int cnt[kPullPer];
     int sum = 0;
+    // every load at a valid index, all in flight together: the source slots,
+    // then the slots' mask words, first leaves and prefixes (slot 0 stands in
+    // for an empty slot; n_src_lower >= 1 whenever there are candidates)
+    int32_t sl[kPullPer];
+#pragma unroll
+    for (int k = 0; k < kPullPer; ++k) sl[k] = cand_src[c * 27 + (min(tid * kPullPer + k, kPullItems - 1) >> 6)];
+    u64 fm[kPullPer];
+    int32_t lfirst[kPullPer];
+    uint16_t lpre[kPullPer];
 #pragma unroll
     for (int k = 0; k < kPullPer; ++k) {
       const int item = tid * kPullPer + k;
-      wd[k] = 0;
-      base[k] = 0;
-      cnt[k] = 0;
-      if (item < kPullItems) {
-        const int js = item >> 6, w = item & 63;
-        const u64 fm = face_word_mask(js, w, lo, hi);
-        if (fm) {
-          int32_t sl = cand_src[c * 27 + js];
-          if (sl >= n_src_lower) {
-            set_flag(flags, kFlagInternal);
-            sl = -1;
-          }
-          if (sl >= 0) {
-            wd[k] = src_lower_mask[(i64)sl * 64 + w];
-            base[k] = src_lower_first[sl] + src_lower_prefix[(i64)sl * 64 + w];
-            cnt[k] = popc64(wd[k] & fm);
-          }
-        }
+      const int js = item >> 6, w = item & 63;
+      fm[k] = item < kPullItems ? face_word_mask(js, w, lo, hi) : 0;
+      if (sl[k] >= n_src_lower) {
+        set_flag(flags, kFlagInternal);
+        sl[k] = -1;
       }
+      if (!fm[k]) sl[k] = -1;
+      const i64 ls = sl[k] >= 0 ? sl[k] : 0;
+      wd[k] = src_lower_mask[ls * 64 + w];
+      lfirst[k] = src_lower_first[ls];
+      lpre[k] = src_lower_prefix[ls * 64 + w];
+    }
+#pragma unroll
+    for (int k = 0; k < kPullPer; ++k) {
+      if (sl[k] < 0) wd[k] = 0;
+      base[k] = sl[k] >= 0 ? lfirst[k] + lpre[k] : 0;
+      cnt[k] = popc64(wd[k] & fm[k]);
       sum += cnt[k];
     }
     int total;
@@ -1187,11 +1209,11 @@ __global__ void __launch_bounds__(256) k_leaf_mark_box(const int32_t* cand_src, 
           }
         }
       }
-      u64 W[kMarkIlp][8];
+      u64 W[kMarkIlp][8];  // leaf 0 stands in for an empty item (its marks are skipped)
 #pragma unroll
       for (int u = 0; u < kMarkIlp; ++u)
 #pragma unroll
-        for (int q = 0; q < 8; ++q) W[u][q] = lf[u] >= 0 ? src_leaf_mask[(i64)lf[u] * 8 + q] : 0;
+        for (int q = 0; q < 8; ++q) W[u][q] = src_leaf_mask[(i64)(lf[u] >= 0 ? lf[u] : 0) * 8 + q];
 #pragma unroll
       for (int u = 0; u < kMarkIlp; ++u)
         if (lf[u] >= 0) mark_box_leaf(W[u], ps[u], lo, hi, s_mask);
@@ -1363,8 +1385,9 @@ __global__ void __launch_bounds__(256) k_leaf_gather(const int4* out_origin, con
 // y and z passes never mix words, and the x pass needs just one more word on
 // each side (from the x-neighbour leaf at the ends). The source lookups are
 // split over the four lanes and their results exchanged with shuffles.
+template <int lo, int hi>  // the box [lo, hi]^3: dilate [-1, 1], pads [-1, 0] and [0, 1]
 __global__ void __launch_bounds__(256) k_leaf_gather_box(const int4* out_origin, const int32_t* leaf_cand, i64 n,
-                                                         int lo, int hi, const int32_t* cand_src,
+                                                         const int32_t* cand_src,
                                                          const u64* src_lower_mask, const uint16_t* src_lower_prefix,
                                                          const int32_t* src_lower_first, const u64* src_leaf_mask,
                                                          int32_t n_src_lower, int32_t n_src_leaf,
@@ -1375,49 +1398,59 @@ __global__ void __launch_bounds__(256) k_leaf_gather_box(const int4* out_origin,
   const i64 i = gt >> 2;
   const int sub = (int)(gt & 3);
   const int grp = (int)(threadIdx.x & (kWave - 1)) & ~3;
+  // Every load goes to a valid index (n, the candidates, the source lowers and
+  // leaves are all non-empty here; index 0 stands in for a missing one) and is
+  // masked afterwards, so each level's loads are in flight together.
+  const i64 ncand = *d_num_cands;
+  const i64 ic = i < n ? i : n - 1;
+  const int4 o = out_origin[ic];
+  i64 c = leaf_cand[ic];
   bool valid = i < n;
-  i64 c = -1;
-  int4 o = make_int4(0, 0, 0, 0);
-  if (valid) {
-    o = out_origin[i];
-    c = leaf_cand[i];
-    if (c < 0 || c >= *d_num_cands) {
-      set_flag(flags, kFlagInternal);
-      valid = false;
-    }
+  if (valid && (c < 0 || c >= ncand)) {
+    set_flag(flags, kFlagInternal);
+    valid = false;
   }
+  if (!valid) c = 0;
   const int lx = (o.x >> 3) & 15, ly = (o.y >> 3) & 15, lz = (o.z >> 3) & 15;
   // source leaf at leaf offset s = (j/9-1, (j/3)%3-1, j%3-1), s in [-hi, -lo]^3;
   // this lane resolves j = sub + 4q, level by level so the loads overlap
   constexpr int kPer = 7;
   int32_t sl[kPer], bit[kPer];
+  bool use[kPer];
 #pragma unroll
   for (int q = 0; q < kPer; ++q) {
     const int j = sub + 4 * q;
-    sl[q] = -1;
-    bit[q] = 0;
     const int sx = j / 9 - 1, sy = (j / 3) % 3 - 1, sz = j % 3 - 1;
-    if (valid && j < 27 && sx >= -hi && sx <= -lo && sy >= -hi && sy <= -lo && sz >= -hi && sz <= -lo) {
-      const int px = lx + sx, py = ly + sy, pz = lz + sz;  // -1 .. 16
-      sl[q] = cand_src[c * 27 + index27(px >> 4, py >> 4, pz >> 4)];
-      bit[q] = ((px & 15) * 16 + (py & 15)) * 16 + (pz & 15);
-      if (sl[q] >= n_src_lower) {
-        set_flag(flags, kFlagInternal);
-        sl[q] = -1;
-      }
+    use[q] = valid && j < 27 && sx >= -hi && sx <= -lo && sy >= -hi && sy <= -lo && sz >= -hi && sz <= -lo;
+    const int px = lx + sx, py = ly + sy, pz = lz + sz;  // -1 .. 16 (j < 27)
+    bit[q] = use[q] ? ((px & 15) * 16 + (py & 15)) * 16 + (pz & 15) : 0;
+    sl[q] = cand_src[c * 27 + (use[q] ? index27(px >> 4, py >> 4, pz >> 4) : 13)];
+  }
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    if (use[q] && sl[q] >= n_src_lower) {
+      set_flag(flags, kFlagInternal);
+      sl[q] = -1;
     }
+    if (!use[q]) sl[q] = -1;
   }
   u64 word[kPer];
+  int32_t lfirst[kPer];
+  uint16_t lpre[kPer];
 #pragma unroll
-  for (int q = 0; q < kPer; ++q) word[q] = sl[q] >= 0 ? src_lower_mask[(i64)sl[q] * 64 + (bit[q] >> 6)] : 0;
+  for (int q = 0; q < kPer; ++q) {
+    const i64 ls = sl[q] >= 0 ? sl[q] : 0;
+    word[q] = src_lower_mask[ls * 64 + (bit[q] >> 6)];
+    lfirst[q] = src_lower_first[ls];
+    lpre[q] = src_lower_prefix[ls * 64 + (bit[q] >> 6)];
+  }
   int32_t r[kPer];
 #pragma unroll
   for (int q = 0; q < kPer; ++q) {
     r[q] = -1;
     const int b = bit[q] & 63;
-    if ((word[q] >> b) & 1ull) {
-      r[q] = src_lower_first[sl[q]] + src_lower_prefix[(i64)sl[q] * 64 + (bit[q] >> 6)] +
-             popc64(word[q] & ((1ull << b) - 1));
+    if (sl[q] >= 0 && ((word[q] >> b) & 1ull)) {
+      r[q] = lfirst[q] + lpre[q] + popc64(word[q] & ((1ull << b) - 1));
       if (r[q] < 0 || r[q] >= n_src_leaf) {
         set_flag(flags, kFlagInternal);
         r[q] = -1;
@@ -1425,6 +1458,46 @@ __global__ void __launch_bounds__(256) k_leaf_gather_box(const int4* out_origin,
     }
   }
   const int x0 = 2 * sub;
+  // words x0-1 .. x0+2 of every needed row (sy, sz) of source leaves, all loads
+  // first (leaf 0 stands in for a missing leaf, whose words are then cleared)
+  int32_t R[3][3][3];  // [sz][sy][sx] source leaf index, gathered from the lanes that resolved it
+#pragma unroll
+  for (int sz = -1; sz <= 1; ++sz)
+#pragma unroll
+    for (int sy = -1; sy <= 1; ++sy)
+#pragma unroll
+      for (int sx = -1; sx <= 1; ++sx) {
+        const int j = (sx + 1) * 9 + (sy + 1) * 3 + (sz + 1);
+        R[sz + 1][sy + 1][sx + 1] =
+            (sz < -hi || sz > -lo || sy < -hi || sy > -lo) ? -1 : __shfl(r[j >> 2], grp | (j & 3), kWave);
+      }
+  u64 w[3][3][4];
+#pragma unroll
+  for (int sz = -1; sz <= 1; ++sz) {
+#pragma unroll
+    for (int sy = -1; sy <= 1; ++sy) {
+      if (sz < -hi || sz > -lo || sy < -hi || sy > -lo) continue;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int x = x0 - 1 + k;
+        const int32_t rr = x < 0 ? R[sz + 1][sy + 1][0] : (x > 7 ? R[sz + 1][sy + 1][2] : R[sz + 1][sy + 1][1]);
+        w[sz + 1][sy + 1][k] = src_leaf_mask[(i64)(rr >= 0 ? rr : 0) * 8 + (x & 7)];
+      }
+    }
+  }
+#pragma unroll
+  for (int sz = -1; sz <= 1; ++sz) {
+#pragma unroll
+    for (int sy = -1; sy <= 1; ++sy) {
+      if (sz < -hi || sz > -lo || sy < -hi || sy > -lo) continue;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int x = x0 - 1 + k;
+        const int32_t rr = x < 0 ? R[sz + 1][sy + 1][0] : (x > 7 ? R[sz + 1][sy + 1][2] : R[sz + 1][sy + 1][1]);
+        if (rr < 0) w[sz + 1][sy + 1][k] = 0;
+      }
+    }
+  }
   u64 ys[3][2];
 #pragma unroll
   for (int sz = -1; sz <= 1; ++sz) {
@@ -1432,21 +1505,9 @@ __global__ void __launch_bounds__(256) k_leaf_gather_box(const int4* out_origin,
 #pragma unroll
     for (int sy = -1; sy <= 1; ++sy) {
       if (sz < -hi || sz > -lo || sy < -hi || sy > -lo) continue;
-      int32_t R[3];
-#pragma unroll
-      for (int sx = -1; sx <= 1; ++sx) {
-        const int j = (sx + 1) * 9 + (sy + 1) * 3 + (sz + 1);
-        R[sx + 1] = __shfl(r[j >> 2], grp | (j & 3), kWave);
-      }
-      u64 w[4];  // words x0-1 .. x0+2 of this row of leaves
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int x = x0 - 1 + k;
-        const int32_t rr = x < 0 ? R[0] : (x > 7 ? R[2] : R[1]);
-        w[k] = rr >= 0 ? src_leaf_mask[(i64)rr * 8 + (x & 7)] : 0;
-      }
-      xs[sy + 1][0] = w[1] | (hi > 0 ? w[0] : 0) | (lo < 0 ? w[2] : 0);
-      xs[sy + 1][1] = w[2] | (hi > 0 ? w[1] : 0) | (lo < 0 ? w[3] : 0);
+      const u64* wr = w[sz + 1][sy + 1];
+      xs[sy + 1][0] = wr[1] | (hi > 0 ? wr[0] : 0) | (lo < 0 ? wr[2] : 0);
+      xs[sy + 1][1] = wr[2] | (hi > 0 ? wr[1] : 0) | (lo < 0 ? wr[3] : 0);
     }
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
@@ -1611,9 +1672,10 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, 
   uint32_t* box_lreach = nullptr;
   if (small_lowers && box_op) {
     box_lreach = a.at<uint32_t>(o_lreach);
-    launch("k_box_reach", k_box_reach, src->n2, 256, s, (const int4*)sv.upper_origin, (const int32_t*)sv.upper_first,
-           (int32_t)src->n2, (const int4*)sv.lower_origin, (const int32_t*)sv.lower_first, (int32_t)src->n1,
-           (const int4*)sv.leaf_origin, (const u64*)sv.leaf_mask, (int32_t)src->nl, op, oi.m,
+    if (src->n1 > kBoxReachLowers) throw Error(TC_ERR_INTERNAL, "pass: too many lowers for the box reach stage");
+    launch("k_box_reach", k_box_reach, src->n2, 256, s, (const int32_t*)sv.upper_first, (int32_t)src->n2,
+           (const int32_t*)sv.lower_first, (int32_t)src->n1, (const int4*)sv.leaf_origin,
+           (const int32_t*)sv.leaf_parent, (const u64*)sv.leaf_mask, (int32_t)src->nl, op, oi.m,
            a.at<uint32_t>(o_ureach), box_lreach);
   }
   if (small_tiles) {
@@ -1729,8 +1791,10 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, 
              (const u64*)sv.leaf_mask, sv.n_lower, sv.n_leaf, (const int32_t*)ts.d_num_cands, ov.leaf_mask,
              ov.leaf_prefix, post.at<uint32_t>(o_box), leaf_inrun, vox_part, ts.flags);
     } else {
-      launch("k_leaf_gather", k_leaf_gather_box, ceil_div(L * 4, 256), 256, s, (const int4*)ov.leaf_origin,
-             (const int32_t*)leaf_cand, L, oi.lo, oi.hi, (const int32_t*)cand_src, (const u64*)sv.lower_mask,
+      auto gather_box = oi.lo < 0 && oi.hi > 0 ? k_leaf_gather_box<-1, 1>
+                        : (oi.lo < 0 ? k_leaf_gather_box<-1, 0> : k_leaf_gather_box<0, 1>);
+      launch("k_leaf_gather", gather_box, ceil_div(L * 4, 256), 256, s, (const int4*)ov.leaf_origin,
+             (const int32_t*)leaf_cand, L, (const int32_t*)cand_src, (const u64*)sv.lower_mask,
              (const uint16_t*)sv.lower_prefix, (const int32_t*)sv.lower_first, (const u64*)sv.leaf_mask,
              sv.n_lower, sv.n_leaf, (const int32_t*)ts.d_num_cands, ov.leaf_mask, ov.leaf_prefix,
              post.at<uint32_t>(o_box), leaf_inrun, vox_part, ts.flags);

@@ -367,7 +367,7 @@ __global__ void __launch_bounds__(256) k_write_nodes(
     const int32_t* d_num_cands, int32_t n_upper, int32_t n_lower, int32_t n_leaf, int4* upper_origin,
     u64* upper_key, int32_t* upper_first, u64* upper_mask, int4* lower_origin, int32_t* lower_first,
     u64* lower_mask, uint16_t* lower_prefix, int4* leaf_origin, int32_t* leaf_parent, int32_t* leaf_cand,
-    tc_grid_header* hdr, int32_t B) {
+    tc_grid_header* hdr, int32_t B, i64 cap_cands) {
   if (blockIdx.x == 0) {  // every grid's box starts empty; the leaf finalizer folds into it
     for (int32_t g = threadIdx.x; g < B; g += 256) {
       for (int a = 0; a < 3; ++a) {
@@ -377,15 +377,25 @@ __global__ void __launch_bounds__(256) k_write_nodes(
     }
   }
   if ((int32_t)blockIdx.x < tile_blocks) {
+    // every load indexed by the tile alone first (t < the tile capacity), then
+    // the two scan entries they select
     const i64 t = blockIdx.x;
-    if (t >= *d_num_tiles) return;
+    const int32_t nt = *d_num_tiles;
     const int32_t cb = tile_lower_base[t], ce = tile_lower_base[t + 1];
+    const i64 u = upper_excl[t];
+    const int4 T = utile[t];
+    u64 words[2];
+    uint16_t pres[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      words[k] = tile_child[t * 512 + threadIdx.x * 2 + k];
+      pres[k] = tile_prefix[t * 512 + threadIdx.x * 2 + k];
+    }
+    if (t >= nt) return;
     const i64 vb = cand_scan[cb];
     if (scan_leaf(cand_scan[ce]) == scan_leaf(vb)) return;  // empty tile, uniform per block
-    const i64 u = upper_excl[t];
     if (u < 0 || u >= n_upper) return;  // cannot happen for consistent counts
     if (threadIdx.x == 0) {
-      const int4 T = utile[t];
       upper_origin[u] = make_int4(T.x * 4096, T.y * 4096, T.z * 4096, T.w);
       upper_key[u] = ((u64)(T.x + kTileBias) << 40) | ((u64)(T.y + kTileBias) << 20) | (u64)(T.z + kTileBias);
       upper_first[u] = scan_lower(vb);
@@ -393,9 +403,9 @@ __global__ void __launch_bounds__(256) k_write_nodes(
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int w = threadIdx.x * 2 + k;
-      u64 word = tile_child[t * 512 + w];
+      u64 word = words[k];
       u64 out = 0;
-      int32_t c = cb + tile_prefix[t * 512 + w];
+      int32_t c = cb + pres[k];
       while (word) {
         const int b = __builtin_ctzll(word);
         if ((int32_t)cand_counts[c] > 0) out |= 1ull << b;
@@ -406,19 +416,23 @@ __global__ void __launch_bounds__(256) k_write_nodes(
     }
     return;
   }
+  // every load indexed by the candidate alone first (clamped to the capacity),
+  // then the two that its origin selects
   const i64 c = ((i64)blockIdx.x - tile_blocks) * 4 + threadIdx.x / kWave;
   const int lane = threadIdx.x & (kWave - 1);
-  if (c >= *d_num_cands) return;
-  const int32_t cnt = (int32_t)cand_counts[c];
+  const i64 cc = c < cap_cands ? c : cap_cands - 1;
+  const int32_t ncand = *d_num_cands;
+  const int32_t cnt = (int32_t)cand_counts[cc];
+  const i64 v = cand_scan[cc];
+  const int4 co = cand_origin[cc];
+  const u64 word = cand_child[cc * 64 + lane];
+  const uint16_t pre = cand_prefix[cc * 64 + lane];
+  if (c >= ncand) return;
   if (cnt == 0) return;  // uniform per wave
-  const i64 v = cand_scan[c];
   const i64 lo = scan_lower(v);
   const int32_t lb = scan_leaf(v);
   if (lo < 0 || lo >= n_lower || lb < 0 || (i64)lb + cnt > n_leaf) return;  // consistency guard
-  const int4 co = cand_origin[c];
   const int32_t g = utile[co.w].w;
-  const u64 word = cand_child[c * 64 + lane];
-  const uint16_t pre = cand_prefix[c * 64 + lane];
   lower_mask[lo * 64 + lane] = word;
   lower_prefix[lo * 64 + lane] = pre;
   if (lane == 0) {
@@ -458,7 +472,7 @@ void tree_write_nodes(TreeScratch& ts, const GridView& out, int32_t* leaf_cand, 
          (const int32_t*)ts.upper_excl, (const int32_t*)ts.d_num_tiles, (const int32_t*)ts.d_num_cands, out.n_upper,
          out.n_lower, out.n_leaf, out.upper_origin, out.upper_key, out.upper_first, out.upper_mask, out.lower_origin,
          out.lower_first, out.lower_mask, out.lower_prefix, out.leaf_origin, out.leaf_parent, leaf_cand, out.headers,
-         out.B);
+         out.B, ts.cap_cands);
 }
 
 // ------------------------------------------------------------------ leaf statistics

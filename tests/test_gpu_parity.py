@@ -146,6 +146,47 @@ def test_octant_corners_of_root_tile():
         _check(op, f, ijk, off, "corners")
 
 
+def _face_members():
+    """One member per placement of a voxel on (or one voxel inside) a face, edge or
+    corner of its lower node (128 voxels) and of its root tile (4096 voxels), on
+    both sides of 0 and of +-4096, each with a voxel in the node's middle too."""
+    members = []
+    bases = [(0, 0, 0), (128 * 5, 0, 256), (4096, -4096, 0), (-128, -4096 * 2, 4096 * 3)]
+    for bx, by, bz in bases:
+        for side in (0, 127, 1, 126):
+            for axes in ((0,), (1,), (2,), (0, 1), (1, 2), (0, 2), (0, 1, 2)):
+                v = [64, 64, 64]
+                for a in axes:
+                    v[a] = side
+                members.append(np.array([[bx + v[0], by + v[1], bz + v[2]], [bx + 64, by + 64, bz + 64]], np.int32))
+    for t in (0, 4095, 1, 4094):  # root-tile faces: the lower at the tile's end
+        for axes in ((0,), (1,), (2,), (0, 1, 2)):
+            v = [2048, 2048, 2048]
+            for a in axes:
+                v[a] = t
+            members.append(np.array([v, [2048, 2048, 2048]], np.int32))
+            members.append(np.array(v, np.int32)[None, :] - 4096)
+    # batches of 24 members keep every batch on the one-workgroup path (at most
+    # 75 source lowers for a box op), where the face test is made
+    return [synth.concat_members(members[i:i + 24]) for i in range(0, len(members), 24)]
+
+
+@pytest.mark.parametrize("op,f", [("dilate", 1), ("pad_neg", 1), ("pad_pos", 1), ("conv_t_k3s2", 2)])
+def test_box_ops_voxels_on_node_faces(op, f):
+    """Box ops prune neighbour tiles and lowers by which faces hold a voxel: a
+    voxel on a face, edge or corner must still reach every neighbour, one voxel
+    inside must reach none (PR page, section 2: box-dilate and pads)."""
+    for n, (ijk, off) in enumerate(_face_members()):
+        _check(op, f, ijk, off, f"faces batch {n}")
+
+
+@pytest.mark.parametrize("op", ["conv_s1", "conv_t_s1"])
+@pytest.mark.parametrize("k", [2, 4, 5])
+def test_kernel_k_voxels_on_node_faces(op, k):
+    for n, (ijk, off) in enumerate(_face_members()):
+        _check(op, k, ijk, off, f"faces batch {n}")
+
+
 def test_empty_members_everywhere():
     ijk, off = synth.make_config(1)
     a, b = ijk[off[0]:off[1]], ijk[off[1]:off[2]]

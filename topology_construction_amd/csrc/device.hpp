@@ -63,6 +63,17 @@ __device__ __forceinline__ int32_t block_run_scan(int32_t v, int64_t* total_dst)
   return off + inc - v;
 }
 
+// Workgroups are dispatched round-robin over the chip's 8 XCDs (workgroup b on
+// XCD b % 8), and each XCD has its own L2. Logical block of dispatched block b
+// out of nb: XCD x takes the contiguous range of about nb / 8 logical blocks
+// starting at x * (nb / 8) + min(x, nb % 8), so neighbouring work items, which
+// read the same source data, share one L2. A bijection on [0, nb).
+__device__ __forceinline__ int64_t xcd_block(int64_t b, int64_t nb) {
+  constexpr int64_t kXcds = 8;
+  const int64_t q = nb / kXcds, r = nb % kXcds, x = b % kXcds;
+  return x * q + (x < r ? x : r) + b / kXcds;
+}
+
 // Index of the r-th set bit (0-based) of w; w must have more than r set bits.
 __device__ __forceinline__ int select_bit(uint64_t w, int r) {
   int pos = 0;

@@ -1130,7 +1130,13 @@ __global__ void __launch_bounds__(256) k_leaf_mark_box(const int32_t* cand_src, 
     }
   }
   const i64 ncand = *d_num_cands;
-  for (i64 c = blockIdx.x; c < ncand; c += gridDim.x) {
+  // the first na workgroups (still spread round-robin over the XCDs) each take a
+  // contiguous share of the candidates, the shares of one XCD adjacent:
+  // neighbouring candidates read the same source lowers and leaves
+  const i64 na = ncand < (i64)gridDim.x ? ncand : (i64)gridDim.x;
+  const i64 per = na > 0 ? (ncand + na - 1) / na : 0;
+  const i64 c0 = (i64)blockIdx.x < na ? xcd_block(blockIdx.x, na) * per : ncand;
+  for (i64 c = c0; c < ncand && c < c0 + per; ++c) {
     if (tid < 64) s_mask[tid] = 0;
     u64 wd[kPullPer];
     int32_t base[kPullPer];
@@ -1301,7 +1307,8 @@ __global__ void __launch_bounds__(256) k_leaf_gather(const int4* out_origin, con
                                                      uint32_t* leaf_box, int32_t* leaf_inrun,
                                                      i64* vox_part, int32_t* flags) {
   constexpr int lpl = KIND == 0 ? 1 : 4;  // lanes per output leaf
-  const i64 gt = (i64)blockIdx.x * 256 + threadIdx.x;
+  const i64 lblk = blockIdx.x;
+  const i64 gt = lblk * 256 + threadIdx.x;
   const i64 i = gt / lpl;
   const int sub = (int)(gt % lpl);
   bool valid = i < n;
@@ -1368,7 +1375,7 @@ __global__ void __launch_bounds__(256) k_leaf_gather(const int4* out_origin, con
     out_prefix[i] = prefix;
   }
   // voxels before this leaf within the block's leaves, and the block's total
-  const int32_t inrun = block_run_scan(count, &vox_part[blockIdx.x]);
+  const int32_t inrun = block_run_scan(count, &vox_part[lblk]);
   if (writer) {
     leaf_box[i] = box;
     leaf_inrun[i] = inrun;
@@ -1394,7 +1401,8 @@ __global__ void __launch_bounds__(256) k_leaf_gather_box(const int4* out_origin,
                                                          const int32_t* d_num_cands, u64* out_mask, u64* out_prefix,
                                                          uint32_t* leaf_box, int32_t* leaf_inrun,
                                                          i64* vox_part, int32_t* flags) {
-  const i64 gt = (i64)blockIdx.x * 256 + threadIdx.x;
+  const i64 lblk = xcd_block(blockIdx.x, gridDim.x);  // contiguous leaves per XCD (shared source leaves)
+  const i64 gt = lblk * 256 + threadIdx.x;
   const i64 i = gt >> 2;
   const int sub = (int)(gt & 3);
   const int grp = (int)(threadIdx.x & (kWave - 1)) & ~3;
@@ -1542,7 +1550,7 @@ __global__ void __launch_bounds__(256) k_leaf_gather_box(const int4* out_origin,
     }
   }
   // voxels before this leaf within the block's leaves, and the block's total
-  const int32_t inrun = block_run_scan(count, &vox_part[blockIdx.x]);
+  const int32_t inrun = block_run_scan(count, &vox_part[lblk]);
   if (i < n && sub == 0) {
     leaf_box[i] = box;
     leaf_inrun[i] = inrun;

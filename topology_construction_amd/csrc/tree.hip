@@ -712,8 +712,10 @@ __global__ void __launch_bounds__(kPartThreads) k_vox_partials(i64* vox_part, i6
     i64 sum = 0;
     const i64 base = c + (i64)threadIdx.x * kPartItems;
 #pragma unroll
+    for (int k = 0; k < kPartItems; ++k) v[k] = vox_part[min(base + k, np - 1)];  // clamped: all in flight
+#pragma unroll
     for (int k = 0; k < kPartItems; ++k) {
-      v[k] = base + k < np ? vox_part[base + k] : 0;
+      if (base + k >= np) v[k] = 0;
       sum += v[k];
     }
     i64 total;

@@ -1056,10 +1056,9 @@ __global__ void __launch_bounds__(256) k_leaf_mark_lower(const int4* leaf_origin
 // binary search over the scan), tests which offsets of the box spill voxels
 // into C and ORs the target bits into an LDS copy of C's 16^3 leaf mask, which
 // is stored whole at the end: no device atomics on the masks and no zero fill.
-constexpr int kPullItems = 27 * 64;                 // (source slot, mask word) pairs
-constexpr int kPullPer = (kPullItems + 255) / 256;  // per thread
+constexpr int kPullItems = 27 * 64;  // (source slot, mask word) pairs
 
-__device__ __forceinline__ u64 face_word_mask(int js, int w, int lo, int hi) {
+__host__ __device__ constexpr u64 face_word_mask(int js, int w, int lo, int hi) {
   const int dx = js / 9 - 1, dy = (js / 3) % 3 - 1, dz = js % 3 - 1;
   if ((dx != 0 && (-dx < lo || -dx > hi)) || (dy != 0 && (-dy < lo || -dy > hi)) ||
       (dz != 0 && (-dz < lo || -dz > hi)))
@@ -1072,6 +1071,33 @@ __device__ __forceinline__ u64 face_word_mask(int js, int w, int lo, int hi) {
   if (dz < 0) m &= 0x8000800080008000ull;               // z = 15
   else if (dz > 0) m &= 0x0001000100010001ull;          // z = 0
   return m;
+}
+
+// The live items of a box: the (slot, word) pairs whose word can hold a leaf
+// facing the candidate (the whole centre lower, the boundary words or bits of
+// the faces, fewer for edges and corners): 324 for [-1,1]^3, 170 for either pad,
+// against 27 * 64. Built at compile time, slot-major.
+constexpr int kLiveMax = 384;
+constexpr int kLivePer = (kLiveMax + 255) / 256;  // per thread
+struct PullTable {
+  int n;
+  uint16_t item[kLiveMax];  // js * 64 + w
+};
+constexpr PullTable make_pull_table(int lo, int hi) {
+  PullTable t{};
+  for (int it = 0; it < kPullItems; ++it)
+    if (face_word_mask(it >> 6, it & 63, lo, hi) != 0 && t.n < kLiveMax) t.item[t.n++] = (uint16_t)it;
+  return t;
+}
+__constant__ PullTable kPullDilate = make_pull_table(-1, 1);
+__constant__ PullTable kPullNeg = make_pull_table(-1, 0);
+__constant__ PullTable kPullPos = make_pull_table(0, 1);
+static_assert(make_pull_table(-1, 1).n == 324 && make_pull_table(-1, 0).n == 170 && make_pull_table(0, 1).n == 170,
+              "live pull items per box");
+
+template <int lo, int hi>
+__device__ __forceinline__ const PullTable& pull_table() {
+  return lo < 0 && hi > 0 ? kPullDilate : (lo < 0 ? kPullNeg : kPullPos);
 }
 
 // Position in C's frame (-1 .. 16 per axis) packed as 3 x 5 bits of p + 1.
@@ -1105,15 +1131,19 @@ __device__ __forceinline__ void mark_box_leaf(const u64 W[8], uint32_t pos, int 
 
 constexpr int kMarkIlp = 2;  // leaves in flight per thread
 
+template <int lo, int hi>  // the box [lo, hi]^3: dilate [-1, 1], pads [-1, 0] and [0, 1]
 __global__ void __launch_bounds__(256) k_leaf_mark_box(const int32_t* cand_src, const int32_t* d_num_cands,
-                                                       int lo, int hi, int32_t B, const tc_grid_header* src_headers,
+                                                       int32_t B, const tc_grid_header* src_headers,
                                                        const u64* src_lower_mask, const uint16_t* src_lower_prefix,
                                                        const int32_t* src_lower_first, const u64* src_leaf_mask,
                                                        int32_t n_src_lower, int32_t n_src_leaf, u64* cand_child,
                                                        int32_t* flags) {
-  __shared__ u64 s_word[kPullItems];          // source mask word of each item (unmasked)
-  __shared__ int32_t s_base[kPullItems];      // leaf index of the word's first leaf
-  __shared__ int32_t s_excl[kPullItems + 1];  // exclusive scan of the items' reaching leaves
+  const PullTable& tab = pull_table<lo, hi>();
+  const int nlive = tab.n;
+  __shared__ u64 s_word[kLiveMax];          // source mask word of each live item (unmasked)
+  __shared__ int32_t s_base[kLiveMax];      // leaf index of the word's first leaf
+  __shared__ int32_t s_excl[kLiveMax + 1];  // exclusive scan of the items' reaching leaves
+  __shared__ uint16_t s_item[kLiveMax];     // js * 64 + w of each live item
   __shared__ unsigned long long s_mask[64];
   __shared__ int32_t s_wave[256 / kWave];
   const int tid = threadIdx.x;
@@ -1138,25 +1168,28 @@ __global__ void __launch_bounds__(256) k_leaf_mark_box(const int32_t* cand_src, 
   const i64 c0 = (i64)blockIdx.x < na ? xcd_block(blockIdx.x, na) * per : ncand;
   for (i64 c = c0; c < ncand && c < c0 + per; ++c) {
     if (tid < 64) s_mask[tid] = 0;
-    u64 wd[kPullPer];
-    int32_t base[kPullPer];
-    int cnt[kPullPer];
+    u64 wd[kLivePer];
+    int32_t base[kLivePer];
+    int cnt[kLivePer];
+    int item[kLivePer];
     int sum = 0;
     // every load at a valid index, all in flight together: the source slots,
     // then the slots' mask words, first leaves and prefixes (slot 0 stands in
     // for an empty slot; n_src_lower >= 1 whenever there are candidates)
-    int32_t sl[kPullPer];
+    int32_t sl[kLivePer];
 #pragma unroll
-    for (int k = 0; k < kPullPer; ++k) sl[k] = cand_src[c * 27 + (min(tid * kPullPer + k, kPullItems - 1) >> 6)];
-    u64 fm[kPullPer];
-    int32_t lfirst[kPullPer];
-    uint16_t lpre[kPullPer];
+    for (int k = 0; k < kLivePer; ++k) {
+      item[k] = tab.item[min(tid * kLivePer + k, nlive - 1)];
+      sl[k] = cand_src[c * 27 + (item[k] >> 6)];
+    }
+    u64 fm[kLivePer];
+    int32_t lfirst[kLivePer];
+    uint16_t lpre[kLivePer];
 #pragma unroll
-    for (int k = 0; k < kPullPer; ++k) {
-      const int item = tid * kPullPer + k;
-      const int js = item >> 6, w = item & 63;
-      fm[k] = item < kPullItems ? face_word_mask(js, w, lo, hi) : 0;
-      if (sl[k] >= n_src_lower) {
+    for (int k = 0; k < kLivePer; ++k) {
+      const int js = item[k] >> 6, w = item[k] & 63;
+      fm[k] = tid * kLivePer + k < nlive ? face_word_mask(js, w, lo, hi) : 0;
+      if (fm[k] && sl[k] >= n_src_lower) {
         set_flag(flags, kFlagInternal);
         sl[k] = -1;
       }
@@ -1167,7 +1200,7 @@ __global__ void __launch_bounds__(256) k_leaf_mark_box(const int32_t* cand_src, 
       lpre[k] = src_lower_prefix[ls * 64 + w];
     }
 #pragma unroll
-    for (int k = 0; k < kPullPer; ++k) {
+    for (int k = 0; k < kLivePer; ++k) {
       if (sl[k] < 0) wd[k] = 0;
       base[k] = sl[k] >= 0 ? lfirst[k] + lpre[k] : 0;
       cnt[k] = popc64(wd[k] & fm[k]);
@@ -1176,16 +1209,17 @@ __global__ void __launch_bounds__(256) k_leaf_mark_box(const int32_t* cand_src, 
     int total;
     int ex = block_excl_scan<int, 256>(sum, s_wave, total);
 #pragma unroll
-    for (int k = 0; k < kPullPer; ++k) {
-      const int item = tid * kPullPer + k;
-      if (item < kPullItems) {
-        s_word[item] = wd[k];
-        s_base[item] = base[k];
-        s_excl[item] = ex;
+    for (int k = 0; k < kLivePer; ++k) {
+      const int li = tid * kLivePer + k;
+      if (li < nlive) {
+        s_word[li] = wd[k];
+        s_base[li] = base[k];
+        s_excl[li] = ex;
+        s_item[li] = (uint16_t)item[k];
       }
       ex += cnt[k];
     }
-    if (tid == 0) s_excl[kPullItems] = total;
+    if (tid == 0) s_excl[nlive] = total;
     __syncthreads();
     for (int k0 = 0; k0 < total; k0 += kMarkIlp * 256) {
       int32_t lf[kMarkIlp];
@@ -1196,13 +1230,13 @@ __global__ void __launch_bounds__(256) k_leaf_mark_box(const int32_t* cand_src, 
         lf[u] = -1;
         ps[u] = 0;
         if (k < total) {
-          int a = 0, z = kPullItems;  // largest item with s_excl[item] <= k
+          int a = 0, z = nlive;  // largest live item with s_excl[item] <= k
           while (z - a > 1) {
             const int mid = (a + z) >> 1;
             if (s_excl[mid] <= k) a = mid;
             else z = mid;
           }
-          const int js = a >> 6, w = a & 63;
+          const int js = s_item[a] >> 6, w = s_item[a] & 63;
           const u64 word = s_word[a];
           const int bit = select_bit(word & face_word_mask(js, w, lo, hi), k - s_excl[a]);
           const i64 leaf = (i64)s_base[a] + popc64(word & ((1ull << bit) - 1));
@@ -1757,8 +1791,10 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, 
            ts.cand_child, ts.flags);
   } else if (nL > 0) {  // no source lowers: nothing to mark and every bbox is empty
     const i64 blocks = nL < 8192 ? nL : 8192;
-    launch("k_leaf_mark_box", k_leaf_mark_box, blocks, 256, s, (const int32_t*)cand_src,
-           (const int32_t*)ts.d_num_cands, oi.lo, oi.hi, B, (const tc_grid_header*)sv.headers,
+    auto mark_box = oi.lo < 0 && oi.hi > 0 ? k_leaf_mark_box<-1, 1>
+                    : (oi.lo < 0 ? k_leaf_mark_box<-1, 0> : k_leaf_mark_box<0, 1>);
+    launch("k_leaf_mark_box", mark_box, blocks, 256, s, (const int32_t*)cand_src,
+           (const int32_t*)ts.d_num_cands, B, (const tc_grid_header*)sv.headers,
            (const u64*)sv.lower_mask, (const uint16_t*)sv.lower_prefix, (const int32_t*)sv.lower_first,
            (const u64*)sv.leaf_mask, sv.n_lower, sv.n_leaf, ts.cand_child, ts.flags);
   }

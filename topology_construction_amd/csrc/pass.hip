@@ -339,6 +339,7 @@ __global__ void __launch_bounds__(256) k_box_reach(const int32_t* upper_first, i
 constexpr int kTilesMax = 4096;
 constexpr int kTilesThreads = 1024;
 constexpr int kTilesItems = kTilesMax / kTilesThreads;
+constexpr int kRankMax = 256;  // keys sorted by rank counting; more go through a bitonic network
 
 __global__ void __launch_bounds__(kTilesThreads) k_tiles_small(const int4* upper_origin, const u64* upper_mask,
                                                                int32_t n_upper, int op, int m, int32_t B,
@@ -437,41 +438,63 @@ __global__ void __launch_bounds__(kTilesThreads) k_tiles_small(const int4* upper
     }
   }
   __shared__ int32_t s_nt;
-  if (K <= kWave) {
-    // few keys: a rank sort (keys are distinct through their candidate index):
-    // wave w compares every key with keys 4w .. 4w+3, wave 0 adds the partial
-    // ranks, places each key at its rank (LDS, past the first kWave entries),
-    // reads the sorted keys back, deduplicates and scatters
-    __shared__ int32_t s_cnt[kTilesThreads / kWave][kWave];
+  // Up to kRankMax keys: a rank sort (keys are distinct through their candidate
+  // index). With Kp = K rounded up to a power of two (>= 64), T = 1024 / Kp
+  // threads share each key: thread (part, i) counts the keys smaller than key i
+  // among its 1/T of the keys; the partial ranks meet in LDS.
+  __shared__ int32_t s_cnt[kTilesThreads];
+  int rank = 0;  // thread tid < K: the rank of key tid, which it holds in rhi, rlo, rv
+  u64 rhi = 0, rlo = 0;
+  uint32_t rv = 0;
+  if (K <= kRankMax) {
+    int Kp = kWave;
+    while (Kp < K) Kp <<= 1;
+    const int T = kTilesThreads / Kp;
+    const int ki = tid % Kp, part = tid / Kp;
+    const int per = (K + T - 1) / T;
     __syncthreads();
     {
       int c = 0;
-      if (lane < K) {
-        const u64 hi = s_hi[lane], lo = s_lo[lane];
-        const uint32_t v = s_v[lane];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int j = wv * 4 + q;
-          if (j < K) {
-            const u64 oh = s_hi[j], ol = s_lo[j];
-            const uint32_t ov = s_v[j];
-            c += (oh != hi ? oh < hi : (ol != lo ? ol < lo : ov < v)) ? 1 : 0;
-          }
+      if (ki < K) {
+        const u64 hi = s_hi[ki], lo = s_lo[ki];
+        const uint32_t v = s_v[ki];
+        const int j1 = min(K, (part + 1) * per);
+        for (int j = part * per; j < j1; ++j) {
+          const u64 oh = s_hi[j], ol = s_lo[j];
+          const uint32_t ov = s_v[j];
+          c += (oh != hi ? oh < hi : (ol != lo ? ol < lo : ov < v)) ? 1 : 0;
         }
       }
-      s_cnt[wv][lane] = c;
+      s_cnt[part * Kp + ki] = c;
     }
     __syncthreads();
+    if (tid < K) {
+      for (int q = 0; q < T; ++q) rank += s_cnt[q * Kp + tid];
+      rhi = s_hi[tid];
+      rlo = s_lo[tid];
+      rv = s_v[tid];
+    }
+    if (K > kWave) {
+      // place every key at its rank, in place (all keys are in registers first),
+      // then the block-wide head flags below
+      __syncthreads();
+      if (tid < K) {
+        s_hi[rank] = rhi;
+        s_lo[rank] = rlo;
+        s_v[rank] = rv;
+      }
+      __syncthreads();
+    }
+  }
+  if (K <= kWave) {
+    // at most 64 keys: wave 0 places them at their ranks (LDS, past the first
+    // kWave entries), reads them back sorted, deduplicates and scatters with no
+    // further block barrier
     if (wv == 0) {
       if (lane < K) {
-        int rank = 0;
-#pragma unroll
-        for (int w = 0; w < kTilesThreads / kWave; ++w) rank += s_cnt[w][lane];
-        const u64 h0 = s_hi[lane], l0 = s_lo[lane];
-        const uint32_t v0 = s_v[lane];
-        s_hi[kWave + rank] = h0;
-        s_lo[kWave + rank] = l0;
-        s_v[kWave + rank] = v0;
+        s_hi[kWave + rank] = rhi;
+        s_lo[kWave + rank] = rlo;
+        s_v[kWave + rank] = rv;
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
@@ -509,82 +532,84 @@ __global__ void __launch_bounds__(kTilesThreads) k_tiles_small(const int4* upper
     }
     return;
   }
-  int P = 2;
-  while (P < K) P <<= 1;
-  if (K <= kTilesThreads) {
-    // one key per thread: stages whose partner is in the same wave exchange with
-    // shuffles, only the wider ones go through LDS
-    __syncthreads();
-    u64 hi = tid < K ? s_hi[tid] : ~0ull, lo = tid < K ? s_lo[tid] : ~0ull;  // padding sorts last
-    uint32_t v = tid < K ? s_v[tid] : 0xffffffffu;
-    const bool act = tid < P;  // whole waves: P is a power of two >= 128
-    for (int k = 2; k <= P; k <<= 1) {
-      for (int jj = k >> 1; jj > 0; jj >>= 1) {
-        u64 oh = 0, ol = 0;
-        uint32_t ov = 0;
-        if (jj >= kWave) {  // uniform
-          __syncthreads();
-          if (act) {
-            s_hi[tid] = hi;
-            s_lo[tid] = lo;
-            s_v[tid] = v;
+  if (K > kRankMax) {  // LDS bitonic sort
+    int P = 2;
+    while (P < K) P <<= 1;
+    if (K <= kTilesThreads) {
+      // one key per thread: stages whose partner is in the same wave exchange with
+      // shuffles, only the wider ones go through LDS
+      __syncthreads();
+      u64 hi = tid < K ? s_hi[tid] : ~0ull, lo = tid < K ? s_lo[tid] : ~0ull;  // padding sorts last
+      uint32_t v = tid < K ? s_v[tid] : 0xffffffffu;
+      const bool act = tid < P;  // whole waves: P is a power of two >= 128
+      for (int k = 2; k <= P; k <<= 1) {
+        for (int jj = k >> 1; jj > 0; jj >>= 1) {
+          u64 oh = 0, ol = 0;
+          uint32_t ov = 0;
+          if (jj >= kWave) {  // uniform
+            __syncthreads();
+            if (act) {
+              s_hi[tid] = hi;
+              s_lo[tid] = lo;
+              s_v[tid] = v;
+            }
+            __syncthreads();
+            if (act) {
+              oh = s_hi[tid ^ jj];
+              ol = s_lo[tid ^ jj];
+              ov = s_v[tid ^ jj];
+            }
+          } else if (act) {
+            oh = __shfl_xor(hi, jj, kWave);
+            ol = __shfl_xor(lo, jj, kWave);
+            ov = (uint32_t)__shfl_xor((int)v, jj, kWave);
           }
-          __syncthreads();
-          if (act) {
-            oh = s_hi[tid ^ jj];
-            ol = s_lo[tid ^ jj];
-            ov = s_v[tid ^ jj];
+          if (!act) continue;
+          const bool gt = hi != oh ? hi > oh : (lo != ol ? lo > ol : v > ov);
+          const bool lt = hi != oh ? hi < oh : (lo != ol ? lo < ol : v < ov);
+          const bool up = (tid & k) == 0, lower = (tid & jj) == 0;
+          if (up ? (lower ? gt : lt) : (lower ? lt : gt)) {
+            hi = oh;
+            lo = ol;
+            v = ov;
           }
-        } else if (act) {
-          oh = __shfl_xor(hi, jj, kWave);
-          ol = __shfl_xor(lo, jj, kWave);
-          ov = (uint32_t)__shfl_xor((int)v, jj, kWave);
-        }
-        if (!act) continue;
-        const bool gt = hi != oh ? hi > oh : (lo != ol ? lo > ol : v > ov);
-        const bool lt = hi != oh ? hi < oh : (lo != ol ? lo < ol : v < ov);
-        const bool up = (tid & k) == 0, lower = (tid & jj) == 0;
-        if (up ? (lower ? gt : lt) : (lower ? lt : gt)) {
-          hi = oh;
-          lo = ol;
-          v = ov;
         }
       }
-    }
-    __syncthreads();
-    if (act) {
-      s_hi[tid] = hi;
-      s_lo[tid] = lo;
-      s_v[tid] = v;
-    }
-    __syncthreads();
-  } else {
-    for (int i = K + tid; i < P; i += kTilesThreads) {  // padding sorts last
-      s_hi[i] = ~0ull;
-      s_lo[i] = ~0ull;
-      s_v[i] = 0xffffffffu;
-    }
-    __syncthreads();
-    for (int k = 2; k <= P; k <<= 1) {
-      for (int jj = k >> 1; jj > 0; jj >>= 1) {
-        for (int i = tid; i < P; i += kTilesThreads) {
-          const int ixj = i ^ jj;
-          if (ixj > i) {
-            const bool up = (i & k) == 0;
-            const u64 ah = s_hi[i], al = s_lo[i], bh = s_hi[ixj], bl = s_lo[ixj];
-            const uint32_t av = s_v[i], bv = s_v[ixj];
-            const bool gt = ah != bh ? ah > bh : (al != bl ? al > bl : av > bv);
-            if (gt == up) {
-              s_hi[i] = bh;
-              s_lo[i] = bl;
-              s_v[i] = bv;
-              s_hi[ixj] = ah;
-              s_lo[ixj] = al;
-              s_v[ixj] = av;
+      __syncthreads();
+      if (act) {
+        s_hi[tid] = hi;
+        s_lo[tid] = lo;
+        s_v[tid] = v;
+      }
+      __syncthreads();
+    } else {
+      for (int i = K + tid; i < P; i += kTilesThreads) {  // padding sorts last
+        s_hi[i] = ~0ull;
+        s_lo[i] = ~0ull;
+        s_v[i] = 0xffffffffu;
+      }
+      __syncthreads();
+      for (int k = 2; k <= P; k <<= 1) {
+        for (int jj = k >> 1; jj > 0; jj >>= 1) {
+          for (int i = tid; i < P; i += kTilesThreads) {
+            const int ixj = i ^ jj;
+            if (ixj > i) {
+              const bool up = (i & k) == 0;
+              const u64 ah = s_hi[i], al = s_lo[i], bh = s_hi[ixj], bl = s_lo[ixj];
+              const uint32_t av = s_v[i], bv = s_v[ixj];
+              const bool gt = ah != bh ? ah > bh : (al != bl ? al > bl : av > bv);
+              if (gt == up) {
+                s_hi[i] = bh;
+                s_lo[i] = bl;
+                s_v[i] = bv;
+                s_hi[ixj] = ah;
+                s_lo[ixj] = al;
+                s_v[ixj] = av;
+              }
             }
           }
+          __syncthreads();
         }
-        __syncthreads();
       }
     }
   }

@@ -795,8 +795,8 @@ __global__ void __launch_bounds__(256) k_lower_nbr(const int4* lower_origin, con
 // and the candidate indices / origins / sources. When the unique tiles are few
 // (at most kLdsTiles, known only here) their candidate masks, prefix tables and
 // bases live in LDS and the masks are copied out at the end; otherwise the same
-// steps run on the global arrays, with a device fence where a later phase reads
-// what other waves wrote. Each thread owns two pairs, whose origins and tile
+// steps run on the global arrays; a block barrier orders what other waves wrote
+// before a later phase reads it. Each thread owns two pairs, whose origins and tile
 // indices are loaded once, up front, all in flight together. Replaces five
 // launches of the general path.
 constexpr int kLowersSmallMax = 2048;  // beyond this the five-launch path is faster
@@ -852,8 +852,9 @@ __global__ void __launch_bounds__(kLowersThreads) k_lowers_small(
   } else {
     ulonglong2* tc2 = reinterpret_cast<ulonglong2*>(tile_child);
     for (i64 k = tid; k < (i64)nt * 256; k += kLowersThreads) tc2[k] = make_ulonglong2(0, 0);
-    __threadfence();  // the zeros land before any wave's atomics below
   }
+  // the barrier orders every wave's global stores before the other waves'
+  // accesses after it (workgroup scope; nothing here is read by another workgroup)
   __syncthreads();
   // targets of the thread's pairs and their tiles
   LowerTarget tg[kLowersItems];
@@ -880,7 +881,6 @@ __global__ void __launch_bounds__(kLowersThreads) k_lowers_small(
     const int bit = upper_child_bit(tg[k].k);
     atomicOr((unsigned long long*)&tch[(i64)tt[k] * 512 + (bit >> 6)], 1ull << (bit & 63));
   }
-  if (!in_lds) __threadfence();
   __syncthreads();
   // per-tile prefix tables: one wave per tile, 8 words per lane
   for (int t = wv; t < nt; t += kWaves) {
@@ -923,8 +923,7 @@ __global__ void __launch_bounds__(kLowersThreads) k_lowers_small(
   for (i64 k = tid; k < (i64)total * m_src; k += kLowersThreads) cand_src[k] = -1;
   if (zero_cand_child)
     for (i64 k = tid; k < (i64)total * 64; k += kLowersThreads) cand_child[k] = 0;
-  __threadfence();  // the fills land before other waves' table entries below
-  __syncthreads();
+  __syncthreads();  // the fills land before other waves' table entries below
   // candidate index of every pair, its origin and its candidate -> source entry
 #pragma unroll
   for (int k = 0; k < kLowersItems; ++k) {

@@ -731,8 +731,7 @@ __global__ void __launch_bounds__(kPartThreads) k_vox_partials(i64* vox_part, i6
     bbox[k] = INT32_MAX;
     bbox[3 * (i64)R * B + k] = INT32_MIN;
   }
-  __threadfence();
-  __syncthreads();  // the scanned runs are read below
+  __syncthreads();  // the scanned runs are read below (by this workgroup only)
   // a grid's voxel begin: its first leaf's run offset plus that leaf's in-run prefix
   for (int32_t g = threadIdx.x; g <= B; g += kPartThreads) {
     const i64 f = g < B ? grid_info[g * 6 + 5] : L;

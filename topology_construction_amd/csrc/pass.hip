@@ -340,6 +340,7 @@ constexpr int kTilesMax = 4096;
 constexpr int kTilesThreads = 1024;
 constexpr int kTilesItems = kTilesMax / kTilesThreads;
 constexpr int kRankMax = 256;  // keys sorted by rank counting; more go through a bitonic network
+constexpr i64 kTileBits = 65536;  // mixed-radix (grid, tile) key space handled by an LDS bitmap
 
 __global__ void __launch_bounds__(kTilesThreads) k_tiles_small(const int4* upper_origin, const u64* upper_mask,
                                                                int32_t n_upper, int op, int m, int32_t B,
@@ -357,7 +358,14 @@ __global__ void __launch_bounds__(kTilesThreads) k_tiles_small(const int4* upper
   const int lane = tid & (kWave - 1);
   const int wv = tid / kWave;
   const int n = n_upper * m;
-  if (tid == 0) readback[0] = 0;
+  __shared__ int32_t s_rng[6];  // min x, y, z, max x, y, z of the kept candidates' tiles
+  if (tid == 0) {
+    readback[0] = 0;
+    for (int a = 0; a < 3; ++a) {
+      s_rng[a] = INT32_MAX;
+      s_rng[3 + a] = INT32_MIN;
+    }
+  }
   if (op != TC_OP_COARSEN && upper_reach) {  // computed by k_node_reach
     for (int u = tid; u < n_upper; u += kTilesThreads) s_code[u] = upper_reach[u];
   } else if (op != TC_OP_COARSEN) {
@@ -438,6 +446,94 @@ __global__ void __launch_bounds__(kTilesThreads) k_tiles_small(const int4* upper
     }
   }
   __shared__ int32_t s_nt;
+  // More than 64 keys: the (grid, tile) keys of the kept candidates, relative to
+  // the batch's tile ranges, index a mixed-radix space of S = B * Rx * Ry * Rz
+  // points in canonical order. When S is at most kTileBits, one bit per
+  // candidate in an LDS bitmap replaces the sort: the set bits are the unique
+  // tiles in order, and a popcount prefix gives every candidate its tile (whose
+  // record every candidate of it writes, with the same value).
+  __shared__ u64 s_bits[kTileBits / 64];
+  __shared__ int32_t s_wpre[kTileBits / 64];
+  if (K > kWave) {  // uniform
+    {
+      int rmin[3] = {INT32_MAX, INT32_MAX, INT32_MAX}, rmax[3] = {INT32_MIN, INT32_MIN, INT32_MIN};
+#pragma unroll
+      for (int k = 0; k < kTilesItems; ++k) {
+        if (!keep[k]) continue;
+        const int tv[3] = {(int)((klo[k] >> 40) & 0xfffff) - kTileBias, (int)((klo[k] >> 20) & 0xfffff) - kTileBias,
+                           (int)(klo[k] & 0xfffff) - kTileBias};
+        for (int a = 0; a < 3; ++a) {
+          rmin[a] = min(rmin[a], tv[a]);
+          rmax[a] = max(rmax[a], tv[a]);
+        }
+      }
+#pragma unroll
+      for (int a = 0; a < 3; ++a) {
+        rmin[a] = wave_min_i32(rmin[a]);
+        rmax[a] = wave_max_i32(rmax[a]);
+      }
+      if (lane == 0 && rmin[0] <= rmax[0]) {
+        for (int a = 0; a < 3; ++a) {
+          atomicMin(&s_rng[a], rmin[a]);
+          atomicMax(&s_rng[3 + a], rmax[a]);
+        }
+      }
+    }
+    __syncthreads();
+    const i64 R64[3] = {(i64)s_rng[3] - s_rng[0] + 1, (i64)s_rng[4] - s_rng[1] + 1, (i64)s_rng[5] - s_rng[2] + 1};
+    i64 S = B;
+    for (int a = 0; a < 3 && S <= kTileBits; ++a) S *= R64[a];
+    if (S <= kTileBits) {  // every index below fits in 32 bits
+      const int R[3] = {(int)R64[0], (int)R64[1], (int)R64[2]};
+      const int nw = (int)((S + 63) >> 6);
+      for (int w = tid; w < nw; w += kTilesThreads) s_bits[w] = 0;
+      __syncthreads();
+      int pk[kTilesItems];
+#pragma unroll
+      for (int k = 0; k < kTilesItems; ++k) {
+        pk[k] = -1;
+        if (!keep[k]) continue;
+        const int g = (int)((khi[k] << 4) | (klo[k] >> 60));
+        const int x = (int)((klo[k] >> 40) & 0xfffff) - kTileBias - s_rng[0];
+        const int y = (int)((klo[k] >> 20) & 0xfffff) - kTileBias - s_rng[1];
+        const int z = (int)(klo[k] & 0xfffff) - kTileBias - s_rng[2];
+        pk[k] = ((g * R[0] + x) * R[1] + y) * R[2] + z;
+        atomicOr((unsigned long long*)&s_bits[pk[k] >> 6], 1ull << (pk[k] & 63));
+      }
+      __syncthreads();
+      int nt;
+      const int wex = block_excl_scan<int, kTilesThreads>(tid < nw ? popc64(s_bits[tid]) : 0, s_wave, nt);
+      if (tid < nw) s_wpre[tid] = wex;
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < kTilesItems; ++k) {
+        if (pk[k] < 0) continue;
+        const int w = pk[k] >> 6;
+        const int t = s_wpre[w] + popc64(s_bits[w] & ((1ull << (pk[k] & 63)) - 1));
+        tile_of_cand[tid * kTilesItems + k] = t;
+        utile[t] = make_int4((int32_t)((klo[k] >> 40) & 0xfffff) - kTileBias,
+                             (int32_t)((klo[k] >> 20) & 0xfffff) - kTileBias, (int32_t)(klo[k] & 0xfffff) - kTileBias,
+                             (int32_t)((khi[k] << 4) | (klo[k] >> 60)));
+      }
+      // grid g's tiles begin at the rank of its first point g * Rx * Ry * Rz
+      const int per_grid = R[0] * R[1] * R[2];
+      for (int g = tid; g <= B; g += kTilesThreads) {
+        if (g == B) {
+          grid_tile_begin[g] = nt;
+        } else {
+          const int q = g * per_grid;
+          const int w = q >> 6;
+          grid_tile_begin[g] = s_wpre[w] + popc64(s_bits[w] & ((1ull << (q & 63)) - 1));
+        }
+      }
+      if (tid == 0) *d_num_tiles = nt;
+      if (zero_child) {
+        ulonglong2* tc = reinterpret_cast<ulonglong2*>(tile_child);
+        for (i64 k = tid; k < (i64)nt * 256; k += kTilesThreads) tc[k] = make_ulonglong2(0, 0);
+      }
+      return;
+    }
+  }
   // Up to kRankMax keys: a rank sort (keys are distinct through their candidate
   // index). With Kp = K rounded up to a power of two (>= 64), T = 1024 / Kp
   // threads share each key: thread (part, i) counts the keys smaller than key i

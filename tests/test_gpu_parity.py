@@ -236,6 +236,31 @@ def test_many_tiles_large_sort_paths():
         _check(op, f, ijk, off, "many-tiles")
 
 
+def _tiles_members(seed, B, tiles_per_member, span):
+    """B members, each with one voxel in every one of `tiles_per_member` distinct
+    root tiles drawn from [-span, span]^3 (tile units)."""
+    rng = np.random.default_rng(seed)
+    members = []
+    for _ in range(B):
+        t = np.unique(rng.integers(-span, span + 1, size=(tiles_per_member * 2, 3)), axis=0)[:tiles_per_member]
+        members.append((t * 4096 + rng.integers(0, 4096, size=t.shape)).astype(np.int32))
+    return synth.concat_members(members)
+
+
+@pytest.mark.parametrize("seed,B,per,span", [
+    (21, 8, 20, 2),     # compact tile ranges: the LDS bitmap over (grid, tile) keys
+    (22, 6, 25, 400),   # 64 < keys <= 256 over a key space too large for the bitmap: the rank sort
+    (23, 8, 60, 400),   # 256 < keys <= 1024: the one-key-per-thread bitonic network
+    (24, 8, 150, 400),  # more than 1024 keys: the LDS bitonic network
+])
+def test_tile_dedup_paths(seed, B, per, span):
+    """Every tile-dedup path of the one-workgroup tile stage (4096 candidates at
+    most) against the oracle."""
+    ijk, off = _tiles_members(seed, B, per, span)
+    for op, f in [("coarsen", 2), ("refine", 2), ("dilate", 1)]:
+        _check(op, f, ijk, off, f"tiles seed={seed}")
+
+
 def test_pyramid_chain_config4():
     """Coarsen x2 three times, then k3s2 transpose back up, each level from the GPU output."""
     from topology_construction_amd import binding

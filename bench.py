@@ -93,7 +93,8 @@ def run_step(binding, src, outs=None):
 #   k_leaf_gather        reads every output leaf's origin 16 B + candidate id 4 B, every
 #                        source mask once (64 B), writes every output mask (64 B)
 #   k_leaf_offsets_bbox  reads origin 16 B + packed bbox 4 B + voxel scan 8 B,
-#                        writes the voxel offset 8 B, per output leaf
+#                        writes the voxel offset 8 B, per output leaf (k_finalize_small,
+#                        the same work in one launch on batches of at most 262144 leaves)
 #   k_enumerate          reads origin, mask, offset and grid base (96 B per leaf),
 #                        writes 12 B per voxel
 def kernel_bytes(name, src_leaves, leaves, voxels):
@@ -101,14 +102,15 @@ def kernel_bytes(name, src_leaves, leaves, voxels):
         return 80 * src_leaves
     if name == "k_leaf_gather":
         return 84 * leaves + 64 * src_leaves
-    if name == "k_leaf_offsets_bbox":
+    if name in ("k_leaf_offsets_bbox", "k_finalize_small"):
         return 36 * leaves
     if name == "k_enumerate":
         return 96 * leaves + 12 * voxels
     raise ValueError(name)
 
 
-LARGE_KERNELS = ["k_leaf_mark_lower", "k_leaf_mark_box", "k_leaf_gather", "k_leaf_offsets_bbox", "k_enumerate"]
+LARGE_KERNELS = ["k_leaf_mark_lower", "k_leaf_mark_box", "k_leaf_gather", "k_leaf_offsets_bbox", "k_finalize_small",
+                 "k_enumerate"]
 
 
 def source_digest():

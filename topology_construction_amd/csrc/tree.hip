@@ -353,6 +353,7 @@ void tree_grid_counts(TreeScratch& ts, int32_t B, hipStream_t s) {
 }
 
 // ------------------------------------------------------------------ node writers
+constexpr int kNodeFlags = 4096;  // candidates per tile whose non-empty flags the tile block stages in LDS
 // One launch, two roles. Blocks [0, tile_blocks) each own one tile and write its
 // upper node record and child mask (candidate bits whose lower turned out empty
 // are cleared). The remaining blocks own four candidate lowers each (one wave
@@ -368,6 +369,7 @@ __global__ void __launch_bounds__(256) k_write_nodes(
     u64* upper_key, int32_t* upper_first, u64* upper_mask, int4* lower_origin, int32_t* lower_first,
     u64* lower_mask, uint16_t* lower_prefix, int4* leaf_origin, int32_t* leaf_parent, int32_t* leaf_cand,
     tc_grid_header* hdr, int32_t B, i64 cap_cands) {
+  __shared__ uint32_t s_flags[kNodeFlags / 32];
   if (blockIdx.x == 0) {  // every grid's box starts empty; the leaf finalizer folds into it
     for (int32_t g = threadIdx.x; g < B; g += 256) {
       for (int a = 0; a < 3; ++a) {
@@ -400,15 +402,35 @@ __global__ void __launch_bounds__(256) k_write_nodes(
       upper_key[u] = ((u64)(T.x + kTileBias) << 40) | ((u64)(T.y + kTileBias) << 20) | (u64)(T.z + kTileBias);
       upper_first[u] = scan_lower(vb);
     }
+    // the tile's candidates' non-empty flags as an LDS bitset (loads of up to
+    // kNodeFlags candidates in flight together), so that the per-bit loop below
+    // waits on no memory; tiles with more candidates read the counts directly
+    const int32_t ncb = ce - cb;
+    const bool lds_flags = ncb <= kNodeFlags;  // uniform
+    if (lds_flags) {
+      const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+      for (int q = 0; q < kNodeFlags / 256; ++q) {
+        const int32_t k = q * 256 + threadIdx.x;
+        const bool ne = k < ncb && (int32_t)cand_counts[cb + min(k, ncb - 1)] > 0;
+        const u64 bal = __ballot(ne);
+        if (lane == 0) {
+          s_flags[k >> 5] = (uint32_t)bal;
+          s_flags[(k >> 5) + 1] = (uint32_t)(bal >> 32);
+        }
+      }
+      __syncthreads();
+    }
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int w = threadIdx.x * 2 + k;
       u64 word = words[k];
       u64 out = 0;
-      int32_t c = cb + pres[k];
+      int32_t c = pres[k];  // candidate index relative to the tile's base
       while (word) {
         const int b = __builtin_ctzll(word);
-        if ((int32_t)cand_counts[c] > 0) out |= 1ull << b;
+        const bool ne = lds_flags ? ((s_flags[c >> 5] >> (c & 31)) & 1u) != 0 : (int32_t)cand_counts[cb + c] > 0;
+        if (ne) out |= 1ull << b;
         word &= word - 1;
         ++c;
       }
@@ -533,14 +555,14 @@ int32_t bbox_replicas(int32_t B) {
 // the offsets of its kFinSlice leaves (wave w: a contiguous run of kFinPer * 64),
 // folds their boxes per grid in LDS, and then into the headers with one set of
 // atomics per grid it touched (the node writer has set every box to empty);
-// workgroup 0 writes the other header fields. Totals stay below 2^31 here (L * 512), so offsets
+// workgroup 0 writes the other header fields. Totals stay below 2^31 here (L * 512 <= 2^27), so offsets
 // are computed in 32 bits. All global loads that do not depend on another are
 // issued first, at clamped indices.
 constexpr int kFinThreads = 256;
 constexpr int kFinPer = 8;
 constexpr int kFinSlice = kFinThreads * kFinPer;  // leaves per workgroup
-constexpr int kFinRuns = 1024;
-constexpr i64 kFinSmallLeaves = 65536;
+constexpr int kFinRuns = 4096;
+constexpr i64 kFinSmallLeaves = 262144;  // totals below 2^31 voxels (512 per leaf)
 constexpr int kFinSmallGrids = 1024;
 
 __device__ __forceinline__ void box_fold_lds(int32_t (*s_box)[kFinSmallGrids], int g, const int v[6]) {
@@ -700,7 +722,7 @@ __global__ void __launch_bounds__(kFinThreads) k_finalize_small(const int4* leaf
 // before it in that run; gvb[B] = total); then every leaf's offset comes from its
 // block's run offset plus a block scan, with no pass over all leaves just to scan.
 constexpr int kPartThreads = 1024;
-constexpr int kPartItems = 16;
+constexpr int kPartItems = 8;
 
 __global__ void __launch_bounds__(kPartThreads) k_vox_partials(i64* vox_part, i64 np, const int32_t* leaf_inrun,
                                                                i64 gran, const int32_t* grid_info, int32_t B, i64 L,

@@ -19,6 +19,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -114,14 +115,17 @@ LARGE_KERNELS = ["k_leaf_mark_lower", "k_leaf_mark_box", "k_leaf_gather", "k_lea
 
 
 def source_digest():
-    """sha256 over the library's kernel sources: counter readings taken from an
-    older build no longer describe the kernels and are then not reported."""
+    """sha256 over the library's kernel sources with // comments, trailing blanks
+    and empty lines removed: counter readings taken from other code no longer
+    describe the kernels and are then not reported (a comment edit changes no
+    kernel, so it keeps them)."""
     csrc = os.path.join(ROOT, "topology_construction_amd", "csrc")
     h = hashlib.sha256()
     for name in sorted(os.listdir(csrc)):
         if name.endswith((".hip", ".hpp")):
-            with open(os.path.join(csrc, name), "rb") as fh:
-                h.update(name.encode() + b"\0" + fh.read())
+            with open(os.path.join(csrc, name), encoding="utf-8") as fh:
+                lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in fh]
+            h.update(name.encode() + b"\0" + "\n".join(ln for ln in lines if ln).encode())
     return h.hexdigest()
 
 

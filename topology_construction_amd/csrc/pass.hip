@@ -331,11 +331,13 @@ __global__ void __launch_bounds__(256) k_box_reach(const int32_t* upper_first, i
 
 // ------------------------------------------------------------------ stage: tiles, fused (small batches)
 // At most 4096 tile candidates: one workgroup builds the reach set of every
-// source upper, compacts the reachable in-range candidates, sorts them in LDS
-// (bitonic over (key, value)), flags and scans the unique keys, scatters the
-// unique tiles and every candidate's tile index, writes the per-grid tile ranges
-// and, when asked (few tiles), zeroes the unique tiles' lower bitmaps; more
-// tiles get a wide fill.
+// source upper, compacts the reachable in-range candidates, brings their
+// (grid, tile) keys into canonical order without duplicates (a rank sort for
+// at most 64 keys; above that an LDS bitmap over the batch's key space when it
+// is small, else a rank sort or an LDS bitonic network, then head flags and a
+// scan), scatters the unique tiles and every candidate's tile index, writes the
+// per-grid tile ranges and, when asked (few tiles), zeroes the unique tiles'
+// lower bitmaps; more tiles get a wide fill.
 constexpr int kTilesMax = 4096;
 constexpr int kTilesThreads = 1024;
 constexpr int kTilesItems = kTilesMax / kTilesThreads;

@@ -1065,18 +1065,6 @@ __global__ void __launch_bounds__(kLowersThreads) k_lowers_small(
 }
 
 // ------------------------------------------------------------------ stage: leaves (pass A)
-// Non-emptiness of the target leaf reached with offset t (each component -1/0/+1)
-// under a box op: the source must hold a voxel on the faces that spill toward t.
-__device__ __forceinline__ bool spill_nonempty(const u64 W[8], const I3& t) {
-  u64 xs;
-  if (t.x > 0) xs = W[7];
-  else if (t.x < 0) xs = W[0];
-  else xs = W[0] | W[1] | W[2] | W[3] | W[4] | W[5] | W[6] | W[7];
-  const u64 ym = t.y > 0 ? 0xff00000000000000ull : (t.y < 0 ? 0xffull : ~0ull);
-  const u64 zm = t.z > 0 ? kZ7 : (t.z < 0 ? kZ0 : ~0ull);
-  return (xs & ym & zm) != 0;
-}
-
 // Refine: the 4^3 sub-block q of the source leaf becomes child leaf q.
 __device__ __forceinline__ bool subblock_nonempty(const u64 W[8], const I3& q) {
   const u64 xs = q.x ? (W[4] | W[5] | W[6] | W[7]) : (W[0] | W[1] | W[2] | W[3]);
@@ -1085,12 +1073,13 @@ __device__ __forceinline__ bool subblock_nonempty(const u64 W[8], const I3& q) {
   return (xs & ym & zm) != 0;
 }
 
-// One workgroup per source lower node: every leaf of that lower marks its
-// non-empty target leaves in LDS copies of the (at most m) target lowers' 16^3
-// masks, then the block flushes whole 64-bit words to the candidate lowers. For
-// refine each target lower has exactly one source lower, so the flush is a plain
-// store of all 64 words (no zero-fill needed); the other ops OR their non-zero
-// words with device-scope atomics, far fewer than one per target leaf.
+// Refine and coarsen. One workgroup per source lower node: every leaf of that
+// lower marks its non-empty target leaves in LDS copies of the (at most 8)
+// target lowers' 16^3 masks, then the block flushes whole 64-bit words to the
+// candidate lowers. For refine each target lower has exactly one source lower,
+// so the flush is a plain store of all 64 words (no zero-fill needed); coarsen
+// ORs its non-zero words with device-scope atomics, far fewer than one per
+// target leaf. (Box ops mark from the target side, below.)
 __device__ __forceinline__ void lds_mark(unsigned long long* s_mask, int j, i64 px, i64 py, i64 pz) {
   const int bit = (int)((px * 16 + py) * 16 + pz);
   atomicOr(&s_mask[j * 64 + (bit >> 6)], 1ull << (bit & 63));
@@ -1101,63 +1090,70 @@ __global__ void __launch_bounds__(256) k_leaf_mark_lower(const int4* leaf_origin
                                                          const uint16_t* lower_prefix, int op, int m,
                                                          const int32_t* lower_nbr, const int32_t* d_num_cands,
                                                          u64* cand_child, int32_t* flags) {
-  __shared__ unsigned long long s_mask[27 * 64];
+  constexpr int kFlush = 8 * 64 / 256;  // target words per thread (m <= 8)
+  constexpr int kPer = 2;               // leaves per thread in flight
+  __shared__ unsigned long long s_mask[8 * 64];
   const i64 l = blockIdx.x;
-  for (int k = threadIdx.x; k < m * 64; k += 256) s_mask[k] = 0;
-  __syncthreads();
+  // loads indexed by the lower alone, first: its leaf range and the candidates
+  // its target lowers became
   const i64 first = lower_first[l];
   const int count = lower_prefix[l * 64 + 63] + popc64(lower_mask[l * 64 + 63]);
-  for (int k = threadIdx.x; k < count; k += 256) {
-    const i64 i = first + k;
-    const int4 o = leaf_origin[i];
-    u64 W[8];
+  const int32_t ncand = *d_num_cands;
+  int32_t nbr[kFlush];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) W[q] = leaf_mask[i * 8 + q];
-    const i64 mx = o.x >> 3, my = o.y >> 3, mz = o.z >> 3;  // leaf coordinates
-    const i64 lx = mx & 15, ly = my & 15, lz = mz & 15;     // position inside the lower
-    if (op == TC_OP_REFINE) {
-      const int j = octant_index(lx >> 3, ly >> 3, lz >> 3);  // all children share one target lower
+  for (int r = 0; r < kFlush; ++r) nbr[r] = lower_nbr[l * m + min((r * 256 + (int)threadIdx.x) >> 6, m - 1)];
+  for (int k = threadIdx.x; k < m * 64; k += 256) s_mask[k] = 0;
+  __syncthreads();
+  for (int k0 = 0; k0 < count; k0 += kPer * 256) {
+    int4 o[kPer];
+    u64 W[kPer][8];
 #pragma unroll
-      for (int qx = 0; qx < 2; ++qx) {
-        u64 word = 0;
-        const i64 x = (2 * lx + qx) & 15;
+    for (int u = 0; u < kPer; ++u) {  // clamped: every leaf of the batch in flight together
+      const i64 i = first + min(k0 + u * 256 + (int)threadIdx.x, count - 1);
+      o[u] = leaf_origin[i];
 #pragma unroll
-        for (int qy = 0; qy < 2; ++qy)
+      for (int q = 0; q < 8; ++q) W[u][q] = leaf_mask[i * 8 + q];
+    }
 #pragma unroll
-          for (int qz = 0; qz < 2; ++qz) {
-            const I3 q{qx, qy, qz};
-            if (!subblock_nonempty(W, q)) continue;
-            if (!leaf_ok(2 * mx + qx) || !leaf_ok(2 * my + qy) || !leaf_ok(2 * mz + qz)) {
-              set_flag(flags, kFlagOverflow);
-              continue;
+    for (int u = 0; u < kPer; ++u) {
+      if (k0 + u * 256 + (int)threadIdx.x >= count) continue;
+      const i64 mx = o[u].x >> 3, my = o[u].y >> 3, mz = o[u].z >> 3;  // leaf coordinates
+      const i64 lx = mx & 15, ly = my & 15, lz = mz & 15;              // position inside the lower
+      if (op == TC_OP_REFINE) {
+        const int j = octant_index(lx >> 3, ly >> 3, lz >> 3);  // all children share one target lower
+#pragma unroll
+        for (int qx = 0; qx < 2; ++qx) {
+          u64 word = 0;
+          const i64 x = (2 * lx + qx) & 15;
+#pragma unroll
+          for (int qy = 0; qy < 2; ++qy)
+#pragma unroll
+            for (int qz = 0; qz < 2; ++qz) {
+              const I3 q{qx, qy, qz};
+              if (!subblock_nonempty(W[u], q)) continue;
+              if (!leaf_ok(2 * mx + qx) || !leaf_ok(2 * my + qy) || !leaf_ok(2 * mz + qz)) {
+                set_flag(flags, kFlagOverflow);
+                continue;
+              }
+              word |= 1ull << ((((2 * ly + qy) & 3) * 16) + ((2 * lz + qz) & 15));
             }
-            word |= 1ull << ((((2 * ly + qy) & 3) * 16) + ((2 * lz + qz) & 15));
-          }
-        // children with this qx share the word x*4 + (y >> 2) of the target mask
-        if (word) atomicOr(&s_mask[j * 64 + x * 4 + (((2 * ly) & 15) >> 2)], word);
-      }
-    } else if (op == TC_OP_COARSEN) {
-      lds_mark(s_mask, 0, (mx >> 1) & 15, (my >> 1) & 15, (mz >> 1) & 15);
-    } else {
-      for (int j = 0; j < m; ++j) {
-        const I3 t = box_offset(j, op);
-        if (!spill_nonempty(W, t)) continue;
-        if (!leaf_ok(mx + t.x) || !leaf_ok(my + t.y) || !leaf_ok(mz + t.z)) {
-          set_flag(flags, kFlagOverflow);
-          continue;
+          // children with this qx share the word x*4 + (y >> 2) of the target mask
+          if (word) atomicOr(&s_mask[j * 64 + x * 4 + (((2 * ly) & 15) >> 2)], word);
         }
-        const i64 px = lx + t.x, py = ly + t.y, pz = lz + t.z;  // -1 .. 16
-        lds_mark(s_mask, box_index(px >> 4, py >> 4, pz >> 4, op), px & 15, py & 15, pz & 15);
+      } else {  // coarsen
+        lds_mark(s_mask, 0, (mx >> 1) & 15, (my >> 1) & 15, (mz >> 1) & 15);
       }
     }
   }
   __syncthreads();
-  const int32_t ncand = *d_num_cands;
-  for (int k = threadIdx.x; k < m * 64; k += 256) {
-    const int j = k >> 6, w = k & 63;
+#pragma unroll
+  for (int r = 0; r < kFlush; ++r) {
+    const int k = r * 256 + threadIdx.x;
+    if (k >= m * 64) break;
+    const int w = k & 63;
     const u64 word = s_mask[k];
     if (op != TC_OP_REFINE && !word) continue;
-    const int32_t c = lower_nbr[l * m + j];
+    const int32_t c = nbr[r];
     if (c < 0 || c >= ncand) {
       if (word) set_flag(flags, kFlagInternal);  // a marked target must have a candidate
       continue;

@@ -171,6 +171,9 @@ void* batch_buffer_take(size_t bytes, hipStream_t s, size_t* cap);
 void batch_buffer_give(void* p, size_t cap, int device, hipStream_t s);
 void batch_buffers_release();
 
+// Compute units of the current device (read once per device).
+int device_cu_count();
+
 // Per-thread pinned host staging buffer (grows on demand, never shrinks).
 void* pinned_staging(size_t bytes);
 

@@ -400,9 +400,7 @@ void kernel_map(const GridView& sv, const GridView& tv, int K, int S, int transp
   const size_t lds = 4 * 512 + waves * wave_bytes;
   // one round of resident blocks (LDS and wave slots per CU decide how many);
   // each wave then walks many leaves, so the next leaf's inputs are always in flight
-  int dev = 0, cus = 256;
-  hip_check(hipGetDevice(&dev), "hipGetDevice");
-  hip_check(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev), "hipDeviceGetAttribute");
+  const int cus = device_cu_count();
   const int per_cu = std::max(1, std::min(32 / waves, (int)((160 * 1024) / lds)));
   const i64 blocks = std::min<i64>(ceil_div(tv.n_leaf, waves), (i64)cus * per_cu);
   launch_lds("k_kernel_map", k_kernel_map, blocks, kWave * waves, lds, s, (const int4*)tv.leaf_origin,

@@ -214,6 +214,19 @@ void* pinned_staging(size_t bytes) {
   return p;
 }
 
+// ------------------------------------------------------------------ device facts
+int device_cu_count() {
+  static int cached[64];  // 0 = not read yet (a benign race: every reader stores the same value)
+  int dev = 0;
+  hip_check(hipGetDevice(&dev), "hipGetDevice");
+  if (dev >= 0 && dev < 64 && cached[dev] > 0) return cached[dev];
+  int cus = 0;
+  hip_check(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev), "hipDeviceGetAttribute");
+  if (cus <= 0) cus = 1;
+  if (dev >= 0 && dev < 64) cached[dev] = cus;
+  return cus;
+}
+
 // ------------------------------------------------------------------ voxel-total slots
 namespace {
 constexpr int kVoxChunk = 256;  // slots per pinned allocation, 16 bytes each

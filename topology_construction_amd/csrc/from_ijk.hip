@@ -440,11 +440,16 @@ __global__ void __launch_bounds__(256) k_voxel_leaf(const int32_t* ijk, const in
   table_flush<false>(s_key, s_val);
 }
 
-static int32_t read_i32(const int32_t* d, hipStream_t s) {
+// Two device words read back with one synchronisation. The pinned staging
+// buffer may still be the source of an earlier upload on the stream: the
+// copies into it are ordered after that upload by the stream itself.
+static void read_two_i32(const int32_t* d0, const int32_t* d1, hipStream_t s, int32_t* v0, int32_t* v1) {
   int32_t* h = static_cast<int32_t*>(pinned_staging(64));
-  hip_check(hipMemcpyAsync(h, d, 4, hipMemcpyDeviceToHost, s), "readback");
+  hip_check(hipMemcpyAsync(h, d0, 4, hipMemcpyDeviceToHost, s), "readback");
+  hip_check(hipMemcpyAsync(h + 1, d1, 4, hipMemcpyDeviceToHost, s), "readback");
   hip_check(hipStreamSynchronize(s), "hipStreamSynchronize");
-  return h[0];
+  *v0 = h[0];
+  *v1 = h[1];
 }
 
 tc_grid_batch* build_from_ijk(const int32_t* d_ijk, const int64_t* h_off, int32_t B, const OutAlloc& oa) {
@@ -482,9 +487,9 @@ tc_grid_batch* build_from_ijk(const int32_t* d_ijk, const int64_t* h_off, int32_
   launch("k_hash_tiles", k_hash_tiles, ceil_div(N, kVoxPerBlockWide), 256, s, d_ijk, (const i64*)d_off, B, N, table, H,
          rep, flag, flags);
   scan_excl_i32(flag, excl, N, nullptr, s);
-  hip_check(hipStreamSynchronize(s), "hipStreamSynchronize");  // the pinned offsets are consumed
-  const int32_t nt = read_i32(excl + N, s);
-  if (read_i32(flags, s) & 2) throw Error(TC_ERR_INTERNAL, "from_ijk: tile hash overflow");
+  int32_t nt = 0, hash_flags = 0;
+  read_two_i32(excl + N, flags, s, &nt, &hash_flags);
+  if (hash_flags & 2) throw Error(TC_ERR_INTERNAL, "from_ijk: tile hash overflow");
 
   // stage 2: sort the unique tiles, candidate lowers
   Arena a2(s);
@@ -531,8 +536,9 @@ tc_grid_batch* build_from_ijk(const int32_t* d_ijk, const int64_t* h_off, int32_
   launch("k_voxel_mark_lower", k_voxel_mark_lower, ceil_div(N, kVoxPerBlockWide), 256, s, d_ijk, (const int32_t*)vtile, N,
          ts.tile_child);
   tree_rank_tiles(ts, s);
-  const int32_t nc = read_i32(ts.d_num_cands, s);
-  if (read_i32(flags, s) & 2) throw Error(TC_ERR_INTERNAL, "from_ijk: tile ranking check failed");
+  int32_t nc = 0, rank_flags = 0;
+  read_two_i32(ts.d_num_cands, flags, s, &nc, &rank_flags);
+  if (rank_flags & 2) throw Error(TC_ERR_INTERNAL, "from_ijk: tile ranking check failed");
 
   // stage 3: candidate lowers, leaves, counts
   Arena a3(s);

@@ -1451,7 +1451,7 @@ __device__ __forceinline__ void coarsen_place(u64 out[8], const u64 W[8], const 
 // KIND: 0 refine, 1 coarsen; one instantiation each.
 template <int KIND>
 __global__ void __launch_bounds__(256) k_leaf_gather(const int4* out_origin, const int32_t* leaf_cand, i64 n,
-                                                     int op, int m, int lo, int hi, const int32_t* cand_src,
+                                                     const int32_t* cand_src,
                                                      const u64* src_lower_mask, const uint16_t* src_lower_prefix,
                                                      const int32_t* src_lower_first, const u64* src_leaf_mask,
                                                      int32_t n_src_lower, int32_t n_src_leaf,
@@ -1948,7 +1948,7 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, 
       const i64 lanes = op == TC_OP_REFINE ? 1 : 4;
       auto gather = op == TC_OP_REFINE ? k_leaf_gather<0> : k_leaf_gather<1>;
       launch("k_leaf_gather", gather, ceil_div(L * lanes, 256), 256, s, (const int4*)ov.leaf_origin,
-             (const int32_t*)leaf_cand, L, op, oi.m, oi.lo, oi.hi, (const int32_t*)cand_src,
+             (const int32_t*)leaf_cand, L, (const int32_t*)cand_src,
              (const u64*)sv.lower_mask, (const uint16_t*)sv.lower_prefix, (const int32_t*)sv.lower_first,
              (const u64*)sv.leaf_mask, sv.n_lower, sv.n_leaf, (const int32_t*)ts.d_num_cands, ov.leaf_mask,
              ov.leaf_prefix, post.at<uint32_t>(o_box), leaf_inrun, vox_part, ts.flags);

@@ -198,7 +198,8 @@ int oracle_build(int op, int factor, const int32_t* ijk, const int64_t* offsets,
     case OP_COARSEN: case OP_REFINE: if (!pow2) return ST_INVALID; break;
     case OP_CONV_T_K3S2: if (factor != 2) return ST_INVALID; break;
     case OP_IDENTITY: case OP_DILATE: case OP_PAD_NEG: case OP_PAD_POS:
-      if (factor != 1) return ST_INVALID; break;
+      if (factor != 1) return ST_INVALID;
+      break;
     case OP_CONV_S1: case OP_CONV_T_S1: if (factor < 1 || factor > 8) return ST_INVALID; break;
     default: return ST_INVALID;
   }

@@ -138,6 +138,30 @@ def test_random_sparse_members(op, f):
     _check(op, f, ijk, off, "random")
 
 
+def _many_members(seed, B, max_vox):
+    """B small members (0..max_vox voxels each, about one in eight empty), each a
+    cloud around its own centre spread over +-3000, so that members straddle root
+    tiles and sign changes."""
+    rng = np.random.default_rng(seed)
+    members = []
+    for _ in range(B):
+        k = 0 if rng.random() < 0.125 else int(rng.integers(1, max_vox + 1))
+        c = rng.integers(-3000, 3001, size=3)
+        members.append((c + rng.integers(-12, 13, size=(k, 3))).astype(np.int32))
+    return synth.concat_members(members)
+
+
+@pytest.mark.parametrize("B", [300, 4200])
+def test_many_members(B):
+    """Batches past the per-batch LDS tables: grid voxel begins read from global
+    memory in the enumeration (above 256 members), the multi-launch finalize path
+    (above 1024) and the ijk front end's global member search (above 4095)."""
+    ijk, off = _many_members(900 + B, B, 24)
+    for op, f in [("identity", 1), ("coarsen", 2), ("refine", 2), ("dilate", 1), ("pad_pos", 1),
+                  ("conv_t_k3s2", 2)]:
+        _check(op, f, ijk, off, f"many members B={B}")
+
+
 def test_octant_corners_of_root_tile():
     corners = np.array([(a, b, c) for a in (0, 4095) for b in (0, 4095) for c in (0, 4095)], np.int32)
     across = corners + np.where(corners > 0, 1, -1).astype(np.int32) * np.array([1, 0, 0], np.int32)

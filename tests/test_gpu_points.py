@@ -63,6 +63,21 @@ def test_random_points_and_ties(mode):
     _check(pts, off, vs, org, mode, "random + ties")
 
 
+@pytest.mark.parametrize("mode", [0, 1])
+def test_many_members(mode):
+    """4200 members (about one in eight empty): past the 4095 members whose
+    offsets the front end searches in LDS, so every point's member comes from
+    the search over global memory."""
+    rng = np.random.default_rng(70 + mode)
+    B = 4200
+    members = [rng.uniform(-40, 40, size=(0 if rng.random() < 0.125 else int(rng.integers(1, 25)), 3))
+               .astype(np.float32) for _ in range(B)]
+    pts = np.concatenate(members).astype(np.float32)
+    off = np.concatenate([[0], np.cumsum([m.shape[0] for m in members])]).astype(np.int64)
+    vs, org = _member_params(rng, B)
+    _check(pts, off, vs, org, mode, "many members")
+
+
 def test_errors():
     import torch
     from topology_construction_amd import binding

@@ -586,6 +586,17 @@ __global__ void __launch_bounds__(kFinThreads) k_finalize_small(const int4* leaf
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int32_t base = (int32_t)blockIdx.x * kFinSlice + (tid / kWave) * (kFinPer * kWave);  // this wave's run
+  // block 0 writes the headers at the end: their node fields are loaded now, in
+  // the first round of loads, rather than after the last barrier
+  int32_t hv[kG][6];
+  if (blockIdx.x == 0) {  // uniform
+#pragma unroll
+    for (int k = 0; k < kG; ++k) {
+      const i64 gg = min(tid + k * kFinThreads, B - 1);  // B >= 1
+#pragma unroll
+      for (int f = 0; f < 6; ++f) hv[k][f] = grid_info[gg * 6 + f];
+    }
+  }
   int32_t total = 0;
   if (L > 0) {  // uniform; np >= 1
     i64 pv[kR];
@@ -604,6 +615,11 @@ __global__ void __launch_bounds__(kFinThreads) k_finalize_small(const int4* leaf
       bx[k] = leaf_box[i];
       inr[k] = leaf_inrun[i];
     }
+    // first leaves' in-run counts (a grid without leaves points at the next
+    // grid's first leaf, or at L): issued once gf is in, ahead of the scan
+    int32_t fi[kG];
+#pragma unroll
+    for (int k = 0; k < kG; ++k) fi[k] = leaf_inrun[min(gf[k], L - 1)];
     // run offsets
     int32_t rv[kR];
     int32_t sum = 0;
@@ -624,11 +640,6 @@ __global__ void __launch_bounds__(kFinThreads) k_finalize_small(const int4* leaf
       s_part[tid * kR + k] = ex;
       ex += rv[k];
     }
-    // first leaves' in-run counts (a grid without leaves points at the next
-    // grid's first leaf, or at L)
-    int32_t fi[kG];
-#pragma unroll
-    for (int k = 0; k < kG; ++k) fi[k] = leaf_inrun[min(gf[k], L - 1)];
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < kG; ++k) {
@@ -692,17 +703,19 @@ __global__ void __launch_bounds__(kFinThreads) k_finalize_small(const int4* leaf
     __syncthreads();
   }
   if (blockIdx.x != 0) return;
-  for (int gg = tid; gg < B; gg += kFinThreads) {
-    const int32_t* gi = grid_info + (i64)gg * 6;
+#pragma unroll
+  for (int k = 0; k < kG; ++k) {  // B <= kFinSmallGrids = kG * kFinThreads
+    const int gg = tid + k * kFinThreads;
+    if (gg >= B) break;
     tc_grid_header* h = hdr + gg;
     h->grid_index = gg;
     h->grid_count = B;
-    h->upper_count = gi[0];
-    h->lower_count = gi[1];
-    h->leaf_count = gi[2];
-    h->upper_begin = gi[3];
-    h->lower_begin = gi[4];
-    h->leaf_begin = gi[5];
+    h->upper_count = hv[k][0];
+    h->lower_count = hv[k][1];
+    h->leaf_count = hv[k][2];
+    h->upper_begin = hv[k][3];
+    h->lower_begin = hv[k][4];
+    h->leaf_begin = hv[k][5];
     h->voxel_begin = s_gvb[gg];
     h->voxel_count = s_gvb[gg + 1] - s_gvb[gg];
     if (L == 0) {  // no leaves: no node writer ran and no box was folded

@@ -24,6 +24,14 @@
  *   - Every entry point validates its arguments on the host before any launch.
  *     On any non-TC_OK status, *out is set to NULL, nothing is leaked and
  *     tc_last_error() returns a message for the calling thread.
+ *   - int32 overflow of an output coordinate is detected on the device, by the
+ *     kernels that compute the output nodes, and reported at the pass's one
+ *     readback (TC_ERR_OVERFLOW, no batch), before any output is allocated.
+ *   - The kernels that write a batch's leaf masks check their indices; a failed
+ *     check (a library defect, never an input property) is reported as
+ *     TC_ERR_INTERNAL by the first call that blocks on the batch afterwards
+ *     (tc_batch_voxel_total, tc_batch_read_headers, tc_enumerate_ijk,
+ *     tc_build_kernel_map, or a pass that reads it), and by every later one.
  *   - Calls on different streams or threads are independent. A tc_grid_batch is
  *     immutable after creation and may be read concurrently.
  *   - Coordinates are int32 voxel indices; counts are int32 (nodes) or int64
@@ -79,13 +87,22 @@ typedef enum tc_op {
   TC_OP_CONV_T_S1 = 8
 } tc_op;
 
-/* Caller-supplied device allocator for output grid buffers (one allocation per
- * output batch). `alloc` returns a device pointer usable on `stream`, aligned to
- * at least 256 bytes, or NULL on failure. `free` receives the same pointer and
- * byte count. Both may be called from the thread that calls into the library.
- * Passing a NULL tc_allocator* makes the library use hipMallocAsync/hipFreeAsync
- * on the call's stream. Scratch memory always comes from hipMallocAsync on the
- * call's stream and is released, stream-ordered, before the call returns. */
+/* Caller-supplied device allocator. When an entry point is given one, all the
+ * device memory of that call comes from it: the output batch's buffer (one
+ * allocation per output batch, returned through `free` by tc_batch_free), the
+ * scratch arrays of the passes and the intermediate batches of chained passes.
+ * `alloc` returns a device pointer usable on `stream`, aligned to at least 256
+ * bytes, or NULL on failure (the call then fails with TC_ERR_ALLOC, *out is NULL
+ * and nothing is leaked). `free` receives the same pointer, byte count and
+ * stream. Both are called from the thread that calls into the library (or, for
+ * cached scratch, from the thread of a later call or of tc_scratch_release).
+ * Scratch blocks are not freed at the end of a call: the library caches them
+ * per (device, stream, allocator) and hands them to the next call with the
+ * same key, so a steady stream of passes makes no allocator calls beyond its
+ * outputs; tc_scratch_release returns the idle ones through `free`.
+ * Passing a NULL tc_allocator* makes the library take all of this from the
+ * device's stream-ordered pool (hipMallocAsync on the call's stream), with
+ * the same caching. */
 typedef struct tc_allocator {
   void* (*alloc)(void* ctx, size_t bytes, void* stream);
   void (*free)(void* ctx, void* ptr, size_t bytes, void* stream);
@@ -169,7 +186,7 @@ const char* tc_last_error(void);
  * topologies built from ijk).
  *   d_ijk      int32[N][3] device, N = h_offsets[B]; may be NULL when N = 0.
  *   h_offsets  int64[B+1] host: member g owns rows [h_offsets[g], h_offsets[g+1]);
- *              h_offsets[0] = 0, non-decreasing, N < 2^31.
+ *              h_offsets[0] = 0, non-decreasing. N >= 2^30 is TC_ERR_UNSUPPORTED.
  *   Duplicate rows collapse; row order is irrelevant.
  * Blocks on a few small readbacks. *out is owned by the caller. */
 tc_status tc_batch_from_ijk(const int32_t* d_ijk, const int64_t* h_offsets, int32_t grid_count,
@@ -263,19 +280,30 @@ tc_status tc_build_kernel_map(const tc_grid_batch* src, const tc_grid_batch* dst
                               int32_t stride, int32_t transposed, int32_t* d_out, int64_t capacity,
                               void* stream);
 
-/* Cached device memory: every call takes its scratch arrays from blocks cached
- * per calling thread, device and stream, and keeps them for the next call on
- * the same stream (reuse is ordered by that stream, so none is waited for).
- * Likewise tc_batch_free keeps the buffer of a batch built without an allocator
- * (up to 64 buffers, 4 GiB) for the next batch on the same device and stream.
- * This returns the calling thread's scratch blocks and every cached batch
- * buffer to the device's memory pool, stream-ordered on the streams that used
- * them; later calls allocate again. Fails only with a HIP error. */
+/* Cached device memory: every call takes its scratch arrays (and the buffers
+ * of intermediate batches) from blocks cached process-wide per device, stream
+ * and allocator, and keeps them for the next call with the same key (reuse is
+ * ordered by that stream, so none is waited for). At most 24 idle blocks and
+ * 8 GiB of idle bytes stay cached; beyond that the least recently used are
+ * freed. tc_batch_free likewise keeps the buffer of a batch built without an
+ * allocator (up to 64 buffers, 4 GiB) for the next batch on the same device
+ * and stream. tc_scratch_release synchronizes the device, then frees every idle
+ * scratch block (through its allocator's `free`, or to the device's pool) and
+ * every cached batch buffer; later calls allocate again. Blocks in use by a
+ * concurrent call are kept. Fails only with a HIP error. */
 tc_status tc_scratch_release(void);
 
 /* Releases the batch's device buffer (through the allocator it was created with,
  * stream-ordered on its creation stream) and the handle. NULL is ignored. */
 void tc_batch_free(tc_grid_batch* batch);
+
+/* Testing hook for the TC_ERR_INTERNAL path above: the next batch that the
+ * calling thread builds (from ijk, from points, or as the output or an
+ * intermediate of a pass) behaves as if its leaf-mask writers had flagged
+ * `bits` (1 or 2; 0 cancels). That batch is written normally and its flags are
+ * read back with its voxel total, so the error surfaces where a real one
+ * would. Bits outside [0, 3] are TC_ERR_INVALID_ARG. */
+tc_status tc_debug_inject_flags(int32_t bits);
 
 /* Kernel timing for measurement: while enabled, every launch of a kernel whose
  * name is in `kernel_names` (comma-separated __global__ function names, e.g.

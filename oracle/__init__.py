@@ -81,6 +81,10 @@ def bind(path: str):
     lib.oracle_build.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
                                  ctypes.c_void_p, ctypes.c_int32,
                                  ctypes.POINTER(ctypes.c_void_p)]
+    lib.oracle_build_threaded.restype = ctypes.c_int
+    lib.oracle_build_threaded.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                          ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                          ctypes.POINTER(ctypes.c_void_p)]
     lib.oracle_build_masked_refine.restype = ctypes.c_int
     lib.oracle_build_masked_refine.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                                                ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(ctypes.c_void_p)]
@@ -157,6 +161,39 @@ def run(op, factor: int, ijk: np.ndarray, offsets: np.ndarray, fields=None, lib=
     if st != OK:
         raise OracleError(st)
     return _collect(lib, handle, fields)
+
+
+def run_threaded(op, factor: int, ijk: np.ndarray, offsets: np.ndarray, threads: int = 0, fields=None,
+                 lib=None) -> dict:
+    """As run(), with the members built in parallel by `threads` host threads
+    (0: host_threads()), each as a batch of one, and concatenated in member
+    order (oracle_build_threaded). The per-member arithmetic is run()'s."""
+    lib = lib or _load()
+    threads = int(threads) if threads else host_threads()
+    if isinstance(op, str):
+        op = OP_IDS[op]
+    ijk = np.ascontiguousarray(np.asarray(ijk, dtype=np.int32).reshape(-1, 3))
+    offsets = np.ascontiguousarray(np.asarray(offsets, dtype=np.int64))
+    handle = ctypes.c_void_p()
+    st = lib.oracle_build_threaded(int(op), int(factor), ijk.ctypes.data if ijk.size else None,
+                                   offsets.ctypes.data, int(offsets.shape[0]) - 1, int(threads),
+                                   ctypes.byref(handle))
+    if st != OK:
+        raise OracleError(st)
+    return _collect(lib, handle, fields)
+
+
+def host_threads() -> int:
+    """Host threads for the threaded driver: OMP_NUM_THREADS when set (a machine
+    that shares its cores states this process's share there), else the cores
+    this process may run on."""
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        return int(env)
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except (AttributeError, OSError):  # pragma: no cover
+        return max(1, os.cpu_count() or 1)
 
 
 def member_offsets(result: dict) -> np.ndarray:

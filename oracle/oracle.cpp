@@ -50,10 +50,13 @@
 //   * any output coordinate outside int32 rejects the whole call (status 2).
 #include <algorithm>
 #include <array>
+#include <atomic>
 #include <map>
 #include <cstdint>
 #include <cstring>
 #include <new>
+#include <system_error>
+#include <thread>
 #include <vector>
 
 namespace {
@@ -316,6 +319,106 @@ int oracle_build(int op, int factor, const int32_t* ijk, const int64_t* offsets,
   }
   *out = r;
   return ST_OK;
+}
+
+// Member-parallel driver of oracle_build. Members never interact (every op
+// acts on one member's voxel set), so each member is built on its own, as a
+// batch of one, by `threads` host threads that take members in turn (threads
+// <= 0: one per hardware thread). The per-member results are then concatenated
+// in member order: grid ids and counts are set to the batch's, node indices
+// (first children, parents) and header begins are shifted by the nodes of the
+// members before, and each member's voxels follow the previous members' voxels.
+// The arithmetic per member is oracle_build's own. Same statuses as oracle_build
+// (the lowest member's failure is reported).
+int oracle_build_threaded(int op, int factor, const int32_t* ijk, const int64_t* offsets, int32_t B,
+                          int32_t threads, oracle_result** out) {
+  if (!out) return ST_INVALID;
+  *out = nullptr;
+  if (B < 1 || !offsets || offsets[0] != 0) return ST_INVALID;
+  for (int g = 0; g < B; ++g)
+    if (offsets[g + 1] < offsets[g]) return ST_INVALID;
+  if (offsets[B] > 0 && !ijk) return ST_INVALID;
+  int nt = threads > 0 ? threads : (int)std::thread::hardware_concurrency();
+  if (nt < 1) nt = 1;
+  if (nt > B) nt = B;
+  std::vector<oracle_result*> part((size_t)B, nullptr);
+  std::vector<int> status((size_t)B, ST_OK);
+  std::atomic<int> next{0};
+  auto worker = [&]() {
+    for (;;) {
+      const int g = next.fetch_add(1);
+      if (g >= B) return;
+      const int64_t one[2] = {0, offsets[g + 1] - offsets[g]};
+      status[(size_t)g] = oracle_build(op, factor, one[1] ? ijk + 3 * offsets[g] : nullptr, one, 1, &part[(size_t)g]);
+    }
+  };
+  std::vector<std::thread> pool;
+  try {
+    pool.reserve((size_t)nt);
+    for (int t = 1; t < nt; ++t) pool.emplace_back(worker);
+  } catch (const std::exception&) {  // fewer threads than asked: the started ones and this one finish
+  }
+  worker();
+  for (std::thread& t : pool) t.join();
+  int st = ST_OK;
+  for (int g = 0; g < B && st == ST_OK; ++g) st = status[(size_t)g];
+  oracle_result* r = st == ST_OK ? new (std::nothrow) oracle_result() : nullptr;
+  if (st == ST_OK && !r) st = ST_NOMEM;
+  if (st == ST_OK) {
+    try {
+      r->B = B;
+      i64 nu = 0, n1 = 0, nl = 0, nv = 0;
+      for (int g = 0; g < B; ++g) {
+        const oracle_result& m = *part[(size_t)g];
+        const i64* mh = m.headers.data();
+        r->headers.insert(r->headers.end(), mh, mh + 16);
+        i64* h = &r->headers[r->headers.size() - 16];
+        h[0] = g;
+        h[1] = B;
+        h[5] = nu;
+        h[6] = n1;
+        h[7] = nl;
+        h[9] = nv;
+        for (size_t i = 0; i < m.upper_key.size(); ++i) {
+          r->upper_origin.insert(r->upper_origin.end(), {m.upper_origin[4 * i], m.upper_origin[4 * i + 1],
+                                                         m.upper_origin[4 * i + 2], (int32_t)g});
+          r->upper_first.push_back((int32_t)(m.upper_first[i] + n1));
+        }
+        r->upper_key.insert(r->upper_key.end(), m.upper_key.begin(), m.upper_key.end());
+        r->upper_mask.insert(r->upper_mask.end(), m.upper_mask.begin(), m.upper_mask.end());
+        for (size_t i = 0; i < m.lower_first.size(); ++i) {
+          r->lower_origin.insert(r->lower_origin.end(), {m.lower_origin[4 * i], m.lower_origin[4 * i + 1],
+                                                         m.lower_origin[4 * i + 2],
+                                                         (int32_t)(m.lower_origin[4 * i + 3] + nu)});
+          r->lower_first.push_back((int32_t)(m.lower_first[i] + nl));
+        }
+        r->lower_mask.insert(r->lower_mask.end(), m.lower_mask.begin(), m.lower_mask.end());
+        r->lower_prefix.insert(r->lower_prefix.end(), m.lower_prefix.begin(), m.lower_prefix.end());
+        for (size_t i = 0; i < m.leaf_parent.size(); ++i) {
+          r->leaf_origin.insert(r->leaf_origin.end(), {m.leaf_origin[4 * i], m.leaf_origin[4 * i + 1],
+                                                       m.leaf_origin[4 * i + 2], (int32_t)g});
+          r->leaf_parent.push_back((int32_t)(m.leaf_parent[i] + n1));
+        }
+        r->leaf_mask.insert(r->leaf_mask.end(), m.leaf_mask.begin(), m.leaf_mask.end());
+        r->leaf_prefix.insert(r->leaf_prefix.end(), m.leaf_prefix.begin(), m.leaf_prefix.end());
+        r->leaf_offset.insert(r->leaf_offset.end(), m.leaf_offset.begin(), m.leaf_offset.end());
+        r->ijk.insert(r->ijk.end(), m.ijk.begin(), m.ijk.end());
+        nu += (i64)m.upper_key.size();
+        n1 += (i64)m.lower_first.size();
+        nl += (i64)m.leaf_parent.size();
+        nv += mh[8];
+        delete part[(size_t)g];
+        part[(size_t)g] = nullptr;
+      }
+    } catch (const std::bad_alloc&) {
+      delete r;
+      r = nullptr;
+      st = ST_NOMEM;
+    }
+  }
+  for (oracle_result* m : part) delete m;
+  *out = r;
+  return st;
 }
 
 // Number of elements (not bytes) of a field.

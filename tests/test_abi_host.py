@@ -121,3 +121,10 @@ def test_no_kernel_uses_scratch_memory(tmp_path):
             if seg and int(seg.group(1)) != 0:
                 bad.append((src, m.group(1), int(seg.group(1))))
     assert not bad, bad
+
+
+def test_debug_inject_flags_validates_on_host(lib):
+    assert lib.tc_debug_inject_flags(7) == binding.TC_ERR_INVALID_ARG
+    assert lib.tc_debug_inject_flags(-1) == binding.TC_ERR_INVALID_ARG
+    assert b"bits" in lib.tc_last_error()
+    assert lib.tc_debug_inject_flags(0) == binding.TC_OK  # cancels (nothing armed here)

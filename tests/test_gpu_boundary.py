@@ -1,0 +1,188 @@
+"""The C-ABI boundary on the GPU: the caller's allocator supplies every device
+byte of a call (outputs, scratch, intermediate batches), an allocator that
+fails gives TC_ERR_ALLOC with nothing leaked, the allocator callback takes its
+memory on the call's stream, and a failed consistency check of the writer
+kernels surfaces as TC_ERR_INTERNAL at the first blocking read.
+Sources: PR page "Batched leaf-mask topology construction for generated conv
+grids", section 1 (one buffer is allocated per output batch after the single
+readback), Test plan (elementwise equality with the oracle).
+"""
+import ctypes
+
+import numpy as np
+import pytest
+
+import oracle
+from tests.gpu_util import assert_same, gpu_fields, headers_as_oracle
+from topology_construction_amd import binding, synth
+
+pytestmark = pytest.mark.gpu
+
+
+class CountingAllocator:
+    """tc_allocator over torch tensors that counts live blocks and fails every
+    request from the `fail_from`-th on (1-based; 0 never fails)."""
+
+    def __init__(self, fail_from=0):
+        import torch
+        self.torch = torch
+        self.fail_from = fail_from
+        self.calls = 0
+        self.live = {}
+        self.streams = set()
+        self._a = binding._ALLOC_FN(self._alloc)
+        self._f = binding._FREE_FN(self._free)
+        self.struct = binding.tc_allocator(ctypes.cast(self._a, ctypes.c_void_p),
+                                           ctypes.cast(self._f, ctypes.c_void_p), None)
+
+    def _alloc(self, ctx, nbytes, stream):
+        self.calls += 1
+        self.streams.add(int(stream or 0))
+        if self.fail_from and self.calls >= self.fail_from:
+            return None
+        t = self.torch.empty(max(int(nbytes), 1), dtype=self.torch.uint8, device="cuda")
+        self.live[t.data_ptr()] = t
+        return t.data_ptr()
+
+    def _free(self, ctx, ptr, nbytes, stream):
+        self.live.pop(int(ptr or 0), None)
+
+
+def _build(lib, src, op, f, alloc, stream=0):
+    h = ctypes.c_void_p()
+    st = lib.tc_build_batched_topology(src.handle, binding.OPS[op], f, ctypes.byref(alloc.struct),
+                                       ctypes.c_void_p(stream), ctypes.byref(h))
+    return st, h
+
+
+def _release_all():
+    import torch
+    torch.cuda.synchronize()
+    binding.tc_scratch_release()
+
+
+def test_allocator_supplies_scratch_and_intermediates():
+    """With a caller allocator, a pass and a chained pass draw scratch and their
+    intermediate batch from it (the library's pool is not touched), the result
+    equals the oracle's, and tc_scratch_release returns every scratch block."""
+    import torch
+    lib = binding.load_library()
+    ijk, off = synth.make_config(3)
+    src = binding.tc_batch_from_ijk(torch.from_numpy(ijk).cuda(), off)
+    _release_all()
+    a = CountingAllocator()
+    for op, f in [("dilate", 1), ("refine", 4), ("conv_t_k3s2", 2)]:
+        st, h = _build(lib, src, op, f, a)
+        assert st == binding.TC_OK, lib.tc_last_error()
+        ref = oracle.run_threaded(op, f, ijk, off, fields=["headers", "ijk"])
+        out = binding.GridBatch(h, torch_owned=False)
+        assert np.array_equal(headers_as_oracle(out.headers()), ref["headers"])
+        assert np.array_equal(out.ijk().cpu().numpy(), ref["ijk"])
+        assert len(a.live) >= 2  # the output and at least one cached scratch block
+        del out
+    assert a.calls >= 3
+    _release_all()
+    assert not a.live, f"{len(a.live)} blocks not returned"
+
+
+@pytest.mark.parametrize("fail_from", [1, 2, 3, 4, 5])
+def test_allocator_failure_is_alloc_error_and_leaks_nothing(fail_from):
+    """The allocator fails from its fail_from-th request on (the first is a
+    scratch arena, a later one the output or an intermediate): the call returns
+    TC_ERR_ALLOC with *out NULL, every block it got is returned once the cache
+    is released, and a following pass with a working allocator is correct."""
+    import torch
+    lib = binding.load_library()
+    ijk, off = synth.make_config(2)
+    src = binding.tc_batch_from_ijk(torch.from_numpy(ijk).cuda(), off)
+    _release_all()
+    a = CountingAllocator(fail_from)
+    st, h = _build(lib, src, "refine", 4, a)
+    if st == binding.TC_OK:  # the chain needed fewer requests than fail_from
+        assert a.calls < fail_from
+        binding.GridBatch(h, torch_owned=False).free()
+    else:
+        assert st == binding.TC_ERR_ALLOC, lib.tc_last_error()
+        assert h.value is None
+        assert b"NULL" in lib.tc_last_error()
+    _release_all()
+    assert not a.live, f"{len(a.live)} blocks leaked"
+    ok = CountingAllocator()
+    st, h = _build(lib, src, "refine", 4, ok)
+    assert st == binding.TC_OK
+    out = binding.GridBatch(h, torch_owned=False)
+    ref = oracle.run_threaded("refine", 4, ijk, off, fields=["headers", "ijk"])
+    assert np.array_equal(out.ijk().cpu().numpy(), ref["ijk"])
+    del out
+    _release_all()
+    assert not ok.live
+
+
+def test_allocator_failure_in_from_ijk():
+    import torch
+    lib = binding.load_library()
+    ijk, off = synth.make_config(1)
+    d = torch.from_numpy(ijk).cuda()
+    o = np.ascontiguousarray(off, dtype=np.int64)
+    for fail_from in (1, 2, 3, 4, 6):
+        a = CountingAllocator(fail_from)
+        h = ctypes.c_void_p()
+        st = lib.tc_batch_from_ijk(ctypes.c_void_p(d.data_ptr()), o.ctypes.data, len(off) - 1,
+                                   ctypes.byref(a.struct), None, ctypes.byref(h))
+        if st == binding.TC_OK:
+            binding.GridBatch(h, torch_owned=False).free()
+        else:
+            assert st == binding.TC_ERR_ALLOC and h.value is None
+        _release_all()
+        assert not a.live
+
+
+def test_torch_allocator_uses_the_given_stream():
+    """A pass on a stream that is not torch's current stream: the torch
+    allocator callback takes its memory on that stream, and the result is right."""
+    import torch
+    ijk, off = synth.make_config(3)
+    ref = oracle.run_threaded("dilate", 1, ijk, off)
+    src = binding.tc_batch_from_ijk(torch.from_numpy(ijk).cuda(), off)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    assert torch.cuda.current_stream().cuda_stream != s.cuda_stream
+    binding._stream_objs.pop(s.cuda_stream, None)
+    out = binding.tc_build_batched_topology(src, "dilate", 1, stream=s)
+    assert s.cuda_stream in binding._stream_objs  # allocated under that stream
+    s.synchronize()
+    fo = {k: v.cpu().numpy() for k, v in out.fields().items()}
+    fo["headers"] = headers_as_oracle(out.headers(stream=s))
+    fo["ijk"] = binding.tc_enumerate_ijk(out, stream=s).cpu().numpy()
+    assert_same(fo, ref, "non-current stream")
+
+
+def test_writer_flag_surfaces_as_internal_error():
+    """A batch whose writers flag an inconsistency (forced from the host by the
+    testing hook) is returned, but its first blocking read fails with
+    TC_ERR_INTERNAL, as does every later read and every pass that reads it; in
+    a chain the flagged intermediate fails the call."""
+    import torch
+    ijk, off = synth.make_config(1)
+    src = binding.tc_batch_from_ijk(torch.from_numpy(ijk).cuda(), off)
+    binding.tc_debug_inject_flags(2)
+    bad = binding.tc_build_batched_topology(src, "refine", 2)
+    for read in (bad.voxel_total, bad.headers, bad.ijk, bad.voxel_total):
+        with pytest.raises(binding.TopoError) as e:
+            read()
+        assert e.value.status == binding.TC_ERR_INTERNAL
+    with pytest.raises(binding.TopoError) as e:
+        binding.tc_build_batched_topology(bad, "coarsen", 2)
+    assert e.value.status == binding.TC_ERR_INTERNAL
+    binding.tc_debug_inject_flags(2)  # the first pass of the chain is flagged
+    with pytest.raises(binding.TopoError) as e:
+        binding.tc_build_batched_topology(src, "refine", 4)
+    assert e.value.status == binding.TC_ERR_INTERNAL
+    binding.tc_debug_inject_flags(2)  # a batch from the ijk front-end
+    bad_src = binding.tc_batch_from_ijk(torch.from_numpy(ijk).cuda(), off)
+    with pytest.raises(binding.TopoError) as e:
+        bad_src.voxel_total()
+    assert e.value.status == binding.TC_ERR_INTERNAL
+    # nothing stays armed: the next builds are good
+    good = binding.tc_build_batched_topology(src, "refine", 4)
+    assert_same(gpu_fields(good), oracle.run("refine", 4, ijk, off), "after the flagged builds")

@@ -25,7 +25,7 @@ OPS = [("coarsen", 2), ("refine", 2), ("dilate", 1), ("pad_neg", 1), ("pad_pos",
 
 def _check(op, f, ijk, off, ctx=""):
     print(f"[parity] {ctx} op={op} f={f} B={len(off) - 1} N={int(off[-1])}", flush=True)
-    ref = oracle.run(op, f, ijk, off)
+    ref = oracle.run_threaded(op, f, ijk, off)
     batch, _ = gpu_build(op, f, ijk, off)
     assert_same(gpu_fields(batch), ref, f"{ctx} {op}x{f}")
 
@@ -61,7 +61,7 @@ def test_config2_ops(op, f):
 
 
 @pytest.mark.parametrize("op,f", [("coarsen", 2), ("refine", 2), ("dilate", 1), ("pad_neg", 1), ("pad_pos", 1),
-                                  ("refine", 4)])
+                                  ("refine", 4), ("conv_t_k3s2", 2), ("coarsen", 4)])
 def test_config3_mixed_straddling_empty(op, f):
     ijk, off = synth.make_config(3)
     _check(op, f, ijk, off, "config3")
@@ -293,23 +293,20 @@ def test_pyramid_chain_config4():
     levels = [batch]
     ref_ijk, ref_off = ijk, off
     for lvl in range(3):
-        ref = oracle.run("coarsen", 2, ref_ijk, ref_off)
+        ref = oracle.run_threaded("coarsen", 2, ref_ijk, ref_off)
         nxt = binding.tc_build_batched_topology(levels[-1], "coarsen", 2)
         assert_same(gpu_fields(nxt), ref, f"pyramid coarsen level {lvl + 1}")
         levels.append(nxt)
         ref_ijk, ref_off = ref["ijk"], np.concatenate([[0], np.cumsum(ref["headers"][:, 8])])
     cur = levels[-1]
     for lvl in range(3):
-        ref = oracle.run("conv_t_k3s2", 2, ref_ijk, ref_off)
+        ref = oracle.run_threaded("conv_t_k3s2", 2, ref_ijk, ref_off)
         cur = binding.tc_build_batched_topology(cur, "conv_t_k3s2", 2)
         assert_same(gpu_fields(cur), ref, f"pyramid k3s2T level {lvl + 1}")
         ref_ijk, ref_off = ref["ijk"], np.concatenate([[0], np.cumsum(ref["headers"][:, 8])])
+    # single calls at factors 4 and 8 on every member (refine x8: ~58M voxels)
     for op, f in [("refine", 4), ("refine", 8), ("coarsen", 4), ("coarsen", 8)]:
-        if op == "refine" and f == 8:
-            sub = synth.concat_members([ijk[off[g]:off[g + 1]] for g in range(3)])
-            _check(op, f, sub[0], sub[1], "config4 3 members")
-        else:
-            _check(op, f, ijk, off, "config4")
+        _check(op, f, ijk, off, "config4")
 
 
 def test_null_allocator_path():
@@ -339,7 +336,7 @@ def test_deterministic_bits():
 
 
 def test_scratch_cache_reuse_and_release():
-    """Passes reuse the calling thread's cached scratch blocks; results stay the
+    """Passes reuse the process-wide cached scratch blocks; results stay the
     same when blocks are reused by a different op (stale contents), after they
     are released, and on another stream."""
     import torch

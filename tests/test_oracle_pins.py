@@ -828,3 +828,34 @@ def test_points_invalid_and_overflow():
     big = np.array([[2.0 ** 31 - 128, 0, 0]], np.float32)
     ijk, _ = oracle.points_to_ijk(big, off, np.ones((1, 3), np.float32), np.zeros((1, 3), np.float32), 0)
     assert int(ijk[0, 0]) == 2 ** 31 - 128
+
+
+# ---------------------------------------------------------------- threaded driver
+@pytest.mark.parametrize("cfg,op,f", [(1, op, f) for op, f in [("coarsen", 2), ("refine", 2), ("dilate", 1),
+                                                                  ("conv_t_k3s2", 2), ("refine", 4), ("pad_pos", 1)]]
+                         + [(3, "coarsen", 2), (3, "dilate", 1), (2, "conv_t_k3s2", 2)])
+def test_threaded_driver_equals_serial(cfg, op, f):
+    """The member-parallel driver (members built one by one on several threads,
+    then concatenated with node indices and voxel begins shifted) gives the
+    serial driver's batch, field by field; workload 3 holds empty members first,
+    in the middle and last, and members that straddle root tiles."""
+    ijk, off = synth.make_config(cfg)
+    serial = oracle.run(op, f, ijk, off)
+    for threads in (1, 5):
+        par = oracle.run_threaded(op, f, ijk, off, threads=threads)
+        for name in oracle.FIELDS:
+            assert par[name].dtype == serial[name].dtype and np.array_equal(par[name], serial[name]), (
+                f"{name} differs with {threads} threads")
+
+
+def test_threaded_driver_errors_and_edges():
+    empty = oracle.run_threaded("dilate", 1, np.zeros((0, 3), np.int32), np.zeros(5, np.int64), threads=4)
+    assert empty["ijk"].shape[0] == 0 and np.array_equal(empty["headers"][:, 0], np.arange(4))
+    assert np.all(empty["headers"][:, 1] == 4)
+    with pytest.raises(oracle.OracleError) as e:  # member 1 of 2 overflows: the whole call fails
+        oracle.run_threaded("refine", 2, np.array([[0, 0, 0], [1 << 30, 0, 0]], np.int32),
+                            np.array([0, 1, 2], np.int64), threads=2)
+    assert e.value.status == oracle.OVERFLOW
+    with pytest.raises(oracle.OracleError) as e:
+        oracle.run_threaded("refine", 3, np.zeros((1, 3), np.int32), np.array([0, 1], np.int64))
+    assert e.value.status == oracle.INVALID

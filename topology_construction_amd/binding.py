@@ -28,8 +28,7 @@ ABI_SYMBOLS = [
     "tc_abi_version", "tc_status_string", "tc_last_error", "tc_batch_from_ijk", "tc_batch_from_points",
     "tc_build_batched_topology", "tc_build_masked_refine", "tc_batch_get_info", "tc_batch_read_headers",
     "tc_batch_voxel_total", "tc_enumerate_ijk", "tc_build_kernel_map", "tc_scratch_release", "tc_batch_free",
-    "tc_profile_enable",
-    "tc_profile_read", "tc_profile_disable",
+    "tc_debug_inject_flags", "tc_profile_enable", "tc_profile_read", "tc_profile_disable",
 ]
 
 HEADER_DTYPE = np.dtype([
@@ -134,6 +133,8 @@ def load_library(path: str = LIB_PATH):
         lib.tc_scratch_release.argtypes = []
         lib.tc_batch_free.restype = None
         lib.tc_batch_free.argtypes = [vp]
+        lib.tc_debug_inject_flags.restype = ctypes.c_int
+        lib.tc_debug_inject_flags.argtypes = [i32]
         lib.tc_profile_enable.restype = ctypes.c_int
         lib.tc_profile_enable.argtypes = [ctypes.c_char_p]
         lib.tc_profile_read.restype = ctypes.c_int
@@ -151,21 +152,51 @@ def _check(status: int):
         raise TopoError(status, lib.tc_last_error().decode(errors="replace"))
 
 
+def _current_raw_stream():
+    """torch's current stream as a raw handle (None if torch cannot say cheaply)."""
+    import torch
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    return int(raw(torch._C._cuda_getDevice())) if raw is not None else None
+
+
 def _stream_handle(stream=None):
     import torch
     if stream is not None:
         return ctypes.c_void_p(stream.cuda_stream)
     # the current stream's raw handle without building a Stream object per call
-    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    raw = _current_raw_stream()
     if raw is not None:
-        return ctypes.c_void_p(raw(torch._C._cuda_getDevice()))
+        return ctypes.c_void_p(raw)
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
+_stream_objs: dict = {}  # raw stream handle -> torch stream object wrapping it
+
+
+def _torch_stream(handle: int):
+    """A torch stream object for a raw hipStream_t handle (0: the null stream)."""
+    import torch
+    st = _stream_objs.get(handle)
+    if st is None:
+        st = torch.cuda.default_stream() if handle == 0 else torch.cuda.ExternalStream(handle)
+        _stream_objs[handle] = st
+    return st
+
+
 def _torch_alloc(ctx, nbytes, stream):
+    """Allocator callback: a uint8 tensor from torch's caching allocator, taken
+    on the stream the library will use it on (so that torch hands the block to
+    other work only in that stream's order once it is freed)."""
     try:
         import torch
-        t = torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device="cuda")
+        handle = int(stream or 0)
+        n = max(int(nbytes), 1)
+        cur = _current_raw_stream()
+        if cur is not None and cur == handle:
+            t = torch.empty(n, dtype=torch.uint8, device="cuda")
+        else:
+            with torch.cuda.stream(_torch_stream(handle)):
+                t = torch.empty(n, dtype=torch.uint8, device="cuda")
         p = t.data_ptr()
         _live_buffers[p] = t
         return p
@@ -340,12 +371,18 @@ def tc_build_kernel_map(src: GridBatch, dst: GridBatch, kernel_size: int, stride
 
 
 def tc_scratch_release():
-    """Return the calling thread's cached scratch blocks to the device pool."""
+    """Free every idle cached scratch block and cached batch buffer."""
     _check(load_library().tc_scratch_release())
 
 
 def tc_batch_read_headers(batch: GridBatch, stream=None) -> np.ndarray:
     return batch.headers(stream)
+
+
+def tc_debug_inject_flags(bits: int):
+    """Testing: the next batch built on this thread reports a failed device
+    consistency check of its writers (TC_ERR_INTERNAL at its first blocking read)."""
+    _check(load_library().tc_debug_inject_flags(int(bits)))
 
 
 def tc_profile_enable(kernel_names: str):

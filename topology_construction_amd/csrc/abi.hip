@@ -62,7 +62,10 @@ tc_grid_batch* new_batch(int32_t B, const int32_t* rb, const OutAlloc& oa) {
     b->bytes = b->layout.total;
     b->stream = oa.stream;
     b->device = current_device();
-    if (oa.alloc) {
+    if (oa.transient) {
+      b->block = scratch_acquire(b->bytes, oa.stream);
+      b->buffer = scratch_ptr(b->block);
+    } else if (oa.alloc) {
       b->has_alloc = true;
       b->alloc = *oa.alloc;
       b->buffer = b->alloc.alloc(b->alloc.ctx, b->bytes, (void*)oa.stream);
@@ -102,7 +105,9 @@ tc_grid_batch* copy_batch(const tc_grid_batch* src, const OutAlloc& oa) {
 void free_batch(tc_grid_batch* b) {
   if (!b) return;
   vox_slot_give(b->vox_slot);  // a copy still in flight is waited for by the slot's next taker
-  if (b->buffer) {
+  if (b->block) {
+    scratch_give_back(b->block, b->stream);
+  } else if (b->buffer) {
     if (b->has_alloc) {
       if (b->alloc.free) b->alloc.free(b->alloc.ctx, b->buffer, b->bytes, (void*)b->stream);
     } else {
@@ -115,17 +120,47 @@ void free_batch(tc_grid_batch* b) {
 static_assert(offsetof(tc_grid_header, voxel_begin) == offsetof(tc_grid_header, voxel_count) + 8,
               "voxel count and begin are read back as one 16-byte pair");
 
+static void take_vox_slot(tc_grid_batch* b) {
+  if (b->vox_slot >= 0) return;
+  const VoxTicket t = vox_slot_take(b->device);
+  b->vox_slot = t.slot;
+  b->vox_h = t.h;
+  b->vox_ev = t.ev;
+}
+
+namespace {
+thread_local int32_t t_inject = 0;
+}
+void debug_set_inject(int32_t bits) { t_inject = bits; }
+
+void queue_status(tc_grid_batch* b, const int32_t* d_flags, hipStream_t s) {
+  take_vox_slot(b);
+  if (t_inject) {  // testing: the writers "found" an inconsistency
+    fill_i32(const_cast<int32_t*>(d_flags), t_inject, 1, nullptr, 1, s);
+    t_inject = 0;
+  }
+  b->vox_h[2] = 0;  // the slot's earlier copies have landed (vox_slot_take)
+  hip_check(hipMemcpyAsync(&b->vox_h[2], d_flags, 4, hipMemcpyDeviceToHost, s), "flag readback");
+  hip_check(hipEventRecord(b->vox_ev, s), "hipEventRecord");
+  b->status_pending = true;
+}
+
+void check_status(const tc_grid_batch* b) {
+  if (b->status_pending) {
+    hip_check(hipEventSynchronize(b->vox_ev), "hipEventSynchronize");
+    b->status_pending = false;
+    if ((int32_t)b->vox_h[2] != 0) b->status_bad = true;
+  }
+  if (b->status_bad)
+    throw Error(TC_ERR_INTERNAL, "a device consistency check failed while this batch was written; its arrays are not valid");
+}
+
 // Queues the copy of the last member's voxel count and begin behind the
 // builder's kernels (stream s) and records the slot's event, so that the first
 // request for the total waits for that event instead of a new round trip.
 static void queue_voxel_total(tc_grid_batch* b, hipStream_t s) {
   if (b->vox_known || b->B <= 0) return;
-  if (b->vox_slot < 0) {
-    const VoxTicket t = vox_slot_take(b->device);
-    b->vox_slot = t.slot;
-    b->vox_h = t.h;
-    b->vox_ev = t.ev;
-  }
+  take_vox_slot(b);
   const GridView v = b->view();
   hip_check(hipMemcpyAsync(b->vox_h, &v.headers[b->B - 1].voxel_count, 16, hipMemcpyDeviceToHost, s),
             "voxel total readback");
@@ -146,6 +181,7 @@ static tc_grid_batch* finish_batch(tc_grid_batch* b, hipStream_t s) {
 }
 
 static i64 read_voxel_total(const tc_grid_batch* b, hipStream_t s) {
+  check_status(b);
   if (b->vox_known) return b->vox_total;
   if (b->vox_pending) {
     hip_check(hipEventSynchronize(b->vox_ev), "hipEventSynchronize");
@@ -200,6 +236,7 @@ tc_status tc_batch_from_ijk(const int32_t* d_ijk, const int64_t* h_offsets, int3
   if (allocator && (!allocator->alloc || !allocator->free))
     return fail(TC_ERR_INVALID_ARG, "allocator callbacks are NULL");
   return guarded([&]() {
+    tc::SourceScope scope(allocator);
     *out = tc::finish_batch(
         tc::build_from_ijk(d_ijk, h_offsets, grid_count, tc::OutAlloc{allocator, (hipStream_t)stream}),
         (hipStream_t)stream);
@@ -230,6 +267,7 @@ tc_status tc_batch_from_points(const float* d_xyz, const int64_t* h_offsets, int
   if (allocator && (!allocator->alloc || !allocator->free))
     return fail(TC_ERR_INVALID_ARG, "allocator callbacks are NULL");
   return guarded([&]() {
+    tc::SourceScope scope(allocator);
     *out = tc::finish_batch(tc::build_from_points(d_xyz, h_offsets, grid_count, h_voxel_size, h_origin, mode,
                                                   tc::OutAlloc{allocator, (hipStream_t)stream}),
                             (hipStream_t)stream);
@@ -282,6 +320,7 @@ tc_status tc_build_batched_topology(const tc_grid_batch* src, int32_t op, int32_
   }
   return guarded([&]() {
     if (current_device() != src->device) throw tc::Error(TC_ERR_INVALID_ARG, "src lives on another device");
+    tc::SourceScope scope(allocator);
     hipStream_t s = (hipStream_t)stream;
     if (passes.empty()) {  // kernel size 1: the target is the source
       *out = tc::finish_batch(tc::copy_batch(src, tc::OutAlloc{allocator, s}), s);
@@ -292,7 +331,7 @@ tc_status tc_build_batched_topology(const tc_grid_batch* src, int32_t op, int32_
     try {
       for (size_t p = 0; p < passes.size(); ++p) {
         const bool last = p + 1 == passes.size();
-        tc_grid_batch* next = tc::build_pass(cur, passes[p], tc::OutAlloc{last ? allocator : nullptr, s});
+        tc_grid_batch* next = tc::build_pass(cur, passes[p], tc::OutAlloc{allocator, s, !last});
         tc::free_batch(owned);
         owned = next;
         cur = next;
@@ -317,6 +356,7 @@ tc_status tc_build_masked_refine(const tc_grid_batch* src, const uint8_t* d_keep
     return fail(factor < 2 ? TC_ERR_INVALID_ARG : TC_ERR_UNSUPPORTED, "refine factor must be 2, 4 or 8");
   return guarded([&]() {
     if (current_device() != src->device) throw tc::Error(TC_ERR_INVALID_ARG, "src lives on another device");
+    tc::SourceScope scope(allocator);
     hipStream_t s = (hipStream_t)stream;
     const int64_t total = tc::read_voxel_total(src, s);
     if (n_keep != total)
@@ -339,7 +379,7 @@ tc_status tc_build_masked_refine(const tc_grid_batch* src, const uint8_t* d_keep
     try {
       for (int p = 0; p < npass; ++p) {
         const bool last = p + 1 == npass;
-        tc_grid_batch* next = tc::build_pass(cur, TC_OP_REFINE, tc::OutAlloc{last ? allocator : nullptr, s},
+        tc_grid_batch* next = tc::build_pass(cur, TC_OP_REFINE, tc::OutAlloc{allocator, s, !last},
                                              p == 0 ? masked : nullptr);
         if (p == 0) {
           int32_t* h = static_cast<int32_t*>(tc::pinned_staging(64));
@@ -395,6 +435,7 @@ tc_status tc_batch_get_info(const tc_grid_batch* b, tc_batch_info* out) {
 tc_status tc_batch_read_headers(const tc_grid_batch* b, tc_grid_header* h_out, void* stream) {
   if (!b || !h_out) return fail(TC_ERR_INVALID_ARG, "NULL argument");
   return guarded([&]() {
+    tc::check_status(b);
     const size_t bytes = sizeof(tc_grid_header) * (size_t)b->B;
     void* h = tc::pinned_staging(bytes);
     hipStream_t s = (hipStream_t)stream;
@@ -469,6 +510,12 @@ void tc_batch_free(tc_grid_batch* b) {
     tc::free_batch(b);
   } catch (...) {
   }
+}
+
+tc_status tc_debug_inject_flags(int32_t bits) {
+  if (bits < 0 || bits > 3) return fail(TC_ERR_INVALID_ARG, "bits must be in [0, 3]");
+  tc::debug_set_inject(bits);
+  return TC_OK;
 }
 
 tc_status tc_profile_enable(const char* kernel_names) {

@@ -386,7 +386,8 @@ __global__ void __launch_bounds__(256) k_voxel_cand(const int32_t* ijk, const in
 
 __global__ void __launch_bounds__(256) k_voxel_leaf(const int32_t* ijk, const int32_t* vcand, i64 n,
                                                     const u64* cand_child, const uint16_t* cand_prefix,
-                                                    const i64* cand_scan, i64 n_leaf, u64* leaf_mask) {
+                                                    const i64* cand_scan, i64 n_leaf, u64* leaf_mask,
+                                                    int32_t* flags) {
   constexpr int V = kVoxPerLane;
   __shared__ unsigned long long s_key[kBlockTable], s_val[kBlockTable];
   table_clear(s_key, s_val);
@@ -402,6 +403,9 @@ __global__ void __launch_bounds__(256) k_voxel_leaf(const int32_t* ijk, const in
     z[v] = in ? ijk[i * 3 + 2] : 0;
     ok[v] = in && c[v] >= 0;
   }
+  bool bad = false;
+#pragma unroll
+  for (int v = 0; v < V; ++v) bad |= (vox_index<V>(v) < n) && !ok[v];  // every voxel has its candidate lower
   int w[V], b[V];
   i64 sc[V];
   uint16_t pre[V];
@@ -426,6 +430,7 @@ __global__ void __launch_bounds__(256) k_voxel_leaf(const int32_t* ijk, const in
       const i64 leaf = (i64)(sc[v] & 0xffffffffll) + pre[v] + popc64(cw[v] & ((1ull << b[v]) - 1));
       if (leaf < 0 || leaf >= n_leaf) {  // consistency guard
         ok[v] = false;
+        bad = true;
       } else {
         word[v] = &leaf_mask[leaf * 8 + (x[v] & 7)];
         bits[v] = 1ull << ((y[v] & 7) * 8 + (z[v] & 7));
@@ -433,6 +438,7 @@ __global__ void __launch_bounds__(256) k_voxel_leaf(const int32_t* ijk, const in
     }
   }
   __syncthreads();  // the cleared table
+  if (bad) atomicOr(flags, 2);
 #pragma unroll
   for (int v = 0; v < V; ++v)
     if (ok[v]) table_or(s_key, s_val, word[v], bits[v]);
@@ -589,10 +595,11 @@ tc_grid_batch* build_from_ijk(const int32_t* d_ijk, const int64_t* h_off, int32_
     fill_u64(ov.leaf_mask, 0, 8 * L, nullptr, 1, s);
     launch("k_voxel_leaf", k_voxel_leaf, ceil_div(N, kVoxPerBlock), 256, s, d_ijk, (const int32_t*)vcand, N,
            (const u64*)ts.cand_child, (const uint16_t*)ts.cand_prefix, (const i64*)ts.cand_scan, L,
-           ov.leaf_mask);
+           ov.leaf_mask, ts.flags);
     tree_leaf_stats(ov, post.at<uint32_t>(o_box), post.at<int32_t>(o_inrun), post.at<i64>(o_part), s);
     tree_finalize_leaves(ov, post.at<uint32_t>(o_box), post.at<int32_t>(o_inrun), post.at<i64>(o_part), 256,
                          post.at<i64>(o_gvb), post.at<int32_t>(o_bb), (const int32_t*)ts.grid_info, s);
+    queue_status(out, ts.flags, s);  // k_voxel_leaf's consistency checks ran after the readback
   } catch (...) {
     free_batch(out);
     throw;

@@ -128,9 +128,35 @@ inline GridView make_view(void* buffer, const Layout& L, int32_t B, int32_t n2, 
 }
 
 // ------------------------------------------------------------------ host-side memory
+// Where a call's device memory comes from: the allocator given to its entry
+// point, or (NULL) the device's stream-ordered pool. Set for the calling thread
+// for the duration of the scope; arenas and intermediate batches use it.
+class SourceScope {
+ public:
+  explicit SourceScope(const tc_allocator* a);
+  ~SourceScope();
+  SourceScope(const SourceScope&) = delete;
+  SourceScope& operator=(const SourceScope&) = delete;
+
+ private:
+  tc_allocator prev_;
+  bool prev_set_;
+};
+
+// Scratch blocks cached per (device, stream, source), process-wide: a block is
+// taken by one arena (or one intermediate batch) at a time and given back
+// without being freed, so reuse is ordered by its stream. scratch_release_all()
+// frees every idle block (after a device synchronisation).
+struct ScratchBlock;
+ScratchBlock* scratch_acquire(size_t bytes, hipStream_t s);
+void scratch_give_back(ScratchBlock* b, hipStream_t s);
+char* scratch_ptr(const ScratchBlock* b);
+void scratch_release_all();
+size_t scratch_cached_bytes();
+
 // Scratch arena: one block carved into 256-byte aligned arrays. The block comes
-// from the calling thread's scratch cache (below) and returns to it when the
-// arena is destroyed.
+// from the scratch cache (current source) and returns to it when the arena is
+// destroyed.
 class Arena {
  public:
   explicit Arena(hipStream_t s) : stream_(s) {}
@@ -153,17 +179,8 @@ class Arena {
   hipStream_t stream_;
   char* base_ = nullptr;
   size_t size_ = 0;
-  int slot_ = -1;
+  ScratchBlock* block_ = nullptr;
 };
-
-// Scratch blocks cached per calling thread, device and stream: an arena takes
-// an idle block of its stream that is large enough (or replaces the largest
-// idle one), and gives it back when destroyed, without freeing it. Reuse is
-// ordered by the stream itself, so no event is needed. scratch_release_all()
-// frees the calling thread's idle blocks (stream-ordered).
-int scratch_acquire(size_t bytes, hipStream_t s, char** p);
-void scratch_give_back(int slot);
-void scratch_release_all();
 
 // Buffers of batches built without an allocator, cached per device and stream
 // between tc_batch_free and the next batch that fits (capacity in *cap).
@@ -177,9 +194,11 @@ int device_cu_count();
 // Per-thread pinned host staging buffer (grows on demand, never shrinks).
 void* pinned_staging(size_t bytes);
 
-// Pinned 16-byte host slots, each with an event, for the voxel total of a batch:
-// the copy is queued behind a builder's last kernel and read when first asked.
-// Slots belong to a device; taking one waits for its previous copy to land.
+// Pinned 32-byte host slots, each with an event, for the voxel total of a batch
+// (words 0 and 1: the last grid's voxel count and begin) and the device flags
+// its writer kernels left (word 2): the copies are queued behind a builder's
+// last kernel and read when first asked. Slots belong to a device; taking one
+// waits for its previous copies to land.
 struct VoxTicket {
   int slot;
   int64_t* h;
@@ -306,9 +325,14 @@ void tree_enumerate(const GridView& v, int32_t* ijk, hipStream_t s);
 
 // Allocation of the single output buffer of a batch.
 struct OutAlloc {
-  const tc_allocator* alloc;  // NULL: hipMallocAsync
+  const tc_allocator* alloc;  // NULL: the library's own (hipMallocAsync, cached)
   hipStream_t stream;
+  bool transient = false;     // an intermediate batch of a chain: a scratch block of the call's source
 };
+
+// Testing: bits that the next batch built on the calling thread ORs into its
+// writers' device flag word (tc_debug_inject_flags).
+void debug_set_inject(int32_t bits);
 
 void prof_enable(const char* name);
 void prof_read(const char* name, double* ms, int64_t* n);
@@ -326,12 +350,16 @@ struct tc_grid_batch {
   tc::Layout layout{};
   bool has_alloc = false;
   tc_allocator alloc{};
+  tc::ScratchBlock* block = nullptr;  // the buffer of an intermediate batch (scratch cache)
   hipStream_t stream = nullptr;
   int device = 0;
   mutable bool vox_known = false;
   mutable int64_t vox_total = 0;
-  // voxel total queued for readback (queue_voxel_total): slot, host words, event
+  // voxel total and writer flags queued for readback (queue_status,
+  // queue_voxel_total): slot, host words, event
   mutable bool vox_pending = false;
+  mutable bool status_pending = false;
+  mutable bool status_bad = false;  // a writer kernel's device consistency check failed
   mutable int vox_slot = -1;
   mutable int64_t* vox_h = nullptr;
   mutable hipEvent_t vox_ev = nullptr;
@@ -347,6 +375,12 @@ namespace tc {
 tc_grid_batch* new_batch(int32_t B, const int32_t* readback, const OutAlloc& oa);
 void free_batch(tc_grid_batch* b);
 tc_grid_batch* copy_batch(const tc_grid_batch* src, const OutAlloc& oa);  // same counts, one D2D copy
+// Queues the copy of the device flag word that a builder's writer kernels set
+// (after its last writer, on stream s) into the batch's pinned slot.
+void queue_status(tc_grid_batch* b, const int32_t* d_flags, hipStream_t s);
+// Throws TC_ERR_INTERNAL when the batch's writers flagged a failed consistency
+// check (waits for the queued flag copy the first time).
+void check_status(const tc_grid_batch* b);
 // Kernel map of `dst` against `src` (same member count): out int32[V_dst][K^3],
 // `entries` = V_dst * K^3.
 void kernel_map(const GridView& src, const GridView& dst, int K, int S, int transposed, int32_t* out, i64 entries,

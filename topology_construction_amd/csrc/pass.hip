@@ -12,11 +12,18 @@
 //           the (grid, tile) keys and a head-flag scan give the unique tiles;
 //   lowers  each source lower sets its candidate target lowers in the target
 //           tile's 32^3 mask; ranks in those masks number the candidates;
-//   leaves  each source leaf sets the bit of every non-empty target leaf in the
-//           target lower's 16^3 mask (pass A, scatter, one atomic OR per target);
+//   leaves  every non-empty target leaf gets its bit in its target lower's 16^3
+//           mask: refine and coarsen from the source side (one workgroup per
+//           source lower marks its leaves' targets in LDS copies of the target
+//           lowers' masks); the box ops from the target side (one workgroup per
+//           candidate lower collects the facing source leaves of its <= 27
+//           source lowers and ORs their reach into an LDS mask), no device
+//           atomics on masks in either case;
 //   counts  popcounts and scans give per-grid counts -> the single readback;
 //   writers node records, then every output leaf gathers its mask from the
-//           (at most 1 / 8 / 27) source leaves that feed it (pass B, no atomics).
+//           (at most 1 / 8 / 27) source leaves that feed it (no atomics); a
+//           consistency check that fails there sets a flag word that is read
+//           back with the batch's voxel total.
 #include "device.hpp"
 #include "internal.hpp"
 
@@ -1922,6 +1929,7 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, 
   int32_t* h_rb = static_cast<int32_t*>(pinned_staging(rb_bytes));
   hip_check(hipMemcpyAsync(h_rb, ts.readback, rb_bytes, hipMemcpyDeviceToHost, s), "readback");
   hip_check(hipStreamSynchronize(s), "hipStreamSynchronize");
+  check_status(src);  // its writers' flags were queued before this pass on the stream
   if (h_rb[0] & kFlagOverflow) throw Error(TC_ERR_OVERFLOW, "an output voxel coordinate leaves int32");
   if (h_rb[0] & kFlagInternal) throw Error(TC_ERR_INTERNAL, "pass: device consistency check failed");
 
@@ -1963,6 +1971,9 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, 
     }
     tree_finalize_leaves(ov, post.at<uint32_t>(o_box), leaf_inrun, vox_part, gran, post.at<i64>(o_gvb),
                          post.at<int32_t>(o_bb), (const int32_t*)ts.grid_info, s);
+    // the gathers' consistency checks set bits in the flag word after the
+    // readback: it goes back with the batch's voxel total
+    queue_status(out, ts.flags, s);
   } catch (...) {
     free_batch(out);
     throw;

@@ -170,17 +170,16 @@ static void scan_excl(const char* tag, const T* in, T* out, i64 n_host, const in
     return;
   }
   const i64 nblk = ceil_div(n_host, kScanTile);
-  const bool own = tmp == nullptr;
-  T* partial = static_cast<T*>(own ? device_alloc_async(sizeof(T) * (size_t)nblk, s) : tmp);
-  try {
-    launch("k_scan_reduce", k_scan_reduce<T>, nblk, kScanThreads, s, in, partial, n_host, d_n);
-    launch("k_scan_partials", k_scan_partials<T>, 1, kScanThreads, s, partial, nblk, out, n_host, d_n, total_out);
-    launch("k_scan_down", k_scan_down<T>, nblk, kScanThreads, s, in, out, (const T*)partial, n_host, d_n);
-  } catch (...) {
-    if (own) device_free_async(partial, s);
-    throw;
+  Arena a(s);  // used only when the caller brings no scratch
+  T* partial = static_cast<T*>(tmp);
+  if (!partial) {
+    const size_t o = a.reserve(sizeof(T) * (size_t)nblk);
+    a.commit();
+    partial = a.at<T>(o);
   }
-  if (own) device_free_async(partial, s);
+  launch("k_scan_reduce", k_scan_reduce<T>, nblk, kScanThreads, s, in, partial, n_host, d_n);
+  launch("k_scan_partials", k_scan_partials<T>, 1, kScanThreads, s, partial, nblk, out, n_host, d_n, total_out);
+  launch("k_scan_down", k_scan_down<T>, nblk, kScanThreads, s, in, out, (const T*)partial, n_host, d_n);
 }
 
 void scan_excl_i32(const int32_t* in, int32_t* out, i64 n_host, const int32_t* d_n, hipStream_t s,

@@ -1,5 +1,6 @@
 // Host runtime helpers: stream-ordered scratch memory, pinned staging buffers,
 // kernel timing with HIP events.
+#include <algorithm>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -43,61 +44,197 @@ void device_free_async(void* p, hipStream_t s) {
   if (p) (void)hipFreeAsync(p, s);
 }
 
+// ------------------------------------------------------------------ memory sources
+// The device memory of a call (scratch arenas, intermediate batches of chained
+// passes) comes from the allocator its entry point was given, or from the
+// device's stream-ordered pool when it was given none. The entry point names
+// the source for its thread with a SourceScope.
 namespace {
-struct ScratchSlot {
+thread_local tc_allocator t_src{};
+thread_local bool t_src_set = false;
+
+bool same_source(const tc_allocator& a, bool a_set, const tc_allocator& b, bool b_set) {
+  if (a_set != b_set) return false;
+  return !a_set || (a.alloc == b.alloc && a.free == b.free && a.ctx == b.ctx);
+}
+}  // namespace
+
+SourceScope::SourceScope(const tc_allocator* a) : prev_(t_src), prev_set_(t_src_set) {
+  t_src_set = a != nullptr;
+  t_src = a ? *a : tc_allocator{};
+}
+SourceScope::~SourceScope() {
+  t_src = prev_;
+  t_src_set = prev_set_;
+}
+
+// ------------------------------------------------------------------ scratch cache
+// Process-wide cache of scratch blocks keyed by (device, stream, source). An
+// arena takes the smallest idle block of its key that fits, else replaces the
+// largest idle block of its key (or adds one), and marks it busy until it is
+// given back; nothing is freed on the per-call path, and reuse is ordered by
+// the stream itself. Idle blocks beyond kIdleBlocks, or beyond kIdleBytes in
+// total, are freed oldest first (after a device synchronisation when they
+// belong to another stream, which may since have been destroyed).
+struct ScratchBlock {
   int device;
   hipStream_t stream;
+  tc_allocator src;
+  bool src_set;
   char* p;
   size_t bytes;
   bool busy;
+  uint64_t stamp;
 };
-thread_local std::vector<ScratchSlot> t_scratch;
-}  // namespace
 
-int scratch_acquire(size_t bytes, hipStream_t s, char** p) {
-  int dev = 0;
-  hip_check(hipGetDevice(&dev), "hipGetDevice");
-  int fit = -1, idle = -1;
-  for (int i = 0; i < (int)t_scratch.size(); ++i) {
-    const ScratchSlot& z = t_scratch[i];
-    if (z.busy || z.device != dev || z.stream != s) continue;
-    if (z.bytes >= bytes && (fit < 0 || z.bytes < t_scratch[fit].bytes)) fit = i;
-    if (idle < 0 || z.bytes > t_scratch[idle].bytes) idle = i;
+namespace {
+constexpr size_t kIdleBlocks = 24;
+constexpr size_t kIdleBytes = size_t(8) << 30;
+
+struct ScratchCache {
+  std::mutex mu;
+  std::vector<ScratchBlock*> blocks;  // stable addresses: arenas hold the pointer
+  uint64_t clock = 0;
+};
+ScratchCache& scratch_cache() {
+  static ScratchCache* c = new ScratchCache();  // never destroyed: no frees during process teardown
+  return *c;
+}
+
+char* source_alloc(const tc_allocator& src, bool src_set, size_t bytes, hipStream_t s) {
+  if (!src_set) return static_cast<char*>(device_alloc_async(bytes, s));
+  void* p = src.alloc(src.ctx, bytes, (void*)s);
+  if (!p) throw Error(TC_ERR_ALLOC, "allocator returned NULL for " + std::to_string(bytes) + " bytes of scratch");
+  return static_cast<char*>(p);
+}
+
+// Frees a block that no queued work uses any more on `s` (its own stream) or
+// anywhere (synced = true after a device synchronisation).
+void block_free(ScratchBlock* b, hipStream_t s, bool synced) {
+  if (!b->p) return;
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return;
+  if (b->device != cur && hipSetDevice(b->device) != hipSuccess) return;
+  if (b->src_set) {
+    b->src.free(b->src.ctx, b->p, b->bytes, (void*)b->stream);
+  } else {
+    device_free_async(b->p, synced ? nullptr : s);
   }
-  if (fit < 0) {
-    // grow: replace the largest idle block of this stream, or add one
-    const size_t want = bytes + bytes / 4 + 4096;
-    char* np = static_cast<char*>(device_alloc_async(want, s));
-    if (idle >= 0) {
-      if (t_scratch[idle].p) device_free_async(t_scratch[idle].p, s);
-      t_scratch[idle].p = np;
-      t_scratch[idle].bytes = want;
-      fit = idle;
-    } else {
-      t_scratch.push_back(ScratchSlot{dev, s, np, want, false});
-      fit = (int)t_scratch.size() - 1;
+  if (b->device != cur) (void)hipSetDevice(cur);
+  b->p = nullptr;
+  b->bytes = 0;
+}
+
+// Drops idle blocks beyond the cache limits (caller holds no lock).
+void scratch_trim(hipStream_t s) {
+  ScratchCache& c = scratch_cache();
+  std::vector<ScratchBlock*> drop;
+  {
+    std::lock_guard<std::mutex> lk(c.mu);
+    for (;;) {
+      size_t idle = 0, idle_bytes = 0;
+      ScratchBlock* oldest = nullptr;
+      for (ScratchBlock* b : c.blocks)
+        if (!b->busy) {
+          ++idle;
+          idle_bytes += b->bytes;
+          if (!oldest || b->stamp < oldest->stamp) oldest = b;
+        }
+      if (!oldest || (idle <= kIdleBlocks && idle_bytes <= kIdleBytes)) break;
+      c.blocks.erase(std::find(c.blocks.begin(), c.blocks.end(), oldest));
+      drop.push_back(oldest);
     }
   }
-  t_scratch[fit].busy = true;
-  *p = t_scratch[fit].p;
-  return fit;
+  bool synced = false;
+  for (ScratchBlock* b : drop) {
+    if (b->stream != s && !synced) synced = hipDeviceSynchronize() == hipSuccess;
+    block_free(b, s, b->stream != s);
+    delete b;
+  }
+}
+}  // namespace
+
+ScratchBlock* scratch_acquire(size_t bytes, hipStream_t s) {
+  int dev = 0;
+  hip_check(hipGetDevice(&dev), "hipGetDevice");
+  ScratchCache& c = scratch_cache();
+  ScratchBlock* fit = nullptr;
+  ScratchBlock* victim = nullptr;
+  {
+    std::lock_guard<std::mutex> lk(c.mu);
+    for (ScratchBlock* b : c.blocks) {
+      if (b->busy || b->device != dev || b->stream != s || !same_source(b->src, b->src_set, t_src, t_src_set))
+        continue;
+      if (b->bytes >= bytes && (!fit || b->bytes < fit->bytes)) fit = b;
+      if (!victim || b->bytes > victim->bytes) victim = b;
+    }
+    if (fit) {
+      fit->busy = true;
+      fit->stamp = ++c.clock;
+      return fit;
+    }
+    if (victim) victim->busy = true;  // replaced below, outside the lock (callbacks may be slow)
+  }
+  // grow: a new block a quarter larger than asked, in place of the largest idle one
+  const size_t want = bytes + bytes / 4 + 4096;
+  if (victim) block_free(victim, s, false);
+  char* p = nullptr;
+  try {
+    p = source_alloc(t_src, t_src_set, want, s);
+  } catch (...) {
+    if (victim) {
+      std::lock_guard<std::mutex> lk(c.mu);
+      c.blocks.erase(std::find(c.blocks.begin(), c.blocks.end(), victim));
+      delete victim;
+    }
+    throw;
+  }
+  std::lock_guard<std::mutex> lk(c.mu);
+  ScratchBlock* b = victim;
+  if (!b) {
+    b = new ScratchBlock();
+    c.blocks.push_back(b);
+  }
+  *b = ScratchBlock{dev, s, t_src, t_src_set, p, want, true, ++c.clock};
+  return b;
 }
 
-void scratch_give_back(int slot) {
-  if (slot >= 0 && slot < (int)t_scratch.size()) t_scratch[slot].busy = false;
+void scratch_give_back(ScratchBlock* b, hipStream_t s) {
+  if (!b) return;
+  {
+    ScratchCache& c = scratch_cache();
+    std::lock_guard<std::mutex> lk(c.mu);
+    b->busy = false;
+    b->stamp = ++c.clock;
+  }
+  scratch_trim(s);
 }
+
+char* scratch_ptr(const ScratchBlock* b) { return b ? b->p : nullptr; }
 
 void scratch_release_all() {
-  int cur = 0;
-  hip_check(hipGetDevice(&cur), "hipGetDevice");
-  for (ScratchSlot& z : t_scratch) {  // slots keep their indices (busy ones belong to live arenas)
-    if (z.busy || !z.p) continue;
-    if (z.device != cur) hip_check(hipSetDevice(z.device), "hipSetDevice");
-    device_free_async(z.p, z.stream);
-    if (z.device != cur) hip_check(hipSetDevice(cur), "hipSetDevice");
-    z.p = nullptr;
-    z.bytes = 0;
+  ScratchCache& c = scratch_cache();
+  std::vector<ScratchBlock*> drop;
+  {
+    std::lock_guard<std::mutex> lk(c.mu);
+    std::vector<ScratchBlock*> keep;
+    for (ScratchBlock* b : c.blocks) (b->busy ? keep : drop).push_back(b);
+    c.blocks.swap(keep);
   }
+  if (drop.empty()) return;
+  hip_check(hipDeviceSynchronize(), "hipDeviceSynchronize");
+  for (ScratchBlock* b : drop) {
+    block_free(b, nullptr, true);
+    delete b;
+  }
+}
+
+size_t scratch_cached_bytes() {
+  ScratchCache& c = scratch_cache();
+  std::lock_guard<std::mutex> lk(c.mu);
+  size_t n = 0;
+  for (const ScratchBlock* b : c.blocks) n += b->bytes;
+  return n;
 }
 
 // ------------------------------------------------------------------ batch buffers
@@ -182,13 +319,14 @@ void batch_buffers_release() {
 
 void Arena::commit() {
   if (base_) throw Error(TC_ERR_INTERNAL, "arena committed twice");
-  slot_ = scratch_acquire(size_, stream_, &base_);
+  block_ = scratch_acquire(size_, stream_);
+  base_ = scratch_ptr(block_);
 }
 
 void Arena::release() {
-  if (base_) scratch_give_back(slot_);
+  if (block_) scratch_give_back(block_, stream_);
   base_ = nullptr;
-  slot_ = -1;
+  block_ = nullptr;
 }
 
 // ------------------------------------------------------------------ pinned staging
@@ -229,7 +367,7 @@ int device_cu_count() {
 
 // ------------------------------------------------------------------ voxel-total slots
 namespace {
-constexpr int kVoxChunk = 256;  // slots per pinned allocation, 16 bytes each
+constexpr int kVoxChunk = 256;  // slots per pinned allocation, 32 bytes each
 struct VoxSlot {
   int64_t* h;
   hipEvent_t ev;
@@ -261,10 +399,10 @@ VoxTicket vox_slot_take(int device) {
     }
     if (t.slot < 0) {
       void* h = nullptr;
-      hip_check(hipHostMalloc(&h, 16 * kVoxChunk, hipHostMallocDefault), "hipHostMalloc");
+      hip_check(hipHostMalloc(&h, 32 * kVoxChunk, hipHostMallocDefault), "hipHostMalloc");
       const int base = (int)p.slots.size();
       for (int k = 0; k < kVoxChunk; ++k) {
-        p.slots.push_back(VoxSlot{static_cast<int64_t*>(h) + 2 * k, nullptr, device});
+        p.slots.push_back(VoxSlot{static_cast<int64_t*>(h) + 4 * k, nullptr, device});
         if (k) p.idle.push_back(base + k);
       }
       t.slot = base;

@@ -132,37 +132,41 @@ namespace {
 thread_local int32_t t_inject = 0;
 }
 void debug_set_inject(int32_t bits) { t_inject = bits; }
+void apply_debug_inject(int32_t* d_flags, hipStream_t s) {
+  if (!t_inject) return;
+  fill_i32(d_flags, t_inject, 1, nullptr, 1, s);  // testing: the writers "found" an inconsistency
+  t_inject = 0;
+}
 
-void queue_status(tc_grid_batch* b, const int32_t* d_flags, hipStream_t s) {
-  take_vox_slot(b);
-  if (t_inject) {  // testing: the writers "found" an inconsistency
-    fill_i32(const_cast<int32_t*>(d_flags), t_inject, 1, nullptr, 1, s);
-    t_inject = 0;
-  }
-  b->vox_h[2] = 0;  // the slot's earlier copies have landed (vox_slot_take)
-  hip_check(hipMemcpyAsync(&b->vox_h[2], d_flags, 4, hipMemcpyDeviceToHost, s), "flag readback");
-  hip_check(hipEventRecord(b->vox_ev, s), "hipEventRecord");
-  b->status_pending = true;
+// The last header's tail (voxel count and begin, bbox, reserved) and the status
+// word after it are one contiguous 64-byte range, read back in one copy.
+static_assert(sizeof(tc_grid_header) - offsetof(tc_grid_header, voxel_count) == 48, "header tail layout");
+constexpr int kStatusWord = 6;  // int64 index of the status word in a 64-byte slot
+
+static void apply_status(const tc_grid_batch* b) {
+  if ((int32_t)b->vox_h[kStatusWord] != 0) b->status_bad = true;
 }
 
 void check_status(const tc_grid_batch* b) {
-  if (b->status_pending) {
+  if (b->vox_pending) {
     hip_check(hipEventSynchronize(b->vox_ev), "hipEventSynchronize");
-    b->status_pending = false;
-    if ((int32_t)b->vox_h[2] != 0) b->status_bad = true;
+    b->vox_total = b->vox_h[0] + b->vox_h[1];
+    b->vox_known = true;
+    b->vox_pending = false;
+    apply_status(b);
   }
   if (b->status_bad)
     throw Error(TC_ERR_INTERNAL, "a device consistency check failed while this batch was written; its arrays are not valid");
 }
 
-// Queues the copy of the last member's voxel count and begin behind the
-// builder's kernels (stream s) and records the slot's event, so that the first
-// request for the total waits for that event instead of a new round trip.
+// Queues the copy of the last member's header tail and the status word behind
+// the builder's kernels (stream s) and records the slot's event, so that the
+// first request for the total waits for that event instead of a new round trip.
 static void queue_voxel_total(tc_grid_batch* b, hipStream_t s) {
   if (b->vox_known || b->B <= 0) return;
   take_vox_slot(b);
   const GridView v = b->view();
-  hip_check(hipMemcpyAsync(b->vox_h, &v.headers[b->B - 1].voxel_count, 16, hipMemcpyDeviceToHost, s),
+  hip_check(hipMemcpyAsync(b->vox_h, &v.headers[b->B - 1].voxel_count, 64, hipMemcpyDeviceToHost, s),
             "voxel total readback");
   hip_check(hipEventRecord(b->vox_ev, s), "hipEventRecord");
   b->vox_pending = true;
@@ -180,22 +184,19 @@ static tc_grid_batch* finish_batch(tc_grid_batch* b, hipStream_t s) {
   return b;
 }
 
+// The batch's voxel total: known, or waited for on its queued copy, or read
+// back into the pinned staging buffer.
 static i64 read_voxel_total(const tc_grid_batch* b, hipStream_t s) {
-  check_status(b);
+  check_status(b);  // also takes the queued total
   if (b->vox_known) return b->vox_total;
-  if (b->vox_pending) {
-    hip_check(hipEventSynchronize(b->vox_ev), "hipEventSynchronize");
-    b->vox_total = b->vox_h[0] + b->vox_h[1];
-    b->vox_known = true;
-    b->vox_pending = false;
-    return b->vox_total;
-  }
-  tc_grid_header* h = static_cast<tc_grid_header*>(pinned_staging(sizeof(tc_grid_header)));
+  // nothing queued: the last header's tail and the status word, read back now
+  int64_t* h = static_cast<int64_t*>(pinned_staging(64));
   const GridView v = b->view();
-  hip_check(hipMemcpyAsync(h, v.headers + (b->B - 1), sizeof(tc_grid_header), hipMemcpyDeviceToHost, s),
-            "header readback");
+  hip_check(hipMemcpyAsync(h, &v.headers[b->B - 1].voxel_count, 64, hipMemcpyDeviceToHost, s), "header readback");
   hip_check(hipStreamSynchronize(s), "hipStreamSynchronize");
-  b->vox_total = h->voxel_begin + h->voxel_count;
+  if ((int32_t)h[kStatusWord] != 0) b->status_bad = true;
+  check_status(b);
+  b->vox_total = h[0] + h[1];
   b->vox_known = true;
   return b->vox_total;
 }
@@ -435,7 +436,7 @@ tc_status tc_batch_get_info(const tc_grid_batch* b, tc_batch_info* out) {
 tc_status tc_batch_read_headers(const tc_grid_batch* b, tc_grid_header* h_out, void* stream) {
   if (!b || !h_out) return fail(TC_ERR_INVALID_ARG, "NULL argument");
   return guarded([&]() {
-    tc::check_status(b);
+    tc::read_voxel_total(b, (hipStream_t)stream);  // the status check; usually no extra wait
     const size_t bytes = sizeof(tc_grid_header) * (size_t)b->B;
     void* h = tc::pinned_staging(bytes);
     hipStream_t s = (hipStream_t)stream;

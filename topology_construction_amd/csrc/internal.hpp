@@ -51,7 +51,7 @@ inline OpInfo op_info(int op) {
 
 // ------------------------------------------------------------------ layout
 struct Layout {
-  size_t headers, upper_origin, upper_key, upper_first, upper_mask, lower_origin, lower_first,
+  size_t headers, status, upper_origin, upper_key, upper_first, upper_mask, lower_origin, lower_first,
       lower_mask, lower_prefix, leaf_origin, leaf_parent, leaf_mask, leaf_prefix, leaf_offset;
   size_t total;
 };
@@ -66,7 +66,10 @@ inline Layout make_layout(i64 B, i64 n2, i64 n1, i64 nl) {
     off = align_up(off + bytes);
     return at;
   };
-  L.headers = take(sizeof(tc_grid_header) * (size_t)B);
+  // the B headers, then a 16-byte status word (int32 flags of the writer
+  // kernels, then zeros) that is read back together with the last header
+  L.headers = take(sizeof(tc_grid_header) * (size_t)B + 16);
+  L.status = L.headers + sizeof(tc_grid_header) * (size_t)B;
   L.upper_origin = take(16 * (size_t)n2);
   L.upper_key = take(8 * (size_t)n2);
   L.upper_first = take(4 * (size_t)n2);
@@ -88,6 +91,7 @@ inline Layout make_layout(i64 B, i64 n2, i64 n1, i64 nl) {
 struct GridView {
   int32_t B, n_upper, n_lower, n_leaf;
   tc_grid_header* headers;
+  int32_t* status;  // [4]: writer flags (non-zero: a failed consistency check), 0, 0, 0
   int4* upper_origin;
   u64* upper_key;
   int32_t* upper_first;
@@ -111,6 +115,7 @@ inline GridView make_view(void* buffer, const Layout& L, int32_t B, int32_t n2, 
   v.n_lower = n1;
   v.n_leaf = nl;
   v.headers = reinterpret_cast<tc_grid_header*>(b + L.headers);
+  v.status = reinterpret_cast<int32_t*>(b + L.status);
   v.upper_origin = reinterpret_cast<int4*>(b + L.upper_origin);
   v.upper_key = reinterpret_cast<u64*>(b + L.upper_key);
   v.upper_first = reinterpret_cast<int32_t*>(b + L.upper_first);
@@ -194,11 +199,11 @@ int device_cu_count();
 // Per-thread pinned host staging buffer (grows on demand, never shrinks).
 void* pinned_staging(size_t bytes);
 
-// Pinned 32-byte host slots, each with an event, for the voxel total of a batch
-// (words 0 and 1: the last grid's voxel count and begin) and the device flags
-// its writer kernels left (word 2): the copies are queued behind a builder's
+// Pinned 64-byte host slots, each with an event, for the tail of a batch's last
+// header and its status word (int64 words 0 and 1: the last grid's voxel count
+// and begin; word 6: the writer flags): the copy is queued behind a builder's
 // last kernel and read when first asked. Slots belong to a device; taking one
-// waits for its previous copies to land.
+// waits for its previous copy to land.
 struct VoxTicket {
   int slot;
   int64_t* h;
@@ -319,8 +324,10 @@ int32_t bbox_replicas(int32_t B);  // replicas of the per-grid bbox accumulators
 // Leaf voxel offsets, per-grid bboxes and headers. The leaf producer wrote, per
 // run of `gran` leaves (gran divides 256), the run's voxel sum (vox_part) and
 // every leaf's voxels before it inside its run (leaf_inrun).
+// `flags` is the builder's flag word; its final value goes to out.status.
 void tree_finalize_leaves(const GridView& out, const uint32_t* leaf_box, const int32_t* leaf_inrun, i64* vox_part,
-                          i64 gran, i64* gvb, int32_t* bbox_accum, const int32_t* grid_info, hipStream_t s);
+                          i64 gran, i64* gvb, int32_t* bbox_accum, const int32_t* grid_info, const int32_t* flags,
+                          hipStream_t s);
 void tree_enumerate(const GridView& v, int32_t* ijk, hipStream_t s);
 
 // Allocation of the single output buffer of a batch.
@@ -331,8 +338,10 @@ struct OutAlloc {
 };
 
 // Testing: bits that the next batch built on the calling thread ORs into its
-// writers' device flag word (tc_debug_inject_flags).
+// writers' device flag word (tc_debug_inject_flags); apply_debug_inject sets
+// them (once) on the flag word of the batch being built, before its finalize.
 void debug_set_inject(int32_t bits);
+void apply_debug_inject(int32_t* d_flags, hipStream_t s);
 
 void prof_enable(const char* name);
 void prof_read(const char* name, double* ms, int64_t* n);
@@ -355,10 +364,9 @@ struct tc_grid_batch {
   int device = 0;
   mutable bool vox_known = false;
   mutable int64_t vox_total = 0;
-  // voxel total and writer flags queued for readback (queue_status,
-  // queue_voxel_total): slot, host words, event
+  // voxel total and status word queued for readback (queue_voxel_total): slot,
+  // host words, event
   mutable bool vox_pending = false;
-  mutable bool status_pending = false;
   mutable bool status_bad = false;  // a writer kernel's device consistency check failed
   mutable int vox_slot = -1;
   mutable int64_t* vox_h = nullptr;
@@ -375,16 +383,16 @@ namespace tc {
 tc_grid_batch* new_batch(int32_t B, const int32_t* readback, const OutAlloc& oa);
 void free_batch(tc_grid_batch* b);
 tc_grid_batch* copy_batch(const tc_grid_batch* src, const OutAlloc& oa);  // same counts, one D2D copy
-// Queues the copy of the device flag word that a builder's writer kernels set
-// (after its last writer, on stream s) into the batch's pinned slot.
-void queue_status(tc_grid_batch* b, const int32_t* d_flags, hipStream_t s);
 // Throws TC_ERR_INTERNAL when the batch's writers flagged a failed consistency
-// check (waits for the queued flag copy the first time).
+// check (the status word comes back with the voxel total: this waits for that
+// copy the first time).
 void check_status(const tc_grid_batch* b);
 // Kernel map of `dst` against `src` (same member count): out int32[V_dst][K^3],
-// `entries` = V_dst * K^3.
+// `entries` = V_dst * K^3. Scratch from an arena, or from `scratch` (device,
+// scratch_cap bytes, at least kernel_map_scratch_bytes) when given.
 void kernel_map(const GridView& src, const GridView& dst, int K, int S, int transposed, int32_t* out, i64 entries,
-                hipStream_t s);
+                hipStream_t s, char* scratch = nullptr, size_t scratch_cap = 0);
+size_t kernel_map_scratch_bytes(const GridView& src, const GridView& dst, int K, int S, int transposed);
 
 // The two producers of grid batches.
 tc_grid_batch* build_from_ijk(const int32_t* d_ijk, const int64_t* h_offsets, int32_t B, const OutAlloc& oa);

@@ -336,14 +336,8 @@ __global__ void __launch_bounds__(256) k_kernel_map(const int4* t_origin, const 
 
 static i64 host_floor_div(i64 a, i64 b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }
 
-void kernel_map(const GridView& sv, const GridView& tv, int K, int S, int transposed, int32_t* out, i64 entries,
-                hipStream_t s) {
-  if (tv.n_leaf == 0) return;
-  if (K < 1 || K > 8 || S < 1 || S > 2) throw Error(TC_ERR_UNSUPPORTED, "kernel_map: kernel/stride out of range");
-  if (sv.n_leaf == 0) {  // no source voxel anywhere: every entry is -1
-    fill_i32(out, -1, entries, nullptr, 1, s);
-    return;
-  }
+// Geometry of a kernel map and its window slots per target leaf.
+static KmapGeom kmap_geom(int K, int S, int transposed, int* slots_per_leaf) {
   KmapGeom gm;
   gm.K = K;
   gm.S = S;
@@ -354,7 +348,6 @@ void kernel_map(const GridView& sv, const GridView& tv, int K, int S, int transp
   gm.KK = K * K * K;
   gm.q64 = kWave / gm.KK;
   gm.r64 = kWave % gm.KK;
-  gm.vol_words = gm.wave_words = 0;  // set once the slot count is known
   // window slots per target leaf: the region's alignment to the leaf grid only
   // depends on the leaf origin modulo 16, so origins 0 and 8 give the maximum
   int sm = 0;
@@ -374,15 +367,56 @@ void kernel_map(const GridView& sv, const GridView& tv, int K, int S, int transp
   // per wave: volume, slot masks and prefixes (18 words per slot), slot bases, 512 uint16 row offsets
   gm.vol_words = (gm.R * gm.R * gm.R + 3) & ~3;
   gm.wave_words = (gm.vol_words + 18 * sm + sm + 256 + 3) & ~3;  // 16-byte aligned waves
+  *slots_per_leaf = sm;
+  return gm;
+}
 
+// Scratch of one call, 256-byte aligned arrays: per source upper the popcount
+// prefix of its child mask (uint16[512]); per (target leaf, window slot) the
+// slot's source leaf and first voxel (int2); per target leaf its first row (int64).
+struct KmapScratch {
+  size_t up, slots, first, total;
+};
+static KmapScratch kmap_scratch(i64 n_upper, i64 n_leaf, int sm) {
+  KmapScratch k{};
+  k.up = 0;
+  k.slots = align_up(k.up + sizeof(uint16_t) * 512 * (size_t)std::max<i64>(n_upper, 1));
+  k.first = align_up(k.slots + sizeof(int2) * (size_t)n_leaf * sm);
+  k.total = align_up(k.first + sizeof(i64) * (size_t)std::max<i64>(n_leaf, 1));
+  return k;
+}
+
+size_t kernel_map_scratch_bytes(const GridView& sv, const GridView& tv, int K, int S, int transposed) {
+  if (tv.n_leaf == 0 || sv.n_leaf == 0) return 0;
+  if (K < 1 || K > 8 || S < 1 || S > 2) throw Error(TC_ERR_UNSUPPORTED, "kernel_map: kernel/stride out of range");
+  int sm = 0;
+  (void)kmap_geom(K, S, transposed, &sm);
+  return kmap_scratch(sv.n_upper, tv.n_leaf, sm).total;
+}
+
+void kernel_map(const GridView& sv, const GridView& tv, int K, int S, int transposed, int32_t* out, i64 entries,
+                hipStream_t s, char* scratch, size_t scratch_cap) {
+  if (tv.n_leaf == 0) return;
+  if (K < 1 || K > 8 || S < 1 || S > 2) throw Error(TC_ERR_UNSUPPORTED, "kernel_map: kernel/stride out of range");
+  if (sv.n_leaf == 0) {  // no source voxel anywhere: every entry is -1
+    fill_i32(out, -1, entries, nullptr, 1, s);
+    return;
+  }
+  int sm = 0;
+  const KmapGeom gm = kmap_geom(K, S, transposed, &sm);
+  const KmapScratch lay = kmap_scratch(sv.n_upper, tv.n_leaf, sm);
   Arena arena(s);
-  const size_t o_up = arena.reserve(sizeof(uint16_t) * 512 * (size_t)std::max(sv.n_upper, 1));
-  const size_t o_slots = arena.reserve(sizeof(int2) * (size_t)tv.n_leaf * sm);
-  const size_t o_first = arena.reserve(sizeof(i64) * (size_t)tv.n_leaf);
-  arena.commit();
-  uint16_t* upper_prefix = arena.at<uint16_t>(o_up);
-  int2* slots = arena.at<int2>(o_slots);
-  i64* t_first = arena.at<i64>(o_first);
+  char* base = scratch;
+  if (base) {
+    if (lay.total > scratch_cap) throw Error(TC_ERR_INTERNAL, "kernel_map: scratch larger than the given buffer");
+  } else {
+    const size_t o = arena.reserve(lay.total);
+    arena.commit();
+    base = arena.at<char>(o);
+  }
+  uint16_t* upper_prefix = reinterpret_cast<uint16_t*>(base + lay.up);
+  int2* slots = reinterpret_cast<int2*>(base + lay.slots);
+  i64* t_first = reinterpret_cast<i64*>(base + lay.first);
   launch("k_upper_prefix", k_upper_prefix, sv.n_upper, 256, s, (const u64*)sv.upper_mask, upper_prefix);
 
   KmapSrc src{(const tc_grid_header*)sv.headers, (const u64*)sv.upper_key, (const int32_t*)sv.upper_first,

@@ -33,6 +33,12 @@ constexpr u64 kZ0 = 0x0101010101010101ull;  // z = 0 bit of every (x, y) row
 constexpr u64 kZ7 = 0x8080808080808080ull;  // z = 7 bit of every row
 constexpr int kFlagOverflow = 1;
 constexpr int kFlagInternal = 2;
+constexpr int kFlagSource = 4;  // the source batch's writers had flagged a failed check
+
+// The pass's flag word starts from the source batch's status word.
+__global__ void k_flags_from_source(int32_t* flags, const int32_t* src_status) {
+  if (threadIdx.x == 0) flags[0] = src_status[0] != 0 ? kFlagSource : 0;
+}
 
 struct I3 {
   i64 x, y, z;
@@ -356,7 +362,8 @@ __global__ void __launch_bounds__(kTilesThreads) k_tiles_small(const int4* upper
                                                                int4* utile, int32_t* tile_of_cand,
                                                                int32_t* d_num_tiles, int32_t* grid_tile_begin,
                                                                u64* tile_child, int zero_child,
-                                                               const uint32_t* upper_reach, int32_t* readback) {
+                                                               const uint32_t* upper_reach, int32_t* readback,
+                                                               const int32_t* src_status) {
   __shared__ u64 s_hi[kTilesMax];
   __shared__ u64 s_lo[kTilesMax];
   __shared__ uint32_t s_v[kTilesMax];
@@ -369,7 +376,7 @@ __global__ void __launch_bounds__(kTilesThreads) k_tiles_small(const int4* upper
   const int n = n_upper * m;
   __shared__ int32_t s_rng[6];  // min x, y, z, max x, y, z of the kept candidates' tiles
   if (tid == 0) {
-    readback[0] = 0;
+    readback[0] = src_status[0] != 0 ? kFlagSource : 0;  // a flawed source fails the pass
     for (int a = 0; a < 3; ++a) {
       s_rng[a] = INT32_MAX;
       s_rng[3 + a] = INT32_MIN;
@@ -1858,10 +1865,11 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, 
     }
     launch("k_tiles_small", k_tiles_small, 1, kTilesThreads, s, (const int4*)sv.upper_origin,
            (const u64*)sv.upper_mask, (int32_t)src->n2, op, oi.m, B, ts.utile, tile_of_cand, ts.d_num_tiles,
-           ts.grid_tile_begin, ts.tile_child, zero_here ? 1 : 0, (const uint32_t*)ureach, ts.readback);
+           ts.grid_tile_begin, ts.tile_child, zero_here ? 1 : 0, (const uint32_t*)ureach, ts.readback,
+           (const int32_t*)sv.status);
     if (!small_lowers && !zero_here) fill_u64(ts.tile_child, 0, nT * 512, ts.d_num_tiles, 512, s);
   } else {
-    fill_i32(ts.readback, 0, 1, nullptr, 1, s);
+    launch("k_flags_from_source", k_flags_from_source, 1, 64, s, ts.readback, (const int32_t*)sv.status);
     if (nT > 0) {
       Key128* keys = a.at<Key128>(o_keys);
       uint32_t* vals = a.at<uint32_t>(o_vals);
@@ -1929,7 +1937,8 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, 
   int32_t* h_rb = static_cast<int32_t*>(pinned_staging(rb_bytes));
   hip_check(hipMemcpyAsync(h_rb, ts.readback, rb_bytes, hipMemcpyDeviceToHost, s), "readback");
   hip_check(hipStreamSynchronize(s), "hipStreamSynchronize");
-  check_status(src);  // its writers' flags were queued before this pass on the stream
+  if (h_rb[0] & kFlagSource)
+    throw Error(TC_ERR_INTERNAL, "the source batch failed a device consistency check when it was written");
   if (h_rb[0] & kFlagOverflow) throw Error(TC_ERR_OVERFLOW, "an output voxel coordinate leaves int32");
   if (h_rb[0] & kFlagInternal) throw Error(TC_ERR_INTERNAL, "pass: device consistency check failed");
 
@@ -1969,11 +1978,12 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, 
              sv.n_lower, sv.n_leaf, (const int32_t*)ts.d_num_cands, ov.leaf_mask, ov.leaf_prefix,
              post.at<uint32_t>(o_box), leaf_inrun, vox_part, ts.flags);
     }
-    tree_finalize_leaves(ov, post.at<uint32_t>(o_box), leaf_inrun, vox_part, gran, post.at<i64>(o_gvb),
-                         post.at<int32_t>(o_bb), (const int32_t*)ts.grid_info, s);
     // the gathers' consistency checks set bits in the flag word after the
-    // readback: it goes back with the batch's voxel total
-    queue_status(out, ts.flags, s);
+    // readback: the finalize copies it into the batch's status word, which goes
+    // back with the voxel total
+    apply_debug_inject(ts.flags, s);
+    tree_finalize_leaves(ov, post.at<uint32_t>(o_box), leaf_inrun, vox_part, gran, post.at<i64>(o_gvb),
+                         post.at<int32_t>(o_bb), (const int32_t*)ts.grid_info, (const int32_t*)ts.flags, s);
   } catch (...) {
     free_batch(out);
     throw;

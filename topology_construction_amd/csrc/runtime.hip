@@ -367,7 +367,7 @@ int device_cu_count() {
 
 // ------------------------------------------------------------------ voxel-total slots
 namespace {
-constexpr int kVoxChunk = 256;  // slots per pinned allocation, 32 bytes each
+constexpr int kVoxChunk = 256;  // slots per pinned allocation, 64 bytes each
 struct VoxSlot {
   int64_t* h;
   hipEvent_t ev;
@@ -399,10 +399,10 @@ VoxTicket vox_slot_take(int device) {
     }
     if (t.slot < 0) {
       void* h = nullptr;
-      hip_check(hipHostMalloc(&h, 32 * kVoxChunk, hipHostMallocDefault), "hipHostMalloc");
+      hip_check(hipHostMalloc(&h, 64 * kVoxChunk, hipHostMallocDefault), "hipHostMalloc");
       const int base = (int)p.slots.size();
       for (int k = 0; k < kVoxChunk; ++k) {
-        p.slots.push_back(VoxSlot{static_cast<int64_t*>(h) + 4 * k, nullptr, device});
+        p.slots.push_back(VoxSlot{static_cast<int64_t*>(h) + 8 * k, nullptr, device});
         if (k) p.idle.push_back(base + k);
       }
       t.slot = base;

@@ -576,7 +576,8 @@ __global__ void __launch_bounds__(kFinThreads) k_finalize_small(const int4* leaf
                                                                 const uint32_t* leaf_box, const i64* vox_part,
                                                                 int32_t np, int32_t gs, const int32_t* grid_info,
                                                                 i64* leaf_offset, int32_t B, int32_t L,
-                                                                tc_grid_header* hdr) {
+                                                                tc_grid_header* hdr, const int32_t* flags,
+                                                                int32_t* status) {
   constexpr int kR = kFinRuns / kFinThreads;
   constexpr int kG = kFinSmallGrids / kFinThreads;
   __shared__ int32_t s_part[kFinRuns];           // exclusive voxel offset of every run
@@ -703,6 +704,7 @@ __global__ void __launch_bounds__(kFinThreads) k_finalize_small(const int4* leaf
     __syncthreads();
   }
   if (blockIdx.x != 0) return;
+  if (tid < 4) status[tid] = tid == 0 ? *flags : 0;  // every writer of the leaves ran before this kernel
 #pragma unroll
   for (int k = 0; k < kG; ++k) {  // B <= kFinSmallGrids = kG * kFinThreads
     const int gg = tid + k * kFinThreads;
@@ -822,9 +824,11 @@ __global__ void __launch_bounds__(256) k_leaf_offsets_runs(const int4* leaf_orig
 // One wave per grid: lanes fold the bbox replicas, lane 0 writes the header.
 __global__ void __launch_bounds__(256) k_write_headers_gvb(const int32_t* grid_info, const i64* gvb,
                                                            const int32_t* bbox, int32_t B, int32_t R,
-                                                           tc_grid_header* hdr) {
+                                                           tc_grid_header* hdr, const int32_t* flags,
+                                                           int32_t* status) {
   const i64 g = (i64)blockIdx.x * 4 + threadIdx.x / kWave;
   const int lane = threadIdx.x & (kWave - 1);
+  if (blockIdx.x == 0 && threadIdx.x < 4) status[threadIdx.x] = threadIdx.x == 0 ? *flags : 0;
   if (g >= B) return;  // uniform per wave
   int v[6] = {INT32_MAX, INT32_MAX, INT32_MAX, INT32_MIN, INT32_MIN, INT32_MIN};
   for (int r = lane; r < R; r += kWave) {
@@ -862,14 +866,16 @@ __global__ void __launch_bounds__(256) k_write_headers_gvb(const int32_t* grid_i
 }
 
 void tree_finalize_leaves(const GridView& out, const uint32_t* leaf_box, const int32_t* leaf_inrun, i64* vox_part,
-                          i64 gran, i64* gvb, int32_t* bbox_accum, const int32_t* grid_info, hipStream_t s) {
+                          i64 gran, i64* gvb, int32_t* bbox_accum, const int32_t* grid_info, const int32_t* flags,
+                          hipStream_t s) {
   const i64 L = out.n_leaf;
   const int32_t B = out.B;
   if (gran <= 0 || (gran & (gran - 1)) != 0) throw Error(TC_ERR_INTERNAL, "finalize: run length not a power of two");
   if (L <= kFinSmallLeaves && B <= kFinSmallGrids && ceil_div(L, gran) <= kFinRuns) {
     launch("k_finalize_small", k_finalize_small, std::max<i64>(1, ceil_div(L, kFinSlice)), kFinThreads, s,
            (const int4*)out.leaf_origin, leaf_inrun, leaf_box, (const i64*)vox_part, (int32_t)ceil_div(L, gran),
-           (int32_t)__builtin_ctzll((u64)gran), grid_info, out.leaf_offset, B, (int32_t)L, out.headers);
+           (int32_t)__builtin_ctzll((u64)gran), grid_info, out.leaf_offset, B, (int32_t)L, out.headers, flags,
+           out.status);
     return;
   }
   const int32_t R = bbox_replicas(B);
@@ -878,7 +884,7 @@ void tree_finalize_leaves(const GridView& out, const uint32_t* leaf_box, const i
   launch("k_leaf_offsets_bbox", k_leaf_offsets_runs, ceil_div(L, 256), 256, s, (const int4*)out.leaf_origin,
          leaf_inrun, leaf_box, (const i64*)vox_part, gran, (const i64*)gvb, out.leaf_offset, bbox_accum, B, R, L);
   launch("k_write_headers", k_write_headers_gvb, ceil_div((i64)B, 4), 256, s, grid_info, (const i64*)gvb,
-         (const int32_t*)bbox_accum, B, R, out.headers);
+         (const int32_t*)bbox_accum, B, R, out.headers, flags, out.status);
 }
 
 // ------------------------------------------------------------------ enumeration

@@ -280,6 +280,24 @@ tc_status tc_build_kernel_map(const tc_grid_batch* src, const tc_grid_batch* dst
                               int32_t stride, int32_t transposed, int32_t* d_out, int64_t capacity,
                               void* stream);
 
+/* Kernel map with no allocation, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc). Arguments, output and errors as for tc_build_kernel_map;
+ * it calls no hipMalloc, hipFree or other allocating routine, and reads the
+ * voxel totals back into host stack memory when they are not yet known.
+ * Scratch: a static device array of 64 MiB per GPU, loaded with the library
+ * and held by every GPU it runs on until the process ends (its device address
+ * is looked up on the first call on each device). The call needs
+ *   256-byte aligned: 1 KiB per source upper node + 8 bytes per target leaf and
+ *   window slot (8 to 64 slots, 27 for k3 s1) + 8 bytes per target leaf;
+ * beyond 64 MiB it returns TC_ERR_UNSUPPORTED before any launch and writes
+ * nothing. Every call on one GPU uses the same array, and no kernel relies on
+ * what an earlier call left there: calls on one stream are ordered, but calls
+ * that overlap on one GPU (other streams, other threads) race on it. */
+tc_status tc_build_kernel_map_noalloc(const tc_grid_batch* src, const tc_grid_batch* dst, int32_t kernel_size,
+                                      int32_t stride, int32_t transposed, int32_t* d_out, int64_t capacity,
+                                      void* stream);
+
 /* Cached device memory: every call takes its scratch arrays (and the buffers
  * of intermediate batches) from blocks cached process-wide per device, stream
  * and allocator, and keeps them for the next call with the same key (reuse is

@@ -28,7 +28,8 @@ ABI_SYMBOLS = [
     "tc_abi_version", "tc_status_string", "tc_last_error", "tc_batch_from_ijk", "tc_batch_from_points",
     "tc_build_batched_topology", "tc_build_masked_refine", "tc_batch_get_info", "tc_batch_read_headers",
     "tc_batch_voxel_total", "tc_enumerate_ijk", "tc_build_kernel_map", "tc_scratch_release", "tc_batch_free",
-    "tc_debug_inject_flags", "tc_profile_enable", "tc_profile_read", "tc_profile_disable",
+    "tc_debug_inject_flags", "tc_build_kernel_map_noalloc", "tc_profile_enable", "tc_profile_read",
+    "tc_profile_disable",
 ]
 
 HEADER_DTYPE = np.dtype([
@@ -127,6 +128,9 @@ def load_library(path: str = LIB_PATH):
         lib.tc_enumerate_ijk.argtypes = [vp, vp, i64, vp]
         lib.tc_build_kernel_map.restype = ctypes.c_int
         lib.tc_build_kernel_map.argtypes = [vp, vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, i64, vp]
+        lib.tc_build_kernel_map_noalloc.restype = ctypes.c_int
+        lib.tc_build_kernel_map_noalloc.argtypes = [vp, vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, i64,
+                                                    vp]
         lib.tc_batch_from_points.restype = ctypes.c_int
         lib.tc_batch_from_points.argtypes = [vp, vp, i32, vp, vp, i32, vp, vp, ctypes.POINTER(vp)]
         lib.tc_scratch_release.restype = ctypes.c_int
@@ -367,6 +371,18 @@ def tc_build_kernel_map(src: GridBatch, dst: GridBatch, kernel_size: int, stride
     _check(lib.tc_build_kernel_map(src.handle, dst.handle, int(kernel_size), int(stride), int(bool(transposed)),
                                    ctypes.c_void_p(out.data_ptr() if out.numel() else 0), int(out.numel()),
                                    _stream_handle(stream)))
+    return out.view(-1)[:rows * kk].view(rows, kk)
+
+
+def tc_build_kernel_map_noalloc(src: GridBatch, dst: GridBatch, kernel_size: int, stride: int, transposed: bool,
+                                out, stream=None):
+    """As tc_build_kernel_map into a caller-allocated `out`, with the library's
+    static scratch (no device allocation by the library)."""
+    kk = int(kernel_size) ** 3
+    rows = dst.voxel_total(stream)
+    _check(load_library().tc_build_kernel_map_noalloc(
+        src.handle, dst.handle, int(kernel_size), int(stride), int(bool(transposed)),
+        ctypes.c_void_p(out.data_ptr() if out.numel() else 0), int(out.numel()), _stream_handle(stream)))
     return out.view(-1)[:rows * kk].view(rows, kk)
 
 

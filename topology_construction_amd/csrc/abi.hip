@@ -185,12 +185,14 @@ static tc_grid_batch* finish_batch(tc_grid_batch* b, hipStream_t s) {
 }
 
 // The batch's voxel total: known, or waited for on its queued copy, or read
-// back into the pinned staging buffer.
-static i64 read_voxel_total(const tc_grid_batch* b, hipStream_t s) {
+// back (into the pinned staging buffer, or with `pageable` into host stack
+// memory, so that nothing is allocated).
+static i64 read_voxel_total(const tc_grid_batch* b, hipStream_t s, bool pageable = false) {
   check_status(b);  // also takes the queued total
   if (b->vox_known) return b->vox_total;
   // nothing queued: the last header's tail and the status word, read back now
-  int64_t* h = static_cast<int64_t*>(pinned_staging(64));
+  int64_t stack_h[8];
+  int64_t* h = pageable ? stack_h : static_cast<int64_t*>(pinned_staging(64));
   const GridView v = b->view();
   hip_check(hipMemcpyAsync(h, &v.headers[b->B - 1].voxel_count, 64, hipMemcpyDeviceToHost, s), "header readback");
   hip_check(hipStreamSynchronize(s), "hipStreamSynchronize");
@@ -494,6 +496,40 @@ tc_status tc_build_kernel_map(const tc_grid_batch* src, const tc_grid_batch* dst
       throw tc::Error(TC_ERR_INVALID_ARG,
                       "capacity " + std::to_string(capacity) + " < " + std::to_string(need) + " entries");
     tc::kernel_map(src->view(), dst->view(), kernel_size, stride, transposed, d_out, need, s);
+    return TC_OK;
+  });
+}
+
+tc_status tc_build_kernel_map_noalloc(const tc_grid_batch* src, const tc_grid_batch* dst, int32_t kernel_size,
+                                      int32_t stride, int32_t transposed, int32_t* d_out, int64_t capacity,
+                                      void* stream) {
+  if (!src || !dst) return fail(TC_ERR_INVALID_ARG, "batch is NULL");
+  if (src->B != dst->B) return fail(TC_ERR_INVALID_ARG, "source and target member counts differ");
+  if (kernel_size < 1 || kernel_size > 8) return fail(TC_ERR_INVALID_ARG, "kernel_size must be in [1, 8]");
+  if (stride < 1) return fail(TC_ERR_INVALID_ARG, "stride must be positive");
+  if (stride > 2) return fail(TC_ERR_UNSUPPORTED, "stride must be 1 or 2");
+  if (transposed != 0 && transposed != 1) return fail(TC_ERR_INVALID_ARG, "transposed must be 0 or 1");
+  return guarded([&]() {
+    if (current_device() != src->device || current_device() != dst->device)
+      throw tc::Error(TC_ERR_INVALID_ARG, "a batch lives on another device");
+    hipStream_t s = (hipStream_t)stream;
+    size_t cap = 0;
+    char* scratch = tc::noalloc_scratch(&cap);  // set-up on the first call on this device
+    const int64_t n_src = tc::read_voxel_total(src, s, true);
+    if (n_src > (int64_t)INT32_MAX) throw tc::Error(TC_ERR_UNSUPPORTED, "source voxel indices exceed int32");
+    const int64_t kk = (int64_t)kernel_size * kernel_size * kernel_size;
+    const int64_t need = tc::read_voxel_total(dst, s, true) * kk;
+    if (need == 0) return TC_OK;
+    if (!d_out) throw tc::Error(TC_ERR_INVALID_ARG, "d_out is NULL");
+    if (capacity < need)
+      throw tc::Error(TC_ERR_INVALID_ARG,
+                      "capacity " + std::to_string(capacity) + " < " + std::to_string(need) + " entries");
+    const size_t want = tc::kernel_map_scratch_bytes(src->view(), dst->view(), kernel_size, stride, transposed);
+    if (want > cap)
+      throw tc::Error(TC_ERR_UNSUPPORTED, "kernel map needs " + std::to_string(want) +
+                                              " bytes of scratch; the no-allocation entry point has " +
+                                              std::to_string(cap) + " (use tc_build_kernel_map)");
+    tc::kernel_map(src->view(), dst->view(), kernel_size, stride, transposed, d_out, need, s, scratch, cap);
     return TC_OK;
   });
 }

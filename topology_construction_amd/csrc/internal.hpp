@@ -393,6 +393,9 @@ void check_status(const tc_grid_batch* b);
 void kernel_map(const GridView& src, const GridView& dst, int K, int S, int transposed, int32_t* out, i64 entries,
                 hipStream_t s, char* scratch = nullptr, size_t scratch_cap = 0);
 size_t kernel_map_scratch_bytes(const GridView& src, const GridView& dst, int K, int S, int transposed);
+// Device address of the current GPU's static no-allocation scratch array and
+// its size (hipGetSymbolAddress once per device).
+char* noalloc_scratch(size_t* cap);
 
 // The two producers of grid batches.
 tc_grid_batch* build_from_ijk(const int32_t* d_ijk, const int64_t* h_offsets, int32_t B, const OutAlloc& oa);

@@ -21,6 +21,8 @@
 //      so consecutive lanes write consecutive int32 (coalesced stores).
 // The volume is kept at the target's fine resolution for the transposed conv
 // (a source voxel c lands at S*c), so both directions share step 3.
+#include <mutex>
+
 #include "device.hpp"
 #include "internal.hpp"
 
@@ -335,6 +337,34 @@ __global__ void __launch_bounds__(256) k_kernel_map(const int4* t_origin, const 
 }  // namespace
 
 static i64 host_floor_div(i64 a, i64 b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }
+
+// Scratch of the no-allocation kernel map (tc_build_kernel_map_noalloc): one
+// array per GPU, loaded with the library and held until the process ends. Its
+// name is a host-side stand-in in host code; kernels get the device address
+// that hipGetSymbolAddress returns for the current device.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_noalloc_mu;
+char* g_noalloc_ptr[kMaxDevices] = {};
+}  // namespace
+
+char* noalloc_scratch(size_t* cap) {
+  int dev = 0;
+  hip_check(hipGetDevice(&dev), "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) throw Error(TC_ERR_UNSUPPORTED, "device index out of range");
+  std::lock_guard<std::mutex> lk(g_noalloc_mu);
+  if (!g_noalloc_ptr[dev]) {  // once per device, with that device current
+    void* p = nullptr;
+    hip_check(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (!p) throw Error(TC_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_noalloc_ptr[dev] = static_cast<char*>(p);
+  }
+  *cap = kNoAllocScratchBytes;
+  return g_noalloc_ptr[dev];
+}
 
 // Geometry of a kernel map and its window slots per target leaf.
 static KmapGeom kmap_geom(int K, int S, int transposed, int* slots_per_leaf) {

@@ -9,11 +9,16 @@ enumeration. Inputs are resident in HBM before timing starts.
 
 Prints one JSON line (rank 0). `value` = output voxels per second over the K
 timed steps. `roofline` reports the dominant kernel's algorithmic bytes per
-launch over its HIP-event-timed average duration; `cpu_baseline` times the CPU
-oracle on whole steps of the same workload. Outside the timed steps the line
-also carries per-op medians (`ops`), the stride-1 kernel-K targets and masked
-refine (`more_ops`), the ijk and points front-ends (`from_ijk`, `from_points`), the plan's kernel maps
-(`kernel_maps`) and the 46M-voxel batch (`large`).
+launch over its HIP-event-timed average duration in those steps (and, beside
+it, the same over its kernel-trace duration from the committed profile);
+`ms_per_step_unprofiled` repeats the K steps without those events.
+`cpu_baseline` times the CPU oracle on whole steps of the same workload, its
+members spread over the host's threads (single-thread and 46M-voxel figures
+beside it). Outside the timed steps the line also carries per-op medians
+(`ops`, B=48 in `b48`, B=2 in `b2`), the pyramid chain and single-call factors
+4 and 8 (`pyramid`), the stride-1 kernel-K targets and masked refine
+(`more_ops`), the ijk and points front-ends (`from_ijk`, `from_points`), the
+plan's kernel maps (`kernel_maps`) and the 46M-voxel batch (`large`).
 """
 from __future__ import annotations
 
@@ -73,6 +78,105 @@ def op_medians(binding, torch, np, src, reps=20):
                             "ms_enumerate_median": float(np.median(enum_ms)),
                             "output_voxels": int(ijk_out.shape[0]), "output_leaves": int(out.leaf_count)}
     return ops
+
+
+def pyramid(binding, torch, np, synth, reps=20):
+    """Workload 4 (16 res-64 shells): the encoder pyramid (coarsen x2 three
+    times, 64 -> 32 -> 16 -> 8) and the decoder chain back up (k3s2 transpose
+    three times from the coarsest level), each level built from the previous
+    one on the GPU, timed as one rebuild (median of `reps`); the same rebuild
+    with the kernel maps a plan pyramid needs (k3 s1 on each encoder level, the
+    k2s2 conv map of each coarsening, the k3s2 transposed map of each decoder
+    step); and single calls of refine / coarsen by 4 and 8 (PR page
+    Measurements: the 4-level plan-pyramid row; section 1: factors 4 and 8)."""
+    ijk, off = synth.make_config(4)
+    src = binding.tc_batch_from_ijk(torch.from_numpy(ijk).cuda(), off)
+    torch.cuda.synchronize()
+
+    def rebuild(with_maps):
+        enc = [src]
+        for _ in range(3):
+            enc.append(binding.tc_build_batched_topology(enc[-1], "coarsen", 2))
+        dec = [enc[-1]]
+        for _ in range(3):
+            dec.append(binding.tc_build_batched_topology(dec[-1], "conv_t_k3s2", 2))
+        maps = []
+        if with_maps:
+            for lvl in enc:
+                maps.append(binding.tc_build_kernel_map(lvl, lvl, 3, 1, False))
+            for a, b in zip(enc[:-1], enc[1:]):
+                maps.append(binding.tc_build_kernel_map(a, b, 2, 2, False))
+            for a, b in zip(dec[:-1], dec[1:]):
+                maps.append(binding.tc_build_kernel_map(a, b, 3, 2, True))
+        return enc, dec, maps
+
+    res = {"workload": synth.CONFIG_NAMES[4], "grids": int(len(off) - 1), "input_voxels": int(off[-1])}
+    for key, with_maps in [("rebuild_topology", False), ("rebuild_with_kernel_maps", True)]:
+        rebuild(with_maps)  # warm-up
+        ms = []
+        for _ in range(reps):
+            torch.cuda.synchronize()
+            a = time.perf_counter()
+            enc, dec, maps = rebuild(with_maps)
+            torch.cuda.synchronize()
+            ms.append((time.perf_counter() - a) * 1e3)
+        res[key] = {"ms_median": float(np.median(ms)), "passes": 3 + 2 * 3, "kernel_maps": len(maps),
+                    "level_voxels": [int(b.voxel_total()) for b in enc + dec[1:]],
+                    "kernel_map_entries": int(sum(m.numel() for m in maps))}
+        del enc, dec, maps
+    singles = {}
+    for op, f in [("refine", 4), ("refine", 8), ("coarsen", 4), ("coarsen", 8)]:
+        binding.tc_build_batched_topology(src, op, f)  # warm-up
+        ms = []
+        for _ in range(reps):
+            torch.cuda.synchronize()
+            a = time.perf_counter()
+            out = binding.tc_build_batched_topology(src, op, f)
+            torch.cuda.synchronize()
+            ms.append((time.perf_counter() - a) * 1e3)
+        singles[f"{op}x{f}"] = {"ms_median": float(np.median(ms)), "passes": f.bit_length() - 1,
+                                "output_voxels": int(out.voxel_total()), "output_leaves": int(out.leaf_count)}
+        del out
+    res["single_calls"] = singles
+    return res
+
+
+def cpu_baseline(np, ijk, off, large_input=None, min_s=10.0):
+    """The CPU oracle (test infrastructure, untouched) on the host: whole steps of
+    the workload with its members spread over the host's threads (>= min_s
+    seconds), one step on one thread, and, when given, coarsen x2 of the
+    46M-voxel batch on the host's threads."""
+    import oracle
+    threads = oracle.host_threads()
+    t = time.perf_counter()
+    cv, reps = 0, 0
+    while True:
+        for op, f in STEP_OPS:
+            r = oracle.run_threaded(op, f, ijk, off, threads=threads, fields=["headers"])
+            cv += int(r["headers"][:, 8].sum())
+        reps += 1
+        if time.perf_counter() - t >= min_s or reps >= 200:
+            break
+    dt = time.perf_counter() - t
+    t1 = time.perf_counter()
+    cv1 = 0
+    for op, f in STEP_OPS:
+        cv1 += int(oracle.run(op, f, ijk, off, fields=["headers"])["headers"][:, 8].sum())
+    dt1 = time.perf_counter() - t1
+    res = {"value": cv / dt, "unit": "voxels/s", "cores": threads, "kind": "oracle",
+           "sample": f"{reps} full step(s) of the bench workload (all members, {len(STEP_OPS)} ops), {dt:.1f} s, "
+                     f"members spread over {threads} host threads",
+           "single_thread": {"value": cv1 / dt1, "unit": "voxels/s", "cores": 1,
+                             "sample": f"one full step, {dt1:.1f} s"}}
+    if large_input is not None:
+        lijk, loff = large_input
+        t2 = time.perf_counter()
+        r = oracle.run_threaded("coarsen", 2, lijk, loff, threads=threads, fields=["headers"])
+        dt2 = time.perf_counter() - t2
+        res["shells512_cubes_coarsenx2"] = {"value": float(r["headers"][:, 8].sum()) / dt2, "unit": "voxels/s",
+                                            "cores": threads, "seconds": dt2,
+                                            "sample": "coarsen x2 of all 72 members of the 46M-voxel batch"}
+    return res
 
 
 def run_step(binding, src, outs=None):
@@ -145,6 +249,25 @@ def recorded_traffic(kernel, workload):
     if kv.get("source_sha256") != source_digest() or "hbm_bytes_per_launch" not in kv:
         return None
     return float(kv["hbm_bytes_per_launch"])
+
+
+def recorded_trace_ms(kernel, workload):
+    """Average kernel-trace duration (ms) of `kernel` over the bench's timed
+    launches, from the committed summary profiles/trace_<kernel>_<workload>.txt
+    (lines `key value`), or None when there is none or it was taken from other
+    kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"trace_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            parts = line.split()
+            if len(parts) == 2 and not line.startswith("#"):
+                kv[parts[0]] = parts[1]
+    if kv.get("source_sha256") != source_digest() or "trace_avg_us_timed" not in kv:
+        return None
+    return float(kv["trace_avg_us_timed"]) * 1e-3
 
 
 def copy_calibration(torch, mib):
@@ -236,11 +359,14 @@ def time_kernel_maps(binding, torch, np, src, reps):
     return res
 
 
-def measure_large(binding, torch, np, synth):
+def measure_large(binding, torch, np, synth, keep_input=None):
     """64 shells at res 512 + 8 solid 128^3 cubes: per-op pass / enumeration time
-    and per-kernel HIP-event timing against the HBM peak."""
+    and per-kernel HIP-event timing against the HBM peak. `keep_input`, a list,
+    receives the host input (ijk, offsets) for the CPU baseline."""
     ijk, off = synth.make_config(5)
     d_ijk = torch.from_numpy(ijk).cuda()
+    if keep_input is not None:
+        keep_input.append((ijk, off))
     del ijk
     src = binding.tc_batch_from_ijk(d_ijk, off)
     torch.cuda.synchronize()
@@ -325,6 +451,13 @@ def main():
     binding.tc_profile_disable()
     elapsed = t1 - t0
     ms_step = elapsed * 1e3 / args.steps
+    # the same steps without the timing events (their cost, beside the headline)
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for _ in range(args.steps):
+        run_step(binding, src)
+    torch.cuda.synchronize()
+    ms_step_plain = (time.perf_counter() - t2) * 1e3 / args.steps
 
     # per-op breakdown (separate, untimed-by-the-step loop): pass and enumeration
     ops = op_medians(binding, torch, np, src)
@@ -337,6 +470,13 @@ def main():
            "ops": ops48,
            "pass_ratio_b48_over_b16": {k: ops48[k]["ms_pass_median"] / ops[k]["ms_pass_median"] for k in ops}}
     del src48
+    # B=2 (resolution 16): the smallest batch, for the flatness in B
+    ijk2, off2 = synth.make_config(1)
+    src2 = binding.tc_batch_from_ijk(torch.from_numpy(ijk2).cuda(), off2)
+    b2 = {"workload": synth.CONFIG_NAMES[1], "grids": int(len(off2) - 1), "input_voxels": int(off2[-1]),
+          "ops": op_medians(binding, torch, np, src2)}
+    del src2
+    pyr = pyramid(binding, torch, np, synth)
 
     # the rows beyond the step: stride-1 kernel-K targets and masked refine (60% kept)
     gen = torch.Generator(device="cuda").manual_seed(11)
@@ -363,37 +503,34 @@ def main():
     avg_ms = k_ms / max(k_n, 1)
     avg_bytes = bytes_per_step / launches_per_step
     achieved = avg_bytes / (avg_ms * 1e-3) / 1e9 if k_n else None
+    tag = WORKLOAD_TAGS.get(args.config, f"config{args.config}")
     roofline = {"bound": "hbm", "kernel": args.roofline_kernel, "achieved": achieved, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": (achieved / HBM_PEAK_GBS) if achieved else None,
-                "traffic": recorded_traffic(args.roofline_kernel, WORKLOAD_TAGS.get(args.config, f"config{args.config}")),
+                "traffic": recorded_traffic(args.roofline_kernel, tag),
                 "avg_launch_ms": avg_ms, "launches": k_n, "algorithmic_bytes_per_launch": avg_bytes}
+    trace_ms = recorded_trace_ms(args.roofline_kernel, tag)
+    if trace_ms:
+        # the kernel's own duration in the rocprofv3 trace of the same timed
+        # launches (the events above also hold each launch's dispatch)
+        roofline["trace_avg_launch_ms"] = trace_ms
+        roofline["achieved_trace"] = avg_bytes / (trace_ms * 1e-3) / 1e9
+        roofline["frac_trace"] = roofline["achieved_trace"] / HBM_PEAK_GBS
 
+    large_input = []
+    large = None if args.no_large else measure_large(binding, torch, np, synth, keep_input=large_input)
     cpu = None
     if not args.no_cpu_baseline:
-        import oracle
-        t = time.perf_counter()
-        cv, reps = 0, 0
-        while True:  # whole steps of the CPU oracle until at least 10 s have passed
-            for op, f in STEP_OPS:
-                r = oracle.run(op, f, ijk, off, fields=["headers"])
-                cv += int(r["headers"][:, 8].sum())
-            reps += 1
-            if time.perf_counter() - t >= 10.0 or reps >= 50:
-                break
-        dt = time.perf_counter() - t
-        cpu = {"value": cv / dt, "unit": "voxels/s", "cores": 1, "kind": "oracle",
-               "sample": f"{reps} full step(s) of workload {args.config} (all members, {len(STEP_OPS)} ops), "
-                         f"{dt:.1f} s on one host thread"}
-
-    large = None if args.no_large else measure_large(binding, torch, np, synth)
+        cpu = cpu_baseline(np, ijk, off, large_input[0] if large_input else None)
 
     rec = {
         "metric": METRIC, "value": voxels / elapsed, "unit": "voxels/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "warmup": args.warmup, "ms_per_step": ms_step, "ms_per_step_unprofiled": ms_step_plain,
+        "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "int32", "data": "synthetic",
         "config": {"workload": synth.CONFIG_NAMES[args.config], "grids": int(len(off) - 1),
                    "input_voxels": int(off[-1]), "ops": [f"{o}x{f}" for o, f in STEP_OPS]},
-        "roofline": roofline, "cpu_baseline": cpu, "ops": ops, "b48": b48, "more_ops": extra,
+        "roofline": roofline, "cpu_baseline": cpu, "ops": ops, "b48": b48, "b2": b2, "pyramid": pyr,
+        "more_ops": extra,
         "from_ijk": time_from_ijk(binding, torch, np, d_ijk, off, 20),
         "from_points": time_from_points(binding, torch, np, d_ijk, off, 20),
         "kernel_maps": time_kernel_maps(binding, torch, np, src, 20), "large": large,

@@ -29,9 +29,11 @@
  *     readback (TC_ERR_OVERFLOW, no batch), before any output is allocated.
  *   - The kernels that write a batch's leaf masks check their indices; a failed
  *     check (a library defect, never an input property) is reported as
- *     TC_ERR_INTERNAL by the first call that blocks on the batch afterwards
- *     (tc_batch_voxel_total, tc_batch_read_headers, tc_enumerate_ijk,
- *     tc_build_kernel_map, or a pass that reads it), and by every later one.
+ *     TC_ERR_INTERNAL: by the pass itself when it ends on the readback of the
+ *     batch's headers (small batches, see tc_build_batched_topology), else by
+ *     the first call that blocks on the batch afterwards (tc_batch_voxel_total,
+ *     tc_batch_read_headers, tc_enumerate_ijk, tc_build_kernel_map, or a pass
+ *     that reads it), and by every later one.
  *   - Calls on different streams or threads are independent. A tc_grid_batch is
  *     immutable after creation and may be read concurrently.
  *   - Coordinates are int32 voxel indices; counts are int32 (nodes) or int64
@@ -212,9 +214,16 @@ tc_status tc_batch_from_points(const float* d_xyz, const int64_t* h_offsets, int
  * (PR page section 1: emission, sorts, dedup, single readback, one allocation,
  * writers; section 2: box-dilate and pads; factors 4, 8 and k3s2 chain passes).
  *   op      a tc_op; factor as documented at tc_op.
- * `src` is borrowed and never modified. Blocks exactly once per pass, on the
- * readback of per-grid node counts; on return the host counts in
- * tc_batch_info are valid and device arrays are valid in stream order.
+ * `src` is borrowed and never modified. Blocks exactly once per pass, on one
+ * readback; on return the host counts in tc_batch_info are valid and device
+ * arrays are valid in stream order. Small batches (an output laid out by
+ * capacities that fits in 32 MiB: at most 8 / 1 / 27 / 8 output leaves per
+ * source leaf for refine / coarsen / dilate / pads, the tile and lower
+ * candidates for the nodes, at most 1024 members and 262144 leaf slots) take
+ * their one allocation before any launch and read back all headers at the end
+ * (the voxel total is then known too); their arrays sit at capacity offsets
+ * inside the buffer and buffer_bytes is the capacity. Larger batches read the
+ * per-grid node counts back first and allocate exactly.
  * Returns TC_ERR_OVERFLOW (and no batch) when any output voxel would leave int32,
  * TC_ERR_UNSUPPORTED for a non-power-of-two refine/coarsen factor. */
 tc_status tc_build_batched_topology(const tc_grid_batch* src, int32_t op, int32_t factor,

@@ -158,15 +158,24 @@ def test_torch_allocator_uses_the_given_stream():
 
 
 def test_writer_flag_surfaces_as_internal_error():
-    """A batch whose writers flag an inconsistency (forced from the host by the
-    testing hook) is returned, but its first blocking read fails with
-    TC_ERR_INTERNAL, as does every later read and every pass that reads it; in
-    a chain the flagged intermediate fails the call."""
+    """Writers that flag an inconsistency (forced from the host by the testing
+    hook): a small batch's pass, which ends on a readback of its headers and
+    status, fails itself with TC_ERR_INTERNAL; a large batch (exact layout,
+    readback before its writers) is returned, but its first blocking read fails,
+    as does every later read and every pass that reads it; in a chain the
+    flagged intermediate fails the call."""
     import torch
     ijk, off = synth.make_config(1)
     src = binding.tc_batch_from_ijk(torch.from_numpy(ijk).cuda(), off)
     binding.tc_debug_inject_flags(2)
-    bad = binding.tc_build_batched_topology(src, "refine", 2)
+    with pytest.raises(binding.TopoError) as e:
+        binding.tc_build_batched_topology(src, "refine", 2)
+    assert e.value.status == binding.TC_ERR_INTERNAL
+    # more than 1024 members take the exact-layout pass
+    many_ijk, many_off = synth.concat_members([np.array([[7 * g, -3 * g, g]], np.int32) for g in range(1100)])
+    many = binding.tc_batch_from_ijk(torch.from_numpy(many_ijk).cuda(), many_off)
+    binding.tc_debug_inject_flags(2)
+    bad = binding.tc_build_batched_topology(many, "refine", 2)
     for read in (bad.voxel_total, bad.headers, bad.ijk, bad.voxel_total):
         with pytest.raises(binding.TopoError) as e:
             read()
@@ -174,6 +183,8 @@ def test_writer_flag_surfaces_as_internal_error():
     with pytest.raises(binding.TopoError) as e:
         binding.tc_build_batched_topology(bad, "coarsen", 2)
     assert e.value.status == binding.TC_ERR_INTERNAL
+    good_many = binding.tc_build_batched_topology(many, "refine", 2)
+    assert_same(gpu_fields(good_many), oracle.run("refine", 2, many_ijk, many_off), "many members after the flag")
     binding.tc_debug_inject_flags(2)  # the first pass of the chain is flagged
     with pytest.raises(binding.TopoError) as e:
         binding.tc_build_batched_topology(src, "refine", 4)

@@ -43,22 +43,15 @@ int current_device() {
 
 namespace tc {
 
-tc_grid_batch* new_batch(int32_t B, const int32_t* rb, const OutAlloc& oa) {
+// A batch handle with its buffer allocated for `layout` (counts still unset).
+static tc_grid_batch* alloc_batch(int32_t B, const Layout& layout, const OutAlloc& oa) {
   tc_grid_batch* b = new tc_grid_batch();
   try {
     b->B = B;
-    b->n2 = rb[1];
-    b->n1 = rb[2];
-    b->nl = rb[3];
-    b->h_upper.resize(B);
-    b->h_lower.resize(B);
-    b->h_leaf.resize(B);
-    for (int32_t g = 0; g < B; ++g) {
-      b->h_upper[g] = rb[4 + 3 * g];
-      b->h_lower[g] = rb[4 + 3 * g + 1];
-      b->h_leaf[g] = rb[4 + 3 * g + 2];
-    }
-    b->layout = make_layout(B, b->n2, b->n1, b->nl);
+    b->h_upper.assign(B, 0);
+    b->h_lower.assign(B, 0);
+    b->h_leaf.assign(B, 0);
+    b->layout = layout;
     b->bytes = b->layout.total;
     b->stream = oa.stream;
     b->device = current_device();
@@ -80,20 +73,60 @@ tc_grid_batch* new_batch(int32_t B, const int32_t* rb, const OutAlloc& oa) {
   return b;
 }
 
-tc_grid_batch* copy_batch(const tc_grid_batch* src, const OutAlloc& oa) {
-  std::vector<int32_t> rb(4 + 3 * (size_t)src->B);
-  rb[0] = 0;
-  rb[1] = src->n2;
-  rb[2] = src->n1;
-  rb[3] = src->nl;
-  for (int32_t g = 0; g < src->B; ++g) {
-    rb[4 + 3 * g] = src->h_upper[g];
-    rb[4 + 3 * g + 1] = src->h_lower[g];
-    rb[4 + 3 * g + 2] = src->h_leaf[g];
+tc_grid_batch* new_batch(int32_t B, const int32_t* rb, const OutAlloc& oa) {
+  tc_grid_batch* b = alloc_batch(B, make_layout(B, rb[1], rb[2], rb[3]), oa);
+  b->n2 = rb[1];
+  b->n1 = rb[2];
+  b->nl = rb[3];
+  for (int32_t g = 0; g < B; ++g) {
+    b->h_upper[g] = rb[4 + 3 * g];
+    b->h_lower[g] = rb[4 + 3 * g + 1];
+    b->h_leaf[g] = rb[4 + 3 * g + 2];
   }
-  tc_grid_batch* b = new_batch(src->B, rb.data(), oa);
+  return b;
+}
+
+tc_grid_batch* new_batch_capacity(int32_t B, i64 n2_cap, i64 n1_cap, i64 nl_cap, const OutAlloc& oa) {
+  return alloc_batch(B, make_layout(B, n2_cap, n1_cap, nl_cap), oa);
+}
+
+void set_counts_from_headers(tc_grid_batch* b, const tc_grid_header* h) {
+  const int32_t B = b->B;
+  i64 n2 = 0, n1 = 0, nl = 0, nv = 0;
+  for (int32_t g = 0; g < B; ++g) {
+    if (h[g].upper_begin != n2 || h[g].lower_begin != n1 || h[g].leaf_begin != nl || h[g].voxel_begin != nv ||
+        h[g].upper_count < 0 || h[g].lower_count < 0 || h[g].leaf_count < 0 || h[g].voxel_count < 0)
+      throw Error(TC_ERR_INTERNAL, "pass: inconsistent header counts");
+    b->h_upper[g] = h[g].upper_count;
+    b->h_lower[g] = h[g].lower_count;
+    b->h_leaf[g] = h[g].leaf_count;
+    n2 += h[g].upper_count;
+    n1 += h[g].lower_count;
+    nl += h[g].leaf_count;
+    nv += h[g].voxel_count;
+  }
+  // the arrays sit at capacity offsets: the counts must fit the capacities
+  const Layout& L = b->layout;
+  if ((size_t)n2 * 16 > L.upper_key - L.upper_origin || (size_t)n1 * 16 > L.lower_first - L.lower_origin ||
+      (size_t)nl * 16 > L.leaf_parent - L.leaf_origin)
+    throw Error(TC_ERR_INTERNAL, "pass: counts above the output capacities");
+  b->n2 = (int32_t)n2;
+  b->n1 = (int32_t)n1;
+  b->nl = (int32_t)nl;
+  b->vox_total = nv;
+  b->vox_known = true;
+}
+
+tc_grid_batch* copy_batch(const tc_grid_batch* src, const OutAlloc& oa) {
+  tc_grid_batch* b = alloc_batch(src->B, src->layout, oa);
+  b->n2 = src->n2;
+  b->n1 = src->n1;
+  b->nl = src->nl;
+  b->h_upper = src->h_upper;
+  b->h_lower = src->h_lower;
+  b->h_leaf = src->h_leaf;
   try {
-    // identical counts give the identical layout, so one copy moves every array
+    // the same layout (exact or by capacities), so one copy moves every array
     hip_check(hipMemcpyAsync(b->buffer, src->buffer, src->bytes, hipMemcpyDeviceToDevice, oa.stream), "copy batch");
   } catch (...) {
     free_batch(b);

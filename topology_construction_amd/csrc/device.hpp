@@ -90,6 +90,39 @@ __device__ __forceinline__ int select_bit(uint64_t w, int r) {
   return pos;
 }
 
+// Quads (4 consecutive lanes): lane q of a quad reads lane p_q of the same
+// quad (DPP quad permutation). A DPP read from a lane that EXEC disables
+// yields 0, so the permutation must run with the whole quad active: the empty
+// volatile asm on its result keeps the compiler from moving it into a branch
+// taken by part of the quad (it would otherwise fold `cond ? x : perm(y)` into
+// a perm executed only by the lanes where cond is false). Call it from code
+// every lane of the quad executes.
+template <int p0, int p1, int p2, int p3>
+__device__ __forceinline__ int quad_perm32(int v) {
+  int r = __builtin_amdgcn_update_dpp(0, v, p0 | (p1 << 2) | (p2 << 4) | (p3 << 6), 0xf, 0xf, false);
+  asm volatile("" : "+v"(r));
+  return r;
+}
+template <int p0, int p1, int p2, int p3>
+__device__ __forceinline__ uint64_t quad_perm64(uint64_t v) {
+  const uint32_t lo = (uint32_t)quad_perm32<p0, p1, p2, p3>((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)quad_perm32<p0, p1, p2, p3>((int)(uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+template <int k>  // lane k of the quad, to all four
+__device__ __forceinline__ int quad_bcast32(int v) {
+  return quad_perm32<k, k, k, k>(v);
+}
+// As quad_bcast32 with k known only after unrolling (k must fold to a constant).
+__device__ __forceinline__ int quad_bcast32(int v, int k) {
+  switch (k & 3) {
+    case 0: return quad_bcast32<0>(v);
+    case 1: return quad_bcast32<1>(v);
+    case 2: return quad_bcast32<2>(v);
+    default: return quad_bcast32<3>(v);
+  }
+}
+
 __device__ __forceinline__ int wave_min_i32(int v) {
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) v = min(v, __shfl_xor(v, d, kWave));
@@ -128,6 +161,58 @@ __device__ __forceinline__ void leaf_stats(const uint64_t W[8], uint64_t& prefix
     return;
   }
   // y extent: non-zero bytes of the OR of all words; z extent: OR of those bytes
+  int ymin = 8, ymax = -1;
+  uint64_t zor = 0;
+#pragma unroll
+  for (int y = 0; y < 8; ++y) {
+    const uint64_t byte = (orw >> (8 * y)) & 0xffull;
+    if (byte) {
+      ymin = min(ymin, y);
+      ymax = max(ymax, y);
+    }
+    zor |= byte;
+  }
+  const int zmin = __builtin_ctzll(zor);
+  const int zmax = 63 - __builtin_clzll(zor);
+  box = (uint32_t)(xmin | (xmax << 3) | (ymin << 6) | (ymax << 9) | (zmin << 12) | (zmax << 15));
+}
+
+// leaf_stats for a leaf whose 8 words are spread over a quad (lane s of the
+// quad holds words 2s and 2s+1): the same prefix word, count and packed box,
+// on every lane of the quad. `sub` is the lane's index in the quad.
+__device__ __forceinline__ void quad_leaf_stats(uint64_t w0, uint64_t w1, int sub, uint64_t& prefix, int& count,
+                                                uint32_t& box) {
+  const int c0 = __popcll(w0), cs = c0 + __popcll(w1);
+  int inc = cs;  // inclusive scan of the lanes' counts over the quad
+  {
+    const int t = quad_perm32<0, 0, 1, 2>(inc);
+    if (sub >= 1) inc += t;
+  }
+  {
+    const int t = quad_perm32<0, 0, 0, 1>(inc);
+    if (sub >= 2) inc += t;
+  }
+  const int ex = inc - cs;  // voxels in words < 2 sub
+  count = quad_bcast32<3>(inc);
+  // field w-1 (9 bits each) = voxels in words < w: this lane's w = 2 sub + 1 and w = 2 sub
+  uint64_t pf = (uint64_t)(ex + c0) << (18 * sub);
+  if (sub > 0) pf |= (uint64_t)ex << (18 * sub - 9);
+  pf |= quad_perm64<1, 0, 3, 2>(pf);
+  pf |= quad_perm64<2, 3, 0, 1>(pf);
+  prefix = pf;
+  int xmin = w0 ? 2 * sub : (w1 ? 2 * sub + 1 : 8);
+  int xmax = w1 ? 2 * sub + 1 : (w0 ? 2 * sub : -1);
+  xmin = min(xmin, quad_perm32<1, 0, 3, 2>(xmin));
+  xmin = min(xmin, quad_perm32<2, 3, 0, 1>(xmin));
+  xmax = max(xmax, quad_perm32<1, 0, 3, 2>(xmax));
+  xmax = max(xmax, quad_perm32<2, 3, 0, 1>(xmax));
+  uint64_t orw = w0 | w1;
+  orw |= quad_perm64<1, 0, 3, 2>(orw);
+  orw |= quad_perm64<2, 3, 0, 1>(orw);
+  if (!orw) {
+    box = kEmptyBox;
+    return;
+  }
   int ymin = 8, ymax = -1;
   uint64_t zor = 0;
 #pragma unroll

@@ -599,8 +599,8 @@ tc_grid_batch* build_from_ijk(const int32_t* d_ijk, const int64_t* h_off, int32_
     tree_leaf_stats(ov, post.at<uint32_t>(o_box), post.at<int32_t>(o_inrun), post.at<i64>(o_part), s);
     apply_debug_inject(ts.flags, s);  // k_voxel_leaf's checks ran after the readback: finalize copies the word
     tree_finalize_leaves(ov, post.at<uint32_t>(o_box), post.at<int32_t>(o_inrun), post.at<i64>(o_part), 256,
-                         post.at<i64>(o_gvb), post.at<int32_t>(o_bb), (const int32_t*)ts.grid_info,
-                         (const int32_t*)ts.flags, s);
+                         post.at<i64>(o_gvb), post.at<int32_t>(o_bb), (const int32_t*)ts.grid_info, ts.flags,
+                         ts.readback + 3, s);
   } catch (...) {
     free_batch(out);
     throw;

@@ -310,6 +310,7 @@ struct TreeScratch {
   int32_t* flags;            // [1] bit 0 overflow, bit 1 internal error (inside readback)
   void* scan_tmp;            // scan scratch: scan_tmp_bytes over cap_tiles (i32) and cap_cands (i64)
   i64 cap_tiles, cap_cands;
+  bool cand_counts_ready;    // the marking wrote cand_prefix and cand_counts (else the counts stage does)
 };
 
 // Launch groups (implemented in tree.hip).
@@ -325,9 +326,13 @@ int32_t bbox_replicas(int32_t B);  // replicas of the per-grid bbox accumulators
 // run of `gran` leaves (gran divides 256), the run's voxel sum (vox_part) and
 // every leaf's voxels before it inside its run (leaf_inrun).
 // `flags` is the builder's flag word; its final value goes to out.status.
+// d_L (device) holds the leaf count; out.n_leaf is that count, or a capacity
+// above it when the batch's arrays were laid out by capacities (small path only).
 void tree_finalize_leaves(const GridView& out, const uint32_t* leaf_box, const int32_t* leaf_inrun, i64* vox_part,
-                          i64 gran, i64* gvb, int32_t* bbox_accum, const int32_t* grid_info, const int32_t* flags,
-                          hipStream_t s);
+                          i64 gran, i64* gvb, int32_t* bbox_accum, const int32_t* grid_info, int32_t* flags,
+                          const int32_t* d_L, hipStream_t s);
+// Whether the one-launch finalize takes L leaves (or a capacity of L) of B grids.
+bool finalize_small_fits(i64 L, int32_t B, i64 gran);
 void tree_enumerate(const GridView& v, int32_t* ijk, hipStream_t s);
 
 // Allocation of the single output buffer of a batch.
@@ -381,6 +386,10 @@ namespace tc {
 // Creates the output batch from the readback of a tree assembly (counts per
 // grid) and allocates its buffer; throws on failure (nothing leaked).
 tc_grid_batch* new_batch(int32_t B, const int32_t* readback, const OutAlloc& oa);
+// A batch whose arrays are laid out by capacities (counts set later from its
+// headers by set_counts_from_headers, which also makes the voxel total known).
+tc_grid_batch* new_batch_capacity(int32_t B, i64 n2_cap, i64 n1_cap, i64 nl_cap, const OutAlloc& oa);
+void set_counts_from_headers(tc_grid_batch* b, const tc_grid_header* h);
 void free_batch(tc_grid_batch* b);
 tc_grid_batch* copy_batch(const tc_grid_batch* src, const OutAlloc& oa);  // same counts, one D2D copy
 // Throws TC_ERR_INTERNAL when the batch's writers flagged a failed consistency

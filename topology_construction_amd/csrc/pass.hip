@@ -66,6 +66,19 @@ __device__ __forceinline__ bool leaf_ok(i64 l) { return l >= -(1ll << 28) && l <
 
 __device__ __forceinline__ void set_flag(int32_t* flags, int f) { atomicOr(flags, f); }
 
+// One wave holds the 64 words of candidate c's 16^3 leaf mask (lane = word):
+// writes the word, the word's exclusive popcount prefix and the candidate's
+// packed count (leaves | non-empty << 32). Every lane of the wave must call it.
+__device__ __forceinline__ void store_candidate(i64 c, u64 word, u64* cand_child, uint16_t* cand_prefix,
+                                                i64* cand_counts) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int cnt = popc64(word);
+  const int inc = wave_incl_scan(cnt);
+  cand_child[c * 64 + lane] = word;
+  cand_prefix[c * 64 + lane] = (uint16_t)(inc - cnt);
+  if (lane == kWave - 1) cand_counts[c] = (i64)inc | ((i64)(inc > 0 ? 1 : 0) << 32);
+}
+
 // ------------------------------------------------------------------ stage: tiles
 __global__ void __launch_bounds__(256) k_tile_candidates(const int4* upper_origin, i64 n, int op, int m,
                                                          Key128* keys, uint32_t* vals) {
@@ -1094,17 +1107,18 @@ __device__ __forceinline__ bool subblock_nonempty(const u64 W[8], const I3& q) {
 // so the flush is a plain store of all 64 words (no zero-fill needed); coarsen
 // ORs its non-zero words with device-scope atomics, far fewer than one per
 // target leaf. (Box ops mark from the target side, below.)
-__device__ __forceinline__ void lds_mark(unsigned long long* s_mask, int j, i64 px, i64 py, i64 pz) {
-  const int bit = (int)((px * 16 + py) * 16 + pz);
-  atomicOr(&s_mask[j * 64 + (bit >> 6)], 1ull << (bit & 63));
-}
 
+// Refine: one workgroup per source lower marks, in LDS copies of its 8 target
+// lowers' 16^3 masks, the non-empty 2^3 sub-blocks of its leaves; each target
+// lower has this one source, so the workgroup stores the whole masks with their
+// prefixes and counts.
 __global__ void __launch_bounds__(256) k_leaf_mark_lower(const int4* leaf_origin, const u64* leaf_mask,
                                                          const int32_t* lower_first, const u64* lower_mask,
                                                          const uint16_t* lower_prefix, int op, int m,
                                                          const int32_t* lower_nbr, const int32_t* d_num_cands,
-                                                         u64* cand_child, int32_t* flags) {
-  constexpr int kFlush = 8 * 64 / 256;  // target words per thread (m <= 8)
+                                                         u64* cand_child, uint16_t* cand_prefix,
+                                                         i64* cand_counts, int32_t* flags) {
+  constexpr int kFlush = 8 * 64 / 256;  // target words per thread (m == 8)
   constexpr int kPer = 2;               // leaves per thread in flight
   __shared__ unsigned long long s_mask[8 * 64];
   const i64 l = blockIdx.x;
@@ -1133,7 +1147,7 @@ __global__ void __launch_bounds__(256) k_leaf_mark_lower(const int4* leaf_origin
       if (k0 + u * 256 + (int)threadIdx.x >= count) continue;
       const i64 mx = o[u].x >> 3, my = o[u].y >> 3, mz = o[u].z >> 3;  // leaf coordinates
       const i64 lx = mx & 15, ly = my & 15, lz = mz & 15;              // position inside the lower
-      if (op == TC_OP_REFINE) {
+      {
         const int j = octant_index(lx >> 3, ly >> 3, lz >> 3);  // all children share one target lower
 #pragma unroll
         for (int qx = 0; qx < 2; ++qx) {
@@ -1154,27 +1168,75 @@ __global__ void __launch_bounds__(256) k_leaf_mark_lower(const int4* leaf_origin
           // children with this qx share the word x*4 + (y >> 2) of the target mask
           if (word) atomicOr(&s_mask[j * 64 + x * 4 + (((2 * ly) & 15) >> 2)], word);
         }
-      } else {  // coarsen
-        lds_mark(s_mask, 0, (mx >> 1) & 15, (my >> 1) & 15, (mz >> 1) & 15);
       }
     }
   }
   __syncthreads();
+  // wave v of round r flushes target 4r + v (its 64 words), whole waves at a time
 #pragma unroll
   for (int r = 0; r < kFlush; ++r) {
     const int k = r * 256 + threadIdx.x;
-    if (k >= m * 64) break;
-    const int w = k & 63;
     const u64 word = s_mask[k];
-    if (op != TC_OP_REFINE && !word) continue;
-    const int32_t c = nbr[r];
+    const int32_t c = nbr[r];  // uniform per wave
     if (c < 0 || c >= ncand) {
       if (word) set_flag(flags, kFlagInternal);  // a marked target must have a candidate
       continue;
     }
-    if (op == TC_OP_REFINE) cand_child[(i64)c * 64 + w] = word;
-    else atomicOr((unsigned long long*)&cand_child[(i64)c * 64 + w], word);
+    store_candidate(c, word, cand_child, cand_prefix, cand_counts);
   }
+}
+
+// Coarsen: one wave per candidate lower T, pulling from the source lowers of its
+// 8 octants (cand_src). Target leaf t = (tx, ty, tz) in [0,16)^3 holds a voxel
+// exactly when one of the 2^3 source leaves 2(t & 7) + {0,1}^3 of the source
+// lower in octant t >> 3 exists (a source leaf is never empty), so the target
+// mask is the OR of 2x2x2 blocks of the source lowers' 16^3 masks; the leaves
+// themselves are not read. Lane w builds target word w (x = w >> 2, rows
+// y = 4 (w & 3) + r, every z) and the wave stores it with prefix and count.
+__global__ void __launch_bounds__(256) k_mark_coarsen(const int32_t* cand_src, const int32_t* d_num_cands,
+                                                      const u64* src_lower_mask, int32_t n_src_lower,
+                                                      u64* cand_child, uint16_t* cand_prefix, i64* cand_counts,
+                                                      int32_t* flags) {
+  const i64 c = (i64)blockIdx.x * 4 + threadIdx.x / kWave;
+  if (c >= *d_num_cands) return;  // uniform per wave
+  const int w = threadIdx.x & (kWave - 1);
+  const int tx = w >> 2, yq = w & 3;
+  int32_t s[2];
+  u64 lo_w[2][2], hi_w[2][2];  // [jz][a]: source rows 8(yq&1) .. +3 and +4 .. +7 of column 2(tx&7) + a
+#pragma unroll
+  for (int jz = 0; jz < 2; ++jz) {
+    s[jz] = cand_src[c * 8 + octant_index(tx >> 3, yq >> 1, jz)];
+    if (s[jz] >= n_src_lower) {
+      set_flag(flags, kFlagInternal);
+      s[jz] = -1;
+    }
+    const i64 ls = s[jz] >= 0 ? s[jz] : 0;
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      const i64 sw = ls * 64 + (2 * (tx & 7) + a) * 4 + 2 * (yq & 1);
+      lo_w[jz][a] = src_lower_mask[sw];
+      hi_w[jz][a] = src_lower_mask[sw + 1];
+    }
+  }
+  u64 word = 0;
+#pragma unroll
+  for (int jz = 0; jz < 2; ++jz) {
+    if (s[jz] < 0) continue;
+    const u64 x0 = lo_w[jz][0] | lo_w[jz][1], x1 = hi_w[jz][0] | hi_w[jz][1];  // both source columns
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      // source rows 2r and 2r + 1 of the 8: rows 0..3 in x0, 4..7 in x1 (16 bits per row)
+      const u64 src = r < 2 ? x0 : x1;
+      const int rr = (2 * r) & 3;
+      uint32_t v = (uint32_t)((src >> (16 * rr)) | (src >> (16 * (rr + 1)))) & 0xffffu;
+      v = (v | (v >> 1)) & 0x5555u;  // z pairs -> even bits
+      v = (v | (v >> 1)) & 0x3333u;
+      v = (v | (v >> 2)) & 0x0f0fu;
+      v = (v | (v >> 4)) & 0x00ffu;  // 8 target z values
+      word |= (u64)v << (16 * r + 8 * jz);
+    }
+  }
+  store_candidate(c, word, cand_child, cand_prefix, cand_counts);
 }
 
 // ------------------------------------------------------------------ stage: leaves, box ops (pull)
@@ -1263,12 +1325,40 @@ __device__ __forceinline__ void mark_box_leaf(const u64 W[8], uint32_t pos, int 
 
 constexpr int kMarkIlp = 2;  // leaves in flight per thread
 
+// Erosion of a lower's 16^3 leaf mask by the box [lo, hi]^3 inside the lower:
+// bit p stays set when p + t is set for every t in the box (positions whose
+// box reaches outside the lower are dropped). Lane w of one wave holds word w
+// (x = w >> 2, rows y = 4 (w & 3) .. +3, bit (y & 3) * 16 + z); every lane of
+// the wave must call it.
+template <int lo, int hi>
+__device__ __forceinline__ u64 erode_lower_mask(u64 m) {
+  const int w = threadIdx.x & (kWave - 1);
+  constexpr u64 kNoZ15 = 0x7fff7fff7fff7fffull, kNoZ0 = 0xfffefffefffefffeull;
+  u64 e = m;  // z: neighbours z + 1 (bit above) and z - 1 (bit below) inside the row
+  if (hi > 0) e &= (m >> 1) & kNoZ15;
+  if (lo < 0) e &= (m << 1) & kNoZ0;
+  // y: rows y + 1 / y - 1, across words for the rows at a word's edge
+  const u64 up = (u64)__shfl_down((unsigned long long)e, 1, kWave);  // word w + 1
+  const u64 dn = (u64)__shfl_up((unsigned long long)e, 1, kWave);    // word w - 1
+  u64 f = e;
+  if (hi > 0) f &= (e >> 16) | ((w & 3) < 3 ? up << 48 : 0ull);
+  if (lo < 0) f &= (e << 16) | ((w & 3) > 0 ? dn >> 48 : 0ull);
+  // x: words w + 4 / w - 4
+  const u64 xp = (u64)__shfl_down((unsigned long long)f, 4, kWave);
+  const u64 xm = (u64)__shfl_up((unsigned long long)f, 4, kWave);
+  u64 g = f;
+  if (hi > 0) g &= (w >> 2) < 15 ? xp : 0ull;
+  if (lo < 0) g &= (w >> 2) > 0 ? xm : 0ull;
+  return g;
+}
+
 template <int lo, int hi>  // the box [lo, hi]^3: dilate [-1, 1], pads [-1, 0] and [0, 1]
 __global__ void __launch_bounds__(256) k_leaf_mark_box(const int32_t* cand_src, const int32_t* d_num_cands,
                                                        int32_t B, const tc_grid_header* src_headers,
                                                        const u64* src_lower_mask, const uint16_t* src_lower_prefix,
                                                        const int32_t* src_lower_first, const u64* src_leaf_mask,
                                                        int32_t n_src_lower, int32_t n_src_leaf, u64* cand_child,
+                                                       uint16_t* cand_prefix, i64* cand_counts,
                                                        int32_t* flags) {
   const PullTable& tab = pull_table<lo, hi>();
   const int nlive = tab.n;
@@ -1277,6 +1367,9 @@ __global__ void __launch_bounds__(256) k_leaf_mark_box(const int32_t* cand_src, 
   __shared__ int32_t s_excl[kLiveMax + 1];  // exclusive scan of the items' reaching leaves
   __shared__ uint16_t s_item[kLiveMax];     // js * 64 + w of each live item
   __shared__ unsigned long long s_mask[64];
+  __shared__ u64 s_fm[kLiveMax];            // the item's mask of leaves to visit
+  __shared__ u64 s_center[64];              // 16^3 mask of the co-located source lower
+  __shared__ u64 s_skip[64];                // its leaves that spill onto marked positions only
   __shared__ int32_t s_wave[256 / kWave];
   const int tid = threadIdx.x;
   // An output coordinate leaves int32 exactly when a grid's bbox, widened by
@@ -1299,7 +1392,6 @@ __global__ void __launch_bounds__(256) k_leaf_mark_box(const int32_t* cand_src, 
   const i64 per = na > 0 ? (ncand + na - 1) / na : 0;
   const i64 c0 = (i64)blockIdx.x < na ? xcd_block(blockIdx.x, na) * per : ncand;
   for (i64 c = c0; c < ncand && c < c0 + per; ++c) {
-    if (tid < 64) s_mask[tid] = 0;
     u64 wd[kLivePer];
     int32_t base[kLivePer];
     int cnt[kLivePer];
@@ -1335,6 +1427,23 @@ __global__ void __launch_bounds__(256) k_leaf_mark_box(const int32_t* cand_src, 
     for (int k = 0; k < kLivePer; ++k) {
       if (sl[k] < 0) wd[k] = 0;
       base[k] = sl[k] >= 0 ? lfirst[k] + lpre[k] : 0;
+      if ((item[k] >> 6) == 13 && tid * kLivePer + k < nlive) s_center[item[k] & 63] = wd[k];
+    }
+    // The co-located source lower (slot 13, every word live) marks its own
+    // leaf positions (the box holds offset 0 and a source leaf is never
+    // empty): its mask goes into the candidate's as is. Its leaves inside the
+    // mask eroded by the box spill only onto positions it already marks, so
+    // they are not visited.
+    __syncthreads();
+    if (tid < 64) {  // wave 0
+      const u64 m = s_center[tid];
+      s_mask[tid] = m;
+      s_skip[tid] = erode_lower_mask<lo, hi>(m);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kLivePer; ++k) {
+      if ((item[k] >> 6) == 13) fm[k] &= ~s_skip[item[k] & 63];
       cnt[k] = popc64(wd[k] & fm[k]);
       sum += cnt[k];
     }
@@ -1348,6 +1457,7 @@ __global__ void __launch_bounds__(256) k_leaf_mark_box(const int32_t* cand_src, 
         s_base[li] = base[k];
         s_excl[li] = ex;
         s_item[li] = (uint16_t)item[k];
+        s_fm[li] = fm[k];
       }
       ex += cnt[k];
     }
@@ -1370,7 +1480,7 @@ __global__ void __launch_bounds__(256) k_leaf_mark_box(const int32_t* cand_src, 
           }
           const int js = s_item[a] >> 6, w = s_item[a] & 63;
           const u64 word = s_word[a];
-          const int bit = select_bit(word & face_word_mask(js, w, lo, hi), k - s_excl[a]);
+          const int bit = select_bit(word & s_fm[a], k - s_excl[a]);
           const i64 leaf = (i64)s_base[a] + popc64(word & ((1ull << bit) - 1));
           if (leaf < 0 || leaf >= n_src_leaf) {
             set_flag(flags, kFlagInternal);
@@ -1391,7 +1501,7 @@ __global__ void __launch_bounds__(256) k_leaf_mark_box(const int32_t* cand_src, 
         if (lf[u] >= 0) mark_box_leaf(W[u], ps[u], lo, hi, s_mask);
     }
     __syncthreads();
-    if (tid < 64) cand_child[c * 64 + tid] = s_mask[tid];
+    if (tid < 64) store_candidate(c, s_mask[tid], cand_child, cand_prefix, cand_counts);  // wave 0
     __syncthreads();
   }
 }
@@ -1463,9 +1573,20 @@ __device__ __forceinline__ void coarsen_place(u64 out[8], const u64 W[8], const 
 // lookups run in parallel. Also writes the leaf's prefix word, packed local bbox
 // and in-run voxel count.
 // KIND: 0 refine, 1 coarsen; one instantiation each.
+// Output leaf count on the device (the counts stage's total; a launch may be
+// sized by a capacity above it): clamped to the capacity, with a flag if above.
+__device__ __forceinline__ i64 device_count(const int32_t* d_n, i64 cap, int32_t* flags) {
+  i64 n = *d_n;
+  if (n < 0 || n > cap) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) set_flag(flags, kFlagInternal);
+    n = n < 0 ? 0 : cap;
+  }
+  return n;
+}
+
 template <int KIND>
-__global__ void __launch_bounds__(256) k_leaf_gather(const int4* out_origin, const int32_t* leaf_cand, i64 n,
-                                                     const int32_t* cand_src,
+__global__ void __launch_bounds__(256) k_leaf_gather(const int4* out_origin, const int32_t* leaf_cand,
+                                                     const int32_t* d_n, i64 n_cap, const int32_t* cand_src,
                                                      const u64* src_lower_mask, const uint16_t* src_lower_prefix,
                                                      const int32_t* src_lower_first, const u64* src_leaf_mask,
                                                      int32_t n_src_lower, int32_t n_src_leaf,
@@ -1473,6 +1594,8 @@ __global__ void __launch_bounds__(256) k_leaf_gather(const int4* out_origin, con
                                                      uint32_t* leaf_box, int32_t* leaf_inrun,
                                                      i64* vox_part, int32_t* flags) {
   constexpr int lpl = KIND == 0 ? 1 : 4;  // lanes per output leaf
+  const i64 n = device_count(d_n, n_cap, flags);
+  if ((i64)blockIdx.x * (256 / lpl) >= n) return;  // past the leaves (uniform per block)
   const i64 lblk = blockIdx.x;
   const i64 gt = lblk * 256 + threadIdx.x;
   const i64 i = gt / lpl;
@@ -1559,119 +1682,86 @@ __global__ void __launch_bounds__(256) k_leaf_gather(const int4* out_origin, con
 // each side (from the x-neighbour leaf at the ends). The source lookups are
 // split over the four lanes and their results exchanged with shuffles.
 template <int lo, int hi>  // the box [lo, hi]^3: dilate [-1, 1], pads [-1, 0] and [0, 1]
-__global__ void __launch_bounds__(256) k_leaf_gather_box(const int4* out_origin, const int32_t* leaf_cand, i64 n,
-                                                         const int32_t* cand_src,
+__global__ void __launch_bounds__(256) k_leaf_gather_box(const int4* out_origin, const int32_t* leaf_cand,
+                                                         const int32_t* d_n, i64 n_cap, const int32_t* cand_src,
                                                          const u64* src_lower_mask, const uint16_t* src_lower_prefix,
                                                          const int32_t* src_lower_first, const u64* src_leaf_mask,
                                                          int32_t n_src_lower, int32_t n_src_leaf,
                                                          const int32_t* d_num_cands, u64* out_mask, u64* out_prefix,
                                                          uint32_t* leaf_box, int32_t* leaf_inrun,
                                                          i64* vox_part, int32_t* flags) {
-  const i64 lblk = xcd_block(blockIdx.x, gridDim.x);  // contiguous leaves per XCD (shared source leaves)
+  const i64 n = device_count(d_n, n_cap, flags);
+  const i64 nb = (n * 4 + 255) / 256;  // workgroups that hold leaves (the launch may hold more)
+  if ((i64)blockIdx.x >= nb) return;  // uniform per block
+  const i64 lblk = xcd_block(blockIdx.x, nb);  // contiguous leaves per XCD (shared source leaves)
   const i64 gt = lblk * 256 + threadIdx.x;
   const i64 i = gt >> 2;
   const int sub = (int)(gt & 3);
-  const int grp = (int)(threadIdx.x & (kWave - 1)) & ~3;
   // Every load goes to a valid index (n, the candidates, the source lowers and
   // leaves are all non-empty here; index 0 stands in for a missing one) and is
-  // masked afterwards, so each level's loads are in flight together.
-  const i64 ncand = *d_num_cands;
-  const i64 ic = i < n ? i : n - 1;
+  // masked afterwards, so each level's loads are in flight together. Indices
+  // fit 32 bits (source lowers < 2^25, checked by the host).
+  const int32_t ncand = *d_num_cands;
+  const int32_t ic = (int32_t)(i < n ? i : n - 1);
   const int4 o = out_origin[ic];
-  i64 c = leaf_cand[ic];
+  int32_t c = leaf_cand[ic];
   bool valid = i < n;
-  if (valid && (c < 0 || c >= ncand)) {
-    set_flag(flags, kFlagInternal);
-    valid = false;
-  }
+  bool bad = valid && (c < 0 || c >= ncand);
+  valid = valid && !bad;
   if (!valid) c = 0;
   const int lx = (o.x >> 3) & 15, ly = (o.y >> 3) & 15, lz = (o.z >> 3) & 15;
-  // source leaf at leaf offset s = (j/9-1, (j/3)%3-1, j%3-1), s in [-hi, -lo]^3;
-  // this lane resolves j = sub + 4q, level by level so the loads overlap
-  constexpr int kPer = 7;
+  // The source leaves of this output leaf sit at leaf offsets s in [-hi, -lo]^3
+  // (W^3 of them), numbered k = ((sx+hi)*W + (sy+hi))*W + (sz+hi); lane `sub`
+  // resolves k = sub + 4q, level by level so that the loads overlap. The
+  // offsets of slot q for the four lanes come from one packed constant.
+  constexpr int W = hi - lo + 1, NK = W * W * W, kPer = (NK + 3) / 4;
   int32_t sl[kPer], bit[kPer];
   bool use[kPer];
 #pragma unroll
   for (int q = 0; q < kPer; ++q) {
-    const int j = sub + 4 * q;
-    const int sx = j / 9 - 1, sy = (j / 3) % 3 - 1, sz = j % 3 - 1;
-    use[q] = valid && j < 27 && sx >= -hi && sx <= -lo && sy >= -hi && sy <= -lo && sz >= -hi && sz <= -lo;
-    const int px = lx + sx, py = ly + sy, pz = lz + sz;  // -1 .. 16 (j < 27)
-    bit[q] = use[q] ? ((px & 15) * 16 + (py & 15)) * 16 + (pz & 15) : 0;
+    uint32_t pack = 0;  // per lane: (sx+hi) | (sy+hi) << 2 | (sz+hi) << 4 | used << 6
+#pragma unroll
+    for (int l = 0; l < 4; ++l) {
+      const int k = 4 * q + l;
+      if (k < NK) pack |= (uint32_t)((k / (W * W)) | (((k / W) % W) << 2) | ((k % W) << 4) | 64) << (8 * l);
+    }
+    const uint32_t code = (pack >> (8 * sub)) & 0xffu;
+    use[q] = valid && (code & 64u);
+    const int px = lx + (int)(code & 3u) - hi, py = ly + (int)((code >> 2) & 3u) - hi, pz = lz + (int)((code >> 4) & 3u) - hi;
+    bit[q] = ((px & 15) * 16 + (py & 15)) * 16 + (pz & 15);
     sl[q] = cand_src[c * 27 + (use[q] ? index27(px >> 4, py >> 4, pz >> 4) : 13)];
   }
 #pragma unroll
   for (int q = 0; q < kPer; ++q) {
-    if (use[q] && sl[q] >= n_src_lower) {
-      set_flag(flags, kFlagInternal);
-      sl[q] = -1;
-    }
-    if (!use[q]) sl[q] = -1;
+    bad |= use[q] && sl[q] >= n_src_lower;
+    if (!use[q] || sl[q] >= n_src_lower) sl[q] = -1;
   }
   u64 word[kPer];
   int32_t lfirst[kPer];
   uint16_t lpre[kPer];
 #pragma unroll
   for (int q = 0; q < kPer; ++q) {
-    const i64 ls = sl[q] >= 0 ? sl[q] : 0;
-    word[q] = src_lower_mask[ls * 64 + (bit[q] >> 6)];
+    const uint32_t ls = sl[q] >= 0 ? (uint32_t)sl[q] : 0u;
+    word[q] = src_lower_mask[ls * 64u + (uint32_t)(bit[q] >> 6)];
     lfirst[q] = src_lower_first[ls];
-    lpre[q] = src_lower_prefix[ls * 64 + (bit[q] >> 6)];
+    lpre[q] = src_lower_prefix[ls * 64u + (uint32_t)(bit[q] >> 6)];
   }
   int32_t r[kPer];
 #pragma unroll
   for (int q = 0; q < kPer; ++q) {
-    r[q] = -1;
     const int b = bit[q] & 63;
-    if (sl[q] >= 0 && ((word[q] >> b) & 1ull)) {
-      r[q] = lfirst[q] + lpre[q] + popc64(word[q] & ((1ull << b) - 1));
-      if (r[q] < 0 || r[q] >= n_src_leaf) {
-        set_flag(flags, kFlagInternal);
-        r[q] = -1;
-      }
-    }
+    const bool hit = sl[q] >= 0 && ((word[q] >> b) & 1ull);
+    r[q] = lfirst[q] + lpre[q] + popc64(word[q] & ((1ull << b) - 1));
+    const bool out_of_range = hit && (r[q] < 0 || r[q] >= n_src_leaf);
+    bad |= out_of_range;
+    if (!hit || out_of_range) r[q] = -1;
   }
-  const int x0 = 2 * sub;
-  // words x0-1 .. x0+2 of every needed row (sy, sz) of source leaves, all loads
-  // first (leaf 0 stands in for a missing leaf, whose words are then cleared)
-  int32_t R[3][3][3];  // [sz][sy][sx] source leaf index, gathered from the lanes that resolved it
-#pragma unroll
-  for (int sz = -1; sz <= 1; ++sz)
-#pragma unroll
-    for (int sy = -1; sy <= 1; ++sy)
-#pragma unroll
-      for (int sx = -1; sx <= 1; ++sx) {
-        const int j = (sx + 1) * 9 + (sy + 1) * 3 + (sz + 1);
-        R[sz + 1][sy + 1][sx + 1] =
-            (sz < -hi || sz > -lo || sy < -hi || sy > -lo) ? -1 : __shfl(r[j >> 2], grp | (j & 3), kWave);
-      }
-  u64 w[3][3][4];
-#pragma unroll
-  for (int sz = -1; sz <= 1; ++sz) {
-#pragma unroll
-    for (int sy = -1; sy <= 1; ++sy) {
-      if (sz < -hi || sz > -lo || sy < -hi || sy > -lo) continue;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int x = x0 - 1 + k;
-        const int32_t rr = x < 0 ? R[sz + 1][sy + 1][0] : (x > 7 ? R[sz + 1][sy + 1][2] : R[sz + 1][sy + 1][1]);
-        w[sz + 1][sy + 1][k] = src_leaf_mask[(i64)(rr >= 0 ? rr : 0) * 8 + (x & 7)];
-      }
-    }
-  }
-#pragma unroll
-  for (int sz = -1; sz <= 1; ++sz) {
-#pragma unroll
-    for (int sy = -1; sy <= 1; ++sy) {
-      if (sz < -hi || sz > -lo || sy < -hi || sy > -lo) continue;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int x = x0 - 1 + k;
-        const int32_t rr = x < 0 ? R[sz + 1][sy + 1][0] : (x > 7 ? R[sz + 1][sy + 1][2] : R[sz + 1][sy + 1][1]);
-        if (rr < 0) w[sz + 1][sy + 1][k] = 0;
-      }
-    }
-  }
+  if (bad) set_flag(flags, kFlagInternal);
+  // Source rows: lane `sub` loads words 2sub and 2sub+1 of every needed row
+  // (sy, sz) of the centre column of source leaves (one 16-byte load), lane 0
+  // also word 7 of the row's x-1 leaf and lane 3 word 0 of its x+1 leaf; the
+  // words 2sub-1 and 2sub+2 come from the neighbouring lanes of the quad.
+  // Leaf indices resolved by other lanes of the quad arrive by quad broadcasts.
   u64 ys[3][2];
 #pragma unroll
   for (int sz = -1; sz <= 1; ++sz) {
@@ -1679,9 +1769,27 @@ __global__ void __launch_bounds__(256) k_leaf_gather_box(const int4* out_origin,
 #pragma unroll
     for (int sy = -1; sy <= 1; ++sy) {
       if (sz < -hi || sz > -lo || sy < -hi || sy > -lo) continue;
-      const u64* wr = w[sz + 1][sy + 1];
-      xs[sy + 1][0] = wr[1] | (hi > 0 ? wr[0] : 0) | (lo < 0 ? wr[2] : 0);
-      xs[sy + 1][1] = wr[2] | (hi > 0 ? wr[1] : 0) | (lo < 0 ? wr[3] : 0);
+      // source leaves at (sx, sy, sz), sx = -1, 0, 1 (the ones in the box): slot k
+      constexpr int kNone = -1;
+      const int ky = sy + hi, kz = sz + hi;
+      const int kc = ((0 + hi) * W + ky) * W + kz;   // sx = 0
+      const int km = ((-1 + hi) * W + ky) * W + kz;  // sx = -1 (hi > 0)
+      const int kp = ((1 + hi) * W + ky) * W + kz;   // sx = +1 (lo < 0)
+      const int32_t rc = quad_bcast32(r[kc >> 2], kc & 3);
+      const int32_t rm = hi > 0 ? quad_bcast32(r[km >> 2], km & 3) : kNone;
+      const int32_t rp = lo < 0 ? quad_bcast32(r[kp >> 2], kp & 3) : kNone;
+      const int32_t re = sub == 0 ? rm : (sub == 3 ? rp : kNone);  // edge leaf of this lane
+      const ulonglong2 own = reinterpret_cast<const ulonglong2*>(src_leaf_mask)[(i64)(rc >= 0 ? rc : 0) * 4 + sub];
+      const u64 edge = src_leaf_mask[(i64)(re >= 0 ? re : 0) * 8 + (sub == 0 ? 7 : 0)];
+      const u64 wa = rc >= 0 ? (u64)own.x : 0ull, wb = rc >= 0 ? (u64)own.y : 0ull;
+      const u64 we = re >= 0 ? edge : 0ull;
+      // The permutations run on the whole quad before the selects (a select
+      // around them would make them conditional, and lane 0 or 3 then absent).
+      const u64 pl = quad_perm64<0, 0, 1, 2>(wb), pr = quad_perm64<1, 2, 3, 3>(wa);
+      const u64 left = sub == 0 ? we : pl;   // word 2sub - 1
+      const u64 right = sub == 3 ? we : pr;  // word 2sub + 2
+      xs[sy + 1][0] = wa | (hi > 0 ? left : 0ull) | (lo < 0 ? wb : 0ull);
+      xs[sy + 1][1] = wb | (hi > 0 ? wa : 0ull) | (lo < 0 ? right : 0ull);
     }
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
@@ -1697,26 +1805,19 @@ __global__ void __launch_bounds__(256) k_leaf_gather_box(const int4* out_origin,
     u64 v = ys[1][e];
     if (hi > 0) v |= ((ys[1][e] & ~kZ7) << 1) | ((ys[0][e] & kZ7) >> 7);
     if (lo < 0) v |= ((ys[1][e] & ~kZ0) >> 1) | ((ys[2][e] & kZ0) << 7);
-    outw[e] = v;
+    outw[e] = valid ? v : 0ull;
   }
-  u64 full[8];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    full[2 * k] = __shfl(outw[0], grp | k, kWave);
-    full[2 * k + 1] = __shfl(outw[1], grp | k, kWave);
-  }
-  u64 prefix = 0;
-  int count = 0;
-  uint32_t box = kEmptyBox;
+  // leaf statistics from the quad's 8 words (lane s: words 2s, 2s+1)
+  u64 prefix;
+  int count;
+  uint32_t box;
+  quad_leaf_stats(outw[0], outw[1], sub, prefix, count, box);
   if (i < n && valid) {
     reinterpret_cast<ulonglong2*>(out_mask)[i * 4 + sub] = make_ulonglong2(outw[0], outw[1]);
-    if (sub == 0) {
-      leaf_stats(full, prefix, count, box);
-      out_prefix[i] = prefix;
-    }
+    if (sub == 0) out_prefix[i] = prefix;
   }
   // voxels before this leaf within the block's leaves, and the block's total
-  const int32_t inrun = block_run_scan(count, &vox_part[lblk]);
+  const int32_t inrun = block_run_scan(sub == 0 && i < n ? count : 0, &vox_part[lblk]);
   if (i < n && sub == 0) {
     leaf_box[i] = box;
     leaf_inrun[i] = inrun;
@@ -1769,6 +1870,16 @@ void mask_leaves(const tc_grid_batch* src, const uint8_t* keep, i64 n_keep, u64*
 }
 
 // ------------------------------------------------------------------ driver
+// Output layouts by capacity are taken while they stay under this size.
+constexpr size_t kBoundedBytes = size_t(32) << 20;
+
+static void check_pass_flags(int32_t f) {
+  if (f & kFlagSource)
+    throw Error(TC_ERR_INTERNAL, "the source batch failed a device consistency check when it was written");
+  if (f & kFlagOverflow) throw Error(TC_ERR_OVERFLOW, "an output voxel coordinate leaves int32");
+  if (f & kFlagInternal) throw Error(TC_ERR_INTERNAL, "pass: device consistency check failed");
+}
+
 tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, const u64* leaf_mask_override) {
   const OpInfo oi = op_info(op);
   hipStream_t s = oa.stream;
@@ -1777,182 +1888,199 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, 
   if (leaf_mask_override) sv.leaf_mask = const_cast<u64*>(leaf_mask_override);
   const i64 nT = (i64)src->n2 * oi.m;
   const i64 nL = (i64)src->n1 * oi.m;
-  if (nT > 0x7fffffffLL || nL > 0x7fffffffLL || nL * oi.m_src > (1ll << 40))
+  if (nT > 0x7fffffffLL || nL > 0x7fffffffLL || nL * oi.m_src > (1ll << 40) || src->n1 >= (1 << 25))
     throw Error(TC_ERR_UNSUPPORTED, "pass: source batch too large");
 
-  Arena a(s);
   const bool small_tiles = nT > 0 && nT <= kTilesMax;
-  const i64 nTs = small_tiles ? 0 : nT;  // sort scratch only for the multi-kernel tile path
-  const size_t o_keys = a.reserve(sizeof(Key128) * nTs);
-  const size_t o_vals = a.reserve(4 * nTs);
-  const size_t o_head = a.reserve(4 * nTs);
-  const size_t o_texcl = a.reserve(4 * (nTs + 1));
-  const size_t o_toc = a.reserve(4 * nT);
-  const size_t o_ntiles = a.reserve(4);
-  const size_t o_ncand = a.reserve(4);
-  const size_t o_utile = a.reserve(16 * nT);
-  const size_t o_tchild = a.reserve(4096 * nT);
-  const size_t o_tpre = a.reserve(1024 * nT);
-  const size_t o_tlc = a.reserve(4 * nT);
-  const size_t o_tlb = a.reserve(4 * (nT + 1));
-  const size_t o_tne = a.reserve(4 * nT);
-  const size_t o_uex = a.reserve(4 * (nT + 1));
-  const size_t o_gtb = a.reserve(4 * ((i64)B + 1));
-  const size_t o_corig = a.reserve(16 * nL);
-  const size_t o_cchild = a.reserve(512 * nL);
-  const size_t o_cpre = a.reserve(128 * nL);
-  const size_t o_ccnt = a.reserve(8 * nL);
-  const size_t o_cscan = a.reserve(8 * (nL + 1));
-  const size_t o_nbr = a.reserve(4 * nL);
-  const size_t o_csrc = a.reserve(4 * nL * oi.m_src);
-  const size_t o_ginfo = a.reserve(4 * 6 * (i64)B);
-  const size_t o_rb = a.reserve(4 * (4 + 3 * (i64)B));
-  const size_t o_ureach = a.reserve(4 * (i64)src->n2);
-  const size_t o_lreach = a.reserve(4 * (i64)src->n1);
-  const size_t o_stmp = a.reserve(std::max(scan_tmp_bytes(nT, 4), scan_tmp_bytes(nL, 8)));
-  a.commit();
-
-  TreeScratch ts{};
-  ts.cap_tiles = nT;
-  ts.cap_cands = nL;
-  ts.d_num_tiles = a.at<int32_t>(o_ntiles);
-  ts.utile = a.at<int4>(o_utile);
-  ts.tile_child = a.at<u64>(o_tchild);
-  ts.tile_prefix = a.at<uint16_t>(o_tpre);
-  ts.tile_lower_count = a.at<int32_t>(o_tlc);
-  ts.tile_lower_base = a.at<int32_t>(o_tlb);
-  ts.tile_nonempty = a.at<int32_t>(o_tne);
-  ts.upper_excl = a.at<int32_t>(o_uex);
-  ts.grid_tile_begin = a.at<int32_t>(o_gtb);
-  ts.d_num_cands = a.at<int32_t>(o_ncand);
-  ts.cand_origin = a.at<int4>(o_corig);
-  ts.cand_child = a.at<u64>(o_cchild);
-  ts.cand_prefix = a.at<uint16_t>(o_cpre);
-  ts.cand_counts = a.at<i64>(o_ccnt);
-  ts.cand_scan = a.at<i64>(o_cscan);
-  ts.grid_info = a.at<int32_t>(o_ginfo);
-  ts.readback = a.at<int32_t>(o_rb);
-  ts.scan_tmp = a.at<char>(o_stmp);
-  ts.flags = ts.readback;
-  int32_t* tile_of_cand = a.at<int32_t>(o_toc);
-  int32_t* lower_nbr = a.at<int32_t>(o_nbr);
-  int32_t* cand_src = a.at<int32_t>(o_csrc);
-
-  // tiles
   const bool small_lowers = small_tiles && nT <= kLowersSmallTiles && nL > 0 && nL <= kLowersSmallMax &&
                             (op == TC_OP_COARSEN || nL / oi.m <= kReachMax);
-  // box ops on small batches: voxel-exact face reach sets of uppers and lowers
-  const bool box_op = op != TC_OP_REFINE && op != TC_OP_COARSEN;
-  uint32_t* box_lreach = nullptr;
-  if (small_lowers && box_op) {
-    box_lreach = a.at<uint32_t>(o_lreach);
-    if (src->n1 > kBoxReachLowers) throw Error(TC_ERR_INTERNAL, "pass: too many lowers for the box reach stage");
-    launch("k_box_reach", k_box_reach, src->n2, 256, s, (const int32_t*)sv.upper_first, (int32_t)src->n2,
-           (const int32_t*)sv.lower_first, (int32_t)src->n1, (const int4*)sv.leaf_origin,
-           (const int32_t*)sv.leaf_parent, (const u64*)sv.leaf_mask, (int32_t)src->nl, op, oi.m,
-           a.at<uint32_t>(o_ureach), box_lreach);
-  }
-  if (small_tiles) {
-    // the bitmaps are zeroed in-kernel when few (at most 1 MiB for one workgroup):
-    // by the fused lower stage, or here; otherwise by a wide fill
-    const bool zero_here = !small_lowers && nT <= 256;
-    // many source uppers: their reach sets in a wide launch first
-    uint32_t* ureach = box_lreach ? a.at<uint32_t>(o_ureach) : nullptr;
-    if (!box_lreach && op != TC_OP_COARSEN && src->n2 > 64) {
-      ureach = a.at<uint32_t>(o_ureach);
-      launch("k_node_reach", k_node_reach, ceil_div((i64)src->n2, 4), 256, s, (const u64*)sv.upper_mask,
-             (i64)src->n2, 512, op, oi.m, ureach);
-    }
-    launch("k_tiles_small", k_tiles_small, 1, kTilesThreads, s, (const int4*)sv.upper_origin,
-           (const u64*)sv.upper_mask, (int32_t)src->n2, op, oi.m, B, ts.utile, tile_of_cand, ts.d_num_tiles,
-           ts.grid_tile_begin, ts.tile_child, zero_here ? 1 : 0, (const uint32_t*)ureach, ts.readback,
-           (const int32_t*)sv.status);
-    if (!small_lowers && !zero_here) fill_u64(ts.tile_child, 0, nT * 512, ts.d_num_tiles, 512, s);
-  } else {
-    launch("k_flags_from_source", k_flags_from_source, 1, 64, s, ts.readback, (const int32_t*)sv.status);
-    if (nT > 0) {
-      Key128* keys = a.at<Key128>(o_keys);
-      uint32_t* vals = a.at<uint32_t>(o_vals);
-      int32_t* head = a.at<int32_t>(o_head);
-      int32_t* texcl = a.at<int32_t>(o_texcl);
-      launch("k_tile_candidates", k_tile_candidates, ceil_div(nT, 256), 256, s, (const int4*)sv.upper_origin, nT,
-             op, oi.m, keys, vals);
-      sort_pairs_128(keys, vals, nT, tile_key_bits(B), s);
-      launch("k_tile_heads", k_tile_heads, ceil_div(nT, 256), 256, s, (const Key128*)keys, nT, head);
-      scan_excl_i32(head, texcl, nT, nullptr, s, ts.d_num_tiles, ts.scan_tmp);
-      launch("k_tile_scatter", k_tile_scatter, ceil_div(nT, 256), 256, s, (const Key128*)keys,
-             (const uint32_t*)vals, (const int32_t*)head, (const int32_t*)texcl, nT, ts.utile, tile_of_cand,
-             ts.flags);
-    } else {
-      fill_i32(ts.d_num_tiles, 0, 1, nullptr, 1, s);
-    }
-    tree_tile_ranges(ts, B, s);
-    fill_u64(ts.tile_child, 0, nT * 512, ts.d_num_tiles, 512, s);
-  }
-  // lowers. The candidate -> source table starts empty; refine and the box ops
-  // store every word of their candidates' leaf masks, coarsen ORs into zeros.
-  if (small_lowers) {
-    launch("k_lowers_small", k_lowers_small, 1, kLowersThreads, s, (const int4*)sv.lower_origin,
-           (const u64*)sv.lower_mask, nL, op, oi.m, oi.m_src, (const int32_t*)tile_of_cand,
-           (const int32_t*)ts.d_num_tiles, ts.tile_child, ts.tile_prefix, ts.tile_lower_base, ts.d_num_cands,
-           ts.cand_child, op == TC_OP_COARSEN ? 1 : 0, lower_nbr, ts.cand_origin, cand_src, ts.flags,
-           (const uint32_t*)box_lreach);
-  } else {
-    uint32_t* lreach = nullptr;
-    if (op != TC_OP_COARSEN) {
-      lreach = a.at<uint32_t>(o_lreach);
-      launch("k_node_reach", k_node_reach, ceil_div((i64)src->n1, 4), 256, s, (const u64*)sv.lower_mask,
-             (i64)src->n1, 64, op, oi.m, lreach);
-    }
-    launch("k_lower_mark", k_lower_mark, ceil_div(nL, 256), 256, s, (const int4*)sv.lower_origin,
-           (const u64*)sv.lower_mask, (const uint32_t*)lreach, nL, op, oi.m, (const int32_t*)tile_of_cand,
-           (const int32_t*)ts.d_num_tiles, ts.tile_child, ts.flags);
-    tree_rank_tiles(ts, s);
-    fill_pair(cand_src, -1, nL * oi.m_src, oi.m_src, ts.cand_child, 0, op == TC_OP_COARSEN ? nL * 64 : 0, 64,
-              ts.d_num_cands, s);
-    launch("k_lower_nbr", k_lower_nbr, ceil_div(nL, 256), 256, s, (const int4*)sv.lower_origin,
-           (const u64*)sv.lower_mask, (const uint32_t*)lreach, nL, op, oi.m, oi.m_src, (const int32_t*)tile_of_cand,
-           (const u64*)ts.tile_child, (const uint16_t*)ts.tile_prefix, (const int32_t*)ts.tile_lower_base,
-           (const int32_t*)ts.d_num_tiles, (const int32_t*)ts.d_num_cands, lower_nbr, ts.cand_origin, cand_src,
-           ts.flags);
-  }
-  // leaves (pass A)
-  if (op == TC_OP_REFINE || op == TC_OP_COARSEN) {
-    launch("k_leaf_mark_lower", k_leaf_mark_lower, (i64)src->n1, 256, s, (const int4*)sv.leaf_origin,
-           (const u64*)sv.leaf_mask, (const int32_t*)sv.lower_first, (const u64*)sv.lower_mask,
-           (const uint16_t*)sv.lower_prefix, op, oi.m, (const int32_t*)lower_nbr, (const int32_t*)ts.d_num_cands,
-           ts.cand_child, ts.flags);
-  } else if (nL > 0) {  // no source lowers: nothing to mark and every bbox is empty
-    const i64 blocks = nL < 8192 ? nL : 8192;
-    auto mark_box = oi.lo < 0 && oi.hi > 0 ? k_leaf_mark_box<-1, 1>
-                    : (oi.lo < 0 ? k_leaf_mark_box<-1, 0> : k_leaf_mark_box<0, 1>);
-    launch("k_leaf_mark_box", mark_box, blocks, 256, s, (const int32_t*)cand_src,
-           (const int32_t*)ts.d_num_cands, B, (const tc_grid_header*)sv.headers,
-           (const u64*)sv.lower_mask, (const uint16_t*)sv.lower_prefix, (const int32_t*)sv.lower_first,
-           (const u64*)sv.leaf_mask, sv.n_lower, sv.n_leaf, ts.cand_child, ts.flags);
-  }
-  // counts and the single readback
-  tree_counts(ts, B, s);
-  const size_t rb_bytes = 4 * (4 + 3 * (size_t)B);
-  int32_t* h_rb = static_cast<int32_t*>(pinned_staging(rb_bytes));
-  hip_check(hipMemcpyAsync(h_rb, ts.readback, rb_bytes, hipMemcpyDeviceToHost, s), "readback");
-  hip_check(hipStreamSynchronize(s), "hipStreamSynchronize");
-  if (h_rb[0] & kFlagSource)
-    throw Error(TC_ERR_INTERNAL, "the source batch failed a device consistency check when it was written");
-  if (h_rb[0] & kFlagOverflow) throw Error(TC_ERR_OVERFLOW, "an output voxel coordinate leaves int32");
-  if (h_rb[0] & kFlagInternal) throw Error(TC_ERR_INTERNAL, "pass: device consistency check failed");
-
-  tc_grid_batch* out = new_batch(B, h_rb, oa);
+  // Small batches lay the output out by capacities known before any launch (a
+  // source leaf feeds at most 8 / 1 / 27 / 8 output leaves for refine, coarsen,
+  // dilate, pads; the tile and lower candidates bound the nodes), so the output
+  // is allocated first and the writers follow the counts stage without a host
+  // round trip; the one readback (headers and status) ends the pass.
+  const i64 per_leaf = op == TC_OP_REFINE ? 8 : (op == TC_OP_COARSEN ? 1 : oi.m);
+  const i64 gran = op == TC_OP_REFINE ? 256 : 64;  // leaves per gather workgroup (voxel-sum runs)
+  const i64 L_cap = (i64)src->nl * per_leaf;
+  const bool bounded = small_lowers && L_cap > 0 && L_cap <= 0x7fffffffLL && finalize_small_fits(L_cap, B, gran) &&
+                       make_layout(B, nT, nL, L_cap).total <= kBoundedBytes;
+  tc_grid_batch* out = bounded ? new_batch_capacity(B, nT, nL, L_cap, oa) : nullptr;
   try {
-    const GridView ov = out->view();
-    const i64 L = out->nl;
+    Arena a(s);
+    const i64 nTs = small_tiles ? 0 : nT;  // sort scratch only for the multi-kernel tile path
+    const size_t o_keys = a.reserve(sizeof(Key128) * nTs);
+    const size_t o_vals = a.reserve(4 * nTs);
+    const size_t o_head = a.reserve(4 * nTs);
+    const size_t o_texcl = a.reserve(4 * (nTs + 1));
+    const size_t o_toc = a.reserve(4 * nT);
+    const size_t o_ntiles = a.reserve(4);
+    const size_t o_ncand = a.reserve(4);
+    const size_t o_utile = a.reserve(16 * nT);
+    const size_t o_tchild = a.reserve(4096 * nT);
+    const size_t o_tpre = a.reserve(1024 * nT);
+    const size_t o_tlc = a.reserve(4 * nT);
+    const size_t o_tlb = a.reserve(4 * (nT + 1));
+    const size_t o_tne = a.reserve(4 * nT);
+    const size_t o_uex = a.reserve(4 * (nT + 1));
+    const size_t o_gtb = a.reserve(4 * ((i64)B + 1));
+    const size_t o_corig = a.reserve(16 * nL);
+    const size_t o_cchild = a.reserve(512 * nL);
+    const size_t o_cpre = a.reserve(128 * nL);
+    const size_t o_ccnt = a.reserve(8 * nL);
+    const size_t o_cscan = a.reserve(8 * (nL + 1));
+    const size_t o_nbr = a.reserve(4 * nL);
+    const size_t o_csrc = a.reserve(4 * nL * oi.m_src);
+    const size_t o_ginfo = a.reserve(4 * 6 * (i64)B);
+    const size_t o_rb = a.reserve(4 * (4 + 3 * (i64)B));
+    const size_t o_ureach = a.reserve(4 * (i64)src->n2);
+    const size_t o_lreach = a.reserve(4 * (i64)src->n1);
+    const size_t o_stmp = a.reserve(std::max(scan_tmp_bytes(nT, 4), scan_tmp_bytes(nL, 8)));
+    a.commit();
+
+    TreeScratch ts{};
+    ts.cap_tiles = nT;
+    ts.cap_cands = nL;
+    ts.d_num_tiles = a.at<int32_t>(o_ntiles);
+    ts.utile = a.at<int4>(o_utile);
+    ts.tile_child = a.at<u64>(o_tchild);
+    ts.tile_prefix = a.at<uint16_t>(o_tpre);
+    ts.tile_lower_count = a.at<int32_t>(o_tlc);
+    ts.tile_lower_base = a.at<int32_t>(o_tlb);
+    ts.tile_nonempty = a.at<int32_t>(o_tne);
+    ts.upper_excl = a.at<int32_t>(o_uex);
+    ts.grid_tile_begin = a.at<int32_t>(o_gtb);
+    ts.d_num_cands = a.at<int32_t>(o_ncand);
+    ts.cand_origin = a.at<int4>(o_corig);
+    ts.cand_child = a.at<u64>(o_cchild);
+    ts.cand_prefix = a.at<uint16_t>(o_cpre);
+    ts.cand_counts = a.at<i64>(o_ccnt);
+    ts.cand_scan = a.at<i64>(o_cscan);
+    ts.grid_info = a.at<int32_t>(o_ginfo);
+    ts.readback = a.at<int32_t>(o_rb);
+    ts.scan_tmp = a.at<char>(o_stmp);
+    ts.flags = ts.readback;
+    int32_t* tile_of_cand = a.at<int32_t>(o_toc);
+    int32_t* lower_nbr = a.at<int32_t>(o_nbr);
+    int32_t* cand_src = a.at<int32_t>(o_csrc);
+
+    // tiles
+    // box ops on small batches: voxel-exact face reach sets of uppers and lowers
+    const bool box_op = op != TC_OP_REFINE && op != TC_OP_COARSEN;
+    uint32_t* box_lreach = nullptr;
+    if (small_lowers && box_op) {
+      box_lreach = a.at<uint32_t>(o_lreach);
+      if (src->n1 > kBoxReachLowers) throw Error(TC_ERR_INTERNAL, "pass: too many lowers for the box reach stage");
+      launch("k_box_reach", k_box_reach, src->n2, 256, s, (const int32_t*)sv.upper_first, (int32_t)src->n2,
+             (const int32_t*)sv.lower_first, (int32_t)src->n1, (const int4*)sv.leaf_origin,
+             (const int32_t*)sv.leaf_parent, (const u64*)sv.leaf_mask, (int32_t)src->nl, op, oi.m,
+             a.at<uint32_t>(o_ureach), box_lreach);
+    }
+    if (small_tiles) {
+      // the bitmaps are zeroed in-kernel when few (at most 1 MiB for one workgroup):
+      // by the fused lower stage, or here; otherwise by a wide fill
+      const bool zero_here = !small_lowers && nT <= 256;
+      // many source uppers: their reach sets in a wide launch first
+      uint32_t* ureach = box_lreach ? a.at<uint32_t>(o_ureach) : nullptr;
+      if (!box_lreach && op != TC_OP_COARSEN && src->n2 > 64) {
+        ureach = a.at<uint32_t>(o_ureach);
+        launch("k_node_reach", k_node_reach, ceil_div((i64)src->n2, 4), 256, s, (const u64*)sv.upper_mask,
+               (i64)src->n2, 512, op, oi.m, ureach);
+      }
+      launch("k_tiles_small", k_tiles_small, 1, kTilesThreads, s, (const int4*)sv.upper_origin,
+             (const u64*)sv.upper_mask, (int32_t)src->n2, op, oi.m, B, ts.utile, tile_of_cand, ts.d_num_tiles,
+             ts.grid_tile_begin, ts.tile_child, zero_here ? 1 : 0, (const uint32_t*)ureach, ts.readback,
+             (const int32_t*)sv.status);
+      if (!small_lowers && !zero_here) fill_u64(ts.tile_child, 0, nT * 512, ts.d_num_tiles, 512, s);
+    } else {
+      launch("k_flags_from_source", k_flags_from_source, 1, 64, s, ts.readback, (const int32_t*)sv.status);
+      if (nT > 0) {
+        Key128* keys = a.at<Key128>(o_keys);
+        uint32_t* vals = a.at<uint32_t>(o_vals);
+        int32_t* head = a.at<int32_t>(o_head);
+        int32_t* texcl = a.at<int32_t>(o_texcl);
+        launch("k_tile_candidates", k_tile_candidates, ceil_div(nT, 256), 256, s, (const int4*)sv.upper_origin, nT,
+               op, oi.m, keys, vals);
+        sort_pairs_128(keys, vals, nT, tile_key_bits(B), s);
+        launch("k_tile_heads", k_tile_heads, ceil_div(nT, 256), 256, s, (const Key128*)keys, nT, head);
+        scan_excl_i32(head, texcl, nT, nullptr, s, ts.d_num_tiles, ts.scan_tmp);
+        launch("k_tile_scatter", k_tile_scatter, ceil_div(nT, 256), 256, s, (const Key128*)keys,
+               (const uint32_t*)vals, (const int32_t*)head, (const int32_t*)texcl, nT, ts.utile, tile_of_cand,
+               ts.flags);
+      } else {
+        fill_i32(ts.d_num_tiles, 0, 1, nullptr, 1, s);
+      }
+      tree_tile_ranges(ts, B, s);
+      fill_u64(ts.tile_child, 0, nT * 512, ts.d_num_tiles, 512, s);
+    }
+    // lowers. The candidate -> source table starts empty; refine and the box ops
+    // store every word of their candidates' leaf masks, coarsen ORs into zeros.
+    if (small_lowers) {
+      launch("k_lowers_small", k_lowers_small, 1, kLowersThreads, s, (const int4*)sv.lower_origin,
+             (const u64*)sv.lower_mask, nL, op, oi.m, oi.m_src, (const int32_t*)tile_of_cand,
+             (const int32_t*)ts.d_num_tiles, ts.tile_child, ts.tile_prefix, ts.tile_lower_base, ts.d_num_cands,
+             ts.cand_child, 0, lower_nbr, ts.cand_origin, cand_src, ts.flags,
+             (const uint32_t*)box_lreach);
+    } else {
+      uint32_t* lreach = nullptr;
+      if (op != TC_OP_COARSEN) {
+        lreach = a.at<uint32_t>(o_lreach);
+        launch("k_node_reach", k_node_reach, ceil_div((i64)src->n1, 4), 256, s, (const u64*)sv.lower_mask,
+               (i64)src->n1, 64, op, oi.m, lreach);
+      }
+      launch("k_lower_mark", k_lower_mark, ceil_div(nL, 256), 256, s, (const int4*)sv.lower_origin,
+             (const u64*)sv.lower_mask, (const uint32_t*)lreach, nL, op, oi.m, (const int32_t*)tile_of_cand,
+             (const int32_t*)ts.d_num_tiles, ts.tile_child, ts.flags);
+      tree_rank_tiles(ts, s);
+      fill_pair(cand_src, -1, nL * oi.m_src, oi.m_src, ts.cand_child, 0, 0, 64, ts.d_num_cands, s);
+      launch("k_lower_nbr", k_lower_nbr, ceil_div(nL, 256), 256, s, (const int4*)sv.lower_origin,
+             (const u64*)sv.lower_mask, (const uint32_t*)lreach, nL, op, oi.m, oi.m_src, (const int32_t*)tile_of_cand,
+             (const u64*)ts.tile_child, (const uint16_t*)ts.tile_prefix, (const int32_t*)ts.tile_lower_base,
+             (const int32_t*)ts.d_num_tiles, (const int32_t*)ts.d_num_cands, lower_nbr, ts.cand_origin, cand_src,
+             ts.flags);
+    }
+    // leaves: every candidate's 16^3 mask, its prefix table and packed count
+    // (each candidate is written by exactly one wave or workgroup)
+    if (op == TC_OP_REFINE) {
+      launch("k_leaf_mark_lower", k_leaf_mark_lower, (i64)src->n1, 256, s, (const int4*)sv.leaf_origin,
+             (const u64*)sv.leaf_mask, (const int32_t*)sv.lower_first, (const u64*)sv.lower_mask,
+             (const uint16_t*)sv.lower_prefix, op, oi.m, (const int32_t*)lower_nbr, (const int32_t*)ts.d_num_cands,
+             ts.cand_child, ts.cand_prefix, ts.cand_counts, ts.flags);
+    } else if (op == TC_OP_COARSEN) {
+      launch("k_mark_coarsen", k_mark_coarsen, ceil_div(nL, 4), 256, s, (const int32_t*)cand_src,
+             (const int32_t*)ts.d_num_cands, (const u64*)sv.lower_mask, sv.n_lower, ts.cand_child, ts.cand_prefix,
+             ts.cand_counts, ts.flags);
+    } else if (nL > 0) {  // no source lowers: nothing to mark and every bbox is empty
+      const i64 blocks = nL < 8192 ? nL : 8192;
+      auto mark_box = oi.lo < 0 && oi.hi > 0 ? k_leaf_mark_box<-1, 1>
+                      : (oi.lo < 0 ? k_leaf_mark_box<-1, 0> : k_leaf_mark_box<0, 1>);
+      launch("k_leaf_mark_box", mark_box, blocks, 256, s, (const int32_t*)cand_src,
+             (const int32_t*)ts.d_num_cands, B, (const tc_grid_header*)sv.headers,
+             (const u64*)sv.lower_mask, (const uint16_t*)sv.lower_prefix, (const int32_t*)sv.lower_first,
+             (const u64*)sv.leaf_mask, sv.n_lower, sv.n_leaf, ts.cand_child, ts.cand_prefix, ts.cand_counts,
+             ts.flags);
+    }
+    ts.cand_counts_ready = true;
+    // counts and the single readback
+    tree_counts(ts, B, s);
+    if (!bounded) {  // exact layout: counts first, then the allocation
+      const size_t rb_bytes = 4 * (4 + 3 * (size_t)B);
+      int32_t* h_rb = static_cast<int32_t*>(pinned_staging(rb_bytes));
+      hip_check(hipMemcpyAsync(h_rb, ts.readback, rb_bytes, hipMemcpyDeviceToHost, s), "readback");
+      hip_check(hipStreamSynchronize(s), "hipStreamSynchronize");
+      check_pass_flags(h_rb[0]);
+      out = new_batch(B, h_rb, oa);
+      if (out->nl > 0 && sv.n_leaf == 0) throw Error(TC_ERR_INTERNAL, "pass: output leaves without source leaves");
+    }
+    // writers (launch bounds and scratch by the leaf count, or its capacity)
+    const GridView ov = bounded ? make_view(out->buffer, out->layout, B, (int32_t)nT, (int32_t)nL, (int32_t)L_cap)
+                                : out->view();
+    const i64 L = ov.n_leaf;
+    const int32_t* d_L = ts.readback + 3;  // the leaf count on the device
     Arena post(s);
     const size_t o_lc = post.reserve(4 * L);
     const size_t o_box = post.reserve(4 * L);
     const size_t o_bb = post.reserve(4 * 6 * (i64)B * bbox_replicas(B));
-    // voxel sums per gather workgroup: 256 output leaves (refine) or 64 (4 lanes per leaf)
-    const i64 gran = op == TC_OP_REFINE ? 256 : 64;
-    const size_t o_part = post.reserve(8 * (ceil_div(L, gran) + 1));
+    const size_t o_part = post.reserve(8 * (ceil_div(L, gran) + 1));  // voxel sums per gather workgroup
     const size_t o_gvb = post.reserve(8 * ((i64)B + 1));
     const size_t o_inrun = post.reserve(4 * L);
     post.commit();
@@ -1960,30 +2088,36 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, 
     i64* vox_part = post.at<i64>(o_part);
     int32_t* leaf_inrun = post.at<int32_t>(o_inrun);
     tree_write_nodes(ts, ov, leaf_cand, s);
-    if (L > 0 && sv.n_leaf == 0) throw Error(TC_ERR_INTERNAL, "pass: output leaves without source leaves");
     if (op == TC_OP_REFINE || op == TC_OP_COARSEN) {
       const i64 lanes = op == TC_OP_REFINE ? 1 : 4;
       auto gather = op == TC_OP_REFINE ? k_leaf_gather<0> : k_leaf_gather<1>;
       launch("k_leaf_gather", gather, ceil_div(L * lanes, 256), 256, s, (const int4*)ov.leaf_origin,
-             (const int32_t*)leaf_cand, L, (const int32_t*)cand_src,
-             (const u64*)sv.lower_mask, (const uint16_t*)sv.lower_prefix, (const int32_t*)sv.lower_first,
-             (const u64*)sv.leaf_mask, sv.n_lower, sv.n_leaf, (const int32_t*)ts.d_num_cands, ov.leaf_mask,
-             ov.leaf_prefix, post.at<uint32_t>(o_box), leaf_inrun, vox_part, ts.flags);
+             (const int32_t*)leaf_cand, d_L, L, (const int32_t*)cand_src, (const u64*)sv.lower_mask,
+             (const uint16_t*)sv.lower_prefix, (const int32_t*)sv.lower_first, (const u64*)sv.leaf_mask, sv.n_lower,
+             sv.n_leaf, (const int32_t*)ts.d_num_cands, ov.leaf_mask, ov.leaf_prefix, post.at<uint32_t>(o_box),
+             leaf_inrun, vox_part, ts.flags);
     } else {
       auto gather_box = oi.lo < 0 && oi.hi > 0 ? k_leaf_gather_box<-1, 1>
                         : (oi.lo < 0 ? k_leaf_gather_box<-1, 0> : k_leaf_gather_box<0, 1>);
       launch("k_leaf_gather", gather_box, ceil_div(L * 4, 256), 256, s, (const int4*)ov.leaf_origin,
-             (const int32_t*)leaf_cand, L, (const int32_t*)cand_src, (const u64*)sv.lower_mask,
-             (const uint16_t*)sv.lower_prefix, (const int32_t*)sv.lower_first, (const u64*)sv.leaf_mask,
-             sv.n_lower, sv.n_leaf, (const int32_t*)ts.d_num_cands, ov.leaf_mask, ov.leaf_prefix,
-             post.at<uint32_t>(o_box), leaf_inrun, vox_part, ts.flags);
+             (const int32_t*)leaf_cand, d_L, L, (const int32_t*)cand_src, (const u64*)sv.lower_mask,
+             (const uint16_t*)sv.lower_prefix, (const int32_t*)sv.lower_first, (const u64*)sv.leaf_mask, sv.n_lower,
+             sv.n_leaf, (const int32_t*)ts.d_num_cands, ov.leaf_mask, ov.leaf_prefix, post.at<uint32_t>(o_box),
+             leaf_inrun, vox_part, ts.flags);
     }
     // the gathers' consistency checks set bits in the flag word after the
-    // readback: the finalize copies it into the batch's status word, which goes
-    // back with the voxel total
+    // counts: the finalize copies it into the batch's status word
     apply_debug_inject(ts.flags, s);
     tree_finalize_leaves(ov, post.at<uint32_t>(o_box), leaf_inrun, vox_part, gran, post.at<i64>(o_gvb),
-                         post.at<int32_t>(o_bb), (const int32_t*)ts.grid_info, (const int32_t*)ts.flags, s);
+                         post.at<int32_t>(o_bb), (const int32_t*)ts.grid_info, ts.flags, d_L, s);
+    if (bounded) {  // the pass's one readback: every header and the status word
+      const size_t hb = sizeof(tc_grid_header) * (size_t)B + 16;
+      char* h = static_cast<char*>(pinned_staging(hb));
+      hip_check(hipMemcpyAsync(h, ov.headers, hb, hipMemcpyDeviceToHost, s), "readback");
+      hip_check(hipStreamSynchronize(s), "hipStreamSynchronize");
+      check_pass_flags(*reinterpret_cast<const int32_t*>(h + sizeof(tc_grid_header) * (size_t)B));
+      set_counts_from_headers(out, reinterpret_cast<const tc_grid_header*>(h));
+    }
   } catch (...) {
     free_batch(out);
     throw;

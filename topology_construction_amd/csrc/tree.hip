@@ -251,7 +251,7 @@ __global__ void __launch_bounds__(kTailThreads) k_counts_small(const u64* cand_c
                                                                const int32_t* d_num_tiles,
                                                                const int32_t* d_num_cands, int32_t B,
                                                                int32_t* upper_excl, int32_t* grid_info,
-                                                               int32_t* readback) {
+                                                               int32_t* readback, int counts_ready) {
   __shared__ i64 s_cc[kCountsSmallMax + 1];
   __shared__ int32_t s_tlb[kTailTiles + 1];
   __shared__ int32_t s_uex[kTailTiles + 1];
@@ -269,7 +269,10 @@ __global__ void __launch_bounds__(kTailThreads) k_counts_small(const u64* cand_c
   // load waits for the candidate count.
   constexpr int kWaves = kTailThreads / kWave;
   constexpr int kPerWave = 4;
-  for (int c0 = wv * kPerWave; c0 < cap_c; c0 += kWaves * kPerWave) {
+  if (counts_ready) {  // prefixes and counts came with the masks
+    for (int c = tid; c < nc; c += kTailThreads) s_cc[c] = cand_counts[c];
+  }
+  for (int c0 = wv * kPerWave; !counts_ready && c0 < cap_c; c0 += kWaves * kPerWave) {
     u64 w[kPerWave];
 #pragma unroll
     for (int v = 0; v < kPerWave; ++v) w[v] = cand_child[(i64)min(c0 + v, cap_c - 1) * 64 + lane];
@@ -323,7 +326,8 @@ void tree_counts(TreeScratch& ts, int32_t B, hipStream_t s) {
     launch("k_counts_small", k_counts_small, 1, kTailThreads, s, (const u64*)ts.cand_child, (int32_t)ts.cap_cands,
            ts.cand_prefix, ts.cand_counts, ts.cand_scan, (const int32_t*)ts.grid_tile_begin,
            (const int32_t*)ts.tile_lower_base, (int32_t)ts.cap_tiles, (const int32_t*)ts.d_num_tiles,
-           (const int32_t*)ts.d_num_cands, B, ts.upper_excl, ts.grid_info, ts.readback);
+           (const int32_t*)ts.d_num_cands, B, ts.upper_excl, ts.grid_info, ts.readback,
+           ts.cand_counts_ready ? 1 : 0);
     return;
   }
   tree_count_cands(ts, s);
@@ -331,8 +335,9 @@ void tree_counts(TreeScratch& ts, int32_t B, hipStream_t s) {
 }
 
 void tree_count_cands(TreeScratch& ts, hipStream_t s) {
-  launch("k_lower_count", k_lower_count, ceil_div(ts.cap_cands, 4), 256, s, (const u64*)ts.cand_child,
-         ts.cand_prefix, ts.cand_counts, (const int32_t*)ts.d_num_cands);
+  if (!ts.cand_counts_ready)
+    launch("k_lower_count", k_lower_count, ceil_div(ts.cap_cands, 4), 256, s, (const u64*)ts.cand_child,
+           ts.cand_prefix, ts.cand_counts, (const int32_t*)ts.d_num_cands);
   scan_excl_i64(ts.cand_counts, ts.cand_scan, ts.cap_cands, ts.d_num_cands, s, nullptr, ts.scan_tmp);
 }
 
@@ -574,12 +579,21 @@ __device__ __forceinline__ void box_fold_lds(int32_t (*s_box)[kFinSmallGrids], i
 
 __global__ void __launch_bounds__(kFinThreads) k_finalize_small(const int4* leaf_origin, const int32_t* leaf_inrun,
                                                                 const uint32_t* leaf_box, const i64* vox_part,
-                                                                int32_t np, int32_t gs, const int32_t* grid_info,
-                                                                i64* leaf_offset, int32_t B, int32_t L,
-                                                                tc_grid_header* hdr, const int32_t* flags,
-                                                                int32_t* status) {
+                                                                int32_t gs, const int32_t* grid_info,
+                                                                i64* leaf_offset, int32_t B, const int32_t* d_L,
+                                                                int32_t L_cap, tc_grid_header* hdr,
+                                                                int32_t* flags, int32_t* status) {
   constexpr int kR = kFinRuns / kFinThreads;
   constexpr int kG = kFinSmallGrids / kFinThreads;
+  // the leaf count from the device (the launch may be sized by a capacity):
+  // workgroups past the leaves leave at once, block 0 always writes the headers
+  int32_t L = *d_L;
+  if (L > L_cap || L < 0) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(flags, 2);
+    L = L < 0 ? 0 : L_cap;
+  }
+  if (blockIdx.x != 0 && (int32_t)blockIdx.x * kFinSlice >= L) return;  // uniform per block
+  const int32_t np = (L + (1 << gs) - 1) >> gs;  // runs of 2^gs leaves
   __shared__ int32_t s_part[kFinRuns];           // exclusive voxel offset of every run
   __shared__ int32_t s_gvb[kFinSmallGrids + 1];  // voxel begin of every grid, then the total
   __shared__ int32_t s_wave[kFinThreads / kWave];
@@ -704,7 +718,8 @@ __global__ void __launch_bounds__(kFinThreads) k_finalize_small(const int4* leaf
     __syncthreads();
   }
   if (blockIdx.x != 0) return;
-  if (tid < 4) status[tid] = tid == 0 ? *flags : 0;  // every writer of the leaves ran before this kernel
+  // thread 0 made any flag update of this kernel itself; the writers ran before it
+  if (tid < 4) status[tid] = tid == 0 ? *flags : 0;
 #pragma unroll
   for (int k = 0; k < kG; ++k) {  // B <= kFinSmallGrids = kG * kFinThreads
     const int gg = tid + k * kFinThreads;
@@ -865,19 +880,24 @@ __global__ void __launch_bounds__(256) k_write_headers_gvb(const int32_t* grid_i
   hdr[g] = h;
 }
 
+bool finalize_small_fits(i64 L, int32_t B, i64 gran) {
+  return L <= kFinSmallLeaves && B <= kFinSmallGrids && ceil_div(L, gran) <= kFinRuns;
+}
+
 void tree_finalize_leaves(const GridView& out, const uint32_t* leaf_box, const int32_t* leaf_inrun, i64* vox_part,
-                          i64 gran, i64* gvb, int32_t* bbox_accum, const int32_t* grid_info, const int32_t* flags,
-                          hipStream_t s) {
-  const i64 L = out.n_leaf;
+                          i64 gran, i64* gvb, int32_t* bbox_accum, const int32_t* grid_info, int32_t* flags,
+                          const int32_t* d_L, hipStream_t s) {
+  const i64 L = out.n_leaf;  // the leaf count, or (d_L given) a capacity with the count at d_L
   const int32_t B = out.B;
   if (gran <= 0 || (gran & (gran - 1)) != 0) throw Error(TC_ERR_INTERNAL, "finalize: run length not a power of two");
-  if (L <= kFinSmallLeaves && B <= kFinSmallGrids && ceil_div(L, gran) <= kFinRuns) {
+  if (finalize_small_fits(L, B, gran)) {
     launch("k_finalize_small", k_finalize_small, std::max<i64>(1, ceil_div(L, kFinSlice)), kFinThreads, s,
-           (const int4*)out.leaf_origin, leaf_inrun, leaf_box, (const i64*)vox_part, (int32_t)ceil_div(L, gran),
-           (int32_t)__builtin_ctzll((u64)gran), grid_info, out.leaf_offset, B, (int32_t)L, out.headers, flags,
-           out.status);
+           (const int4*)out.leaf_origin, leaf_inrun, leaf_box, (const i64*)vox_part,
+           (int32_t)__builtin_ctzll((u64)gran), grid_info, out.leaf_offset, B, d_L, (int32_t)L, out.headers,
+           flags, out.status);
     return;
   }
+  // the wide path runs on exact counts only (its launches are sized by them)
   const int32_t R = bbox_replicas(B);
   launch("k_vox_partials", k_vox_partials, 1, kPartThreads, s, vox_part, ceil_div(L, gran), leaf_inrun, gran,
          grid_info, B, L, bbox_accum, R, gvb);

@@ -274,6 +274,11 @@ struct Key128 {
 };
 void sort_pairs_128(Key128* keys, uint32_t* vals, i64 n, int key_bits, hipStream_t s);
 
+// Bits of a builder's device flag word (copied into the batch's status word).
+constexpr int kFlagOverflow = 1;
+constexpr int kFlagInternal = 2;  // a consistency check of a kernel failed
+constexpr int kFlagSource = 4;    // the source batch's writers had flagged a failed check
+
 // ------------------------------------------------------------------ tile keys
 // A tile key packs (grid, Tx+2^19, Ty+2^19, Tz+2^19) as grid<<60 | tx<<40 | ty<<20 | tz
 // over 128 bits; INVALID sorts after every valid key.
@@ -320,7 +325,10 @@ void tree_rank_tiles(TreeScratch& t, hipStream_t s);            // prefix per ti
 void tree_count_cands(TreeScratch& t, hipStream_t s);           // leaf counts per cand + their scan
 void tree_counts(TreeScratch& t, int32_t B, hipStream_t s);     // tree_count_cands + tree_grid_counts (fused when small)
 void tree_write_nodes(TreeScratch& t, const GridView& out, int32_t* leaf_cand, hipStream_t s);
-void tree_leaf_stats(const GridView& out, uint32_t* leaf_box, int32_t* leaf_inrun, i64* vox_part, hipStream_t s);
+// Leaf masks from eight word slices (slice k: word k of every leaf), and their
+// statistics.
+void tree_leaf_stats(const GridView& out, const u64* slices, uint32_t* leaf_box, int32_t* leaf_inrun, i64* vox_part,
+                     hipStream_t s);
 int32_t bbox_replicas(int32_t B);  // replicas of the per-grid bbox accumulators
 // Leaf voxel offsets, per-grid bboxes and headers. The leaf producer wrote, per
 // run of `gran` leaves (gran divides 256), the run's voxel sum (vox_part) and

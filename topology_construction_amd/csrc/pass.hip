@@ -31,9 +31,6 @@ namespace tc {
 
 constexpr u64 kZ0 = 0x0101010101010101ull;  // z = 0 bit of every (x, y) row
 constexpr u64 kZ7 = 0x8080808080808080ull;  // z = 7 bit of every row
-constexpr int kFlagOverflow = 1;
-constexpr int kFlagInternal = 2;
-constexpr int kFlagSource = 4;  // the source batch's writers had flagged a failed check
 
 // The pass's flag word starts from the source batch's status word.
 __global__ void k_flags_from_source(int32_t* flags, const int32_t* src_status) {

@@ -503,10 +503,12 @@ void tree_write_nodes(TreeScratch& ts, const GridView& out, int32_t* leaf_cand, 
 }
 
 // ------------------------------------------------------------------ leaf statistics
-// Per leaf (masks written by the ijk front-end): prefix word, voxel count and
+// Per leaf (masks built by the ijk front-end as eight word slices, slice k
+// holding word k of every leaf): the leaf mask, prefix word, voxel count and
 // packed local bbox. The topology pass computes the same values in its gather.
-__global__ void __launch_bounds__(256) k_leaf_stats(const u64* leaf_mask, u64* leaf_prefix, uint32_t* leaf_box,
-                                                    int32_t* leaf_inrun, i64* vox_part, i64 n_leaf) {
+__global__ void __launch_bounds__(256) k_leaf_stats(const u64* slices, u64* leaf_mask, u64* leaf_prefix,
+                                                    uint32_t* leaf_box, int32_t* leaf_inrun, i64* vox_part,
+                                                    i64 n_leaf) {
   const i64 i = (i64)blockIdx.x * 256 + threadIdx.x;
   int count = 0;
   u64 prefix = 0;
@@ -514,7 +516,9 @@ __global__ void __launch_bounds__(256) k_leaf_stats(const u64* leaf_mask, u64* l
   if (i < n_leaf) {
     u64 W[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) W[k] = leaf_mask[i * 8 + k];
+    for (int k = 0; k < 8; ++k) W[k] = slices[k * n_leaf + i];
+#pragma unroll
+    for (int k = 0; k < 8; k += 2) reinterpret_cast<ulonglong2*>(leaf_mask)[i * 4 + k / 2] = make_ulonglong2(W[k], W[k + 1]);
     leaf_stats(W, prefix, count, box);
   }
   const int32_t inrun = block_run_scan(count, &vox_part[blockIdx.x]);
@@ -525,8 +529,9 @@ __global__ void __launch_bounds__(256) k_leaf_stats(const u64* leaf_mask, u64* l
   }
 }
 
-void tree_leaf_stats(const GridView& out, uint32_t* leaf_box, int32_t* leaf_inrun, i64* vox_part, hipStream_t s) {
-  launch("k_leaf_stats", k_leaf_stats, ceil_div((i64)out.n_leaf, 256), 256, s, (const u64*)out.leaf_mask,
+void tree_leaf_stats(const GridView& out, const u64* slices, uint32_t* leaf_box, int32_t* leaf_inrun, i64* vox_part,
+                     hipStream_t s) {
+  launch("k_leaf_stats", k_leaf_stats, ceil_div((i64)out.n_leaf, 256), 256, s, slices, out.leaf_mask,
          out.leaf_prefix, leaf_box, leaf_inrun, vox_part, (i64)out.n_leaf);
 }
 

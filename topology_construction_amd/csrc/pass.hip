@@ -367,24 +367,36 @@ constexpr int kTilesItems = kTilesMax / kTilesThreads;
 constexpr int kRankMax = 256;  // keys sorted by rank counting; more go through a bitonic network
 constexpr i64 kTileBits = 65536;  // mixed-radix (grid, tile) key space handled by an LDS bitmap
 
-__global__ void __launch_bounds__(kTilesThreads) k_tiles_small(const int4* upper_origin, const u64* upper_mask,
-                                                               int32_t n_upper, int op, int m, int32_t B,
-                                                               int4* utile, int32_t* tile_of_cand,
-                                                               int32_t* d_num_tiles, int32_t* grid_tile_begin,
-                                                               u64* tile_child, int zero_child,
-                                                               const uint32_t* upper_reach, int32_t* readback,
-                                                               const int32_t* src_status) {
-  __shared__ u64 s_hi[kTilesMax];
-  __shared__ u64 s_lo[kTilesMax];
-  __shared__ uint32_t s_v[kTilesMax];
-  __shared__ int32_t s_g[kTilesMax];  // reach set per upper first, grid per unique tile later
-  __shared__ int32_t s_wave[kTilesThreads / kWave];
+// LDS of the tile stage, carved from one block so that the fused node stage
+// can reuse it for the lower stage (offsets in bytes, 16-byte aligned).
+constexpr int kTL_hi = 0;
+constexpr int kTL_lo = kTL_hi + 8 * kTilesMax;
+constexpr int kTL_v = kTL_lo + 8 * kTilesMax;
+constexpr int kTL_g = kTL_v + 4 * kTilesMax;
+constexpr int kTL_bits = kTL_g + 4 * kTilesMax;
+constexpr int kTL_wpre = kTL_bits + 8 * (kTileBits / 64);
+constexpr int kTL_cnt = kTL_wpre + 4 * (kTileBits / 64);
+constexpr int kTL_wave = kTL_cnt + 4 * kTilesThreads;
+constexpr int kTL_rng = kTL_wave + 4 * (kTilesThreads / kWave);
+constexpr int kTL_nt = kTL_rng + 4 * 8;
+constexpr int kTilesLds = kTL_nt + 16;
+
+__device__ __forceinline__ void tiles_small_body(const int4* upper_origin, const u64* upper_mask, int32_t n_upper,
+                                                 int op, int m, int32_t B, int4* utile, int32_t* tile_of_cand,
+                                                 int32_t* d_num_tiles, int32_t* grid_tile_begin, u64* tile_child,
+                                                 int zero_child, const uint32_t* upper_reach, int32_t* readback,
+                                                 const int32_t* src_status, char* lds) {
+  u64* s_hi = reinterpret_cast<u64*>(lds + kTL_hi);
+  u64* s_lo = reinterpret_cast<u64*>(lds + kTL_lo);
+  uint32_t* s_v = reinterpret_cast<uint32_t*>(lds + kTL_v);
+  int32_t* s_g = reinterpret_cast<int32_t*>(lds + kTL_g);  // reach set per upper first, grid per unique tile later
+  int32_t* s_wave = reinterpret_cast<int32_t*>(lds + kTL_wave);
   uint32_t* s_code = reinterpret_cast<uint32_t*>(s_g);
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wv = tid / kWave;
   const int n = n_upper * m;
-  __shared__ int32_t s_rng[6];  // min x, y, z, max x, y, z of the kept candidates' tiles
+  int32_t* s_rng = reinterpret_cast<int32_t*>(lds + kTL_rng);  // min x, y, z, max x, y, z of the kept candidates' tiles
   if (tid == 0) {
     readback[0] = src_status[0] != 0 ? kFlagSource : 0;  // a flawed source fails the pass
     for (int a = 0; a < 3; ++a) {
@@ -471,15 +483,15 @@ __global__ void __launch_bounds__(kTilesThreads) k_tiles_small(const int4* upper
       ++pos;
     }
   }
-  __shared__ int32_t s_nt;
+  int32_t& s_nt = *reinterpret_cast<int32_t*>(lds + kTL_nt);
   // More than 64 keys: the (grid, tile) keys of the kept candidates, relative to
   // the batch's tile ranges, index a mixed-radix space of S = B * Rx * Ry * Rz
   // points in canonical order. When S is at most kTileBits, one bit per
   // candidate in an LDS bitmap replaces the sort: the set bits are the unique
   // tiles in order, and a popcount prefix gives every candidate its tile (whose
   // record every candidate of it writes, with the same value).
-  __shared__ u64 s_bits[kTileBits / 64];
-  __shared__ int32_t s_wpre[kTileBits / 64];
+  u64* s_bits = reinterpret_cast<u64*>(lds + kTL_bits);
+  int32_t* s_wpre = reinterpret_cast<int32_t*>(lds + kTL_wpre);
   if (K > kWave) {  // uniform
     {
       int rmin[3] = {INT32_MAX, INT32_MAX, INT32_MAX}, rmax[3] = {INT32_MIN, INT32_MIN, INT32_MIN};
@@ -564,7 +576,7 @@ __global__ void __launch_bounds__(kTilesThreads) k_tiles_small(const int4* upper
   // index). With Kp = K rounded up to a power of two (>= 64), T = 1024 / Kp
   // threads share each key: thread (part, i) counts the keys smaller than key i
   // among its 1/T of the keys; the partial ranks meet in LDS.
-  __shared__ int32_t s_cnt[kTilesThreads];
+  int32_t* s_cnt = reinterpret_cast<int32_t*>(lds + kTL_cnt);
   int rank = 0;  // thread tid < K: the rank of key tid, which it holds in rhi, rlo, rv
   u64 rhi = 0, rlo = 0;
   uint32_t rv = 0;
@@ -783,6 +795,18 @@ __global__ void __launch_bounds__(kTilesThreads) k_tiles_small(const int4* upper
   }
 }
 
+__global__ void __launch_bounds__(kTilesThreads) k_tiles_small(const int4* upper_origin, const u64* upper_mask,
+                                                               int32_t n_upper, int op, int m, int32_t B,
+                                                               int4* utile, int32_t* tile_of_cand,
+                                                               int32_t* d_num_tiles, int32_t* grid_tile_begin,
+                                                               u64* tile_child, int zero_child,
+                                                               const uint32_t* upper_reach, int32_t* readback,
+                                                               const int32_t* src_status) {
+  __shared__ __align__(16) char lds[kTilesLds];
+  tiles_small_body(upper_origin, upper_mask, n_upper, op, m, B, utile, tile_of_cand, d_num_tiles, grid_tile_begin,
+                   tile_child, zero_child, upper_reach, readback, src_status, lds);
+}
+
 // ------------------------------------------------------------------ stage: lowers
 // Target lower of source lower K for candidate j, and the index (among the
 // parent upper's tile candidates) of the tile that holds it.
@@ -928,16 +952,23 @@ constexpr int kLowersItems = kLowersSmallMax / kLowersThreads;
 constexpr int kLdsTiles = 28;
 constexpr int kReachMax = 512;  // source lowers with a reach set: n / m for m >= 8
 
-__global__ void __launch_bounds__(kLowersThreads) k_lowers_small(
+constexpr int kLL_tile = 0;
+constexpr int kLL_tpre = kLL_tile + 8 * kLdsTiles * 512;
+constexpr int kLL_base = kLL_tpre + 2 * kLdsTiles * 512;
+constexpr int kLL_reach = kLL_base + 4 * ((kLowersSmallTiles + 4) / 4 * 4);
+constexpr int kLL_wave = kLL_reach + 4 * kReachMax;
+constexpr int kLowersLds = kLL_wave + 4 * (kLowersThreads / kWave);
+
+__device__ __forceinline__ void lowers_small_body(
     const int4* lower_origin, const u64* lower_mask, i64 n, int op, int m, int m_src, const int32_t* tile_of_cand,
     const int32_t* d_num_tiles, u64* tile_child, uint16_t* tile_prefix, int32_t* tile_lower_base,
     int32_t* d_num_cands, u64* cand_child, int zero_cand_child, int32_t* lower_nbr, int4* cand_origin,
-    int32_t* cand_src, int32_t* flags, const uint32_t* lower_reach) {
-  __shared__ __align__(16) u64 s_tile[kLdsTiles * 512];
-  __shared__ __align__(16) uint16_t s_tpre[kLdsTiles * 512];
-  __shared__ int32_t s_base[kLowersSmallTiles + 1];
-  __shared__ uint32_t s_reach[kReachMax];
-  __shared__ int32_t s_wave[kLowersThreads / kWave];
+    int32_t* cand_src, int32_t* flags, const uint32_t* lower_reach, char* lds) {
+  u64* s_tile = reinterpret_cast<u64*>(lds + kLL_tile);
+  uint16_t* s_tpre = reinterpret_cast<uint16_t*>(lds + kLL_tpre);
+  int32_t* s_base = reinterpret_cast<int32_t*>(lds + kLL_base);
+  uint32_t* s_reach = reinterpret_cast<uint32_t*>(lds + kLL_reach);
+  int32_t* s_wave = reinterpret_cast<int32_t*>(lds + kLL_wave);
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wv = tid / kWave;
@@ -1086,6 +1117,27 @@ __global__ void __launch_bounds__(kLowersThreads) k_lowers_small(
     ulonglong2* dst2 = reinterpret_cast<ulonglong2*>(tile_child);
     for (int k = tid; k < nt * 256; k += kLowersThreads) dst2[k] = src2[k];
   }
+}
+
+// Tile and lower stages of a small batch in one workgroup: the tile stage's
+// results reach the lower stage through global memory written and read by this
+// workgroup (ordered by the block barrier between them), and both stages carve
+// their LDS from the same block.
+constexpr int kNodesLds = kTilesLds > kLowersLds ? kTilesLds : kLowersLds;
+static_assert(kTilesThreads == kLowersThreads, "one workgroup shape for both stages");
+__global__ void __launch_bounds__(kTilesThreads) k_nodes_small(
+    const int4* upper_origin, const u64* upper_mask, int32_t n_upper, int32_t B, int4* utile,
+    int32_t* grid_tile_begin, const uint32_t* upper_reach, int32_t* readback, const int32_t* src_status,
+    const int4* lower_origin, const u64* lower_mask, i64 n, int op, int m, int m_src, int32_t* tile_of_cand,
+    int32_t* d_num_tiles, u64* tile_child, uint16_t* tile_prefix, int32_t* tile_lower_base, int32_t* d_num_cands,
+    u64* cand_child, int32_t* lower_nbr, int4* cand_origin, int32_t* cand_src, const uint32_t* lower_reach) {
+  __shared__ __align__(16) char lds[kNodesLds];
+  tiles_small_body(upper_origin, upper_mask, n_upper, op, m, B, utile, tile_of_cand, d_num_tiles, grid_tile_begin,
+                   tile_child, 0, upper_reach, readback, src_status, lds);
+  __syncthreads();
+  lowers_small_body(lower_origin, lower_mask, n, op, m, m_src, tile_of_cand, d_num_tiles, tile_child, tile_prefix,
+                    tile_lower_base, d_num_cands, cand_child, 0, lower_nbr, cand_origin, cand_src, readback,
+                    lower_reach, lds);
 }
 
 // ------------------------------------------------------------------ stage: leaves (pass A)
@@ -1983,11 +2035,20 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, 
         launch("k_node_reach", k_node_reach, ceil_div((i64)src->n2, 4), 256, s, (const u64*)sv.upper_mask,
                (i64)src->n2, 512, op, oi.m, ureach);
       }
-      launch("k_tiles_small", k_tiles_small, 1, kTilesThreads, s, (const int4*)sv.upper_origin,
-             (const u64*)sv.upper_mask, (int32_t)src->n2, op, oi.m, B, ts.utile, tile_of_cand, ts.d_num_tiles,
-             ts.grid_tile_begin, ts.tile_child, zero_here ? 1 : 0, (const uint32_t*)ureach, ts.readback,
-             (const int32_t*)sv.status);
-      if (!small_lowers && !zero_here) fill_u64(ts.tile_child, 0, nT * 512, ts.d_num_tiles, 512, s);
+      if (small_lowers) {  // the lower stage follows in the same workgroup
+        launch("k_nodes_small", k_nodes_small, 1, kTilesThreads, s, (const int4*)sv.upper_origin,
+               (const u64*)sv.upper_mask, (int32_t)src->n2, B, ts.utile, ts.grid_tile_begin,
+               (const uint32_t*)ureach, ts.readback, (const int32_t*)sv.status, (const int4*)sv.lower_origin,
+               (const u64*)sv.lower_mask, nL, op, oi.m, oi.m_src, tile_of_cand, ts.d_num_tiles, ts.tile_child,
+               ts.tile_prefix, ts.tile_lower_base, ts.d_num_cands, ts.cand_child, lower_nbr, ts.cand_origin, cand_src,
+               (const uint32_t*)box_lreach);
+      } else {
+        launch("k_tiles_small", k_tiles_small, 1, kTilesThreads, s, (const int4*)sv.upper_origin,
+               (const u64*)sv.upper_mask, (int32_t)src->n2, op, oi.m, B, ts.utile, tile_of_cand, ts.d_num_tiles,
+               ts.grid_tile_begin, ts.tile_child, zero_here ? 1 : 0, (const uint32_t*)ureach, ts.readback,
+               (const int32_t*)sv.status);
+        if (!zero_here) fill_u64(ts.tile_child, 0, nT * 512, ts.d_num_tiles, 512, s);
+      }
     } else {
       launch("k_flags_from_source", k_flags_from_source, 1, 64, s, ts.readback, (const int32_t*)sv.status);
       if (nT > 0) {
@@ -2011,13 +2072,7 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, 
     }
     // lowers. The candidate -> source table starts empty; refine and the box ops
     // store every word of their candidates' leaf masks, coarsen ORs into zeros.
-    if (small_lowers) {
-      launch("k_lowers_small", k_lowers_small, 1, kLowersThreads, s, (const int4*)sv.lower_origin,
-             (const u64*)sv.lower_mask, nL, op, oi.m, oi.m_src, (const int32_t*)tile_of_cand,
-             (const int32_t*)ts.d_num_tiles, ts.tile_child, ts.tile_prefix, ts.tile_lower_base, ts.d_num_cands,
-             ts.cand_child, 0, lower_nbr, ts.cand_origin, cand_src, ts.flags,
-             (const uint32_t*)box_lreach);
-    } else {
+    if (!small_lowers) {
       uint32_t* lreach = nullptr;
       if (op != TC_OP_COARSEN) {
         lreach = a.at<uint32_t>(o_lreach);

@@ -48,6 +48,37 @@ def test_from_ijk_unsorted_duplicated_rows():
     _check("identity", 1, ijk2, off2, "shuffled+dup")
 
 
+def test_from_ijk_scattered_rows():
+    """Rows too far apart to share a packed key (more than 2^15 in x, leaf y or
+    leaf z from their chunk's first row) take the front-end's unpacked path, one
+    record per run; clustered members beside them take the packed one."""
+    rng = np.random.default_rng(11)
+    members = []
+    for g in range(6):
+        if g % 2 == 0:  # scattered over +-2^28, in arbitrary order, with repeats
+            m = rng.integers(-(1 << 28), 1 << 28, size=(3000, 3))
+            m = np.concatenate([m, m[:500]])
+        else:  # a clustered blob in the same batch
+            m = rng.integers(0, 40, size=(3000, 3)) + rng.integers(-(1 << 20), 1 << 20, size=3)
+        members.append(m[rng.permutation(len(m))].astype(np.int32))
+    ijk, off = synth.concat_members(members)
+    _check("identity", 1, ijk, off, "scattered")
+    _check("dilate", 1, ijk, off, "scattered")
+
+
+def test_from_ijk_tile_table_rerun():
+    """More distinct root tiles (36^3 = 46656) than the front-end's first tile
+    table takes at half load (2^15): the record pass runs again with a table
+    sized by its record count."""
+    t = np.arange(36) * 4096 - 18 * 4096
+    X, Y, Z = np.meshgrid(t, t, t, indexing="ij")
+    v = np.stack([X.ravel(), Y.ravel(), Z.ravel()], axis=1) + np.array([5, 1, 3])
+    rng = np.random.default_rng(12)
+    v = v[rng.permutation(len(v))].astype(np.int32)
+    ijk, off = synth.concat_members([v[:20000], v[20000:]])
+    _check("identity", 1, ijk, off, "many tiles")
+
+
 @pytest.mark.parametrize("op,f", OPS)
 def test_config1_ops(op, f):
     ijk, off = synth.make_config(1)

@@ -229,14 +229,15 @@ __device__ __forceinline__ i64 lower_key(int32_t slot, int32_t x, int32_t y, int
 // repeats away). At most one listing per record.
 constexpr int kLowSet = 256;
 __device__ __forceinline__ void lower_add(i64 lk, u64* s_low, int32_t* s_lcnt, i64* low_out) {
-  unsigned h = (unsigned)(((u64)lk * 0x9e3779b97f4a7c15ull) >> 56);
-  for (int probe = 0; probe < kLowSet; ++probe) {
-    const u64 prev = atomicCAS((unsigned long long*)&s_low[h], (unsigned long long)kRecEmpty, (unsigned long long)lk);
-    if (prev == (u64)lk) return;
-    if (prev == kRecEmpty) break;
+  unsigned h = ((uint32_t)lk * 0x9e3779b1u ^ (uint32_t)((u64)lk >> 32) * 0x85ebca6bu) >> 24;
+  u64 prev;
+  int probe = 0;
+#pragma unroll 1
+  do {  // one exit: the key's entry, a free entry, or a full set
+    prev = atomicCAS((unsigned long long*)&s_low[h], (unsigned long long)kRecEmpty, (unsigned long long)lk);
     h = (h + 1) & (kLowSet - 1);
-  }
-  low_out[atomicAdd(s_lcnt, 1)] = lk;
+  } while (prev != kRecEmpty && prev != (u64)lk && ++probe < kLowSet);
+  if (prev != (u64)lk) low_out[atomicAdd(s_lcnt, 1)] = lk;
 }
 
 // Claims or finds `key` in the LDS table and ORs `bits` into its entry. The
@@ -244,21 +245,25 @@ __device__ __forceinline__ void lower_add(i64 lk, u64* s_low, int32_t* s_lcnt, i
 // entry there and stores its representative row. The table holds at most
 // kRecChunk keys, so a free entry is always found.
 __device__ __forceinline__ void rec_insert(u64* s_key, u64* s_bits, int32_t* s_rep, int16_t* s_list, int32_t* s_cnt,
-                                           u64 key, u64 bits, int32_t rep) {
+                                           u64 key, u64 bits, int32_t rep, int32_t* flags) {
   unsigned h = ((uint32_t)key * 0x9e3779b1u ^ (uint32_t)(key >> 32) * 0x85ebca6bu) >> (32 - kRecTableBits);
-  for (int probe = 0; probe < kRecTable; ++probe) {
-    const u64 prev = atomicCAS((unsigned long long*)&s_key[h], (unsigned long long)kRecEmpty,
-                               (unsigned long long)key);
-    if (prev == kRecEmpty) {
-      s_rep[h] = rep;
-      s_list[atomicAdd(s_cnt, 1)] = (int16_t)h;
-    }
-    if (prev == kRecEmpty || prev == key) {
-      atomicOr((unsigned long long*)&s_bits[h], (unsigned long long)bits);
-      return;
-    }
+  u64 prev;
+  int probe = 0;
+#pragma unroll 1
+  do {  // one exit: the key's entry or a free one (always found: a chunk has at most kRecChunk keys)
+    prev = atomicCAS((unsigned long long*)&s_key[h], (unsigned long long)kRecEmpty, (unsigned long long)key);
+    if (prev == kRecEmpty || prev == key) break;
     h = (h + 1) & (kRecTable - 1);
+  } while (++probe < kRecTable);
+  if (prev != kRecEmpty && prev != key) {  // consistency guard
+    atomicOr(flags, kFlagInternal);
+    return;
   }
+  if (prev == kRecEmpty) {
+    s_rep[h] = rep;
+    s_list[atomicAdd(s_cnt, 1)] = (int16_t)h;
+  }
+  atomicOr((unsigned long long*)&s_bits[h], (unsigned long long)bits);
 }
 
 // The record pass. One persistent workgroup per region; it takes the region's
@@ -386,7 +391,7 @@ __global__ void __launch_bounds__(256) k_ijk_records(const int32_t* ijk, const i
     if (packed) {
 #pragma unroll
       for (int r = 0; r < kRecRows; ++r)
-        if (head[r]) rec_insert(s_key, s_bits, s_rep, s_list, &s_cnt, key[r], rb[r], (int32_t)(i0 + r));
+        if (head[r]) rec_insert(s_key, s_bits, s_rep, s_list, &s_cnt, key[r], rb[r], (int32_t)(i0 + r), &ctl[2]);
     } else {  // each run is a record now; its list entry says so
 #pragma unroll
       for (int r = 0; r < kRecRows; ++r) {
@@ -483,7 +488,7 @@ constexpr int kPerLane = 4;  // kernels that merge through the block's LDS table
 constexpr int kPerBlock = 256 * kPerLane;
 constexpr int kPerLaneWide = 8;
 constexpr int kPerBlockWide = 256 * kPerLaneWide;
-constexpr int kRecSplit = 4;  // consumer workgroups per region
+constexpr int kRecSplit = 2;  // consumer workgroups per region
 
 // Every lower key sets its bit in its tile's candidate-lower mask (merged per
 // mask word in LDS first: lower keys of nearby chunks repeat the same few

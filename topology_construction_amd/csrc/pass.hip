@@ -1130,8 +1130,10 @@ __global__ void __launch_bounds__(kTilesThreads) k_nodes_small(
     int32_t* grid_tile_begin, const uint32_t* upper_reach, int32_t* readback, const int32_t* src_status,
     const int4* lower_origin, const u64* lower_mask, i64 n, int op, int m, int m_src, int32_t* tile_of_cand,
     int32_t* d_num_tiles, u64* tile_child, uint16_t* tile_prefix, int32_t* tile_lower_base, int32_t* d_num_cands,
-    u64* cand_child, int32_t* lower_nbr, int4* cand_origin, int32_t* cand_src, const uint32_t* lower_reach) {
+    u64* cand_child, int32_t* lower_nbr, int4* cand_origin, int32_t* cand_src, const uint32_t* lower_reach,
+    int32_t* zero_word) {
   __shared__ __align__(16) char lds[kNodesLds];
+  if (threadIdx.x == 0) *zero_word = 0;
   tiles_small_body(upper_origin, upper_mask, n_upper, op, m, B, utile, tile_of_cand, d_num_tiles, grid_tile_begin,
                    tile_child, 0, upper_reach, readback, src_status, lds);
   __syncthreads();
@@ -1946,14 +1948,15 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, 
   // Small batches lay the output out by capacities known before any launch (a
   // source leaf feeds at most 8 / 1 / 27 / 8 output leaves for refine, coarsen,
   // dilate, pads; the tile and lower candidates bound the nodes), so the output
-  // is allocated first and the writers follow the counts stage without a host
-  // round trip; the one readback (headers and status) ends the pass.
+  // is allocated while the node, marking and count stages run (they do not touch
+  // it) and the writers follow the counts stage without a host round trip; the
+  // one readback (headers and status) ends the pass.
   const i64 per_leaf = op == TC_OP_REFINE ? 8 : (op == TC_OP_COARSEN ? 1 : oi.m);
   const i64 gran = op == TC_OP_REFINE ? 256 : 64;  // leaves per gather workgroup (voxel-sum runs)
   const i64 L_cap = (i64)src->nl * per_leaf;
   const bool bounded = small_lowers && L_cap > 0 && L_cap <= 0x7fffffffLL && finalize_small_fits(L_cap, B, gran) &&
                        make_layout(B, nT, nL, L_cap).total <= kBoundedBytes;
-  tc_grid_batch* out = bounded ? new_batch_capacity(B, nT, nL, L_cap, oa) : nullptr;
+  tc_grid_batch* out = nullptr;
   try {
     Arena a(s);
     const i64 nTs = small_tiles ? 0 : nT;  // sort scratch only for the multi-kernel tile path
@@ -1980,7 +1983,7 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, 
     const size_t o_nbr = a.reserve(4 * nL);
     const size_t o_csrc = a.reserve(4 * nL * oi.m_src);
     const size_t o_ginfo = a.reserve(4 * 6 * (i64)B);
-    const size_t o_rb = a.reserve(4 * (4 + 3 * (i64)B));
+    const size_t o_rb = a.reserve(4 * (5 + 3 * (i64)B));  // readback words, then the finalize's done counter
     const size_t o_ureach = a.reserve(4 * (i64)src->n2);
     const size_t o_lreach = a.reserve(4 * (i64)src->n1);
     const size_t o_stmp = a.reserve(std::max(scan_tmp_bytes(nT, 4), scan_tmp_bytes(nL, 8)));
@@ -2041,7 +2044,7 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, 
                (const uint32_t*)ureach, ts.readback, (const int32_t*)sv.status, (const int4*)sv.lower_origin,
                (const u64*)sv.lower_mask, nL, op, oi.m, oi.m_src, tile_of_cand, ts.d_num_tiles, ts.tile_child,
                ts.tile_prefix, ts.tile_lower_base, ts.d_num_cands, ts.cand_child, lower_nbr, ts.cand_origin, cand_src,
-               (const uint32_t*)box_lreach);
+               (const uint32_t*)box_lreach, ts.readback + 4 + 3 * B);
       } else {
         launch("k_tiles_small", k_tiles_small, 1, kTilesThreads, s, (const int4*)sv.upper_origin,
                (const u64*)sv.upper_mask, (int32_t)src->n2, op, oi.m, B, ts.utile, tile_of_cand, ts.d_num_tiles,
@@ -2114,7 +2117,9 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, 
     ts.cand_counts_ready = true;
     // counts and the single readback
     tree_counts(ts, B, s);
-    if (!bounded) {  // exact layout: counts first, then the allocation
+    if (bounded) {  // capacity layout: allocated while the stages above run
+      out = new_batch_capacity(B, nT, nL, L_cap, oa);
+    } else {  // exact layout: counts first, then the allocation
       const size_t rb_bytes = 4 * (4 + 3 * (size_t)B);
       int32_t* h_rb = static_cast<int32_t*>(pinned_staging(rb_bytes));
       hip_check(hipMemcpyAsync(h_rb, ts.readback, rb_bytes, hipMemcpyDeviceToHost, s), "readback");
@@ -2160,12 +2165,14 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, 
     // the gathers' consistency checks set bits in the flag word after the
     // counts: the finalize copies it into the batch's status word
     apply_debug_inject(ts.flags, s);
+    // small batches: the finalize's last workgroup copies every header and the
+    // status word into pinned host memory (the pass's one readback)
+    const size_t hb = sizeof(tc_grid_header) * (size_t)B + 16;
+    char* h = bounded ? static_cast<char*>(pinned_staging(hb)) : nullptr;
     tree_finalize_leaves(ov, post.at<uint32_t>(o_box), leaf_inrun, vox_part, gran, post.at<i64>(o_gvb),
-                         post.at<int32_t>(o_bb), (const int32_t*)ts.grid_info, ts.flags, d_L, s);
-    if (bounded) {  // the pass's one readback: every header and the status word
-      const size_t hb = sizeof(tc_grid_header) * (size_t)B + 16;
-      char* h = static_cast<char*>(pinned_staging(hb));
-      hip_check(hipMemcpyAsync(h, ov.headers, hb, hipMemcpyDeviceToHost, s), "readback");
+                         post.at<int32_t>(o_bb), (const int32_t*)ts.grid_info, ts.flags, d_L, s,
+                         bounded ? ts.readback + 4 + 3 * B : nullptr, reinterpret_cast<int32_t*>(h));
+    if (bounded) {
       hip_check(hipStreamSynchronize(s), "hipStreamSynchronize");
       check_pass_flags(*reinterpret_cast<const int32_t*>(h + sizeof(tc_grid_header) * (size_t)B));
       set_counts_from_headers(out, reinterpret_cast<const tc_grid_header*>(h));

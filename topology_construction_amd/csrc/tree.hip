@@ -582,12 +582,11 @@ __device__ __forceinline__ void box_fold_lds(int32_t (*s_box)[kFinSmallGrids], i
   }
 }
 
-__global__ void __launch_bounds__(kFinThreads) k_finalize_small(const int4* leaf_origin, const int32_t* leaf_inrun,
-                                                                const uint32_t* leaf_box, const i64* vox_part,
-                                                                int32_t gs, const int32_t* grid_info,
-                                                                i64* leaf_offset, int32_t B, const int32_t* d_L,
-                                                                int32_t L_cap, tc_grid_header* hdr,
-                                                                int32_t* flags, int32_t* status) {
+__device__ __forceinline__ void finalize_small_body(const int4* leaf_origin, const int32_t* leaf_inrun,
+                                                    const uint32_t* leaf_box, const i64* vox_part, int32_t gs,
+                                                    const int32_t* grid_info, i64* leaf_offset, int32_t B,
+                                                    const int32_t* d_L, int32_t L_cap, tc_grid_header* hdr,
+                                                    int32_t* flags, int32_t* status) {
   constexpr int kR = kFinRuns / kFinThreads;
   constexpr int kG = kFinSmallGrids / kFinThreads;
   // the leaf count from the device (the launch may be sized by a capacity):
@@ -751,6 +750,41 @@ __global__ void __launch_bounds__(kFinThreads) k_finalize_small(const int4* leaf
   }
 }
 
+// With a host mirror (pinned host memory the device can write), the last
+// workgroup to finish copies every header and the status word there, so that
+// the host reads them after the stream's completion with no copy command. Each
+// workgroup publishes its writes (device fence) before it counts itself in
+// done_ctr (zeroed before the launch); the last one takes the others' with a
+// device fence and reads the words with device-scope loads.
+__device__ __forceinline__ void mirror_headers_last(const tc_grid_header* hdr, int32_t B, int32_t* done_ctr,
+                                                    int32_t* host_words) {
+  __shared__ int32_t s_last;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __threadfence();
+    s_last = atomicAdd(done_ctr, 1) == (int32_t)gridDim.x - 1 ? 1 : 0;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  const int32_t* words = reinterpret_cast<const int32_t*>(hdr);  // the status word follows the headers
+  const int32_t n = (int32_t)((sizeof(tc_grid_header) * (size_t)B + 16) / 4);
+  for (int32_t k = threadIdx.x; k < n; k += blockDim.x)
+    host_words[k] = __hip_atomic_load(&words[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__global__ void __launch_bounds__(kFinThreads) k_finalize_small(const int4* leaf_origin, const int32_t* leaf_inrun,
+                                                                const uint32_t* leaf_box, const i64* vox_part,
+                                                                int32_t gs, const int32_t* grid_info,
+                                                                i64* leaf_offset, int32_t B, const int32_t* d_L,
+                                                                int32_t L_cap, tc_grid_header* hdr,
+                                                                int32_t* flags, int32_t* status, int32_t* done_ctr,
+                                                                int32_t* host_words) {
+  finalize_small_body(leaf_origin, leaf_inrun, leaf_box, vox_part, gs, grid_info, leaf_offset, B, d_L, L_cap, hdr,
+                      flags, status);
+  if (host_words) mirror_headers_last(hdr, B, done_ctr, host_words);
+}
+
 // Large batches: the leaf producer left one voxel sum per run of `gran` leaves
 // (vox_part). One workgroup scans those sums, sets up the bbox accumulators and
 // derives every grid's voxel begin (its first leaf's run offset plus the leaves
@@ -891,7 +925,9 @@ bool finalize_small_fits(i64 L, int32_t B, i64 gran) {
 
 void tree_finalize_leaves(const GridView& out, const uint32_t* leaf_box, const int32_t* leaf_inrun, i64* vox_part,
                           i64 gran, i64* gvb, int32_t* bbox_accum, const int32_t* grid_info, int32_t* flags,
-                          const int32_t* d_L, hipStream_t s) {
+                          const int32_t* d_L, hipStream_t s, int32_t* done_ctr, int32_t* host_words) {
+  if (host_words && !finalize_small_fits(out.n_leaf, out.B, gran))
+    throw Error(TC_ERR_INTERNAL, "finalize: a host mirror needs the one-launch finalize");
   const i64 L = out.n_leaf;  // the leaf count, or (d_L given) a capacity with the count at d_L
   const int32_t B = out.B;
   if (gran <= 0 || (gran & (gran - 1)) != 0) throw Error(TC_ERR_INTERNAL, "finalize: run length not a power of two");
@@ -899,7 +935,7 @@ void tree_finalize_leaves(const GridView& out, const uint32_t* leaf_box, const i
     launch("k_finalize_small", k_finalize_small, std::max<i64>(1, ceil_div(L, kFinSlice)), kFinThreads, s,
            (const int4*)out.leaf_origin, leaf_inrun, leaf_box, (const i64*)vox_part,
            (int32_t)__builtin_ctzll((u64)gran), grid_info, out.leaf_offset, B, d_L, (int32_t)L, out.headers,
-           flags, out.status);
+           flags, out.status, done_ctr, host_words);
     return;
   }
   // the wide path runs on exact counts only (its launches are sized by them)

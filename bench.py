@@ -4,14 +4,16 @@ A step is one pass of the whole hot path over the B=16 resolution-64 shell
 batch (16 ellipsoid shells, ~7.4k voxels each; it stands in for the pages'
 shape-VAE workload of 16 shoes at resolution 64): conv k2s2 (coarsen x2),
 k2s2 transpose (refine x2), k3s1 (box-dilate [-1,1]^3) and the chained k3s2
-transpose (refine x2 then pad {-1,0}^3), each followed by the jagged voxel
-enumeration. Inputs are resident in HBM before timing starts.
+transpose (refine x2 then pad {-1,0}^3), built by one multi-target call, then
+each target's jagged voxel enumeration. Inputs are resident in HBM before
+timing starts.
 
 Prints one JSON line (rank 0). `value` = output voxels per second over the K
 timed steps. `roofline` reports the dominant kernel's algorithmic bytes per
 launch over its HIP-event-timed average duration in those steps (and, beside
 it, the same over its kernel-trace duration from the committed profile);
-`ms_per_step_unprofiled` repeats the K steps without those events.
+`ms_per_step_unprofiled` repeats the K steps without those events, and
+`ms_per_step_one_call_per_op` with one build call per op.
 `cpu_baseline` times the CPU oracle on whole steps of the same workload, its
 members spread over the host's threads (single-thread and 46M-voxel figures
 beside it). Outside the timed steps the line also carries per-op medians
@@ -179,11 +181,17 @@ def cpu_baseline(np, ijk, off, large_input=None, min_s=10.0):
     return res
 
 
-def run_step(binding, src, outs=None):
-    """One step: every op, each followed by the voxel enumeration. Returns voxels."""
+def run_step(binding, src, outs=None, one_call=True):
+    """One step: every op's target, then each target's voxel enumeration. With
+    `one_call` the targets come from one tc_build_batched_topology_many call
+    (their passes enqueued back to back, one wait), else from one
+    tc_build_batched_topology call per op. Returns voxels."""
     total = 0
-    for op, f in STEP_OPS:
-        out = binding.tc_build_batched_topology(src, op, f)
+    if one_call:
+        built = binding.tc_build_batched_topology_many(src, STEP_OPS)
+    else:
+        built = [binding.tc_build_batched_topology(src, op, f) for op, f in STEP_OPS]
+    for (op, f), out in zip(STEP_OPS, built):
         ijk = binding.tc_enumerate_ijk(out)
         total += ijk.shape[0]
         if outs is not None:
@@ -458,6 +466,13 @@ def main():
         run_step(binding, src)
     torch.cuda.synchronize()
     ms_step_plain = (time.perf_counter() - t2) * 1e3 / args.steps
+    # the same steps with one build call per op (each waits for its own headers)
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for _ in range(args.steps):
+        run_step(binding, src, one_call=False)
+    torch.cuda.synchronize()
+    ms_step_single = (time.perf_counter() - t2) * 1e3 / args.steps
 
     # per-op breakdown (separate, untimed-by-the-step loop): pass and enumeration
     ops = op_medians(binding, torch, np, src)
@@ -525,6 +540,7 @@ def main():
     rec = {
         "metric": METRIC, "value": voxels / elapsed, "unit": "voxels/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_step, "ms_per_step_unprofiled": ms_step_plain,
+        "ms_per_step_one_call_per_op": ms_step_single,
         "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "int32", "data": "synthetic",
         "config": {"workload": synth.CONFIG_NAMES[args.config], "grids": int(len(off) - 1),

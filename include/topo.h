@@ -220,8 +220,9 @@ tc_status tc_batch_from_points(const float* d_xyz, const int64_t* h_offsets, int
  * capacities that fits in 32 MiB: at most 8 / 1 / 27 / 8 output leaves per
  * source leaf for refine / coarsen / dilate / pads, the tile and lower
  * candidates for the nodes, at most 1024 members and 262144 leaf slots) take
- * their one allocation before any launch and read back all headers at the end
- * (the voxel total is then known too); their arrays sit at capacity offsets
+ * their one allocation after the node, marking and count launches, with no
+ * readback before it, and read back all headers at the end (the voxel total is
+ * then known too); their arrays sit at capacity offsets
  * inside the buffer and buffer_bytes is the capacity. Larger batches read the
  * per-grid node counts back first and allocate exactly.
  * Returns TC_ERR_OVERFLOW (and no batch) when any output voxel would leave int32,
@@ -229,6 +230,24 @@ tc_status tc_batch_from_points(const float* d_xyz, const int64_t* h_offsets, int
 tc_status tc_build_batched_topology(const tc_grid_batch* src, int32_t op, int32_t factor,
                                     const tc_allocator* allocator, void* stream,
                                     tc_grid_batch** out);
+
+/* Several generated targets of one source in one call (PR page section 1: the
+ * per-iteration plan builds every target of a source; section 2: the box ops
+ * and the k3s2 chain). Equivalent to n_ops calls of tc_build_batched_topology,
+ * op h_ops[i] with factor h_factors[i] into out[i], on the same stream and
+ * allocator, but the small-batch passes of consecutive ops are enqueued back to
+ * back: each keeps its header readback pending, in a pinned host block of its
+ * own, and the call waits once, at the end, for all of them (a chain's
+ * intermediate passes still wait for their own counts).
+ *   n_ops      >= 1; h_ops, h_factors int32[n_ops] host; out tc_grid_batch*[n_ops]
+ *              host, every entry set (NULL on failure).
+ * On return every out[i] is as tc_build_batched_topology leaves it. Validation
+ * of every (op, factor) happens before any launch; an error in any op frees
+ * every batch the call made and reports that op's status (its index in the
+ * message when n_ops > 1). */
+tc_status tc_build_batched_topology_many(const tc_grid_batch* src, int32_t n_ops, const int32_t* h_ops,
+                                         const int32_t* h_factors, const tc_allocator* allocator,
+                                         void* stream, tc_grid_batch** out);
 
 /* Masked refine (PR page, test plan: masked refine): the voxels of `src` whose
  * keep flag is zero are dropped, the rest are refined by `factor` (2, 4 or 8),

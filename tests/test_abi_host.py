@@ -74,6 +74,19 @@ def test_build_rejects_bad_arguments_on_host(lib):
     assert lib.tc_build_batched_topology(None, 2, 2, None, None, None) == binding.TC_ERR_INVALID_ARG
 
 
+def test_build_many_rejects_bad_arguments_on_host(lib):
+    ops = (ctypes.c_int32 * 2)(binding.OPS["refine"], binding.OPS["dilate"])
+    facs = (ctypes.c_int32 * 2)(2, 1)
+    outs = (ctypes.c_void_p * 2)(123, 456)
+    assert lib.tc_build_batched_topology_many(None, 2, ops, facs, None, None, outs) == binding.TC_ERR_INVALID_ARG
+    assert outs[0] is None and outs[1] is None
+    assert b"src" in lib.tc_last_error()
+    assert lib.tc_build_batched_topology_many(None, 0, ops, facs, None, None, outs) == binding.TC_ERR_INVALID_ARG
+    assert b"n_ops" in lib.tc_last_error()
+    assert lib.tc_build_batched_topology_many(None, 2, None, facs, None, None, outs) == binding.TC_ERR_INVALID_ARG
+    assert lib.tc_build_batched_topology_many(None, 2, ops, facs, None, None, None) == binding.TC_ERR_INVALID_ARG
+
+
 def test_null_handles_are_rejected(lib):
     info = binding.tc_batch_info()
     assert lib.tc_batch_get_info(None, ctypes.byref(info)) == binding.TC_ERR_INVALID_ARG

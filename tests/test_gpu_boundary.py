@@ -197,3 +197,76 @@ def test_writer_flag_surfaces_as_internal_error():
     # nothing stays armed: the next builds are good
     good = binding.tc_build_batched_topology(src, "refine", 4)
     assert_same(gpu_fields(good), oracle.run("refine", 4, ijk, off), "after the flagged builds")
+
+
+MANY_OPS = [("coarsen", 2), ("refine", 2), ("dilate", 1), ("conv_t_k3s2", 2), ("refine", 4), ("conv_s1", 3),
+            ("conv_s1", 1), ("pad_pos", 1), ("coarsen", 8)]
+
+
+@pytest.mark.parametrize("cfg,allocator", [(3, "torch"), (1, None), (2, "torch")])
+def test_many_ops_equal_the_oracle_and_single_builds(cfg, allocator):
+    """Several targets of one source in one call (small-batch passes enqueued
+    back to back, one wait at the end): every output equals the oracle's and the
+    output of its own tc_build_batched_topology call, array by array, including
+    the headers, the voxel total and the enumeration."""
+    import torch
+    ijk, off = synth.make_config(cfg)
+    src = binding.tc_batch_from_ijk(torch.from_numpy(ijk).cuda(), off)
+    alloc = allocator or "none"
+    outs = binding.tc_build_batched_topology_many(src, MANY_OPS, allocator=alloc)
+    assert len(outs) == len(MANY_OPS)
+    for (op, f), out in zip(MANY_OPS, outs):
+        ref = oracle.run_threaded(op, f, ijk, off)
+        single = binding.tc_build_batched_topology(src, op, f, allocator=alloc)
+        if allocator == "torch":  # array views need the torch allocator
+            got = gpu_fields(out)
+            assert_same(got, ref, f"many {op} {f}")
+            ones = gpu_fields(single)
+        else:
+            got = {"headers": headers_as_oracle(out.headers()), "ijk": out.ijk().cpu().numpy()}
+            for name in got:
+                assert np.array_equal(got[name], ref[name]), f"many {op} {f} {name}"
+            ones = {"headers": headers_as_oracle(single.headers()), "ijk": single.ijk().cpu().numpy()}
+        for name in ones:
+            assert np.array_equal(got[name], ones[name]), f"{op} {f} {name}"
+        assert out.voxel_total() == ref["ijk"].shape[0]
+
+
+def test_many_ops_failures_free_every_output():
+    """An op that fails on the device (a flagged writer in a deferred pass), an
+    allocator that fails part way, and an invalid op in the list: the call
+    returns the error, every out entry is NULL, nothing is leaked, and the next
+    call is correct."""
+    import torch
+    lib = binding.load_library()
+    ijk, off = synth.make_config(1)
+    src = binding.tc_batch_from_ijk(torch.from_numpy(ijk).cuda(), off)
+    ops = [("refine", 2), ("dilate", 1), ("conv_t_k3s2", 2)]
+    n = len(ops)
+    op_ids = (ctypes.c_int32 * n)(*[binding.OPS[o] for o, _ in ops])
+    facs = (ctypes.c_int32 * n)(*[f for _, f in ops])
+    binding.tc_debug_inject_flags(2)  # the first op's (deferred) pass is flagged
+    with pytest.raises(binding.TopoError) as e:
+        binding.tc_build_batched_topology_many(src, ops)
+    assert e.value.status == binding.TC_ERR_INTERNAL
+    _release_all()
+    for fail_from in (1, 2, 3, 4, 5, 6, 8):
+        a = CountingAllocator(fail_from)
+        hs = (ctypes.c_void_p * n)(*([ctypes.c_void_p(8)] * n))
+        st = lib.tc_build_batched_topology_many(src.handle, n, op_ids, facs, ctypes.byref(a.struct), None, hs)
+        if st == binding.TC_OK:
+            for i in range(n):
+                binding.GridBatch(ctypes.c_void_p(hs[i]), torch_owned=False).free()
+        else:
+            assert st == binding.TC_ERR_ALLOC, lib.tc_last_error()
+            assert all(hs[i] is None for i in range(n))
+        _release_all()
+        assert not a.live, f"fail_from {fail_from}: {len(a.live)} blocks leaked"
+    bad = (ctypes.c_int32 * n)(binding.OPS["refine"], binding.OPS["dilate"], 99)
+    hs = (ctypes.c_void_p * n)()
+    assert lib.tc_build_batched_topology_many(src.handle, n, bad, facs, None, None, hs) == binding.TC_ERR_INVALID_ARG
+    assert b"op 2" in lib.tc_last_error()
+    assert all(hs[i] is None for i in range(n))
+    outs = binding.tc_build_batched_topology_many(src, ops)
+    for (op, f), out in zip(ops, outs):
+        assert_same(gpu_fields(out), oracle.run(op, f, ijk, off), f"after failures {op} {f}")

@@ -29,7 +29,7 @@ ABI_SYMBOLS = [
     "tc_build_batched_topology", "tc_build_masked_refine", "tc_batch_get_info", "tc_batch_read_headers",
     "tc_batch_voxel_total", "tc_enumerate_ijk", "tc_build_kernel_map", "tc_scratch_release", "tc_batch_free",
     "tc_debug_inject_flags", "tc_build_kernel_map_noalloc", "tc_profile_enable", "tc_profile_read",
-    "tc_profile_disable",
+    "tc_profile_disable", "tc_build_batched_topology_many",
 ]
 
 HEADER_DTYPE = np.dtype([
@@ -116,6 +116,8 @@ def load_library(path: str = LIB_PATH):
         lib.tc_batch_from_ijk.argtypes = [vp, vp, i32, vp, vp, ctypes.POINTER(vp)]
         lib.tc_build_batched_topology.restype = ctypes.c_int
         lib.tc_build_batched_topology.argtypes = [vp, i32, i32, vp, vp, ctypes.POINTER(vp)]
+        lib.tc_build_batched_topology_many.restype = ctypes.c_int
+        lib.tc_build_batched_topology_many.argtypes = [vp, i32, vp, vp, vp, vp, vp]
         lib.tc_build_masked_refine.restype = ctypes.c_int
         lib.tc_build_masked_refine.argtypes = [vp, vp, i64, i32, vp, vp, ctypes.POINTER(vp)]
         lib.tc_batch_get_info.restype = ctypes.c_int
@@ -328,6 +330,30 @@ def tc_build_batched_topology(src: GridBatch, op, factor: int, stream=None, allo
     _check(lib.tc_build_batched_topology(src.handle, op_id, int(factor), alloc, _stream_handle(stream),
                                          ctypes.byref(h)))
     return GridBatch(h, allocator == "torch")
+
+
+def tc_build_batched_topology_many(src: GridBatch, ops, stream=None, allocator: str = "torch") -> list:
+    """Several targets of one source in one call: `ops` is a sequence of
+    (op, factor) pairs (op a name or tc_op id); returns one GridBatch per pair."""
+    lib = load_library()
+    ops = list(ops)
+    n = len(ops)
+    if n < 1:
+        raise ValueError("ops is empty")
+    op_ids = (ctypes.c_int32 * n)(*[OPS[o] if isinstance(o, str) else int(o) for o, _ in ops])
+    factors = (ctypes.c_int32 * n)(*[int(f) for _, f in ops])
+    handles = (ctypes.c_void_p * n)()
+    alloc = ctypes.byref(TORCH_ALLOCATOR) if allocator == "torch" else None
+    _check(lib.tc_build_batched_topology_many(src.handle, n, op_ids, factors, alloc, _stream_handle(stream), handles))
+    out = []
+    try:
+        for i in range(n):
+            out.append(GridBatch(ctypes.c_void_p(handles[i]), allocator == "torch"))
+    except BaseException:
+        for j in range(len(out) + 1, n):  # handles not wrapped yet (the failed one frees itself)
+            lib.tc_batch_free(ctypes.c_void_p(handles[j]))
+        raise
+    return out
 
 
 def tc_build_masked_refine(src: GridBatch, keep, factor: int, stream=None, allocator: str = "torch") -> GridBatch:

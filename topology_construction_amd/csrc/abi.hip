@@ -137,6 +137,11 @@ tc_grid_batch* copy_batch(const tc_grid_batch* src, const OutAlloc& oa) {
 
 void free_batch(tc_grid_batch* b) {
   if (!b) return;
+  if (b->hdr_host) {  // headers still on their way land before the block is reused
+    if (b->hdr_pending && b->hdr_ev) (void)hipEventSynchronize(b->hdr_ev);
+    pinned_block_give(b->hdr_host, b->hdr_host_cap);
+  }
+  pending_event_give(b->device, b->hdr_ev);
   vox_slot_give(b->vox_slot);  // a copy still in flight is waited for by the slot's next taker
   if (b->block) {
     scratch_give_back(b->block, b->stream);
@@ -236,6 +241,63 @@ static i64 read_voxel_total(const tc_grid_batch* b, hipStream_t s, bool pageable
   return b->vox_total;
 }
 
+// The passes that build `op` with `factor`: a factor of 4 or 8 is two or three
+// factor-2 passes, the k3s2 transpose is a refine and a negative pad, and a
+// stride-1 convolution of kernel size k is the box [lo, hi] per axis made of
+// dilates (one step on both sides) and pads (one step on one side).
+tc_status op_passes(int32_t op, int32_t factor, std::vector<int>& passes, std::string& msg) {
+  passes.clear();
+  switch (op) {
+    case TC_OP_COARSEN:
+    case TC_OP_REFINE: {
+      if (factor < 2) {
+        msg = "refine/coarsen factor must be >= 2";
+        return TC_ERR_INVALID_ARG;
+      }
+      if (factor != 2 && factor != 4 && factor != 8) {
+        msg = "refine/coarsen factor must be 2, 4 or 8";
+        return TC_ERR_UNSUPPORTED;
+      }
+      for (int f = factor; f > 1; f >>= 1) passes.push_back(op);
+      return TC_OK;
+    }
+    case TC_OP_DILATE:
+    case TC_OP_PAD_NEG:
+    case TC_OP_PAD_POS:
+      if (factor != 1) {
+        msg = "box ops take factor 1";
+        return TC_ERR_INVALID_ARG;
+      }
+      passes.push_back(op);
+      return TC_OK;
+    case TC_OP_CONV_T_K3S2:
+      if (factor != 2) {
+        msg = "k3s2 transpose takes factor 2";
+        return TC_ERR_INVALID_ARG;
+      }
+      passes.push_back(TC_OP_REFINE);
+      passes.push_back(TC_OP_PAD_NEG);
+      return TC_OK;
+    case TC_OP_CONV_S1:
+    case TC_OP_CONV_T_S1: {
+      if (factor < 1 || factor > 8) {
+        msg = "kernel size must be in [1, 8]";
+        return TC_ERR_INVALID_ARG;
+      }
+      const int o_lo = -((factor - 1) / 2), o_hi = factor / 2;
+      const int lo = op == TC_OP_CONV_T_S1 ? o_lo : -o_hi, hi = op == TC_OP_CONV_T_S1 ? o_hi : -o_lo;
+      const int both = std::min(-lo, hi);
+      for (int i = 0; i < both; ++i) passes.push_back(TC_OP_DILATE);
+      for (int i = 0; i < -lo - both; ++i) passes.push_back(TC_OP_PAD_NEG);
+      for (int i = 0; i < hi - both; ++i) passes.push_back(TC_OP_PAD_POS);
+      return TC_OK;
+    }
+    default:
+      msg = "unknown op " + std::to_string(op);
+      return TC_ERR_INVALID_ARG;
+  }
+}
+
 }  // namespace tc
 
 extern "C" {
@@ -313,72 +375,69 @@ tc_status tc_batch_from_points(const float* d_xyz, const int64_t* h_offsets, int
 
 tc_status tc_build_batched_topology(const tc_grid_batch* src, int32_t op, int32_t factor,
                                     const tc_allocator* allocator, void* stream, tc_grid_batch** out) {
+  return tc_build_batched_topology_many(src, 1, &op, &factor, allocator, stream, out);
+}
+
+tc_status tc_build_batched_topology_many(const tc_grid_batch* src, int32_t n_ops, const int32_t* h_ops,
+                                         const int32_t* h_factors, const tc_allocator* allocator, void* stream,
+                                         tc_grid_batch** out) {
   if (!out) return fail(TC_ERR_INVALID_ARG, "out is NULL");
-  *out = nullptr;
+  if (n_ops < 1) return fail(TC_ERR_INVALID_ARG, "n_ops must be >= 1");
+  for (int32_t i = 0; i < n_ops; ++i) out[i] = nullptr;
+  if (!h_ops || !h_factors) return fail(TC_ERR_INVALID_ARG, "h_ops or h_factors is NULL");
   if (!src) return fail(TC_ERR_INVALID_ARG, "src is NULL");
   if (allocator && (!allocator->alloc || !allocator->free))
     return fail(TC_ERR_INVALID_ARG, "allocator callbacks are NULL");
-  std::vector<int> passes;
-  switch (op) {
-    case TC_OP_COARSEN:
-    case TC_OP_REFINE: {
-      if (factor < 2) return fail(TC_ERR_INVALID_ARG, "refine/coarsen factor must be >= 2");
-      if (factor != 2 && factor != 4 && factor != 8)
-        return fail(TC_ERR_UNSUPPORTED, "refine/coarsen factor must be 2, 4 or 8");
-      for (int f = factor; f > 1; f >>= 1) passes.push_back(op);
-      break;
-    }
-    case TC_OP_DILATE:
-    case TC_OP_PAD_NEG:
-    case TC_OP_PAD_POS:
-      if (factor != 1) return fail(TC_ERR_INVALID_ARG, "box ops take factor 1");
-      passes.push_back(op);
-      break;
-    case TC_OP_CONV_T_K3S2:
-      if (factor != 2) return fail(TC_ERR_INVALID_ARG, "k3s2 transpose takes factor 2");
-      passes.push_back(TC_OP_REFINE);
-      passes.push_back(TC_OP_PAD_NEG);
-      break;
-    case TC_OP_CONV_S1:
-    case TC_OP_CONV_T_S1: {
-      if (factor < 1 || factor > 8) return fail(TC_ERR_INVALID_ARG, "kernel size must be in [1, 8]");
-      // per-axis box [lo, hi]: each dilate adds one step on both sides, each pad one on its side
-      const int o_lo = -((factor - 1) / 2), o_hi = factor / 2;
-      const int lo = op == TC_OP_CONV_T_S1 ? o_lo : -o_hi, hi = op == TC_OP_CONV_T_S1 ? o_hi : -o_lo;
-      const int both = std::min(-lo, hi);
-      for (int i = 0; i < both; ++i) passes.push_back(TC_OP_DILATE);
-      for (int i = 0; i < -lo - both; ++i) passes.push_back(TC_OP_PAD_NEG);
-      for (int i = 0; i < hi - both; ++i) passes.push_back(TC_OP_PAD_POS);
-      break;
-    }
-    default:
-      return fail(TC_ERR_INVALID_ARG, "unknown op " + std::to_string(op));
+  std::vector<std::vector<int>> plan(n_ops);
+  for (int32_t i = 0; i < n_ops; ++i) {
+    std::string msg;
+    const tc_status st = tc::op_passes(h_ops[i], h_factors[i], plan[i], msg);
+    if (st != TC_OK) return fail(st, n_ops > 1 ? "op " + std::to_string(i) + ": " + msg : msg);
   }
-  return guarded([&]() {
+  std::vector<tc_grid_batch*> made(n_ops, nullptr);
+  const tc_status st = guarded([&]() {
     if (current_device() != src->device) throw tc::Error(TC_ERR_INVALID_ARG, "src lives on another device");
     tc::SourceScope scope(allocator);
     hipStream_t s = (hipStream_t)stream;
-    if (passes.empty()) {  // kernel size 1: the target is the source
-      *out = tc::finish_batch(tc::copy_batch(src, tc::OutAlloc{allocator, s}), s);
-      return TC_OK;
-    }
-    const tc_grid_batch* cur = src;
-    tc_grid_batch* owned = nullptr;  // intermediate result of the previous pass
-    try {
-      for (size_t p = 0; p < passes.size(); ++p) {
-        const bool last = p + 1 == passes.size();
-        tc_grid_batch* next = tc::build_pass(cur, passes[p], tc::OutAlloc{allocator, s, !last});
-        tc::free_batch(owned);
-        owned = next;
-        cur = next;
+    // every op's passes are enqueued back to back; a small batch's last pass
+    // leaves its header readback pending, and all are waited for at the end
+    for (int32_t i = 0; i < n_ops; ++i) {
+      const std::vector<int>& passes = plan[i];
+      if (passes.empty()) {  // kernel size 1: the target is the source
+        made[i] = tc::copy_batch(src, tc::OutAlloc{allocator, s});
+        continue;
       }
-    } catch (...) {
-      tc::free_batch(owned);
-      throw;
+      const tc_grid_batch* cur = src;
+      tc_grid_batch* owned = nullptr;  // intermediate result of the previous pass
+      try {
+        for (size_t p = 0; p < passes.size(); ++p) {
+          const bool last = p + 1 == passes.size();
+          tc_grid_batch* next =
+              tc::build_pass(cur, passes[p], tc::OutAlloc{allocator, s, !last}, nullptr, last && n_ops > 1);
+          tc::free_batch(owned);
+          owned = next;
+          cur = next;
+        }
+      } catch (...) {
+        tc::free_batch(owned);
+        throw;
+      }
+      made[i] = owned;
     }
-    *out = tc::finish_batch(owned, s);
+    for (int32_t i = 0; i < n_ops; ++i) tc::resolve_counts(made[i]);
+    for (int32_t i = 0; i < n_ops; ++i) {
+      tc::queue_voxel_total(made[i], s);  // no-op where the headers gave the total
+      out[i] = made[i];
+    }
     return TC_OK;
   });
+  if (st != TC_OK) {
+    for (int32_t i = 0; i < n_ops; ++i) {
+      tc::free_batch(made[i]);
+      out[i] = nullptr;
+    }
+  }
+  return st;
 }
 
 tc_status tc_build_masked_refine(const tc_grid_batch* src, const uint8_t* d_keep, int64_t n_keep, int32_t factor,

@@ -212,6 +212,13 @@ struct VoxTicket {
 VoxTicket vox_slot_take(int device);
 void vox_slot_give(int slot);
 
+// Pinned host blocks and events for batches whose headers are still being read
+// back (pooled; a block's size is the power of two >= bytes, at least 4 KiB).
+void* pinned_block_take(size_t bytes, size_t* cap);
+void pinned_block_give(void* p, size_t cap);
+hipEvent_t pending_event_take(int device);
+void pending_event_give(int device, hipEvent_t e);
+
 // Stream-ordered device allocation from the device's default pool (release
 // threshold raised once per device so that memory is cached across calls).
 void* device_alloc_async(size_t bytes, hipStream_t s);
@@ -388,6 +395,14 @@ struct tc_grid_batch {
   mutable int vox_slot = -1;
   mutable int64_t* vox_h = nullptr;
   mutable hipEvent_t vox_ev = nullptr;
+  // a small batch built with its headers still on their way (a pass of
+  // tc_build_batched_topology_many): its last workgroup writes every header and
+  // the status word into hdr_host, and hdr_ev follows that kernel; the counts
+  // are set by resolve_counts
+  mutable bool hdr_pending = false;
+  mutable void* hdr_host = nullptr;
+  mutable size_t hdr_host_cap = 0;
+  mutable hipEvent_t hdr_ev = nullptr;
 
   tc::GridView view() const {
     return tc::make_view(buffer, layout, B, n2, n1, nl);
@@ -426,8 +441,13 @@ tc_grid_batch* build_from_points(const float* d_xyz, const int64_t* h_offsets, i
                                  const float* h_origin, int mode, const OutAlloc& oa);
 // One batched pass. leaf_mask_override (device, one 512-bit mask per source leaf)
 // replaces the source leaf masks, e.g. masked copies for masked refine.
+// Waits for a pending batch's headers (hdr_pending) and sets its counts from
+// them; throws on a flagged pass (the batch stays to be freed by its owner).
+void resolve_counts(const tc_grid_batch* b);
+// With `defer`, a small batch's pass returns with its headers pending (see
+// tc_grid_batch::hdr_pending); the caller resolves them (resolve_counts).
 tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa,
-                          const u64* leaf_mask_override = nullptr);
+                          const u64* leaf_mask_override = nullptr, bool defer = false);
 // Masked copies of src's leaf masks from per-voxel keep flags (enumeration order);
 // a flag index outside [0, n_keep) sets the internal-error bit in *flags.
 void mask_leaves(const tc_grid_batch* src, const uint8_t* keep, i64 n_keep, u64* out_mask, int32_t* flags,

@@ -1931,7 +1931,32 @@ static void check_pass_flags(int32_t f) {
   if (f & kFlagInternal) throw Error(TC_ERR_INTERNAL, "pass: device consistency check failed");
 }
 
-tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, const u64* leaf_mask_override) {
+void resolve_counts(const tc_grid_batch* cb) {
+  if (!cb->hdr_pending) return;
+  tc_grid_batch* b = const_cast<tc_grid_batch*>(cb);
+  auto release = [&]() {
+    pinned_block_give(b->hdr_host, b->hdr_host_cap);
+    pending_event_give(b->device, b->hdr_ev);
+    b->hdr_host = nullptr;
+    b->hdr_host_cap = 0;
+    b->hdr_ev = nullptr;
+    b->hdr_pending = false;
+  };
+  try {
+    hip_check(hipEventSynchronize(b->hdr_ev), "hipEventSynchronize");
+    const char* h = static_cast<const char*>(b->hdr_host);
+    check_pass_flags(*reinterpret_cast<const int32_t*>(h + sizeof(tc_grid_header) * (size_t)b->B));
+    set_counts_from_headers(b, reinterpret_cast<const tc_grid_header*>(h));
+  } catch (...) {
+    release();
+    throw;
+  }
+  release();
+}
+
+tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, const u64* leaf_mask_override,
+                          bool defer) {
+  resolve_counts(src);  // a source whose headers are still on their way
   const OpInfo oi = op_info(op);
   hipStream_t s = oa.stream;
   const int32_t B = src->B;
@@ -2166,13 +2191,24 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, 
     // counts: the finalize copies it into the batch's status word
     apply_debug_inject(ts.flags, s);
     // small batches: the finalize's last workgroup copies every header and the
-    // status word into pinned host memory (the pass's one readback)
+    // status word into pinned host memory (the pass's one readback); a deferred
+    // pass keeps that memory with the batch and leaves the wait to resolve_counts
     const size_t hb = sizeof(tc_grid_header) * (size_t)B + 16;
-    char* h = bounded ? static_cast<char*>(pinned_staging(hb)) : nullptr;
+    char* h = nullptr;
+    if (bounded && defer) {
+      out->hdr_host = pinned_block_take(hb, &out->hdr_host_cap);
+      h = static_cast<char*>(out->hdr_host);
+    } else if (bounded) {
+      h = static_cast<char*>(pinned_staging(hb));
+    }
     tree_finalize_leaves(ov, post.at<uint32_t>(o_box), leaf_inrun, vox_part, gran, post.at<i64>(o_gvb),
                          post.at<int32_t>(o_bb), (const int32_t*)ts.grid_info, ts.flags, d_L, s,
                          bounded ? ts.readback + 4 + 3 * B : nullptr, reinterpret_cast<int32_t*>(h));
-    if (bounded) {
+    if (bounded && defer) {
+      out->hdr_ev = pending_event_take(out->device);
+      hip_check(hipEventRecord(out->hdr_ev, s), "hipEventRecord");
+      out->hdr_pending = true;
+    } else if (bounded) {
       hip_check(hipStreamSynchronize(s), "hipStreamSynchronize");
       check_pass_flags(*reinterpret_cast<const int32_t*>(h + sizeof(tc_grid_header) * (size_t)B));
       set_counts_from_headers(out, reinterpret_cast<const tc_grid_header*>(h));

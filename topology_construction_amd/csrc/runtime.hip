@@ -384,6 +384,78 @@ VoxPool& vox_pool() {
 }
 }  // namespace
 
+// ------------------------------------------------------------------ pending headers
+// Pinned host blocks (power-of-two sizes, from 4 KiB) and timing-free events
+// per device, kept between uses: a batch whose headers are still on their way
+// holds one of each until its counts are resolved.
+namespace {
+struct PendingPool {
+  std::mutex mu;
+  std::vector<std::pair<void*, size_t>> blocks;
+  std::vector<std::pair<int, hipEvent_t>> events;
+};
+PendingPool& pending_pool() {
+  static PendingPool* p = new PendingPool();  // never destroyed: batches may outlive static teardown
+  return *p;
+}
+}  // namespace
+
+void* pinned_block_take(size_t bytes, size_t* cap) {
+  size_t want = 4096;
+  while (want < bytes) want <<= 1;
+  PendingPool& pp = pending_pool();
+  {
+    std::lock_guard<std::mutex> lk(pp.mu);
+    for (size_t k = 0; k < pp.blocks.size(); ++k) {
+      if (pp.blocks[k].second == want) {
+        void* p = pp.blocks[k].first;
+        pp.blocks.erase(pp.blocks.begin() + (long)k);
+        *cap = want;
+        return p;
+      }
+    }
+  }
+  void* p = nullptr;
+  hip_check(hipHostMalloc(&p, want, hipHostMallocDefault), "hipHostMalloc");
+  *cap = want;
+  return p;
+}
+
+void pinned_block_give(void* p, size_t cap) {
+  if (!p) return;
+  PendingPool& pp = pending_pool();
+  std::lock_guard<std::mutex> lk(pp.mu);
+  if (pp.blocks.size() < 64) {
+    pp.blocks.emplace_back(p, cap);
+    return;
+  }
+  (void)hipHostFree(p);
+}
+
+hipEvent_t pending_event_take(int device) {
+  PendingPool& pp = pending_pool();
+  {
+    std::lock_guard<std::mutex> lk(pp.mu);
+    for (size_t k = 0; k < pp.events.size(); ++k) {
+      if (pp.events[k].first == device) {
+        hipEvent_t e = pp.events[k].second;
+        pp.events.erase(pp.events.begin() + (long)k);
+        return e;
+      }
+    }
+  }
+  hipEvent_t e = nullptr;
+  hip_check(hipEventCreateWithFlags(&e, hipEventDisableTiming), "hipEventCreateWithFlags");
+  return e;
+}
+
+void pending_event_give(int device, hipEvent_t e) {
+  if (!e) return;
+  PendingPool& pp = pending_pool();
+  std::lock_guard<std::mutex> lk(pp.mu);
+  pp.events.emplace_back(device, e);
+}
+
 VoxTicket vox_slot_take(int device) {
   VoxPool& p = vox_pool();
   VoxTicket t{-1, nullptr, nullptr};

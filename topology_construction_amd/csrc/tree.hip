@@ -756,13 +756,13 @@ __device__ __forceinline__ void finalize_small_body(const int4* leaf_origin, con
 // workgroup publishes its writes (device fence) before it counts itself in
 // done_ctr (zeroed before the launch); the last one takes the others' with a
 // device fence and reads the words with device-scope loads.
-__device__ __forceinline__ void mirror_headers_last(const tc_grid_header* hdr, int32_t B, int32_t* done_ctr,
-                                                    int32_t* host_words) {
+__device__ __forceinline__ void mirror_headers_last(const tc_grid_header* hdr, int32_t B, int32_t nwork,
+                                                    int32_t* done_ctr, int32_t* host_words) {
   __shared__ int32_t s_last;
   __syncthreads();
   if (threadIdx.x == 0) {
     __threadfence();
-    s_last = atomicAdd(done_ctr, 1) == (int32_t)gridDim.x - 1 ? 1 : 0;
+    s_last = atomicAdd(done_ctr, 1) == nwork - 1 ? 1 : 0;
   }
   __syncthreads();
   if (!s_last) return;
@@ -782,7 +782,14 @@ __global__ void __launch_bounds__(kFinThreads) k_finalize_small(const int4* leaf
                                                                 int32_t* host_words) {
   finalize_small_body(leaf_origin, leaf_inrun, leaf_box, vox_part, gs, grid_info, leaf_offset, B, d_L, L_cap, hdr,
                       flags, status);
-  if (host_words) mirror_headers_last(hdr, B, done_ctr, host_words);
+  if (!host_words) return;
+  // the workgroups that held leaves (block 0 always works; the launch may be
+  // sized by a capacity, and the others left at once without writing)
+  int32_t L = *d_L;
+  L = L < 0 ? 0 : (L > L_cap ? L_cap : L);
+  const int32_t nwork = L > 0 ? (L + kFinSlice - 1) / kFinSlice : 1;
+  if ((int32_t)blockIdx.x >= nwork) return;
+  mirror_headers_last(hdr, B, nwork, done_ctr, host_words);
 }
 
 // Large batches: the leaf producer left one voxel sum per run of `gran` leaves

@@ -344,12 +344,11 @@ int32_t bbox_replicas(int32_t B);  // replicas of the per-grid bbox accumulators
 // d_L (device) holds the leaf count; out.n_leaf is that count, or a capacity
 // above it when the batch's arrays were laid out by capacities (small path only).
 // With host_words (pinned host memory of at least B headers + 16 bytes) the
-// one-launch finalize also copies every header and the status word there, its
-// last workgroup after all the others (done_ctr: a device word zeroed before).
+// one-launch finalize's workgroup 0 also writes there every header's counts and
+// begins (not its box) and, after the headers, the status word.
 void tree_finalize_leaves(const GridView& out, const uint32_t* leaf_box, const int32_t* leaf_inrun, i64* vox_part,
                           i64 gran, i64* gvb, int32_t* bbox_accum, const int32_t* grid_info, int32_t* flags,
-                          const int32_t* d_L, hipStream_t s, int32_t* done_ctr = nullptr,
-                          int32_t* host_words = nullptr);
+                          const int32_t* d_L, hipStream_t s, int32_t* host_words = nullptr);
 // Whether the one-launch finalize takes L leaves (or a capacity of L) of B grids.
 bool finalize_small_fits(i64 L, int32_t B, i64 gran);
 void tree_enumerate(const GridView& v, int32_t* ijk, hipStream_t s);
@@ -396,8 +395,8 @@ struct tc_grid_batch {
   mutable int64_t* vox_h = nullptr;
   mutable hipEvent_t vox_ev = nullptr;
   // a small batch built with its headers still on their way (a pass of
-  // tc_build_batched_topology_many): its last workgroup writes every header and
-  // the status word into hdr_host, and hdr_ev follows that kernel; the counts
+  // tc_build_batched_topology_many): its finalize writes every header's counts
+  // and the status word into hdr_host, and hdr_ev follows that kernel; the counts
   // are set by resolve_counts
   mutable bool hdr_pending = false;
   mutable void* hdr_host = nullptr;

@@ -357,14 +357,18 @@ __global__ void __launch_bounds__(256) k_box_reach(const int32_t* upper_first, i
 // source upper, compacts the reachable in-range candidates, brings their
 // (grid, tile) keys into canonical order without duplicates (a rank sort for
 // at most 64 keys; above that an LDS bitmap over the batch's key space when it
-// is small, else a rank sort or an LDS bitonic network, then head flags and a
-// scan), scatters the unique tiles and every candidate's tile index, writes the
+// is small, else a rank sort up to 1024 keys or an LDS bitonic network, then
+// head flags and a scan), scatters the unique tiles and every candidate's tile index, writes the
 // per-grid tile ranges and, when asked (few tiles), zeroes the unique tiles'
 // lower bitmaps; more tiles get a wide fill.
 constexpr int kTilesMax = 4096;
 constexpr int kTilesThreads = 1024;
 constexpr int kTilesItems = kTilesMax / kTilesThreads;
-constexpr int kRankMax = 256;  // keys sorted by rank counting; more go through a bitonic network
+// keys sorted by rank counting (every thread scans up to kRankMax keys with
+// wave-uniform LDS reads, about 1 us per 200 keys); more go through a bitonic
+// network, whose ~50 dependent exchange stages cost more below 1024 keys
+constexpr int kRankMax = 1024;
+static_assert(kRankMax == kTilesThreads, "the rank counts take one LDS slot per thread");
 constexpr i64 kTileBits = 65536;  // mixed-radix (grid, tile) key space handled by an LDS bitmap
 
 // LDS of the tile stage, carved from one block so that the fused node stage
@@ -666,84 +670,35 @@ __device__ __forceinline__ void tiles_small_body(const int4* upper_origin, const
     }
     return;
   }
-  if (K > kRankMax) {  // LDS bitonic sort
+  if (K > kRankMax) {  // LDS bitonic sort (K > kTilesThreads: several keys per thread)
     int P = 2;
     while (P < K) P <<= 1;
-    if (K <= kTilesThreads) {
-      // one key per thread: stages whose partner is in the same wave exchange with
-      // shuffles, only the wider ones go through LDS
-      __syncthreads();
-      u64 hi = tid < K ? s_hi[tid] : ~0ull, lo = tid < K ? s_lo[tid] : ~0ull;  // padding sorts last
-      uint32_t v = tid < K ? s_v[tid] : 0xffffffffu;
-      const bool act = tid < P;  // whole waves: P is a power of two >= 128
-      for (int k = 2; k <= P; k <<= 1) {
-        for (int jj = k >> 1; jj > 0; jj >>= 1) {
-          u64 oh = 0, ol = 0;
-          uint32_t ov = 0;
-          if (jj >= kWave) {  // uniform
-            __syncthreads();
-            if (act) {
-              s_hi[tid] = hi;
-              s_lo[tid] = lo;
-              s_v[tid] = v;
+    for (int i = K + tid; i < P; i += kTilesThreads) {  // padding sorts last
+      s_hi[i] = ~0ull;
+      s_lo[i] = ~0ull;
+      s_v[i] = 0xffffffffu;
+    }
+    __syncthreads();
+    for (int k = 2; k <= P; k <<= 1) {
+      for (int jj = k >> 1; jj > 0; jj >>= 1) {
+        for (int i = tid; i < P; i += kTilesThreads) {
+          const int ixj = i ^ jj;
+          if (ixj > i) {
+            const bool up = (i & k) == 0;
+            const u64 ah = s_hi[i], al = s_lo[i], bh = s_hi[ixj], bl = s_lo[ixj];
+            const uint32_t av = s_v[i], bv = s_v[ixj];
+            const bool gt = ah != bh ? ah > bh : (al != bl ? al > bl : av > bv);
+            if (gt == up) {
+              s_hi[i] = bh;
+              s_lo[i] = bl;
+              s_v[i] = bv;
+              s_hi[ixj] = ah;
+              s_lo[ixj] = al;
+              s_v[ixj] = av;
             }
-            __syncthreads();
-            if (act) {
-              oh = s_hi[tid ^ jj];
-              ol = s_lo[tid ^ jj];
-              ov = s_v[tid ^ jj];
-            }
-          } else if (act) {
-            oh = __shfl_xor(hi, jj, kWave);
-            ol = __shfl_xor(lo, jj, kWave);
-            ov = (uint32_t)__shfl_xor((int)v, jj, kWave);
-          }
-          if (!act) continue;
-          const bool gt = hi != oh ? hi > oh : (lo != ol ? lo > ol : v > ov);
-          const bool lt = hi != oh ? hi < oh : (lo != ol ? lo < ol : v < ov);
-          const bool up = (tid & k) == 0, lower = (tid & jj) == 0;
-          if (up ? (lower ? gt : lt) : (lower ? lt : gt)) {
-            hi = oh;
-            lo = ol;
-            v = ov;
           }
         }
-      }
-      __syncthreads();
-      if (act) {
-        s_hi[tid] = hi;
-        s_lo[tid] = lo;
-        s_v[tid] = v;
-      }
-      __syncthreads();
-    } else {
-      for (int i = K + tid; i < P; i += kTilesThreads) {  // padding sorts last
-        s_hi[i] = ~0ull;
-        s_lo[i] = ~0ull;
-        s_v[i] = 0xffffffffu;
-      }
-      __syncthreads();
-      for (int k = 2; k <= P; k <<= 1) {
-        for (int jj = k >> 1; jj > 0; jj >>= 1) {
-          for (int i = tid; i < P; i += kTilesThreads) {
-            const int ixj = i ^ jj;
-            if (ixj > i) {
-              const bool up = (i & k) == 0;
-              const u64 ah = s_hi[i], al = s_lo[i], bh = s_hi[ixj], bl = s_lo[ixj];
-              const uint32_t av = s_v[i], bv = s_v[ixj];
-              const bool gt = ah != bh ? ah > bh : (al != bl ? al > bl : av > bv);
-              if (gt == up) {
-                s_hi[i] = bh;
-                s_lo[i] = bl;
-                s_v[i] = bv;
-                s_hi[ixj] = ah;
-                s_lo[ixj] = al;
-                s_v[ixj] = av;
-              }
-            }
-          }
-          __syncthreads();
-        }
+        __syncthreads();
       }
     }
   }
@@ -1130,10 +1085,8 @@ __global__ void __launch_bounds__(kTilesThreads) k_nodes_small(
     int32_t* grid_tile_begin, const uint32_t* upper_reach, int32_t* readback, const int32_t* src_status,
     const int4* lower_origin, const u64* lower_mask, i64 n, int op, int m, int m_src, int32_t* tile_of_cand,
     int32_t* d_num_tiles, u64* tile_child, uint16_t* tile_prefix, int32_t* tile_lower_base, int32_t* d_num_cands,
-    u64* cand_child, int32_t* lower_nbr, int4* cand_origin, int32_t* cand_src, const uint32_t* lower_reach,
-    int32_t* zero_word) {
+    u64* cand_child, int32_t* lower_nbr, int4* cand_origin, int32_t* cand_src, const uint32_t* lower_reach) {
   __shared__ __align__(16) char lds[kNodesLds];
-  if (threadIdx.x == 0) *zero_word = 0;
   tiles_small_body(upper_origin, upper_mask, n_upper, op, m, B, utile, tile_of_cand, d_num_tiles, grid_tile_begin,
                    tile_child, 0, upper_reach, readback, src_status, lds);
   __syncthreads();
@@ -1970,7 +1923,9 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, 
   const bool small_tiles = nT > 0 && nT <= kTilesMax;
   const bool small_lowers = small_tiles && nT <= kLowersSmallTiles && nL > 0 && nL <= kLowersSmallMax &&
                             (op == TC_OP_COARSEN || nL / oi.m <= kReachMax);
-  // Small batches lay the output out by capacities known before any launch (a
+  // Small batches (a tile stage in one workgroup; the lower stage in one
+  // workgroup too, or in its multi-launch form) lay the output out by
+  // capacities known before any launch (a
   // source leaf feeds at most 8 / 1 / 27 / 8 output leaves for refine, coarsen,
   // dilate, pads; the tile and lower candidates bound the nodes), so the output
   // is allocated while the node, marking and count stages run (they do not touch
@@ -1979,8 +1934,8 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, 
   const i64 per_leaf = op == TC_OP_REFINE ? 8 : (op == TC_OP_COARSEN ? 1 : oi.m);
   const i64 gran = op == TC_OP_REFINE ? 256 : 64;  // leaves per gather workgroup (voxel-sum runs)
   const i64 L_cap = (i64)src->nl * per_leaf;
-  const bool bounded = small_lowers && L_cap > 0 && L_cap <= 0x7fffffffLL && finalize_small_fits(L_cap, B, gran) &&
-                       make_layout(B, nT, nL, L_cap).total <= kBoundedBytes;
+  const bool bounded = small_tiles && nL > 0 && L_cap > 0 && L_cap <= 0x7fffffffLL &&
+                       finalize_small_fits(L_cap, B, gran) && make_layout(B, nT, nL, L_cap).total <= kBoundedBytes;
   tc_grid_batch* out = nullptr;
   try {
     Arena a(s);
@@ -2008,7 +1963,7 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, 
     const size_t o_nbr = a.reserve(4 * nL);
     const size_t o_csrc = a.reserve(4 * nL * oi.m_src);
     const size_t o_ginfo = a.reserve(4 * 6 * (i64)B);
-    const size_t o_rb = a.reserve(4 * (5 + 3 * (i64)B));  // readback words, then the finalize's done counter
+    const size_t o_rb = a.reserve(4 * (4 + 3 * (i64)B));  // readback words
     const size_t o_ureach = a.reserve(4 * (i64)src->n2);
     const size_t o_lreach = a.reserve(4 * (i64)src->n1);
     const size_t o_stmp = a.reserve(std::max(scan_tmp_bytes(nT, 4), scan_tmp_bytes(nL, 8)));
@@ -2069,7 +2024,7 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, 
                (const uint32_t*)ureach, ts.readback, (const int32_t*)sv.status, (const int4*)sv.lower_origin,
                (const u64*)sv.lower_mask, nL, op, oi.m, oi.m_src, tile_of_cand, ts.d_num_tiles, ts.tile_child,
                ts.tile_prefix, ts.tile_lower_base, ts.d_num_cands, ts.cand_child, lower_nbr, ts.cand_origin, cand_src,
-               (const uint32_t*)box_lreach, ts.readback + 4 + 3 * B);
+               (const uint32_t*)box_lreach);
       } else {
         launch("k_tiles_small", k_tiles_small, 1, kTilesThreads, s, (const int4*)sv.upper_origin,
                (const u64*)sv.upper_mask, (int32_t)src->n2, op, oi.m, B, ts.utile, tile_of_cand, ts.d_num_tiles,
@@ -2190,8 +2145,8 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, 
     // the gathers' consistency checks set bits in the flag word after the
     // counts: the finalize copies it into the batch's status word
     apply_debug_inject(ts.flags, s);
-    // small batches: the finalize's last workgroup copies every header and the
-    // status word into pinned host memory (the pass's one readback); a deferred
+    // small batches: the finalize's workgroup 0 writes every header's counts and
+    // the status word into pinned host memory (the pass's one readback); a deferred
     // pass keeps that memory with the batch and leaves the wait to resolve_counts
     const size_t hb = sizeof(tc_grid_header) * (size_t)B + 16;
     char* h = nullptr;
@@ -2203,7 +2158,7 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, 
     }
     tree_finalize_leaves(ov, post.at<uint32_t>(o_box), leaf_inrun, vox_part, gran, post.at<i64>(o_gvb),
                          post.at<int32_t>(o_bb), (const int32_t*)ts.grid_info, ts.flags, d_L, s,
-                         bounded ? ts.readback + 4 + 3 * B : nullptr, reinterpret_cast<int32_t*>(h));
+                         reinterpret_cast<int32_t*>(h));
     if (bounded && defer) {
       out->hdr_ev = pending_event_take(out->device);
       hip_check(hipEventRecord(out->hdr_ev, s), "hipEventRecord");

@@ -586,18 +586,14 @@ __device__ __forceinline__ void finalize_small_body(const int4* leaf_origin, con
                                                     const uint32_t* leaf_box, const i64* vox_part, int32_t gs,
                                                     const int32_t* grid_info, i64* leaf_offset, int32_t B,
                                                     const int32_t* d_L, int32_t L_cap, tc_grid_header* hdr,
-                                                    int32_t* flags, int32_t* status) {
+                                                    int32_t* flags, int32_t* status, int32_t* host_words) {
   constexpr int kR = kFinRuns / kFinThreads;
   constexpr int kG = kFinSmallGrids / kFinThreads;
   // the leaf count from the device (the launch may be sized by a capacity):
-  // workgroups past the leaves leave at once, block 0 always writes the headers
+  // workgroups past the leaves leave once it is in, block 0 always writes the
+  // headers. The loads below are clamped to the capacity, so none waits for it.
   int32_t L = *d_L;
-  if (L > L_cap || L < 0) {
-    if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(flags, 2);
-    L = L < 0 ? 0 : L_cap;
-  }
-  if (blockIdx.x != 0 && (int32_t)blockIdx.x * kFinSlice >= L) return;  // uniform per block
-  const int32_t np = (L + (1 << gs) - 1) >> gs;  // runs of 2^gs leaves
+  const int32_t np_cap = (L_cap + (1 << gs) - 1) >> gs;  // runs of 2^gs leaves, by the capacity (>= 1)
   __shared__ int32_t s_part[kFinRuns];           // exclusive voxel offset of every run
   __shared__ int32_t s_gvb[kFinSmallGrids + 1];  // voxel begin of every grid, then the total
   __shared__ int32_t s_wave[kFinThreads / kWave];
@@ -616,29 +612,38 @@ __device__ __forceinline__ void finalize_small_body(const int4* leaf_origin, con
       for (int f = 0; f < 6; ++f) hv[k][f] = grid_info[gg * 6 + f];
     }
   }
-  int32_t total = 0;
-  if (L > 0) {  // uniform; np >= 1
-    i64 pv[kR];
-    int32_t gf[kG];
-    int4 o[kFinPer];
-    uint32_t bx[kFinPer];
-    int32_t inr[kFinPer];
+  const bool live = L_cap > 0;  // uniform; the launch holds ceil(L_cap / kFinSlice) workgroups, or one
+  i64 pv[kR];
+  int32_t gf[kG];
+  int4 o[kFinPer];
+  uint32_t bx[kFinPer];
+  int32_t inr[kFinPer];
+  if (live) {
 #pragma unroll
-    for (int k = 0; k < kR; ++k) pv[k] = vox_part[min(tid * kR + k, np - 1)];
+    for (int k = 0; k < kR; ++k) pv[k] = vox_part[min(tid * kR + k, np_cap - 1)];
 #pragma unroll
     for (int k = 0; k < kG; ++k) gf[k] = grid_info[(i64)min(tid * kG + k, B - 1) * 6 + 5];
 #pragma unroll
     for (int k = 0; k < kFinPer; ++k) {
-      const int32_t i = min(base + k * kWave + lane, L - 1);
+      const int32_t i = min(base + k * kWave + lane, L_cap - 1);
       o[k] = leaf_origin[i];
       bx[k] = leaf_box[i];
       inr[k] = leaf_inrun[i];
     }
+  }
+  if (L > L_cap || L < 0) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(flags, 2);
+    L = L < 0 ? 0 : L_cap;
+  }
+  if (blockIdx.x != 0 && (int32_t)blockIdx.x * kFinSlice >= L) return;  // uniform per block
+  const int32_t np = (L + (1 << gs) - 1) >> gs;  // runs of 2^gs leaves
+  int32_t total = 0;
+  if (L > 0) {  // uniform; np >= 1
     // first leaves' in-run counts (a grid without leaves points at the next
     // grid's first leaf, or at L): issued once gf is in, ahead of the scan
     int32_t fi[kG];
 #pragma unroll
-    for (int k = 0; k < kG; ++k) fi[k] = leaf_inrun[min(gf[k], L - 1)];
+    for (int k = 0; k < kG; ++k) fi[k] = leaf_inrun[min(gf[k], L_cap - 1)];
     // run offsets
     int32_t rv[kR];
     int32_t sum = 0;
@@ -748,29 +753,24 @@ __device__ __forceinline__ void finalize_small_body(const int4* leaf_origin, con
     h->reserved[0] = 0;
     h->reserved[1] = 0;
   }
-}
-
-// With a host mirror (pinned host memory the device can write), the last
-// workgroup to finish copies every header and the status word there, so that
-// the host reads them after the stream's completion with no copy command. Each
-// workgroup publishes its writes (device fence) before it counts itself in
-// done_ctr (zeroed before the launch); the last one takes the others' with a
-// device fence and reads the words with device-scope loads.
-__device__ __forceinline__ void mirror_headers_last(const tc_grid_header* hdr, int32_t B, int32_t nwork,
-                                                    int32_t* done_ctr, int32_t* host_words) {
-  __shared__ int32_t s_last;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    __threadfence();
-    s_last = atomicAdd(done_ctr, 1) == nwork - 1 ? 1 : 0;
+  if (!host_words) return;
+  // the host mirror: every header's node and voxel counts and begins (its box,
+  // folded by every workgroup, is left out) and the status word after them
+  tc_grid_header* hh = reinterpret_cast<tc_grid_header*>(host_words);
+#pragma unroll
+  for (int k = 0; k < kG; ++k) {
+    const int gg = tid + k * kFinThreads;
+    if (gg >= B) break;
+    int32_t* w = reinterpret_cast<int32_t*>(hh + gg);
+    w[0] = gg;
+    w[1] = B;
+#pragma unroll
+    for (int f = 0; f < 6; ++f) w[2 + f] = hv[k][f];
+    int64_t* v = reinterpret_cast<int64_t*>(&hh[gg].voxel_count);
+    v[0] = s_gvb[gg + 1] - s_gvb[gg];
+    v[1] = s_gvb[gg];
   }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  const int32_t* words = reinterpret_cast<const int32_t*>(hdr);  // the status word follows the headers
-  const int32_t n = (int32_t)((sizeof(tc_grid_header) * (size_t)B + 16) / 4);
-  for (int32_t k = threadIdx.x; k < n; k += blockDim.x)
-    host_words[k] = __hip_atomic_load(&words[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid < 4) host_words[(sizeof(tc_grid_header) * (size_t)B) / 4 + tid] = tid == 0 ? *flags : 0;
 }
 
 __global__ void __launch_bounds__(kFinThreads) k_finalize_small(const int4* leaf_origin, const int32_t* leaf_inrun,
@@ -778,18 +778,10 @@ __global__ void __launch_bounds__(kFinThreads) k_finalize_small(const int4* leaf
                                                                 int32_t gs, const int32_t* grid_info,
                                                                 i64* leaf_offset, int32_t B, const int32_t* d_L,
                                                                 int32_t L_cap, tc_grid_header* hdr,
-                                                                int32_t* flags, int32_t* status, int32_t* done_ctr,
+                                                                int32_t* flags, int32_t* status,
                                                                 int32_t* host_words) {
   finalize_small_body(leaf_origin, leaf_inrun, leaf_box, vox_part, gs, grid_info, leaf_offset, B, d_L, L_cap, hdr,
-                      flags, status);
-  if (!host_words) return;
-  // the workgroups that held leaves (block 0 always works; the launch may be
-  // sized by a capacity, and the others left at once without writing)
-  int32_t L = *d_L;
-  L = L < 0 ? 0 : (L > L_cap ? L_cap : L);
-  const int32_t nwork = L > 0 ? (L + kFinSlice - 1) / kFinSlice : 1;
-  if ((int32_t)blockIdx.x >= nwork) return;
-  mirror_headers_last(hdr, B, nwork, done_ctr, host_words);
+                      flags, status, host_words);
 }
 
 // Large batches: the leaf producer left one voxel sum per run of `gran` leaves
@@ -932,7 +924,7 @@ bool finalize_small_fits(i64 L, int32_t B, i64 gran) {
 
 void tree_finalize_leaves(const GridView& out, const uint32_t* leaf_box, const int32_t* leaf_inrun, i64* vox_part,
                           i64 gran, i64* gvb, int32_t* bbox_accum, const int32_t* grid_info, int32_t* flags,
-                          const int32_t* d_L, hipStream_t s, int32_t* done_ctr, int32_t* host_words) {
+                          const int32_t* d_L, hipStream_t s, int32_t* host_words) {
   if (host_words && !finalize_small_fits(out.n_leaf, out.B, gran))
     throw Error(TC_ERR_INTERNAL, "finalize: a host mirror needs the one-launch finalize");
   const i64 L = out.n_leaf;  // the leaf count, or (d_L given) a capacity with the count at d_L
@@ -942,7 +934,7 @@ void tree_finalize_leaves(const GridView& out, const uint32_t* leaf_box, const i
     launch("k_finalize_small", k_finalize_small, std::max<i64>(1, ceil_div(L, kFinSlice)), kFinThreads, s,
            (const int4*)out.leaf_origin, leaf_inrun, leaf_box, (const i64*)vox_part,
            (int32_t)__builtin_ctzll((u64)gran), grid_info, out.leaf_offset, B, d_L, (int32_t)L, out.headers,
-           flags, out.status, done_ctr, host_words);
+           flags, out.status, host_words);
     return;
   }
   // the wide path runs on exact counts only (its launches are sized by them)

@@ -233,12 +233,29 @@ class GridBatch:
         self.upper_count = info.upper_count
         self.lower_count = info.lower_count
         self.leaf_count = info.leaf_count
-        B = info.grid_count
-        self.upper_counts = np.ctypeslib.as_array(info.h_upper_counts, (B,)).copy()
-        self.lower_counts = np.ctypeslib.as_array(info.h_lower_counts, (B,)).copy()
-        self.leaf_counts = np.ctypeslib.as_array(info.h_leaf_counts, (B,)).copy()
         self._info = info
+        self._counts = None  # per-grid host counts, copied on first use
+        self._total = None  # voxel total, once read
         self._buffer = _live_buffers.get(int(info.d_buffer or 0)) if torch_owned else None
+
+    def _grid_counts(self):
+        if self._counts is None:
+            B, info = self.grid_count, self._info
+            self._counts = tuple(np.ctypeslib.as_array(p, (B,)).copy()
+                                 for p in (info.h_upper_counts, info.h_lower_counts, info.h_leaf_counts))
+        return self._counts
+
+    @property
+    def upper_counts(self) -> np.ndarray:
+        return self._grid_counts()[0]
+
+    @property
+    def lower_counts(self) -> np.ndarray:
+        return self._grid_counts()[1]
+
+    @property
+    def leaf_counts(self) -> np.ndarray:
+        return self._grid_counts()[2]
 
     def __del__(self):
         h = getattr(self, "handle", None)
@@ -271,9 +288,11 @@ class GridBatch:
         return out
 
     def voxel_total(self, stream=None) -> int:
-        v = ctypes.c_int64()
-        _check(self._lib.tc_batch_voxel_total(self.handle, ctypes.byref(v), _stream_handle(stream)))
-        return int(v.value)
+        if self._total is None:  # the batch never changes: one read
+            v = ctypes.c_int64()
+            _check(self._lib.tc_batch_voxel_total(self.handle, ctypes.byref(v), _stream_handle(stream)))
+            self._total = int(v.value)
+        return self._total
 
     def ijk(self, stream=None):
         return tc_enumerate_ijk(self, stream=stream)

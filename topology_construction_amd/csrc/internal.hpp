@@ -328,7 +328,11 @@ struct TreeScratch {
 // Launch groups (implemented in tree.hip).
 void tree_tile_ranges(TreeScratch& t, int32_t B, hipStream_t s);
 void tree_grid_counts(TreeScratch& t, int32_t B, hipStream_t s);
-void tree_rank_tiles(TreeScratch& t, hipStream_t s);            // prefix per tile + scan -> cand numbering
+void tree_rank_tiles(TreeScratch& t, hipStream_t s);
+// tree_rank_tiles and the candidate -> source table's fill (nc * m_src entries
+// of cand_src set to -1) in one launch, for at most 4096 tile slots; done_ctr is
+// a device word zeroed before the launch (by the tile stage).
+void tree_rank_tiles_last(TreeScratch& t, int32_t* done_ctr, int32_t* cand_src, int32_t m_src, hipStream_t s);            // prefix per tile + scan -> cand numbering
 void tree_count_cands(TreeScratch& t, hipStream_t s);           // leaf counts per cand + their scan
 void tree_counts(TreeScratch& t, int32_t B, hipStream_t s);     // tree_count_cands + tree_grid_counts (fused when small)
 void tree_write_nodes(TreeScratch& t, const GridView& out, int32_t* leaf_cand, hipStream_t s);

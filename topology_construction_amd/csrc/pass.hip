@@ -756,8 +756,9 @@ __global__ void __launch_bounds__(kTilesThreads) k_tiles_small(const int4* upper
                                                                int32_t* d_num_tiles, int32_t* grid_tile_begin,
                                                                u64* tile_child, int zero_child,
                                                                const uint32_t* upper_reach, int32_t* readback,
-                                                               const int32_t* src_status) {
+                                                               const int32_t* src_status, int32_t* zero_word) {
   __shared__ __align__(16) char lds[kTilesLds];
+  if (zero_word && threadIdx.x == 0) *zero_word = 0;
   tiles_small_body(upper_origin, upper_mask, n_upper, op, m, B, utile, tile_of_cand, d_num_tiles, grid_tile_begin,
                    tile_child, zero_child, upper_reach, readback, src_status, lds);
 }
@@ -1963,7 +1964,7 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, 
     const size_t o_nbr = a.reserve(4 * nL);
     const size_t o_csrc = a.reserve(4 * nL * oi.m_src);
     const size_t o_ginfo = a.reserve(4 * 6 * (i64)B);
-    const size_t o_rb = a.reserve(4 * (4 + 3 * (i64)B));  // readback words
+    const size_t o_rb = a.reserve(4 * (5 + 3 * (i64)B));  // readback words, then the rank stage's counter
     const size_t o_ureach = a.reserve(4 * (i64)src->n2);
     const size_t o_lreach = a.reserve(4 * (i64)src->n1);
     const size_t o_stmp = a.reserve(std::max(scan_tmp_bytes(nT, 4), scan_tmp_bytes(nL, 8)));
@@ -1991,6 +1992,7 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, 
     ts.readback = a.at<int32_t>(o_rb);
     ts.scan_tmp = a.at<char>(o_stmp);
     ts.flags = ts.readback;
+    int32_t* rank_ctr = ts.readback + 4 + 3 * B;
     int32_t* tile_of_cand = a.at<int32_t>(o_toc);
     int32_t* lower_nbr = a.at<int32_t>(o_nbr);
     int32_t* cand_src = a.at<int32_t>(o_csrc);
@@ -1999,9 +2001,8 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, 
     // box ops on small batches: voxel-exact face reach sets of uppers and lowers
     const bool box_op = op != TC_OP_REFINE && op != TC_OP_COARSEN;
     uint32_t* box_lreach = nullptr;
-    if (small_lowers && box_op) {
+    if (box_op && small_tiles && src->n1 <= kBoxReachLowers) {
       box_lreach = a.at<uint32_t>(o_lreach);
-      if (src->n1 > kBoxReachLowers) throw Error(TC_ERR_INTERNAL, "pass: too many lowers for the box reach stage");
       launch("k_box_reach", k_box_reach, src->n2, 256, s, (const int32_t*)sv.upper_first, (int32_t)src->n2,
              (const int32_t*)sv.lower_first, (int32_t)src->n1, (const int4*)sv.leaf_origin,
              (const int32_t*)sv.leaf_parent, (const u64*)sv.leaf_mask, (int32_t)src->nl, op, oi.m,
@@ -2013,7 +2014,7 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, 
       const bool zero_here = !small_lowers && nT <= 256;
       // many source uppers: their reach sets in a wide launch first
       uint32_t* ureach = box_lreach ? a.at<uint32_t>(o_ureach) : nullptr;
-      if (!box_lreach && op != TC_OP_COARSEN && src->n2 > 64) {
+      if (!box_lreach && op != TC_OP_COARSEN && src->n2 > 128) {
         ureach = a.at<uint32_t>(o_ureach);
         launch("k_node_reach", k_node_reach, ceil_div((i64)src->n2, 4), 256, s, (const u64*)sv.upper_mask,
                (i64)src->n2, 512, op, oi.m, ureach);
@@ -2029,7 +2030,7 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, 
         launch("k_tiles_small", k_tiles_small, 1, kTilesThreads, s, (const int4*)sv.upper_origin,
                (const u64*)sv.upper_mask, (int32_t)src->n2, op, oi.m, B, ts.utile, tile_of_cand, ts.d_num_tiles,
                ts.grid_tile_begin, ts.tile_child, zero_here ? 1 : 0, (const uint32_t*)ureach, ts.readback,
-               (const int32_t*)sv.status);
+               (const int32_t*)sv.status, rank_ctr);
         if (!zero_here) fill_u64(ts.tile_child, 0, nT * 512, ts.d_num_tiles, 512, s);
       }
     } else {
@@ -2056,8 +2057,8 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, 
     // lowers. The candidate -> source table starts empty; refine and the box ops
     // store every word of their candidates' leaf masks, coarsen ORs into zeros.
     if (!small_lowers) {
-      uint32_t* lreach = nullptr;
-      if (op != TC_OP_COARSEN) {
+      uint32_t* lreach = box_lreach;
+      if (!lreach && op != TC_OP_COARSEN) {
         lreach = a.at<uint32_t>(o_lreach);
         launch("k_node_reach", k_node_reach, ceil_div((i64)src->n1, 4), 256, s, (const u64*)sv.lower_mask,
                (i64)src->n1, 64, op, oi.m, lreach);
@@ -2065,8 +2066,14 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, 
       launch("k_lower_mark", k_lower_mark, ceil_div(nL, 256), 256, s, (const int4*)sv.lower_origin,
              (const u64*)sv.lower_mask, (const uint32_t*)lreach, nL, op, oi.m, (const int32_t*)tile_of_cand,
              (const int32_t*)ts.d_num_tiles, ts.tile_child, ts.flags);
-      tree_rank_tiles(ts, s);
-      fill_pair(cand_src, -1, nL * oi.m_src, oi.m_src, ts.cand_child, 0, 0, 64, ts.d_num_cands, s);
+      // small batches: one launch, the table filled by its last workgroup (the
+      // tile stage zeroed the counter); larger ones fill the table wide
+      if (bounded) {
+        tree_rank_tiles_last(ts, rank_ctr, cand_src, oi.m_src, s);
+      } else {
+        tree_rank_tiles(ts, s);
+        fill_pair(cand_src, -1, nL * oi.m_src, oi.m_src, ts.cand_child, 0, 0, 64, ts.d_num_cands, s);
+      }
       launch("k_lower_nbr", k_lower_nbr, ceil_div(nL, 256), 256, s, (const int4*)sv.lower_origin,
              (const u64*)sv.lower_mask, (const uint32_t*)lreach, nL, op, oi.m, oi.m_src, (const int32_t*)tile_of_cand,
              (const u64*)ts.tile_child, (const uint16_t*)ts.tile_prefix, (const int32_t*)ts.tile_lower_base,

@@ -49,34 +49,45 @@ __device__ __forceinline__ T tile_scan_striped(const T v[kScanItems], T ex[kScan
   return total;
 }
 
-// Single-workgroup scans (at most one tile, and the partials) hold items blocked:
-// thread t owns items t*kScanItems .. +kScanItems-1, which needs one block scan
-// only; these launches are latency-bound, so fewer steps beat coalescing.
+// Single-workgroup scans (up to kScanSingleTiles tiles) hold items blocked:
+// thread t owns items t*kScanItems .. +kScanItems-1 of the current tile, which
+// needs one block scan per tile; the next tile's loads are issued before the
+// current one is scanned. These launches are latency-bound, so fewer steps (and
+// one launch instead of three) beat coalescing.
+constexpr int kScanSingleTiles = 16;
+
 template <typename T>
 __global__ void __launch_bounds__(kScanThreads) k_scan_single(const T* in, T* out, i64 n_host,
                                                               const int32_t* d_n, T* total_out) {
   __shared__ T s_wave[kScanThreads / kWave];
   const i64 n = clamp_n(n_host, d_n);
+  const i64 tb = (i64)threadIdx.x * kScanItems;
   T v[kScanItems];
-  T sum = 0;
-  const i64 base = (i64)threadIdx.x * kScanItems;
 #pragma unroll
-  for (int k = 0; k < kScanItems; ++k) {
-    const i64 i = base + k;
-    v[k] = i < n ? in[i] : T(0);
-    sum += v[k];
-  }
-  T total;
-  T excl = block_excl_scan<T, kScanThreads>(sum, s_wave, total);
+  for (int k = 0; k < kScanItems; ++k) v[k] = tb + k < n ? in[tb + k] : T(0);
+  T carry = 0;
+  for (i64 c = 0; c < n; c += kScanTile) {  // uniform
+    T nx[kScanItems];
+    const i64 nb = c + kScanTile + tb;
 #pragma unroll
-  for (int k = 0; k < kScanItems; ++k) {
-    const i64 i = base + k;
-    if (i < n) out[i] = excl;
-    excl += v[k];
+    for (int k = 0; k < kScanItems; ++k) nx[k] = nb + k < n ? in[nb + k] : T(0);
+    T sum = 0;
+#pragma unroll
+    for (int k = 0; k < kScanItems; ++k) sum += v[k];
+    T total;
+    T excl = block_excl_scan<T, kScanThreads>(sum, s_wave, total) + carry;
+#pragma unroll
+    for (int k = 0; k < kScanItems; ++k) {
+      const i64 i = c + tb + k;
+      if (i < n) out[i] = excl;
+      excl += v[k];
+      v[k] = nx[k];
+    }
+    carry += total;
   }
   if (threadIdx.x == 0) {
-    out[n] = total;
-    if (total_out) *total_out = total;
+    out[n] = carry;
+    if (total_out) *total_out = carry;
   }
 }
 
@@ -152,7 +163,7 @@ __global__ void __launch_bounds__(kScanThreads) k_scan_down(const T* in, T* out,
 }
 
 size_t scan_tmp_bytes(i64 n_host, size_t elem) {
-  return n_host <= kScanTile ? 0 : elem * (size_t)ceil_div(n_host, kScanTile);
+  return n_host <= (i64)kScanTile * kScanSingleTiles ? 0 : elem * (size_t)ceil_div(n_host, kScanTile);
 }
 
 template <typename T>
@@ -165,7 +176,7 @@ static void scan_excl(const char* tag, const T* in, T* out, i64 n_host, const in
            total_out);
     return;
   }
-  if (n_host <= kScanTile) {
+  if (n_host <= (i64)kScanTile * kScanSingleTiles) {
     launch("k_scan_single", k_scan_single<T>, 1, kScanThreads, s, in, out, n_host, d_n, total_out);
     return;
   }

@@ -61,6 +61,78 @@ __global__ void __launch_bounds__(256) k_tile_rank(const u64* tile_child, uint16
   if (threadIdx.x == 0) tile_lower_count[t] = total;
 }
 
+// At most kRankLastTiles tiles: k_tile_rank, the scan of the tiles' lower counts
+// and the start of the candidate -> source table in one launch. Each tile's
+// workgroup writes its prefix table and count, publishes them (device fence)
+// and counts itself in done_ctr (zeroed by the tile stage); the last one reads
+// every count with device-scope loads, scans them into the tile bases and the
+// candidate count, and sets the table's first nc * m_src entries to -1.
+constexpr int kRankLastTiles = 4096;
+
+__global__ void __launch_bounds__(256) k_tile_rank_last(const u64* tile_child, uint16_t* tile_prefix,
+                                                        int32_t* tile_lower_count, int32_t* tile_lower_base,
+                                                        const int32_t* d_num_tiles, int32_t* d_num_cands,
+                                                        int32_t* done_ctr, int32_t* cand_src, int32_t m_src) {
+  __shared__ int32_t s_wave[4];
+  __shared__ int32_t s_last;
+  const int32_t nt = *d_num_tiles;
+  const i64 t = blockIdx.x;
+  const int tid = threadIdx.x;
+  if (nt <= 0) {  // no tiles: no workgroup counts itself
+    if (t == 0 && tid == 0) {
+      tile_lower_base[0] = 0;
+      *d_num_cands = 0;
+    }
+    return;
+  }
+  if (t >= nt) return;  // uniform per block
+  const int w0 = tid * 2;
+  const u64 a = tile_child[t * 512 + w0];
+  const u64 b = tile_child[t * 512 + w0 + 1];
+  const int ca = popc64(a), cb = popc64(b);
+  int32_t total;
+  const int32_t ex = block_excl_scan<int32_t, 256>(ca + cb, s_wave, total);
+  tile_prefix[t * 512 + w0] = (uint16_t)ex;
+  tile_prefix[t * 512 + w0 + 1] = (uint16_t)(ex + ca);
+  if (tid == 0) {
+    tile_lower_count[t] = total;
+    __threadfence();
+    s_last = atomicAdd(done_ctr, 1) == nt - 1 ? 1 : 0;
+  }
+  __syncthreads();
+  if (!s_last) return;  // uniform per block
+  __threadfence();
+  constexpr int kPer = kRankLastTiles / 256;
+  int32_t v[kPer];
+  int32_t sum = 0;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int i = tid * kPer + k;
+    v[k] = i < nt ? __hip_atomic_load(&tile_lower_count[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+    sum += v[k];
+  }
+  int32_t nc;
+  int32_t base = block_excl_scan<int32_t, 256>(sum, s_wave, nc);
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int i = tid * kPer + k;
+    if (i < nt) tile_lower_base[i] = base;
+    base += v[k];
+  }
+  if (tid == 0) {
+    tile_lower_base[nt] = nc;
+    *d_num_cands = nc;
+  }
+  for (i64 e = tid; e < (i64)nc * m_src; e += 256) cand_src[e] = -1;
+}
+
+void tree_rank_tiles_last(TreeScratch& ts, int32_t* done_ctr, int32_t* cand_src, int32_t m_src, hipStream_t s) {
+  if (ts.cap_tiles > kRankLastTiles) throw Error(TC_ERR_INTERNAL, "rank: too many tiles for the one-launch stage");
+  launch("k_tile_rank", k_tile_rank_last, std::max<i64>(1, ts.cap_tiles), 256, s, (const u64*)ts.tile_child,
+         ts.tile_prefix, ts.tile_lower_count, ts.tile_lower_base, (const int32_t*)ts.d_num_tiles, ts.d_num_cands,
+         done_ctr, cand_src, m_src);
+}
+
 void tree_rank_tiles(TreeScratch& ts, hipStream_t s) {
   launch("k_tile_rank", k_tile_rank, ts.cap_tiles, 256, s, (const u64*)ts.tile_child, ts.tile_prefix,
          ts.tile_lower_count, (const int32_t*)ts.d_num_tiles);
@@ -242,7 +314,7 @@ __global__ void __launch_bounds__(kTailThreads) k_counts_tail(const int32_t* gri
 // in one workgroup. Every global load (the counts, the candidate masks up to
 // the host-known capacity cap_c, the tile bases, the grid ranges) is issued
 // before the first wait.
-constexpr int kCountsSmallMax = 2048;  // beyond this the multi-launch path is faster
+constexpr int kCountsSmallMax = 4096;
 
 __global__ void __launch_bounds__(kTailThreads) k_counts_small(const u64* cand_child, int32_t cap_c,
                                                                uint16_t* cand_prefix, i64* cand_counts,

@@ -181,6 +181,11 @@ def cpu_baseline(np, ijk, off, large_input=None, min_s=10.0):
     return res
 
 
+def progress(msg):
+    """A progress line on stderr (the JSON result is the only stdout line)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def run_step(binding, src, outs=None, one_call=True):
     """One step: every op's target, then each target's voxel enumeration. With
     `one_call` the targets come from one tc_build_batched_topology_many call
@@ -414,6 +419,7 @@ def measure_large(binding, torch, np, synth, keep_input=None):
                            "frac_of_peak": gbs / HBM_PEAK_GBS}
         binding.tc_profile_disable()
         pm = float(np.median(pass_ms))
+        progress(f"large {op}x{f} done")
         res["ops"][f"{op}x{f}"] = {"ms_pass_median": pm, "ms_enumerate_median": float(np.median(enum_ms)),
                                    "output_voxels": V, "output_leaves": L,
                                    "output_voxels_per_s_pass": V / (pm * 1e-3), "kernels": kern}
@@ -475,12 +481,15 @@ def main():
     ms_step_single = (time.perf_counter() - t2) * 1e3 / args.steps
 
     # per-op breakdown (separate, untimed-by-the-step loop): pass and enumeration
+    progress(f"timed steps done: {ms_step:.4f} ms per step")
     ops = op_medians(binding, torch, np, src)
+    progress("per-op medians, 16 shells, done")
     # the same at B=48 (mixed member sizes, three empty members, members
     # straddling +-4096 tiles): how flat the batched pass stays as B triples
     ijk48, off48 = synth.make_config(3)
     src48 = binding.tc_batch_from_ijk(torch.from_numpy(ijk48).cuda(), off48)
     ops48 = op_medians(binding, torch, np, src48)
+    progress("per-op medians, 48 shells, done")
     b48 = {"workload": synth.CONFIG_NAMES[3], "grids": int(len(off48) - 1), "input_voxels": int(off48[-1]),
            "ops": ops48,
            "pass_ratio_b48_over_b16": {k: ops48[k]["ms_pass_median"] / ops[k]["ms_pass_median"] for k in ops}}
@@ -492,6 +501,7 @@ def main():
           "ops": op_medians(binding, torch, np, src2)}
     del src2
     pyr = pyramid(binding, torch, np, synth)
+    progress("pyramid done")
 
     # the rows beyond the step: stride-1 kernel-K targets and masked refine (60% kept)
     gen = torch.Generator(device="cuda").manual_seed(11)
@@ -532,6 +542,7 @@ def main():
         roofline["frac_trace"] = roofline["achieved_trace"] / HBM_PEAK_GBS
 
     large_input = []
+    progress("extra ops done")
     large = None if args.no_large else measure_large(binding, torch, np, synth, keep_input=large_input)
     cpu = None
     if not args.no_cpu_baseline:

@@ -401,6 +401,10 @@ __device__ __forceinline__ void tiles_small_body(const int4* upper_origin, const
   const int wv = tid / kWave;
   const int n = n_upper * m;
   int32_t* s_rng = reinterpret_cast<int32_t*>(lds + kTL_rng);  // min x, y, z, max x, y, z of the kept candidates' tiles
+  // the candidates' upper origins, issued first: no wait on the reach sets
+  int4 org[kTilesItems];
+#pragma unroll
+  for (int k = 0; k < kTilesItems; ++k) org[k] = upper_origin[min(tid * kTilesItems + k, n - 1) / m];  // n >= 1
   if (tid == 0) {
     readback[0] = src_status[0] != 0 ? kFlagSource : 0;  // a flawed source fails the pass
     for (int a = 0; a < 3; ++a) {
@@ -438,10 +442,7 @@ __device__ __forceinline__ void tiles_small_body(const int4* upper_origin, const
   // the origins are loaded first, at clamped indices, all in flight at once
   u64 khi[kTilesItems], klo[kTilesItems];
   int keep[kTilesItems];
-  int4 org[kTilesItems];
   int nkeep = 0;
-#pragma unroll
-  for (int k = 0; k < kTilesItems; ++k) org[k] = upper_origin[min(tid * kTilesItems + k, n - 1) / m];  // n >= 1
 #pragma unroll
   for (int k = 0; k < kTilesItems; ++k) {
     const int i = tid * kTilesItems + k;
@@ -907,6 +908,7 @@ constexpr int kLowersThreads = 1024;
 constexpr int kLowersItems = kLowersSmallMax / kLowersThreads;
 constexpr int kLdsTiles = 28;
 constexpr int kReachMax = 512;  // source lowers with a reach set: n / m for m >= 8
+static_assert(kReachMax <= kLowersThreads, "one given reach set per thread");
 
 constexpr int kLL_tile = 0;
 constexpr int kLL_tpre = kLL_tile + 8 * kLdsTiles * 512;
@@ -919,7 +921,8 @@ __device__ __forceinline__ void lowers_small_body(
     const int4* lower_origin, const u64* lower_mask, i64 n, int op, int m, int m_src, const int32_t* tile_of_cand,
     const int32_t* d_num_tiles, u64* tile_child, uint16_t* tile_prefix, int32_t* tile_lower_base,
     int32_t* d_num_cands, u64* cand_child, int zero_cand_child, int32_t* lower_nbr, int4* cand_origin,
-    int32_t* cand_src, int32_t* flags, const uint32_t* lower_reach, char* lds) {
+    int32_t* cand_src, int32_t* flags, const uint32_t* lower_reach, const int4 (&po)[kLowersItems],
+    uint32_t reach_pre, char* lds) {
   u64* s_tile = reinterpret_cast<u64*>(lds + kLL_tile);
   uint16_t* s_tpre = reinterpret_cast<uint16_t*>(lds + kLL_tpre);
   int32_t* s_base = reinterpret_cast<int32_t*>(lds + kLL_base);
@@ -931,14 +934,12 @@ __device__ __forceinline__ void lowers_small_body(
   constexpr int kWaves = kLowersThreads / kWave;
   const int32_t nt = *d_num_tiles;
   const i64 n_lower = n / m;
-  // the origins of this thread's pairs (clamped, n >= 1: no load waits on another)
-  int4 po[kLowersItems];
-#pragma unroll
-  for (int k = 0; k < kLowersItems; ++k) po[k] = lower_origin[min((i64)(tid + k * kLowersThreads), n - 1) / m];
-  // reach set of every source lower: given (k_box_reach), or one wave per lower,
-  // one mask word per lane, four lowers per wave in flight
+  // po: the origins of this thread's pairs (pair tid + k * kLowersThreads, clamped), loaded by the caller
+  // reach set of every source lower: given (k_box_reach; thread l loaded lower l's
+  // set, reach_pre), or one wave per lower, one mask word per lane, four lowers
+  // per wave in flight
   if (lower_reach) {
-    for (i64 l = tid; l < n_lower; l += kLowersThreads) s_reach[l] = lower_reach[l];
+    if (tid < n_lower) s_reach[tid] = reach_pre;
   } else if (op != TC_OP_COARSEN) {
     constexpr int kPer = 4;
     for (i64 l0 = wv * kPer; l0 < n_lower; l0 += kWaves * kPer) {
@@ -1088,12 +1089,19 @@ __global__ void __launch_bounds__(kTilesThreads) k_nodes_small(
     int32_t* d_num_tiles, u64* tile_child, uint16_t* tile_prefix, int32_t* tile_lower_base, int32_t* d_num_cands,
     u64* cand_child, int32_t* lower_nbr, int4* cand_origin, int32_t* cand_src, const uint32_t* lower_reach) {
   __shared__ __align__(16) char lds[kNodesLds];
+  // the lower stage's first loads (its pairs' origins, the given reach sets)
+  // go out with the tile stage's (n >= 1; clamped indices)
+  int4 po[kLowersItems];
+#pragma unroll
+  for (int k = 0; k < kLowersItems; ++k)
+    po[k] = lower_origin[min((i64)(threadIdx.x + k * kLowersThreads), n - 1) / m];
+  const uint32_t reach_pre = lower_reach ? lower_reach[min((i64)threadIdx.x, n / m - 1)] : 0u;
   tiles_small_body(upper_origin, upper_mask, n_upper, op, m, B, utile, tile_of_cand, d_num_tiles, grid_tile_begin,
                    tile_child, 0, upper_reach, readback, src_status, lds);
   __syncthreads();
   lowers_small_body(lower_origin, lower_mask, n, op, m, m_src, tile_of_cand, d_num_tiles, tile_child, tile_prefix,
                     tile_lower_base, d_num_cands, cand_child, 0, lower_nbr, cand_origin, cand_src, readback,
-                    lower_reach, lds);
+                    lower_reach, po, reach_pre, lds);
 }
 
 // ------------------------------------------------------------------ stage: leaves (pass A)

@@ -304,8 +304,8 @@ def _tiles_members(seed, B, tiles_per_member, span):
 
 @pytest.mark.parametrize("seed,B,per,span", [
     (21, 8, 20, 2),     # compact tile ranges: the LDS bitmap over (grid, tile) keys
-    (22, 6, 25, 400),   # 64 < keys <= 1024 over a key space too large for the bitmap: the rank sort
-    (23, 8, 60, 400),   # several hundred keys: the rank sort with two threads per key
+    (22, 6, 25, 400),   # 64 < keys <= 256 over a key space too large for the bitmap: the rank sort
+    (23, 8, 60, 400),   # 256 < keys <= 1024: the one-key-per-thread bitonic network
     (24, 8, 150, 400),  # more than 1024 keys: the LDS bitonic network
 ])
 def test_tile_dedup_paths(seed, B, per, span):

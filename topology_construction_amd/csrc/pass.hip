@@ -357,18 +357,18 @@ __global__ void __launch_bounds__(256) k_box_reach(const int32_t* upper_first, i
 // source upper, compacts the reachable in-range candidates, brings their
 // (grid, tile) keys into canonical order without duplicates (a rank sort for
 // at most 64 keys; above that an LDS bitmap over the batch's key space when it
-// is small, else a rank sort up to 1024 keys or an LDS bitonic network, then
+// is small, else a rank sort up to 256 keys or an LDS bitonic network, then
 // head flags and a scan), scatters the unique tiles and every candidate's tile index, writes the
 // per-grid tile ranges and, when asked (few tiles), zeroes the unique tiles'
 // lower bitmaps; more tiles get a wide fill.
 constexpr int kTilesMax = 4096;
 constexpr int kTilesThreads = 1024;
 constexpr int kTilesItems = kTilesMax / kTilesThreads;
-// keys sorted by rank counting (every thread scans up to kRankMax keys with
-// wave-uniform LDS reads, about 1 us per 200 keys); more go through a bitonic
-// network, whose ~50 dependent exchange stages cost more below 1024 keys
-constexpr int kRankMax = 1024;
-static_assert(kRankMax == kTilesThreads, "the rank counts take one LDS slot per thread");
+// keys sorted by rank counting (each of T = 1024 / K threads per key scans K / T
+// keys: a serial chain of LDS reads); more keys go through a bitonic network,
+// which is faster from a few hundred keys on (at 388 keys the rank sort took
+// twice as long)
+constexpr int kRankMax = 256;
 constexpr i64 kTileBits = 65536;  // mixed-radix (grid, tile) key space handled by an LDS bitmap
 
 // LDS of the tile stage, carved from one block so that the fused node stage
@@ -671,35 +671,84 @@ __device__ __forceinline__ void tiles_small_body(const int4* upper_origin, const
     }
     return;
   }
-  if (K > kRankMax) {  // LDS bitonic sort (K > kTilesThreads: several keys per thread)
+  if (K > kRankMax) {  // LDS bitonic sort
     int P = 2;
     while (P < K) P <<= 1;
-    for (int i = K + tid; i < P; i += kTilesThreads) {  // padding sorts last
-      s_hi[i] = ~0ull;
-      s_lo[i] = ~0ull;
-      s_v[i] = 0xffffffffu;
-    }
-    __syncthreads();
-    for (int k = 2; k <= P; k <<= 1) {
-      for (int jj = k >> 1; jj > 0; jj >>= 1) {
-        for (int i = tid; i < P; i += kTilesThreads) {
-          const int ixj = i ^ jj;
-          if (ixj > i) {
-            const bool up = (i & k) == 0;
-            const u64 ah = s_hi[i], al = s_lo[i], bh = s_hi[ixj], bl = s_lo[ixj];
-            const uint32_t av = s_v[i], bv = s_v[ixj];
-            const bool gt = ah != bh ? ah > bh : (al != bl ? al > bl : av > bv);
-            if (gt == up) {
-              s_hi[i] = bh;
-              s_lo[i] = bl;
-              s_v[i] = bv;
-              s_hi[ixj] = ah;
-              s_lo[ixj] = al;
-              s_v[ixj] = av;
+    if (K <= kTilesThreads) {
+      // one key per thread: stages whose partner is in the same wave exchange with
+      // shuffles, only the wider ones go through LDS
+      __syncthreads();
+      u64 hi = tid < K ? s_hi[tid] : ~0ull, lo = tid < K ? s_lo[tid] : ~0ull;  // padding sorts last
+      uint32_t v = tid < K ? s_v[tid] : 0xffffffffu;
+      const bool act = tid < P;  // whole waves: P is a power of two >= 128
+      for (int k = 2; k <= P; k <<= 1) {
+        for (int jj = k >> 1; jj > 0; jj >>= 1) {
+          u64 oh = 0, ol = 0;
+          uint32_t ov = 0;
+          if (jj >= kWave) {  // uniform
+            __syncthreads();
+            if (act) {
+              s_hi[tid] = hi;
+              s_lo[tid] = lo;
+              s_v[tid] = v;
             }
+            __syncthreads();
+            if (act) {
+              oh = s_hi[tid ^ jj];
+              ol = s_lo[tid ^ jj];
+              ov = s_v[tid ^ jj];
+            }
+          } else if (act) {
+            oh = __shfl_xor(hi, jj, kWave);
+            ol = __shfl_xor(lo, jj, kWave);
+            ov = (uint32_t)__shfl_xor((int)v, jj, kWave);
+          }
+          if (!act) continue;
+          const bool gt = hi != oh ? hi > oh : (lo != ol ? lo > ol : v > ov);
+          const bool lt = hi != oh ? hi < oh : (lo != ol ? lo < ol : v < ov);
+          const bool up = (tid & k) == 0, lower = (tid & jj) == 0;
+          if (up ? (lower ? gt : lt) : (lower ? lt : gt)) {
+            hi = oh;
+            lo = ol;
+            v = ov;
           }
         }
-        __syncthreads();
+      }
+      __syncthreads();
+      if (act) {
+        s_hi[tid] = hi;
+        s_lo[tid] = lo;
+        s_v[tid] = v;
+      }
+      __syncthreads();
+    } else {
+      for (int i = K + tid; i < P; i += kTilesThreads) {  // padding sorts last
+        s_hi[i] = ~0ull;
+        s_lo[i] = ~0ull;
+        s_v[i] = 0xffffffffu;
+      }
+      __syncthreads();
+      for (int k = 2; k <= P; k <<= 1) {
+        for (int jj = k >> 1; jj > 0; jj >>= 1) {
+          for (int i = tid; i < P; i += kTilesThreads) {
+            const int ixj = i ^ jj;
+            if (ixj > i) {
+              const bool up = (i & k) == 0;
+              const u64 ah = s_hi[i], al = s_lo[i], bh = s_hi[ixj], bl = s_lo[ixj];
+              const uint32_t av = s_v[i], bv = s_v[ixj];
+              const bool gt = ah != bh ? ah > bh : (al != bl ? al > bl : av > bv);
+              if (gt == up) {
+                s_hi[i] = bh;
+                s_lo[i] = bl;
+                s_v[i] = bv;
+                s_hi[ixj] = ah;
+                s_lo[ixj] = al;
+                s_v[ixj] = av;
+              }
+            }
+          }
+          __syncthreads();
+        }
       }
     }
   }

@@ -369,6 +369,7 @@ constexpr int kTilesItems = kTilesMax / kTilesThreads;
 // which is faster from a few hundred keys on (at 388 keys the rank sort took
 // twice as long)
 constexpr int kRankMax = 256;
+constexpr int kSegMax = 128;  // keys per grid for the per-grid rank sort
 constexpr i64 kTileBits = 65536;  // mixed-radix (grid, tile) key space handled by an LDS bitmap
 
 // LDS of the tile stage, carved from one block so that the fused node stage
@@ -577,15 +578,73 @@ __device__ __forceinline__ void tiles_small_body(const int4* upper_origin, const
       return;
     }
   }
+  int rank = 0;  // thread tid < K: the rank of key tid, which it holds in rhi, rlo, rv
+  u64 rhi = 0, rlo = 0;
+  uint32_t rv = 0;
+  // More than 64 and at most kTilesThreads keys: the compacted keys are grouped
+  // by grid (candidates follow the source uppers, which are in grid order), so a
+  // key's rank is the first index of its grid's run plus its rank inside the
+  // run. The run bounds come from two binary searches over the keys' grids;
+  // when no run holds more than kSegMax keys, each thread ranks its key against
+  // its own run only (a few keys per grid on large batches of small members).
+  bool ranked = false;  // uniform
+  if (K > kWave && K <= kTilesThreads) {
+    __syncthreads();
+    auto grid_at = [&](int i) { return (int32_t)((s_hi[i] << 4) | (s_lo[i] >> 60)); };
+    int lo_b = 0, hi_b = 0;
+    if (tid < K) {
+      const int32_t g = grid_at(tid);
+      int a = 0, b = tid;  // first index of grid g: in [0, tid]
+      while (a < b) {
+        const int mid = (a + b) >> 1;
+        if (grid_at(mid) < g) a = mid + 1; else b = mid;
+      }
+      lo_b = a;
+      a = tid + 1;
+      b = K;  // one past its last index: in [tid + 1, K]
+      while (a < b) {
+        const int mid = (a + b) >> 1;
+        if (grid_at(mid) <= g) a = mid + 1; else b = mid;
+      }
+      hi_b = a;
+    }
+    const int mseg = wave_max_i32(hi_b - lo_b);
+    if (lane == 0) s_wave[wv] = mseg;
+    __syncthreads();
+    int mx = 0;
+#pragma unroll
+    for (int w = 0; w < kTilesThreads / kWave; ++w) mx = max(mx, s_wave[w]);
+    __syncthreads();  // s_wave is free again
+    if (mx <= kSegMax) {
+      ranked = true;
+      if (tid < K) {
+        rhi = s_hi[tid];
+        rlo = s_lo[tid];
+        rv = s_v[tid];
+        int c = 0;
+        for (int j = lo_b; j < hi_b; ++j) {
+          const u64 oh = s_hi[j], ol = s_lo[j];
+          const uint32_t ov = s_v[j];
+          c += (oh != rhi ? oh < rhi : (ol != rlo ? ol < rlo : ov < rv)) ? 1 : 0;
+        }
+        rank = lo_b + c;
+      }
+      // place every key at its rank, in place, then the head flags below
+      __syncthreads();
+      if (tid < K) {
+        s_hi[rank] = rhi;
+        s_lo[rank] = rlo;
+        s_v[rank] = rv;
+      }
+      __syncthreads();
+    }
+  }
   // Up to kRankMax keys: a rank sort (keys are distinct through their candidate
   // index). With Kp = K rounded up to a power of two (>= 64), T = 1024 / Kp
   // threads share each key: thread (part, i) counts the keys smaller than key i
   // among its 1/T of the keys; the partial ranks meet in LDS.
   int32_t* s_cnt = reinterpret_cast<int32_t*>(lds + kTL_cnt);
-  int rank = 0;  // thread tid < K: the rank of key tid, which it holds in rhi, rlo, rv
-  u64 rhi = 0, rlo = 0;
-  uint32_t rv = 0;
-  if (K <= kRankMax) {
+  if (!ranked && K <= kRankMax) {
     int Kp = kWave;
     while (Kp < K) Kp <<= 1;
     const int T = kTilesThreads / Kp;
@@ -671,7 +730,7 @@ __device__ __forceinline__ void tiles_small_body(const int4* upper_origin, const
     }
     return;
   }
-  if (K > kRankMax) {  // LDS bitonic sort
+  if (!ranked && K > kRankMax) {  // LDS bitonic sort
     int P = 2;
     while (P < K) P <<= 1;
     if (K <= kTilesThreads) {

@@ -304,9 +304,11 @@ def _tiles_members(seed, B, tiles_per_member, span):
 
 @pytest.mark.parametrize("seed,B,per,span", [
     (21, 8, 20, 2),     # compact tile ranges: the LDS bitmap over (grid, tile) keys
-    (22, 6, 25, 400),   # 64 < keys <= 256 over a key space too large for the bitmap: the rank sort
-    (23, 8, 60, 400),   # 256 < keys <= 1024: the one-key-per-thread bitonic network
+    (22, 6, 25, 400),   # 64 < keys, at most 128 per grid, key space too large for the bitmap: per-grid rank
+    (23, 8, 60, 400),   # several hundred keys, at most 128 per grid: the per-grid rank sort
     (24, 8, 150, 400),  # more than 1024 keys: the LDS bitonic network
+    (25, 1, 200, 400),  # one grid above 128 keys (no per-grid rank), at most 256 keys: the rank sort
+    (26, 2, 300, 400),  # grids above 128 keys, 256 < keys <= 1024: the one-key-per-thread bitonic network
 ])
 def test_tile_dedup_paths(seed, B, per, span):
     """Every tile-dedup path of the one-workgroup tile stage (4096 candidates at

@@ -53,18 +53,19 @@ static tc_grid_batch* alloc_batch(int32_t B, const Layout& layout, const OutAllo
     b->h_leaf.assign(B, 0);
     b->layout = layout;
     b->bytes = b->layout.total;
-    b->stream = oa.stream;
+    const hipStream_t as = oa.transient || !oa.alloc_stream ? oa.stream : oa.alloc_stream;
+    b->stream = as;
     b->device = current_device();
     if (oa.transient) {
-      b->block = scratch_acquire(b->bytes, oa.stream);
+      b->block = scratch_acquire(b->bytes, as);
       b->buffer = scratch_ptr(b->block);
     } else if (oa.alloc) {
       b->has_alloc = true;
       b->alloc = *oa.alloc;
-      b->buffer = b->alloc.alloc(b->alloc.ctx, b->bytes, (void*)oa.stream);
+      b->buffer = b->alloc.alloc(b->alloc.ctx, b->bytes, (void*)as);
       if (!b->buffer) throw Error(TC_ERR_ALLOC, "allocator returned NULL for " + std::to_string(b->bytes) + " bytes");
     } else {
-      b->buffer = batch_buffer_take(b->bytes, oa.stream, &b->cap);
+      b->buffer = batch_buffer_take(b->bytes, as, &b->cap);
     }
   } catch (...) {
     delete b;
@@ -399,30 +400,115 @@ tc_status tc_build_batched_topology_many(const tc_grid_batch* src, int32_t n_ops
     if (current_device() != src->device) throw tc::Error(TC_ERR_INVALID_ARG, "src lives on another device");
     tc::SourceScope scope(allocator);
     hipStream_t s = (hipStream_t)stream;
-    // every op's passes are enqueued back to back; a small batch's last pass
-    // leaves its header readback pending, and all are waited for at the end
-    for (int32_t i = 0; i < n_ops; ++i) {
-      const std::vector<int>& passes = plan[i];
+    if (n_ops == 1) {  // one target: its passes on the caller's stream, each waiting for its own counts
+      const std::vector<int>& passes = plan[0];
       if (passes.empty()) {  // kernel size 1: the target is the source
-        made[i] = tc::copy_batch(src, tc::OutAlloc{allocator, s});
-        continue;
-      }
-      const tc_grid_batch* cur = src;
-      tc_grid_batch* owned = nullptr;  // intermediate result of the previous pass
-      try {
-        for (size_t p = 0; p < passes.size(); ++p) {
-          const bool last = p + 1 == passes.size();
-          tc_grid_batch* next =
-              tc::build_pass(cur, passes[p], tc::OutAlloc{allocator, s, !last}, nullptr, last && n_ops > 1);
+        made[0] = tc::copy_batch(src, tc::OutAlloc{allocator, s});
+      } else {
+        const tc_grid_batch* cur = src;
+        tc_grid_batch* owned = nullptr;  // intermediate result of the previous pass
+        try {
+          for (size_t p = 0; p < passes.size(); ++p) {
+            const bool last = p + 1 == passes.size();
+            tc_grid_batch* next = tc::build_pass(cur, passes[p], tc::OutAlloc{allocator, s, !last});
+            tc::free_batch(owned);
+            owned = next;
+            cur = next;
+          }
+        } catch (...) {
           tc::free_batch(owned);
-          owned = next;
-          cur = next;
+          throw;
         }
+        made[0] = owned;
+      }
+    } else {
+      // Several targets, longest chain first: the first runs on s, the others on
+      // kSideStreams internal streams (round robin) that wait once for all earlier
+      // work on s, so that the targets' kernel chains overlap on the device. The
+      // passes go out round by round (every target's first pass, then the second
+      // passes, ...), each leaving its header readback pending, so that a chain's
+      // next pass finds the counts of its intermediate ready when it starts.
+      // Outputs are allocated on s. An output whose pass left its headers pending
+      // is complete once they are read (its finalize is its last kernel); for any
+      // other output built on an internal stream (a large batch's writers, a
+      // copy) s waits for that stream before the call returns, so later work on s,
+      // and reuse of its memory in s order, comes after the kernels that wrote it.
+      // Cross-stream waits cost the host several microseconds each, hence one
+      // side stream and no join when nothing needs it.
+      const int dev = src->device;
+      const int nside = std::min<int>(n_ops - 1, tc::kSideStreams);
+      std::vector<int32_t> order(n_ops);
+      for (int32_t i = 0; i < n_ops; ++i) order[i] = i;
+      std::stable_sort(order.begin(), order.end(),
+                       [&](int32_t a, int32_t b) { return plan[a].size() > plan[b].size(); });
+      std::vector<hipEvent_t> evs;
+      auto ev_take = [&]() {
+        evs.push_back(tc::pending_event_take(dev));
+        return evs.back();
+      };
+      auto give_events = [&]() {
+        for (hipEvent_t e : evs) tc::pending_event_give(dev, e);
+        evs.clear();
+      };
+      std::vector<char> needs_join(nside, 0);
+      auto join = [&](bool all) {  // s waits for the side streams that need it
+        for (int k = 0; k < nside; ++k) {
+          if (!all && !needs_join[k]) continue;
+          needs_join[k] = 0;
+          hipEvent_t e = ev_take();
+          tc::hip_check(hipEventRecord(e, tc::internal_stream(dev, k)), "hipEventRecord");
+          tc::hip_check(hipStreamWaitEvent(s, e, 0), "hipStreamWaitEvent");
+        }
+      };
+      std::vector<const tc_grid_batch*> cur(n_ops, src);
+      std::vector<tc_grid_batch*> owned(n_ops, nullptr);  // intermediates of chains
+      bool started = false;
+      try {
+        if (nside > 0) {
+          hipEvent_t e0 = ev_take();
+          tc::hip_check(hipEventRecord(e0, s), "hipEventRecord");
+          for (int k = 0; k < nside; ++k)
+            tc::hip_check(hipStreamWaitEvent(tc::internal_stream(dev, k), e0, 0), "hipStreamWaitEvent");
+        }
+        started = true;
+        const size_t rounds = std::max<size_t>(1, plan[order[0]].size());
+        for (size_t r = 0; r < rounds; ++r) {
+          for (int32_t q = 0; q < n_ops; ++q) {
+            const int32_t i = order[q];
+            const int side = q == 0 ? -1 : (q - 1) % nside;
+            const hipStream_t si = side < 0 ? s : tc::internal_stream(dev, side);
+            const std::vector<int>& passes = plan[i];
+            if (passes.empty()) {  // kernel size 1: a copy of the source
+              if (r == 0) {
+                made[i] = tc::copy_batch(src, tc::OutAlloc{allocator, si, false, s});
+                if (side >= 0) needs_join[side] = 1;
+              }
+              continue;
+            }
+            if (r >= passes.size()) continue;
+            const bool last = r + 1 == passes.size();
+            tc_grid_batch* next = tc::build_pass(
+                cur[i], passes[r], tc::OutAlloc{allocator, si, !last, last && side >= 0 ? s : nullptr}, nullptr, true);
+            if (last && side >= 0 && !next->hdr_pending) needs_join[side] = 1;
+            tc::free_batch(owned[i]);  // its readers are on si, before any later reuse on si
+            owned[i] = last ? nullptr : next;
+            cur[i] = next;
+            if (last) made[i] = next;
+          }
+        }
+        join(false);
       } catch (...) {
-        tc::free_batch(owned);
+        if (started) {
+          try {
+            join(true);
+          } catch (...) {
+          }
+        }
+        for (int32_t i = 0; i < n_ops; ++i) tc::free_batch(owned[i]);
+        give_events();
         throw;
       }
-      made[i] = owned;
+      give_events();
     }
     for (int32_t i = 0; i < n_ops; ++i) tc::resolve_counts(made[i]);
     for (int32_t i = 0; i < n_ops; ++i) {

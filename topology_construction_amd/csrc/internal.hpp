@@ -217,6 +217,11 @@ void vox_slot_give(int slot);
 void* pinned_block_take(size_t bytes, size_t* cap);
 void pinned_block_give(void* p, size_t cap);
 hipEvent_t pending_event_take(int device);
+// Internal stream k (0 <= k < kInternalStreams) of the current device: created
+// once, non-blocking, default priority, kept until the process ends.
+constexpr int kInternalStreams = 4;
+constexpr int kSideStreams = 1;  // internal streams a multi-target build spreads its targets over
+hipStream_t internal_stream(int device, int k);
 void pending_event_give(int device, hipEvent_t e);
 
 // Stream-ordered device allocation from the device's default pool (release
@@ -360,8 +365,12 @@ void tree_enumerate(const GridView& v, int32_t* ijk, hipStream_t s);
 // Allocation of the single output buffer of a batch.
 struct OutAlloc {
   const tc_allocator* alloc;  // NULL: the library's own (hipMallocAsync, cached)
-  hipStream_t stream;
+  hipStream_t stream;         // the stream the pass's work is enqueued on
   bool transient = false;     // an intermediate batch of a chain: a scratch block of the call's source
+  // when set, the output's buffer is taken on (and later handed back on) this
+  // stream instead: the caller's stream, for outputs built on an internal stream
+  // whose work the caller's stream waits for
+  hipStream_t alloc_stream = nullptr;
 };
 
 // Testing: bits that the next batch built on the calling thread ORs into its

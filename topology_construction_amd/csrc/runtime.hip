@@ -456,6 +456,21 @@ void pending_event_give(int device, hipEvent_t e) {
   pp.events.emplace_back(device, e);
 }
 
+hipStream_t internal_stream(int device, int k) {
+  if (k < 0 || k >= kInternalStreams) throw Error(TC_ERR_INTERNAL, "internal stream index out of range");
+  static std::mutex mu;
+  static std::vector<std::vector<hipStream_t>>* streams = new std::vector<std::vector<hipStream_t>>();
+  std::lock_guard<std::mutex> lk(mu);
+  if ((int)streams->size() <= device) streams->resize(device + 1);
+  std::vector<hipStream_t>& v = (*streams)[device];
+  while ((int)v.size() <= k) {
+    hipStream_t st = nullptr;
+    hip_check(hipStreamCreateWithFlags(&st, hipStreamNonBlocking), "hipStreamCreateWithFlags");
+    v.push_back(st);
+  }
+  return v[k];
+}
+
 VoxTicket vox_slot_take(int device) {
   VoxPool& p = vox_pool();
   VoxTicket t{-1, nullptr, nullptr};

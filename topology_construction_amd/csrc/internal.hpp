@@ -341,6 +341,10 @@ void tree_rank_tiles_last(TreeScratch& t, int32_t* done_ctr, int32_t* cand_src, 
 void tree_count_cands(TreeScratch& t, hipStream_t s);           // leaf counts per cand + their scan
 void tree_counts(TreeScratch& t, int32_t B, hipStream_t s);     // tree_count_cands + tree_grid_counts (fused when small)
 void tree_write_nodes(TreeScratch& t, const GridView& out, int32_t* leaf_cand, hipStream_t s);
+// tree_counts and tree_write_nodes in one launch, for at most 2048 candidate and
+// tile slots once the marking wrote the candidates' counts (..._fits says when).
+bool write_nodes_counted_fits(const TreeScratch& t, int32_t B);
+void tree_write_nodes_counted(TreeScratch& t, const GridView& out, int32_t* leaf_cand, hipStream_t s);
 // Leaf masks from eight word slices (slice k: word k of every leaf), and their
 // statistics.
 void tree_leaf_stats(const GridView& out, const u64* slices, uint32_t* leaf_box, int32_t* leaf_inrun, i64* vox_part,

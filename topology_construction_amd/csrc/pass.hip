@@ -2218,8 +2218,10 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, 
              ts.flags);
     }
     ts.cand_counts_ready = true;
-    // counts and the single readback
-    tree_counts(ts, B, s);
+    // counts (small batches whose lower stage ran in one workgroup: inside the
+    // node writer's launch below)
+    const bool counted_writer = bounded && small_lowers && write_nodes_counted_fits(ts, B);
+    if (!counted_writer) tree_counts(ts, B, s);
     if (bounded) {  // capacity layout: allocated while the stages above run
       out = new_batch_capacity(B, nT, nL, L_cap, oa);
     } else {  // exact layout: counts first, then the allocation
@@ -2247,7 +2249,11 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, 
     int32_t* leaf_cand = post.at<int32_t>(o_lc);
     i64* vox_part = post.at<i64>(o_part);
     int32_t* leaf_inrun = post.at<int32_t>(o_inrun);
-    tree_write_nodes(ts, ov, leaf_cand, s);
+    if (counted_writer) {
+      tree_write_nodes_counted(ts, ov, leaf_cand, s);
+    } else {
+      tree_write_nodes(ts, ov, leaf_cand, s);
+    }
     if (op == TC_OP_REFINE || op == TC_OP_COARSEN) {
       const i64 lanes = op == TC_OP_REFINE ? 1 : 4;
       auto gather = op == TC_OP_REFINE ? k_leaf_gather<0> : k_leaf_gather<1>;

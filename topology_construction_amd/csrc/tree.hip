@@ -438,15 +438,15 @@ constexpr int kNodeFlags = 4096;  // candidates per tile whose non-empty flags t
 // grid, parent) per set bit of its leaf mask; leaf_cand[leaf] remembers the
 // candidate for the leaf-mask producers. Block 0 also sets every header's box
 // to empty for the leaf finalizer.
-__global__ void __launch_bounds__(256) k_write_nodes(
+// cand_scan and upper_excl may point into LDS (the fused writer below).
+__device__ __forceinline__ void write_nodes_body(
     int32_t tile_blocks, const int4* utile, const u64* tile_child, const uint16_t* tile_prefix,
     const int32_t* tile_lower_base, const int4* cand_origin, const u64* cand_child, const uint16_t* cand_prefix,
     const i64* cand_counts, const i64* cand_scan, const int32_t* upper_excl, const int32_t* d_num_tiles,
     const int32_t* d_num_cands, int32_t n_upper, int32_t n_lower, int32_t n_leaf, int4* upper_origin,
     u64* upper_key, int32_t* upper_first, u64* upper_mask, int4* lower_origin, int32_t* lower_first,
     u64* lower_mask, uint16_t* lower_prefix, int4* leaf_origin, int32_t* leaf_parent, int32_t* leaf_cand,
-    tc_grid_header* hdr, int32_t B, i64 cap_cands) {
-  __shared__ uint32_t s_flags[kNodeFlags / 32];
+    tc_grid_header* hdr, int32_t B, i64 cap_cands, uint32_t* s_flags) {
   if (blockIdx.x == 0) {  // every grid's box starts empty; the leaf finalizer folds into it
     for (int32_t g = threadIdx.x; g < B; g += 256) {
       for (int a = 0; a < 3; ++a) {
@@ -560,6 +560,154 @@ __global__ void __launch_bounds__(256) k_write_nodes(
     leaf_parent[idx] = (int32_t)lo;
     leaf_cand[idx] = (int32_t)c;
   }
+}
+
+__global__ void __launch_bounds__(256) k_write_nodes(
+    int32_t tile_blocks, const int4* utile, const u64* tile_child, const uint16_t* tile_prefix,
+    const int32_t* tile_lower_base, const int4* cand_origin, const u64* cand_child, const uint16_t* cand_prefix,
+    const i64* cand_counts, const i64* cand_scan, const int32_t* upper_excl, const int32_t* d_num_tiles,
+    const int32_t* d_num_cands, int32_t n_upper, int32_t n_lower, int32_t n_leaf, int4* upper_origin,
+    u64* upper_key, int32_t* upper_first, u64* upper_mask, int4* lower_origin, int32_t* lower_first,
+    u64* lower_mask, uint16_t* lower_prefix, int4* leaf_origin, int32_t* leaf_parent, int32_t* leaf_cand,
+    tc_grid_header* hdr, int32_t B, i64 cap_cands) {
+  __shared__ uint32_t s_flags[kNodeFlags / 32];
+  write_nodes_body(tile_blocks, utile, tile_child, tile_prefix, tile_lower_base, cand_origin, cand_child, cand_prefix,
+                   cand_counts, cand_scan, upper_excl, d_num_tiles, d_num_cands, n_upper, n_lower, n_leaf,
+                   upper_origin, upper_key, upper_first, upper_mask, lower_origin, lower_first, lower_mask,
+                   lower_prefix, leaf_origin, leaf_parent, leaf_cand, hdr, B, cap_cands, s_flags);
+}
+
+// Small batches whose marking wrote the candidates' packed counts (at most
+// kWnCands candidates and kWnTiles tiles): the counts stage and the node writer
+// in one launch, which saves the host one launch per pass. Every working block
+// first scans the packed counts and the tiles' non-empty flags itself, into LDS
+// (a few KB of loads, all in flight together), so no block waits on another;
+// block 0 also writes the per-grid counts and begins (grid_info) and the batch
+// totals (readback) that the later stages read. Blocks past the live tiles and
+// candidates leave first.
+constexpr int kWnCands = 2048;
+constexpr int kWnTiles = 2048;
+constexpr int kWnPer = kWnCands / 256;
+static_assert(kWnTiles / 256 == kWnPer, "one item count for both scans");
+
+__global__ void __launch_bounds__(256) k_write_nodes_counted(
+    int32_t tile_blocks, const int4* utile, const u64* tile_child, const uint16_t* tile_prefix,
+    const int32_t* tile_lower_base, const int4* cand_origin, const u64* cand_child, const uint16_t* cand_prefix,
+    const i64* cand_counts, const int32_t* d_num_tiles, const int32_t* d_num_cands, int32_t n_upper,
+    int32_t n_lower, int32_t n_leaf, int4* upper_origin, u64* upper_key, int32_t* upper_first, u64* upper_mask,
+    int4* lower_origin, int32_t* lower_first, u64* lower_mask, uint16_t* lower_prefix, int4* leaf_origin,
+    int32_t* leaf_parent, int32_t* leaf_cand, tc_grid_header* hdr, int32_t B, i64 cap_cands,
+    const int32_t* grid_tile_begin, int32_t* grid_info, int32_t* readback) {
+  __shared__ i64 s_cc[kWnCands + 1];
+  __shared__ int32_t s_tlb[kWnTiles + 1];
+  __shared__ int32_t s_uex[kWnTiles + 1];
+  __shared__ i64 s_wave64[256 / kWave];
+  __shared__ int32_t s_wave[256 / kWave];
+  __shared__ uint32_t s_flags[kNodeFlags / 32];
+  const int tid = threadIdx.x;
+  const int32_t cap_c = (int32_t)cap_cands, cap_t = tile_blocks;
+  // every load first, at clamped indices (the counts up to the capacities)
+  i64 v[kWnPer];
+  int32_t tb[kWnPer + 1];
+#pragma unroll
+  for (int k = 0; k < kWnPer; ++k) v[k] = cand_counts[min(tid * kWnPer + k, cap_c - 1)];
+#pragma unroll
+  for (int k = 0; k <= kWnPer; ++k) tb[k] = tile_lower_base[min(tid * kWnPer + k, cap_t)];
+  int32_t nt = *d_num_tiles, nc = *d_num_cands;
+  if (nt < 0 || nt > cap_t || nc < 0 || nc > cap_c) {  // consistency guard (the LDS holds the capacities)
+    if (blockIdx.x == 0 && tid == 0) atomicOr(&readback[0], kFlagInternal);
+    nt = min(max(nt, 0), cap_t);
+    nc = min(max(nc, 0), cap_c);
+  }
+  const int32_t bx = blockIdx.x;
+  if (bx != 0 && (bx < tile_blocks ? bx >= nt : (i64)(bx - tile_blocks) * 4 >= nc)) return;  // uniform
+  // exclusive scan of the packed counts: a candidate's first leaf and output lower
+  i64 sum = 0;
+#pragma unroll
+  for (int k = 0; k < kWnPer; ++k) {
+    if (tid * kWnPer + k >= nc) v[k] = 0;
+    sum += v[k];
+  }
+  i64 total;
+  i64 ex = block_excl_scan<i64, 256>(sum, s_wave64, total);
+#pragma unroll
+  for (int k = 0; k < kWnPer; ++k) {
+    const int c = tid * kWnPer + k;
+    if (c < nc) s_cc[c] = ex;
+    ex += v[k];
+  }
+  if (tid == 0) s_cc[nc] = total;
+#pragma unroll
+  for (int k = 0; k <= kWnPer; ++k) {
+    const int t = tid * kWnPer + k;
+    if (t <= nt) s_tlb[t] = tb[k];
+  }
+  __syncthreads();
+  // non-empty tiles and their exclusive scan: the output upper indices
+  int f[kWnPer];
+  int fsum = 0;
+#pragma unroll
+  for (int k = 0; k < kWnPer; ++k) {
+    const int t = tid * kWnPer + k;
+    f[k] = t < nt && scan_leaf(s_cc[s_tlb[t + 1]]) > scan_leaf(s_cc[s_tlb[t]]) ? 1 : 0;
+    fsum += f[k];
+  }
+  int nu;
+  int fex = block_excl_scan<int, 256>(fsum, s_wave, nu);
+#pragma unroll
+  for (int k = 0; k < kWnPer; ++k) {
+    const int t = tid * kWnPer + k;
+    if (t < nt) s_uex[t] = fex;
+    fex += f[k];
+  }
+  if (tid == 0) s_uex[nt] = nu;
+  __syncthreads();
+  if (bx == 0) {  // per-grid counts and begins, batch totals
+    if (tid == 0) {
+      readback[1] = nu;
+      readback[2] = scan_lower(s_cc[nc]);
+      readback[3] = scan_leaf(s_cc[nc]);
+    }
+    for (int32_t g = tid; g < B; g += 256) {
+      const int32_t t0 = grid_tile_begin[g], t1 = grid_tile_begin[g + 1];
+      const i64 vb = s_cc[s_tlb[t0]], ve = s_cc[s_tlb[t1]];
+      const int32_t nug = s_uex[t1] - s_uex[t0];
+      const int32_t n1 = scan_lower(ve) - scan_lower(vb);
+      const int32_t nl = scan_leaf(ve) - scan_leaf(vb);
+      int32_t* gi = grid_info + (i64)g * 6;
+      gi[0] = nug;
+      gi[1] = n1;
+      gi[2] = nl;
+      gi[3] = s_uex[t0];
+      gi[4] = scan_lower(vb);
+      gi[5] = scan_leaf(vb);
+      readback[4 + g * 3 + 0] = nug;
+      readback[4 + g * 3 + 1] = n1;
+      readback[4 + g * 3 + 2] = nl;
+    }
+  }
+  write_nodes_body(tile_blocks, utile, tile_child, tile_prefix, tile_lower_base, cand_origin, cand_child, cand_prefix,
+                   cand_counts, s_cc, s_uex, d_num_tiles, d_num_cands, n_upper, n_lower, n_leaf, upper_origin,
+                   upper_key, upper_first, upper_mask, lower_origin, lower_first, lower_mask, lower_prefix,
+                   leaf_origin, leaf_parent, leaf_cand, hdr, B, cap_cands, s_flags);
+}
+
+bool write_nodes_counted_fits(const TreeScratch& ts, int32_t B) {
+  return ts.cand_counts_ready && ts.cap_cands >= 1 && ts.cap_cands <= kWnCands && ts.cap_tiles >= 1 &&
+         ts.cap_tiles <= kWnTiles && B >= 1;
+}
+
+void tree_write_nodes_counted(TreeScratch& ts, const GridView& out, int32_t* leaf_cand, hipStream_t s) {
+  if (!write_nodes_counted_fits(ts, out.B)) throw Error(TC_ERR_INTERNAL, "nodes: too many candidates for one launch");
+  const i64 tile_blocks = ts.cap_tiles;
+  launch("k_write_nodes", k_write_nodes_counted, tile_blocks + ceil_div(ts.cap_cands, 4), 256, s,
+         (int32_t)tile_blocks, (const int4*)ts.utile, (const u64*)ts.tile_child, (const uint16_t*)ts.tile_prefix,
+         (const int32_t*)ts.tile_lower_base, (const int4*)ts.cand_origin, (const u64*)ts.cand_child,
+         (const uint16_t*)ts.cand_prefix, (const i64*)ts.cand_counts, (const int32_t*)ts.d_num_tiles,
+         (const int32_t*)ts.d_num_cands, out.n_upper, out.n_lower, out.n_leaf, out.upper_origin, out.upper_key,
+         out.upper_first, out.upper_mask, out.lower_origin, out.lower_first, out.lower_mask, out.lower_prefix,
+         out.leaf_origin, out.leaf_parent, leaf_cand, out.headers, out.B, ts.cap_cands,
+         (const int32_t*)ts.grid_tile_begin, ts.grid_info, ts.readback);
 }
 
 void tree_write_nodes(TreeScratch& ts, const GridView& out, int32_t* leaf_cand, hipStream_t s) {

@@ -188,16 +188,20 @@ def progress(msg):
 
 def run_step(binding, src, outs=None, one_call=True):
     """One step: every op's target, then each target's voxel enumeration. With
-    `one_call` the targets come from one tc_build_batched_topology_many call
-    (their passes enqueued back to back, one wait), else from one
-    tc_build_batched_topology call per op. Returns voxels."""
+    `one_call` the targets come from one tc_build_batched_topology_many call and
+    their enumerations from one tc_enumerate_ijk_many launch, else from one
+    tc_build_batched_topology and one tc_enumerate_ijk call per op. Returns
+    voxels."""
     total = 0
     if one_call:
         built = binding.tc_build_batched_topology_many(src, STEP_OPS)
     else:
         built = [binding.tc_build_batched_topology(src, op, f) for op, f in STEP_OPS]
-    for (op, f), out in zip(STEP_OPS, built):
-        ijk = binding.tc_enumerate_ijk(out)
+    if one_call:
+        ijks = binding.tc_enumerate_ijk_many(built)
+    else:
+        ijks = [binding.tc_enumerate_ijk(out) for out in built]
+    for (op, f), out, ijk in zip(STEP_OPS, built, ijks):
         total += ijk.shape[0]
         if outs is not None:
             outs.append((op, f, out.leaf_count, int(ijk.shape[0])))
@@ -524,7 +528,9 @@ def main():
         del out
 
     bytes_per_step = sum(kernel_bytes(args.roofline_kernel, int(src.leaf_count), L, V) for (_, _, L, V) in facts)
-    launches_per_step = len(facts)
+    # launches of the kernel per step, as the timed steps made them (one batched
+    # enumeration per step; a per-op kernel would launch once per op)
+    launches_per_step = k_n / args.steps if k_n else len(facts)
     avg_ms = k_ms / max(k_n, 1)
     avg_bytes = bytes_per_step / launches_per_step
     achieved = avg_bytes / (avg_ms * 1e-3) / 1e9 if k_n else None

@@ -283,6 +283,16 @@ tc_status tc_batch_voxel_total(const tc_grid_batch* batch, int64_t* h_total, voi
 tc_status tc_enumerate_ijk(const tc_grid_batch* batch, int32_t* d_ijk_out, int64_t capacity,
                            void* stream);
 
+/* tc_enumerate_ijk of n batches in one launch (up to eight per launch, so a
+ * group of small batches fills the device once instead of n times): batch j's
+ * rows go to d_ijk_outs[j] (int32[V_j][3] device, capacities[j] >= V_j rows;
+ * 16-byte aligned outputs take the vector stores). A NULL output is allowed for
+ * a batch without voxels.
+ *   n           >= 1; batches, d_ijk_outs, capacities: host arrays of n entries.
+ * Every argument is checked before the launch. */
+tc_status tc_enumerate_ijk_many(int32_t n, const tc_grid_batch* const* batches, int32_t* const* d_ijk_outs,
+                                const int64_t* capacities, void* stream);
+
 /* Kernel map of a convolution plan between two batches with the same member
  * count (issue page "Generated-topology grid construction dominates
  * per-iteration ConvolutionPlan cost", Measurements: a plan builds a k3 s1 map

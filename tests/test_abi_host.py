@@ -87,6 +87,16 @@ def test_build_many_rejects_bad_arguments_on_host(lib):
     assert lib.tc_build_batched_topology_many(None, 2, ops, facs, None, None, None) == binding.TC_ERR_INVALID_ARG
 
 
+def test_enumerate_many_rejects_bad_arguments_on_host(lib):
+    outs = (ctypes.c_void_p * 2)()
+    caps = (ctypes.c_int64 * 2)(0, 0)
+    hs = (ctypes.c_void_p * 2)()
+    assert lib.tc_enumerate_ijk_many(0, hs, outs, caps, None) == binding.TC_ERR_INVALID_ARG
+    assert lib.tc_enumerate_ijk_many(2, None, outs, caps, None) == binding.TC_ERR_INVALID_ARG
+    assert lib.tc_enumerate_ijk_many(2, hs, outs, caps, None) == binding.TC_ERR_INVALID_ARG
+    assert b"batch 0 is NULL" in lib.tc_last_error()
+
+
 def test_null_handles_are_rejected(lib):
     info = binding.tc_batch_info()
     assert lib.tc_batch_get_info(None, ctypes.byref(info)) == binding.TC_ERR_INVALID_ARG

@@ -270,3 +270,37 @@ def test_many_ops_failures_free_every_output():
     outs = binding.tc_build_batched_topology_many(src, ops)
     for (op, f), out in zip(ops, outs):
         assert_same(gpu_fields(out), oracle.run(op, f, ijk, off), f"after failures {op} {f}")
+
+
+def test_enumerate_many_equals_single_enumerations():
+    """One launch over several batches (more than eight, so two launches; an
+    empty batch; outputs at 16-byte boundaries through the binding and at
+    unaligned addresses through the C ABI): every batch's rows equal its own
+    tc_enumerate_ijk."""
+    import torch
+    lib = binding.load_library()
+    ijk, off = synth.make_config(3)
+    src = binding.tc_batch_from_ijk(torch.from_numpy(ijk).cuda(), off)
+    empty = binding.tc_batch_from_ijk(torch.zeros((0, 3), dtype=torch.int32).cuda(), np.array([0, 0]))
+    ops = MANY_OPS + [("coarsen", 4), ("dilate", 1)]
+    batches = binding.tc_build_batched_topology_many(src, ops) + [empty, src]
+    singles = [binding.tc_enumerate_ijk(b).cpu().numpy() for b in batches]
+    many = binding.tc_enumerate_ijk_many(batches)
+    assert len(many) == len(batches)
+    for j, (a, b) in enumerate(zip(many, singles)):
+        assert np.array_equal(a.cpu().numpy(), b), f"batch {j}"
+    # unaligned outputs (scalar stores): rows 1 past a 16-byte boundary
+    totals = [int(b.voxel_total()) for b in batches]
+    bufs = [torch.full((t + 2, 3), -7, dtype=torch.int32, device="cuda") for t in totals]
+    n = len(batches)
+    outs = (ctypes.c_void_p * n)(*[bf.data_ptr() + 12 for bf in bufs])
+    caps = (ctypes.c_int64 * n)(*totals)
+    hs = (ctypes.c_void_p * n)(*[b.handle.value for b in batches])
+    assert lib.tc_enumerate_ijk_many(n, hs, outs, caps, None) == binding.TC_OK, lib.tc_last_error()
+    torch.cuda.synchronize()
+    for j, (bf, ref) in enumerate(zip(bufs, singles)):
+        got = bf.cpu().numpy()
+        assert np.array_equal(got[1:1 + totals[j]], ref), f"unaligned batch {j}"
+        assert (got[0] == -7).all() and (got[1 + totals[j]:] == -7).all(), f"batch {j} wrote outside its rows"
+    caps_small = (ctypes.c_int64 * n)(*[max(t - 1, 0) for t in totals])
+    assert lib.tc_enumerate_ijk_many(n, hs, outs, caps_small, None) == binding.TC_ERR_INVALID_ARG

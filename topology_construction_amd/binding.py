@@ -29,7 +29,7 @@ ABI_SYMBOLS = [
     "tc_build_batched_topology", "tc_build_masked_refine", "tc_batch_get_info", "tc_batch_read_headers",
     "tc_batch_voxel_total", "tc_enumerate_ijk", "tc_build_kernel_map", "tc_scratch_release", "tc_batch_free",
     "tc_debug_inject_flags", "tc_build_kernel_map_noalloc", "tc_profile_enable", "tc_profile_read",
-    "tc_profile_disable", "tc_build_batched_topology_many",
+    "tc_profile_disable", "tc_build_batched_topology_many", "tc_enumerate_ijk_many",
 ]
 
 HEADER_DTYPE = np.dtype([
@@ -118,6 +118,8 @@ def load_library(path: str = LIB_PATH):
         lib.tc_build_batched_topology.argtypes = [vp, i32, i32, vp, vp, ctypes.POINTER(vp)]
         lib.tc_build_batched_topology_many.restype = ctypes.c_int
         lib.tc_build_batched_topology_many.argtypes = [vp, i32, vp, vp, vp, vp, vp]
+        lib.tc_enumerate_ijk_many.restype = ctypes.c_int
+        lib.tc_enumerate_ijk_many.argtypes = [i32, vp, vp, vp, vp]
         lib.tc_build_masked_refine.restype = ctypes.c_int
         lib.tc_build_masked_refine.argtypes = [vp, vp, i64, i32, vp, vp, ctypes.POINTER(vp)]
         lib.tc_batch_get_info.restype = ctypes.c_int
@@ -401,6 +403,31 @@ def tc_enumerate_ijk(batch: GridBatch, out=None, stream=None):
     _check(lib.tc_enumerate_ijk(batch.handle, ctypes.c_void_p(out.data_ptr() if out.numel() else 0), int(cap),
                                 _stream_handle(stream)))
     return out[:total]
+
+
+def tc_enumerate_ijk_many(batches, stream=None) -> list:
+    """Jagged voxel enumerations of several batches in one launch: one int32
+    [V_j, 3] view per batch into one allocation (each view starting on a
+    16-byte boundary)."""
+    import torch
+    lib = load_library()
+    batches = list(batches)
+    n = len(batches)
+    if n < 1:
+        raise ValueError("batches is empty")
+    totals = [b.voxel_total(stream) for b in batches]
+    starts, at = [], 0
+    for t in totals:
+        starts.append(at)
+        at += (t + 3) // 4 * 4  # rows of 12 bytes: a multiple of 4 rows keeps 16-byte alignment
+    buf = torch.empty((max(at, 1), 3), dtype=torch.int32, device="cuda")
+    base = buf.data_ptr()
+    outs = (ctypes.c_void_p * n)(*[base + 12 * a if t else 0 for a, t in zip(starts, totals)])
+    caps = (ctypes.c_int64 * n)(*totals)
+    hs = (ctypes.c_void_p * n)(*[b.handle.value if isinstance(b.handle, ctypes.c_void_p) else b.handle
+                                 for b in batches])
+    _check(lib.tc_enumerate_ijk_many(n, hs, outs, caps, _stream_handle(stream)))
+    return [buf[a:a + t] for a, t in zip(starts, totals)]
 
 
 def tc_build_kernel_map(src: GridBatch, dst: GridBatch, kernel_size: int, stride: int, transposed: bool,

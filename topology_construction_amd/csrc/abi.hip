@@ -653,6 +653,36 @@ tc_status tc_enumerate_ijk(const tc_grid_batch* b, int32_t* d_ijk_out, int64_t c
   });
 }
 
+tc_status tc_enumerate_ijk_many(int32_t n, const tc_grid_batch* const* batches, int32_t* const* d_ijk_outs,
+                                const int64_t* capacities, void* stream) {
+  if (n < 1) return fail(TC_ERR_INVALID_ARG, "n must be >= 1");
+  if (!batches || !d_ijk_outs || !capacities) return fail(TC_ERR_INVALID_ARG, "NULL argument");
+  for (int32_t j = 0; j < n; ++j)
+    if (!batches[j]) return fail(TC_ERR_INVALID_ARG, "batch " + std::to_string(j) + " is NULL");
+  return guarded([&]() {
+    hipStream_t s = (hipStream_t)stream;
+    const int dev = current_device();
+    std::vector<tc::GridView> views;
+    std::vector<int32_t*> outs;
+    views.reserve(n);
+    outs.reserve(n);
+    for (int32_t j = 0; j < n; ++j) {
+      const tc_grid_batch* b = batches[j];
+      if (b->device != dev) throw tc::Error(TC_ERR_INVALID_ARG, "batch " + std::to_string(j) + " lives on another device");
+      const int64_t total = tc::read_voxel_total(b, s);
+      if (total == 0) continue;
+      if (!d_ijk_outs[j]) throw tc::Error(TC_ERR_INVALID_ARG, "d_ijk_outs[" + std::to_string(j) + "] is NULL");
+      if (capacities[j] < total)
+        throw tc::Error(TC_ERR_INVALID_ARG, "capacity " + std::to_string(capacities[j]) + " < voxel total " +
+                                                std::to_string(total) + " of batch " + std::to_string(j));
+      views.push_back(b->view());
+      outs.push_back(d_ijk_outs[j]);
+    }
+    if (!views.empty()) tc::tree_enumerate_many(views.data(), outs.data(), (int)views.size(), s);
+    return TC_OK;
+  });
+}
+
 tc_status tc_build_kernel_map(const tc_grid_batch* src, const tc_grid_batch* dst, int32_t kernel_size,
                               int32_t stride, int32_t transposed, int32_t* d_out, int64_t capacity,
                               void* stream) {

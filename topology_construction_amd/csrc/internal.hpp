@@ -365,6 +365,8 @@ void tree_finalize_leaves(const GridView& out, const uint32_t* leaf_box, const i
 // Whether the one-launch finalize takes L leaves (or a capacity of L) of B grids.
 bool finalize_small_fits(i64 L, int32_t B, i64 gran);
 void tree_enumerate(const GridView& v, int32_t* ijk, hipStream_t s);
+// tree_enumerate of n batches (output ijk[j] for batch j), up to eight per launch.
+void tree_enumerate_many(const GridView* v, int32_t* const* ijk, int n, hipStream_t s);
 
 // Allocation of the single output buffer of a batch.
 struct OutAlloc {

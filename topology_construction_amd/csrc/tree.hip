@@ -1179,14 +1179,33 @@ void tree_finalize_leaves(const GridView& out, const uint32_t* leaf_box, const i
 constexpr int kEnumMaxLeaves = 8;
 constexpr int kEnumLdsGrids = 256;  // up to this many grids, voxel begins come from LDS
 
-__global__ void __launch_bounds__(256) k_enumerate(const tc_grid_header* hdr, const int4* leaf_origin,
-                                                   const u64* leaf_mask, const i64* leaf_offset, int32_t* ijk,
-                                                   i64 n_leaf, int32_t B, int lpw, int vec_ok) {
-  __shared__ __align__(16) int32_t s_rows[4][3 * 512 + 4];
-  __shared__ i64 s_vb[kEnumLdsGrids];  // grids' voxel begins, loaded beside the leaves
+// Kernel argument of k_enumerate_many: up to kEnumMany batches.
+constexpr int kEnumMany = 8;
+struct EnumBatch {
+  const tc_grid_header* hdr;
+  const int4* leaf_origin;
+  const u64* leaf_mask;
+  const i64* leaf_offset;
+  int32_t* ijk;
+  i64 n_leaf;
+  int32_t B;
+  int32_t vec_ok;
+};
+struct EnumBatches {
+  EnumBatch b[kEnumMany];
+  i64 block_begin[kEnumMany];
+  int32_t n;
+  int32_t lpw;
+};
+
+// One block's share (block `blk` of the batch's launch shape) of k_enumerate.
+__device__ __forceinline__ void enumerate_block(const tc_grid_header* hdr, const int4* leaf_origin,
+                                                const u64* leaf_mask, const i64* leaf_offset, int32_t* ijk,
+                                                i64 n_leaf, int32_t B, int lpw, int vec_ok, i64 blk,
+                                                int32_t (*s_rows)[3 * 512 + 4], i64* s_vb) {
   const int w = threadIdx.x / kWave;
   const int lane = threadIdx.x & (kWave - 1);
-  const i64 l0 = ((i64)blockIdx.x * 4 + w) * lpw;
+  const i64 l0 = (blk * 4 + w) * lpw;
   const int nl = (int)max((i64)0, min((i64)lpw, n_leaf - l0));
   const int jl = lane >> 3;
   const u64 myword = jl < nl ? leaf_mask[(l0 + jl) * 8 + (lane & 7)] : 0ull;
@@ -1252,14 +1271,67 @@ __global__ void __launch_bounds__(256) k_enumerate(const tc_grid_header* hdr, co
   }
 }
 
+__global__ void __launch_bounds__(256) k_enumerate(const tc_grid_header* hdr, const int4* leaf_origin,
+                                                   const u64* leaf_mask, const i64* leaf_offset, int32_t* ijk,
+                                                   i64 n_leaf, int32_t B, int lpw, int vec_ok) {
+  __shared__ __align__(16) int32_t s_rows[4][3 * 512 + 4];
+  __shared__ i64 s_vb[kEnumLdsGrids];  // grids' voxel begins, loaded beside the leaves
+  enumerate_block(hdr, leaf_origin, leaf_mask, leaf_offset, ijk, n_leaf, B, lpw, vec_ok, blockIdx.x, s_rows, s_vb);
+}
+
+// Several batches in one launch: the blocks of batch j follow those of batch
+// j - 1 (block_begin, by value); every block finds its batch among at most
+// kEnumMany and runs that batch's share. One launch fills the chip where a
+// small batch alone would not, and saves the launches.
+__global__ void __launch_bounds__(256) k_enumerate_many(EnumBatches eb) {
+  __shared__ __align__(16) int32_t s_rows[4][3 * 512 + 4];
+  __shared__ i64 s_vb[kEnumLdsGrids];
+  int j = 0;
+#pragma unroll
+  for (int q = 1; q < kEnumMany; ++q) j += q < eb.n && (i64)blockIdx.x >= eb.block_begin[q] ? 1 : 0;
+  const EnumBatch& b = eb.b[j];
+  enumerate_block(b.hdr, b.leaf_origin, b.leaf_mask, b.leaf_offset, b.ijk, b.n_leaf, b.B, eb.lpw, b.vec_ok,
+                  (i64)blockIdx.x - eb.block_begin[j], s_rows, s_vb);
+}
+
+// one leaf per wave while the waves fit in one round of the chip (about 6k
+// resident at this LDS use), then two, then eight on large batches
+static int enumerate_lpw(i64 n_leaf) { return n_leaf >= 256 * 1024 ? kEnumMaxLeaves : (n_leaf >= 6 * 1024 ? 2 : 1); }
+
 void tree_enumerate(const GridView& v, int32_t* ijk, hipStream_t s) {
   const int vec_ok = (reinterpret_cast<uintptr_t>(ijk) & 15) == 0 ? 1 : 0;
-  // one leaf per wave while the waves fit in one round of the chip (about 6k
-  // resident at this LDS use), then two, then eight on large batches
-  const int lpw = v.n_leaf >= 256 * 1024 ? kEnumMaxLeaves : (v.n_leaf >= 6 * 1024 ? 2 : 1);
+  const int lpw = enumerate_lpw(v.n_leaf);
   launch("k_enumerate", k_enumerate, ceil_div((i64)v.n_leaf, 4 * lpw), 256, s,
          (const tc_grid_header*)v.headers, (const int4*)v.leaf_origin, (const u64*)v.leaf_mask,
          (const i64*)v.leaf_offset, ijk, (i64)v.n_leaf, v.B, lpw, vec_ok);
+}
+
+void tree_enumerate_many(const GridView* v, int32_t* const* ijk, int n, hipStream_t s) {
+  for (int j0 = 0; j0 < n; j0 += kEnumMany) {
+    const int m = std::min(kEnumMany, n - j0);
+    i64 leaves = 0;
+    for (int j = 0; j < m; ++j) leaves += v[j0 + j].n_leaf;
+    EnumBatches eb{};
+    eb.n = m;
+    eb.lpw = enumerate_lpw(leaves);  // one launch shape for the whole launch
+    i64 blocks = 0;
+    for (int j = 0; j < m; ++j) {
+      const GridView& g = v[j0 + j];
+      EnumBatch& b = eb.b[j];
+      b.hdr = g.headers;
+      b.leaf_origin = g.leaf_origin;
+      b.leaf_mask = g.leaf_mask;
+      b.leaf_offset = g.leaf_offset;
+      b.ijk = ijk[j0 + j];
+      b.n_leaf = g.n_leaf;
+      b.B = g.B;
+      b.vec_ok = (reinterpret_cast<uintptr_t>(b.ijk) & 15) == 0 ? 1 : 0;
+      eb.block_begin[j] = blocks;
+      blocks += ceil_div((i64)g.n_leaf, 4 * eb.lpw);
+    }
+    for (int j = m; j < kEnumMany; ++j) eb.block_begin[j] = blocks;
+    launch("k_enumerate", k_enumerate_many, blocks, 256, s, eb);
+  }
 }
 
 }  // namespace tc

@@ -229,16 +229,41 @@ class GridBatch:
         self._lib = load_library()
         self.handle = handle
         self.torch_owned = torch_owned
-        info = tc_batch_info()
-        _check(self._lib.tc_batch_get_info(handle, ctypes.byref(info)))
-        self.grid_count = info.grid_count
-        self.upper_count = info.upper_count
-        self.lower_count = info.lower_count
-        self.leaf_count = info.leaf_count
-        self._info = info
+        self._info_cache = None  # tc_batch_info, read on first use
         self._counts = None  # per-grid host counts, copied on first use
         self._total = None  # voxel total, once read
-        self._buffer = _live_buffers.get(int(info.d_buffer or 0)) if torch_owned else None
+        self._buffer_cache = None
+
+    @property
+    def _info(self):
+        if self._info_cache is None:
+            info = tc_batch_info()
+            _check(self._lib.tc_batch_get_info(self.handle, ctypes.byref(info)))
+            self._info_cache = info
+            if self.torch_owned:
+                self._buffer_cache = _live_buffers.get(int(info.d_buffer or 0))
+        return self._info_cache
+
+    @property
+    def _buffer(self):
+        self._info  # noqa: B018 (reads the info, which finds the buffer)
+        return self._buffer_cache
+
+    @property
+    def grid_count(self) -> int:
+        return self._info.grid_count
+
+    @property
+    def upper_count(self) -> int:
+        return self._info.upper_count
+
+    @property
+    def lower_count(self) -> int:
+        return self._info.lower_count
+
+    @property
+    def leaf_count(self) -> int:
+        return self._info.leaf_count
 
     def _grid_counts(self):
         if self._counts is None:

@@ -12,8 +12,11 @@ Prints one JSON line (rank 0). `value` = output voxels per second over the K
 timed steps. `roofline` reports the dominant kernel's algorithmic bytes per
 launch over its HIP-event-timed average duration in those steps (and, beside
 it, the same over its kernel-trace duration from the committed profile);
-`ms_per_step_unprofiled` repeats the K steps without those events, and
-`ms_per_step_one_call_per_op` with one build call per op.
+`ms_per_step_unprofiled` repeats the K steps without those events,
+`ms_per_step_one_call_per_op` with one build call per op, and
+`ms_per_step_torch_allocator` with torch's caching allocator supplying the
+outputs (the step itself takes them from the library's pool, the C ABI's
+default).
 `cpu_baseline` times the CPU oracle on whole steps of the same workload, its
 members spread over the host's threads (single-thread and 46M-voxel figures
 beside it). Outside the timed steps the line also carries per-op medians
@@ -186,17 +189,19 @@ def progress(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def run_step(binding, src, outs=None, one_call=True):
+def run_step(binding, src, outs=None, one_call=True, allocator="none"):
     """One step: every op's target, then each target's voxel enumeration. With
     `one_call` the targets come from one tc_build_batched_topology_many call and
     their enumerations from one tc_enumerate_ijk_many launch, else from one
-    tc_build_batched_topology and one tc_enumerate_ijk call per op. Returns
-    voxels."""
+    tc_build_batched_topology and one tc_enumerate_ijk call per op. `allocator`
+    "none" takes the outputs from the library's own stream-ordered pool (the C
+    ABI's default, a NULL allocator), "torch" from torch's caching allocator
+    through the binding's callback. Returns voxels."""
     total = 0
     if one_call:
-        built = binding.tc_build_batched_topology_many(src, STEP_OPS)
+        built = binding.tc_build_batched_topology_many(src, STEP_OPS, allocator=allocator)
     else:
-        built = [binding.tc_build_batched_topology(src, op, f) for op, f in STEP_OPS]
+        built = [binding.tc_build_batched_topology(src, op, f, allocator=allocator) for op, f in STEP_OPS]
     if one_call:
         ijks = binding.tc_enumerate_ijk_many(built)
     else:
@@ -483,6 +488,15 @@ def main():
         run_step(binding, src, one_call=False)
     torch.cuda.synchronize()
     ms_step_single = (time.perf_counter() - t2) * 1e3 / args.steps
+    # and with torch's caching allocator supplying the outputs (a ctypes callback each)
+    for _ in range(args.warmup):
+        run_step(binding, src, allocator="torch")
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for _ in range(args.steps):
+        run_step(binding, src, allocator="torch")
+    torch.cuda.synchronize()
+    ms_step_torch = (time.perf_counter() - t2) * 1e3 / args.steps
 
     # per-op breakdown (separate, untimed-by-the-step loop): pass and enumeration
     progress(f"timed steps done: {ms_step:.4f} ms per step")
@@ -557,7 +571,7 @@ def main():
     rec = {
         "metric": METRIC, "value": voxels / elapsed, "unit": "voxels/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_step, "ms_per_step_unprofiled": ms_step_plain,
-        "ms_per_step_one_call_per_op": ms_step_single,
+        "ms_per_step_one_call_per_op": ms_step_single, "ms_per_step_torch_allocator": ms_step_torch,
         "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "int32", "data": "synthetic",
         "config": {"workload": synth.CONFIG_NAMES[args.config], "grids": int(len(off) - 1),

@@ -1168,14 +1168,18 @@ void tree_finalize_leaves(const GridView& out, const uint32_t* leaf_box, const i
 }
 
 // ------------------------------------------------------------------ enumeration
-// One wave walks `lpw` (1..8) consecutive leaves. Their masks, origins and voxel
-// offsets are loaded once, up front, while the block stages the grids' voxel
-// begins in LDS (so no load waits on a leaf's grid index); many leaves per wave amortise the load
-// latency on large batches, one leaf per wave keeps small batches wide. For each leaf, lane r owns row r = x*8 + y
-// (byte y of word x, at most 8 voxels along z); a wave scan of the row popcounts
-// places every row, lanes expand their rows into LDS in bit order, and the wave
-// streams the leaf's rows out with 16-byte stores (the LDS image is shifted so
-// that its 16-byte chunks line up with the destination's).
+// One wave walks `lpw` (1..8) consecutive leaves. Their masks, prefix words,
+// origins and voxel offsets are loaded once, up front, while the block stages
+// the grids' voxel begins in LDS (so no load waits on a leaf's grid index); many
+// leaves per wave amortise the load latency on large batches, one leaf per wave
+// keeps small batches wide. For each leaf, lane r owns row r = x*8 + y (byte y
+// of word x, at most 8 voxels along z). The row's first voxel is the leaf's
+// prefix field for the words before x plus the set bits of word x before byte
+// y, so no cross-lane scan is needed; lanes expand their rows into LDS in bit
+// order, and the wave streams the leaf's rows out with 16-byte non-temporal
+// stores (the output is not read back by this kernel; the LDS image is shifted
+// so that its 16-byte chunks line up with the destination's). The wave index is
+// made uniform, so the per-leaf values of the loop come from lane reads.
 constexpr int kEnumMaxLeaves = 8;
 constexpr int kEnumLdsGrids = 256;  // up to this many grids, voxel begins come from LDS
 
@@ -1185,6 +1189,7 @@ struct EnumBatch {
   const tc_grid_header* hdr;
   const int4* leaf_origin;
   const u64* leaf_mask;
+  const u64* leaf_prefix;
   const i64* leaf_offset;
   int32_t* ijk;
   i64 n_leaf;
@@ -1198,12 +1203,21 @@ struct EnumBatches {
   int32_t lpw;
 };
 
+typedef int v4i32 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ i64 readlane64(i64 v, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)((u64)v >> 32), l);
+  return (i64)(((u64)hi << 32) | lo);
+}
+
 // One block's share (block `blk` of the batch's launch shape) of k_enumerate.
 __device__ __forceinline__ void enumerate_block(const tc_grid_header* hdr, const int4* leaf_origin,
-                                                const u64* leaf_mask, const i64* leaf_offset, int32_t* ijk,
-                                                i64 n_leaf, int32_t B, int lpw, int vec_ok, i64 blk,
-                                                int32_t (*s_rows)[3 * 512 + 4], i64* s_vb) {
-  const int w = threadIdx.x / kWave;
+                                                const u64* leaf_mask, const u64* leaf_prefix,
+                                                const i64* leaf_offset, int32_t* ijk, i64 n_leaf, int32_t B,
+                                                int lpw, int vec_ok, i64 blk, int32_t (*s_rows)[3 * 512 + 4],
+                                                i64* s_vb) {
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x & (kWave - 1);
   const i64 l0 = (blk * 4 + w) * lpw;
   const int nl = (int)max((i64)0, min((i64)lpw, n_leaf - l0));
@@ -1211,9 +1225,11 @@ __device__ __forceinline__ void enumerate_block(const tc_grid_header* hdr, const
   const u64 myword = jl < nl ? leaf_mask[(l0 + jl) * 8 + (lane & 7)] : 0ull;
   int4 myo = make_int4(0, 0, 0, 0);
   i64 myoff = 0;
+  u64 mypre = 0;
   if (lane < nl) {
     myo = leaf_origin[l0 + lane];
     myoff = leaf_offset[l0 + lane];
+    mypre = leaf_prefix[l0 + lane];
   }
   const bool lds_vb = B <= kEnumLdsGrids;  // uniform
   if (lds_vb) {
@@ -1225,21 +1241,26 @@ __device__ __forceinline__ void enumerate_block(const tc_grid_header* hdr, const
   if (lane < nl) mybase = (lds_vb ? s_vb[myo.w] : hdr[myo.w].voxel_begin) + myoff;
   int32_t* rows = s_rows[w];
   const int x = lane >> 3, y = lane & 7;
+  const u64 below = (1ull << (8 * y)) - 1;  // the bits of word x before row y
   for (int j = 0; j < nl; ++j) {
     const u64 word = __shfl(myword, j * 8 + x, kWave);
-    const int ox = __shfl(myo.x, j, kWave), oy = __shfl(myo.y, j, kWave), oz = __shfl(myo.z, j, kWave);
-    const i64 base = __shfl(mybase, j, kWave);
-    const u64 row = (word >> (8 * y)) & 0xffull;
-    const int cnt = __popcll(row);
-    const int inc = wave_incl_scan(cnt);
-    const int total = __shfl(inc, kWave - 1, kWave);
+    const int ox = __builtin_amdgcn_readlane(myo.x, j), oy = __builtin_amdgcn_readlane(myo.y, j),
+              oz = __builtin_amdgcn_readlane(myo.z, j);
+    const i64 base = readlane64(mybase, j);
+    const u64 pre = (u64)readlane64((i64)mypre, j);
+    const uint32_t row = (uint32_t)(word >> (8 * y)) & 0xffu;
+    // voxels before this row: in the words before x (prefix field x - 1), then in word x
+    const int pw = x == 0 ? 0 : (int)((pre >> (9 * (x - 1))) & 511u);
+    const int ex = pw + popc64(word & below);
+    const int total = __builtin_amdgcn_readlane(ex + __popc(row), kWave - 1);  // lane 63: the last row
     const int a = vec_ok ? (int)((base * 3) & 3) : 0;
-    int at = a + 3 * (inc - cnt);
-    u64 rest = row;
+    int at = a + 3 * ex;
+    const int X = ox + x, Y = oy + y;
+    uint32_t rest = row;
     while (rest) {
-      const int z = __builtin_ctzll(rest);
-      rows[at + 0] = ox + x;
-      rows[at + 1] = oy + y;
+      const int z = __builtin_ctz(rest);
+      rows[at + 0] = X;
+      rows[at + 1] = Y;
       rows[at + 2] = oz + z;
       rest &= rest - 1;
       at += 3;
@@ -1250,20 +1271,32 @@ __device__ __forceinline__ void enumerate_block(const tc_grid_header* hdr, const
     const int n = a + 3 * total;
     int32_t* dst = ijk + base * 3 - a;  // 16-byte aligned when vec_ok
     if (vec_ok) {
-      int4* dst4 = reinterpret_cast<int4*>(dst);
-      const int4* src4 = reinterpret_cast<const int4*>(rows);
-      for (int q = lane; q < ((n + 3) >> 2); q += kWave) {
-        const int e0 = q * 4;
-        if (e0 >= a && e0 + 4 <= n) {
-          dst4[q] = src4[q];
-        } else {
+      v4i32* dst4 = reinterpret_cast<v4i32*>(dst);
+      const v4i32* src4 = reinterpret_cast<const v4i32*>(rows);
+      const int nq = (n + 3) >> 2;
+      for (int q0 = 0; q0 < nq; q0 += 2 * kWave) {
+        v4i32 v[2];
 #pragma unroll
-          for (int t = 0; t < 4; ++t)
-            if (e0 + t >= a && e0 + t < n) dst[e0 + t] = rows[e0 + t];
+        for (int u = 0; u < 2; ++u) {
+          const int q = q0 + u * kWave + lane;
+          if (q < nq) v[u] = src4[q];
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int q = q0 + u * kWave + lane;
+          const int e0 = q * 4;
+          if (q >= nq) continue;
+          if (e0 >= a && e0 + 4 <= n) {
+            __builtin_nontemporal_store(v[u], dst4 + q);
+          } else {
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+              if (e0 + t >= a && e0 + t < n) __builtin_nontemporal_store(v[u][t], dst + e0 + t);
+          }
         }
       }
     } else {
-      for (int e = lane; e < n; e += kWave) dst[e] = rows[e];
+      for (int e = lane; e < n; e += kWave) __builtin_nontemporal_store(rows[e], dst + e);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -1272,11 +1305,13 @@ __device__ __forceinline__ void enumerate_block(const tc_grid_header* hdr, const
 }
 
 __global__ void __launch_bounds__(256) k_enumerate(const tc_grid_header* hdr, const int4* leaf_origin,
-                                                   const u64* leaf_mask, const i64* leaf_offset, int32_t* ijk,
-                                                   i64 n_leaf, int32_t B, int lpw, int vec_ok) {
+                                                   const u64* leaf_mask, const u64* leaf_prefix,
+                                                   const i64* leaf_offset, int32_t* ijk, i64 n_leaf, int32_t B,
+                                                   int lpw, int vec_ok) {
   __shared__ __align__(16) int32_t s_rows[4][3 * 512 + 4];
   __shared__ i64 s_vb[kEnumLdsGrids];  // grids' voxel begins, loaded beside the leaves
-  enumerate_block(hdr, leaf_origin, leaf_mask, leaf_offset, ijk, n_leaf, B, lpw, vec_ok, blockIdx.x, s_rows, s_vb);
+  enumerate_block(hdr, leaf_origin, leaf_mask, leaf_prefix, leaf_offset, ijk, n_leaf, B, lpw, vec_ok, blockIdx.x,
+                  s_rows, s_vb);
 }
 
 // Several batches in one launch: the blocks of batch j follow those of batch
@@ -1290,8 +1325,8 @@ __global__ void __launch_bounds__(256) k_enumerate_many(EnumBatches eb) {
 #pragma unroll
   for (int q = 1; q < kEnumMany; ++q) j += q < eb.n && (i64)blockIdx.x >= eb.block_begin[q] ? 1 : 0;
   const EnumBatch& b = eb.b[j];
-  enumerate_block(b.hdr, b.leaf_origin, b.leaf_mask, b.leaf_offset, b.ijk, b.n_leaf, b.B, eb.lpw, b.vec_ok,
-                  (i64)blockIdx.x - eb.block_begin[j], s_rows, s_vb);
+  enumerate_block(b.hdr, b.leaf_origin, b.leaf_mask, b.leaf_prefix, b.leaf_offset, b.ijk, b.n_leaf, b.B, eb.lpw,
+                  b.vec_ok, (i64)blockIdx.x - eb.block_begin[j], s_rows, s_vb);
 }
 
 // one leaf per wave while the waves fit in one round of the chip (about 6k
@@ -1303,7 +1338,7 @@ void tree_enumerate(const GridView& v, int32_t* ijk, hipStream_t s) {
   const int lpw = enumerate_lpw(v.n_leaf);
   launch("k_enumerate", k_enumerate, ceil_div((i64)v.n_leaf, 4 * lpw), 256, s,
          (const tc_grid_header*)v.headers, (const int4*)v.leaf_origin, (const u64*)v.leaf_mask,
-         (const i64*)v.leaf_offset, ijk, (i64)v.n_leaf, v.B, lpw, vec_ok);
+         (const u64*)v.leaf_prefix, (const i64*)v.leaf_offset, ijk, (i64)v.n_leaf, v.B, lpw, vec_ok);
 }
 
 void tree_enumerate_many(const GridView* v, int32_t* const* ijk, int n, hipStream_t s) {
@@ -1321,6 +1356,7 @@ void tree_enumerate_many(const GridView* v, int32_t* const* ijk, int n, hipStrea
       b.hdr = g.headers;
       b.leaf_origin = g.leaf_origin;
       b.leaf_mask = g.leaf_mask;
+      b.leaf_prefix = g.leaf_prefix;
       b.leaf_offset = g.leaf_offset;
       b.ijk = ijk[j0 + j];
       b.n_leaf = g.n_leaf;

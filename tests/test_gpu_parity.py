@@ -235,6 +235,26 @@ def test_box_ops_voxels_on_node_faces(op, f):
         _check(op, f, ijk, off, f"faces batch {n}")
 
 
+def _solid_members():
+    """Dense sources: solid cubes of 8^3 full leaves against the low and the high
+    faces of a lower (its interior leaves and its face leaves next to outside
+    positions), a solid cube across lower and root-tile boundaries at negative
+    coordinates, a two-voxel slab, and an empty member."""
+    g = np.mgrid[0:120, 0:120, 0:2].reshape(3, -1).T
+    slab = (g + np.array([-100, 37, 5])).astype(np.int32)
+    return synth.concat_members([synth.cube_voxels(64, (0, 0, 0)), synth.cube_voxels(64, (64, 64, 64)),
+                                 np.zeros((0, 3), np.int32), synth.cube_voxels(40, (-4115, -20, 4080)), slab])
+
+
+@pytest.mark.parametrize("op,f", [("dilate", 1), ("pad_neg", 1), ("pad_pos", 1)])
+def test_box_ops_solid_sources(op, f):
+    """Box ops on dense sources: a lower whose leaves are all present (its
+    interior leaves spill only onto marked positions), dense runs of candidates
+    and faces of full neighbours (PR page, section 2: box-dilate and pads)."""
+    ijk, off = _solid_members()
+    _check(op, f, ijk, off, "solid")
+
+
 @pytest.mark.parametrize("op", ["conv_s1", "conv_t_s1"])
 @pytest.mark.parametrize("k", [2, 4, 5])
 def test_kernel_k_voxels_on_node_faces(op, k):

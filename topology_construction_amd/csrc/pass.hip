@@ -24,6 +24,8 @@
 //           (at most 1 / 8 / 27) source leaves that feed it (no atomics); a
 //           consistency check that fails there sets a flag word that is read
 //           back with the batch's voxel total.
+#include <atomic>
+
 #include "device.hpp"
 #include "internal.hpp"
 
@@ -1361,16 +1363,17 @@ __global__ void __launch_bounds__(256) k_mark_coarsen(const int32_t* cand_src, c
 }
 
 // ------------------------------------------------------------------ stage: leaves, box ops (pull)
-// Box ops mark from the target side: workgroup b takes candidate lowers C = b,
-// b + G, ... (G workgroups; usually one candidate each). C's
+// Box ops mark from the target side: one resident round of workgroups, each
+// looping over its candidate lowers C (the next one's loads in flight). C's
 // sources are the source lowers at C + d, d in {-1,0,1}^3; from the one at
 // offset d only the leaves on the face / edge / corner that touches C can reach
 // it (offset t = -d on each axis where d is non-zero). The workgroup stages the
 // mask words that hold such leaves and a block scan of their counts in LDS;
-// every thread then takes leaves a few at a time (finding each leaf's word by
-// binary search over the scan), tests which offsets of the box spill voxels
-// into C and ORs the target bits into an LDS copy of C's 16^3 leaf mask, which
-// is stored whole at the end: no device atomics on the masks and no zero fill.
+// every thread then takes one leaf at a time (its word from an LDS map of the
+// scan, or a binary search over it past the map), tests which offsets of the
+// box spill voxels into C and ORs the target bits into an LDS copy of C's 16^3
+// leaf mask, which is stored whole at the end: no device atomics on the masks
+// and no zero fill.
 constexpr int kPullItems = 27 * 64;  // (source slot, mask word) pairs
 
 __host__ __device__ constexpr u64 face_word_mask(int js, int w, int lo, int hi) {
@@ -1444,34 +1447,37 @@ __device__ __forceinline__ void mark_box_leaf(const u64 W[8], uint32_t pos, int 
   }
 }
 
-constexpr int kMarkIlp = 2;  // leaves in flight per thread
+constexpr int kMarkIlp = 1;  // leaves in flight per thread
 
-// Erosion of a lower's 16^3 leaf mask by the box [lo, hi]^3 inside the lower:
-// bit p stays set when p + t is set for every t in the box (positions whose
-// box reaches outside the lower are dropped). Lane w of one wave holds word w
+// Erosion of a lower's 16^3 leaf mask by the box [lo, hi]^3, with positions
+// outside the lower counted as set: bit p stays set when p + t is set or lies
+// outside the lower for every t in the box. Lane w of one wave holds word w
 // (x = w >> 2, rows y = 4 (w & 3) .. +3, bit (y & 3) * 16 + z); every lane of
-// the wave must call it.
+// the wave must call it. The three axis passes run one after another (erosion
+// by a box is erosion by its three axis segments in turn).
 template <int lo, int hi>
 __device__ __forceinline__ u64 erode_lower_mask(u64 m) {
   const int w = threadIdx.x & (kWave - 1);
-  constexpr u64 kNoZ15 = 0x7fff7fff7fff7fffull, kNoZ0 = 0xfffefffefffefffeull;
+  constexpr u64 kZ15 = 0x8000800080008000ull, kZ0s = 0x0001000100010001ull;  // z = 15 / z = 0 of each row
   u64 e = m;  // z: neighbours z + 1 (bit above) and z - 1 (bit below) inside the row
-  if (hi > 0) e &= (m >> 1) & kNoZ15;
-  if (lo < 0) e &= (m << 1) & kNoZ0;
+  if (hi > 0) e &= (m >> 1) | kZ15;
+  if (lo < 0) e &= (m << 1) | kZ0s;
   // y: rows y + 1 / y - 1, across words for the rows at a word's edge
   const u64 up = (u64)__shfl_down((unsigned long long)e, 1, kWave);  // word w + 1
   const u64 dn = (u64)__shfl_up((unsigned long long)e, 1, kWave);    // word w - 1
   u64 f = e;
-  if (hi > 0) f &= (e >> 16) | ((w & 3) < 3 ? up << 48 : 0ull);
-  if (lo < 0) f &= (e << 16) | ((w & 3) > 0 ? dn >> 48 : 0ull);
+  if (hi > 0) f &= (e >> 16) | ((w & 3) < 3 ? up << 48 : 0xffff000000000000ull);
+  if (lo < 0) f &= (e << 16) | ((w & 3) > 0 ? dn >> 48 : 0xffffull);
   // x: words w + 4 / w - 4
   const u64 xp = (u64)__shfl_down((unsigned long long)f, 4, kWave);
   const u64 xm = (u64)__shfl_up((unsigned long long)f, 4, kWave);
   u64 g = f;
-  if (hi > 0) g &= (w >> 2) < 15 ? xp : 0ull;
-  if (lo < 0) g &= (w >> 2) > 0 ? xm : 0ull;
+  if (hi > 0) g &= (w >> 2) < 15 ? xp : ~0ull;
+  if (lo < 0) g &= (w >> 2) > 0 ? xm : ~0ull;
   return g;
 }
+
+constexpr int kMarkMap = 4096;  // reaching leaves whose live item a workgroup maps in LDS (more: binary search)
 
 template <int lo, int hi>  // the box [lo, hi]^3: dilate [-1, 1], pads [-1, 0] and [0, 1]
 __global__ void __launch_bounds__(256) k_leaf_mark_box(const int32_t* cand_src, const int32_t* d_num_cands,
@@ -1491,6 +1497,7 @@ __global__ void __launch_bounds__(256) k_leaf_mark_box(const int32_t* cand_src, 
   __shared__ u64 s_fm[kLiveMax];            // the item's mask of leaves to visit
   __shared__ u64 s_center[64];              // 16^3 mask of the co-located source lower
   __shared__ u64 s_skip[64];                // its leaves that spill onto marked positions only
+  __shared__ uint16_t s_map[kMarkMap];      // live item of each reaching leaf
   __shared__ int32_t s_wave[256 / kWave];
   const int tid = threadIdx.x;
   // An output coordinate leaves int32 exactly when a grid's bbox, widened by
@@ -1506,55 +1513,70 @@ __global__ void __launch_bounds__(256) k_leaf_mark_box(const int32_t* cand_src, 
     }
   }
   const i64 ncand = *d_num_cands;
-  // the first na workgroups (still spread round-robin over the XCDs) each take a
-  // contiguous share of the candidates, the shares of one XCD adjacent:
-  // neighbouring candidates read the same source lowers and leaves
-  const i64 na = ncand < (i64)gridDim.x ? ncand : (i64)gridDim.x;
-  const i64 per = na > 0 ? (ncand + na - 1) / na : 0;
-  const i64 c0 = (i64)blockIdx.x < na ? xcd_block(blockIdx.x, na) * per : ncand;
-  for (i64 c = c0; c < ncand && c < c0 + per; ++c) {
-    u64 wd[kLivePer];
-    int32_t base[kLivePer];
-    int cnt[kLivePer];
-    int item[kLivePer];
-    int sum = 0;
-    // every load at a valid index, all in flight together: the source slots,
-    // then the slots' mask words, first leaves and prefixes (slot 0 stands in
-    // for an empty slot; n_src_lower >= 1 whenever there are candidates)
-    int32_t sl[kLivePer];
+  // Candidates: the workgroups of XCD x (workgroup b runs on XCD b % 8; the
+  // launch is a multiple of 8 workgroups) take the x-th eighth of the
+  // candidates, interleaved over that range, so neighbouring candidates, which
+  // read the same source lowers and leaves, share one L2, and dense runs of
+  // candidates spread over the XCD's workgroups.
+  const int bpx = (int)(gridDim.x >> 3), xr = (int)(blockIdx.x & 7);
+  const i64 c_end = ncand * (xr + 1) / 8;
+  // this thread's live items (the same for every candidate)
+  int item[kLivePer];
+  u64 fm0[kLivePer];
+#pragma unroll
+  for (int k = 0; k < kLivePer; ++k) {
+    const int li = tid * kLivePer + k;
+    item[k] = tab.item[min(li, nlive - 1)];
+    fm0[k] = li < nlive ? face_word_mask(item[k] >> 6, item[k] & 63, lo, hi) : 0;
+  }
+  // A candidate's staging loads in two levels, the next candidate's issued
+  // while the current one is processed: its source lowers (slot 0 stands in for
+  // an empty slot; n_src_lower >= 1 whenever there are candidates), then their
+  // mask words, first leaves and prefixes.
+  auto load_src = [&](i64 c, int32_t* sl) {
 #pragma unroll
     for (int k = 0; k < kLivePer; ++k) {
-      item[k] = tab.item[min(tid * kLivePer + k, nlive - 1)];
-      sl[k] = cand_src[c * 27 + (item[k] >> 6)];
+      sl[k] = c < c_end && fm0[k] ? cand_src[c * 27 + (item[k] >> 6)] : -1;
+      if (sl[k] >= n_src_lower) {
+        set_flag(flags, kFlagInternal);
+        sl[k] = -1;
+      }
     }
-    u64 fm[kLivePer];
+  };
+  auto load_words = [&](const int32_t* sl, u64* wd, int32_t* base) {
     int32_t lfirst[kLivePer];
     uint16_t lpre[kLivePer];
 #pragma unroll
     for (int k = 0; k < kLivePer; ++k) {
-      const int js = item[k] >> 6, w = item[k] & 63;
-      fm[k] = tid * kLivePer + k < nlive ? face_word_mask(js, w, lo, hi) : 0;
-      if (fm[k] && sl[k] >= n_src_lower) {
-        set_flag(flags, kFlagInternal);
-        sl[k] = -1;
-      }
-      if (!fm[k]) sl[k] = -1;
       const i64 ls = sl[k] >= 0 ? sl[k] : 0;
-      wd[k] = src_lower_mask[ls * 64 + w];
+      wd[k] = src_lower_mask[ls * 64 + (item[k] & 63)];
       lfirst[k] = src_lower_first[ls];
-      lpre[k] = src_lower_prefix[ls * 64 + w];
+      lpre[k] = src_lower_prefix[ls * 64 + (item[k] & 63)];
     }
 #pragma unroll
     for (int k = 0; k < kLivePer; ++k) {
       if (sl[k] < 0) wd[k] = 0;
       base[k] = sl[k] >= 0 ? lfirst[k] + lpre[k] : 0;
-      if ((item[k] >> 6) == 13 && tid * kLivePer + k < nlive) s_center[item[k] & 63] = wd[k];
     }
+  };
+  i64 c = ncand * xr / 8 + (blockIdx.x >> 3);
+  int32_t sl[kLivePer];
+  u64 wd[kLivePer];
+  int32_t base[kLivePer];
+  load_src(c, sl);
+  load_words(sl, wd, base);
+  for (; c < c_end; c += bpx) {
+    int32_t sln[kLivePer];
+    load_src(c + bpx, sln);  // next candidate, first level
+#pragma unroll
+    for (int k = 0; k < kLivePer; ++k)
+      if ((item[k] >> 6) == 13 && tid * kLivePer + k < nlive) s_center[item[k] & 63] = wd[k];
     // The co-located source lower (slot 13, every word live) marks its own
     // leaf positions (the box holds offset 0 and a source leaf is never
-    // empty): its mask goes into the candidate's as is. Its leaves inside the
-    // mask eroded by the box spill only onto positions it already marks, so
-    // they are not visited.
+    // empty): its mask goes into the candidate's as is. A leaf of it whose box
+    // neighbours inside the candidate are all source leaves spills only onto
+    // positions already marked (or outside the candidate, which are other
+    // candidates' to mark), so the leaves of its eroded mask are not visited.
     __syncthreads();
     if (tid < 64) {  // wave 0
       const u64 m = s_center[tid];
@@ -1562,8 +1584,12 @@ __global__ void __launch_bounds__(256) k_leaf_mark_box(const int32_t* cand_src, 
       s_skip[tid] = erode_lower_mask<lo, hi>(m);
     }
     __syncthreads();
+    u64 fm[kLivePer];
+    int cnt[kLivePer];
+    int sum = 0;
 #pragma unroll
     for (int k = 0; k < kLivePer; ++k) {
+      fm[k] = fm0[k];
       if ((item[k] >> 6) == 13) fm[k] &= ~s_skip[item[k] & 63];
       cnt[k] = popc64(wd[k] & fm[k]);
       sum += cnt[k];
@@ -1579,11 +1605,14 @@ __global__ void __launch_bounds__(256) k_leaf_mark_box(const int32_t* cand_src, 
         s_excl[li] = ex;
         s_item[li] = (uint16_t)item[k];
         s_fm[li] = fm[k];
+        for (int j = ex, e = min(ex + cnt[k], kMarkMap); j < e; ++j) s_map[j] = (uint16_t)li;
       }
       ex += cnt[k];
     }
     if (tid == 0) s_excl[nlive] = total;
     __syncthreads();
+    // the next candidate's second level, in flight during this one's leaves
+    load_words(sln, wd, base);
     for (int k0 = 0; k0 < total; k0 += kMarkIlp * 256) {
       int32_t lf[kMarkIlp];
       uint32_t ps[kMarkIlp];
@@ -1593,11 +1622,17 @@ __global__ void __launch_bounds__(256) k_leaf_mark_box(const int32_t* cand_src, 
         lf[u] = -1;
         ps[u] = 0;
         if (k < total) {
-          int a = 0, z = nlive;  // largest live item with s_excl[item] <= k
-          while (z - a > 1) {
-            const int mid = (a + z) >> 1;
-            if (s_excl[mid] <= k) a = mid;
-            else z = mid;
+          int a;  // the live item holding reaching leaf k: largest with s_excl[item] <= k
+          if (k < kMarkMap) {
+            a = s_map[k];
+          } else {
+            int z = nlive;
+            a = 0;
+            while (z - a > 1) {
+              const int mid = (a + z) >> 1;
+              if (s_excl[mid] <= k) a = mid;
+              else z = mid;
+            }
           }
           const int js = s_item[a] >> 6, w = s_item[a] & 63;
           const u64 word = s_word[a];
@@ -1624,7 +1659,24 @@ __global__ void __launch_bounds__(256) k_leaf_mark_box(const int32_t* cand_src, 
     __syncthreads();
     if (tid < 64) store_candidate(c, s_mask[tid], cand_child, cand_prefix, cand_counts);  // wave 0
     __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kLivePer; ++k) sl[k] = sln[k];
   }
+}
+
+// Workgroups of k_leaf_mark_box<lo, hi> resident at once on the current device:
+// its CUs times the kernel's workgroups per CU (read once per instantiation).
+template <int lo, int hi>
+static i64 mark_box_resident() {
+  static std::atomic<int> per_cu{0};
+  int n = per_cu.load(std::memory_order_relaxed);
+  if (n <= 0) {
+    hip_check(hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_leaf_mark_box<lo, hi>, 256, 0),
+              "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+    n = n > 0 ? n : 1;
+    per_cu.store(n, std::memory_order_relaxed);
+  }
+  return (i64)device_cu_count() * n;
 }
 
 // ------------------------------------------------------------------ writers: leaf masks (pass B)
@@ -2208,7 +2260,10 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, 
              (const int32_t*)ts.d_num_cands, (const u64*)sv.lower_mask, sv.n_lower, ts.cand_child, ts.cand_prefix,
              ts.cand_counts, ts.flags);
     } else if (nL > 0) {  // no source lowers: nothing to mark and every bbox is empty
-      const i64 blocks = nL < 8192 ? nL : 8192;
+      // one resident round of workgroups (a multiple of 8), each looping over its candidates
+      const i64 resident = oi.lo < 0 && oi.hi > 0 ? mark_box_resident<-1, 1>()
+                           : (oi.lo < 0 ? mark_box_resident<-1, 0>() : mark_box_resident<0, 1>());
+      const i64 blocks = std::max<i64>(8, std::min(ceil_div(ts.cap_cands, 8), resident / 8) * 8);
       auto mark_box = oi.lo < 0 && oi.hi > 0 ? k_leaf_mark_box<-1, 1>
                       : (oi.lo < 0 ? k_leaf_mark_box<-1, 0> : k_leaf_mark_box<0, 1>);
       launch("k_leaf_mark_box", mark_box, blocks, 256, s, (const int32_t*)cand_src,

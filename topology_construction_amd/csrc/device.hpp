@@ -91,15 +91,15 @@ __device__ __forceinline__ int select_bit(uint64_t w, int r) {
 }
 
 // Quads (4 consecutive lanes): lane q of a quad reads lane p_q of the same
-// quad (DPP quad permutation). A DPP read from a lane that EXEC disables
-// yields 0, so the permutation must run with the whole quad active: the empty
-// volatile asm on its result keeps the compiler from moving it into a branch
-// taken by part of the quad (it would otherwise fold `cond ? x : perm(y)` into
-// a perm executed only by the lanes where cond is false). Call it from code
-// every lane of the quad executes.
+// quad (DPP quad permutation, no old value: one instruction). A DPP read from a
+// lane that EXEC disables is undefined, so the permutation must run with the
+// whole quad active: the empty volatile asm on its result keeps the compiler
+// from moving it into a branch taken by part of the quad (it would otherwise
+// fold `cond ? x : perm(y)` into a perm executed only by the lanes where cond
+// is false). Call it from code every lane of the quad executes.
 template <int p0, int p1, int p2, int p3>
 __device__ __forceinline__ int quad_perm32(int v) {
-  int r = __builtin_amdgcn_update_dpp(0, v, p0 | (p1 << 2) | (p2 << 4) | (p3 << 6), 0xf, 0xf, false);
+  int r = __builtin_amdgcn_mov_dpp(v, p0 | (p1 << 2) | (p2 << 4) | (p3 << 6), 0xf, 0xf, false);
   asm volatile("" : "+v"(r));
   return r;
 }

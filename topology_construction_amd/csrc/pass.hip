@@ -1854,7 +1854,19 @@ __global__ void __launch_bounds__(256) k_leaf_gather(const int4* out_origin, con
 // y and z passes never mix words, and the x pass needs just one more word on
 // each side (from the x-neighbour leaf at the ends). The source lookups are
 // split over the four lanes and their results exchanged with shuffles.
-template <int lo, int hi>  // the box [lo, hi]^3: dilate [-1, 1], pads [-1, 0] and [0, 1]
+// Raw buffer loads (the kBuf form, for source arrays under 2 GiB): 32-bit byte
+// offsets off one resource, and an offset past the array (kOff) reads zeros, so
+// a missing source costs no select. The resource's third word is the gfx9
+// family's raw-buffer format word.
+constexpr uint32_t kOff = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
+}
+
+// kBuf: the source arrays and the candidate table are read through buffer
+// resources (each under 2 GiB, checked by the host); otherwise through 64-bit
+// addresses, with index 0 standing in for a missing source and a select after.
+template <int lo, int hi, bool kBuf>  // the box [lo, hi]^3: dilate [-1, 1], pads [-1, 0] and [0, 1]
 __global__ void __launch_bounds__(256) k_leaf_gather_box(const int4* out_origin, const int32_t* leaf_cand,
                                                          const int32_t* d_n, i64 n_cap, const int32_t* cand_src,
                                                          const u64* src_lower_mask, const uint16_t* src_lower_prefix,
@@ -1862,7 +1874,7 @@ __global__ void __launch_bounds__(256) k_leaf_gather_box(const int4* out_origin,
                                                          int32_t n_src_lower, int32_t n_src_leaf,
                                                          const int32_t* d_num_cands, u64* out_mask, u64* out_prefix,
                                                          uint32_t* leaf_box, int32_t* leaf_inrun,
-                                                         i64* vox_part, int32_t* flags) {
+                                                         i64* vox_part, int32_t* flags, uint32_t cand_src_bytes) {
   const i64 n = device_count(d_n, n_cap, flags);
   const i64 nb = (n * 4 + 255) / 256;  // workgroups that hold leaves (the launch may hold more)
   if ((i64)blockIdx.x >= nb) return;  // uniform per block
@@ -1870,10 +1882,18 @@ __global__ void __launch_bounds__(256) k_leaf_gather_box(const int4* out_origin,
   const i64 gt = lblk * 256 + threadIdx.x;
   const i64 i = gt >> 2;
   const int sub = (int)(gt & 3);
+  [[maybe_unused]] __amdgpu_buffer_rsrc_t r_cand, r_lmask, r_lpre, r_lfirst, r_leaf;
+  if constexpr (kBuf) {
+    r_cand = buf_rsrc(cand_src, cand_src_bytes);
+    r_lmask = buf_rsrc(src_lower_mask, (uint32_t)n_src_lower * 512u);
+    r_lpre = buf_rsrc(src_lower_prefix, (uint32_t)n_src_lower * 128u);
+    r_lfirst = buf_rsrc(src_lower_first, (uint32_t)n_src_lower * 4u);
+    r_leaf = buf_rsrc(src_leaf_mask, (uint32_t)n_src_leaf * 64u);
+  }
   // Every load goes to a valid index (n, the candidates, the source lowers and
-  // leaves are all non-empty here; index 0 stands in for a missing one) and is
-  // masked afterwards, so each level's loads are in flight together. Indices
-  // fit 32 bits (source lowers < 2^25, checked by the host).
+  // leaves are all non-empty here; index 0 stands in for a missing one, or an
+  // offset past a buffer) and is masked afterwards, so each level's loads are in
+  // flight together. Indices fit 32 bits (source lowers < 2^25, checked by the host).
   const int32_t ncand = *d_num_cands;
   const int32_t ic = (int32_t)(i < n ? i : n - 1);
   const int4 o = out_origin[ic];
@@ -1902,7 +1922,12 @@ __global__ void __launch_bounds__(256) k_leaf_gather_box(const int4* out_origin,
     use[q] = valid && (code & 64u);
     const int px = lx + (int)(code & 3u) - hi, py = ly + (int)((code >> 2) & 3u) - hi, pz = lz + (int)((code >> 4) & 3u) - hi;
     bit[q] = ((px & 15) * 16 + (py & 15)) * 16 + (pz & 15);
-    sl[q] = cand_src[c * 27 + (use[q] ? index27(px >> 4, py >> 4, pz >> 4) : 13)];
+    const int slot = index27(px >> 4, py >> 4, pz >> 4);
+    if constexpr (kBuf) {
+      sl[q] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(r_cand, use[q] ? (uint32_t)(c * 27 + slot) * 4u : kOff, 0, 0);
+    } else {
+      sl[q] = cand_src[c * 27 + (use[q] ? slot : 13)];
+    }
   }
 #pragma unroll
   for (int q = 0; q < kPer; ++q) {
@@ -1914,18 +1939,28 @@ __global__ void __launch_bounds__(256) k_leaf_gather_box(const int4* out_origin,
   uint16_t lpre[kPer];
 #pragma unroll
   for (int q = 0; q < kPer; ++q) {
-    const uint32_t ls = sl[q] >= 0 ? (uint32_t)sl[q] : 0u;
-    word[q] = src_lower_mask[ls * 64u + (uint32_t)(bit[q] >> 6)];
-    lfirst[q] = src_lower_first[ls];
-    lpre[q] = src_lower_prefix[ls * 64u + (uint32_t)(bit[q] >> 6)];
+    const uint32_t w = (uint32_t)(bit[q] >> 6);
+    if constexpr (kBuf) {  // a missing source reads zeros
+      const uint32_t at = sl[q] >= 0 ? (uint32_t)sl[q] * 64u + w : kOff / 8u;
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(r_lmask, at * 8u, 0, 0);
+      word[q] = ((u64)v[1] << 32) | v[0];
+      lfirst[q] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(r_lfirst, sl[q] >= 0 ? (uint32_t)sl[q] * 4u : kOff, 0, 0);
+      lpre[q] = __builtin_amdgcn_raw_buffer_load_b16(r_lpre, at * 2u, 0, 0);
+    } else {
+      const uint32_t ls = sl[q] >= 0 ? (uint32_t)sl[q] : 0u;
+      word[q] = src_lower_mask[ls * 64u + w];
+      lfirst[q] = src_lower_first[ls];
+      lpre[q] = src_lower_prefix[ls * 64u + w];
+      if (sl[q] < 0) word[q] = 0;
+    }
   }
   int32_t r[kPer];
 #pragma unroll
   for (int q = 0; q < kPer; ++q) {
     const int b = bit[q] & 63;
-    const bool hit = sl[q] >= 0 && ((word[q] >> b) & 1ull);
+    const bool hit = (word[q] >> b) & 1ull;  // zero word for a missing source
     r[q] = lfirst[q] + lpre[q] + popc64(word[q] & ((1ull << b) - 1));
-    const bool out_of_range = hit && (r[q] < 0 || r[q] >= n_src_leaf);
+    const bool out_of_range = hit && (uint32_t)r[q] >= (uint32_t)n_src_leaf;
     bad |= out_of_range;
     if (!hit || out_of_range) r[q] = -1;
   }
@@ -1935,12 +1970,16 @@ __global__ void __launch_bounds__(256) k_leaf_gather_box(const int4* out_origin,
   // also word 7 of the row's x-1 leaf and lane 3 word 0 of its x+1 leaf; the
   // words 2sub-1 and 2sub+2 come from the neighbouring lanes of the quad.
   // Leaf indices resolved by other lanes of the quad arrive by quad broadcasts.
-  u64 ys[3][2];
+  // Every row's leaf indices come first (quad broadcasts), then the loads of
+  // one z offset's rows are issued together, before any of their quad
+  // permutations (the compiler moves no load across those).
+  int32_t rcs[3][3], res[3][3];  // [sz + 1][sy + 1]: centre and edge leaf of the row
 #pragma unroll
-  for (int sz = -1; sz <= 1; ++sz) {
-    u64 xs[3][2] = {{0, 0}, {0, 0}, {0, 0}};
+  for (int sz = -1; sz <= 1; ++sz)
 #pragma unroll
     for (int sy = -1; sy <= 1; ++sy) {
+      rcs[sz + 1][sy + 1] = -1;
+      res[sz + 1][sy + 1] = -1;
       if (sz < -hi || sz > -lo || sy < -hi || sy > -lo) continue;
       // source leaves at (sx, sy, sz), sx = -1, 0, 1 (the ones in the box): slot k
       constexpr int kNone = -1;
@@ -1948,21 +1987,44 @@ __global__ void __launch_bounds__(256) k_leaf_gather_box(const int4* out_origin,
       const int kc = ((0 + hi) * W + ky) * W + kz;   // sx = 0
       const int km = ((-1 + hi) * W + ky) * W + kz;  // sx = -1 (hi > 0)
       const int kp = ((1 + hi) * W + ky) * W + kz;   // sx = +1 (lo < 0)
-      const int32_t rc = quad_bcast32(r[kc >> 2], kc & 3);
+      rcs[sz + 1][sy + 1] = quad_bcast32(r[kc >> 2], kc & 3);
       const int32_t rm = hi > 0 ? quad_bcast32(r[km >> 2], km & 3) : kNone;
       const int32_t rp = lo < 0 ? quad_bcast32(r[kp >> 2], kp & 3) : kNone;
-      const int32_t re = sub == 0 ? rm : (sub == 3 ? rp : kNone);  // edge leaf of this lane
-      const ulonglong2 own = reinterpret_cast<const ulonglong2*>(src_leaf_mask)[(i64)(rc >= 0 ? rc : 0) * 4 + sub];
-      const u64 edge = src_leaf_mask[(i64)(re >= 0 ? re : 0) * 8 + (sub == 0 ? 7 : 0)];
-      const u64 wa = rc >= 0 ? (u64)own.x : 0ull, wb = rc >= 0 ? (u64)own.y : 0ull;
-      const u64 we = re >= 0 ? edge : 0ull;
+      res[sz + 1][sy + 1] = sub == 0 ? rm : (sub == 3 ? rp : kNone);  // edge leaf of this lane
+    }
+  u64 ys[3][2];
+#pragma unroll
+  for (int sz = -1; sz <= 1; ++sz) {
+    u64 xs[3][2] = {{0, 0}, {0, 0}, {0, 0}};
+    u64 wa[3] = {0, 0, 0}, wb[3] = {0, 0, 0}, we[3] = {0, 0, 0};
+#pragma unroll
+    for (int sy = -1; sy <= 1; ++sy) {
+      if (sz < -hi || sz > -lo || sy < -hi || sy > -lo) continue;
+      const int32_t rc = rcs[sz + 1][sy + 1], re = res[sz + 1][sy + 1];
+      if constexpr (kBuf) {  // a missing leaf reads zeros
+        const auto own = __builtin_amdgcn_raw_buffer_load_b128(r_leaf, rc >= 0 ? (uint32_t)rc * 64u + (uint32_t)sub * 16u : kOff, 0, 0);
+        const auto edge = __builtin_amdgcn_raw_buffer_load_b64(r_leaf, re >= 0 ? (uint32_t)re * 64u + (sub == 0 ? 56u : 0u) : kOff, 0, 0);
+        wa[sy + 1] = ((u64)own[1] << 32) | own[0];
+        wb[sy + 1] = ((u64)own[3] << 32) | own[2];
+        we[sy + 1] = ((u64)edge[1] << 32) | edge[0];
+      } else {
+        const ulonglong2 own = reinterpret_cast<const ulonglong2*>(src_leaf_mask)[(i64)(rc >= 0 ? rc : 0) * 4 + sub];
+        const u64 edge = src_leaf_mask[(i64)(re >= 0 ? re : 0) * 8 + (sub == 0 ? 7 : 0)];
+        wa[sy + 1] = rc >= 0 ? (u64)own.x : 0ull;
+        wb[sy + 1] = rc >= 0 ? (u64)own.y : 0ull;
+        we[sy + 1] = re >= 0 ? edge : 0ull;
+      }
+    }
+#pragma unroll
+    for (int sy = -1; sy <= 1; ++sy) {
+      if (sz < -hi || sz > -lo || sy < -hi || sy > -lo) continue;
       // The permutations run on the whole quad before the selects (a select
       // around them would make them conditional, and lane 0 or 3 then absent).
-      const u64 pl = quad_perm64<0, 0, 1, 2>(wb), pr = quad_perm64<1, 2, 3, 3>(wa);
-      const u64 left = sub == 0 ? we : pl;   // word 2sub - 1
-      const u64 right = sub == 3 ? we : pr;  // word 2sub + 2
-      xs[sy + 1][0] = wa | (hi > 0 ? left : 0ull) | (lo < 0 ? wb : 0ull);
-      xs[sy + 1][1] = wb | (hi > 0 ? wa : 0ull) | (lo < 0 ? right : 0ull);
+      const u64 pl = quad_perm64<0, 0, 1, 2>(wb[sy + 1]), pr = quad_perm64<1, 2, 3, 3>(wa[sy + 1]);
+      const u64 left = sub == 0 ? we[sy + 1] : pl;   // word 2sub - 1
+      const u64 right = sub == 3 ? we[sy + 1] : pr;  // word 2sub + 2
+      xs[sy + 1][0] = wa[sy + 1] | (hi > 0 ? left : 0ull) | (lo < 0 ? wb[sy + 1] : 0ull);
+      xs[sy + 1][1] = wb[sy + 1] | (hi > 0 ? wa[sy + 1] : 0ull) | (lo < 0 ? right : 0ull);
     }
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
@@ -2318,13 +2380,17 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, 
              sv.n_leaf, (const int32_t*)ts.d_num_cands, ov.leaf_mask, ov.leaf_prefix, post.at<uint32_t>(o_box),
              leaf_inrun, vox_part, ts.flags);
     } else {
-      auto gather_box = oi.lo < 0 && oi.hi > 0 ? k_leaf_gather_box<-1, 1>
-                        : (oi.lo < 0 ? k_leaf_gather_box<-1, 0> : k_leaf_gather_box<0, 1>);
+      // buffer loads when every array they read stays under 2 GiB
+      const bool buf = (i64)sv.n_leaf * 64 < (1ll << 31) && (i64)sv.n_lower * 512 < (1ll << 31) &&
+                       ts.cap_cands * 27 * 4 < (1ll << 31);
+      auto gather_box = oi.lo < 0 && oi.hi > 0 ? (buf ? k_leaf_gather_box<-1, 1, true> : k_leaf_gather_box<-1, 1, false>)
+                        : oi.lo < 0 ? (buf ? k_leaf_gather_box<-1, 0, true> : k_leaf_gather_box<-1, 0, false>)
+                                    : (buf ? k_leaf_gather_box<0, 1, true> : k_leaf_gather_box<0, 1, false>);
       launch("k_leaf_gather", gather_box, ceil_div(L * 4, 256), 256, s, (const int4*)ov.leaf_origin,
              (const int32_t*)leaf_cand, d_L, L, (const int32_t*)cand_src, (const u64*)sv.lower_mask,
              (const uint16_t*)sv.lower_prefix, (const int32_t*)sv.lower_first, (const u64*)sv.leaf_mask, sv.n_lower,
              sv.n_leaf, (const int32_t*)ts.d_num_cands, ov.leaf_mask, ov.leaf_prefix, post.at<uint32_t>(o_box),
-             leaf_inrun, vox_part, ts.flags);
+             leaf_inrun, vox_part, ts.flags, (uint32_t)std::min<i64>(ts.cap_cands * 27 * 4, (1ll << 31) - 1));
     }
     // the gathers' consistency checks set bits in the flag word after the
     // counts: the finalize copies it into the batch's status word

@@ -361,6 +361,14 @@ void tc_batch_free(tc_grid_batch* batch);
  * would. Bits outside [0, 3] are TC_ERR_INVALID_ARG. */
 tc_status tc_debug_inject_flags(int32_t bits);
 
+/* Testing hook for the large-batch form of the box ops' leaf gather: while `on`
+ * is 1, the calling thread's dilate and pad passes read their source arrays
+ * through 64-bit addresses, as they do by themselves when a source array is
+ * 2 GiB or more; 0 restores the default (32-bit buffer offsets below that
+ * size). Results are the same either way. Values other than 0 and 1 are
+ * TC_ERR_INVALID_ARG. */
+tc_status tc_debug_wide_loads(int32_t on);
+
 /* Kernel timing for measurement: while enabled, every launch of a kernel whose
  * name is in `kernel_names` (comma-separated __global__ function names, e.g.
  * "k_leaf_gather,k_enumerate"; "*" selects every kernel) is bracketed by HIP

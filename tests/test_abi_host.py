@@ -151,3 +151,11 @@ def test_debug_inject_flags_validates_on_host(lib):
     assert lib.tc_debug_inject_flags(-1) == binding.TC_ERR_INVALID_ARG
     assert b"bits" in lib.tc_last_error()
     assert lib.tc_debug_inject_flags(0) == binding.TC_OK  # cancels (nothing armed here)
+
+
+def test_debug_wide_loads_validates_on_host(lib):
+    assert lib.tc_debug_wide_loads(2) == binding.TC_ERR_INVALID_ARG
+    assert lib.tc_debug_wide_loads(-1) == binding.TC_ERR_INVALID_ARG
+    assert b"on must be" in lib.tc_last_error()
+    assert lib.tc_debug_wide_loads(1) == binding.TC_OK
+    assert lib.tc_debug_wide_loads(0) == binding.TC_OK

@@ -255,6 +255,21 @@ def test_box_ops_solid_sources(op, f):
     _check(op, f, ijk, off, "solid")
 
 
+@pytest.mark.parametrize("op,f", [("dilate", 1), ("pad_neg", 1), ("pad_pos", 1), ("conv_t_k3s2", 2)])
+def test_box_ops_wide_address_form(op, f):
+    """The box ops' leaf gather in the form batches with source arrays of 2 GiB or
+    more take (64-bit addresses), forced on small inputs: same results."""
+    from topology_construction_amd import binding
+    binding.tc_debug_wide_loads(True)
+    try:
+        ijk, off = synth.make_config(3)
+        _check(op, f, ijk, off, "wide config 3")
+        ijk, off = _solid_members()
+        _check(op, f, ijk, off, "wide solid")
+    finally:
+        binding.tc_debug_wide_loads(False)
+
+
 @pytest.mark.parametrize("op", ["conv_s1", "conv_t_s1"])
 @pytest.mark.parametrize("k", [2, 4, 5])
 def test_kernel_k_voxels_on_node_faces(op, k):

@@ -29,7 +29,7 @@ ABI_SYMBOLS = [
     "tc_build_batched_topology", "tc_build_masked_refine", "tc_batch_get_info", "tc_batch_read_headers",
     "tc_batch_voxel_total", "tc_enumerate_ijk", "tc_build_kernel_map", "tc_scratch_release", "tc_batch_free",
     "tc_debug_inject_flags", "tc_build_kernel_map_noalloc", "tc_profile_enable", "tc_profile_read",
-    "tc_profile_disable", "tc_build_batched_topology_many", "tc_enumerate_ijk_many",
+    "tc_profile_disable", "tc_build_batched_topology_many", "tc_enumerate_ijk_many", "tc_debug_wide_loads",
 ]
 
 HEADER_DTYPE = np.dtype([
@@ -143,6 +143,8 @@ def load_library(path: str = LIB_PATH):
         lib.tc_batch_free.argtypes = [vp]
         lib.tc_debug_inject_flags.restype = ctypes.c_int
         lib.tc_debug_inject_flags.argtypes = [i32]
+        lib.tc_debug_wide_loads.restype = ctypes.c_int
+        lib.tc_debug_wide_loads.argtypes = [i32]
         lib.tc_profile_enable.restype = ctypes.c_int
         lib.tc_profile_enable.argtypes = [ctypes.c_char_p]
         lib.tc_profile_read.restype = ctypes.c_int
@@ -490,6 +492,12 @@ def tc_scratch_release():
 
 def tc_batch_read_headers(batch: GridBatch, stream=None) -> np.ndarray:
     return batch.headers(stream)
+
+
+def tc_debug_wide_loads(on: bool):
+    """Testing: this thread's box-op passes read their sources through 64-bit
+    addresses (the form for source arrays of 2 GiB or more) while `on`."""
+    _check(load_library().tc_debug_wide_loads(1 if on else 0))
 
 
 def tc_debug_inject_flags(bits: int):

@@ -169,8 +169,11 @@ static void take_vox_slot(tc_grid_batch* b) {
 
 namespace {
 thread_local int32_t t_inject = 0;
+thread_local bool t_wide_loads = false;
 }
 void debug_set_inject(int32_t bits) { t_inject = bits; }
+void debug_set_wide_loads(bool on) { t_wide_loads = on; }
+bool debug_wide_loads() { return t_wide_loads; }
 void apply_debug_inject(int32_t* d_flags, hipStream_t s) {
   if (!t_inject) return;
   fill_i32(d_flags, t_inject, 1, nullptr, 1, s);  // testing: the writers "found" an inconsistency
@@ -760,6 +763,12 @@ void tc_batch_free(tc_grid_batch* b) {
 tc_status tc_debug_inject_flags(int32_t bits) {
   if (bits < 0 || bits > 3) return fail(TC_ERR_INVALID_ARG, "bits must be in [0, 3]");
   tc::debug_set_inject(bits);
+  return TC_OK;
+}
+
+tc_status tc_debug_wide_loads(int32_t on) {
+  if (on != 0 && on != 1) return fail(TC_ERR_INVALID_ARG, "on must be 0 or 1");
+  tc::debug_set_wide_loads(on == 1);
   return TC_OK;
 }
 

@@ -384,6 +384,10 @@ struct OutAlloc {
 // them (once) on the flag word of the batch being built, before its finalize.
 void debug_set_inject(int32_t bits);
 void apply_debug_inject(int32_t* d_flags, hipStream_t s);
+// Testing: while set on the calling thread, the box ops' leaf gather takes its
+// 64-bit-address form (the one batches with source arrays of 2 GiB or more use).
+void debug_set_wide_loads(bool on);
+bool debug_wide_loads();
 
 void prof_enable(const char* name);
 void prof_read(const char* name, double* ms, int64_t* n);

@@ -2382,7 +2382,7 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, 
     } else {
       // buffer loads when every array they read stays under 2 GiB
       const bool buf = (i64)sv.n_leaf * 64 < (1ll << 31) && (i64)sv.n_lower * 512 < (1ll << 31) &&
-                       ts.cap_cands * 27 * 4 < (1ll << 31);
+                       ts.cap_cands * 27 * 4 < (1ll << 31) && !debug_wide_loads();
       auto gather_box = oi.lo < 0 && oi.hi > 0 ? (buf ? k_leaf_gather_box<-1, 1, true> : k_leaf_gather_box<-1, 1, false>)
                         : oi.lo < 0 ? (buf ? k_leaf_gather_box<-1, 0, true> : k_leaf_gather_box<-1, 0, false>)
                                     : (buf ? k_leaf_gather_box<0, 1, true> : k_leaf_gather_box<0, 1, false>);

@@ -1176,9 +1176,11 @@ void tree_finalize_leaves(const GridView& out, const uint32_t* leaf_box, const i
 // of word x, at most 8 voxels along z). The row's first voxel is the leaf's
 // prefix field for the words before x plus the set bits of word x before byte
 // y, so no cross-lane scan is needed; lanes expand their rows into LDS in bit
-// order, and the wave streams the leaf's rows out with 16-byte non-temporal
-// stores (the output is not read back by this kernel; the LDS image is shifted
-// so that its 16-byte chunks line up with the destination's). The wave index is
+// order, and the wave streams the leaf's rows out with 16-byte stores (the LDS
+// image is shifted so that its 16-byte chunks line up with the destination's).
+// Launches below eight leaves per wave (up to 256K leaves) make them
+// non-temporal: their output then leaves few dirty lines behind at the kernel's
+// end (measured faster there, and slower on the largest launches). The wave index is
 // made uniform, so the per-leaf values of the loop come from lane reads.
 constexpr int kEnumMaxLeaves = 8;
 constexpr int kEnumLdsGrids = 256;  // up to this many grids, voxel begins come from LDS
@@ -1212,11 +1214,12 @@ __device__ __forceinline__ i64 readlane64(i64 v, int l) {
 }
 
 // One block's share (block `blk` of the batch's launch shape) of k_enumerate.
+template <bool NT>
 __device__ __forceinline__ void enumerate_block(const tc_grid_header* hdr, const int4* leaf_origin,
                                                 const u64* leaf_mask, const u64* leaf_prefix,
                                                 const i64* leaf_offset, int32_t* ijk, i64 n_leaf, int32_t B,
-                                                int lpw, int vec_ok, i64 blk, int32_t (*s_rows)[3 * 512 + 4],
-                                                i64* s_vb) {
+                                                int lpw, int vec_ok, i64 blk,
+                                                int32_t (*s_rows)[3 * 512 + 4], i64* s_vb) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x & (kWave - 1);
   const i64 l0 = (blk * 4 + w) * lpw;
@@ -1287,16 +1290,21 @@ __device__ __forceinline__ void enumerate_block(const tc_grid_header* hdr, const
           const int e0 = q * 4;
           if (q >= nq) continue;
           if (e0 >= a && e0 + 4 <= n) {
-            __builtin_nontemporal_store(v[u], dst4 + q);
+            if constexpr (NT) __builtin_nontemporal_store(v[u], dst4 + q);
+            else dst4[q] = v[u];
           } else {
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
-              if (e0 + t >= a && e0 + t < n) __builtin_nontemporal_store(v[u][t], dst + e0 + t);
+            for (int t = 0; t < 4; ++t) {
+              if (e0 + t >= a && e0 + t < n) {
+                if constexpr (NT) __builtin_nontemporal_store(v[u][t], dst + e0 + t);
+                else dst[e0 + t] = v[u][t];
+              }
+            }
           }
         }
       }
     } else {
-      for (int e = lane; e < n; e += kWave) __builtin_nontemporal_store(rows[e], dst + e);
+      for (int e = lane; e < n; e += kWave) dst[e] = rows[e];
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -1304,20 +1312,22 @@ __device__ __forceinline__ void enumerate_block(const tc_grid_header* hdr, const
   }
 }
 
+template <bool NT>
 __global__ void __launch_bounds__(256) k_enumerate(const tc_grid_header* hdr, const int4* leaf_origin,
                                                    const u64* leaf_mask, const u64* leaf_prefix,
                                                    const i64* leaf_offset, int32_t* ijk, i64 n_leaf, int32_t B,
                                                    int lpw, int vec_ok) {
   __shared__ __align__(16) int32_t s_rows[4][3 * 512 + 4];
   __shared__ i64 s_vb[kEnumLdsGrids];  // grids' voxel begins, loaded beside the leaves
-  enumerate_block(hdr, leaf_origin, leaf_mask, leaf_prefix, leaf_offset, ijk, n_leaf, B, lpw, vec_ok, blockIdx.x,
-                  s_rows, s_vb);
+  enumerate_block<NT>(hdr, leaf_origin, leaf_mask, leaf_prefix, leaf_offset, ijk, n_leaf, B, lpw, vec_ok,
+                      blockIdx.x, s_rows, s_vb);
 }
 
 // Several batches in one launch: the blocks of batch j follow those of batch
 // j - 1 (block_begin, by value); every block finds its batch among at most
 // kEnumMany and runs that batch's share. One launch fills the chip where a
 // small batch alone would not, and saves the launches.
+template <bool NT>
 __global__ void __launch_bounds__(256) k_enumerate_many(EnumBatches eb) {
   __shared__ __align__(16) int32_t s_rows[4][3 * 512 + 4];
   __shared__ i64 s_vb[kEnumLdsGrids];
@@ -1325,8 +1335,8 @@ __global__ void __launch_bounds__(256) k_enumerate_many(EnumBatches eb) {
 #pragma unroll
   for (int q = 1; q < kEnumMany; ++q) j += q < eb.n && (i64)blockIdx.x >= eb.block_begin[q] ? 1 : 0;
   const EnumBatch& b = eb.b[j];
-  enumerate_block(b.hdr, b.leaf_origin, b.leaf_mask, b.leaf_prefix, b.leaf_offset, b.ijk, b.n_leaf, b.B, eb.lpw,
-                  b.vec_ok, (i64)blockIdx.x - eb.block_begin[j], s_rows, s_vb);
+  enumerate_block<NT>(b.hdr, b.leaf_origin, b.leaf_mask, b.leaf_prefix, b.leaf_offset, b.ijk, b.n_leaf, b.B,
+                      eb.lpw, b.vec_ok, (i64)blockIdx.x - eb.block_begin[j], s_rows, s_vb);
 }
 
 // one leaf per wave while the waves fit in one round of the chip (about 6k
@@ -1336,7 +1346,7 @@ static int enumerate_lpw(i64 n_leaf) { return n_leaf >= 256 * 1024 ? kEnumMaxLea
 void tree_enumerate(const GridView& v, int32_t* ijk, hipStream_t s) {
   const int vec_ok = (reinterpret_cast<uintptr_t>(ijk) & 15) == 0 ? 1 : 0;
   const int lpw = enumerate_lpw(v.n_leaf);
-  launch("k_enumerate", k_enumerate, ceil_div((i64)v.n_leaf, 4 * lpw), 256, s,
+  launch("k_enumerate", lpw < kEnumMaxLeaves ? k_enumerate<true> : k_enumerate<false>, ceil_div((i64)v.n_leaf, 4 * lpw), 256, s,
          (const tc_grid_header*)v.headers, (const int4*)v.leaf_origin, (const u64*)v.leaf_mask,
          (const u64*)v.leaf_prefix, (const i64*)v.leaf_offset, ijk, (i64)v.n_leaf, v.B, lpw, vec_ok);
 }
@@ -1366,7 +1376,8 @@ void tree_enumerate_many(const GridView* v, int32_t* const* ijk, int n, hipStrea
       blocks += ceil_div((i64)g.n_leaf, 4 * eb.lpw);
     }
     for (int j = m; j < kEnumMany; ++j) eb.block_begin[j] = blocks;
-    launch("k_enumerate", k_enumerate_many, blocks, 256, s, eb);
+    launch("k_enumerate", eb.lpw < kEnumMaxLeaves ? k_enumerate_many<true> : k_enumerate_many<false>, blocks, 256,
+           s, eb);
   }
 }
 

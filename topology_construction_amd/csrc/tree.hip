@@ -438,7 +438,10 @@ constexpr int kNodeFlags = 4096;  // candidates per tile whose non-empty flags t
 // grid, parent) per set bit of its leaf mask; leaf_cand[leaf] remembers the
 // candidate for the leaf-mask producers. Block 0 also sets every header's box
 // to empty for the leaf finalizer.
-// cand_scan and upper_excl may point into LDS (the fused writer below).
+// cand_scan and upper_excl may point into LDS (the fused writer below, kLdsScan):
+// then a candidate's leaf count and non-empty flag come from its two scan
+// entries, and no count is loaded.
+template <bool kLdsScan>
 __device__ __forceinline__ void write_nodes_body(
     int32_t tile_blocks, const int4* utile, const u64* tile_child, const uint16_t* tile_prefix,
     const int32_t* tile_lower_base, const int4* cand_origin, const u64* cand_child, const uint16_t* cand_prefix,
@@ -483,7 +486,7 @@ __device__ __forceinline__ void write_nodes_body(
     // kNodeFlags candidates in flight together), so that the per-bit loop below
     // waits on no memory; tiles with more candidates read the counts directly
     const int32_t ncb = ce - cb;
-    const bool lds_flags = ncb <= kNodeFlags;  // uniform
+    const bool lds_flags = !kLdsScan && ncb <= kNodeFlags;  // uniform
     if (lds_flags) {
       const int lane = threadIdx.x & (kWave - 1);
 #pragma unroll
@@ -506,7 +509,9 @@ __device__ __forceinline__ void write_nodes_body(
       int32_t c = pres[k];  // candidate index relative to the tile's base
       while (word) {
         const int b = __builtin_ctzll(word);
-        const bool ne = lds_flags ? ((s_flags[c >> 5] >> (c & 31)) & 1u) != 0 : (int32_t)cand_counts[cb + c] > 0;
+        bool ne;
+        if constexpr (kLdsScan) ne = scan_leaf(cand_scan[cb + c + 1]) > scan_leaf(cand_scan[cb + c]);
+        else ne = lds_flags ? ((s_flags[c >> 5] >> (c & 31)) & 1u) != 0 : (int32_t)cand_counts[cb + c] > 0;
         if (ne) out |= 1ull << b;
         word &= word - 1;
         ++c;
@@ -521,8 +526,8 @@ __device__ __forceinline__ void write_nodes_body(
   const int lane = threadIdx.x & (kWave - 1);
   const i64 cc = c < cap_cands ? c : cap_cands - 1;
   const int32_t ncand = *d_num_cands;
-  const int32_t cnt = (int32_t)cand_counts[cc];
   const i64 v = cand_scan[cc];
+  const int32_t cnt = kLdsScan ? scan_leaf(cand_scan[cc + 1]) - scan_leaf(v) : (int32_t)cand_counts[cc];
   const int4 co = cand_origin[cc];
   const u64 word = cand_child[cc * 64 + lane];
   const uint16_t pre = cand_prefix[cc * 64 + lane];
@@ -571,7 +576,7 @@ __global__ void __launch_bounds__(256) k_write_nodes(
     u64* lower_mask, uint16_t* lower_prefix, int4* leaf_origin, int32_t* leaf_parent, int32_t* leaf_cand,
     tc_grid_header* hdr, int32_t B, i64 cap_cands) {
   __shared__ uint32_t s_flags[kNodeFlags / 32];
-  write_nodes_body(tile_blocks, utile, tile_child, tile_prefix, tile_lower_base, cand_origin, cand_child, cand_prefix,
+  write_nodes_body<false>(tile_blocks, utile, tile_child, tile_prefix, tile_lower_base, cand_origin, cand_child, cand_prefix,
                    cand_counts, cand_scan, upper_excl, d_num_tiles, d_num_cands, n_upper, n_lower, n_leaf,
                    upper_origin, upper_key, upper_first, upper_mask, lower_origin, lower_first, lower_mask,
                    lower_prefix, leaf_origin, leaf_parent, leaf_cand, hdr, B, cap_cands, s_flags);
@@ -686,8 +691,8 @@ __global__ void __launch_bounds__(256) k_write_nodes_counted(
       readback[4 + g * 3 + 2] = nl;
     }
   }
-  write_nodes_body(tile_blocks, utile, tile_child, tile_prefix, tile_lower_base, cand_origin, cand_child, cand_prefix,
-                   cand_counts, s_cc, s_uex, d_num_tiles, d_num_cands, n_upper, n_lower, n_leaf, upper_origin,
+  write_nodes_body<true>(tile_blocks, utile, tile_child, tile_prefix, tile_lower_base, cand_origin, cand_child,
+                         cand_prefix, cand_counts, s_cc, s_uex, d_num_tiles, d_num_cands, n_upper, n_lower, n_leaf, upper_origin,
                    upper_key, upper_first, upper_mask, lower_origin, lower_first, lower_mask, lower_prefix,
                    leaf_origin, leaf_parent, leaf_cand, hdr, B, cap_cands, s_flags);
 }

@@ -1423,26 +1423,37 @@ __device__ __forceinline__ uint32_t pack_pos(int px, int py, int pz) {
   return (uint32_t)(px + 1) | ((uint32_t)(py + 1) << 5) | ((uint32_t)(pz + 1) << 10);
 }
 
+// Marks the target leaves of C that a source leaf at `pos` (C's frame, packed
+// by pack_pos) with mask words W spills voxels into: offset t of the box is
+// marked when the leaf holds a voxel on each face t points across (x: word 0 or
+// 7, y: row byte 0 or 7, z: bit 0 or 7 of the row bytes; t = 0 on an axis asks
+// for any voxel). Per (tx, ty) the three z flags form a 3-bit pattern that is
+// shifted into place (and clipped to the leaf row) at once.
+__device__ __forceinline__ uint32_t z_pattern(uint32_t r) {  // r: the OR of the rows' bytes (8 bits)
+  return (r & 1u) | (r != 0u ? 2u : 0u) | ((r >> 5) & 4u);  // tz = -1, 0, +1
+}
 __device__ __forceinline__ void mark_box_leaf(const u64 W[8], uint32_t pos, int lo, int hi,
                                               unsigned long long* s_mask) {
   const int px = (int)(pos & 31) - 1, py = (int)((pos >> 5) & 31) - 1, pz = (int)((pos >> 10) & 31) - 1;
   const u64 all = W[0] | W[1] | W[2] | W[3] | W[4] | W[5] | W[6] | W[7];
+  // the z run of a pattern: bit k <-> target z = pz - 1 + k, kept inside [0, 15]
+  const uint32_t zmask = lo < 0 ? 7u : 6u, zmask2 = hi > 0 ? 7u : 3u;  // taps the box holds
+#pragma unroll
   for (int tx = lo; tx <= hi; ++tx) {
     const int qx = px + tx;
-    if (qx < 0 || qx > 15) continue;
     const u64 xs = tx > 0 ? W[7] : (tx < 0 ? W[0] : all);  // voxels that spill toward tx
+    const uint32_t xl = (uint32_t)xs, xh = (uint32_t)(xs >> 32);
+    uint32_t fold = xl | xh;  // OR of the eight row bytes
+    fold |= fold >> 16;
+    fold |= fold >> 8;
+#pragma unroll
     for (int ty = lo; ty <= hi; ++ty) {
       const int qy = py + ty;
-      if (qy < 0 || qy > 15) continue;
-      const u64 xy = xs & (ty > 0 ? 0xff00000000000000ull : (ty < 0 ? 0xffull : ~0ull));
-      if (!xy) continue;
-      u64 bits = 0;
-      for (int tz = lo; tz <= hi; ++tz) {
-        const int qz = pz + tz;
-        if (qz < 0 || qz > 15) continue;
-        if (xy & (tz > 0 ? kZ7 : (tz < 0 ? kZ0 : ~0ull))) bits |= 1ull << ((qy & 3) * 16 + qz);
-      }
-      if (bits) atomicOr(&s_mask[qx * 4 + (qy >> 2)], bits);
+      const uint32_t r = ty < 0 ? (xl & 0xffu) : (ty > 0 ? (xh >> 24) : (fold & 0xffu));  // row 0, row 7, any
+      const uint32_t p3 = z_pattern(r) & zmask & zmask2;
+      const uint32_t run = ((p3 << (pz + 1)) >> 2) & 0xffffu;  // bits of target z in 0..15
+      if (!run || qx < 0 || qx > 15 || qy < 0 || qy > 15) continue;
+      atomicOr(&s_mask[qx * 4 + (qy >> 2)], (unsigned long long)run << ((qy & 3) * 16));
     }
   }
 }

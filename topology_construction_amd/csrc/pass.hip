@@ -1242,7 +1242,7 @@ __global__ void __launch_bounds__(256) k_leaf_mark_lower(const int4* leaf_origin
                                                          u64* cand_child, uint16_t* cand_prefix,
                                                          i64* cand_counts, int32_t* flags) {
   constexpr int kFlush = 8 * 64 / 256;  // target words per thread (m == 8)
-  constexpr int kPer = 2;               // leaves per thread in flight
+  constexpr int kPer = 1;               // leaves per thread per batch
   __shared__ unsigned long long s_mask[8 * 64];
   const i64 l = blockIdx.x;
   // loads indexed by the lower alone, first: its leaf range and the candidates
@@ -1255,20 +1255,34 @@ __global__ void __launch_bounds__(256) k_leaf_mark_lower(const int4* leaf_origin
   for (int r = 0; r < kFlush; ++r) nbr[r] = lower_nbr[l * m + min((r * 256 + (int)threadIdx.x) >> 6, m - 1)];
   for (int k = threadIdx.x; k < m * 64; k += 256) s_mask[k] = 0;
   __syncthreads();
-  for (int k0 = 0; k0 < count; k0 += kPer * 256) {
-    int4 o[kPer];
-    u64 W[kPer][8];
+  // leaves kPer * 256 at a time, the next batch's loads issued before this
+  // batch is marked (a dense lower has up to 4096 leaves)
+  int4 o[kPer];
+  u64 W[kPer][8];
+  auto load_batch = [&](int k0) {
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {  // clamped: every leaf of the batch in flight together
-      const i64 i = first + min(k0 + u * 256 + (int)threadIdx.x, count - 1);
+      const i64 i = first + max(0, min(k0 + u * 256 + (int)threadIdx.x, count - 1));
       o[u] = leaf_origin[i];
 #pragma unroll
       for (int q = 0; q < 8; ++q) W[u][q] = leaf_mask[i * 8 + q];
     }
+  };
+  if (count > 0) load_batch(0);
+  for (int k0 = 0; k0 < count; k0 += kPer * 256) {
+    int4 oc[kPer];
+    u64 Wc[kPer][8];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      oc[u] = o[u];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) Wc[u][q] = W[u][q];
+    }
+    if (k0 + kPer * 256 < count) load_batch(k0 + kPer * 256);
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       if (k0 + u * 256 + (int)threadIdx.x >= count) continue;
-      const i64 mx = o[u].x >> 3, my = o[u].y >> 3, mz = o[u].z >> 3;  // leaf coordinates
+      const i64 mx = oc[u].x >> 3, my = oc[u].y >> 3, mz = oc[u].z >> 3;  // leaf coordinates
       const i64 lx = mx & 15, ly = my & 15, lz = mz & 15;              // position inside the lower
       {
         const int j = octant_index(lx >> 3, ly >> 3, lz >> 3);  // all children share one target lower
@@ -1281,7 +1295,7 @@ __global__ void __launch_bounds__(256) k_leaf_mark_lower(const int4* leaf_origin
 #pragma unroll
             for (int qz = 0; qz < 2; ++qz) {
               const I3 q{qx, qy, qz};
-              if (!subblock_nonempty(W[u], q)) continue;
+              if (!subblock_nonempty(Wc[u], q)) continue;
               if (!leaf_ok(2 * mx + qx) || !leaf_ok(2 * my + qy) || !leaf_ok(2 * mz + qz)) {
                 set_flag(flags, kFlagOverflow);
                 continue;

@@ -431,6 +431,7 @@ void tree_grid_counts(TreeScratch& ts, int32_t B, hipStream_t s) {
 
 // ------------------------------------------------------------------ node writers
 constexpr int kNodeFlags = 4096;  // candidates per tile whose non-empty flags the tile block stages in LDS
+constexpr int kNodesDense = 1024;  // leaves of a candidate from which the node writer goes word by word
 // One launch, two roles. Blocks [0, tile_blocks) each own one tile and write its
 // upper node record and child mask (candidate bits whose lower turned out empty
 // are cleared). The remaining blocks own four candidate lowers each (one wave
@@ -520,50 +521,73 @@ __device__ __forceinline__ void write_nodes_body(
     }
     return;
   }
-  // every load indexed by the candidate alone first (clamped to the capacity),
-  // then the two that its origin selects
-  const i64 c = ((i64)blockIdx.x - tile_blocks) * 4 + threadIdx.x / kWave;
+  // Candidate waves loop over the candidates (wave k takes k, k + K, ... for K
+  // candidate waves in the launch, which may be fewer than the capacity), so no
+  // wave runs for a candidate past the device count. Per candidate, every load
+  // indexed by the candidate alone first (clamped to the capacity), then the two
+  // that its origin selects.
   const int lane = threadIdx.x & (kWave - 1);
-  const i64 cc = c < cap_cands ? c : cap_cands - 1;
   const int32_t ncand = *d_num_cands;
-  const i64 v = cand_scan[cc];
-  const int32_t cnt = kLdsScan ? scan_leaf(cand_scan[cc + 1]) - scan_leaf(v) : (int32_t)cand_counts[cc];
-  const int4 co = cand_origin[cc];
-  const u64 word = cand_child[cc * 64 + lane];
-  const uint16_t pre = cand_prefix[cc * 64 + lane];
-  if (c >= ncand) return;
-  if (cnt == 0) return;  // uniform per wave
-  const i64 lo = scan_lower(v);
-  const int32_t lb = scan_leaf(v);
-  if (lo < 0 || lo >= n_lower || lb < 0 || (i64)lb + cnt > n_leaf) return;  // consistency guard
-  const int32_t g = utile[co.w].w;
-  lower_mask[lo * 64 + lane] = word;
-  lower_prefix[lo * 64 + lane] = pre;
-  if (lane == 0) {
-    lower_origin[lo] = make_int4(co.x, co.y, co.z, upper_excl[co.w]);
-    lower_first[lo] = lb;
-  }
-  // leaf records in output order, 64 at a time: lane j takes leaf r = k0 + j, finds
-  // its word (last word whose prefix is <= r, by binary search over the lanes'
-  // prefixes) and bit, so consecutive lanes store consecutive records
-  const int pre_i = pre;
-  for (int32_t k0 = 0; k0 < cnt; k0 += kWave) {
-    const int32_t r = k0 + lane;
-    int w = 0;
-#pragma unroll
-    for (int step = 32; step >= 1; step >>= 1) {
-      const int p = __shfl(pre_i, w + step, kWave);
-      if (w + step < kWave && p <= r) w += step;
+  const i64 nstride = ((i64)gridDim.x - tile_blocks) * 4;
+  for (i64 c = ((i64)blockIdx.x - tile_blocks) * 4 + threadIdx.x / kWave; c < ncand; c += nstride) {
+    const i64 cc = c < cap_cands ? c : cap_cands - 1;
+    const i64 v = cand_scan[cc];
+    const int32_t cnt = kLdsScan ? scan_leaf(cand_scan[cc + 1]) - scan_leaf(v) : (int32_t)cand_counts[cc];
+    const int4 co = cand_origin[cc];
+    const u64 word = cand_child[cc * 64 + lane];
+    const uint16_t pre = cand_prefix[cc * 64 + lane];
+    if (c >= cap_cands) break;  // cannot happen for a consistent count
+    if (cnt == 0) continue;  // uniform per wave
+    const i64 lo = scan_lower(v);
+    const int32_t lb = scan_leaf(v);
+    if (lo < 0 || lo >= n_lower || lb < 0 || (i64)lb + cnt > n_leaf) continue;  // consistency guard
+    const int32_t g = utile[co.w].w;
+    lower_mask[lo * 64 + lane] = word;
+    lower_prefix[lo * 64 + lane] = pre;
+    if (lane == 0) {
+      lower_origin[lo] = make_int4(co.x, co.y, co.z, upper_excl[co.w]);
+      lower_first[lo] = lb;
     }
-    const u64 ww = __shfl(word, w, kWave);
-    const int pw = __shfl(pre_i, w, kWave);
-    if (r >= cnt) continue;
-    const int bit = w * 64 + select_bit(ww, r - pw);  // (x*16 + y)*16 + z
-    const int px = bit >> 8, py = (bit >> 4) & 15, pz = bit & 15;
-    const i64 idx = (i64)lb + r;
-    leaf_origin[idx] = make_int4(co.x + px * 8, co.y + py * 8, co.z + pz * 8, g);
-    leaf_parent[idx] = (int32_t)lo;
-    leaf_cand[idx] = (int32_t)c;
+    // leaf records in output order, 64 at a time: lane j takes leaf r = k0 + j, finds
+    // its word (last word whose prefix is <= r, by binary search over the lanes'
+    // prefixes) and bit, so consecutive lanes store consecutive records
+    // Dense candidates (at least kNodesDense leaves) go word by word instead:
+    // for each non-empty word j (a wave-uniform loop), lane l writes the record
+    // of its l-th set bit, so no lane searches (a full word needs no select).
+    const int pre_i = pre;
+    auto put = [&](int r, int bit) {
+      const int px = bit >> 8, py = (bit >> 4) & 15, pz = bit & 15;
+      const i64 idx = (i64)lb + r;
+      leaf_origin[idx] = make_int4(co.x + px * 8, co.y + py * 8, co.z + pz * 8, g);
+      leaf_parent[idx] = (int32_t)lo;
+      leaf_cand[idx] = (int32_t)c;
+    };
+    if (cnt >= kNodesDense) {  // uniform
+      u64 ne = (u64)__ballot(word != 0);
+      while (ne) {
+        const int j = __builtin_ctzll(ne);
+        ne &= ne - 1;
+        const u64 wj = ((u64)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(word >> 32), j) << 32) |
+                       (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)word, j);
+        const int pj = __builtin_amdgcn_readlane(pre_i, j);
+        const int pc = popc64(wj);
+        if (lane < pc) put(pj + lane, j * 64 + (pc == 64 ? lane : select_bit(wj, lane)));
+      }
+      continue;
+    }
+    for (int32_t k0 = 0; k0 < cnt; k0 += kWave) {
+      const int32_t r = k0 + lane;
+      int w = 0;
+#pragma unroll
+      for (int step = 32; step >= 1; step >>= 1) {
+        const int p = __shfl(pre_i, w + step, kWave);
+        if (w + step < kWave && p <= r) w += step;
+      }
+      const u64 ww = __shfl(word, w, kWave);
+      const int pw = __shfl(pre_i, w, kWave);
+      if (r >= cnt) continue;
+      put(r, w * 64 + select_bit(ww, r - pw));  // bit (x*16 + y)*16 + z
+    }
   }
 }
 
@@ -717,7 +741,9 @@ void tree_write_nodes_counted(TreeScratch& ts, const GridView& out, int32_t* lea
 
 void tree_write_nodes(TreeScratch& ts, const GridView& out, int32_t* leaf_cand, hipStream_t s) {
   const i64 tile_blocks = ts.cap_tiles;
-  launch("k_write_nodes", k_write_nodes, tile_blocks + ceil_div(ts.cap_cands, 4), 256, s, (int32_t)tile_blocks,
+  // candidate workgroups: one resident round at most (the waves loop over the candidates)
+  const i64 cand_blocks = std::min(ceil_div(ts.cap_cands, 4), (i64)device_cu_count() * 8);
+  launch("k_write_nodes", k_write_nodes, tile_blocks + cand_blocks, 256, s, (int32_t)tile_blocks,
          (const int4*)ts.utile, (const u64*)ts.tile_child, (const uint16_t*)ts.tile_prefix,
          (const int32_t*)ts.tile_lower_base, (const int4*)ts.cand_origin, (const u64*)ts.cand_child,
          (const uint16_t*)ts.cand_prefix, (const i64*)ts.cand_counts, (const i64*)ts.cand_scan,

@@ -1231,32 +1231,38 @@ __device__ __forceinline__ bool subblock_nonempty(const u64 W[8], const I3& q) {
 // ORs its non-zero words with device-scope atomics, far fewer than one per
 // target leaf. (Box ops mark from the target side, below.)
 
-// Refine: one workgroup per source lower marks, in LDS copies of its 8 target
-// lowers' 16^3 masks, the non-empty 2^3 sub-blocks of its leaves; each target
-// lower has this one source, so the workgroup stores the whole masks with their
-// prefixes and counts.
+// Refine: two workgroups per source lower, one per half along x (the leaves
+// with local x < 8 come first in x-major order, so each half is a contiguous
+// range of leaves, and its children land in the 4 target lowers of that x
+// octant only). A workgroup marks, in LDS copies of its 4 target lowers' 16^3
+// masks, the non-empty 2^3 sub-blocks of its leaves; each target lower has this
+// one source, so the workgroup stores the whole masks with their prefixes and
+// counts (wave v: target 4h + v). Halving the lower keeps the largest
+// workgroups short.
 __global__ void __launch_bounds__(256) k_leaf_mark_lower(const int4* leaf_origin, const u64* leaf_mask,
                                                          const int32_t* lower_first, const u64* lower_mask,
                                                          const uint16_t* lower_prefix, int op, int m,
                                                          const int32_t* lower_nbr, const int32_t* d_num_cands,
                                                          u64* cand_child, uint16_t* cand_prefix,
                                                          i64* cand_counts, int32_t* flags) {
-  constexpr int kFlush = 8 * 64 / 256;  // target words per thread (m == 8)
-  constexpr int kPer = 1;               // leaves per thread per batch
-  __shared__ unsigned long long s_mask[8 * 64];
-  const i64 l = blockIdx.x;
-  // loads indexed by the lower alone, first: its leaf range and the candidates
-  // its target lowers became
-  const i64 first = lower_first[l];
-  const int count = lower_prefix[l * 64 + 63] + popc64(lower_mask[l * 64 + 63]);
+  constexpr int kPer = 1;  // leaves per thread per batch
+  __shared__ unsigned long long s_mask[4 * 64];
+  const i64 l = blockIdx.x >> 1;
+  const int h = (int)(blockIdx.x & 1);
+  const int wv = threadIdx.x / kWave;
+  // loads indexed by the lower alone, first: its leaf range (words 0..31 hold
+  // x < 8) and the candidate its wave's target lower became
+  const i64 first0 = lower_first[l];
+  const int half = lower_prefix[l * 64 + 32];  // leaves with x < 8
+  const int total = lower_prefix[l * 64 + 63] + popc64(lower_mask[l * 64 + 63]);
   const int32_t ncand = *d_num_cands;
-  int32_t nbr[kFlush];
-#pragma unroll
-  for (int r = 0; r < kFlush; ++r) nbr[r] = lower_nbr[l * m + min((r * 256 + (int)threadIdx.x) >> 6, m - 1)];
-  for (int k = threadIdx.x; k < m * 64; k += 256) s_mask[k] = 0;
+  const int32_t nbr = lower_nbr[l * m + 4 * h + wv];  // m == 8
+  s_mask[threadIdx.x] = 0;
+  const i64 first = first0 + (h ? half : 0);
+  const int count = h ? total - half : half;
   __syncthreads();
   // leaves kPer * 256 at a time, the next batch's loads issued before this
-  // batch is marked (a dense lower has up to 4096 leaves)
+  // batch is marked (half a dense lower has up to 2048 leaves)
   int4 o[kPer];
   u64 W[kPer][8];
   auto load_batch = [&](int k0) {
@@ -1284,43 +1290,40 @@ __global__ void __launch_bounds__(256) k_leaf_mark_lower(const int4* leaf_origin
       if (k0 + u * 256 + (int)threadIdx.x >= count) continue;
       const i64 mx = oc[u].x >> 3, my = oc[u].y >> 3, mz = oc[u].z >> 3;  // leaf coordinates
       const i64 lx = mx & 15, ly = my & 15, lz = mz & 15;              // position inside the lower
-      {
-        const int j = octant_index(lx >> 3, ly >> 3, lz >> 3);  // all children share one target lower
+      if ((int)(lx >> 3) != h) {  // cannot happen for a consistent lower
+        set_flag(flags, kFlagInternal);
+        continue;
+      }
+      const int j = octant_index(0, ly >> 3, lz >> 3);  // all children share one target lower (4h + j)
 #pragma unroll
-        for (int qx = 0; qx < 2; ++qx) {
-          u64 word = 0;
-          const i64 x = (2 * lx + qx) & 15;
+      for (int qx = 0; qx < 2; ++qx) {
+        u64 word = 0;
+        const i64 x = (2 * lx + qx) & 15;
 #pragma unroll
-          for (int qy = 0; qy < 2; ++qy)
+        for (int qy = 0; qy < 2; ++qy)
 #pragma unroll
-            for (int qz = 0; qz < 2; ++qz) {
-              const I3 q{qx, qy, qz};
-              if (!subblock_nonempty(Wc[u], q)) continue;
-              if (!leaf_ok(2 * mx + qx) || !leaf_ok(2 * my + qy) || !leaf_ok(2 * mz + qz)) {
-                set_flag(flags, kFlagOverflow);
-                continue;
-              }
-              word |= 1ull << ((((2 * ly + qy) & 3) * 16) + ((2 * lz + qz) & 15));
+          for (int qz = 0; qz < 2; ++qz) {
+            const I3 q{qx, qy, qz};
+            if (!subblock_nonempty(Wc[u], q)) continue;
+            if (!leaf_ok(2 * mx + qx) || !leaf_ok(2 * my + qy) || !leaf_ok(2 * mz + qz)) {
+              set_flag(flags, kFlagOverflow);
+              continue;
             }
-          // children with this qx share the word x*4 + (y >> 2) of the target mask
-          if (word) atomicOr(&s_mask[j * 64 + x * 4 + (((2 * ly) & 15) >> 2)], word);
-        }
+            word |= 1ull << ((((2 * ly + qy) & 3) * 16) + ((2 * lz + qz) & 15));
+          }
+        // children with this qx share the word x*4 + (y >> 2) of the target mask
+        if (word) atomicOr(&s_mask[j * 64 + x * 4 + (((2 * ly) & 15) >> 2)], word);
       }
     }
   }
   __syncthreads();
-  // wave v of round r flushes target 4r + v (its 64 words), whole waves at a time
-#pragma unroll
-  for (int r = 0; r < kFlush; ++r) {
-    const int k = r * 256 + threadIdx.x;
-    const u64 word = s_mask[k];
-    const int32_t c = nbr[r];  // uniform per wave
-    if (c < 0 || c >= ncand) {
-      if (word) set_flag(flags, kFlagInternal);  // a marked target must have a candidate
-      continue;
-    }
-    store_candidate(c, word, cand_child, cand_prefix, cand_counts);
+  // wave v flushes target 4h + v (its 64 words)
+  const u64 word = s_mask[threadIdx.x];
+  if (nbr < 0 || nbr >= ncand) {  // uniform per wave
+    if (word) set_flag(flags, kFlagInternal);  // a marked target must have a candidate
+    return;
   }
+  store_candidate(nbr, word, cand_child, cand_prefix, cand_counts);
 }
 
 // Coarsen: one wave per candidate lower T, pulling from the source lowers of its
@@ -2338,7 +2341,7 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, 
     // leaves: every candidate's 16^3 mask, its prefix table and packed count
     // (each candidate is written by exactly one wave or workgroup)
     if (op == TC_OP_REFINE) {
-      launch("k_leaf_mark_lower", k_leaf_mark_lower, (i64)src->n1, 256, s, (const int4*)sv.leaf_origin,
+      launch("k_leaf_mark_lower", k_leaf_mark_lower, 2 * (i64)src->n1, 256, s, (const int4*)sv.leaf_origin,
              (const u64*)sv.leaf_mask, (const int32_t*)sv.lower_first, (const u64*)sv.lower_mask,
              (const uint16_t*)sv.lower_prefix, op, oi.m, (const int32_t*)lower_nbr, (const int32_t*)ts.d_num_cands,
              ts.cand_child, ts.cand_prefix, ts.cand_counts, ts.flags);

@@ -141,17 +141,28 @@ __device__ __forceinline__ int wave_max_i32(int v) {
 //           zmax<<15 (3 bits each); kEmptyBox for an empty mask
 constexpr uint32_t kEmptyBox = 0xffffffffu;
 
+// Bit k of the result is set when byte k of w (8 bytes) is non-zero.
+__device__ __forceinline__ uint32_t nonzero_bytes(uint64_t w) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t x = (uint32_t)(w >> (32 * h));
+    uint32_t t = (((x & 0x7f7f7f7fu) + 0x7f7f7f7fu) | x) & 0x80808080u;  // top bit of a non-zero byte
+    t >>= 7;                                                             // bits 0, 8, 16, 24
+    t = (t | (t >> 7) | (t >> 14) | (t >> 21)) & 0xfu;
+    m |= t << (4 * h);
+  }
+  return m;
+}
+
 __device__ __forceinline__ void leaf_stats(const uint64_t W[8], uint64_t& prefix, int& count, uint32_t& box) {
-  uint64_t packed = 0, run = 0, orw = 0;
-  int xmin = 8, xmax = -1;
+  uint64_t packed = 0, orw = 0;
+  uint32_t run = 0, nzw = 0;  // running popcount; non-empty words (bit k: word k = x)
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    if (k > 0) packed |= run << (9 * (k - 1));
-    run += (uint64_t)__popcll(W[k]);
-    if (W[k]) {
-      xmin = min(xmin, k);
-      xmax = max(xmax, k);
-    }
+    if (k > 0) packed |= (uint64_t)run << (9 * (k - 1));
+    run += (uint32_t)__popcll(W[k]);
+    nzw |= (W[k] != 0 ? 1u : 0u) << k;
     orw |= W[k];
   }
   prefix = packed;
@@ -161,19 +172,13 @@ __device__ __forceinline__ void leaf_stats(const uint64_t W[8], uint64_t& prefix
     return;
   }
   // y extent: non-zero bytes of the OR of all words; z extent: OR of those bytes
-  int ymin = 8, ymax = -1;
-  uint64_t zor = 0;
-#pragma unroll
-  for (int y = 0; y < 8; ++y) {
-    const uint64_t byte = (orw >> (8 * y)) & 0xffull;
-    if (byte) {
-      ymin = min(ymin, y);
-      ymax = max(ymax, y);
-    }
-    zor |= byte;
-  }
-  const int zmin = __builtin_ctzll(zor);
-  const int zmax = 63 - __builtin_clzll(zor);
+  const uint32_t nzy = nonzero_bytes(orw);
+  uint32_t zor = (uint32_t)orw | (uint32_t)(orw >> 32);
+  zor |= zor >> 16;
+  zor = (zor | (zor >> 8)) & 0xffu;
+  const int xmin = __builtin_ctz(nzw), xmax = 31 - __builtin_clz(nzw);
+  const int ymin = __builtin_ctz(nzy), ymax = 31 - __builtin_clz(nzy);
+  const int zmin = __builtin_ctz(zor), zmax = 31 - __builtin_clz(zor);
   box = (uint32_t)(xmin | (xmax << 3) | (ymin << 6) | (ymax << 9) | (zmin << 12) | (zmax << 15));
 }
 

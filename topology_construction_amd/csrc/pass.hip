@@ -1737,15 +1737,18 @@ __device__ __forceinline__ u64 double_bits4(u64 b) {
 }
 
 // Refine: output rows 2r, 2r+1 and bits 2c, 2c+1 come from row 4qy + r, bit 4qz + c of w.
+// The four source rows are the 32-bit half qy of w (one byte each); their nibble
+// qz, one per byte, has every bit doubled in place, and each byte then fills two
+// 8-bit output rows.
 __device__ __forceinline__ u64 refine_word(u64 w, int qy, int qz) {
-  u64 out = 0;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const u64 nib = (w >> ((4 * qy + r) * 8 + 4 * qz)) & 0xfull;
-    const u64 b = double_bits4(nib);
-    out |= (b << (16 * r)) | (b << (16 * r + 8));
-  }
-  return out;
+  uint32_t t = (uint32_t)(w >> (32 * qy));
+  t = (t >> (4 * qz)) & 0x0f0f0f0fu;   // nibble of row r in byte r
+  t = (t | (t << 2)) & 0x33333333u;    // bits 0..3 -> 0, 1, 4, 5
+  t = (t | (t << 1)) & 0x55555555u;    // -> 0, 2, 4, 6
+  t |= t << 1;                         // doubled: byte r = row 2r's bits
+  const uint32_t lo = (t & 0xffu) | ((t & 0xff00u) << 8);            // rows 0, 1 -> bytes 0, 2
+  const uint32_t hi = ((t >> 16) & 0xffu) | ((t >> 8) & 0xff0000u);  // rows 2, 3 -> bytes 0, 2
+  return ((u64)(hi | (hi << 8)) << 32) | (lo | (lo << 8));           // each byte twice
 }
 
 // Coarsen: OR each 2x2x2 block of the source into one bit, giving a 4^3 block

@@ -2273,9 +2273,10 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, 
       // the bitmaps are zeroed in-kernel when few (at most 1 MiB for one workgroup):
       // by the fused lower stage, or here; otherwise by a wide fill
       const bool zero_here = !small_lowers && nT <= 256;
-      // many source uppers: their reach sets in a wide launch first
+      // more source uppers than one round of the tile stage's in-kernel reach (64:
+      // sixteen waves of four): their reach sets in a wide launch first
       uint32_t* ureach = box_lreach ? a.at<uint32_t>(o_ureach) : nullptr;
-      if (!box_lreach && op != TC_OP_COARSEN && src->n2 > 128) {
+      if (!box_lreach && op != TC_OP_COARSEN && src->n2 > 64) {
         ureach = a.at<uint32_t>(o_ureach);
         launch("k_node_reach", k_node_reach, ceil_div((i64)src->n2, 4), 256, s, (const u64*)sv.upper_mask,
                (i64)src->n2, 512, op, oi.m, ureach);

@@ -153,7 +153,9 @@ def test_torch_allocator_uses_the_given_stream():
     s.synchronize()
     fo = {k: v.cpu().numpy() for k, v in out.fields().items()}
     fo["headers"] = headers_as_oracle(out.headers(stream=s))
-    fo["ijk"] = binding.tc_enumerate_ijk(out, stream=s).cpu().numpy()
+    ijk_s = binding.tc_enumerate_ijk(out, stream=s)
+    s.synchronize()  # written on s: the copy below runs on the current stream
+    fo["ijk"] = ijk_s.cpu().numpy()
     assert_same(fo, ref, "non-current stream")
 
 

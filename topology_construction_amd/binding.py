@@ -193,6 +193,17 @@ def _torch_stream(handle: int):
     return st
 
 
+def _empty_on(stream, shape, dtype):
+    """torch.empty taken on `stream`, the stream the library writes the tensor on
+    (the current stream when None), so torch's caching allocator orders its
+    reuse after that stream's work."""
+    import torch
+    if stream is None:
+        return torch.empty(shape, dtype=dtype, device="cuda")
+    with torch.cuda.stream(stream):
+        return torch.empty(shape, dtype=dtype, device="cuda")
+
+
 def _torch_alloc(ctx, nbytes, stream):
     """Allocator callback: a uint8 tensor from torch's caching allocator, taken
     on the stream the library will use it on (so that torch hands the block to
@@ -420,12 +431,14 @@ def tc_build_masked_refine(src: GridBatch, keep, factor: int, stream=None, alloc
 
 
 def tc_enumerate_ijk(batch: GridBatch, out=None, stream=None):
-    """Jagged voxel enumeration int32 [V, 3] (grid after grid, canonical order)."""
+    """Jagged voxel enumeration int32 [V, 3] (grid after grid, canonical order),
+    written on `stream` (torch's current stream when None): a reader on another
+    stream synchronizes with it first."""
     import torch
     lib = load_library()
     total = batch.voxel_total(stream)
     if out is None:
-        out = torch.empty((total, 3), dtype=torch.int32, device="cuda")
+        out = _empty_on(stream, (total, 3), torch.int32)
     cap = out.shape[0] if out.dim() == 2 else out.numel() // 3
     _check(lib.tc_enumerate_ijk(batch.handle, ctypes.c_void_p(out.data_ptr() if out.numel() else 0), int(cap),
                                 _stream_handle(stream)))
@@ -447,7 +460,7 @@ def tc_enumerate_ijk_many(batches, stream=None) -> list:
     for t in totals:
         starts.append(at)
         at += (t + 3) // 4 * 4  # rows of 12 bytes: a multiple of 4 rows keeps 16-byte alignment
-    buf = torch.empty((max(at, 1), 3), dtype=torch.int32, device="cuda")
+    buf = _empty_on(stream, (max(at, 1), 3), torch.int32)
     base = buf.data_ptr()
     outs = (ctypes.c_void_p * n)(*[base + 12 * a if t else 0 for a, t in zip(starts, totals)])
     caps = (ctypes.c_int64 * n)(*totals)
@@ -466,7 +479,7 @@ def tc_build_kernel_map(src: GridBatch, dst: GridBatch, kernel_size: int, stride
     kk = int(kernel_size) ** 3
     rows = dst.voxel_total(stream)
     if out is None:
-        out = torch.empty((rows, kk), dtype=torch.int32, device="cuda")
+        out = _empty_on(stream, (rows, kk), torch.int32)
     _check(lib.tc_build_kernel_map(src.handle, dst.handle, int(kernel_size), int(stride), int(bool(transposed)),
                                    ctypes.c_void_p(out.data_ptr() if out.numel() else 0), int(out.numel()),
                                    _stream_handle(stream)))

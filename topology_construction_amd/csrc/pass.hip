@@ -1223,13 +1223,9 @@ __device__ __forceinline__ bool subblock_nonempty(const u64 W[8], const I3& q) {
   return (xs & ym & zm) != 0;
 }
 
-// Refine and coarsen. One workgroup per source lower node: every leaf of that
-// lower marks its non-empty target leaves in LDS copies of the (at most 8)
-// target lowers' 16^3 masks, then the block flushes whole 64-bit words to the
-// candidate lowers. For refine each target lower has exactly one source lower,
-// so the flush is a plain store of all 64 words (no zero-fill needed); coarsen
-// ORs its non-zero words with device-scope atomics, far fewer than one per
-// target leaf. (Box ops mark from the target side, below.)
+// Leaf marking: refine from the source side (a target lower has exactly one
+// source lower, so its mask is stored whole, no zero fill), coarsen and the box
+// ops from the target side (below).
 
 // Refine: two workgroups per source lower, one per half along x (the leaves
 // with local x < 8 come first in x-major order, so each half is a contiguous

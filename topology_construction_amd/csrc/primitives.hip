@@ -49,35 +49,44 @@ __device__ __forceinline__ T tile_scan_striped(const T v[kScanItems], T ex[kScan
   return total;
 }
 
-// Single-workgroup scans (up to kScanSingleTiles tiles) hold items blocked:
-// thread t owns items t*kScanItems .. +kScanItems-1 of the current tile, which
-// needs one block scan per tile; the next tile's loads are issued before the
-// current one is scanned. These launches are latency-bound, so fewer steps (and
-// one launch instead of three) beat coalescing.
-constexpr int kScanSingleTiles = 16;
+// Single-workgroup scans (up to kScanSingleMax items, one workgroup of NT
+// threads) hold items blocked: thread t owns items t*I .. +I-1 of the current
+// tile of NT I items (I = 16, or 8 for 8-byte items in 1024-thread workgroups
+// so that the next tile's registers fit beside the current one's), which needs
+// one block scan per tile; the next tile's loads are issued before the current
+// one is scanned. These launches are latency-bound, so fewer steps (and one
+// launch instead of three) beat coalescing: scans of more than kScanSingleWide
+// items take a 1024-thread workgroup (fewer steps), smaller ones 256 threads
+// (a shorter launch and block scan).
+constexpr i64 kScanSingleMax = 65536;
+constexpr i64 kScanSingleWide = 16384;
+template <typename T, int NT>
+constexpr int kScanSingleItems = sizeof(T) == 8 && NT > 256 ? 8 : 16;
 
-template <typename T>
-__global__ void __launch_bounds__(kScanThreads) k_scan_single(const T* in, T* out, i64 n_host,
-                                                              const int32_t* d_n, T* total_out) {
-  __shared__ T s_wave[kScanThreads / kWave];
+template <typename T, int NT>
+__global__ void __launch_bounds__(NT) k_scan_single(const T* in, T* out, i64 n_host, const int32_t* d_n,
+                                                    T* total_out) {
+  constexpr int I = kScanSingleItems<T, NT>;
+  constexpr i64 kTile = (i64)NT * I;
+  __shared__ T s_wave[NT / kWave];
   const i64 n = clamp_n(n_host, d_n);
-  const i64 tb = (i64)threadIdx.x * kScanItems;
-  T v[kScanItems];
+  const i64 tb = (i64)threadIdx.x * I;
+  T v[I];
 #pragma unroll
-  for (int k = 0; k < kScanItems; ++k) v[k] = tb + k < n ? in[tb + k] : T(0);
+  for (int k = 0; k < I; ++k) v[k] = tb + k < n ? in[tb + k] : T(0);
   T carry = 0;
-  for (i64 c = 0; c < n; c += kScanTile) {  // uniform
-    T nx[kScanItems];
-    const i64 nb = c + kScanTile + tb;
+  for (i64 c = 0; c < n; c += kTile) {  // uniform
+    T nx[I];
+    const i64 nb = c + kTile + tb;
 #pragma unroll
-    for (int k = 0; k < kScanItems; ++k) nx[k] = nb + k < n ? in[nb + k] : T(0);
+    for (int k = 0; k < I; ++k) nx[k] = nb + k < n ? in[nb + k] : T(0);
     T sum = 0;
 #pragma unroll
-    for (int k = 0; k < kScanItems; ++k) sum += v[k];
+    for (int k = 0; k < I; ++k) sum += v[k];
     T total;
-    T excl = block_excl_scan<T, kScanThreads>(sum, s_wave, total) + carry;
+    T excl = block_excl_scan<T, NT>(sum, s_wave, total) + carry;
 #pragma unroll
-    for (int k = 0; k < kScanItems; ++k) {
+    for (int k = 0; k < I; ++k) {
       const i64 i = c + tb + k;
       if (i < n) out[i] = excl;
       excl += v[k];
@@ -163,7 +172,7 @@ __global__ void __launch_bounds__(kScanThreads) k_scan_down(const T* in, T* out,
 }
 
 size_t scan_tmp_bytes(i64 n_host, size_t elem) {
-  return n_host <= (i64)kScanTile * kScanSingleTiles ? 0 : elem * (size_t)ceil_div(n_host, kScanTile);
+  return n_host <= kScanSingleMax ? 0 : elem * (size_t)ceil_div(n_host, kScanTile);
 }
 
 template <typename T>
@@ -172,12 +181,16 @@ static void scan_excl(const char* tag, const T* in, T* out, i64 n_host, const in
   (void)tag;
   if (n_host <= 0) {
     // n is zero: out[0] = 0
-    launch("k_scan_single", k_scan_single<T>, 1, kScanThreads, s, in, out, (i64)0, (const int32_t*)nullptr,
+    launch("k_scan_single", k_scan_single<T, 256>, 1, 256, s, in, out, (i64)0, (const int32_t*)nullptr,
            total_out);
     return;
   }
-  if (n_host <= (i64)kScanTile * kScanSingleTiles) {
-    launch("k_scan_single", k_scan_single<T>, 1, kScanThreads, s, in, out, n_host, d_n, total_out);
+  if (n_host <= kScanSingleWide) {
+    launch("k_scan_single", k_scan_single<T, 256>, 1, 256, s, in, out, n_host, d_n, total_out);
+    return;
+  }
+  if (n_host <= kScanSingleMax) {
+    launch("k_scan_single", k_scan_single<T, 1024>, 1, 1024, s, in, out, n_host, d_n, total_out);
     return;
   }
   const i64 nblk = ceil_div(n_host, kScanTile);

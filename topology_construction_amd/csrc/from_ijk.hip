@@ -869,10 +869,10 @@ tc_grid_batch* build_from_ijk(const int32_t* d_ijk, const int64_t* h_off, int32_
          (const int32_t*)ts.tile_lower_base, (const int32_t*)ts.d_num_cands, vcand, ts.cand_origin, ts.cand_child,
          ts.flags);
   a_tab.reset();
-  tree_counts(ts, B, s);
   const size_t rb_bytes = 4 * (4 + 3 * (size_t)B);
   int32_t* h_rb = static_cast<int32_t*>(pinned_staging(rb_bytes));
-  hip_check(hipMemcpyAsync(h_rb, ts.readback, rb_bytes, hipMemcpyDeviceToHost, s), "readback");
+  if (!tree_counts(ts, B, s, h_rb))  // else the counts stage wrote the words into h_rb
+    hip_check(hipMemcpyAsync(h_rb, ts.readback, rb_bytes, hipMemcpyDeviceToHost, s), "readback");
   hip_check(hipStreamSynchronize(s), "hipStreamSynchronize");
   if (h_rb[0] != 0) throw Error(TC_ERR_INTERNAL, "from_ijk: device consistency check failed");
 

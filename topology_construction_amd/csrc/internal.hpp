@@ -332,14 +332,18 @@ struct TreeScratch {
 
 // Launch groups (implemented in tree.hip).
 void tree_tile_ranges(TreeScratch& t, int32_t B, hipStream_t s);
-void tree_grid_counts(TreeScratch& t, int32_t B, hipStream_t s);
+// The counts stages below also write the readback words (flag word, totals,
+// per-grid counts) to `host_rb` (pinned host memory, or null) when one
+// workgroup computes them all; they return whether they did, else the caller
+// copies the words back itself.
+bool tree_grid_counts(TreeScratch& t, int32_t B, hipStream_t s, int32_t* host_rb = nullptr);
 void tree_rank_tiles(TreeScratch& t, hipStream_t s);
 // tree_rank_tiles and the candidate -> source table's fill (nc * m_src entries
 // of cand_src set to -1) in one launch, for at most 4096 tile slots; done_ctr is
 // a device word zeroed before the launch (by the tile stage).
 void tree_rank_tiles_last(TreeScratch& t, int32_t* done_ctr, int32_t* cand_src, int32_t m_src, hipStream_t s);            // prefix per tile + scan -> cand numbering
 void tree_count_cands(TreeScratch& t, hipStream_t s);           // leaf counts per cand + their scan
-void tree_counts(TreeScratch& t, int32_t B, hipStream_t s);     // tree_count_cands + tree_grid_counts (fused when small)
+bool tree_counts(TreeScratch& t, int32_t B, hipStream_t s, int32_t* host_rb = nullptr);  // tree_count_cands + tree_grid_counts (fused when small)
 void tree_write_nodes(TreeScratch& t, const GridView& out, int32_t* leaf_cand, hipStream_t s);
 // tree_counts and tree_write_nodes in one launch, for at most 2048 candidate and
 // tile slots once the marking wrote the candidates' counts (..._fits says when).

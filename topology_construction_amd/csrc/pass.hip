@@ -2365,14 +2365,17 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, 
     ts.cand_counts_ready = true;
     // counts (small batches whose lower stage ran in one workgroup: inside the
     // node writer's launch below)
+    // (exact layout: the one-workgroup counts stages write the readback words
+    // straight into pinned host memory, the others leave them for a copy)
     const bool counted_writer = bounded && small_lowers && write_nodes_counted_fits(ts, B);
-    if (!counted_writer) tree_counts(ts, B, s);
+    const size_t rb_bytes = 4 * (4 + 3 * (size_t)B);
+    int32_t* h_rb = bounded ? nullptr : static_cast<int32_t*>(pinned_staging(rb_bytes));
+    bool rb_written = false;
+    if (!counted_writer) rb_written = tree_counts(ts, B, s, h_rb);
     if (bounded) {  // capacity layout: allocated while the stages above run
       out = new_batch_capacity(B, nT, nL, L_cap, oa);
     } else {  // exact layout: counts first, then the allocation
-      const size_t rb_bytes = 4 * (4 + 3 * (size_t)B);
-      int32_t* h_rb = static_cast<int32_t*>(pinned_staging(rb_bytes));
-      hip_check(hipMemcpyAsync(h_rb, ts.readback, rb_bytes, hipMemcpyDeviceToHost, s), "readback");
+      if (!rb_written) hip_check(hipMemcpyAsync(h_rb, ts.readback, rb_bytes, hipMemcpyDeviceToHost, s), "readback");
       hip_check(hipStreamSynchronize(s), "hipStreamSynchronize");
       check_pass_flags(h_rb[0]);
       out = new_batch(B, h_rb, oa);

@@ -237,7 +237,7 @@ __device__ __forceinline__ void stage_tile_bases(const int32_t* tile_lower_base,
 __device__ __forceinline__ void counts_tail_body(const int32_t* grid_tile_begin, int2 gt, const int32_t* s_tlb,
                                                  const i64* cs, int32_t nt, int32_t nc, int32_t B, int32_t* s_uex,
                                                  int32_t* upper_excl, int32_t* grid_info, int32_t* readback,
-                                                 int32_t* s_wave) {
+                                                 int32_t* s_wave, int32_t* host_rb) {
   const int tid = threadIdx.x;
   int32_t lv[kTailItems + 1];
 #pragma unroll
@@ -267,6 +267,12 @@ __device__ __forceinline__ void counts_tail_body(const int32_t* grid_tile_begin,
     readback[1] = total;
     readback[2] = scan_lower(last);
     readback[3] = scan_leaf(last);
+    if (host_rb) {  // the flag word as the earlier launches left it (this one sets none)
+      host_rb[0] = readback[0];
+      host_rb[1] = total;
+      host_rb[2] = scan_lower(last);
+      host_rb[3] = scan_leaf(last);
+    }
   }
   __syncthreads();
   for (int32_t g = tid; g < B; g += kTailThreads) {
@@ -285,6 +291,11 @@ __device__ __forceinline__ void counts_tail_body(const int32_t* grid_tile_begin,
     readback[4 + g * 3 + 0] = nu;
     readback[4 + g * 3 + 1] = n1;
     readback[4 + g * 3 + 2] = nl;
+    if (host_rb) {
+      host_rb[4 + g * 3 + 0] = nu;
+      host_rb[4 + g * 3 + 1] = n1;
+      host_rb[4 + g * 3 + 2] = nl;
+    }
   }
 }
 
@@ -298,7 +309,7 @@ __global__ void __launch_bounds__(kTailThreads) k_counts_tail(const int32_t* gri
                                                               const i64* cand_scan, const int32_t* d_num_tiles,
                                                               const int32_t* d_num_cands, int32_t B,
                                                               int32_t* upper_excl, int32_t* grid_info,
-                                                              int32_t* readback) {
+                                                              int32_t* readback, int32_t* host_rb) {
   __shared__ int32_t s_tlb[kTailTiles + 1];
   __shared__ int32_t s_uex[kTailTiles + 1];
   __shared__ int32_t s_wave[kTailThreads / kWave];
@@ -306,7 +317,8 @@ __global__ void __launch_bounds__(kTailThreads) k_counts_tail(const int32_t* gri
   const int2 gt = load_grid_tiles(grid_tile_begin, B);
   stage_tile_bases(tile_lower_base, cap_t, s_tlb);
   __syncthreads();
-  counts_tail_body(grid_tile_begin, gt, s_tlb, cand_scan, nt, nc, B, s_uex, upper_excl, grid_info, readback, s_wave);
+  counts_tail_body(grid_tile_begin, gt, s_tlb, cand_scan, nt, nc, B, s_uex, upper_excl, grid_info, readback, s_wave,
+                   host_rb);
 }
 
 // Small batches (at most kCountsSmallMax candidates and kTailTiles tiles):
@@ -323,7 +335,8 @@ __global__ void __launch_bounds__(kTailThreads) k_counts_small(const u64* cand_c
                                                                const int32_t* d_num_tiles,
                                                                const int32_t* d_num_cands, int32_t B,
                                                                int32_t* upper_excl, int32_t* grid_info,
-                                                               int32_t* readback, int counts_ready) {
+                                                               int32_t* readback, int counts_ready,
+                                                               int32_t* host_rb) {
   __shared__ i64 s_cc[kCountsSmallMax + 1];
   __shared__ int32_t s_tlb[kTailTiles + 1];
   __shared__ int32_t s_uex[kTailTiles + 1];
@@ -390,20 +403,21 @@ __global__ void __launch_bounds__(kTailThreads) k_counts_small(const u64* cand_c
     s_cc[nc] = total;
   }
   __syncthreads();
-  counts_tail_body(grid_tile_begin, gt, s_tlb, s_cc, nt, nc, B, s_uex, upper_excl, grid_info, readback, s_wave);
+  counts_tail_body(grid_tile_begin, gt, s_tlb, s_cc, nt, nc, B, s_uex, upper_excl, grid_info, readback, s_wave,
+                   host_rb);
 }
 
-void tree_counts(TreeScratch& ts, int32_t B, hipStream_t s) {
+bool tree_counts(TreeScratch& ts, int32_t B, hipStream_t s, int32_t* host_rb) {
   if (ts.cap_cands <= kCountsSmallMax && ts.cap_tiles <= (i64)kTailThreads * kTailItems) {
     launch("k_counts_small", k_counts_small, 1, kTailThreads, s, (const u64*)ts.cand_child, (int32_t)ts.cap_cands,
            ts.cand_prefix, ts.cand_counts, ts.cand_scan, (const int32_t*)ts.grid_tile_begin,
            (const int32_t*)ts.tile_lower_base, (int32_t)ts.cap_tiles, (const int32_t*)ts.d_num_tiles,
            (const int32_t*)ts.d_num_cands, B, ts.upper_excl, ts.grid_info, ts.readback,
-           ts.cand_counts_ready ? 1 : 0);
-    return;
+           ts.cand_counts_ready ? 1 : 0, host_rb);
+    return host_rb != nullptr;
   }
   tree_count_cands(ts, s);
-  tree_grid_counts(ts, B, s);
+  return tree_grid_counts(ts, B, s, host_rb);
 }
 
 void tree_count_cands(TreeScratch& ts, hipStream_t s) {
@@ -413,13 +427,13 @@ void tree_count_cands(TreeScratch& ts, hipStream_t s) {
   scan_excl_i64(ts.cand_counts, ts.cand_scan, ts.cap_cands, ts.d_num_cands, s, nullptr, ts.scan_tmp);
 }
 
-void tree_grid_counts(TreeScratch& ts, int32_t B, hipStream_t s) {
+bool tree_grid_counts(TreeScratch& ts, int32_t B, hipStream_t s, int32_t* host_rb) {
   if (ts.cap_tiles <= (i64)kTailThreads * kTailItems) {
     launch("k_counts_tail", k_counts_tail, 1, kTailThreads, s, (const int32_t*)ts.grid_tile_begin,
            (const int32_t*)ts.tile_lower_base, (int32_t)ts.cap_tiles, (const i64*)ts.cand_scan,
            (const int32_t*)ts.d_num_tiles, (const int32_t*)ts.d_num_cands, B, ts.upper_excl, ts.grid_info,
-           ts.readback);
-    return;
+           ts.readback, host_rb);
+    return host_rb != nullptr;
   }
   launch("k_tile_flags", k_tile_flags, ceil_div(ts.cap_tiles, 256), 256, s, (const int32_t*)ts.tile_lower_base,
          (const i64*)ts.cand_scan, ts.tile_nonempty, (const int32_t*)ts.d_num_tiles);
@@ -427,6 +441,7 @@ void tree_grid_counts(TreeScratch& ts, int32_t B, hipStream_t s) {
   launch("k_grid_counts", k_grid_counts, ceil_div((i64)B, 256), 256, s, (const int32_t*)ts.grid_tile_begin,
          (const int32_t*)ts.tile_lower_base, (const int32_t*)ts.upper_excl, (const i64*)ts.cand_scan,
          (const int32_t*)ts.d_num_tiles, (const int32_t*)ts.d_num_cands, B, ts.grid_info, ts.readback);
+  return false;
 }
 
 // ------------------------------------------------------------------ node writers

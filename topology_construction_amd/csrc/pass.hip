@@ -13,12 +13,14 @@
 //   lowers  each source lower sets its candidate target lowers in the target
 //           tile's 32^3 mask; ranks in those masks number the candidates;
 //   leaves  every non-empty target leaf gets its bit in its target lower's 16^3
-//           mask: refine and coarsen from the source side (one workgroup per
-//           source lower marks its leaves' targets in LDS copies of the target
-//           lowers' masks); the box ops from the target side (one workgroup per
-//           candidate lower collects the facing source leaves of its <= 27
-//           source lowers and ORs their reach into an LDS mask), no device
-//           atomics on masks in either case;
+//           mask: refine from the source side (two workgroups per source
+//           lower, one per x half, mark their leaves' children in LDS copies
+//           of the target lowers' masks); coarsen from the target side (one
+//           wave per candidate lower ORs 2x2x2 blocks of its source lowers'
+//           masks); the box ops from the target side too (workgroups loop
+//           over candidate lowers, collect the facing source leaves of each
+//           one's <= 27 source lowers and OR their reach into an LDS mask); no
+//           device atomics on masks in any case;
 //   counts  popcounts and scans give per-grid counts -> the single readback;
 //   writers node records, then every output leaf gathers its mask from the
 //           (at most 1 / 8 / 27) source leaves that feed it (no atomics); a
@@ -1214,7 +1216,7 @@ __global__ void __launch_bounds__(kTilesThreads) k_nodes_small(
                     lower_reach, po, reach_pre, lds);
 }
 
-// ------------------------------------------------------------------ stage: leaves (pass A)
+// ------------------------------------------------------------------ stage: leaves (marking)
 // Refine: the 4^3 sub-block q of the source leaf becomes child leaf q.
 __device__ __forceinline__ bool subblock_nonempty(const u64 W[8], const I3& q) {
   const u64 xs = q.x ? (W[4] | W[5] | W[6] | W[7]) : (W[0] | W[1] | W[2] | W[3]);

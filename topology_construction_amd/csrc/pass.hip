@@ -2268,9 +2268,13 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, 
              a.at<uint32_t>(o_ureach), box_lreach);
     }
     if (small_tiles) {
-      // the bitmaps are zeroed in-kernel when few (at most 1 MiB for one workgroup):
-      // by the fused lower stage, or here; otherwise by a wide fill
-      const bool zero_here = !small_lowers && nT <= 256;
+      // the bitmaps are zeroed in-kernel (only the live tiles') by the fused
+      // lower stage, or here when few are expected: at most 1 MiB of capacity,
+      // or refine's at most 8 tiles per source upper (up to 4 MiB), or box ops
+      // with voxel-exact reach (only uppers with voxels on a face reach a
+      // neighbour tile; up to 8 MiB of capacity); otherwise by a wide fill
+      const bool zero_here = !small_lowers && (nT <= 256 || (op == TC_OP_REFINE && nT <= 1024) ||
+                                               (box_lreach != nullptr && nT <= 2048));
       // more source uppers than one round of the tile stage's in-kernel reach (64:
       // sixteen waves of four): their reach sets in a wide launch first
       uint32_t* ureach = box_lreach ? a.at<uint32_t>(o_ureach) : nullptr;

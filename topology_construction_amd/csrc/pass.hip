@@ -264,11 +264,21 @@ __device__ __forceinline__ uint32_t upper_word_reach(u64 word, int w, int op) {
 
 // Reach set of every source node, one wave per node (uppers: 8 mask words per
 // lane; lowers: one), for batches too large to do it inside the single-workgroup
-// stages.
+// stages. Workgroups from `lo_block` on take the lowers of a second node set
+// (mask_lo, n_lo, reach_lo), so that the uppers' and the lowers' sets come from
+// one launch.
 __global__ void __launch_bounds__(256) k_node_reach(const u64* mask, i64 n_nodes, int words, int op, int m,
-                                                    uint32_t* reach) {
-  const i64 u = (i64)blockIdx.x * 4 + threadIdx.x / kWave;
+                                                    uint32_t* reach, i64 lo_block, const u64* mask_lo, i64 n_lo,
+                                                    uint32_t* reach_lo) {
+  i64 u = (i64)blockIdx.x * 4 + threadIdx.x / kWave;
   const int lane = threadIdx.x & (kWave - 1);
+  if ((i64)blockIdx.x >= lo_block) {  // uniform per block: the second set (lowers)
+    u = ((i64)blockIdx.x - lo_block) * 4 + threadIdx.x / kWave;
+    mask = mask_lo;
+    n_nodes = n_lo;
+    words = 64;
+    reach = reach_lo;
+  }
   if (u >= n_nodes) return;  // uniform per wave
   uint32_t code = 0;
   if (words == 512) {
@@ -2260,6 +2270,7 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, 
     // box ops on small batches: voxel-exact face reach sets of uppers and lowers
     const bool box_op = op != TC_OP_REFINE && op != TC_OP_COARSEN;
     uint32_t* box_lreach = nullptr;
+    uint32_t* lreach_early = nullptr;  // lower reach sets computed with the uppers' (one launch)
     if (box_op && small_tiles && src->n1 <= kBoxReachLowers) {
       box_lreach = a.at<uint32_t>(o_lreach);
       launch("k_box_reach", k_box_reach, src->n2, 256, s, (const int32_t*)sv.upper_first, (int32_t)src->n2,
@@ -2280,8 +2291,12 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, 
       uint32_t* ureach = box_lreach ? a.at<uint32_t>(o_ureach) : nullptr;
       if (!box_lreach && op != TC_OP_COARSEN && src->n2 > 64) {
         ureach = a.at<uint32_t>(o_ureach);
-        launch("k_node_reach", k_node_reach, ceil_div((i64)src->n2, 4), 256, s, (const u64*)sv.upper_mask,
-               (i64)src->n2, 512, op, oi.m, ureach);
+        // the multi-launch lower stage's reach sets come from the same launch
+        const i64 ub = ceil_div((i64)src->n2, 4);
+        const i64 nlo = small_lowers ? 0 : (i64)src->n1;
+        if (nlo > 0) lreach_early = a.at<uint32_t>(o_lreach);
+        launch("k_node_reach", k_node_reach, ub + ceil_div(nlo, 4), 256, s, (const u64*)sv.upper_mask,
+               (i64)src->n2, 512, op, oi.m, ureach, ub, (const u64*)sv.lower_mask, nlo, lreach_early);
       }
       if (small_lowers) {  // the lower stage follows in the same workgroup
         launch("k_nodes_small", k_nodes_small, 1, kTilesThreads, s, (const int4*)sv.upper_origin,
@@ -2321,11 +2336,12 @@ tc_grid_batch* build_pass(const tc_grid_batch* src, int op, const OutAlloc& oa, 
     // lowers. The candidate -> source table starts empty; refine and the box ops
     // store every word of their candidates' leaf masks, coarsen ORs into zeros.
     if (!small_lowers) {
-      uint32_t* lreach = box_lreach;
+      uint32_t* lreach = box_lreach ? box_lreach : lreach_early;
       if (!lreach && op != TC_OP_COARSEN) {
         lreach = a.at<uint32_t>(o_lreach);
-        launch("k_node_reach", k_node_reach, ceil_div((i64)src->n1, 4), 256, s, (const u64*)sv.lower_mask,
-               (i64)src->n1, 64, op, oi.m, lreach);
+        const i64 lb = ceil_div((i64)src->n1, 4);
+        launch("k_node_reach", k_node_reach, lb, 256, s, (const u64*)sv.lower_mask, (i64)src->n1, 64, op, oi.m,
+               lreach, lb, (const u64*)nullptr, (i64)0, (uint32_t*)nullptr);
       }
       launch("k_lower_mark", k_lower_mark, ceil_div(nL, 256), 256, s, (const int4*)sv.lower_origin,
              (const u64*)sv.lower_mask, (const uint32_t*)lreach, nL, op, oi.m, (const int32_t*)tile_of_cand,

@@ -41,6 +41,43 @@ __device__ __forceinline__ T block_excl_scan(T v, T* s_wave, T& total) {
   return off + inc - v;
 }
 
+// Exclusive scan of in[0, n) into out[0, n], out[n] = the total (also written
+// to *total_out when given), by one workgroup of NT threads; every thread calls
+// it. Items are held blocked, I per thread per tile of NT * I items, and the
+// next tile's loads are issued before the current tile is scanned.
+template <typename T, int NT, int I>
+__device__ __forceinline__ void block_scan_all(const T* in, T* out, int64_t n, T* total_out, T* s_wave) {
+  constexpr int64_t kTile = (int64_t)NT * I;
+  const int64_t tb = (int64_t)threadIdx.x * I;
+  T v[I];
+#pragma unroll
+  for (int k = 0; k < I; ++k) v[k] = tb + k < n ? in[tb + k] : T(0);
+  T carry = 0;
+  for (int64_t c = 0; c < n; c += kTile) {  // uniform
+    T nx[I];
+    const int64_t nb = c + kTile + tb;
+#pragma unroll
+    for (int k = 0; k < I; ++k) nx[k] = nb + k < n ? in[nb + k] : T(0);
+    T sum = 0;
+#pragma unroll
+    for (int k = 0; k < I; ++k) sum += v[k];
+    T total;
+    T excl = block_excl_scan<T, NT>(sum, s_wave, total) + carry;
+#pragma unroll
+    for (int k = 0; k < I; ++k) {
+      const int64_t i = c + tb + k;
+      if (i < n) out[i] = excl;
+      excl += v[k];
+      v[k] = nx[k];
+    }
+    carry += total;
+  }
+  if (threadIdx.x == 0) {
+    out[n] = carry;
+    if (total_out) *total_out = carry;
+  }
+}
+
 __device__ __forceinline__ int popc64(uint64_t x) { return __popcll(x); }
 
 // Voxel counts of a 256-thread block's leaves (v = 0 on lanes that own no leaf):

@@ -66,38 +66,8 @@ constexpr int kScanSingleItems = sizeof(T) == 8 && NT > 256 ? 8 : 16;
 template <typename T, int NT>
 __global__ void __launch_bounds__(NT) k_scan_single(const T* in, T* out, i64 n_host, const int32_t* d_n,
                                                     T* total_out) {
-  constexpr int I = kScanSingleItems<T, NT>;
-  constexpr i64 kTile = (i64)NT * I;
   __shared__ T s_wave[NT / kWave];
-  const i64 n = clamp_n(n_host, d_n);
-  const i64 tb = (i64)threadIdx.x * I;
-  T v[I];
-#pragma unroll
-  for (int k = 0; k < I; ++k) v[k] = tb + k < n ? in[tb + k] : T(0);
-  T carry = 0;
-  for (i64 c = 0; c < n; c += kTile) {  // uniform
-    T nx[I];
-    const i64 nb = c + kTile + tb;
-#pragma unroll
-    for (int k = 0; k < I; ++k) nx[k] = nb + k < n ? in[nb + k] : T(0);
-    T sum = 0;
-#pragma unroll
-    for (int k = 0; k < I; ++k) sum += v[k];
-    T total;
-    T excl = block_excl_scan<T, NT>(sum, s_wave, total) + carry;
-#pragma unroll
-    for (int k = 0; k < I; ++k) {
-      const i64 i = c + tb + k;
-      if (i < n) out[i] = excl;
-      excl += v[k];
-      v[k] = nx[k];
-    }
-    carry += total;
-  }
-  if (threadIdx.x == 0) {
-    out[n] = carry;
-    if (total_out) *total_out = carry;
-  }
+  block_scan_all<T, NT, kScanSingleItems<T, NT>>(in, out, clamp_n(n_host, d_n), total_out, s_wave);
 }
 
 template <typename T>

@@ -321,6 +321,32 @@ __global__ void __launch_bounds__(kTailThreads) k_counts_tail(const int32_t* gri
                    host_rb);
 }
 
+// Up to kScanTailMax candidates whose packed counts the marking wrote: the
+// scan of the counts and the tail above in one workgroup (one launch instead of
+// two; the tail reads the scan this workgroup wrote, after a block barrier).
+constexpr i64 kScanTailMax = 65536;
+
+__global__ void __launch_bounds__(kTailThreads) k_scan_counts_tail(const i64* cand_counts, i64* cand_scan,
+                                                                   int32_t cap_c, const int32_t* grid_tile_begin,
+                                                                   const int32_t* tile_lower_base, int32_t cap_t,
+                                                                   const int32_t* d_num_tiles,
+                                                                   const int32_t* d_num_cands, int32_t B,
+                                                                   int32_t* upper_excl, int32_t* grid_info,
+                                                                   int32_t* readback, int32_t* host_rb) {
+  __shared__ int32_t s_tlb[kTailTiles + 1];
+  __shared__ int32_t s_uex[kTailTiles + 1];
+  __shared__ int32_t s_wave[kTailThreads / kWave];
+  __shared__ i64 s_wave64[kTailThreads / kWave];
+  const int32_t nt = *d_num_tiles;
+  const int32_t nc = min(max(*d_num_cands, 0), cap_c);
+  const int2 gt = load_grid_tiles(grid_tile_begin, B);
+  stage_tile_bases(tile_lower_base, cap_t, s_tlb);
+  block_scan_all<i64, kTailThreads, 8>(cand_counts, cand_scan, nc, nullptr, s_wave64);
+  __syncthreads();  // the scan is read below, by this workgroup only
+  counts_tail_body(grid_tile_begin, gt, s_tlb, cand_scan, nt, nc, B, s_uex, upper_excl, grid_info, readback, s_wave,
+                   host_rb);
+}
+
 // Small batches (at most kCountsSmallMax candidates and kTailTiles tiles):
 // candidate leaf counts and prefix tables, their packed scan and the tail above,
 // in one workgroup. Every global load (the counts, the candidate masks up to
@@ -414,6 +440,13 @@ bool tree_counts(TreeScratch& ts, int32_t B, hipStream_t s, int32_t* host_rb) {
            (const int32_t*)ts.tile_lower_base, (int32_t)ts.cap_tiles, (const int32_t*)ts.d_num_tiles,
            (const int32_t*)ts.d_num_cands, B, ts.upper_excl, ts.grid_info, ts.readback,
            ts.cand_counts_ready ? 1 : 0, host_rb);
+    return host_rb != nullptr;
+  }
+  if (ts.cand_counts_ready && ts.cap_cands <= kScanTailMax && ts.cap_tiles <= (i64)kTailTiles) {
+    launch("k_scan_counts_tail", k_scan_counts_tail, 1, kTailThreads, s, (const i64*)ts.cand_counts,
+           ts.cand_scan, (int32_t)ts.cap_cands, (const int32_t*)ts.grid_tile_begin,
+           (const int32_t*)ts.tile_lower_base, (int32_t)ts.cap_tiles, (const int32_t*)ts.d_num_tiles,
+           (const int32_t*)ts.d_num_cands, B, ts.upper_excl, ts.grid_info, ts.readback, host_rb);
     return host_rb != nullptr;
   }
   tree_count_cands(ts, s);
